@@ -1,0 +1,280 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than its own formula: a
+library routine (torch's bf16 conversion, torch's scaled-dot-product attention
+in fp64), a closed form, a brute-force enumeration, or an invariant that any
+correct implementation must satisfy.  A planted mistake in the oracle (a dropped
+term, a wrong sign, a transposed operand, an off-by-one in the top-p scan)
+fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rtp_oracle as O
+
+D = 128
+
+
+def _bits_from_f32(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _f32_from_bits(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ bf16 rounding
+
+def test_bf16_round_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    assert np.array_equal(O.f64_to_bf16(x.astype(np.float64)), _bits_from_f32(x))
+
+
+def test_bf16_round_ties_to_even_and_no_double_rounding():
+    one = 0x3F80
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7: tie goes to the even mantissa (1.0)
+    assert O.f64_to_bf16(np.array([1 + 2.0 ** -8]))[0] == one
+    # 1 + 3*2^-8 is the midpoint of 1+2^-7 (odd) and 1+2^-6 (even): rounds up
+    assert O.f64_to_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == one + 2
+    # slightly above a midpoint in fp64 but equal to it after fp32 rounding: must go up
+    assert O.f64_to_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -40]))[0] == one + 1
+    assert O.f64_to_bf16(np.array([-(1 + 2.0 ** -8 + 2.0 ** -40)]))[0] == (one + 1) | 0x8000
+    assert O.f64_to_bf16(np.array([0.0]))[0] == 0
+
+
+# ------------------------------------------------------------------ RoPE
+
+def _rope_complex(x, pos, base=1e6):
+    """Textbook RoPE as complex multiplication: (x_i + i x_{i+D/2}) * exp(i pos theta_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    d2 = x.shape[-1] // 2
+    theta = np.array([base ** (-(2.0 * i) / x.shape[-1]) for i in range(d2)])
+    z = (x[..., :d2] + 1j * x[..., d2:]) * np.exp(1j * np.asarray(pos, float)[..., None] * theta)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_rope_matches_complex_rotation():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((64, D))
+    pos = rng.integers(0, 1 << 20, 64)
+    # theta_i may differ by an ulp between the two pow evaluations: pos * 1 ulp ~ 2e-10
+    assert np.allclose(O.rope(x, pos), _rope_complex(x, pos), rtol=0, atol=1e-9)
+
+
+def test_rope_identity_norm_and_relative_position():
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    assert np.allclose(O.rope(q, 0), q, atol=0)
+    for p in (1, 77, 65535, 1048575):
+        assert abs(np.linalg.norm(O.rope(q, p)) - np.linalg.norm(q)) < 1e-12
+    d1 = O.rope(q, 1000) @ O.rope(k, 10)
+    d2 = O.rope(q, 5990) @ O.rope(k, 5000)
+    assert abs(d1 - d2) < 1e-10
+    # highest-frequency pair (theta_0 = 1): e_0 -> cos(p) e_0 + sin(p) e_64
+    e0 = np.zeros(D); e0[0] = 1
+    r = O.rope(e0, 3)
+    assert abs(r[0] - math.cos(3)) < 1e-15 and abs(r[64] - math.sin(3)) < 1e-15
+    e64 = np.zeros(D); e64[64] = 1
+    r = O.rope(e64, 3)
+    assert abs(r[0] + math.sin(3)) < 1e-15 and abs(r[64] - math.cos(3)) < 1e-15
+
+
+# ------------------------------------------------------------------ top-p
+
+def _brute_min_set(w, p):
+    n = len(w)
+    Z = w.sum()
+    for size in range(1, n + 1):
+        best = None
+        for U in itertools.combinations(range(n), size):
+            m = w[list(U)].sum()
+            if m >= p * Z and (best is None or m > best[0]):
+                best = (m, set(U))
+        if best is not None:
+            return best[1]
+    return set(range(n))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_top_p_brute_force_small(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 13))
+    s = (rng.standard_normal(n) * 3).astype(np.float32)
+    for p in (1e-6, 0.3, 0.5, 0.9, 0.999):
+        got = set(O.top_p_set(s, p)["set"].tolist())
+        w = np.exp(s.astype(np.float64) - s.max())
+        assert got == _brute_min_set(w, p), (n, p)
+
+
+def test_top_p_geometric_closed_form():
+    n = 20
+    s = (-np.arange(n) * math.log(2)).astype(np.float32)
+    for p, k in ((0.6, 2), (0.9, 4), (0.97, 6), (0.2, 1)):
+        assert math.ceil(-math.log2(1 - p * (1 - 2.0 ** -n))) == k
+        assert O.top_p_set(s, p)["set"].tolist() == list(range(k))
+
+
+def test_top_p_needles_closed_form():
+    N, n = 4096, 3
+    for L in (5.0, 8.0, 12.0):
+        s = np.zeros(N, dtype=np.float32)
+        pos = [10, 999, 3000]
+        s[pos] = L
+        E = math.exp(L)
+        share = n * E / (n * E + N - n)
+        T = O.top_p_set(s, 0.9)["set"].tolist()
+        if share >= 0.9:
+            assert T == pos
+        else:
+            assert T == list(range(N))  # the rest are tied zeros: all of them join
+
+
+def test_top_p_ties_and_p_one():
+    s = np.full(50, 1.5, dtype=np.float32)
+    assert len(O.top_p_set(s, 0.5)["set"]) == 50
+    r = np.random.default_rng(3).standard_normal(50).astype(np.float32)
+    t = O.top_p_set(r, 1.0)
+    assert len(t["set"]) == 50 and t["tau"] == -np.inf
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_top_p_invariants(seed):
+    rng = np.random.default_rng(200 + seed)
+    s = (rng.standard_normal(5000) * rng.uniform(0.5, 6)).astype(np.float32)
+    for p in (0.5, 0.8, 0.9, 0.95, 0.999):
+        t = O.top_p_set(s, p)
+        w = np.exp(s.astype(np.float64) - s.max())
+        Z = w.sum()
+        T = t["set"]
+        assert w[T].sum() >= p * Z                       # reaches p
+        above = s > np.float32(t["tau"])
+        assert w[above].sum() < p * Z                    # minimal threshold
+        assert s[T].min() >= np.float32(t["tau"])         # upward closed
+        assert (s[~np.isin(np.arange(len(s)), T)] < np.float32(t["tau"])).all()
+
+
+# ------------------------------------------------------------------ attention
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(4)
+    K = _bits_from_f32(rng.standard_normal((40, D)))
+    vrow = _bits_from_f32(rng.standard_normal(D))
+    V = np.tile(vrow, (40, 1))
+    q = rng.standard_normal(D)
+    assert np.allclose(O.attention(q, K, V, 0.1), _f32_from_bits(vrow), atol=1e-12)
+    V2 = _bits_from_f32(rng.standard_normal((40, D)))
+    assert np.allclose(O.attention(np.zeros(D), K, V2, 0.1),
+                       _f32_from_bits(V2).astype(np.float64).mean(0), atol=1e-12)
+    assert np.allclose(O.attention(q, K[7:8], V2[7:8], 0.1), _f32_from_bits(V2[7]), atol=0)
+
+
+def _sdpa64(q, K, V, scale, mask=None):
+    qt = torch.from_numpy(np.asarray(q, np.float64)).view(1, 1, 1, -1)
+    kt = torch.from_numpy(np.asarray(K, np.float64)).view(1, 1, K.shape[0], -1)
+    vt = torch.from_numpy(np.asarray(V, np.float64)).view(1, 1, V.shape[0], -1)
+    m = None if mask is None else torch.from_numpy(mask).view(1, 1, 1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=m, scale=scale).view(-1).numpy()
+
+
+def _small_wl(seed=5, N=700, window=128):
+    import workloads
+    return workloads.random_decode(seed, B=1, Hq=4, Hkv=2, N=N, ret_kv=[0], window=window,
+                                   n_sink=4, n_needles=3)
+
+
+def test_p_one_equals_dense_attention():
+    wl = _small_wl()
+    kc, vc, idx = O.caches_for(wl)
+    res = O.decode(wl, kc, vc, idx, top_p=1.0, heads=[0, 1])
+    pos = wl.N - 1
+    for h in (0, 1):
+        q = _rope_complex(O.bf16_to_f64(wl.q_pre[0, h]), pos)
+        K = _rope_complex(O.bf16_to_f64(wl.k_pre[0, 0]), np.arange(wl.N))
+        # the cache holds bf16(RoPE(k)); use the same rounded rows for the reference
+        K = O.bf16_to_f64(O.f64_to_bf16(K))
+        ref = _sdpa64(q, K, O.bf16_to_f64(wl.v[0, 0]), wl.attn_scale)
+        assert len(res[(0, h)]["S"]) == wl.N
+        assert np.allclose(res[(0, h)]["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_swa_equals_masked_dense_attention():
+    wl = _small_wl(seed=6, N=900, window=200)
+    kc, vc, idx = O.caches_for(wl)
+    res = O.decode(wl, kc, vc, idx, top_p=0.9, heads=[2, 3])
+    pos = wl.N - 1
+    j = np.arange(wl.N)
+    mask = ((j > pos - wl.window) & (j <= pos)) | (j < wl.n_sink)
+    assert mask.sum() == wl.window + wl.n_sink
+    for h in (2, 3):
+        q = _rope_complex(O.bf16_to_f64(wl.q_pre[0, h]), pos)
+        K = O.bf16_to_f64(O.f64_to_bf16(_rope_complex(O.bf16_to_f64(wl.k_pre[0, 1]), j)))
+        ref = _sdpa64(q, K, O.bf16_to_f64(wl.v[0, 1]), wl.attn_scale, mask)
+        assert np.allclose(res[(0, h)]["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_swa_window_covers_sinks_when_short():
+    L = O.swa_keys(pos=5, window=8192, n_sink=4)
+    assert L.tolist() == list(range(6))
+    L = O.swa_keys(pos=100, window=10, n_sink=4)
+    assert L.tolist() == [0, 1, 2, 3] + list(range(91, 101))
+
+
+def test_sinks_added_after_top_p():
+    wl = _small_wl(seed=7)
+    kc, vc, idx = O.caches_for(wl)
+    r = O.decode(wl, kc, vc, idx, top_p=0.5, heads=[0])[(0, 0)]
+    assert set(range(4)) <= set(r["S"].tolist())
+    assert set(r["T"].tolist()) <= set(r["S"].tolist())
+    assert set(r["S"].tolist()) == set(r["T"].tolist()) | {0, 1, 2, 3}
+
+
+# ------------------------------------------------------------------ append / index
+
+def test_index_matches_library_matmul():
+    wl = _small_wl(seed=8, N=2048)
+    _, _, idx = O.caches_for(wl)
+    k = torch.from_numpy(O.bf16_to_f64(wl.k_pre[0, 0]))
+    W = torch.from_numpy(O.bf16_to_f64(wl.w_k[0]))
+    exact = (k @ W).numpy()                     # products of bf16 are exact in fp64
+    f32 = exact.astype(np.float32)
+    lib = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = idx[0, 0]
+    diff = ours != lib
+    # the library path rounds twice (fp64 -> fp32 -> bf16); it may differ only where
+    # the fp32 image sits exactly on a bf16 midpoint
+    u = f32.view(np.uint32)
+    assert np.all((u[diff] & 0xFFFF) == 0x8000)
+    assert diff.mean() < 1e-3
+
+
+def test_scores_use_pre_rope_index():
+    wl = _small_wl(seed=9, N=300)
+    kc, vc, idx = O.caches_for(wl)
+    r = O.decode(wl, kc, vc, idx, top_p=0.9, heads=[1])[(0, 1)]
+    qi = O.bf16_to_f64(wl.q_pre[0, 1]) @ O.bf16_to_f64(wl.w_q[1])
+    s_ref = O.bf16_to_f64(idx[0, 0]) @ qi.astype(np.float32).astype(np.float64)
+    assert np.allclose(r["scores"], s_ref, rtol=1e-6, atol=1e-6)
+    # the index is not the projection of the rotated key
+    rot = O.bf16_to_f64(kc[0, 0]) @ O.bf16_to_f64(wl.w_k[0])
+    assert not np.allclose(O.bf16_to_f64(idx[0, 0]), rot, atol=1e-2)
+
+
+def test_prefill_row_p_one_is_causal_dense():
+    import workloads
+    wl = workloads.random_prefill(11, B=1, Hq=4, Hkv=2, N=400, Tq=16, ret_kv=[0], window=64)
+    kc, vc, idx = O.caches_for(wl)
+    for t in (0, 7, 15):
+        pos = wl.q_start + t
+        r = O.prefill_row(wl, kc, vc, idx, 0, 1, t, 1.0)
+        q = _rope_complex(O.bf16_to_f64(wl.q_pre[0, 1, t]), pos)
+        K = O.bf16_to_f64(kc[0, 0, :pos + 1])
+        ref = _sdpa64(q, K, O.bf16_to_f64(wl.v[0, 0, :pos + 1]), wl.attn_scale)
+        assert np.allclose(r["out"], ref, atol=1e-12)
+        assert len(r["S"]) == pos + 1
