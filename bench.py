@@ -1,0 +1,260 @@
+"""Benchmark of the head-wise sparse attention decode step on one MI355X.
+
+One step = the whole decode hot path of one layer over one batch:
+  append of the newest token (K/V caches + 16-dim index), the retrieval-head
+  decode (indexer scan + histogram, threshold, select, resolve, gather attention,
+  merge) and the local-head sliding-window attention.
+Default workload: 1M-context decode shaped like Qwen3-30B-A3B attention (B=1,
+32 q / 4 KV heads, KV head 0 retrieval with a 1M x 16 index, 3 SWA heads with
+window 8192 + 4 sinks, 512 planted clusters, p = 0.9), synthetic seeded inputs.
+
+Timing: W warm-up steps, then K timed steps.  Before each timed step a 512 MiB
+scratch write flushes the 256 MB Infinity Cache, so every step reads its
+working set from HBM; HIP events around each step (flush excluded) give the
+step time.  A second pass of K steps records the library's phase events for the
+per-kernel durations used by the roofline.  The CPU oracle is timed on a sample
+of whole steps on the host cores (rank 0, N=1 only).
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode μs/step + achieved HBM GB/s (% peak) at 128K–1M ctx; prefill tok/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Hip:
+    """Raw HIP events from the runtime torch already loaded (same SONAME)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e: int, stream: int) -> None:
+        assert self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a),
+                                            ctypes.c_void_p(b)) == 0
+        return f.value
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4])
+    ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
+              "step shards by (batch, KV head) with no exchange, see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_retrieval_amd as R
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl = W.make(args.config)
+    top_p = args.top_p if args.top_p is not None else wl.top_p[min(1, len(wl.top_p) - 1)]
+    log(f"workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} N={wl.N} ret={wl.ret_kv_heads} "
+        f"p={top_p} generated in {time.time() - t0:.1f}s")
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    layer = R.Layer(wl.B, wl.Hq, wl.Hkv, wl.N, wl.ret_kv_heads, wl.n_sink, wl.window,
+                    wl.rope_base)
+    N, B, G = wl.N, wl.B, wl.G
+    k_cache = torch.empty((B, wl.Hkv, N, 128), dtype=torch.int16, device="cuda")
+    v_cache = torch.empty_like(k_cache)
+    index = torch.empty((B, wl.n_ret, N, 16), dtype=torch.int16, device="cuda")
+    w_q, w_k, q = dev(wl.w_q), dev(wl.w_k), dev(wl.q_pre)
+    k_pre, v_pre = dev(wl.k_pre), dev(wl.v)
+    R.index_append(layer, k_pre, v_pre, w_k, 0, k_cache, v_cache, index)   # bulk prefill of caches
+    new_k = k_pre[:, :, N - 1:N].contiguous()
+    new_v = v_pre[:, :, N - 1:N].contiguous()
+    del k_pre, v_pre
+    out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+    ws = torch.empty(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
+    wss = torch.empty(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"caches built on the GPU ({time.time() - t0:.1f}s)")
+
+    hip = Hip()
+    stream = torch.cuda.current_stream().cuda_stream
+    n_ph = 7
+    ph_events = [hip.event() for _ in range(n_ph)]
+    extra = [hip.event() for _ in range(3)]
+    dbg_ph = R.Debug(0, 0, events=ph_events, pairs=B * wl.n_ret)
+
+    def step(debug=None, mark=False):
+        if mark:
+            hip.record(extra[0], stream)
+        R.index_append(layer, new_k, new_v, w_k, N - 1, k_cache, v_cache, index)
+        R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws,
+                             debug=debug)
+        if mark:
+            hip.record(extra[1], stream)
+        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss)
+        if mark:
+            hip.record(extra[2], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- headline: K steps, Infinity Cache flushed before each, events around each step
+    e0, e1 = hip.event(), hip.event()
+    step_ms = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        hip.record(e0, stream)
+        step()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        step_ms.append(hip.elapsed_ms(e0, e1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = float(np.mean(step_ms))
+    log(f"cold step: mean {ms * 1e3:.1f} us, median {np.median(step_ms) * 1e3:.1f} us")
+
+    # ---- warm: K back-to-back steps without flushing (working set may sit in the MALL)
+    torch.cuda.synchronize()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    warm_ms = hip.elapsed_ms(e0, e1) / args.steps
+
+    # ---- phases: K more cold steps with the library's phase events
+    names = ["score_hist", "threshold", "select", "resolve", "gather", "merge"]
+    ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        step(debug=dbg_ph, mark=True)
+        torch.cuda.synchronize()
+        for k, n in enumerate(names):
+            ph[n].append(hip.elapsed_ms(ph_events[k], ph_events[k + 1]))
+        ph["append"].append(hip.elapsed_ms(extra[0], ph_events[0]))
+        ph["swa"].append(hip.elapsed_ms(extra[1], extra[2]))
+        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[6]))
+    phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
+    union = dbg_ph.union_count.cpu().numpy().astype(np.int64)
+
+    # ---- algorithmic bytes of one step
+    n_loc = wl.Hkv - wl.n_ret
+    lo = max(0, N - 1 - wl.window + 1)
+    swa_rows = min(wl.n_sink, lo) + (N - 1 - lo + 1)
+    bytes_index = B * wl.n_ret * N * 32
+    bytes_gather = int(union.sum()) * 512
+    bytes_swa = B * n_loc * swa_rows * 512
+    bytes_small = B * wl.Hq * 256 * 2 + wl.w_q.size * 2 + B * wl.Hkv * (512 + 512) + \
+        B * wl.n_ret * 32
+    step_bytes = bytes_index + bytes_gather + bytes_swa + bytes_small
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    score_us = phases_us["score_hist"]
+    ach = bytes_index / (score_us * 1e-6) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(ms * 1e3, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 compute",
+        "data": "synthetic (seeded planted-cluster keys, random-init indexer projections)",
+        "config": {"workload": wl.name, "batch": B, "context": N, "q_heads": wl.Hq,
+                   "kv_heads": wl.Hkv, "retrieval_kv_heads": wl.ret_kv_heads,
+                   "window": wl.window, "sinks": wl.n_sink, "top_p": top_p,
+                   "parallelism": "single GPU"},
+        "achieved_GBps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "median_us_per_step": round(float(np.median(step_ms)) * 1e3, 2),
+        "wall_s_timed": round(wall, 3),
+        "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
+                       "small": bytes_small, "union_rows": int(union.sum())},
+        "phases_us": phases_us,
+        "roofline": {"bound": "hbm", "kernel": "k_score_hist (indexer scan + mass histogram)",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, top_p, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, top_p: float, budget_s: float):
+    """Time the CPU oracle on whole decode steps of the same workload (host cores)."""
+    import numpy as np
+
+    from oracle import rtp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    t0 = time.time()
+    N = wl.N
+    lo = max(0, N - wl.window)
+    rows = {kv: (None if kv in wl.ret_kv_heads else
+                 np.union1d(np.arange(lo, N), np.arange(min(wl.n_sink, N))))
+            for kv in range(wl.Hkv)}
+    kc, vc, idx = O.caches_for(wl, rows_needed=rows)
+    log(f"oracle caches built in {time.time() - t0:.1f}s")
+    n, spent = 0, 0.0
+    while n == 0 or spent + spent / n <= budget_s:
+        t = time.perf_counter()
+        O.append(wl.k_pre[:, :, N - 1:N], wl.v[:, :, N - 1:N], wl.w_k, wl.ret_kv_heads, N - 1,
+                 wl.rope_base)
+        O.decode(wl, kc, vc, idx, top_p)
+        spent += time.perf_counter() - t
+        n += 1
+    us = spent / n * 1e6
+    log(f"oracle: {n} steps, {us / 1e3:.1f} ms/step")
+    return {"value": round(us, 1), "unit": "us/step", "cores": int(threads),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{n} whole decode steps (append of the newest token + all {wl.Hq} "
+                      f"heads) of the same workload; oracle caches built beforehand"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,217 @@
+/*
+ * rtp.h - C ABI of the MI355X (gfx950) head-wise sparse attention step of
+ * RTPurbo ("Full Attention Strikes Back", arXiv 2605.16928).
+ *
+ * Sources cited below (pages about the paper):
+ *   [techwalker] techwalker article: §2 head roles (retrieval vs local heads,
+ *                attention sinks), §3 16-dim indexer, §4 dynamic top-p budget,
+ *                §6 GPU kernels (histogram top-p, split-KV gather), §8 window
+ *                8192 + 4 sinks.
+ *   [ngjoo]      ngjoo paper digest: abstract (full KV only for retrieval heads
+ *                plus a lightweight token indexer) and core method (pre-RoPE
+ *                low-dimensional projections, dynamic top-p thresholding).
+ *   [v2]         RTPurboV2 article (aitntnews): finding 1 (85% of heads are
+ *                streaming heads served by a sliding window), finding 2
+ *                (16-dim projector), finding 4 (top-p).
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are raw bf16 bit patterns (rtp_bf16), row-major, contiguous,
+ *     in DEVICE memory, 16-byte aligned.  D (head_dim) = 128, r (idx_rank) = 16.
+ *   - desc and everything it points to (ret_kv_heads) is HOST memory, read
+ *     during the call only.
+ *   - The caller owns every buffer.  The library allocates nothing, frees
+ *     nothing, never synchronises and never copies between host and device.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously; device faults surface at the caller's next
+ *     synchronisation as a HIP error.
+ *   - Host-side validation runs before any launch.  A non-zero rtp_status
+ *     means nothing was enqueued.  RTP_ERR_HIP means a launch failed;
+ *     rtp_last_error() then holds the HIP error text (thread-local).
+ *   - Query heads map to KV heads as kv(h) = h / G with G = n_q_heads /
+ *     n_kv_heads.  Retrieval KV heads are listed in desc->ret_kv_heads; every
+ *     other KV head is a local (streaming) head ([techwalker] §2; [v2] finding 1).
+ *   - Token j of the cache sits at RoPE position j.  RoPE pairs dimension i with
+ *     i + D/2, theta_i = rope_base^(-2i/D), angles evaluated in fp64.
+ *   - Workspace: scratch device memory of at least rtp_workspace_size() bytes,
+ *     256-byte aligned.  Its contents need no initialisation; calls that share
+ *     one workspace must not overlap in time.
+ *   - NaN/Inf inputs are outside the contract.
+ */
+#ifndef RTP_H_
+#define RTP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rtp_bf16; /* bf16 bit pattern */
+
+typedef enum {
+  RTP_OK = 0,
+  RTP_ERR_NULL = 1,        /* a required pointer is NULL */
+  RTP_ERR_ALIGN = 2,       /* a device pointer is not 16-byte aligned (workspace: 256) */
+  RTP_ERR_SHAPE = 3,       /* inconsistent or non-positive sizes */
+  RTP_ERR_RANGE = 4,       /* positions, top_p or head ids out of range */
+  RTP_ERR_UNSUPPORTED = 5, /* head_dim != 128, idx_rank != 16, unsupported G */
+  RTP_ERR_WORKSPACE = 6,   /* workspace smaller than rtp_workspace_size() */
+  RTP_ERR_HIP = 7          /* a HIP launch failed */
+} rtp_status;
+
+/* Layer description (host memory). */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t idx_rank;     /* must be 16 */
+  int32_t max_seq;      /* capacity of the caches in tokens */
+  int32_t n_ret;        /* number of retrieval KV heads, 0..Hkv */
+  const int32_t* ret_kv_heads; /* [n_ret] ascending, distinct, in [0, Hkv) */
+  int32_t n_sink;       /* attention-sink tokens kept by every head (4) */
+  int32_t window;       /* sliding window of local heads, in tokens (8192) */
+  double rope_base;     /* RoPE base (1e6) */
+} rtp_layer_desc;
+
+/* Optional outputs for inspection and timing.  Any member may be NULL / 0.
+ * Layout per call: decode [B][n_ret*G] entries; prefill [B][n_ret*G][Tq].
+ * sel_idx holds the selected token ids (top-p set united with the sinks) of each
+ * entry in unspecified order, at most sel_cap of them; sel_count holds the true
+ * set size even when it exceeds sel_cap; tau holds the threshold score (-inf
+ * when top_p >= 1 keeps every key); union_count [B][n_ret] holds, per retrieval
+ * KV head, the number of distinct K/V rows read (the union of the G sets).
+ * phase_events, when non-NULL, are n_phase_events caller-created hipEvent_t
+ * handles; the decode records event 0 before its first kernel and event k after
+ * kernel k of: 1 score+histogram, 2 threshold, 3 select, 4 resolve, 5 gather,
+ * 6 merge (n_phase_events must be >= 7). */
+typedef struct {
+  int32_t* sel_idx;     /* [entries][sel_cap] device */
+  int32_t* sel_count;   /* [entries] device */
+  float* tau;           /* [entries] device */
+  int32_t sel_cap;
+  int32_t* union_count; /* [B][n_ret] device */
+  void* const* phase_events; /* host array of hipEvent_t */
+  int32_t n_phase_events;
+} rtp_debug_out;
+
+/* Operation ids for rtp_workspace_size(). */
+enum { RTP_OP_DECODE = 0, RTP_OP_PREFILL = 1, RTP_OP_SWA = 2, RTP_OP_APPEND = 3 };
+
+/*
+ * rtp_index_append - write T new tokens at positions start_pos .. start_pos+T-1.
+ *
+ * For every (b, kv head, token):  k_cache row = bf16(RoPE(k_pre row, position)),
+ * v_cache row = v row.  For every retrieval KV head i (desc->ret_kv_heads[i]):
+ * index row = bf16(k_pre row . w_k[i]), computed from the PRE-RoPE key
+ * ([techwalker] §3: a pair of 128->16 projections per retrieval head;
+ * [ngjoo] core method: pre-RoPE projections; the index is kept per cached token).
+ * Both roundings are round-to-nearest-even of the exact (fp64) value.
+ *
+ *   k_pre, v  [B][Hkv][T][D]       bf16, device, read
+ *   w_k       [n_ret][D][r]        bf16, device, read
+ *   k_cache   [B][Hkv][max_seq][D] bf16, device, rows written
+ *   v_cache   [B][Hkv][max_seq][D] bf16, device, rows written
+ *   index     [B][n_ret][max_seq][r] bf16, device, rows written (may be NULL if n_ret == 0)
+ * Errors: RTP_ERR_RANGE if start_pos < 0 or start_pos + T > max_seq; RTP_ERR_SHAPE if T < 1.
+ */
+rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre,
+                            const rtp_bf16* v, const rtp_bf16* w_k, int32_t start_pos,
+                            int32_t T, rtp_bf16* k_cache, rtp_bf16* v_cache,
+                            rtp_bf16* index, void* stream);
+
+/*
+ * rtp_decode_sparse_attn - one decode step of every retrieval q-head.
+ *
+ * The query of each batch row sits at position seq_len-1 (its own token is
+ * already in the caches).  For retrieval q-head h of KV head kv:
+ *   qi   = q_pre[b][h] . w_q[h]                     (16-dim, fp32)
+ *   s_j  = idx_scale * <qi, index[b][kv][j]>        for every cached j < seq_len
+ *                                                   ([techwalker] §3)
+ *   T    = smallest highest-scoring set of keys whose softmax mass
+ *          exp(s_j - max s) / Z reaches top_p; realised as {j : s_j >= tau} with
+ *          ties at tau included; top_p >= 1 keeps every key
+ *          ([techwalker] §4; [ngjoo] core method; [v2] finding 4)
+ *   S    = T united with the first n_sink tokens ([techwalker] §2, §8)
+ *   out  = softmax over S of attn_scale * <RoPE(q_pre, seq_len-1), k_cache[j]>,
+ *          weighted sum of v_cache[j] over S ([techwalker] §3: exact 128-dim
+ *          attention on the selected tokens only)
+ * Scores and masses are fp32 per token with fp64 reductions; the attention
+ * accumulates in fp32 and rounds the output to bf16.  The selection is
+ * deterministic (integer-exact mass sums).
+ *
+ *   q_pre    [B][Hq][D] bf16 device; only retrieval q-heads are read
+ *   w_q      [n_ret*G][D][r] bf16 device: retrieval q-heads in head order
+ *   k_cache, v_cache [B][Hkv][max_seq][D] bf16 device (k_cache post-RoPE)
+ *   index    [B][n_ret][max_seq][r] bf16 device
+ *   out      [B][Hq][D] bf16 device; only retrieval q-head rows are written
+ *   dbg      optional (NULL or host struct with device pointers)
+ * Errors: RTP_ERR_RANGE if seq_len < 1 or > max_seq, top_p not in (0, 1] or NaN;
+ *   RTP_ERR_UNSUPPORTED if G is not 1, 2, 4 or 8; RTP_ERR_WORKSPACE if ws_bytes is
+ *   smaller than rtp_workspace_size(desc, RTP_OP_DECODE, 1, seq_len).
+ */
+rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                  const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                  const rtp_bf16* v_cache, const rtp_bf16* index,
+                                  int32_t seq_len, float top_p, float idx_scale,
+                                  float attn_scale, rtp_bf16* out, const rtp_debug_out* dbg,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_prefill_chunk - retrieval q-heads of a chunk of Tq query rows at positions
+ * q_start .. q_start+Tq-1 (their tokens already appended).  Each row t runs the
+ * decode computation above with keys j <= q_start+t (causal): indexer scores,
+ * its own top-p set plus sinks, exact attention over that set.
+ *
+ *   q_pre  [B][Hq][Tq][D] bf16 device;  out [B][Hq][Tq][D] bf16 device (retrieval
+ *   q-head rows written).  Other arguments as for rtp_decode_sparse_attn.
+ * Errors: RTP_ERR_RANGE if q_start < 0 or q_start + Tq > max_seq; RTP_ERR_SHAPE if
+ *   Tq < 1; otherwise as for decode (workspace op RTP_OP_PREFILL).
+ */
+rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                             int32_t q_start, int32_t Tq, const rtp_bf16* w_q,
+                             const rtp_bf16* k_cache, const rtp_bf16* v_cache,
+                             const rtp_bf16* index, float top_p, float idx_scale,
+                             float attn_scale, rtp_bf16* out, const rtp_debug_out* dbg,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_swa_attn - local (streaming) q-heads: attention over the sliding window
+ * (pos - window, pos] plus the first n_sink tokens, for query rows at positions
+ * q_start .. q_start+Tq-1 ([techwalker] §2 and §8: window 8192 + 4 sinks;
+ * [v2] finding 1).  Tq = 1 is a decode step (q_pre [B][Hq][D]); Tq > 1 is a
+ * causal prefill chunk (q_pre [B][Hq][Tq][D]).  out has the layout of q_pre;
+ * only local q-head rows are written.
+ * Errors: RTP_ERR_RANGE if q_start < 0 or q_start + Tq > max_seq or window < 1;
+ *   RTP_ERR_UNSUPPORTED if G is not 1, 2, 4 or 8; RTP_ERR_WORKSPACE as above
+ *   (op RTP_OP_SWA).
+ */
+rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                        int32_t Tq, const rtp_bf16* k_cache, const rtp_bf16* v_cache,
+                        float attn_scale, rtp_bf16* out, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * rtp_workspace_size - bytes of workspace an operation needs.
+ *   op = RTP_OP_DECODE (Tq ignored), RTP_OP_PREFILL, RTP_OP_SWA (Tq query rows),
+ *   RTP_OP_APPEND (always 0).  seq_len = context length of the call (for prefill
+ *   and SWA: q_start + Tq).  *bytes is written on success.
+ */
+rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq,
+                              int32_t seq_len, size_t* bytes);
+
+/* Static text for a status code. */
+const char* rtp_status_string(rtp_status status);
+
+/* Detail text of the last non-OK status returned on this thread ("" if none). */
+const char* rtp_last_error(void);
+
+/* ABI version of this header: 1. */
+int32_t rtp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTP_H_ */

@@ -1,0 +1,10 @@
+"""MI355X (gfx950) head-wise sparse attention step of RTPurbo.
+
+The compute path is librtp.so (hand-written HIP kernels behind the C ABI in
+include/rtp.h); this package only binds it.  Build with
+`python -m sparse_attention_long_retrieval_amd.build`.
+"""
+from .binding import (  # noqa: F401
+    OP_APPEND, OP_DECODE, OP_PREFILL, OP_SWA, EXPORTED, LIB_PATH, Debug, Layer, RtpError,
+    decode_sparse_attn, index_append, lib, prefill_chunk, swa_attn, workspace_size,
+)

@@ -1,0 +1,293 @@
+// C ABI of the head-wise sparse attention step: host-side validation, workspace
+// planning and launch.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rtp.h"
+#include "rtp_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+rtp_status fail(rtp_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+rtp_status check_desc(const rtp_layer_desc* d) {
+  if (!d) return fail(RTP_ERR_NULL, "desc is NULL");
+  if (d->head_dim != 128) return fail(RTP_ERR_UNSUPPORTED, "head_dim %d (only 128)", d->head_dim);
+  if (d->idx_rank != 16) return fail(RTP_ERR_UNSUPPORTED, "idx_rank %d (only 16)", d->idx_rank);
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->max_seq < 1)
+    return fail(RTP_ERR_SHAPE, "batch, n_q_heads, n_kv_heads and max_seq must be >= 1");
+  if (d->n_kv_heads > rtp::kMaxKv) return fail(RTP_ERR_UNSUPPORTED, "n_kv_heads > %d", rtp::kMaxKv);
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(RTP_ERR_SHAPE, "n_q_heads %d not a multiple of n_kv_heads %d", d->n_q_heads,
+                d->n_kv_heads);
+  if (d->max_seq > (1 << 27)) return fail(RTP_ERR_UNSUPPORTED, "max_seq > 2^27");
+  if (d->n_ret < 0 || d->n_ret > d->n_kv_heads)
+    return fail(RTP_ERR_SHAPE, "n_ret %d outside [0, n_kv_heads]", d->n_ret);
+  if (d->n_ret > 0 && !d->ret_kv_heads) return fail(RTP_ERR_NULL, "ret_kv_heads is NULL");
+  for (int i = 0; i < d->n_ret; ++i) {
+    const int h = d->ret_kv_heads[i];
+    if (h < 0 || h >= d->n_kv_heads) return fail(RTP_ERR_RANGE, "ret_kv_heads[%d]=%d out of range", i, h);
+    if (i > 0 && h <= d->ret_kv_heads[i - 1])
+      return fail(RTP_ERR_RANGE, "ret_kv_heads must be ascending and distinct");
+  }
+  if (d->n_sink < 0) return fail(RTP_ERR_RANGE, "n_sink < 0");
+  if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base)) return fail(RTP_ERR_RANGE, "rope_base");
+  return RTP_OK;
+}
+
+int group(const rtp_layer_desc* d) { return d->n_q_heads / d->n_kv_heads; }
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
+rtp_status check_dev(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(RTP_ERR_NULL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(RTP_ERR_ALIGN, "%s not %zu-byte aligned", name, align);
+  return RTP_OK;
+}
+
+#define RTP_TRY(x)                  \
+  do {                              \
+    rtp_status _s = (x);            \
+    if (_s != RTP_OK) return _s;    \
+  } while (0)
+
+int swa_rows(int pos, int window, int n_sink) {
+  const int lo = pos - window + 1 > 0 ? pos - window + 1 : 0;
+  const int ns_out = n_sink < lo ? n_sink : lo;
+  return ns_out + (pos - lo + 1);
+}
+
+void local_heads(const rtp_layer_desc* d, int* loc, int* n_loc) {
+  int n = 0;
+  for (int h = 0; h < d->n_kv_heads; ++h) {
+    bool ret = false;
+    for (int i = 0; i < d->n_ret; ++i) ret |= d->ret_kv_heads[i] == h;
+    if (!ret) loc[n++] = h;
+  }
+  *n_loc = n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rtp_status_string(rtp_status s) {
+  switch (s) {
+    case RTP_OK: return "ok";
+    case RTP_ERR_NULL: return "null pointer";
+    case RTP_ERR_ALIGN: return "misaligned pointer";
+    case RTP_ERR_SHAPE: return "inconsistent shape";
+    case RTP_ERR_RANGE: return "value out of range";
+    case RTP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case RTP_ERR_WORKSPACE: return "workspace too small";
+    case RTP_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* rtp_last_error(void) { return g_last_error; }
+
+int32_t rtp_abi_version(void) { return 1; }
+
+rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq, int32_t seq_len,
+                              size_t* bytes) {
+  RTP_TRY(check_desc(desc));
+  if (!bytes) return fail(RTP_ERR_NULL, "bytes is NULL");
+  if (seq_len < 1 || seq_len > desc->max_seq) return fail(RTP_ERR_RANGE, "seq_len %d", seq_len);
+  const int G = group(desc);
+  switch (op) {
+    case RTP_OP_APPEND: *bytes = 0; return RTP_OK;
+    case RTP_OP_DECODE:
+      *bytes = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+      return RTP_OK;
+    case RTP_OP_SWA: {
+      if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
+      if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+      int loc[rtp::kMaxKv], n_loc;
+      local_heads(desc, loc, &n_loc);
+      *bytes = rtp::swa_workspace(desc->batch, n_loc, G, Tq,
+                                  swa_rows(seq_len - 1, desc->window, desc->n_sink), nullptr, nullptr);
+      return RTP_OK;
+    }
+    case RTP_OP_PREFILL:
+      return fail(RTP_ERR_UNSUPPORTED, "rtp_prefill_chunk not available yet");
+    default: return fail(RTP_ERR_RANGE, "unknown op %d", op);
+  }
+}
+
+rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, const rtp_bf16* v,
+                            const rtp_bf16* w_k, int32_t start_pos, int32_t T, rtp_bf16* k_cache,
+                            rtp_bf16* v_cache, rtp_bf16* index, void* stream) {
+  RTP_TRY(check_desc(desc));
+  RTP_TRY(check_dev(k_pre, "k_pre"));
+  RTP_TRY(check_dev(v, "v"));
+  RTP_TRY(check_dev(k_cache, "k_cache"));
+  RTP_TRY(check_dev(v_cache, "v_cache"));
+  if (desc->n_ret > 0) {
+    RTP_TRY(check_dev(w_k, "w_k"));
+    RTP_TRY(check_dev(index, "index"));
+  }
+  if (T < 1) return fail(RTP_ERR_SHAPE, "T %d < 1", T);
+  if (start_pos < 0 || (int64_t)start_pos + T > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "start_pos %d + T %d outside max_seq %d", start_pos, T, desc->max_seq);
+  rtp::AppendPlan p;
+  p.k_pre = k_pre;
+  p.v = v;
+  p.w_k = w_k;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.index = index;
+  p.B = desc->batch;
+  p.Hkv = desc->n_kv_heads;
+  p.n_ret = desc->n_ret;
+  p.max_seq = desc->max_seq;
+  p.start_pos = start_pos;
+  p.T = T;
+  p.rope_base = desc->rope_base;
+  for (int h = 0; h < rtp::kMaxKv; ++h) p.ret_slot[h] = -1;
+  for (int i = 0; i < desc->n_ret; ++i) p.ret_slot[desc->ret_kv_heads[i]] = i;
+  hipError_t e = rtp::launch_append(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return RTP_OK;
+}
+
+rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                  const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                  const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                                  float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                                  const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  RTP_TRY(check_desc(desc));
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
+  if (desc->n_ret == 0) return RTP_OK;
+  RTP_TRY(check_dev(q_pre, "q_pre"));
+  RTP_TRY(check_dev(w_q, "w_q"));
+  RTP_TRY(check_dev(k_cache, "k_cache"));
+  RTP_TRY(check_dev(v_cache, "v_cache"));
+  RTP_TRY(check_dev(index, "index"));
+  RTP_TRY(check_dev(out, "out"));
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  if (seq_len < 1 || seq_len > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "seq_len %d outside [1, max_seq %d]", seq_len, desc->max_seq);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(RTP_ERR_RANGE, "top_p must lie in (0, 1]");
+  if (!std::isfinite(idx_scale) || !std::isfinite(attn_scale))
+    return fail(RTP_ERR_RANGE, "idx_scale and attn_scale must be finite");
+  if (dbg && (dbg->sel_idx && dbg->sel_cap < 1)) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
+  if (dbg && dbg->phase_events && dbg->n_phase_events < 7)
+    return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 7");
+  const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+  if (ws_bytes < need)
+    return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rtp::DecPlan p;
+  memset(&p, 0, sizeof(p));
+  p.q_pre = q_pre;
+  p.w_q = w_q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.index = index;
+  p.out = out;
+  p.B = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.Hkv = desc->n_kv_heads;
+  p.G = G;
+  p.n_ret = desc->n_ret;
+  p.max_seq = desc->max_seq;
+  p.N = seq_len;
+  p.n_sink = desc->n_sink;
+  for (int i = 0; i < desc->n_ret; ++i) p.ret_kv[i] = desc->ret_kv_heads[i];
+  p.top_p = top_p;
+  p.idx_scale = idx_scale;
+  p.attn_scale = attn_scale;
+  p.rope_base = desc->rope_base;
+  rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, &p, (char*)workspace);
+  if (dbg) {
+    p.dbg_idx = dbg->sel_idx;
+    p.dbg_cnt = dbg->sel_count;
+    p.dbg_tau = dbg->tau;
+    p.dbg_cap = dbg->sel_cap;
+    p.dbg_union = dbg->union_count;
+    p.events = (hipEvent_t*)dbg->phase_events;
+  }
+  hipError_t e = rtp::launch_decode(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return RTP_OK;
+}
+
+rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                             int32_t Tq, const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                             const rtp_bf16* v_cache, const rtp_bf16* index, float top_p,
+                             float idx_scale, float attn_scale, rtp_bf16* out,
+                             const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  (void)q_pre; (void)q_start; (void)Tq; (void)w_q; (void)k_cache; (void)v_cache; (void)index;
+  (void)top_p; (void)idx_scale; (void)attn_scale; (void)out; (void)dbg; (void)workspace;
+  (void)ws_bytes; (void)stream;
+  RTP_TRY(check_desc(desc));
+  return fail(RTP_ERR_UNSUPPORTED, "rtp_prefill_chunk not available yet");
+}
+
+rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                        int32_t Tq, const rtp_bf16* k_cache, const rtp_bf16* v_cache,
+                        float attn_scale, rtp_bf16* out, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  RTP_TRY(check_desc(desc));
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
+  if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
+  if (q_start < 0 || (int64_t)q_start + Tq > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "q_start %d + Tq %d outside max_seq", q_start, Tq);
+  if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+  if (!std::isfinite(attn_scale)) return fail(RTP_ERR_RANGE, "attn_scale must be finite");
+  int loc[rtp::kMaxKv], n_loc;
+  local_heads(desc, loc, &n_loc);
+  if (n_loc == 0) return RTP_OK;
+  RTP_TRY(check_dev(q_pre, "q_pre"));
+  RTP_TRY(check_dev(k_cache, "k_cache"));
+  RTP_TRY(check_dev(v_cache, "v_cache"));
+  RTP_TRY(check_dev(out, "out"));
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
+  const int rows = swa_rows(q_start, desc->window, desc->n_sink);
+  const size_t need = rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, nullptr, nullptr);
+  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rtp::SwaPlan p;
+  memset(&p, 0, sizeof(p));
+  p.q_pre = q_pre;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.out = out;
+  p.B = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.Hkv = desc->n_kv_heads;
+  p.G = G;
+  p.max_seq = desc->max_seq;
+  p.n_sink = desc->n_sink;
+  p.window = desc->window;
+  p.n_loc = n_loc;
+  for (int i = 0; i < n_loc; ++i) p.loc_kv[i] = loc[i];
+  p.attn_scale = attn_scale;
+  p.rope_base = desc->rope_base;
+  p.q_start = q_start;
+  p.Tq = Tq;
+  rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, &p, (char*)workspace);
+  hipError_t e = rtp::launch_swa_decode(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "swa launch: %s", hipGetErrorString(e));
+  return RTP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, run the C ABI, compare
+against the oracle.
+
+Tolerances (stated once here, used by every GPU test):
+  * selected sets: bit-exact except tokens whose oracle fp32 score lies within
+    BAND_REL * max(|tau|, 1) of the oracle threshold tau.  When a set differs
+    outside that band, the GPU's own threshold must still be a valid top-p
+    threshold under the oracle's fp64 masses within MASS_TOL (relative): the
+    GPU scores differ from the oracle's by fp32 rounding (a 128-term fp32 dot
+    for qi, a 16-term fp32 dot for s: |ds| <~ 1e-5 at |s| ~ 20), which moves every
+    weight exp(s - m) by up to ~1e-5 relative, so a running mass that crosses
+    p*Z within that margin may end one token earlier or later.
+  * outputs: |o_gpu - o_oracle| <= OUT_TOL (bf16 output, fp32 accumulation); for
+    |o| >= 4, where half a bf16 ulp alone exceeds it, OUT_TOL + half an ulp.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+import sparse_attention_long_retrieval_amd as R
+from oracle import rtp_oracle as O
+
+BAND_REL = 1e-5
+MASS_TOL = 1e-4
+OUT_TOL = 1e-2
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda")
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def bf16_f64(bits):
+    return O.bf16_to_f64(bits)
+
+
+class Device:
+    """One workload's caches and index resident on the GPU (oracle append output)."""
+
+    def __init__(self, wl, kc: np.ndarray, vc: np.ndarray, idx: np.ndarray,
+                 max_seq: Optional[int] = None):
+        self.wl = wl
+        self.max_seq = max_seq or wl.N
+        B, Hkv, N, D = kc.shape
+        self.layer = R.Layer(wl.B, wl.Hq, wl.Hkv, self.max_seq, wl.ret_kv_heads, wl.n_sink,
+                             wl.window, wl.rope_base)
+        if self.max_seq == N:
+            self.kc, self.vc = to_dev(kc), to_dev(vc)
+            self.idx = to_dev(idx) if wl.n_ret else torch.zeros(16, dtype=torch.int16,
+                                                                 device="cuda")
+        else:
+            self.kc = torch.zeros((B, Hkv, self.max_seq, D), dtype=torch.int16, device="cuda")
+            self.vc = torch.zeros_like(self.kc)
+            self.kc[:, :, :N] = to_dev(kc)
+            self.vc[:, :, :N] = to_dev(vc)
+            self.idx = torch.zeros((B, max(1, wl.n_ret), self.max_seq, 16), dtype=torch.int16,
+                                   device="cuda")
+            if wl.n_ret:
+                self.idx[:, :, :N] = to_dev(idx)
+        self.q = to_dev(wl.q_pre)
+        self.w_q = to_dev(wl.w_q) if wl.n_ret else torch.zeros(16, dtype=torch.int16,
+                                                                 device="cuda")
+
+    def decode(self, top_p: float, debug_cap: int = 0, idx_scale: float = 1.0):
+        wl = self.wl
+        out = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+        ws = torch.empty(max(256, R.workspace_size(self.layer, R.OP_DECODE, wl.N)),
+                         dtype=torch.uint8, device="cuda")
+        dbg = R.Debug(wl.B * wl.n_ret * wl.G, debug_cap) if debug_cap else None
+        R.decode_sparse_attn(self.layer, self.q, self.w_q, self.kc, self.vc, self.idx, wl.N,
+                             top_p, out, ws, idx_scale=idx_scale, debug=dbg)
+        wss = torch.empty(max(256, R.workspace_size(self.layer, R.OP_SWA, wl.N)),
+                          dtype=torch.uint8, device="cuda")
+        R.swa_attn(self.layer, self.q, wl.N - 1, 1, self.kc, self.vc, out, wss)
+        torch.cuda.synchronize()
+        res = {"out": from_dev(out)}
+        if dbg is not None:
+            res["cnt"] = dbg.sel_count.cpu().numpy()
+            res["idx"] = dbg.sel_idx.cpu().numpy()
+            res["tau"] = dbg.tau.cpu().numpy()
+        return res
+
+
+def gpu_set(res, unit: int) -> np.ndarray:
+    c = int(res["cnt"][unit])
+    cap = res["idx"].shape[1]
+    assert c <= cap, f"debug capacity {cap} < set size {c}"
+    return np.sort(res["idx"][unit, :c].astype(np.int64))
+
+
+def check_set(S_gpu: np.ndarray, tau_gpu: float, r: Dict, p: float, n_sink: int) -> str:
+    """Compare a GPU set with the oracle's; return 'exact', 'band' or 'valid-alt'."""
+    n = len(r["scores"])
+    if p >= 1.0:
+        assert np.array_equal(S_gpu, np.arange(n)), "p=1 must keep every key"
+        return "exact"
+    S_o = r["S"]
+    if np.array_equal(S_gpu, S_o):
+        return "exact"
+    s = r["scores"].astype(np.float64)
+    tau = float(r["tau"])
+    band = BAND_REL * max(abs(tau), 1.0)
+    diff = np.setxor1d(S_gpu, S_o)
+    if np.all(np.abs(s[diff] - tau) <= band):
+        return "band"
+    # a different rank boundary: the GPU threshold must be a valid top-p threshold
+    mm = O.mass(r["scores"])
+    w, Z = mm["w"], mm["Z"]
+    tg = float(tau_gpu)
+    bandg = BAND_REL * max(abs(tg), 1.0)
+    T_g = np.nonzero(s >= tg - bandg)[0]
+    strict = s > tg + bandg
+    assert w[T_g].sum() >= p * Z * (1 - MASS_TOL), "GPU set does not reach p"
+    assert w[strict].sum() < p * Z * (1 + MASS_TOL), "GPU threshold is not minimal"
+    core = np.union1d(np.nonzero(strict)[0], np.arange(min(n_sink, n)))
+    assert np.all(np.isin(core, S_gpu)), "GPU set misses keys above its threshold"
+    allowed = np.union1d(T_g, np.arange(min(n_sink, n)))
+    assert np.all(np.isin(S_gpu, allowed)), "GPU set holds keys below its threshold"
+    return "valid-alt"
+
+
+def check_out(o_gpu_bits: np.ndarray, o_ref: np.ndarray, what: str = "") -> float:
+    o = bf16_f64(o_gpu_bits)
+    err = np.abs(o - o_ref)
+    ulp_half = np.where(np.abs(o_ref) >= 4.0,
+                        np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 8), 0.0)
+    bad = err > OUT_TOL + ulp_half
+    assert not bad.any(), f"{what}: max err {err.max():.3g} at {np.argmax(err)}"
+    return float(err.max())
+
+
+def compare_decode(wl, kc, vc, idx, res, top_p: float, heads=None, batches=None,
+                   ret_only: bool = False):
+    """Oracle decode vs GPU result; returns a summary dict."""
+    G = wl.G
+    ref = O.decode(wl, kc, vc, idx, top_p, heads=heads, batches=batches)
+    kinds = {"exact": 0, "band": 0, "valid-alt": 0}
+    worst = 0.0
+    for (b, h), r in ref.items():
+        kv = h // G
+        is_ret = kv in wl.ret_kv_heads
+        if ret_only and not is_ret:
+            continue
+        if is_ret and "cnt" in res:
+            i = wl.ret_kv_heads.index(kv)
+            unit = (b * wl.n_ret + i) * G + h % G
+            S_g = gpu_set(res, unit)
+            kinds[check_set(S_g, res["tau"][unit], r, top_p, wl.n_sink)] += 1
+            # the attention step alone: oracle attention over the GPU's own set
+            qr = O.rope(bf16_f64(wl.q_pre[b, h]), wl.N - 1, wl.rope_base)
+            o_own = O.attention(qr, kc[b, kv][S_g], vc[b, kv][S_g], wl.attn_scale)
+            check_out(res["out"][b, h], o_own, f"attention over GPU set b{b} h{h}")
+        worst = max(worst, check_out(res["out"][b, h], r["out"], f"b{b} h{h}"))
+    kinds["max_err"] = worst
+    return kinds

@@ -1,0 +1,112 @@
+"""C ABI contract checks that need no GPU: the library loads, exports every symbol
+the header declares, and host-side validation returns its status before any
+launch (only invalid arguments are passed here, so nothing is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_long_retrieval_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtp.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced (validation fails first)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rtp_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.lib()
+    declared = _declared()
+    assert set(declared) >= {"rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk",
+                             "rtp_swa_attn", "rtp_workspace_size"}
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.rtp_abi_version() == 1
+    out = os.popen(f"nm -D --defined-only {R.LIB_PATH}").read()
+    exported = sorted(set(re.findall(r" T (rtp_\w+)", out)))
+    assert exported == declared, (exported, declared)
+
+
+def _layer(**kw):
+    args = dict(batch=1, n_q_heads=8, n_kv_heads=2, max_seq=1000, ret_kv_heads=[0])
+    args.update(kw)
+    return R.Layer(**args)
+
+
+def _status(fn):
+    try:
+        fn()
+    except R.RtpError as e:
+        return e.status
+    return 0
+
+
+def test_status_strings():
+    lib = R.lib()
+    for s in range(8):
+        assert lib.rtp_status_string(s)
+    assert lib.rtp_status_string(99) == b"unknown status"
+
+
+def test_workspace_query():
+    lay = _layer()
+    a = R.workspace_size(lay, R.OP_DECODE, 1000)
+    b = R.workspace_size(lay, R.OP_DECODE, 10)
+    assert a > b > 0 and a % 256 == 0
+    assert R.workspace_size(lay, R.OP_APPEND, 5) == 0
+    assert R.workspace_size(lay, R.OP_SWA, 1000) > 0
+    assert _status(lambda: R.workspace_size(lay, R.OP_DECODE, 0)) == 4
+    assert _status(lambda: R.workspace_size(lay, R.OP_DECODE, 1001)) == 4
+    assert _status(lambda: R.workspace_size(lay, 17, 10)) == 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 5), (dict(idx_rank=8), 5), (dict(batch=0), 3),
+    (dict(n_q_heads=7), 3), (dict(ret_kv_heads=[2]), 4), (dict(ret_kv_heads=[1, 0]), 4),
+    (dict(ret_kv_heads=[0, 0]), 4), (dict(n_sink=-1), 4), (dict(rope_base=0.0), 4),
+    (dict(n_q_heads=6, n_kv_heads=2), 5),  # G = 3 unsupported by the decode kernels
+])
+def test_desc_validation(kw, status):
+    lay = _layer(**kw)
+    lib = R.lib()
+    st = lib.rtp_decode_sparse_attn(lay.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, 10, 0.9, 1.0,
+                                    0.088, FAKE, None, FAKE, 1 << 30, None)
+    assert st == status, R.lib().rtp_last_error()
+
+
+def test_decode_argument_validation():
+    lay = _layer()
+    lib = R.lib()
+    call = lambda **o: lib.rtp_decode_sparse_attn(  # noqa: E731
+        lay.desc(), o.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, o.get("n", 10), o.get("p", 0.9),
+        1.0, 0.088, FAKE, None, o.get("ws", FAKE), o.get("wsb", 16), None)
+    assert call(q=None) == 1
+    assert call(q=MISALIGNED) == 2
+    assert call(n=0) == 4 and call(n=1001) == 4
+    for p in (0.0, -0.5, 1.5, float("nan")):
+        assert call(p=p) == 4
+    assert call(ws=ctypes.c_void_p(0x10010)) == 2     # workspace must be 256-byte aligned
+    assert call(wsb=16) == 6                         # workspace too small
+    assert b"workspace" in lib.rtp_last_error()
+
+
+def test_append_and_swa_validation():
+    lay = _layer()
+    lib = R.lib()
+    assert lib.rtp_index_append(lay.desc(), FAKE, FAKE, FAKE, 995, 6, FAKE, FAKE, FAKE, None) == 4
+    assert lib.rtp_index_append(lay.desc(), FAKE, FAKE, FAKE, -1, 1, FAKE, FAKE, FAKE, None) == 4
+    assert lib.rtp_index_append(lay.desc(), FAKE, FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, None) == 3
+    assert lib.rtp_index_append(lay.desc(), FAKE, FAKE, None, 0, 1, FAKE, FAKE, FAKE, None) == 1
+    assert lib.rtp_swa_attn(lay.desc(), FAKE, 999, 2, FAKE, FAKE, 0.088, FAKE, FAKE, 1 << 20,
+                            None) == 4
+    assert lib.rtp_swa_attn(_layer(window=0).desc(), FAKE, 5, 1, FAKE, FAKE, 0.088, FAKE, FAKE,
+                            1 << 20, None) == 4
+    assert lib.rtp_swa_attn(lay.desc(), FAKE, 5, 1, FAKE, FAKE, 0.088, FAKE, FAKE, 16,
+                            None) == 6

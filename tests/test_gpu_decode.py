@@ -1,0 +1,142 @@
+"""GPU parity of the decode path (append, retrieval decode, SWA) against the oracle.
+
+All cases are seeded; each runs the C ABI on cuda:0 and compares with the CPU
+oracle on the same bytes (caches and index produced by the oracle's append).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import rtp_oracle as O
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, top_p, cap=None, max_seq=None, idx_scale=1.0):
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx, max_seq=max_seq)
+    res = dev.decode(top_p, debug_cap=cap or wl.N, idx_scale=idx_scale)
+    return kc, vc, idx, res
+
+
+def test_append_matches_oracle():
+    wl = W.random_decode(21, B=2, Hq=8, Hkv=4, N=300, ret_kv=[1, 3], window=64)
+    layer = P.R.Layer(wl.B, wl.Hq, wl.Hkv, 400, wl.ret_kv_heads, 4, 64)
+    kc = torch.zeros((2, 4, 400, 128), dtype=torch.int16, device="cuda")
+    vc = torch.zeros_like(kc)
+    idx = torch.zeros((2, 2, 400, 16), dtype=torch.int16, device="cuda")
+    start = 37
+    P.R.index_append(layer, P.to_dev(wl.k_pre), P.to_dev(wl.v), P.to_dev(wl.w_k), start,
+                     kc, vc, idx)
+    # a one-token append right after (the decode-step shape)
+    one_k = wl.k_pre[:, :, :1].copy()
+    one_v = wl.v[:, :, :1].copy()
+    P.R.index_append(layer, P.to_dev(one_k), P.to_dev(one_v), P.to_dev(wl.w_k), start + 300,
+                     kc, vc, idx)
+    torch.cuda.synchronize()
+    ok, ov, oi = O.append(wl.k_pre, wl.v, wl.w_k, wl.ret_kv_heads, start)
+    gk = P.from_dev(kc)[:, :, start:start + 300]
+    gi = P.from_dev(idx)[:, :, start:start + 300]
+    assert np.array_equal(P.from_dev(vc)[:, :, start:start + 300], ov)
+    assert np.array_equal(gi, oi), "index rows must be the exact bf16 of the fp64 projection"
+    d = np.abs(gk.astype(np.int32) - ok.astype(np.int32))
+    assert d.max() <= 1 and (d != 0).mean() < 1e-4, (d.max(), (d != 0).mean())
+    k1, _, i1 = O.append(one_k, one_v, wl.w_k, wl.ret_kv_heads, start + 300)
+    assert np.array_equal(P.from_dev(idx)[:, :, start + 300:start + 301], i1)
+    d1 = np.abs(P.from_dev(kc)[:, :, start + 300:start + 301].astype(np.int32) - k1.astype(np.int32))
+    assert d1.max() <= 1
+    # rows outside the appended range stay untouched
+    assert not P.from_dev(kc)[:, :, :start].any() and not P.from_dev(kc)[:, :, start + 301:].any()
+
+
+@pytest.mark.parametrize("top_p", [0.9, 1e-6, 0.5, 0.999, 1.0])
+def test_tiny_decode(top_p):
+    wl = W.make(1)
+    kc, vc, idx, res = _run(wl, top_p)
+    summ = P.compare_decode(wl, kc, vc, idx, res, top_p)
+    print("tiny", top_p, summ)
+    if top_p == 0.9:
+        # the needles of each head are selected
+        for h in (0, 1):
+            mine = [pp for pp, o in zip(wl.meta["needles"], wl.meta["needle_owner"]) if o == h]
+            assert set(mine) <= set(P.gpu_set(res, h).tolist())
+
+
+CASES = [
+    # seed, B, Hq, Hkv, N, ret, window, needles, q_scale
+    (31, 1, 2, 1, 1, [0], 16, 0, 1.0),
+    (32, 1, 2, 2, 3, [1], 2, 0, 1.0),
+    (33, 1, 4, 1, 4, [0], 8, 0, 1.0),
+    (34, 2, 4, 2, 5, [0], 3, 0, 1.0),
+    (35, 1, 8, 1, 17, [0], 5, 1, 1.0),
+    (36, 1, 8, 2, 511, [0, 1], 100, 3, 1.0),
+    (37, 2, 16, 4, 4099, [1, 2], 300, 4, 1.0),
+    (38, 1, 8, 8, 6149, [0, 3, 7], 2048, 2, 2.0),
+    (39, 1, 32, 4, 2 * 2048 + 1, [0], 1024, 0, 3.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"s{c[0]}_N{c[4]}_G{c[2] // c[3]}" for c in CASES])
+@pytest.mark.parametrize("top_p", [1e-6, 0.5, 0.9, 0.999, 1.0])
+def test_random_shapes(case, top_p):
+    seed, B, Hq, Hkv, N, ret, window, needles, qs = case
+    wl = W.random_decode(seed, B, Hq, Hkv, N, ret, window, n_needles=needles, q_scale=qs)
+    kc, vc, idx, res = _run(wl, top_p, max_seq=N + 7)
+    summ = P.compare_decode(wl, kc, vc, idx, res, top_p)
+    print(case, top_p, summ)
+
+
+def test_all_scores_tied():
+    """q = 0 on every head: all indexer scores are 0, every key joins (ties), and
+    the output is the mean of V over all keys."""
+    wl = W.random_decode(41, 1, 4, 2, 700, [0], 64)
+    wl.q_pre[:] = 0
+    kc, vc, idx, res = _run(wl, 0.5)
+    for h in (0, 1):
+        assert len(P.gpu_set(res, h)) == wl.N
+    P.compare_decode(wl, kc, vc, idx, res, 0.5)
+
+
+def test_boundary_below_histogram_window():
+    """One key 17.5 above a flat background and p close to 1: the needle alone does
+    not reach p, so the threshold falls 17.5 below the max, beyond the 16-unit
+    histogram window; the tail of the window becomes the candidate set."""
+    wl = W.random_decode(42, 1, 8, 1, 9000, [0], 512)
+    kc, vc, idx = O.caches_for(wl)
+    rng = np.random.default_rng(7)
+    qi0 = O.query_index(wl.q_pre[0, 0], wl.w_q[0]).astype(np.float64)
+    rows = 0.01 * rng.standard_normal((wl.N, 16))
+    rows[1234] = 17.5 * qi0 / (qi0 @ qi0)
+    idx = idx.copy()
+    idx[0, 0] = O.f64_to_bf16(rows)
+    res = P.Device(wl, kc, vc, idx).decode(0.9999, debug_cap=wl.N)
+    r0 = O.decode(wl, kc, vc, idx, 0.9999, heads=[0])[(0, 0)]
+    assert r0["m"] - r0["tau"] > 16 and len(r0["T"]) > 100, (r0["m"], r0["tau"], len(r0["T"]))
+    print(P.compare_decode(wl, kc, vc, idx, res, 0.9999))
+
+
+def test_idx_scale():
+    wl = W.random_decode(43, 1, 4, 1, 3000, [0], 256, n_needles=2)
+    kc, vc, idx, res = _run(wl, 0.9, idx_scale=0.25)
+    wl.idx_scale = 0.25
+    print(P.compare_decode(wl, kc, vc, idx, res, 0.9))
+
+
+def test_deterministic_repeat():
+    wl = W.random_decode(44, 2, 8, 2, 20000, [0], 1000, n_needles=3, q_scale=1.5)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx)
+    a = dev.decode(0.9, debug_cap=wl.N)
+    b = dev.decode(0.9, debug_cap=wl.N)
+    assert np.array_equal(a["cnt"], b["cnt"]) and np.array_equal(a["tau"], b["tau"])
+    for u in range(len(a["cnt"])):
+        assert np.array_equal(P.gpu_set(a, u), P.gpu_set(b, u))
+
+
+@pytest.mark.parametrize("window,n_sink", [(1, 4), (5000, 4), (64, 0), (8, 30)])
+def test_swa_edges(window, n_sink):
+    wl = W.random_decode(45, 1, 8, 2, 1000, [0], window, n_sink=n_sink)
+    kc, vc, idx, res = _run(wl, 0.9)
+    print(P.compare_decode(wl, kc, vc, idx, res, 0.9))
