@@ -102,34 +102,47 @@ def main() -> int:
     new_v = v_pre[:, :, N - 1:N].contiguous()
     del k_pre, v_pre
     out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
-    ws = torch.empty(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
-    wss = torch.empty(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
+    wss = torch.zeros(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"caches built on the GPU ({time.time() - t0:.1f}s)")
 
     hip = Hip()
-    stream = torch.cuda.current_stream().cuda_stream
-    n_ph = 7
+    main_s = torch.cuda.current_stream()
+    side_s = torch.cuda.Stream()          # local heads run beside the retrieval chain
+    stream = main_s.cuda_stream
+    n_ph = 4
     ph_events = [hip.event() for _ in range(n_ph)]
     extra = [hip.event() for _ in range(3)]
-    dbg_ph = R.Debug(0, 0, events=ph_events, pairs=B * wl.n_ret)
+    dbg_ph = R.Debug(0, 0, events=ph_events)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
 
     def step(debug=None, mark=False):
         if mark:
             hip.record(extra[0], stream)
         R.index_append(layer, new_k, new_v, w_k, N - 1, k_cache, v_cache, index)
+        fork.record(main_s)
+        side_s.wait_event(fork)
+        if mark:
+            hip.record(extra[1], side_s.cuda_stream)
+        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss, stream=side_s)
+        if mark:
+            hip.record(extra[2], side_s.cuda_stream)
+        join.record(side_s)
         R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws,
                              debug=debug)
-        if mark:
-            hip.record(extra[1], stream)
-        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss)
-        if mark:
-            hip.record(extra[2], stream)
+        main_s.wait_event(join)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # one untimed step with the inspection outputs: union sizes for the byte count
+    dbg_sets = R.Debug(B * wl.n_ret * G, 1, pairs=B * wl.n_ret)
+    step(debug=dbg_sets)
+    torch.cuda.synchronize()
+    union = dbg_sets.union_count.cpu().numpy().astype(np.int64)
+    set_sizes = dbg_sets.sel_count.cpu().numpy().tolist()
 
     # ---- headline: K steps, Infinity Cache flushed before each, events around each step
     e0, e1 = hip.event(), hip.event()
@@ -158,7 +171,7 @@ def main() -> int:
     warm_ms = hip.elapsed_ms(e0, e1) / args.steps
 
     # ---- phases: K more cold steps with the library's phase events
-    names = ["score_hist", "threshold", "select", "resolve", "gather", "merge"]
+    names = ["score_hist", "select_attend", "finish"]
     ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
     for i in range(args.steps):
         flush.fill_(i & 0xFF)
@@ -168,9 +181,8 @@ def main() -> int:
             ph[n].append(hip.elapsed_ms(ph_events[k], ph_events[k + 1]))
         ph["append"].append(hip.elapsed_ms(extra[0], ph_events[0]))
         ph["swa"].append(hip.elapsed_ms(extra[1], extra[2]))
-        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[6]))
+        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[3]))
     phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
-    union = dbg_ph.union_count.cpu().numpy().astype(np.int64)
 
     # ---- algorithmic bytes of one step
     n_loc = wl.Hkv - wl.n_ret
@@ -208,6 +220,7 @@ def main() -> int:
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "median_us_per_step": round(float(np.median(step_ms)) * 1e3, 2),
         "wall_s_timed": round(wall, 3),
+        "set_sizes": set_sizes,
         "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
                        "small": bytes_small, "union_rows": int(union.sum())},
         "phases_us": phases_us,

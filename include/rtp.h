@@ -33,8 +33,11 @@
  *   - Token j of the cache sits at RoPE position j.  RoPE pairs dimension i with
  *     i + D/2, theta_i = rope_base^(-2i/D), angles evaluated in fp64.
  *   - Workspace: scratch device memory of at least rtp_workspace_size() bytes,
- *     256-byte aligned.  Its contents need no initialisation; calls that share
- *     one workspace must not overlap in time.
+ *     256-byte aligned.  Its first 64 KiB hold counters that the kernels reset
+ *     after use: zero-fill the workspace once before its first call (e.g. with
+ *     a fill kernel or hipMemset); every completed call leaves them at zero, so
+ *     the same workspace serves later calls of any shape.  Calls that share one
+ *     workspace must not overlap in time.
  *   - NaN/Inf inputs are outside the contract.
  */
 #ifndef RTP_H_
@@ -84,8 +87,9 @@ typedef struct {
  * KV head, the number of distinct K/V rows read (the union of the G sets).
  * phase_events, when non-NULL, are n_phase_events caller-created hipEvent_t
  * handles; the decode records event 0 before its first kernel and event k after
- * kernel k of: 1 score+histogram, 2 threshold, 3 select, 4 resolve, 5 gather,
- * 6 merge (n_phase_events must be >= 7). */
+ * kernel k of: 1 index scan + histogram + threshold, 2 select + attention of
+ * the keys above the boundary bin, 3 exact threshold + boundary keys + merge
+ * (n_phase_events must be >= 4). */
 typedef struct {
   int32_t* sel_idx;     /* [entries][sel_cap] device */
   int32_t* sel_count;   /* [entries] device */

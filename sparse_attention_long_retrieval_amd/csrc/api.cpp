@@ -65,6 +65,11 @@ rtp_status check_dev(const void* p, const char* name, size_t align = 16) {
     if (_s != RTP_OK) return _s;    \
   } while (0)
 
+// RoPE frequencies theta_i = base^(-2i/D), i < D/2, in fp64.
+void rope_theta(double base, double* theta) {
+  for (int i = 0; i < rtp::kD / 2; ++i) theta[i] = std::pow(base, -2.0 * i / rtp::kD);
+}
+
 int swa_rows(int pos, int window, int n_sink) {
   const int lo = pos - window + 1 > 0 ? pos - window + 1 : 0;
   const int ns_out = n_sink < lo ? n_sink : lo;
@@ -113,6 +118,7 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
     case RTP_OP_APPEND: *bytes = 0; return RTP_OK;
     case RTP_OP_DECODE:
       *bytes = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+      if (*bytes == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
       return RTP_OK;
     case RTP_OP_SWA: {
       if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
@@ -121,6 +127,7 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
       local_heads(desc, loc, &n_loc);
       *bytes = rtp::swa_workspace(desc->batch, n_loc, G, Tq,
                                   swa_rows(seq_len - 1, desc->window, desc->n_sink), nullptr, nullptr);
+      if (*bytes == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * local heads too large");
       return RTP_OK;
     }
     case RTP_OP_PREFILL:
@@ -157,7 +164,7 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, c
   p.max_seq = desc->max_seq;
   p.start_pos = start_pos;
   p.T = T;
-  p.rope_base = desc->rope_base;
+  rope_theta(desc->rope_base, p.theta);
   for (int h = 0; h < rtp::kMaxKv; ++h) p.ret_slot[h] = -1;
   for (int i = 0; i < desc->n_ret; ++i) p.ret_slot[desc->ret_kv_heads[i]] = i;
   hipError_t e = rtp::launch_append(p, (hipStream_t)stream);
@@ -188,9 +195,10 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
   if (!std::isfinite(idx_scale) || !std::isfinite(attn_scale))
     return fail(RTP_ERR_RANGE, "idx_scale and attn_scale must be finite");
   if (dbg && (dbg->sel_idx && dbg->sel_cap < 1)) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
-  if (dbg && dbg->phase_events && dbg->n_phase_events < 7)
-    return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 7");
+  if (dbg && dbg->phase_events && dbg->n_phase_events < 4)
+    return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 4");
   const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+  if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
   if (ws_bytes < need)
     return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::DecPlan p;
@@ -213,7 +221,7 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
   p.top_p = top_p;
   p.idx_scale = idx_scale;
   p.attn_scale = attn_scale;
-  p.rope_base = desc->rope_base;
+  rope_theta(desc->rope_base, p.theta);
   rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, &p, (char*)workspace);
   if (dbg) {
     p.dbg_idx = dbg->sel_idx;
@@ -264,6 +272,7 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
   const int rows = swa_rows(q_start, desc->window, desc->n_sink);
   const size_t need = rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, nullptr, nullptr);
+  if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * local heads too large");
   if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::SwaPlan p;
   memset(&p, 0, sizeof(p));
@@ -281,7 +290,7 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   p.n_loc = n_loc;
   for (int i = 0; i < n_loc; ++i) p.loc_kv[i] = loc[i];
   p.attn_scale = attn_scale;
-  p.rope_base = desc->rope_base;
+  rope_theta(desc->rope_base, p.theta);
   p.q_start = q_start;
   p.Tq = Tq;
   rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, &p, (char*)workspace);

@@ -6,7 +6,7 @@
 // 128->16 projection pair per retrieval head; ngjoo digest core method, pre-RoPE
 // projections).  RoPE runs in fp64 (angles and rotation) and the projection sums
 // the 128 exact bf16 products in fp64, so both rows are the round-to-nearest-even
-// bf16 of the exact value.
+// bf16 of the exact value.  theta_i = base^(-2i/D) comes from the host in fp64.
 #include "rtp_common.h"
 #include "rtp_internal.h"
 
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AppendPlan p) {
       const int pos = p.start_pos + t;
       uint16_t xb = ks[i], yb = ks[i + 64];
       double c, s;
-      rope_cs(pos, i, p.rope_base, &c, &s);
+      sincos((double)pos * p.theta[i], &s, &c);
       double x = (double)bf16_to_f32(xb), y = (double)bf16_to_f32(yb);
       uint16_t* kd = p.k_cache + (dst_head + pos) * kD;
       uint16_t* vd = p.v_cache + (dst_head + pos) * kD;

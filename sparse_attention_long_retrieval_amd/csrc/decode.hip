@@ -5,38 +5,48 @@
 // smallest highest-scoring set whose softmax mass reaches p (§4), attention
 // sinks are always kept (§2, §8), and exact 128-dim attention runs on the
 // selected rows only (§3).  The pages' decode kernel (§6) fuses scoring with a
-// 256-bucket mass histogram and merges split-KV partials; this gfx950 path keeps
-// those two ideas and adds what an exact threshold needs:
+// 256-bucket mass histogram and lets the last CTA merge split-KV partials; this
+// gfx950 path keeps both ideas, adds what an exact threshold needs, and uses
+// three dependent launches:
 //
-//   k_score_hist  pass A: stream the N x 16 bf16 index once; G fp32 scores per
-//                 token stay in registers; per block the max m_b, the exact mass
-//                 Z_b = sum exp(s - m_b) and a 32-bin mass histogram on an
-//                 absolute score grid (bins of 0.5 below the block's top key).
-//                 Masses are 2^50 fixed point, so sums are exact and order free.
-//   k_threshold   merge the block summaries of one (pair, q-head): global m, Z,
-//                 histogram; locate the boundary bin where the running mass
-//                 reaches p*Z.  If the boundary lies below the 16-unit window the
-//                 whole tail becomes the candidate set (exact, slower).
-//   k_select      pass B: recompute the same scores (bit-identical FMA order);
-//                 keys above the boundary bin are selected, keys in it become
-//                 candidates; append the union over the G q-heads.  Blocks whose
-//                 max lies below every head's boundary skip the pass.
-//   k_resolve     exact threshold inside the boundary bin: radix select by mass
-//                 over the ordered fp32 keys of the candidates (4 digits of 8 bits).
-//   k_gather      split the union list over blocks; LDS-staged K/V tiles,
-//                 online softmax per q-head (lane = row for logits, lane = dim
-//                 pair for P.V), partial state per block.
-//   k_merge       combine the partial states and round the output to bf16.
+//   k_score_hist     pass A: stream the N x 16 bf16 index once; G fp32 scores per
+//                    token stay in registers; per block the max m_b, the exact
+//                    mass Z_b = sum exp(s - m_b) (fixed point) and a 32-bin mass
+//                    histogram on an absolute score grid (bins of 0.5 below the
+//                    block's top key; each weight taken relative to its bin's
+//                    upper edge, so integer bin sums merge across blocks without
+//                    rescaling).  The last block of each group merges its group,
+//                    the last group locates the boundary bin where the running
+//                    mass reaches p*Z.  A boundary below the 16-unit window makes
+//                    the whole tail the candidate set (exact, slower).
+//   k_select_attend  pass B: recompute the same scores (bit-identical FMA order);
+//                    keys above the boundary bin (and the sinks) are attended at
+//                    once from LDS-staged K/V tiles, keys in the boundary bin are
+//                    appended as candidates; the last block of each group merges
+//                    the group's partial softmax states.
+//   k_finish         per (pair, q-head), nF blocks: exact threshold inside the
+//                    boundary bin (radix select by mass over the ordered fp32 keys
+//                    of the candidates), attention over the selected candidates
+//                    of a token range, and the last block merges everything into
+//                    the bf16 output.
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
 
 namespace rtp {
 
-constexpr int kPassThreads = 256;
-constexpr int kTokPerThread = 8;
-constexpr int kPassTokens = kPassThreads * kTokPerThread;  // TA
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <int G>
+struct PassCfg {
+  static constexpr int NT = (64 * G > 256) ? 64 * G : 256;
+  static constexpr int TPT = kPassTokens / NT;
+  static constexpr int NW = NT / 64;
+};
+
+constexpr int kMaxGroup = 256;        // blocks per merge group (and groups per pair)
+constexpr int kFinishThreads = 256;
+constexpr int kCandCap = 4096;        // candidates resolved in LDS
 
 __device__ __forceinline__ void load_index_row(const uint16_t* row, uint32_t (&w)[8]) {
   const uint4 a = *(const uint4*)row;
@@ -60,24 +70,108 @@ __device__ __forceinline__ void compute_qi(const DecPlan& p, int b, int ret_i, f
   }
 }
 
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // ------------------------------------------------------------------ pass A
 
+// Merge per-block (or per-group) summaries of one pair: max, Z, absolute-grid
+// bins.  src_m [n][G]; src_z fixed-point u64 (blocks) or double (groups);
+// src_bins [n][G][kNB] u32 (blocks) or u64 (groups).  All NT threads call it;
+// results land in LDS (m_s, kt_s, z_s, bins_s).  Every sum runs in a fixed order.
+template <int G, int NT, bool kBlockLevel>
+__device__ void merge_summaries(const float* src_m, const void* src_z, const void* src_bins,
+                                int n, float* m_s, int* kt_s, double* z_s,
+                                unsigned long long (*bins_s)[kNB], float* mm_tmp,
+                                double* zz_tmp) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n * G; e += NT) mm_tmp[e] = ld_dev(&src_m[e]);
+  __syncthreads();
+  if (tid < G) {
+    float m = -INFINITY;
+    for (int k = 0; k < n; ++k) m = fmaxf(m, mm_tmp[k * G + tid]);
+    m_s[tid] = m;
+    kt_s[tid] = score_key(m, kInvDelta);
+  }
+  __syncthreads();
+  for (int e = tid; e < n * G; e += NT) {
+    const int h = e % G;
+    double zk;
+    if (kBlockLevel)
+      zk = (double)ld_dev(&((const unsigned long long*)src_z)[e]) / kFxZ;
+    else
+      zk = ld_dev(&((const double*)src_z)[e]);
+    zz_tmp[e] = zk * exp((double)mm_tmp[e] - (double)m_s[h]);
+  }
+  for (int e = tid; e < G * kNB; e += NT) {
+    const int h = e / kNB, i = e % kNB;
+    unsigned long long acc = 0ull;
+    const int kt = kt_s[h];
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      unsigned long long v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = k0 + u;
+        v[u] = 0ull;
+        if (k < n) {
+          const int j = i - (kt - score_key(mm_tmp[k * G + h], kInvDelta));
+          if (j >= 0) {
+            const size_t off = ((size_t)k * G + h) * kNB + j;
+            v[u] = kBlockLevel ? (unsigned long long)ld_dev(&((const unsigned*)src_bins)[off])
+                               : ld_dev(&((const unsigned long long*)src_bins)[off]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    bins_s[h][i] = acc;
+  }
+  __syncthreads();
+  if (tid < G) {
+    double z = 0.0;
+    for (int k = 0; k < n; ++k) z += zz_tmp[k * G + tid];
+    z_s[tid] = z;
+  }
+  __syncthreads();
+}
+
 template <int G>
-__global__ __launch_bounds__(kPassThreads) void k_score_hist(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
+  constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+  const int tid = threadIdx.x;
   __shared__ float qi_s[G][kR];
-  __shared__ float red_m[kPassThreads / 64][G];
+  __shared__ float red_m[NW][G];
   __shared__ float mb_s[G];
-  __shared__ unsigned long long hist[G][kNB];
-  __shared__ unsigned long long zsum[G];
+  __shared__ int kt_s[G];
+  __shared__ unsigned bins[G][kNB];
+  __shared__ unsigned long long zred[NW][G];
+  __shared__ float mm_tmp[kMaxGroup * G];
+  __shared__ double zz_tmp[kMaxGroup * G];
+  __shared__ double gz_s[G];
+  __shared__ unsigned long long gbins[G][kNB];
+
+  if (blk == 0) {
+    // counters of the two later kernels start from zero on every call
+    for (int e = tid; e < p.nGrp; e += NT) p.cntB_grp[pair * p.nGrp + e] = 0u;
+    if (tid < G) {
+      p.cntF[pair * G + tid] = 0u;
+      p.cand_cnt[pair * G + tid] = 0u;
+    }
+    if (tid == 0) p.uni_cnt[pair] = 0u;
+  }
 
   const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
   const int tok0 = blk * kPassTokens;
-  uint32_t w[kTokPerThread][8];
+  uint32_t w[TPT][8];
 #pragma unroll
-  for (int k = 0; k < kTokPerThread; ++k) {
-    const int t = tok0 + k * kPassThreads + threadIdx.x;
+  for (int k = 0; k < TPT; ++k) {
+    const int t = tok0 + k * NT + tid;
     if (t < p.N) {
       load_index_row(idx + (size_t)t * kR, w[k]);
     } else {
@@ -86,13 +180,11 @@ __global__ __launch_bounds__(kPassThreads) void k_score_hist(DecPlan p) {
     }
   }
   compute_qi<G>(p, b, ret_i, qi_s);
-  for (int e = threadIdx.x; e < G * kNB; e += kPassThreads) (&hist[0][0])[e] = 0ull;
-  if (threadIdx.x < G) zsum[threadIdx.x] = 0ull;
+  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
   __syncthreads();
-  if (blk == 0 && threadIdx.x < G * kR)
-    p.qi[(size_t)pair * G * kR + threadIdx.x] = (&qi_s[0][0])[threadIdx.x];
+  if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
 
-  float s[kTokPerThread][G];
+  float s[TPT][G];
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -101,251 +193,502 @@ __global__ __launch_bounds__(kPassThreads) void k_score_hist(DecPlan p) {
     for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
     mloc[h] = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) {
-      const int t = tok0 + k * kPassThreads + threadIdx.x;
+    for (int k = 0; k < TPT; ++k) {
+      const int t = tok0 + k * NT + tid;
       s[k][h] = (t < p.N) ? idx_score(w[k], q) : -INFINITY;
       mloc[h] = fmaxf(mloc[h], s[k][h]);
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float v = wave_max(mloc[h]);
     if (lane == 0) red_m[wave][h] = v;
   }
   __syncthreads();
-  if (threadIdx.x < G) {
-    float v = red_m[0][threadIdx.x];
-    for (int q = 1; q < kPassThreads / 64; ++q) v = fmaxf(v, red_m[q][threadIdx.x]);
-    mb_s[threadIdx.x] = v;
+  if (tid < G) {
+    float v = red_m[0][tid];
+    for (int q = 1; q < NW; ++q) v = fmaxf(v, red_m[q][tid]);
+    mb_s[tid] = v;
+    kt_s[tid] = score_key(v, kInvDelta);
   }
   __syncthreads();
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float mb = mb_s[h];
-    const int kt = score_key(mb, kInvDelta);
-    unsigned long long zacc = 0ull;
+    const int kt = kt_s[h];
+    float z = 0.f;
 #pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) {
+    for (int k = 0; k < TPT; ++k) {
       const float sv = s[k][h];
-      const float wt = exp2f((sv - mb) * kLog2e);
-      const unsigned long long fx = __float2ull_rz(wt * 0x1p50f);
-      zacc += fx;
-      const int j = kt - score_key(sv, kInvDelta);
-      if (j < kNB && sv > -INFINITY) atomicAdd(&hist[h][j], fx);
+      if (sv > -INFINITY) {
+        z += exp2f((sv - mb) * kLog2e);
+        const int key = score_key(sv, kInvDelta);
+        const int j = kt - key;
+        if (j < kNB) {
+          const float edge = (float)(key + 1) * kDelta;
+          const float wb = exp2f((sv - edge) * kLog2e);
+          atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
+        }
+      }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) zacc += __shfl_xor(zacc, o, 64);
-    if (lane == 0) atomicAdd(&zsum[h], zacc);
+    const unsigned long long zfx = wave_sum_u64((unsigned long long)((double)z * kFxZ));
+    if (lane == 0) zred[wave][h] = zfx;
   }
   __syncthreads();
   const size_t so = ((size_t)pair * p.nA + blk) * G;
-  if (threadIdx.x < G) {
-    p.blk_m[so + threadIdx.x] = mb_s[threadIdx.x];
-    p.blk_z[so + threadIdx.x] = zsum[threadIdx.x];
+  if (tid < G) {
+    unsigned long long zb = 0ull;
+    for (int q = 0; q < NW; ++q) zb += zred[q][tid];
+    st_dev(&p.blk_m[so + tid], mb_s[tid]);
+    st_dev(&p.blk_z[so + tid], zb);
   }
-  for (int e = threadIdx.x; e < G * kNB; e += kPassThreads) p.blk_hist[so * kNB + e] = (&hist[0][0])[e];
-}
+  for (int e = tid; e < G * kNB; e += NT) st_dev(&p.blk_bins[so * kNB + e], (&bins[0][0])[e]);
 
-// ------------------------------------------------------------------ threshold
-
-template <int G>
-__global__ __launch_bounds__(256) void k_threshold(DecPlan p) {
-  const int unit = blockIdx.x;
-  const int pair = unit / G, h = unit % G;
-  __shared__ float red[4];
-  __shared__ unsigned long long H[kNB];
-  __shared__ unsigned long long Zs;
-  float ml = -INFINITY;
-  for (int k = threadIdx.x; k < p.nA; k += 256) ml = fmaxf(ml, p.blk_m[((size_t)pair * p.nA + k) * G + h]);
-  ml = wave_max(ml);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ml;
-  if (threadIdx.x < kNB) H[threadIdx.x] = 0ull;
-  if (threadIdx.x == 0) Zs = 0ull;
-  __syncthreads();
-  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const int kt = score_key(m, kInvDelta);
-  for (int k = threadIdx.x; k < p.nA; k += 256) {
-    const size_t so = ((size_t)pair * p.nA + k) * G + h;
-    const float mb = p.blk_m[so];
-    // block masses are relative to m_b at 2^50; rescale to m at 2^36
-    const double scale = exp((double)mb - (double)m) * (kFxGlobal / kFxBlock);
-    atomicAdd(&Zs, (unsigned long long)((double)p.blk_z[so] * scale));
-    const int shift = kt - score_key(mb, kInvDelta);
-    const unsigned long long* hb = p.blk_hist + so * kNB;
-    for (int j = 0; j + shift < kNB; ++j) {
-      const unsigned long long v = hb[j];
-      if (v) atomicAdd(&H[j + shift], (unsigned long long)((double)v * scale));
+  // ---- group merge by the last block of the group
+  const int grp = blk / p.gsz;
+  const int b0 = grp * p.gsz;
+  const int nin = min(p.gsz, p.nA - b0);
+  if (!arrive_last(&p.cntA_grp[pair * p.nGrp + grp], (unsigned)nin)) return;
+  {
+    const size_t sb = ((size_t)pair * p.nA + b0) * G;
+    merge_summaries<G, NT, true>(p.blk_m + sb, p.blk_z + sb, p.blk_bins + sb * kNB, nin, mb_s,
+                                 kt_s, gz_s, gbins, mm_tmp, zz_tmp);
+    const size_t go = ((size_t)pair * p.nGrp + grp) * G;
+    if (tid < G) {
+      st_dev(&p.grp_m[go + tid], mb_s[tid]);
+      st_dev(&p.grp_z[go + tid], gz_s[tid]);
     }
+    for (int e = tid; e < G * kNB; e += NT) st_dev(&p.grp_bins[go * kNB + e], (&gbins[0][0])[e]);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    ThrInfo t;
-    t.key_top = kt;
-    t.m = m;
-    t.Z = (double)Zs / kFxGlobal;
-    t.tau = -INFINITY;
-    t.n_cand = 0;
-    if (p.top_p >= 1.0f) {
-      t.mode = 2;
-      t.key_bnd = INT_MIN;
-      t.above = t.Z;
-      t.need = 0.0;
-    } else {
-      const double target = (double)p.top_p * (double)Zs;
-      unsigned long long cum = 0ull;
-      int g = 0;
-      for (; g < kNB; ++g) {
-        if ((double)(cum + H[g]) >= target) break;
-        cum += H[g];
-      }
-      if (g < kNB) {
-        t.mode = 0;
-        t.key_bnd = kt - g;
+  // ---- final merge by the last group of the pair
+  if (!arrive_last(&p.cntA_top[pair], (unsigned)p.nGrp)) return;
+  {
+    const size_t go = (size_t)pair * p.nGrp * G;
+    merge_summaries<G, NT, false>(p.grp_m + go, p.grp_z + go, p.grp_bins + go * kNB, p.nGrp,
+                                  mb_s, kt_s, gz_s, gbins, mm_tmp, zz_tmp);
+    // bin masses relative to the global max, in parallel (zz_tmp reused)
+    for (int e = tid; e < G * kNB; e += NT) {
+      const int h = e / kNB, g = e % kNB;
+      zz_tmp[e] = (double)gbins[h][g] / (double)kFxBin *
+                  exp((double)(kt_s[h] - g + 1) * (double)kDelta - (double)mb_s[h]);
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int h = tid;
+      ThrInfo t;
+      t.key_top = kt_s[h];
+      t.m = mb_s[h];
+      t.Z = gz_s[h];
+      t.tau = -INFINITY;
+      t.n_cand = 0;
+      if (p.top_p >= 1.0f) {
+        t.mode = 2;
+        t.key_bnd = INT_MIN;
+        t.above = t.Z;
+        t.need = 0.0;
       } else {
-        t.mode = 1;
-        t.key_bnd = kt - kNB;
+        const double target = (double)p.top_p * t.Z;
+        double cum = 0.0;
+        int g = 0;
+        for (; g < kNB; ++g) {
+          const double mass = zz_tmp[h * kNB + g];
+          if (cum + mass >= target) break;
+          cum += mass;
+        }
+        t.mode = g < kNB ? 0 : 1;
+        t.key_bnd = g < kNB ? t.key_top - g : t.key_top - kNB;
+        t.above = cum;
+        t.need = target - cum;
       }
-      t.above = (double)cum / kFxGlobal;
-      t.need = (target - (double)cum) / kFxGlobal;
+      p.thr[pair * G + h] = t;
     }
-    p.thr[unit] = t;
-    p.cand_cnt[unit] = 0u;
-    if (h == 0) p.uni_cnt[pair] = 0u;
   }
 }
 
 // ------------------------------------------------------------------ pass B
 
 template <int G>
-__global__ __launch_bounds__(kPassThreads) void k_select(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
+  constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+  const int kv = p.ret_kv[ret_i];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ TileSmem<G> sm;
   __shared__ float qi_s[G][kR];
   __shared__ int kb_s[G], mode_s[G];
   __shared__ int relevant;
-  if (threadIdx.x == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
+  __shared__ unsigned ccount[G], cbase[G];
+  __shared__ unsigned list[kPassTokens];
+  __shared__ unsigned wsum[NW];
+  __shared__ unsigned n_list_s, ubase_s;
+
+  if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
+  if (tid < G) ccount[tid] = 0u;
   __syncthreads();
-  if (threadIdx.x < G) {
-    const ThrInfo t = p.thr[pair * G + threadIdx.x];
-    kb_s[threadIdx.x] = t.key_bnd;
-    mode_s[threadIdx.x] = t.mode;
-    const float mb = p.blk_m[((size_t)pair * p.nA + blk) * G + threadIdx.x];
+  if (tid < G) {
+    const ThrInfo t = p.thr[pair * G + tid];
+    kb_s[tid] = t.key_bnd;
+    mode_s[tid] = t.mode;
+    const float mb = p.blk_m[((size_t)pair * p.nA + blk) * G + tid];
     if (t.mode != 0 || score_key(mb, kInvDelta) >= t.key_bnd) atomicOr(&relevant, 1);
   }
-  if (threadIdx.x < G * kR) (&qi_s[0][0])[threadIdx.x] = p.qi[(size_t)pair * G * kR + threadIdx.x];
+  if (tid < G * kR) (&qi_s[0][0])[tid] = p.qi[(size_t)pair * G * kR + tid];
   __syncthreads();
-  if (!relevant) return;
 
-  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
-  const int tok0 = blk * kPassTokens;
-  const int lane = threadIdx.x & 63;
-  float2* cand = p.cand + (size_t)pair * G * p.N;
-  int2* uni = p.uni + (size_t)pair * p.N;
-  const unsigned long long lanemask_lt = (1ull << lane) - 1ull;
-  for (int k = 0; k < kTokPerThread; ++k) {
-    const int t = tok0 + k * kPassThreads + threadIdx.x;
-    const bool in = t < p.N;
-    uint32_t w[8];
-    if (in) load_index_row(idx + (size_t)t * kR, w);
-    uint32_t dm = 0u, cm = 0u;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  if (relevant) {
+    const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+    load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.theta,
+                   p.attn_scale * kLog2e);
+    const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+    const int tok0 = blk * kPassTokens;
+    uint32_t w[TPT][8];
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int t = tok0 + k * NT + tid;
+      if (t < p.N) {
+        load_index_row(idx + (size_t)t * kR, w[k]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[k][c] = 0u;
+      }
+    }
+    float s[TPT][G];
+    uint32_t dm[TPT], cm[TPT];
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) dm[k] = cm[k] = 0u;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float q[kR];
 #pragma unroll
       for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
-      float sv = 0.f;
-      bool is_c = false;
-      if (in) {
-        sv = idx_score(w, q);
-        const int key = score_key(sv, kInvDelta);
-        const int mode = mode_s[h], kb = kb_s[h];
-        if (mode == 2 || key > kb) dm |= 1u << h;
-        else if ((mode == 0 && key == kb) || (mode == 1 && key <= kb)) is_c = true;
-      }
-      const unsigned long long bal = __ballot(is_c);
-      if (bal) {
-        unsigned base = 0;
-        const int leader = __ffsll((long long)bal) - 1;
-        if (lane == leader) base = atomicAdd(&p.cand_cnt[pair * G + h], (unsigned)__popcll(bal));
-        base = __shfl(base, leader, 64);
-        if (is_c) {
-          cand[(size_t)h * p.N + base + __popcll(bal & lanemask_lt)] = make_float2(sv, __int_as_float(t));
-          cm |= 1u << h;
+      const int mode = mode_s[h], kb = kb_s[h];
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int t = tok0 + k * NT + tid;
+        if (t < p.N) {
+          const float sv = idx_score(w[k], q);
+          s[k][h] = sv;
+          const int key = score_key(sv, kInvDelta);
+          if (mode == 2 || key > kb) dm[k] |= 1u << h;
+          else if ((mode == 0 && key == kb) || (mode == 1 && key <= kb)) cm[k] |= 1u << h;
+        } else {
+          s[k][h] = -INFINITY;
         }
       }
     }
-    if (in && t < p.n_sink) dm = (1u << G) - 1u;
-    const bool member = (dm | cm) != 0u;
-    const unsigned long long bal = __ballot(member);
-    if (bal) {
-      unsigned base = 0;
-      const int leader = __ffsll((long long)bal) - 1;
-      if (lane == leader) base = atomicAdd(&p.uni_cnt[pair], (unsigned)__popcll(bal));
-      base = __shfl(base, leader, 64);
-      if (member) uni[base + __popcll(bal & lanemask_lt)] = make_int2(t, (int)(dm | (cm << 8)));
+    // candidates: block-local offsets in LDS, one global atomic per head
+    unsigned coff[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      unsigned c = 0u;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) c += (cm[k] >> h) & 1u;
+      coff[h] = c ? atomicAdd(&ccount[h], c) : 0u;
     }
+    __syncthreads();
+    if (tid < G && ccount[tid]) cbase[tid] = atomicAdd(&p.cand_cnt[pair * G + tid], ccount[tid]);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float2* cd = p.cand + ((size_t)pair * G + h) * p.N + cbase[h] + coff[h];
+      unsigned c = 0u;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        if ((cm[k] >> h) & 1u) {
+          cd[c++] = make_float2(s[k][h], __int_as_float(tok0 + k * NT + tid));
+        }
+      }
+    }
+    // definite rows (sinks join every head): ordered compaction into LDS
+    unsigned cnt = 0u;
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int t = tok0 + k * NT + tid;
+      if (t < p.N && t < p.n_sink) dm[k] = (1u << G) - 1u;
+      cnt += dm[k] ? 1u : 0u;
+    }
+    unsigned incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    unsigned off = incl - cnt;
+    for (int q = 0; q < wave; ++q) off += wsum[q];
+    if (tid == NT - 1) n_list_s = off + cnt;
+#pragma unroll
+    for (int k = 0; k < TPT; ++k)
+      if (dm[k]) list[off++] = ((unsigned)(k * NT + tid) << 8) | dm[k];
+    if (p.dbg_cnt || p.dbg_idx || p.dbg_union) {
+      // inspection only: the union of definite and candidate keys of this block
+      unsigned uc = 0u;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) uc += (dm[k] | cm[k]) ? 1u : 0u;
+      __syncthreads();
+      if (tid == 0) ccount[0] = 0u;
+      __syncthreads();
+      const unsigned uo = uc ? atomicAdd(&ccount[0], uc) : 0u;
+      __syncthreads();
+      if (tid == 0) ubase_s = ccount[0] ? atomicAdd(&p.uni_cnt[pair], ccount[0]) : 0u;
+      __syncthreads();
+      unsigned u = ubase_s + uo;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k)
+        if (dm[k] | cm[k])
+          p.uni[(size_t)pair * p.N + u++] =
+              make_int2(tok0 + k * NT + tid, (int)(dm[k] | (cm[k] << 8)));
+    }
+    __syncthreads();
+    const int n_list = (int)n_list_s;
+    for (int t0 = 0; t0 < n_list; t0 += kTileRows) {
+      const int nr = min(kTileRows, n_list - t0);
+      if (tid < nr) {
+        const unsigned e = list[t0 + tid];
+        sm.rows[tid] = tok0 + (int)(e >> 8);
+        sm.masks[tid] = e & 0xffu;
+      }
+      __syncthreads();
+      tile_attend<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+    }
+  }
+  const int unit0 = pair * G;
+  if (wave < G)
+    store_partial(p.partB + ((size_t)(unit0 + wave) * p.nA + blk) * kPartStride, m, l, o0, o1);
+
+  // ---- group merge of the partial states by the last block of the group
+  const int grp = blk / p.gsz;
+  const int b0 = grp * p.gsz;
+  const int nin = min(p.gsz, p.nA - b0);
+  if (!arrive_last(&p.cntB_grp[pair * p.nGrp + grp], (unsigned)nin)) return;
+  if (wave < G) {
+    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
+    merge_partials_wave(p.partB + ((size_t)(unit0 + wave) * p.nA + b0) * kPartStride, nin, gm, gl,
+                        g0, g1);
+    store_partial(p.partBg + ((size_t)(unit0 + wave) * p.nGrp + grp) * kPartStride, gm, gl, g0,
+                  g1);
   }
 }
 
-// ------------------------------------------------------------------ resolve
+// ------------------------------------------------------------------ finish
 
-__global__ __launch_bounds__(256) void k_resolve(DecPlan p) {
-  const int unit = blockIdx.x;
-  const int pair = unit / p.G;
-  __shared__ unsigned long long dig[256];
-  __shared__ uint32_t prefix_s, mask_s;
-  __shared__ unsigned long long acc_s;
-  ThrInfo t = p.thr[unit];
-  if (t.mode == 2) return;
-  const unsigned C = p.cand_cnt[unit];
-  const float2* cand = p.cand + ((size_t)pair * p.G + (unit % p.G)) * p.N;
-  const double need_fx = t.need * kFxGlobal;
-  if (threadIdx.x == 0) {
-    prefix_s = 0u;
-    mask_s = 0u;
-    acc_s = 0ull;
+// Radix select by mass over candidate scores: the largest threshold tau whose
+// candidates at or above it carry at least need (2^36 fixed point, relative to
+// the global max).  Four 8-bit digits of the ordered fp32 key, high to low; wave
+// 0 scans the 256 digit sums from the top with a prefix sum.  If rounding puts
+// need above the total, every candidate is kept (tau = lowest score).
+template <int NT>
+__device__ float radix_select_tau(unsigned C, bool in_lds, const float* cs,
+                                  const unsigned long long* cw, const float2* cand, float m,
+                                  double need_fx, unsigned long long* dig, uint32_t* prefix_s,
+                                  uint32_t* pmask_s, unsigned long long* acc_s) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid == 0) {
+    *prefix_s = 0u;
+    *pmask_s = 0u;
+    *acc_s = 0ull;
   }
   for (int shift = 24; shift >= 0; shift -= 8) {
-    dig[threadIdx.x] = 0ull;
+    for (int e = tid; e < 256; e += NT) dig[e] = 0ull;
     __syncthreads();
-    const uint32_t prefix = prefix_s, pmask = mask_s;
-    for (unsigned c = threadIdx.x; c < C; c += 256) {
-      const float sv = cand[c].x;
-      const uint32_t key = f32_ord(sv);
-      if ((key & pmask) == prefix) {
-        const double wt = exp((double)sv - (double)t.m) * kFxGlobal;
-        atomicAdd(&dig[(key >> shift) & 255u], (unsigned long long)wt);
+    const uint32_t prefix = *prefix_s, pmask = *pmask_s;
+    for (unsigned c = tid; c < C; c += NT) {
+      float sv;
+      unsigned long long wv;
+      if (in_lds) {
+        sv = cs[c];
+        wv = cw[c];
+      } else {
+        sv = cand[c].x;
+        wv = (unsigned long long)(exp((double)sv - (double)m) * kFxCand);
       }
+      const uint32_t key = f32_ord(sv);
+      if ((key & pmask) == prefix) atomicAdd(&dig[(key >> shift) & 255u], wv);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned long long acc = acc_s;
-      int d = 255, lowest = -1;
-      for (; d >= 0; --d) {
-        if (dig[d] == 0ull) continue;
-        lowest = d;
-        if ((double)(acc + dig[d]) >= need_fx) break;
-        acc += dig[d];
+    if (wave == 0) {
+      unsigned long long d4[4], sum = 0ull;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        d4[j] = dig[255 - 4 * lane - j];
+        sum += d4[j];
       }
-      if (d < 0) {  // rounding left the target above every candidate: keep them all
-        d = lowest < 0 ? 0 : lowest;
-        acc -= (lowest < 0) ? 0ull : dig[d];
+      unsigned long long incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
       }
-      acc_s = acc;
-      prefix_s = prefix | ((uint32_t)d << shift);
-      mask_s = pmask | (255u << shift);
+      const unsigned long long acc0 = *acc_s;
+      const unsigned long long hit = __ballot((double)(acc0 + incl) >= need_fx);
+      int digit = 0;
+      unsigned long long acc_new = acc0;
+      if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        if (lane == L) {
+          unsigned long long run = acc0 + incl - sum;
+          for (int j = 0; j < 4; ++j) {
+            if ((double)(run + d4[j]) >= need_fx) {
+              digit = 255 - 4 * lane - j;
+              break;
+            }
+            run += d4[j];
+          }
+          acc_new = run;
+        }
+        digit = __shfl(digit, L, 64);
+        acc_new = __shfl(acc_new, L, 64);
+      } else {
+        const unsigned long long nz = __ballot(sum != 0ull);
+        if (nz) {
+          const int L = 63 - __clzll((long long)nz);
+          if (lane == L) {
+            unsigned long long run = acc0 + incl - sum;
+            for (int j = 0; j < 4; ++j) {
+              if (d4[j]) {
+                digit = 255 - 4 * lane - j;
+                acc_new = run;
+              }
+              run += d4[j];
+            }
+          }
+          digit = __shfl(digit, L, 64);
+          acc_new = __shfl(acc_new, L, 64);
+        }
+      }
+      if (lane == 0) {
+        *acc_s = acc_new;
+        *prefix_s = prefix | ((uint32_t)digit << shift);
+        *pmask_s = pmask | (255u << shift);
+      }
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    p.thr[unit].tau = C ? ord_f32(prefix_s) : INFINITY;
+  return ord_f32(*prefix_s);
+}
+
+template <int G>
+__global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
+  constexpr int NT = kFinishThreads;
+  const int unit = blockIdx.y, f = blockIdx.x;
+  const int pair = unit / G, h = unit % G;
+  const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+  const int kv = p.ret_kv[ret_i], qh = kv * G + h;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  __shared__ TileSmem<1> sm;
+  __shared__ float cs[kCandCap];
+  __shared__ int ct[kCandCap];
+  __shared__ unsigned long long cw[kCandCap];
+  __shared__ unsigned long long dig[256];
+  __shared__ uint32_t prefix_s, pmask_s;
+  __shared__ unsigned long long acc_s;
+  __shared__ int sel_n, chunk_n;
+  __shared__ int sel[kCandCap];
+
+  const ThrInfo t = p.thr[unit];
+  const unsigned C = (t.mode == 2) ? 0u : p.cand_cnt[unit];
+  const float2* cand = p.cand + (size_t)unit * p.N;
+  const bool in_lds = C <= (unsigned)kCandCap;
+  if (tid == 0) sel_n = 0;
+  if (in_lds) {
+    for (unsigned c = tid; c < C; c += NT) {
+      const float2 e = cand[c];
+      cs[c] = e.x;
+      ct[c] = __float_as_int(e.y);
+      cw[c] = (unsigned long long)(exp((double)e.x - (double)t.m) * kFxCand);
+    }
+  }
+  load_q_rope<1>(sm, p.q_pre + ((size_t)b * p.Hq + qh) * kD, 0, p.N - 1, p.theta,
+                 p.attn_scale * kLog2e);
+  __syncthreads();
+  float tau = -INFINITY;
+  if (t.mode != 2) {
+    tau = C ? radix_select_tau<NT>(C, in_lds, cs, cw, cand, t.m, t.need * kFxCand, dig, &prefix_s,
+                                   &pmask_s, &acc_s)
+            : INFINITY;
+  }
+  if (f == 0 && tid == 0) {
+    p.thr[unit].tau = tau;
     p.thr[unit].n_cand = (int)C;
+  }
+
+  // selected candidates of this block's token range, attended in token order
+  const int lo = (int)(((long long)p.N * f) / p.nF);
+  const int hi = (int)(((long long)p.N * (f + 1)) / p.nF);
+  const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  if (in_lds) {
+    for (unsigned c = tid; c < C; c += NT) {
+      const int tok = ct[c];
+      // sinks were attended in pass B already
+      if (cs[c] >= tau && tok >= lo && tok < hi && tok >= p.n_sink) sel[atomicAdd(&sel_n, 1)] = tok;
+    }
+    __syncthreads();
+    const int n_sel = sel_n;
+    int pw = 1;
+    while (pw < n_sel) pw <<= 1;
+    for (int e = n_sel + tid; e < pw; e += NT) sel[e] = INT_MAX;
+    __syncthreads();
+    for (int k = 2; k <= pw; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int e = tid; e < pw; e += NT) {
+          const int x = e ^ j;
+          if (x > e) {
+            const int a = sel[e], c2 = sel[x];
+            if ((a > c2) == ((e & k) == 0)) {
+              sel[e] = c2;
+              sel[x] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int t0 = 0; t0 < n_sel; t0 += kTileRows) {
+      const int nr = min(kTileRows, n_sel - t0);
+      if (tid < nr) {
+        sm.rows[tid] = sel[t0 + tid];
+        sm.masks[tid] = 1u;
+      }
+      __syncthreads();
+      tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+    }
+  } else {
+    // more candidates than LDS holds: walk the list in chunks of 64 (list order)
+    for (unsigned c0 = 0; c0 < C; c0 += kTileRows) {
+      if (tid == 0) chunk_n = 0;
+      __syncthreads();
+      if (tid < kTileRows && c0 + tid < C) {
+        const float2 e = cand[c0 + tid];
+        const int tok = __float_as_int(e.y);
+        if (e.x >= tau && tok >= lo && tok < hi && tok >= p.n_sink) {
+          const int slot = atomicAdd(&chunk_n, 1);
+          sm.rows[slot] = tok;
+          sm.masks[slot] = 1u;
+        }
+      }
+      __syncthreads();
+      const int nr = chunk_n;
+      if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+      __syncthreads();
+    }
+  }
+  if (wave == 0) store_partial(p.partF + ((size_t)unit * p.nF + f) * kPartStride, m, l, o0, o1);
+  if (!arrive_last(&p.cntF[unit], (unsigned)p.nF)) return;
+  if (wave == 0) {
+    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
+    merge_partials_wave(p.partF + (size_t)unit * p.nF * kPartStride, p.nF, gm, gl, g0, g1);
+    merge_partials_wave(p.partBg + (size_t)unit * p.nGrp * kPartStride, p.nGrp, gm, gl, g0, g1);
+    store_output(p.out + ((size_t)b * p.Hq + qh) * kD, gl, g0, g1);
   }
 }
 
-// ------------------------------------------------------------------ membership
+// ------------------------------------------------------------------ debug sets
 
 // Head mask of a union entry: definite heads, sinks, and candidates whose score
 // reaches the resolved threshold (the score is recomputed bit-identically).
@@ -369,80 +712,6 @@ __device__ __forceinline__ uint32_t entry_mask(const int2 e, const uint16_t* idx
   }
   return dm;
 }
-
-// ------------------------------------------------------------------ gather
-
-template <int G>
-__global__ __launch_bounds__(64 * G) void k_gather(DecPlan p) {
-  const int pair = blockIdx.y, blk = blockIdx.x;
-  const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
-  const int kv = p.ret_kv[ret_i];
-  __shared__ TileSmem<G> sm;
-  __shared__ float qi_s[G][kR];
-  __shared__ float tau_s[G];
-  const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-  const uint16_t* kbase = p.k_cache + head_base;
-  const uint16_t* vbase = p.v_cache + head_base;
-  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
-  load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.rope_base,
-                 p.attn_scale * kLog2e);
-  if (threadIdx.x < G * kR) (&qi_s[0][0])[threadIdx.x] = p.qi[(size_t)pair * G * kR + threadIdx.x];
-  if (threadIdx.x < G) tau_s[threadIdx.x] = p.thr[pair * G + threadIdx.x].tau;
-  const unsigned M = p.uni_cnt[pair];
-  const unsigned lo = (unsigned)(((unsigned long long)M * blk) / p.nGat);
-  const unsigned hi = (unsigned)(((unsigned long long)M * (blk + 1)) / p.nGat);
-  const int2* uni = p.uni + (size_t)pair * p.N;
-  __syncthreads();
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (unsigned t0 = lo; t0 < hi; t0 += kTileRows) {
-    const int nr = (int)min((unsigned)kTileRows, hi - t0);
-    if ((int)threadIdx.x < nr) {
-      const int2 e = uni[t0 + threadIdx.x];
-      sm.rows[threadIdx.x] = e.x;
-      sm.masks[threadIdx.x] = entry_mask<G>(e, idx, qi_s, tau_s);
-    }
-    __syncthreads();
-    tile_attend<G>(sm, kbase, vbase, nr, m, l, o0, o1);
-  }
-  const int h = threadIdx.x >> 6;
-  store_partial(p.part + ((size_t)(pair * G + h) * p.nGat + blk) * kPartStride, m, l, o0, o1);
-}
-
-// ------------------------------------------------------------------ merge
-
-struct MergeMap {
-  uint16_t* out;
-  int B, Hq, G, n_sub, Tq;
-  int kv[kMaxKv];
-};
-
-// unit = ((b * n_sub + i) * G + g) * Tq + t  ->  out[b][kv[i]*G + g][t][:]
-__global__ __launch_bounds__(128) void k_merge(const float* part, int n_part, MergeMap mp) {
-  const int unit = blockIdx.x;
-  const int t = unit % mp.Tq;
-  const int g = (unit / mp.Tq) % mp.G;
-  const int bi = unit / (mp.Tq * mp.G);
-  const int b = bi / mp.n_sub, i = bi % mp.n_sub;
-  const int qh = mp.kv[i] * mp.G + g;
-  const float* pp = part + (size_t)unit * n_part * kPartStride;
-  float M = -INFINITY;
-  for (int k = 0; k < n_part; ++k) M = fmaxf(M, pp[(size_t)k * kPartStride]);
-  float L = 0.f, O = 0.f;
-  if (M > -INFINITY) {
-    for (int k = 0; k < n_part; ++k) {
-      const float* q = pp + (size_t)k * kPartStride;
-      const float mk = q[0];
-      if (mk == -INFINITY) continue;
-      const float sc = exp2f(mk - M);
-      L = fmaf(q[1], sc, L);
-      O = fmaf(q[4 + threadIdx.x], sc, O);
-    }
-  }
-  const float r = (L > 0.f) ? O / L : 0.f;
-  mp.out[(((size_t)b * mp.Hq + qh) * mp.Tq + t) * kD + threadIdx.x] = f32_to_bf16(r);
-}
-
-// ------------------------------------------------------------------ debug sets
 
 template <int G>
 __global__ __launch_bounds__(256) void k_debug_sets(DecPlan p) {
@@ -479,30 +748,16 @@ __global__ __launch_bounds__(256) void k_debug_sets(DecPlan p) {
 template <int G>
 static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   auto mark = [&](int k) {
-    if (p.events) hipEventRecord(p.events[k], s);
+    if (p.events) (void)hipEventRecord(p.events[k], s);
   };
   mark(0);
-  hipLaunchKernelGGL(k_score_hist<G>, dim3(p.nA, p.P), dim3(kPassThreads), 0, s, p);
+  hipLaunchKernelGGL(k_score_hist<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
   mark(1);
-  hipLaunchKernelGGL(k_threshold<G>, dim3(p.P * G), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_select_attend<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
   mark(2);
-  hipLaunchKernelGGL(k_select<G>, dim3(p.nA, p.P), dim3(kPassThreads), 0, s, p);
+  hipLaunchKernelGGL(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), 0, s, p);
   mark(3);
-  hipLaunchKernelGGL(k_resolve, dim3(p.P * G), dim3(256), 0, s, p);
-  mark(4);
-  hipLaunchKernelGGL(k_gather<G>, dim3(p.nGat, p.P), dim3(64 * G), 0, s, p);
-  mark(5);
-  MergeMap mp;
-  mp.out = p.out;
-  mp.B = p.B;
-  mp.Hq = p.Hq;
-  mp.G = G;
-  mp.n_sub = p.n_ret;
-  mp.Tq = 1;
-  for (int i = 0; i < p.n_ret; ++i) mp.kv[i] = p.ret_kv[i];
-  hipLaunchKernelGGL(k_merge, dim3(p.P * G), dim3(128), 0, s, (const float*)p.part, p.nGat, mp);
-  mark(6);
-  if (p.dbg_idx || p.dbg_cnt || p.dbg_tau || p.dbg_union)
+  if (p.dbg_cnt || p.dbg_idx || p.dbg_tau || p.dbg_union)
     hipLaunchKernelGGL(k_debug_sets<G>, dim3(p.P * G), dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -522,39 +777,61 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base) {
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
-  int nGat = N / 4096;
-  nGat = nGat < 1 ? 1 : (nGat > 64 ? 64 : nGat);
-  size_t off = 0;
+  int gsz = 8;
+  while (gsz * gsz < nA) ++gsz;
+  if (gsz > kMaxGroup) gsz = kMaxGroup;
+  const int nGrp = (nA + gsz - 1) / gsz;
+  if (nGrp > kMaxGroup) return 0;
+  const int nF = 8;
+  if ((size_t)P * (nGrp + 1) * sizeof(unsigned) > kCounterBytes) return 0;
+  size_t off = kCounterBytes;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += align256(bytes);
     return base ? base + o : nullptr;
   };
+  char* cB = take((size_t)P * nGrp * 4);
+  char* cF = take((size_t)P * G * 4);
+  char* cc = take((size_t)P * G * 4);
+  char* uc = take((size_t)P * 4);
   char* qi = take((size_t)P * G * kR * 4);
   char* bm = take((size_t)P * nA * G * 4);
   char* bz = take((size_t)P * nA * G * 8);
-  char* bh = take((size_t)P * nA * G * kNB * 8);
+  char* bb = take((size_t)P * nA * G * kNB * 4);
+  char* gm = take((size_t)P * nGrp * G * 4);
+  char* gz = take((size_t)P * nGrp * G * 8);
+  char* gb = take((size_t)P * nGrp * G * kNB * 8);
   char* th = take((size_t)P * G * sizeof(ThrInfo));
-  char* cc = take((size_t)P * G * 4);
   char* ca = take((size_t)P * G * N * 8);
-  char* uc = take((size_t)P * 4);
   char* un = take((size_t)P * N * 8);
-  char* pa = take((size_t)P * G * nGat * kPartStride * 4);
+  char* pB = take((size_t)P * G * nA * kPartStride * 4);
+  char* pG = take((size_t)P * G * nGrp * kPartStride * 4);
+  char* pF = take((size_t)P * G * nF * kPartStride * 4);
   if (plan) {
     plan->P = P;
-    plan->TA = kPassTokens;
     plan->nA = nA;
-    plan->nGat = nGat;
+    plan->gsz = gsz;
+    plan->nGrp = nGrp;
+    plan->nF = nF;
+    plan->cntA_grp = (unsigned*)base;
+    plan->cntA_top = (unsigned*)base + (size_t)P * nGrp;
+    plan->cntB_grp = (unsigned*)cB;
+    plan->cntF = (unsigned*)cF;
+    plan->cand_cnt = (unsigned*)cc;
+    plan->uni_cnt = (unsigned*)uc;
     plan->qi = (float*)qi;
     plan->blk_m = (float*)bm;
     plan->blk_z = (unsigned long long*)bz;
-    plan->blk_hist = (unsigned long long*)bh;
+    plan->blk_bins = (unsigned*)bb;
+    plan->grp_m = (float*)gm;
+    plan->grp_z = (double*)gz;
+    plan->grp_bins = (unsigned long long*)gb;
     plan->thr = (ThrInfo*)th;
-    plan->cand_cnt = (unsigned*)cc;
     plan->cand = (float2*)ca;
-    plan->uni_cnt = (unsigned*)uc;
     plan->uni = (int2*)un;
-    plan->part = (float*)pa;
+    plan->partB = (float*)pB;
+    plan->partBg = (float*)pG;
+    plan->partF = (float*)pF;
   }
   return off;
 }

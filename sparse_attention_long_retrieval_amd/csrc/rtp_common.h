@@ -75,15 +75,6 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
-// ------------------------------------------------------------------ RoPE (fp64 angles)
-
-// theta_i = base^(-2i/D); angle = pos * theta_i in fp64.
-__device__ __forceinline__ void rope_cs(int pos, int i, double base, double* c, double* s) {
-  double theta = pow(base, -2.0 * (double)i / (double)RTP_D);
-  double ang = (double)pos * theta;
-  sincos(ang, s, c);
-}
-
 // ------------------------------------------------------------------ indexer score
 
 // Score of one index row (16 bf16 packed in 8 dwords) against an fp32 query

@@ -13,12 +13,20 @@ constexpr int kD = 128;
 constexpr int kR = 16;
 constexpr int kMaxKv = 64;
 
-// Score-grid histogram: NB bins of width 1/kInvDelta below each block's top key.
+// Score-grid histogram: kNB bins of width 1/kInvDelta below each block's top key.
 constexpr int kNB = 32;
-constexpr float kInvDelta = 2.0f;   // bin width 0.5 score units, exact in fp32
-// Fixed-point scales of the integer mass sums (exact, order independent).
-constexpr double kFxBlock = 1125899906842624.0;  // 2^50: per-block sums, weights <= 1, <= 4096 tokens
-constexpr double kFxGlobal = 68719476736.0;      // 2^36: global sums, <= 2^27 tokens
+constexpr float kInvDelta = 2.0f;  // bin width 0.5 score units, exact in fp32
+constexpr float kDelta = 0.5f;
+// Bin masses are sums of exp(s - e) with e the bin's upper edge (weights in
+// (e^-0.5, 1]), rounded to 2^-20 units: integer sums, exact and order free.
+constexpr float kFxBin = 1048576.0f;            // 2^20
+constexpr double kFxZ = 1125899906842624.0;     // 2^50: per-block Z relative to the block max
+constexpr double kFxCand = 68719476736.0;       // 2^36: candidate masses relative to the max
+
+// Tokens per block of the two index passes.
+constexpr int kPassTokens = 2048;
+// Bytes reserved at the start of each workspace for self-resetting counters.
+constexpr size_t kCounterBytes = 65536;
 
 // Threshold state of one (pair, q-head).
 struct ThrInfo {
@@ -27,15 +35,14 @@ struct ThrInfo {
   int mode;      // 0 normal, 1 boundary below the histogram window, 2 keep all keys
   float m;       // global max score
   double Z;      // sum of exp(s - m) over all keys
-  double above;  // mass of keys with key > key_bnd
+  double above;  // mass of keys with key > key_bnd (relative to m)
   double need;   // top_p * Z - above
   float tau;     // resolved threshold score
   int n_cand;    // candidates seen by the resolver
 };
 
-// Parameters of one decode or prefill-row retrieval pass.
+// Parameters of the retrieval decode.
 struct DecPlan {
-  // inputs
   const uint16_t* q_pre;
   const uint16_t* w_q;
   const uint16_t* k_cache;
@@ -45,33 +52,42 @@ struct DecPlan {
   int B, Hq, Hkv, G, n_ret, max_seq, N, n_sink;
   int ret_kv[kMaxKv];
   float top_p, idx_scale, attn_scale;
-  double rope_base;
+  double theta[kD / 2];
   // decomposition
-  int P;        // B * n_ret pairs
-  int TA;       // tokens per pass-A/B block
-  int nA;       // blocks per pair
-  int nGat;     // gather blocks per pair
-  // workspace
+  int P;       // B * n_ret pairs
+  int nA;      // blocks per pair in the index passes
+  int gsz;     // blocks per merge group
+  int nGrp;    // groups per pair
+  int nF;      // finish blocks per (pair, q-head)
+  // workspace: counters (fixed region at the start)
+  unsigned* cntA_grp;  // [P][nGrp]
+  unsigned* cntA_top;  // [P]
+  // workspace: data
+  unsigned* cntB_grp;  // [P][nGrp]    zeroed by pass A
+  unsigned* cntF;      // [P*G]        zeroed by pass A
+  unsigned* cand_cnt;  // [P*G]        zeroed by pass A
+  unsigned* uni_cnt;   // [P]          zeroed by pass A
   float* qi;                      // [P][G][16] (idx_scale folded in)
   float* blk_m;                   // [P][nA][G]
-  unsigned long long* blk_z;      // [P][nA][G]   Z_b in 2^50 fixed point
-  unsigned long long* blk_hist;   // [P][nA][G][kNB]
+  unsigned long long* blk_z;      // [P][nA][G]   Z_b * 2^50 relative to m_b
+  unsigned* blk_bins;             // [P][nA][G][kNB]
+  float* grp_m;                   // [P][nGrp][G]
+  double* grp_z;                  // [P][nGrp][G] relative to m_g
+  unsigned long long* grp_bins;   // [P][nGrp][G][kNB]
   ThrInfo* thr;                   // [P][G]
-  unsigned* cand_cnt;             // [P][G]
   float2* cand;                   // [P][G][N]  (score, token id bits)
-  unsigned* uni_cnt;              // [P]
-  int2* uni;                      // [P][N]     (token, definite mask | candidate mask << 8)
-  float* part;                    // [P*G][nGat][kPartStride]
+  int2* uni;                      // [P][N]     debug: (token, definite | candidate << 8)
+  float* partB;                   // [P*G][nA][kPartStride]
+  float* partBg;                  // [P*G][nGrp][kPartStride]
+  float* partF;                   // [P*G][nF][kPartStride]
   // debug (device pointers or null)
   int32_t* dbg_idx;
   int32_t* dbg_cnt;
   float* dbg_tau;
   int dbg_cap;
   int32_t* dbg_union;
-  hipEvent_t* events;   // 7 phase events or null
+  hipEvent_t* events;  // phase events or null
 };
-
-constexpr int kPartStride = 132;  // m, l, pad, pad, o[128]
 
 struct SwaPlan {
   const uint16_t* q_pre;
@@ -82,11 +98,15 @@ struct SwaPlan {
   int n_loc;
   int loc_kv[kMaxKv];
   float attn_scale;
-  double rope_base;
+  double theta[kD / 2];
   int q_start, Tq;
-  int nSeg;       // segments per (b, local kv head) for decode
-  int segRows;    // rows per segment (multiple of 64)
-  float* part;    // [B*n_loc*G][nSeg][kPartStride]
+  int nSeg;      // segments per (b, local kv head)
+  int segRows;   // rows per segment (multiple of 64)
+  int gsz, nGrp;
+  unsigned* cnt_grp;  // [B*n_loc][nGrp]   (counter region)
+  unsigned* cnt_top;  // [B*n_loc]
+  float* part;        // [B*n_loc*G][nSeg][kPartStride]
+  float* partg;       // [B*n_loc*G][nGrp][kPartStride]
 };
 
 struct AppendPlan {
@@ -97,11 +117,11 @@ struct AppendPlan {
   uint16_t* v_cache;
   uint16_t* index;
   int B, Hkv, n_ret, max_seq, start_pos, T;
-  int ret_slot[kMaxKv];   // kv head -> retrieval slot or -1
-  double rope_base;
+  int ret_slot[kMaxKv];  // kv head -> retrieval slot or -1
+  double theta[kD / 2];
 };
 
-// Workspace sizing (bytes, 256-aligned sections).
+// Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base);
 

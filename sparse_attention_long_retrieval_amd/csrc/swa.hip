@@ -4,8 +4,9 @@
 // tokens ("Full Attention Strikes Back": techwalker article §2; §8 sets the
 // window to 8192 tokens with 4 sinks; RTPurboV2 article finding 1 serves 85% of
 // heads this way).  The decode step reads the contiguous window rows (coalesced
-// 16-byte loads) split into segments, one block per segment and KV head, and
-// merges the per-segment softmax states afterwards.
+// 16-byte loads) split into segments, one block per segment and KV head; the
+// last block of each group of segments merges the group's softmax states and the
+// last group writes the bf16 output, all in one launch.
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
@@ -24,15 +25,17 @@ __device__ __forceinline__ void swa_rows(int pos, int window, int n_sink, int* l
 
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
+  constexpr int NT = 64 * G;
   const int bl = blockIdx.y, seg = blockIdx.x;
   const int b = bl / p.n_loc, li = bl % p.n_loc;
   const int kv = p.loc_kv[li];
+  const int h = threadIdx.x >> 6;
   __shared__ TileSmem<G> sm;
   const int pos = p.q_start;
   int lo, ns_out, L;
   swa_rows(pos, p.window, p.n_sink, &lo, &ns_out, &L);
   const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-  load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, pos, p.rope_base,
+  load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, pos, p.theta,
                  p.attn_scale * kLog2eS);
   const int r0 = seg * p.segRows;
   const int r1 = min(L, r0 + p.segRows);
@@ -45,49 +48,31 @@ __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
       sm.masks[threadIdx.x] = 0xffffffffu;
     }
     __syncthreads();
-    tile_attend<G>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+    tile_attend<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
   }
-  const int h = threadIdx.x >> 6;
-  store_partial(p.part + ((size_t)(bl * G + h) * p.nSeg + seg) * kPartStride, m, l, o0, o1);
-}
+  const size_t unit = (size_t)bl * G + h;
+  store_partial(p.part + (unit * p.nSeg + seg) * kPartStride, m, l, o0, o1);
 
-struct SwaMergeMap {
-  uint16_t* out;
-  int Hq, G, n_loc;
-  int kv[kMaxKv];
-};
-
-__global__ __launch_bounds__(128) void k_swa_merge(const float* part, int n_part, SwaMergeMap mp) {
-  const int unit = blockIdx.x;  // (b * n_loc + li) * G + g
-  const int g = unit % mp.G;
-  const int bl = unit / mp.G;
-  const int b = bl / mp.n_loc, li = bl % mp.n_loc;
-  const int qh = mp.kv[li] * mp.G + g;
-  const float* pp = part + (size_t)unit * n_part * kPartStride;
-  float M = -INFINITY;
-  for (int k = 0; k < n_part; ++k) M = fmaxf(M, pp[(size_t)k * kPartStride]);
-  float Ls = 0.f, O = 0.f;
-  for (int k = 0; k < n_part; ++k) {
-    const float* q = pp + (size_t)k * kPartStride;
-    if (q[0] == -INFINITY) continue;
-    const float sc = exp2f(q[0] - M);
-    Ls = fmaf(q[1], sc, Ls);
-    O = fmaf(q[4 + threadIdx.x], sc, O);
+  const int grp = seg / p.gsz;
+  const int s0 = grp * p.gsz;
+  const int nin = min(p.gsz, p.nSeg - s0);
+  if (!arrive_last(&p.cnt_grp[bl * p.nGrp + grp], (unsigned)nin)) return;
+  {
+    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
+    merge_partials_wave(p.part + (unit * p.nSeg + s0) * kPartStride, nin, gm, gl, g0, g1);
+    store_partial(p.partg + (unit * p.nGrp + grp) * kPartStride, gm, gl, g0, g1);
   }
-  mp.out[((size_t)b * mp.Hq + qh) * kD + threadIdx.x] = f32_to_bf16(Ls > 0.f ? O / Ls : 0.f);
+  if (!arrive_last(&p.cnt_top[bl], (unsigned)p.nGrp)) return;
+  {
+    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
+    merge_partials_wave(p.partg + unit * p.nGrp * kPartStride, p.nGrp, gm, gl, g0, g1);
+    store_output(p.out + ((size_t)b * p.Hq + kv * G + h) * kD, gl, g0, g1);
+  }
 }
 
 template <int G>
 static hipError_t launch_swa_decode_g(const SwaPlan& p, hipStream_t s) {
   hipLaunchKernelGGL(k_swa_decode<G>, dim3(p.nSeg, p.B * p.n_loc), dim3(64 * G), 0, s, p);
-  SwaMergeMap mp;
-  mp.out = p.out;
-  mp.Hq = p.Hq;
-  mp.G = G;
-  mp.n_loc = p.n_loc;
-  for (int i = 0; i < p.n_loc; ++i) mp.kv[i] = p.loc_kv[i];
-  hipLaunchKernelGGL(k_swa_merge, dim3(p.B * p.n_loc * G), dim3(128), 0, s, (const float*)p.part,
-                     p.nSeg, mp);
   return hipGetLastError();
 }
 
@@ -104,11 +89,11 @@ hipError_t launch_swa_decode(const SwaPlan& p, hipStream_t s) {
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Decode sizing: rows = window rows + sinks outside the window; segments of a
-// multiple of 64 rows so that about 1024 blocks cover the GPU.
+// multiple of 64 rows so that about 2048 blocks cover the GPU.
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base) {
   (void)Tq;
   const int units = B * n_loc;
-  int nSeg = units > 0 ? (1024 + units - 1) / units : 1;
+  int nSeg = units > 0 ? (2048 + units - 1) / units : 1;
   const int max_seg = (rows + kTileRows - 1) / kTileRows;
   if (nSeg > max_seg) nSeg = max_seg;
   if (nSeg < 1) nSeg = 1;
@@ -116,13 +101,24 @@ size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, c
   segRows = (segRows + kTileRows - 1) / kTileRows * kTileRows;
   nSeg = (rows + segRows - 1) / segRows;
   if (nSeg < 1) nSeg = 1;
-  const size_t bytes = align256s((size_t)units * G * nSeg * kPartStride * 4);
+  int gsz = 4;
+  while (gsz * gsz < nSeg) ++gsz;
+  const int nGrp = (nSeg + gsz - 1) / gsz;
+  if ((size_t)units * (nGrp + 1) * sizeof(unsigned) > kCounterBytes) return 0;
+  size_t off = kCounterBytes;
+  const size_t part_bytes = align256s((size_t)units * G * nSeg * kPartStride * 4);
+  const size_t partg_bytes = align256s((size_t)units * G * nGrp * kPartStride * 4);
   if (plan) {
     plan->nSeg = nSeg;
     plan->segRows = segRows;
-    plan->part = (float*)base;
+    plan->gsz = gsz;
+    plan->nGrp = nGrp;
+    plan->cnt_grp = (unsigned*)base;
+    plan->cnt_top = (unsigned*)base + (size_t)units * nGrp;
+    plan->part = (float*)(base + off);
+    plan->partg = (float*)(base + off + part_bytes);
   }
-  return bytes;
+  return off + part_bytes + partg_bytes;
 }
 
 }  // namespace rtp

@@ -68,16 +68,19 @@ class Device:
         self.w_q = to_dev(wl.w_q) if wl.n_ret else torch.zeros(16, dtype=torch.int16,
                                                                  device="cuda")
 
-    def decode(self, top_p: float, debug_cap: int = 0, idx_scale: float = 1.0):
+    def decode(self, top_p: float, debug_cap: int = 0, idx_scale: float = 1.0, ws=None,
+               wss=None):
         wl = self.wl
         out = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.int16, device="cuda")
-        ws = torch.empty(max(256, R.workspace_size(self.layer, R.OP_DECODE, wl.N)),
-                         dtype=torch.uint8, device="cuda")
+        if ws is None:
+            ws = torch.zeros(max(256, R.workspace_size(self.layer, R.OP_DECODE, wl.N)),
+                             dtype=torch.uint8, device="cuda")
         dbg = R.Debug(wl.B * wl.n_ret * wl.G, debug_cap) if debug_cap else None
         R.decode_sparse_attn(self.layer, self.q, self.w_q, self.kc, self.vc, self.idx, wl.N,
                              top_p, out, ws, idx_scale=idx_scale, debug=dbg)
-        wss = torch.empty(max(256, R.workspace_size(self.layer, R.OP_SWA, wl.N)),
-                          dtype=torch.uint8, device="cuda")
+        if wss is None:
+            wss = torch.zeros(max(256, R.workspace_size(self.layer, R.OP_SWA, wl.N)),
+                              dtype=torch.uint8, device="cuda")
         R.swa_attn(self.layer, self.q, wl.N - 1, 1, self.kc, self.vc, out, wss)
         torch.cuda.synchronize()
         res = {"out": from_dev(out)}

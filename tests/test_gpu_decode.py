@@ -135,6 +135,28 @@ def test_deterministic_repeat():
         assert np.array_equal(P.gpu_set(a, u), P.gpu_set(b, u))
 
 
+def test_workspace_reuse_across_shapes():
+    """One workspace, zero-filled once, serves consecutive calls of different
+    lengths and top-p values; each result equals the one from a fresh workspace
+    (the kernels leave their counters at zero)."""
+    wls = [W.random_decode(46, 1, 8, 2, n, [0], 256, n_needles=2, q_scale=1.5)
+           for n in (5000, 300, 70000)]
+    devs = []
+    for wl in wls:
+        kc, vc, idx = O.caches_for(wl)
+        devs.append(P.Device(wl, kc, vc, idx))
+    big = max(P.R.workspace_size(d.layer, P.R.OP_DECODE, d.wl.N) for d in devs)
+    bigs = max(P.R.workspace_size(d.layer, P.R.OP_SWA, d.wl.N) for d in devs)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    wss = torch.zeros(bigs, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for d, p in zip(devs, (0.9, 0.5, 0.95)):
+            a = d.decode(p, debug_cap=d.wl.N, ws=ws, wss=wss)
+            b = d.decode(p, debug_cap=d.wl.N)
+            assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["cnt"], b["cnt"])
+            assert np.array_equal(a["tau"], b["tau"])
+
+
 @pytest.mark.parametrize("window,n_sink", [(1, 4), (5000, 4), (64, 0), (8, 30)])
 def test_swa_edges(window, n_sink):
     wl = W.random_decode(45, 1, 8, 2, 1000, [0], window, n_sink=n_sink)
