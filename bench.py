@@ -112,7 +112,7 @@ def main() -> int:
     main_s = torch.cuda.current_stream()
     side_s = torch.cuda.Stream()          # local heads run beside the retrieval chain
     stream = main_s.cuda_stream
-    n_ph = 4
+    n_ph = 6
     ph_events = [hip.event() for _ in range(n_ph)]
     extra = [hip.event() for _ in range(3)]
     dbg_ph = R.Debug(0, 0, events=ph_events)
@@ -171,7 +171,7 @@ def main() -> int:
     warm_ms = hip.elapsed_ms(e0, e1) / args.steps
 
     # ---- phases: K more cold steps with the library's phase events
-    names = ["score_hist", "select_attend", "finish"]
+    names = ["scan", "threshold", "select", "finish", "merge"]
     ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
     for i in range(args.steps):
         flush.fill_(i & 0xFF)
@@ -181,7 +181,7 @@ def main() -> int:
             ph[n].append(hip.elapsed_ms(ph_events[k], ph_events[k + 1]))
         ph["append"].append(hip.elapsed_ms(extra[0], ph_events[0]))
         ph["swa"].append(hip.elapsed_ms(extra[1], extra[2]))
-        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[3]))
+        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[5]))
     phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
 
     # ---- algorithmic bytes of one step
@@ -195,7 +195,7 @@ def main() -> int:
         B * wl.n_ret * 32
     step_bytes = bytes_index + bytes_gather + bytes_swa + bytes_small
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    score_us = phases_us["score_hist"]
+    score_us = phases_us["scan"]
     ach = bytes_index / (score_us * 1e-6) / 1e9
 
     res = {
@@ -224,7 +224,7 @@ def main() -> int:
         "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
                        "small": bytes_small, "union_rows": int(union.sum())},
         "phases_us": phases_us,
-        "roofline": {"bound": "hbm", "kernel": "k_score_hist (indexer scan + mass histogram)",
+        "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
     }

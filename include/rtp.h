@@ -87,9 +87,9 @@ typedef struct {
  * KV head, the number of distinct K/V rows read (the union of the G sets).
  * phase_events, when non-NULL, are n_phase_events caller-created hipEvent_t
  * handles; the decode records event 0 before its first kernel and event k after
- * kernel k of: 1 index scan + histogram + threshold, 2 select + attention of
- * the keys above the boundary bin, 3 exact threshold + boundary keys + merge
- * (n_phase_events must be >= 4). */
+ * kernel k of: 1 index scan + mass histogram, 2 threshold bin, 3 select +
+ * attention of the keys above the boundary bin, 4 exact threshold + boundary
+ * keys, 5 merge of the partial states (n_phase_events must be >= 6). */
 typedef struct {
   int32_t* sel_idx;     /* [entries][sel_cap] device */
   int32_t* sel_count;   /* [entries] device */

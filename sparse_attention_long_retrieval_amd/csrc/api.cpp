@@ -195,8 +195,8 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
   if (!std::isfinite(idx_scale) || !std::isfinite(attn_scale))
     return fail(RTP_ERR_RANGE, "idx_scale and attn_scale must be finite");
   if (dbg && (dbg->sel_idx && dbg->sel_cap < 1)) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
-  if (dbg && dbg->phase_events && dbg->n_phase_events < 4)
-    return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 4");
+  if (dbg && dbg->phase_events && dbg->n_phase_events < 6)
+    return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 6");
   const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
   if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
   if (ws_bytes < need)

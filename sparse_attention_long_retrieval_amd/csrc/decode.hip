@@ -5,30 +5,30 @@
 // smallest highest-scoring set whose softmax mass reaches p (§4), attention
 // sinks are always kept (§2, §8), and exact 128-dim attention runs on the
 // selected rows only (§3).  The pages' decode kernel (§6) fuses scoring with a
-// 256-bucket mass histogram and lets the last CTA merge split-KV partials; this
-// gfx950 path keeps both ideas, adds what an exact threshold needs, and uses
-// three dependent launches:
+// 256-bucket mass histogram and merges split-KV partial states at the end; this
+// gfx950 path keeps both ideas and adds what an exact threshold needs:
 //
-//   k_score_hist     pass A: stream the N x 16 bf16 index once; G fp32 scores per
-//                    token stay in registers; per block the max m_b, the exact
-//                    mass Z_b = sum exp(s - m_b) (fixed point) and a 32-bin mass
-//                    histogram on an absolute score grid (bins of 0.5 below the
-//                    block's top key; each weight taken relative to its bin's
-//                    upper edge, so integer bin sums merge across blocks without
-//                    rescaling).  The last block of each group merges its group,
-//                    the last group locates the boundary bin where the running
-//                    mass reaches p*Z.  A boundary below the 16-unit window makes
-//                    the whole tail the candidate set (exact, slower).
-//   k_select_attend  pass B: recompute the same scores (bit-identical FMA order);
-//                    keys above the boundary bin (and the sinks) are attended at
-//                    once from LDS-staged K/V tiles, keys in the boundary bin are
-//                    appended as candidates; the last block of each group merges
-//                    the group's partial softmax states.
-//   k_finish         per (pair, q-head), nF blocks: exact threshold inside the
-//                    boundary bin (radix select by mass over the ordered fp32 keys
-//                    of the candidates), attention over the selected candidates
-//                    of a token range, and the last block merges everything into
-//                    the bf16 output.
+//   k_scan       pass A: stream the N x 16 bf16 index once; G fp32 scores per
+//                token stay in registers; per block the max, the exact mass
+//                Z_b = sum exp(s - e_top) (fixed point, e_top the upper edge of
+//                the block max's bin) and a 32-bin mass histogram on an absolute
+//                score grid (bins of 0.5 below the block's top bin; each weight
+//                taken relative to its bin's upper edge, so integer bin sums of
+//                different blocks add without rescaling).  One exp per score.
+//   k_threshold  per (pair, q-head): merge the block summaries, locate the
+//                boundary bin where the running mass reaches p*Z.  A boundary
+//                below the 16-unit window makes the whole tail the candidate set
+//                (exact, slower).
+//   k_select     pass B: recompute the same scores (bit-identical FMA order);
+//                keys above the boundary bin (and the sinks) are attended at once
+//                from LDS-staged K/V tiles, keys in the boundary bin are written
+//                as candidates to the block's own region (fixed order).
+//   k_finish     per (pair, q-head), nF blocks: exact threshold inside the
+//                boundary bin (bisection on the ordered fp32 key with exact
+//                integer mass sums, candidates held in LDS when they fit), then
+//                attention over a share of the selected candidates.
+//   k_merge      combine all partial softmax states into the bf16 output.
+// Every sum and row order is fixed, so results are bit-identical across runs.
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
@@ -44,9 +44,12 @@ struct PassCfg {
   static constexpr int NW = NT / 64;
 };
 
-constexpr int kMaxGroup = 256;        // blocks per merge group (and groups per pair)
+constexpr int kThrThreads = 256;
 constexpr int kFinishThreads = 256;
 constexpr int kCandCap = 4096;        // candidates resolved in LDS
+constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 8;         // output dimensions per merge block
 
 __device__ __forceinline__ void load_index_row(const uint16_t* row, uint32_t (&w)[8]) {
   const uint4 a = *(const uint4*)row;
@@ -55,22 +58,13 @@ __device__ __forceinline__ void load_index_row(const uint16_t* row, uint32_t (&w
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-// qi = q_pre . W_q (fp32, fixed order) times idx_scale, for the G q-heads of a pair.
-template <int G>
-__device__ __forceinline__ void compute_qi(const DecPlan& p, int b, int ret_i, float (*qi_s)[kR]) {
-  const int t = threadIdx.x;
-  if (t < G * kR) {
-    const int h = t / kR, c = t % kR;
-    const int qh = p.ret_kv[ret_i] * G + h;
-    const uint16_t* q = p.q_pre + ((size_t)b * p.Hq + qh) * kD;
-    const uint16_t* w = p.w_q + (size_t)(ret_i * G + h) * kD * kR;
-    float acc = 0.f;
-    for (int d = 0; d < kD; ++d) acc = __fmaf_rn(bf16_to_f32(q[d]), bf16_to_f32(w[d * kR + c]), acc);
-    qi_s[h][c] = acc * p.idx_scale;
-  }
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -78,93 +72,36 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 
 // ------------------------------------------------------------------ pass A
 
-// Merge per-block (or per-group) summaries of one pair: max, Z, absolute-grid
-// bins.  src_m [n][G]; src_z fixed-point u64 (blocks) or double (groups);
-// src_bins [n][G][kNB] u32 (blocks) or u64 (groups).  All NT threads call it;
-// results land in LDS (m_s, kt_s, z_s, bins_s).  Every sum runs in a fixed order.
-template <int G, int NT, bool kBlockLevel>
-__device__ void merge_summaries(const float* src_m, const void* src_z, const void* src_bins,
-                                int n, float* m_s, int* kt_s, double* z_s,
-                                unsigned long long (*bins_s)[kNB], float* mm_tmp,
-                                double* zz_tmp) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < n * G; e += NT) mm_tmp[e] = ld_dev(&src_m[e]);
-  __syncthreads();
-  if (tid < G) {
-    float m = -INFINITY;
-    for (int k = 0; k < n; ++k) m = fmaxf(m, mm_tmp[k * G + tid]);
-    m_s[tid] = m;
-    kt_s[tid] = score_key(m, kInvDelta);
-  }
-  __syncthreads();
-  for (int e = tid; e < n * G; e += NT) {
-    const int h = e % G;
-    double zk;
-    if (kBlockLevel)
-      zk = (double)ld_dev(&((const unsigned long long*)src_z)[e]) / kFxZ;
-    else
-      zk = ld_dev(&((const double*)src_z)[e]);
-    zz_tmp[e] = zk * exp((double)mm_tmp[e] - (double)m_s[h]);
-  }
-  for (int e = tid; e < G * kNB; e += NT) {
-    const int h = e / kNB, i = e % kNB;
-    unsigned long long acc = 0ull;
-    const int kt = kt_s[h];
-    for (int k0 = 0; k0 < n; k0 += 8) {
-      unsigned long long v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = k0 + u;
-        v[u] = 0ull;
-        if (k < n) {
-          const int j = i - (kt - score_key(mm_tmp[k * G + h], kInvDelta));
-          if (j >= 0) {
-            const size_t off = ((size_t)k * G + h) * kNB + j;
-            v[u] = kBlockLevel ? (unsigned long long)ld_dev(&((const unsigned*)src_bins)[off])
-                               : ld_dev(&((const unsigned long long*)src_bins)[off]);
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += v[u];
-    }
-    bins_s[h][i] = acc;
-  }
-  __syncthreads();
-  if (tid < G) {
-    double z = 0.0;
-    for (int k = 0; k < n; ++k) z += zz_tmp[k * G + tid];
-    z_s[tid] = z;
-  }
-  __syncthreads();
-}
-
 template <int G>
-__global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
+  constexpr int WQ_VEC = G * kD * kR / 8;           // uint4 of W_q for the pair
+  constexpr int WQ_PER = (WQ_VEC + NT - 1) / NT;
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float qi_s[G][kR];
   __shared__ float red_m[NW][G];
   __shared__ float mb_s[G];
   __shared__ int kt_s[G];
   __shared__ unsigned bins[G][kNB];
   __shared__ unsigned long long zred[NW][G];
-  __shared__ float mm_tmp[kMaxGroup * G];
-  __shared__ double zz_tmp[kMaxGroup * G];
-  __shared__ double gz_s[G];
-  __shared__ unsigned long long gbins[G][kNB];
+  __shared__ float bscale[kNB];
+  __shared__ __align__(16) uint16_t wq_s[G * kD * kR];
+  __shared__ __align__(16) uint16_t q_s[G * kD];
 
-  if (blk == 0) {
-    // counters of the two later kernels start from zero on every call
-    for (int e = tid; e < p.nGrp; e += NT) p.cntB_grp[pair * p.nGrp + e] = 0u;
-    if (tid < G) {
-      p.cntF[pair * G + tid] = 0u;
-      p.cand_cnt[pair * G + tid] = 0u;
-    }
-    if (tid == 0) p.uni_cnt[pair] = 0u;
+  // the projection and the queries first: they are shared by every block and
+  // come back from L2 while the index rows stream in
+  uint4 wreg[WQ_PER];
+  const uint4* wsrc = (const uint4*)(p.w_q + (size_t)ret_i * G * kD * kR);
+#pragma unroll
+  for (int u = 0; u < WQ_PER; ++u) {
+    const int e = u * NT + tid;
+    if (e < WQ_VEC) wreg[u] = wsrc[e];
   }
+  uint4 qreg = make_uint4(0, 0, 0, 0);
+  const uint4* qsrc = (const uint4*)(p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G) * kD);
+  if (tid < G * kD / 8) qreg = qsrc[tid];
 
   const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
   const int tok0 = blk * kPassTokens;
@@ -179,8 +116,29 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
       for (int c = 0; c < 8; ++c) w[k][c] = 0u;
     }
   }
-  compute_qi<G>(p, b, ret_i, qi_s);
+#pragma unroll
+  for (int u = 0; u < WQ_PER; ++u) {
+    const int e = u * NT + tid;
+    if (e < WQ_VEC) ((uint4*)wq_s)[e] = wreg[u];
+  }
+  if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
   for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
+  if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
+  __syncthreads();
+  {
+    // qi = q . W_q (fp32): four threads per output, 32 terms each, (p0+p1)+(p2+p3)
+    float acc = 0.f;
+    const int h = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
+    if (h < G) {
+      const uint16_t* wq = wq_s + h * kD * kR;
+      const uint16_t* qq = q_s + h * kD;
+      for (int d = 32 * part; d < 32 * part + 32; ++d)
+        acc = __fmaf_rn(bf16_to_f32(qq[d]), bf16_to_f32(wq[d * kR + c]), acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (h < G && part == 0) qi_s[h][c] = acc * p.idx_scale;
+  }
   __syncthreads();
   if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
 
@@ -199,7 +157,6 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
       mloc[h] = fmaxf(mloc[h], s[k][h]);
     }
   }
-  const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float v = wave_max(mloc[h]);
@@ -216,19 +173,19 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mb = mb_s[h];
     const int kt = kt_s[h];
+    const float e_top = (float)(kt + 1) * kDelta;  // exact: a multiple of 0.5
     float z = 0.f;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const float sv = s[k][h];
       if (sv > -INFINITY) {
-        z += exp2f((sv - mb) * kLog2e);
-        const int key = score_key(sv, kInvDelta);
-        const int j = kt - key;
+        const float wt = exp2f((sv - e_top) * kLog2e);  // <= 1
+        z += wt;
+        const int j = kt - score_key(sv, kInvDelta);
         if (j < kNB) {
-          const float edge = (float)(key + 1) * kDelta;
-          const float wb = exp2f((sv - edge) * kLog2e);
+          // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1]
+          const float wb = fminf(wt * bscale[j], 1.0f);
           atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
         }
       }
@@ -241,76 +198,114 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_score_hist(DecPlan p) {
   if (tid < G) {
     unsigned long long zb = 0ull;
     for (int q = 0; q < NW; ++q) zb += zred[q][tid];
-    st_dev(&p.blk_m[so + tid], mb_s[tid]);
-    st_dev(&p.blk_z[so + tid], zb);
+    p.blk_m[so + tid] = mb_s[tid];
+    p.blk_z[so + tid] = zb;
   }
-  for (int e = tid; e < G * kNB; e += NT) st_dev(&p.blk_bins[so * kNB + e], (&bins[0][0])[e]);
+  for (int e = tid; e < G * kNB; e += NT) p.blk_bins[so * kNB + e] = (&bins[0][0])[e];
+}
 
-  // ---- group merge by the last block of the group
-  const int grp = blk / p.gsz;
-  const int b0 = grp * p.gsz;
-  const int nin = min(p.gsz, p.nA - b0);
-  if (!arrive_last(&p.cntA_grp[pair * p.nGrp + grp], (unsigned)nin)) return;
-  {
-    const size_t sb = ((size_t)pair * p.nA + b0) * G;
-    merge_summaries<G, NT, true>(p.blk_m + sb, p.blk_z + sb, p.blk_bins + sb * kNB, nin, mb_s,
-                                 kt_s, gz_s, gbins, mm_tmp, zz_tmp);
-    const size_t go = ((size_t)pair * p.nGrp + grp) * G;
-    if (tid < G) {
-      st_dev(&p.grp_m[go + tid], mb_s[tid]);
-      st_dev(&p.grp_z[go + tid], gz_s[tid]);
-    }
-    for (int e = tid; e < G * kNB; e += NT) st_dev(&p.grp_bins[go * kNB + e], (&gbins[0][0])[e]);
+// ------------------------------------------------------------------ threshold
+
+// One block per (pair, q-head).  Every thread owns whole pass-A blocks; their
+// bins, shifted onto the global window, accumulate in the thread's own LDS row
+// and the rows are summed per bin afterwards (integers, order free).  Z is summed
+// in a fixed order (per thread, then a fixed butterfly).
+template <int G>
+__global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
+  constexpr int NT = kThrThreads;
+  const int unit = blockIdx.x;
+  const int pair = unit / G, h = unit % G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float redm[NT / 64];
+  __shared__ double redz[NT / 64];
+  __shared__ unsigned long long rows[NT][kNB];
+  __shared__ unsigned long long colp[NT / kNB][kNB];
+  __shared__ double mass_s[kNB];
+
+  if (tid == 0 && h == 0) p.uni_cnt[pair] = 0u;
+  const size_t base = (size_t)pair * p.nA;
+  float ml = -INFINITY;
+  for (int k = tid; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
+  ml = wave_max(ml);
+  if (lane == 0) redm[wave] = ml;
+#pragma unroll
+  for (int i = 0; i < kNB; ++i) rows[tid][i] = 0ull;
+  __syncthreads();
+  float m = redm[0];
+  for (int q = 1; q < NT / 64; ++q) m = fmaxf(m, redm[q]);
+  const int kt = score_key(m, kInvDelta);
+
+  double z = 0.0;
+  for (int k = tid; k < p.nA; k += NT) {
+    const size_t so = (base + k) * G + h;
+    const float mb = p.blk_m[so];
+    const int ktb = score_key(mb, kInvDelta);
+    const double e_top_b = (double)(ktb + 1) * (double)kDelta;
+    z += (double)p.blk_z[so] / kFxZ * exp(e_top_b - (double)m);
+    const uint4* src = (const uint4*)(p.blk_bins + so * kNB);
+    uint4 v[kNB / 4];
+#pragma unroll
+    for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
+    const int shift = kt - ktb;
+    const unsigned* vv = (const unsigned*)v;
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+      if (j + shift < kNB) rows[tid][j + shift] += vv[j];
   }
-  // ---- final merge by the last group of the pair
-  if (!arrive_last(&p.cntA_top[pair], (unsigned)p.nGrp)) return;
+  z = wave_sum_f64(z);
+  if (lane == 0) redz[wave] = z;
+  __syncthreads();
+  // column sums: thread (part, i) sums kNB rows of column i
   {
-    const size_t go = (size_t)pair * p.nGrp * G;
-    merge_summaries<G, NT, false>(p.grp_m + go, p.grp_z + go, p.grp_bins + go * kNB, p.nGrp,
-                                  mb_s, kt_s, gz_s, gbins, mm_tmp, zz_tmp);
-    // bin masses relative to the global max, in parallel (zz_tmp reused)
-    for (int e = tid; e < G * kNB; e += NT) {
-      const int h = e / kNB, g = e % kNB;
-      zz_tmp[e] = (double)gbins[h][g] / (double)kFxBin *
-                  exp((double)(kt_s[h] - g + 1) * (double)kDelta - (double)mb_s[h]);
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int h = tid;
-      ThrInfo t;
-      t.key_top = kt_s[h];
-      t.m = mb_s[h];
-      t.Z = gz_s[h];
-      t.tau = -INFINITY;
-      t.n_cand = 0;
-      if (p.top_p >= 1.0f) {
-        t.mode = 2;
-        t.key_bnd = INT_MIN;
-        t.above = t.Z;
-        t.need = 0.0;
-      } else {
-        const double target = (double)p.top_p * t.Z;
-        double cum = 0.0;
-        int g = 0;
-        for (; g < kNB; ++g) {
-          const double mass = zz_tmp[h * kNB + g];
-          if (cum + mass >= target) break;
-          cum += mass;
-        }
-        t.mode = g < kNB ? 0 : 1;
-        t.key_bnd = g < kNB ? t.key_top - g : t.key_top - kNB;
-        t.above = cum;
-        t.need = target - cum;
+    const int i = tid % kNB, part = tid / kNB;
+    unsigned long long acc = 0ull;
+    for (int r = part * kNB; r < part * kNB + kNB; ++r) acc += rows[r][i];
+    colp[part][i] = acc;
+  }
+  __syncthreads();
+  if (tid < kNB) {
+    unsigned long long acc = 0ull;
+    for (int q = 0; q < NT / kNB; ++q) acc += colp[q][tid];
+    // bin tid covers key kt - tid; its weights are relative to its upper edge
+    mass_s[tid] = (double)acc / (double)kFxBin *
+                  exp((double)(kt - tid + 1) * (double)kDelta - (double)m);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double Z = 0.0;
+    for (int q = 0; q < NT / 64; ++q) Z += redz[q];
+    ThrInfo t;
+    t.key_top = kt;
+    t.m = m;
+    t.Z = Z;
+    t.tau = -INFINITY;
+    t.n_cand = 0;
+    if (p.top_p >= 1.0f) {
+      t.mode = 2;
+      t.key_bnd = INT_MIN;
+      t.above = Z;
+      t.need = 0.0;
+    } else {
+      const double target = (double)p.top_p * Z;
+      double cum = 0.0;
+      int g = 0;
+      for (; g < kNB; ++g) {
+        if (cum + mass_s[g] >= target) break;
+        cum += mass_s[g];
       }
-      p.thr[pair * G + h] = t;
+      t.mode = g < kNB ? 0 : 1;
+      t.key_bnd = g < kNB ? kt - g : kt - kNB;
+      t.above = cum;
+      t.need = target - cum;
     }
+    p.thr[unit] = t;
   }
 }
 
 // ------------------------------------------------------------------ pass B
 
 template <int G>
-__global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
@@ -320,13 +315,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
   __shared__ float qi_s[G][kR];
   __shared__ int kb_s[G], mode_s[G];
   __shared__ int relevant;
-  __shared__ unsigned ccount[G], cbase[G];
+  __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned list[kPassTokens];
   __shared__ unsigned wsum[NW];
-  __shared__ unsigned n_list_s, ubase_s;
+  __shared__ unsigned n_list_s, ubase_s, ucount_s;
 
   if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
-  if (tid < G) ccount[tid] = 0u;
   __syncthreads();
   if (tid < G) {
     const ThrInfo t = p.thr[pair * G + tid];
@@ -339,10 +333,9 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
   __syncthreads();
 
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  if (!relevant && tid < G) p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = 0u;
   if (relevant) {
     const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-    load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.theta,
-                   p.attn_scale * kLog2e);
     const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
     const int tok0 = blk * kPassTokens;
     uint32_t w[TPT][8];
@@ -356,6 +349,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
         for (int c = 0; c < 8; ++c) w[k][c] = 0u;
       }
     }
+    load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.theta,
+                   p.attn_scale * kLog2e);
     float s[TPT][G];
     uint32_t dm[TPT], cm[TPT];
 #pragma unroll
@@ -380,28 +375,38 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
         }
       }
     }
-    // candidates: block-local offsets in LDS, one global atomic per head
+    // candidates: the block's own region of the head's list, positions from a
+    // block scan (fixed order), and the block's count for the finish kernel
     unsigned coff[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       unsigned c = 0u;
 #pragma unroll
       for (int k = 0; k < TPT; ++k) c += (cm[k] >> h) & 1u;
-      coff[h] = c ? atomicAdd(&ccount[h], c) : 0u;
+      unsigned inc = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+      }
+      coff[h] = inc - c;
+      if (lane == 63) cwsum[wave][h] = inc;
     }
-    __syncthreads();
-    if (tid < G && ccount[tid]) cbase[tid] = atomicAdd(&p.cand_cnt[pair * G + tid], ccount[tid]);
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float2* cd = p.cand + ((size_t)pair * G + h) * p.N + cbase[h] + coff[h];
+      for (int q = 0; q < wave; ++q) coff[h] += cwsum[q][h];
+      float2* cd = p.cand + ((size_t)pair * G + h) * p.N + (size_t)blk * kPassTokens + coff[h];
       unsigned c = 0u;
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
-        if ((cm[k] >> h) & 1u) {
-          cd[c++] = make_float2(s[k][h], __int_as_float(tok0 + k * NT + tid));
-        }
+        if ((cm[k] >> h) & 1u) cd[c++] = make_float2(s[k][h], __int_as_float(tok0 + k * NT + tid));
       }
+    }
+    if (tid < G) {
+      unsigned tot = 0u;
+      for (int q = 0; q < NW; ++q) tot += cwsum[q][tid];
+      p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = tot;
     }
     // definite rows (sinks join every head): ordered compaction into LDS
     unsigned cnt = 0u;
@@ -430,19 +435,17 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
       unsigned uc = 0u;
 #pragma unroll
       for (int k = 0; k < TPT; ++k) uc += (dm[k] | cm[k]) ? 1u : 0u;
+      if (tid == 0) ucount_s = 0u;
       __syncthreads();
-      if (tid == 0) ccount[0] = 0u;
+      const unsigned uo = uc ? atomicAdd(&ucount_s, uc) : 0u;
       __syncthreads();
-      const unsigned uo = uc ? atomicAdd(&ccount[0], uc) : 0u;
-      __syncthreads();
-      if (tid == 0) ubase_s = ccount[0] ? atomicAdd(&p.uni_cnt[pair], ccount[0]) : 0u;
+      if (tid == 0) ubase_s = ucount_s ? atomicAdd(&p.uni_cnt[pair], ucount_s) : 0u;
       __syncthreads();
       unsigned u = ubase_s + uo;
 #pragma unroll
       for (int k = 0; k < TPT; ++k)
         if (dm[k] | cm[k])
-          p.uni[(size_t)pair * p.N + u++] =
-              make_int2(tok0 + k * NT + tid, (int)(dm[k] | (cm[k] << 8)));
+          p.uni[(size_t)pair * p.N + u++] = make_int2(tok0 + k * NT + tid, (int)(dm[k] | (cm[k] << 8)));
     }
     __syncthreads();
     const int n_list = (int)n_list_s;
@@ -457,119 +460,102 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select_attend(DecPlan p) {
       tile_attend<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
     }
   }
-  const int unit0 = pair * G;
-  if (wave < G)
-    store_partial(p.partB + ((size_t)(unit0 + wave) * p.nA + blk) * kPartStride, m, l, o0, o1);
-
-  // ---- group merge of the partial states by the last block of the group
-  const int grp = blk / p.gsz;
-  const int b0 = grp * p.gsz;
-  const int nin = min(p.gsz, p.nA - b0);
-  if (!arrive_last(&p.cntB_grp[pair * p.nGrp + grp], (unsigned)nin)) return;
   if (wave < G) {
-    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
-    merge_partials_wave(p.partB + ((size_t)(unit0 + wave) * p.nA + b0) * kPartStride, nin, gm, gl,
-                        g0, g1);
-    store_partial(p.partBg + ((size_t)(unit0 + wave) * p.nGrp + grp) * kPartStride, gm, gl, g0,
-                  g1);
+    float* dst = p.partB + ((size_t)(pair * G + wave) * p.nA + blk) * kPartStride;
+    if (lane == 0) {
+      dst[0] = m;
+      dst[1] = l;
+    }
+    *(float2*)&dst[4 + 2 * lane] = make_float2(o0, o1);
   }
 }
 
 // ------------------------------------------------------------------ finish
 
-// Radix select by mass over candidate scores: the largest threshold tau whose
-// candidates at or above it carry at least need (2^36 fixed point, relative to
-// the global max).  Four 8-bit digits of the ordered fp32 key, high to low; wave
-// 0 scans the 256 digit sums from the top with a prefix sum.  If rounding puts
-// need above the total, every candidate is kept (tau = lowest score).
+// Exact threshold inside the boundary bin by bisection on the ordered fp32 key:
+// the largest key k with mass{candidates with key >= k} >= need.  Masses are
+// 2^36 fixed point relative to the global max, summed over the block as
+// integers (exact, order free).  All NT threads call it; the candidate keys and
+// weights come from LDS (in_lds) or are recomputed from the global list.
 template <int NT>
-__device__ float radix_select_tau(unsigned C, bool in_lds, const float* cs,
-                                  const unsigned long long* cw, const float2* cand, float m,
-                                  double need_fx, unsigned long long* dig, uint32_t* prefix_s,
-                                  uint32_t* pmask_s, unsigned long long* acc_s) {
+__device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
+                               const unsigned long long* w_s, const float2* cand,
+                               const unsigned* blk_cnt, int nA, float m, double need_fx,
+                               unsigned long long* red) {
+  constexpr int CPT = kCandCap / NT;  // candidates per thread when they fit in LDS
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid == 0) {
-    *prefix_s = 0u;
-    *pmask_s = 0u;
-    *acc_s = 0ull;
-  }
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int e = tid; e < 256; e += NT) dig[e] = 0ull;
-    __syncthreads();
-    const uint32_t prefix = *prefix_s, pmask = *pmask_s;
-    for (unsigned c = tid; c < C; c += NT) {
-      float sv;
-      unsigned long long wv;
-      if (in_lds) {
-        sv = cs[c];
-        wv = cw[c];
-      } else {
-        sv = cand[c].x;
-        wv = (unsigned long long)(exp((double)sv - (double)m) * kFxCand);
-      }
-      const uint32_t key = f32_ord(sv);
-      if ((key & pmask) == prefix) atomicAdd(&dig[(key >> shift) & 255u], wv);
+  uint32_t kr[CPT];
+  unsigned long long wr[CPT];
+  if (in_lds) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const unsigned c = i * NT + tid;
+      kr[i] = c < C ? key_s[c] : 0u;
+      wr[i] = c < C ? w_s[c] : 0ull;
     }
-    __syncthreads();
-    if (wave == 0) {
-      unsigned long long d4[4], sum = 0ull;
+  }
+  auto visit = [&](auto&& fn) {
+    if (in_lds) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        d4[j] = dig[255 - 4 * lane - j];
-        sum += d4[j];
-      }
-      unsigned long long incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned long long v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      const unsigned long long acc0 = *acc_s;
-      const unsigned long long hit = __ballot((double)(acc0 + incl) >= need_fx);
-      int digit = 0;
-      unsigned long long acc_new = acc0;
-      if (hit) {
-        const int L = __ffsll((long long)hit) - 1;
-        if (lane == L) {
-          unsigned long long run = acc0 + incl - sum;
-          for (int j = 0; j < 4; ++j) {
-            if ((double)(run + d4[j]) >= need_fx) {
-              digit = 255 - 4 * lane - j;
-              break;
-            }
-            run += d4[j];
-          }
-          acc_new = run;
-        }
-        digit = __shfl(digit, L, 64);
-        acc_new = __shfl(acc_new, L, 64);
-      } else {
-        const unsigned long long nz = __ballot(sum != 0ull);
-        if (nz) {
-          const int L = 63 - __clzll((long long)nz);
-          if (lane == L) {
-            unsigned long long run = acc0 + incl - sum;
-            for (int j = 0; j < 4; ++j) {
-              if (d4[j]) {
-                digit = 255 - 4 * lane - j;
-                acc_new = run;
-              }
-              run += d4[j];
-            }
-          }
-          digit = __shfl(digit, L, 64);
-          acc_new = __shfl(acc_new, L, 64);
+      for (int i = 0; i < CPT; ++i) fn(kr[i], wr[i]);
+    } else {
+      for (int bb = 0; bb < nA; ++bb) {
+        const unsigned n = blk_cnt[bb];
+        const float2* src = cand + (size_t)bb * kPassTokens;
+        for (unsigned c = tid; c < n; c += NT) {
+          const float sv = src[c].x;
+          fn(f32_ord(sv), (unsigned long long)(exp((double)sv - (double)m) * kFxCand));
         }
       }
-      if (lane == 0) {
-        *acc_s = acc_new;
-        *prefix_s = prefix | ((uint32_t)digit << shift);
-        *pmask_s = pmask | (255u << shift);
-      }
     }
-    __syncthreads();
+  };
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  visit([&](uint32_t k, unsigned long long) {
+    if (k) {  // 0 pads the register slots; no finite score maps to it
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
-  return ord_f32(*prefix_s);
+  __shared__ uint32_t rmin[NT / 64], rmax[NT / 64];
+  if (lane == 0) {
+    rmin[wave] = kmin;
+    rmax[wave] = kmax;
+  }
+  __syncthreads();
+  uint32_t lo = rmin[0], hi = rmax[0];
+  for (int q = 1; q < NT / 64; ++q) {
+    lo = min(lo, rmin[q]);
+    hi = max(hi, rmax[q]);
+  }
+  __syncthreads();
+  auto mass_at_least = [&](uint32_t k) {
+    unsigned long long s = 0ull;
+    visit([&](uint32_t kk, unsigned long long w) {
+      if (kk >= k) s += w;
+    });
+    s = wave_sum_u64(s);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    unsigned long long tot = 0ull;
+    for (int q = 0; q < NT / 64; ++q) tot += red[q];
+    __syncthreads();
+    return tot;
+  };
+  // the answer lies in [lo, hi]; every candidate is kept if even the total mass
+  // falls short of need (rounding)
+  while (lo < hi) {
+    const uint32_t mid = lo + (uint32_t)(((unsigned long long)hi - lo + 1ull) >> 1);
+    if ((double)mass_at_least(mid) >= need_fx)
+      lo = mid;
+    else
+      hi = mid - 1u;
+  }
+  return lo;
 }
 
 template <int G>
@@ -579,112 +565,226 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const int pair = unit / G, h = unit % G;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int kv = p.ret_kv[ret_i], qh = kv * G + h;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ TileSmem<1> sm;
-  __shared__ float cs[kCandCap];
-  __shared__ int ct[kCandCap];
-  __shared__ unsigned long long cw[kCandCap];
-  __shared__ unsigned long long dig[256];
-  __shared__ uint32_t prefix_s, pmask_s;
-  __shared__ unsigned long long acc_s;
-  __shared__ int sel_n, chunk_n;
-  __shared__ int sel[kCandCap];
+  __shared__ uint32_t key_s[kCandCap];
+  __shared__ int tok_s[kCandCap];
+  __shared__ unsigned long long w_s[kCandCap];
+  __shared__ unsigned boff[kMaxBlocksLds + 1];
+  __shared__ unsigned long long red[NT / 64];
+  __shared__ unsigned wtot[NT / 64];
+  __shared__ unsigned C_s, nr_s;
 
   const ThrInfo t = p.thr[unit];
-  const unsigned C = (t.mode == 2) ? 0u : p.cand_cnt[unit];
+  const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
   const float2* cand = p.cand + (size_t)unit * p.N;
-  const bool in_lds = C <= (unsigned)kCandCap;
-  if (tid == 0) sel_n = 0;
-  if (in_lds) {
-    for (unsigned c = tid; c < C; c += NT) {
-      const float2 e = cand[c];
-      cs[c] = e.x;
-      ct[c] = __float_as_int(e.y);
-      cw[c] = (unsigned long long)(exp((double)e.x - (double)t.m) * kFxCand);
-    }
-  }
   load_q_rope<1>(sm, p.q_pre + ((size_t)b * p.Hq + qh) * kD, 0, p.N - 1, p.theta,
                  p.attn_scale * kLog2e);
+  // candidate counts of the pass-B blocks and their exclusive prefix (fixed order)
+  const bool small_nA = p.nA <= kMaxBlocksLds;
+  unsigned C = 0u;
+  if (t.mode != 2) {
+    if (small_nA) {
+      const int per = (p.nA + NT - 1) / NT;
+      const int b0 = tid * per, b1 = min(p.nA, b0 + per);
+      unsigned run = 0u;
+      for (int bb = b0; bb < b1; ++bb) {
+        boff[bb] = run;
+        run += blk_cnt[bb];
+      }
+      unsigned inc = run;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+      }
+      if (lane == 63) wtot[wave] = inc;
+      __syncthreads();
+      unsigned base = inc - run;
+      for (int q = 0; q < wave; ++q) base += wtot[q];
+      for (int bb = b0; bb < b1; ++bb) boff[bb] += base;
+      if (tid == NT - 1) C_s = base + run;
+    } else if (tid == 0) {
+      unsigned s = 0u;
+      for (int bb = 0; bb < p.nA; ++bb) s += blk_cnt[bb];
+      C_s = s;
+    }
+    __syncthreads();
+    C = C_s;
+  }
+  const bool in_lds = small_nA && C <= (unsigned)kCandCap;
+  if (in_lds && C > 0) {
+    // gather into LDS in canonical order; each thread copies whole blocks, with
+    // the loads of a block issued together
+    for (int bb = tid; bb < p.nA; bb += NT) {
+      const unsigned n = blk_cnt[bb], o = boff[bb];
+      const float2* src = cand + (size_t)bb * kPassTokens;
+      for (unsigned c0 = 0; c0 < n; c0 += 8) {
+        float2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (c0 + u < n) e[u] = src[c0 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u < n) {
+            key_s[o + c0 + u] = f32_ord(e[u].x);
+            tok_s[o + c0 + u] = __float_as_int(e[u].y);
+            w_s[o + c0 + u] = (unsigned long long)(exp((double)e[u].x - (double)t.m) * kFxCand);
+          }
+        }
+      }
+    }
+  }
   __syncthreads();
+  uint32_t kstar = 0u;
   float tau = -INFINITY;
   if (t.mode != 2) {
-    tau = C ? radix_select_tau<NT>(C, in_lds, cs, cw, cand, t.m, t.need * kFxCand, dig, &prefix_s,
-                                   &pmask_s, &acc_s)
-            : INFINITY;
+    if (C == 0) {
+      tau = INFINITY;
+      kstar = 0xffffffffu;
+    } else {
+      kstar = bisect_key<NT>(C, in_lds, key_s, w_s, cand, blk_cnt, p.nA, t.m, t.need * kFxCand,
+                             red);
+      tau = ord_f32(kstar);
+    }
   }
   if (f == 0 && tid == 0) {
     p.thr[unit].tau = tau;
     p.thr[unit].n_cand = (int)C;
   }
 
-  // selected candidates of this block's token range, attended in token order
-  const int lo = (int)(((long long)p.N * f) / p.nF);
-  const int hi = (int)(((long long)p.N * (f + 1)) / p.nF);
+  // the selected candidates (key >= kstar; sinks excluded, pass B attended them)
+  // of this block's share, in canonical order, 64 at a time
   const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  if (in_lds) {
-    for (unsigned c = tid; c < C; c += NT) {
-      const int tok = ct[c];
-      // sinks were attended in pass B already
-      if (cs[c] >= tau && tok >= lo && tok < hi && tok >= p.n_sink) sel[atomicAdd(&sel_n, 1)] = tok;
-    }
-    __syncthreads();
-    const int n_sel = sel_n;
-    int pw = 1;
-    while (pw < n_sel) pw <<= 1;
-    for (int e = n_sel + tid; e < pw; e += NT) sel[e] = INT_MAX;
-    __syncthreads();
-    for (int k = 2; k <= pw; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int e = tid; e < pw; e += NT) {
-          const int x = e ^ j;
-          if (x > e) {
-            const int a = sel[e], c2 = sel[x];
-            if ((a > c2) == ((e & k) == 0)) {
-              sel[e] = c2;
-              sel[x] = a;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-    for (int t0 = 0; t0 < n_sel; t0 += kTileRows) {
-      const int nr = min(kTileRows, n_sel - t0);
-      if (tid < nr) {
-        sm.rows[tid] = sel[t0 + tid];
-        sm.masks[tid] = 1u;
-      }
-      __syncthreads();
-      tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
-    }
-  } else {
-    // more candidates than LDS holds: walk the list in chunks of 64 (list order)
-    for (unsigned c0 = 0; c0 < C; c0 += kTileRows) {
-      if (tid == 0) chunk_n = 0;
-      __syncthreads();
-      if (tid < kTileRows && c0 + tid < C) {
-        const float2 e = cand[c0 + tid];
-        const int tok = __float_as_int(e.y);
-        if (e.x >= tau && tok >= lo && tok < hi && tok >= p.n_sink) {
-          const int slot = atomicAdd(&chunk_n, 1);
-          sm.rows[slot] = tok;
+  if (C > 0 && in_lds) {
+    const int lo = (int)(((long long)C * f) / p.nF), hi = (int)(((long long)C * (f + 1)) / p.nF);
+    for (int c0 = lo; c0 < hi; c0 += kTileRows) {
+      const int c = c0 + tid;
+      const bool sel = tid < kTileRows && c < hi && key_s[c] >= kstar && tok_s[c] >= p.n_sink;
+      const unsigned long long bal = __ballot(sel);
+      if (wave == 0) {
+        if (sel) {
+          const int slot = __popcll(bal & ((1ull << lane) - 1ull));
+          sm.rows[slot] = tok_s[c];
           sm.masks[slot] = 1u;
         }
+        if (lane == 0) nr_s = (unsigned)__popcll(bal);
       }
       __syncthreads();
-      const int nr = chunk_n;
+      const int nr = (int)nr_s;
       if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
       __syncthreads();
     }
+  } else if (C > 0) {
+    // list too long for LDS: this block walks its range of pass-B blocks
+    const int b_lo = (int)(((long long)p.nA * f) / p.nF);
+    const int b_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
+    for (int bb = b_lo; bb < b_hi; ++bb) {
+      const unsigned n = blk_cnt[bb];
+      const float2* src = cand + (size_t)bb * kPassTokens;
+      for (unsigned c0 = 0; c0 < n; c0 += kTileRows) {
+        bool sel = false;
+        int tok = 0;
+        if (tid < kTileRows && c0 + tid < n) {
+          const float2 e = src[c0 + tid];
+          tok = __float_as_int(e.y);
+          sel = f32_ord(e.x) >= kstar && tok >= p.n_sink;
+        }
+        const unsigned long long bal = __ballot(sel);
+        if (wave == 0) {
+          if (sel) {
+            const int slot = __popcll(bal & ((1ull << lane) - 1ull));
+            sm.rows[slot] = tok;
+            sm.masks[slot] = 1u;
+          }
+          if (lane == 0) nr_s = (unsigned)__popcll(bal);
+        }
+        __syncthreads();
+        const int nr = (int)nr_s;
+        if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+        __syncthreads();
+      }
+    }
   }
-  if (wave == 0) store_partial(p.partF + ((size_t)unit * p.nF + f) * kPartStride, m, l, o0, o1);
-  if (!arrive_last(&p.cntF[unit], (unsigned)p.nF)) return;
   if (wave == 0) {
-    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
-    merge_partials_wave(p.partF + (size_t)unit * p.nF * kPartStride, p.nF, gm, gl, g0, g1);
-    merge_partials_wave(p.partBg + (size_t)unit * p.nGrp * kPartStride, p.nGrp, gm, gl, g0, g1);
-    store_output(p.out + ((size_t)b * p.Hq + qh) * kD, gl, g0, g1);
+    float* dst = p.partF + ((size_t)unit * p.nF + f) * kPartStride;
+    if (lane == 0) {
+      dst[0] = m;
+      dst[1] = l;
+    }
+    *(float2*)&dst[4 + 2 * lane] = make_float2(o0, o1);
+  }
+}
+
+// ------------------------------------------------------------------ merge
+
+// Combine the partial states of one (pair, q-head): nA from pass B and nF from
+// the finish kernel.  Block (unit, chunk) produces kMergeDims output dimensions;
+// thread t folds partials t, t + NT, ... in order, then a fixed butterfly and a
+// fixed sum over waves combine the threads.
+__global__ __launch_bounds__(kMergeThreads) void k_merge(DecPlan p) {
+  constexpr int NT = kMergeThreads;
+  const int unit = blockIdx.x, chunk = blockIdx.y;
+  const int pair = unit / p.G, h = unit % p.G;
+  const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+  const int qh = p.ret_kv[ret_i] * p.G + h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float wm[NT / 64], wl[NT / 64];
+  __shared__ float wo[NT / 64][kMergeDims];
+  const int n = p.nA + p.nF;
+  float M = -INFINITY, L = 0.f, O[kMergeDims];
+#pragma unroll
+  for (int d = 0; d < kMergeDims; ++d) O[d] = 0.f;
+  for (int k = tid; k < n; k += NT) {
+    const float* q = (k < p.nA) ? p.partB + ((size_t)unit * p.nA + k) * kPartStride
+                                : p.partF + ((size_t)unit * p.nF + (k - p.nA)) * kPartStride;
+    const float mk = q[0];
+    if (mk == -INFINITY) continue;
+    const float lk = q[1];
+    const float4 a = *(const float4*)&q[4 + chunk * kMergeDims];
+    const float4 c = *(const float4*)&q[8 + chunk * kMergeDims];
+    const float nm = fmaxf(M, mk);
+    const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
+    const float sk = exp2f(mk - nm);
+    L = L * so + lk * sk;
+    const float ov[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int d = 0; d < kMergeDims; ++d) O[d] = O[d] * so + ov[d] * sk;
+    M = nm;
+  }
+  // butterfly over the wave
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(M, o, 64);
+    const float l2 = __shfl_xor(L, o, 64);
+    const float nm = fmaxf(M, m2);
+    const float s1 = (M == -INFINITY) ? 0.f : exp2f(M - nm);
+    const float s2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - nm);
+    L = L * s1 + l2 * s2;
+#pragma unroll
+    for (int d = 0; d < kMergeDims; ++d) O[d] = O[d] * s1 + __shfl_xor(O[d], o, 64) * s2;
+    M = nm;
+  }
+  if (lane == 0) {
+    wm[wave] = M;
+    wl[wave] = L;
+#pragma unroll
+    for (int d = 0; d < kMergeDims; ++d) wo[wave][d] = O[d];
+  }
+  __syncthreads();
+  if (tid < kMergeDims) {
+    float MM = -INFINITY;
+    for (int q = 0; q < NT / 64; ++q) MM = fmaxf(MM, wm[q]);
+    float LL = 0.f, OO = 0.f;
+    for (int q = 0; q < NT / 64; ++q) {
+      if (wm[q] == -INFINITY) continue;
+      const float sc = exp2f(wm[q] - MM);
+      LL += wl[q] * sc;
+      OO += wo[q][tid] * sc;
+    }
+    p.out[((size_t)b * p.Hq + qh) * kD + chunk * kMergeDims + tid] =
+        f32_to_bf16(LL > 0.f ? OO / LL : 0.f);
   }
 }
 
@@ -751,12 +851,16 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
     if (p.events) (void)hipEventRecord(p.events[k], s);
   };
   mark(0);
-  hipLaunchKernelGGL(k_score_hist<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
+  hipLaunchKernelGGL(k_scan<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
   mark(1);
-  hipLaunchKernelGGL(k_select_attend<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
+  hipLaunchKernelGGL(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), 0, s, p);
   mark(2);
-  hipLaunchKernelGGL(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), 0, s, p);
+  hipLaunchKernelGGL(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
   mark(3);
+  hipLaunchKernelGGL(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), 0, s, p);
+  mark(4);
+  hipLaunchKernelGGL(k_merge, dim3(p.P * G, kD / kMergeDims), dim3(kMergeThreads), 0, s, p);
+  mark(5);
   if (p.dbg_cnt || p.dbg_idx || p.dbg_tau || p.dbg_union)
     hipLaunchKernelGGL(k_debug_sets<G>, dim3(p.P * G), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -777,60 +881,38 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base) {
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
-  int gsz = 8;
-  while (gsz * gsz < nA) ++gsz;
-  if (gsz > kMaxGroup) gsz = kMaxGroup;
-  const int nGrp = (nA + gsz - 1) / gsz;
-  if (nGrp > kMaxGroup) return 0;
-  const int nF = 8;
-  if ((size_t)P * (nGrp + 1) * sizeof(unsigned) > kCounterBytes) return 0;
-  size_t off = kCounterBytes;
+  const int nF = 32;
+  size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += align256(bytes);
     return base ? base + o : nullptr;
   };
-  char* cB = take((size_t)P * nGrp * 4);
-  char* cF = take((size_t)P * G * 4);
-  char* cc = take((size_t)P * G * 4);
+  char* cc = take((size_t)P * G * nA * 4);
   char* uc = take((size_t)P * 4);
   char* qi = take((size_t)P * G * kR * 4);
   char* bm = take((size_t)P * nA * G * 4);
   char* bz = take((size_t)P * nA * G * 8);
   char* bb = take((size_t)P * nA * G * kNB * 4);
-  char* gm = take((size_t)P * nGrp * G * 4);
-  char* gz = take((size_t)P * nGrp * G * 8);
-  char* gb = take((size_t)P * nGrp * G * kNB * 8);
   char* th = take((size_t)P * G * sizeof(ThrInfo));
   char* ca = take((size_t)P * G * N * 8);
   char* un = take((size_t)P * N * 8);
   char* pB = take((size_t)P * G * nA * kPartStride * 4);
-  char* pG = take((size_t)P * G * nGrp * kPartStride * 4);
   char* pF = take((size_t)P * G * nF * kPartStride * 4);
   if (plan) {
     plan->P = P;
     plan->nA = nA;
-    plan->gsz = gsz;
-    plan->nGrp = nGrp;
     plan->nF = nF;
-    plan->cntA_grp = (unsigned*)base;
-    plan->cntA_top = (unsigned*)base + (size_t)P * nGrp;
-    plan->cntB_grp = (unsigned*)cB;
-    plan->cntF = (unsigned*)cF;
-    plan->cand_cnt = (unsigned*)cc;
+    plan->cand_blk = (unsigned*)cc;
     plan->uni_cnt = (unsigned*)uc;
     plan->qi = (float*)qi;
     plan->blk_m = (float*)bm;
     plan->blk_z = (unsigned long long*)bz;
     plan->blk_bins = (unsigned*)bb;
-    plan->grp_m = (float*)gm;
-    plan->grp_z = (double*)gz;
-    plan->grp_bins = (unsigned long long*)gb;
     plan->thr = (ThrInfo*)th;
     plan->cand = (float2*)ca;
     plan->uni = (int2*)un;
     plan->partB = (float*)pB;
-    plan->partBg = (float*)pG;
     plan->partF = (float*)pF;
   }
   return off;

@@ -56,29 +56,20 @@ struct DecPlan {
   // decomposition
   int P;       // B * n_ret pairs
   int nA;      // blocks per pair in the index passes
-  int gsz;     // blocks per merge group
-  int nGrp;    // groups per pair
   int nF;      // finish blocks per (pair, q-head)
-  // workspace: counters (fixed region at the start)
-  unsigned* cntA_grp;  // [P][nGrp]
-  unsigned* cntA_top;  // [P]
-  // workspace: data
-  unsigned* cntB_grp;  // [P][nGrp]    zeroed by pass A
-  unsigned* cntF;      // [P*G]        zeroed by pass A
-  unsigned* cand_cnt;  // [P*G]        zeroed by pass A
-  unsigned* uni_cnt;   // [P]          zeroed by pass A
+  // workspace
+  unsigned* cand_blk;  // [P*G][nA]    candidates of each pass-B block
+  unsigned* uni_cnt;   // [P]          zeroed by the threshold kernel
   float* qi;                      // [P][G][16] (idx_scale folded in)
-  float* blk_m;                   // [P][nA][G]
-  unsigned long long* blk_z;      // [P][nA][G]   Z_b * 2^50 relative to m_b
+  float* blk_m;                   // [P][nA][G]   block max score
+  unsigned long long* blk_z;      // [P][nA][G]   sum exp(s - e_top) * 2^50, e_top the
+                                  //              upper edge of the block max's bin
   unsigned* blk_bins;             // [P][nA][G][kNB]
-  float* grp_m;                   // [P][nGrp][G]
-  double* grp_z;                  // [P][nGrp][G] relative to m_g
-  unsigned long long* grp_bins;   // [P][nGrp][G][kNB]
   ThrInfo* thr;                   // [P][G]
-  float2* cand;                   // [P][G][N]  (score, token id bits)
+  float2* cand;                   // [P][G][N]  (score, token id bits); block b's
+                                  //            candidates start at b * kPassTokens
   int2* uni;                      // [P][N]     debug: (token, definite | candidate << 8)
   float* partB;                   // [P*G][nA][kPartStride]
-  float* partBg;                  // [P*G][nGrp][kPartStride]
   float* partF;                   // [P*G][nF][kPartStride]
   // debug (device pointers or null)
   int32_t* dbg_idx;
