@@ -32,6 +32,43 @@ if ROOT not in sys.path:
 
 METRIC = "sparse decode μs/step + achieved HBM GB/s (% peak) at 128K–1M ctx; prefill tok/s"
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "sparse_attention_long_retrieval_amd", "csrc")
+# Sources that define the scan kernel; its counter summary is void once they change.
+SCAN_SOURCES = ("decode.hip", "rtp_common.h", "rtp_internal.h", "attn_tile.h")
+CALIB_BYTES = 256 << 20   # plain device copy run once per bench for counter calibration
+
+
+def source_digest(names) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per scan launch from the committed counter summary, or None.
+
+    The summary (profiles/traffic_k_scan_<workload>.txt) holds the FETCH_SIZE and
+    WRITE_SIZE readings of the scan kernel already scaled by the plain-copy
+    calibration, and the digest of the sources it was taken on.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_k_scan_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest(SCAN_SOURCES):
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg: str) -> None:
@@ -105,6 +142,12 @@ def main() -> int:
     ws = torch.zeros(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
     wss = torch.zeros(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # plain copy of known size: the reference point for the FETCH_SIZE / WRITE_SIZE counters
+    calib_src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    for _ in range(2):
+        calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
     torch.cuda.synchronize()
     log(f"caches built on the GPU ({time.time() - t0:.1f}s)")
 
@@ -226,7 +269,9 @@ def main() -> int:
         "phases_us": phases_us,
         "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name),
+                     "algorithmic_bytes": bytes_index},
     }
 
     if not args.no_cpu_baseline:

@@ -76,7 +76,8 @@ template <int G>
 __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   constexpr int WQ_VEC = G * kD * kR / 8;           // uint4 of W_q for the pair
-  constexpr int WQ_PER = (WQ_VEC + NT - 1) / NT;
+  constexpr int WQ_PER = WQ_VEC / NT;
+  static_assert(WQ_VEC % NT == 0, "every thread loads the same number of W_q vectors");
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -95,10 +96,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   uint4 wreg[WQ_PER];
   const uint4* wsrc = (const uint4*)(p.w_q + (size_t)ret_i * G * kD * kR);
 #pragma unroll
-  for (int u = 0; u < WQ_PER; ++u) {
-    const int e = u * NT + tid;
-    if (e < WQ_VEC) wreg[u] = wsrc[e];
-  }
+  for (int u = 0; u < WQ_PER; ++u) wreg[u] = wsrc[u * NT + tid];
   uint4 qreg = make_uint4(0, 0, 0, 0);
   const uint4* qsrc = (const uint4*)(p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G) * kD);
   if (tid < G * kD / 8) qreg = qsrc[tid];
@@ -117,10 +115,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < WQ_PER; ++u) {
-    const int e = u * NT + tid;
-    if (e < WQ_VEC) ((uint4*)wq_s)[e] = wreg[u];
-  }
+  for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
   for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
