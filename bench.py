@@ -14,6 +14,13 @@ working set from HBM; HIP events around each step (flush excluded) give the
 step time.  A second pass of K steps records the library's phase events for the
 per-kernel durations used by the roofline.  The CPU oracle is timed on a sample
 of whole steps on the host cores (rank 0, N=1 only).
+The same run also measures the chunked prefill at 256K (a 4096-row chunk
+appended to 262,144 cached keys, 32 q / 8 KV heads, 2 retrieval KV heads,
+6 local heads with window 8192 + 4 sinks, p = 0.9): append of the chunk,
+per-row top-p selection and gather attention of the retrieval heads, and the
+causal window attention of the local heads on MFMA tiles; prefill tok/s is
+4096 / step time.  Its summary goes in the "prefill" field (skip with
+--no-prefill).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -32,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse decode μs/step + achieved HBM GB/s (% peak) at 128K–1M ctx; prefill tok/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "sparse_attention_long_retrieval_amd", "csrc")
 # Sources that define the scan kernel; its counter summary is void once they change.
 SCAN_SOURCES = ("decode.hip", "rtp_common.h", "rtp_internal.h", "attn_tile.h")
@@ -105,20 +113,34 @@ def main() -> int:
     ap.add_argument("--top-p", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-decode", action="store_true", help="prefill only (profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
               "step shards by (batch, KV head) with no exchange, see DESIGN.md)", file=sys.stderr)
         return 2
 
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    res = {} if args.no_decode else decode_leg(args)
+    if not args.no_prefill:
+        res["prefill"] = prefill_leg(args)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def decode_leg(args):
+    """The decode step (headline): returns the JSON fields of the bench line."""
     import numpy as np
     import torch
 
     import sparse_attention_long_retrieval_amd as R
     import workloads as W
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
     t0 = time.time()
     wl = W.make(args.config)
     top_p = args.top_p if args.top_p is not None else wl.top_p[min(1, len(wl.top_p) - 1)]
@@ -276,8 +298,158 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, top_p, args.cpu_seconds)
-    print(json.dumps(res), flush=True)
-    return 0
+    del k_cache, v_cache, index, flush, ws, wss
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_leg(args):
+    """Chunked prefill at 256K: one step = append of the 4096-row chunk, retrieval
+    heads (per-row top-p + gather attention), local heads (causal window attention)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_long_retrieval_amd as R
+    import workloads as W
+
+    t0 = time.time()
+    wl = W.make(5)
+    top_p = wl.top_p[0]
+    B, N, Tq, q0 = wl.B, wl.N, wl.Tq, wl.q_start
+    log(f"prefill workload {wl.name}: N={N} Tq={Tq} ret={wl.ret_kv_heads} generated in "
+        f"{time.time() - t0:.1f}s")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    layer = R.Layer(B, wl.Hq, wl.Hkv, N, wl.ret_kv_heads, wl.n_sink, wl.window, wl.rope_base)
+    k_cache = torch.empty((B, wl.Hkv, N, 128), dtype=torch.int16, device="cuda")
+    v_cache = torch.empty_like(k_cache)
+    index = torch.empty((B, wl.n_ret, N, 16), dtype=torch.int16, device="cuda")
+    w_q, w_k, q = dev(wl.w_q), dev(wl.w_k), dev(wl.q_pre)
+    k_pre, v_pre = dev(wl.k_pre), dev(wl.v)
+    R.index_append(layer, k_pre[:, :, :q0].contiguous(), v_pre[:, :, :q0].contiguous(), w_k, 0,
+                   k_cache, v_cache, index)                      # the cached prefix
+    ck = k_pre[:, :, q0:].contiguous()
+    cv = v_pre[:, :, q0:].contiguous()
+    del k_pre, v_pre
+    out = torch.zeros((B, wl.Hq, Tq, 128), dtype=torch.int16, device="cuda")
+    ws = torch.empty(R.workspace_size(layer, R.OP_PREFILL, N, Tq=Tq), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    main_s = torch.cuda.current_stream()
+    side_s = torch.cuda.Stream()
+    stream = main_s.cuda_stream
+    ph = [hip.event() for _ in range(5)]
+    ex = [hip.event() for _ in range(4)]
+    dbg_ph = R.Debug(0, 0, events=ph)
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def step(mark=False):
+        if mark:
+            hip.record(ex[0], stream)
+        R.index_append(layer, ck, cv, w_k, q0, k_cache, v_cache, index)
+        fork.record(main_s)
+        side_s.wait_event(fork)
+        if mark:
+            hip.record(ex[1], side_s.cuda_stream)
+        R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out, stream=side_s)
+        if mark:
+            hip.record(ex[2], side_s.cuda_stream)
+        join.record(side_s)
+        R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, top_p, out, ws,
+                        debug=dbg_ph if mark else None)
+        main_s.wait_event(join)
+        if mark:
+            hip.record(ex[3], stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    step_ms = []
+    for i in range(args.prefill_steps):
+        flush.fill_(i & 0xFF)
+        hip.record(e0, stream)
+        step()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        step_ms.append(hip.elapsed_ms(e0, e1))
+    names = ["qprep", "index", "resolve", "attend"]
+    phs = {n: [] for n in names + ["append", "swa_local", "retrieval_total", "step"]}
+    for i in range(max(3, args.prefill_steps // 2)):
+        flush.fill_(i & 0xFF)
+        step(mark=True)
+        torch.cuda.synchronize()
+        for k, n in enumerate(names):
+            phs[n].append(hip.elapsed_ms(ph[k], ph[k + 1]))
+        phs["append"].append(hip.elapsed_ms(ex[0], ph[0]))
+        phs["swa_local"].append(hip.elapsed_ms(ex[1], ex[2]))
+        phs["retrieval_total"].append(hip.elapsed_ms(ph[0], ph[4]))
+        phs["step"].append(hip.elapsed_ms(ex[0], ex[3]))
+    phases_ms = {k: round(float(np.median(v)), 4) for k, v in phs.items()}
+    ms = float(np.mean(step_ms))
+    # local heads: causal window attention, 4 D flops (QK + PV) per (row, key) pair
+    n_loc_q = (wl.Hkv - wl.n_ret) * wl.G * B
+    pairs = sum(min(q0 + t + 1, wl.window) + (wl.n_sink if q0 + t + 1 > wl.window else 0)
+                for t in range(Tq))
+    swa_flops = 4.0 * 128 * pairs * n_loc_q
+    swa_tflops = swa_flops / (phases_ms["swa_local"] * 1e-3) / 1e12
+    # retrieval indexer: 2 r = 32 flops per causal (row, key) pair and retrieval q-head
+    ret_pairs = sum(q0 + t + 1 for t in range(Tq)) * wl.n_ret * wl.G * B
+    idx_tflops = 32.0 * ret_pairs / (phases_ms["index"] * 1e-3) / 1e12
+    res = {
+        "workload": wl.name, "context": N, "chunk": Tq, "top_p": top_p,
+        "value": round(Tq * B / (ms * 1e-3), 1), "unit": "tok/s",
+        "ms_per_chunk": round(ms, 4), "steps": args.prefill_steps,
+        "phases_ms": phases_ms,
+        "swa_mfma": {"kernel": "k_swa_prefill (causal window 8192 + 4 sinks, bf16 MFMA)",
+                     "algorithmic_tflop": round(swa_flops / 1e12, 2),
+                     "achieved": round(swa_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(swa_tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "indexer": {"kernel": "k_pf_index (scores on MFMA, mass histogram, selection)",
+                    "pairs": ret_pairs, "algorithmic_tflop": round(32.0 * ret_pairs / 1e12, 3),
+                    "achieved": round(idx_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(idx_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+                    "scores_per_s": round(ret_pairs / (phases_ms["index"] * 1e-3), 1)},
+    }
+    log(f"prefill: {ms:.3f} ms/chunk -> {res['value']:.0f} tok/s; phases {phases_ms}")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(wl, top_p)
+    del k_cache, v_cache, index, flush, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_cpu_baseline(wl, top_p: float, n_rows: int = 6):
+    """The oracle on a sample of chunk rows (every q-head), scaled to the whole chunk."""
+    import numpy as np
+
+    from oracle import rtp_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    t0 = time.time()
+    rows_loc = np.union1d(np.arange(max(0, wl.q_start - wl.window), wl.N),
+                          np.arange(min(wl.n_sink, wl.N)))
+    kc, vc, idx = O.caches_for(wl, rows_needed={kv: rows_loc for kv in range(wl.Hkv)
+                                                 if kv not in wl.ret_kv_heads})
+    log(f"oracle prefill caches built in {time.time() - t0:.1f}s")
+    rows = np.linspace(0, wl.Tq - 1, n_rows).astype(int)
+    t = time.perf_counter()
+    for r in rows:
+        for h in range(wl.Hq):
+            O.prefill_row(wl, kc, vc, idx, 0, h, int(r), top_p)
+    spent = time.perf_counter() - t
+    per_row = spent / len(rows)
+    tok_s = 1.0 / per_row
+    log(f"oracle prefill: {per_row * 1e3:.1f} ms per row (all heads)")
+    return {"value": round(tok_s, 3), "unit": "tok/s", "cores": int(threads),
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{len(rows)} chunk rows spread over the chunk, all {wl.Hq} q-heads each "
+                      f"(append excluded), extrapolated to the {wl.Tq}-row chunk"}
 
 
 def cpu_baseline(wl, top_p: float, budget_s: float):

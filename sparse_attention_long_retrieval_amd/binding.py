@@ -149,6 +149,10 @@ def _p(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -176,7 +180,7 @@ def decode_sparse_attn(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_le
     _check(lib().rtp_decode_sparse_attn(
         layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
         top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
-        _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _p(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def prefill_chunk(layer: Layer, q_pre, q_start: int, w_q, k_cache, v_cache, index,
@@ -189,13 +193,15 @@ def prefill_chunk(layer: Layer, q_pre, q_start: int, w_q, k_cache, v_cache, inde
     _check(lib().rtp_prefill_chunk(
         layer.desc(), _p(q_pre), q_start, Tq, _p(w_q), _p(k_cache), _p(v_cache), _p(index),
         top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
-        _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+        _p(workspace), _nbytes(workspace), _stream(stream)))
 
 
-def swa_attn(layer: Layer, q_pre, q_start: int, Tq: int, k_cache, v_cache, out, workspace,
-             attn_scale: Optional[float] = None, stream=None) -> None:
+def swa_attn(layer: Layer, q_pre, q_start: int, Tq: int, k_cache, v_cache, out,
+             workspace=None, attn_scale: Optional[float] = None, stream=None) -> None:
+    """Local heads.  Tq = 1: decode (q_pre [B][Hq][D], needs a workspace); Tq > 1: causal
+    chunk (q_pre [B][Hq][Tq][D]; no workspace)."""
     if attn_scale is None:
         attn_scale = 1.0 / math.sqrt(layer.head_dim)
     _check(lib().rtp_swa_attn(layer.desc(), _p(q_pre), q_start, Tq, _p(k_cache), _p(v_cache),
-                              attn_scale, _p(out), _p(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream)))
+                              attn_scale, _p(out), _p(workspace), _nbytes(workspace),
+                              _stream(stream)))

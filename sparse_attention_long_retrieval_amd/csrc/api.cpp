@@ -121,8 +121,12 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
       if (*bytes == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
       return RTP_OK;
     case RTP_OP_SWA: {
-      if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
+      if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
       if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+      if (Tq > 1) {  // the chunk kernel keeps its state on chip
+        *bytes = 0;
+        return RTP_OK;
+      }
       int loc[rtp::kMaxKv], n_loc;
       local_heads(desc, loc, &n_loc);
       *bytes = rtp::swa_workspace(desc->batch, n_loc, G, Tq,
@@ -131,7 +135,13 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
       return RTP_OK;
     }
     case RTP_OP_PREFILL:
-      return fail(RTP_ERR_UNSUPPORTED, "rtp_prefill_chunk not available yet");
+      if (Tq < 1 || Tq > seq_len) return fail(RTP_ERR_SHAPE, "Tq %d outside [1, seq_len]", Tq);
+      if (desc->n_ret == 0) {
+        *bytes = 0;
+        return RTP_OK;
+      }
+      *bytes = rtp::prefill_workspace(desc->batch, desc->n_ret, G, Tq, seq_len, nullptr, nullptr);
+      return RTP_OK;
     default: return fail(RTP_ERR_RANGE, "unknown op %d", op);
   }
 }
@@ -242,11 +252,103 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
                              float idx_scale, float attn_scale, rtp_bf16* out,
                              const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
                              void* stream) {
-  (void)q_pre; (void)q_start; (void)Tq; (void)w_q; (void)k_cache; (void)v_cache; (void)index;
-  (void)top_p; (void)idx_scale; (void)attn_scale; (void)out; (void)dbg; (void)workspace;
-  (void)ws_bytes; (void)stream;
   RTP_TRY(check_desc(desc));
-  return fail(RTP_ERR_UNSUPPORTED, "rtp_prefill_chunk not available yet");
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
+  if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
+  if (q_start < 0 || (int64_t)q_start + Tq > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "q_start %d + Tq %d outside max_seq", q_start, Tq);
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(RTP_ERR_RANGE, "top_p must be in (0, 1]");
+  if (!std::isfinite(idx_scale) || !std::isfinite(attn_scale))
+    return fail(RTP_ERR_RANGE, "idx_scale and attn_scale must be finite");
+  if (desc->n_ret == 0) return RTP_OK;
+  if ((int64_t)desc->batch * desc->n_ret * G * Tq > (int64_t)1 << 30)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads * Tq > 2^30");
+  if ((int64_t)desc->batch * desc->n_ret > 65535)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret > 65535");
+  RTP_TRY(check_dev(q_pre, "q_pre"));
+  RTP_TRY(check_dev(k_cache, "k_cache"));
+  RTP_TRY(check_dev(v_cache, "v_cache"));
+  RTP_TRY(check_dev(out, "out"));
+  if (dbg && dbg->sel_idx && dbg->sel_cap < 1) return fail(RTP_ERR_RANGE, "sel_cap < 1");
+  if (dbg && dbg->phase_events && dbg->n_phase_events < 5)
+    return fail(RTP_ERR_RANGE, "prefill records 5 phase events");
+  const int n_keys = q_start + Tq;
+
+  rtp::PfPlan p;
+  memset(&p, 0, sizeof(p));
+  p.q_pre = q_pre;
+  p.w_q = w_q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.index = index;
+  p.out = out;
+  p.B = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.Hkv = desc->n_kv_heads;
+  p.G = G;
+  p.n_ret = desc->n_ret;
+  p.max_seq = desc->max_seq;
+  p.n_sink = desc->n_sink;
+  p.q_start = q_start;
+  p.Tq = Tq;
+  for (int i = 0; i < desc->n_ret; ++i) p.ret_kv[i] = desc->ret_kv_heads[i];
+  p.top_p = top_p;
+  p.idx_scale = idx_scale;
+  p.attn_scale = attn_scale;
+  rope_theta(desc->rope_base, p.theta);
+  p.V = desc->batch * desc->n_ret * G * Tq;
+  if (dbg) {
+    p.dbg_idx = dbg->sel_idx;
+    p.dbg_cnt = dbg->sel_count;
+    p.dbg_tau = dbg->tau;
+    p.dbg_cap = dbg->sel_cap;
+    p.events = dbg->phase_events ? (hipEvent_t*)dbg->phase_events : nullptr;
+  }
+
+  if (top_p >= 1.f) {
+    // every key selected: dense causal attention on the matrix cores
+    if ((int64_t)desc->batch * desc->n_ret * G > 65535)
+      return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > 65535");
+    rtp::SwaPlan d;
+    memset(&d, 0, sizeof(d));
+    d.q_pre = q_pre;
+    d.k_cache = k_cache;
+    d.v_cache = v_cache;
+    d.out = out;
+    d.B = desc->batch;
+    d.Hq = desc->n_q_heads;
+    d.Hkv = desc->n_kv_heads;
+    d.G = G;
+    d.max_seq = desc->max_seq;
+    d.n_sink = desc->n_sink;
+    d.window = n_keys;  // (pos - window, pos] holds every earlier key
+    d.n_loc = desc->n_ret;
+    for (int i = 0; i < desc->n_ret; ++i) d.loc_kv[i] = desc->ret_kv_heads[i];
+    d.attn_scale = attn_scale;
+    memcpy(d.theta, p.theta, sizeof(d.theta));
+    d.q_start = q_start;
+    d.Tq = Tq;
+    if (p.events) hipEventRecord(p.events[0], (hipStream_t)stream);
+    hipError_t e = rtp::launch_swa_prefill(d, (hipStream_t)stream);
+    if (p.events)
+      for (int k = 1; k < 5; ++k) hipEventRecord(p.events[k], (hipStream_t)stream);
+    if (e == hipSuccess && (p.dbg_idx || p.dbg_cnt || p.dbg_tau))
+      e = rtp::launch_prefill_debug_all(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RTP_ERR_HIP, "dense prefill launch: %s", hipGetErrorString(e));
+    return RTP_OK;
+  }
+
+  RTP_TRY(check_dev(w_q, "w_q"));
+  RTP_TRY(check_dev(index, "index"));
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  const size_t need = rtp::prefill_workspace(desc->batch, desc->n_ret, G, Tq, n_keys, nullptr,
+                                             nullptr);
+  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rtp::prefill_workspace(desc->batch, desc->n_ret, G, Tq, n_keys, &p, (char*)workspace);
+  hipError_t e = rtp::launch_prefill(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return RTP_OK;
 }
 
 rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
@@ -268,12 +370,6 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   RTP_TRY(check_dev(k_cache, "k_cache"));
   RTP_TRY(check_dev(v_cache, "v_cache"));
   RTP_TRY(check_dev(out, "out"));
-  RTP_TRY(check_dev(workspace, "workspace", 256));
-  if (Tq != 1) return fail(RTP_ERR_UNSUPPORTED, "rtp_swa_attn: Tq > 1 not available yet");
-  const int rows = swa_rows(q_start, desc->window, desc->n_sink);
-  const size_t need = rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, nullptr, nullptr);
-  if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * local heads too large");
-  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::SwaPlan p;
   memset(&p, 0, sizeof(p));
   p.q_pre = q_pre;
@@ -293,6 +389,18 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   rope_theta(desc->rope_base, p.theta);
   p.q_start = q_start;
   p.Tq = Tq;
+  if (Tq > 1) {
+    if ((int64_t)desc->batch * n_loc * G > 65535)
+      return fail(RTP_ERR_UNSUPPORTED, "batch * local q-heads > 65535");
+    hipError_t e = rtp::launch_swa_prefill(p, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RTP_ERR_HIP, "swa prefill launch: %s", hipGetErrorString(e));
+    return RTP_OK;
+  }
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  const int rows = swa_rows(q_start, desc->window, desc->n_sink);
+  const size_t need = rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, nullptr, nullptr);
+  if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * local heads too large");
+  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::swa_workspace(desc->batch, n_loc, G, Tq, rows, &p, (char*)workspace);
   hipError_t e = rtp::launch_swa_decode(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RTP_ERR_HIP, "swa launch: %s", hipGetErrorString(e));

@@ -112,12 +112,73 @@ struct AppendPlan {
   double theta[kD / 2];
 };
 
+// ------------------------------------------------------------------ chunked prefill
+
+constexpr int kPfVecs = 64;                  // query vectors (row, q-head) per index block
+constexpr int kPfSubLists = 8;               // candidate sub-lists per vector
+constexpr int kPfCandSub = 256;              // candidates per sub-list
+constexpr int kPfLevels = 4;                 // histogram refinements below the first one
+
+// Selection state of one query vector after the index pass.
+enum PfMode : int {
+  kPfNormal = 0,    // definite words + candidates >= tau
+  kPfAll = 1,       // every key <= pos (top_p >= 1)
+  kPfInclusive = 2, // definite words hold the boundary bin too (finest level overflowed)
+  kPfEmpty = 3      // padding vector of the last block
+};
+
+struct PfVec {
+  float m;        // max score over keys <= pos
+  float tau;      // threshold score (normal mode), set by the resolver
+  int mode;
+  int b0;         // integer part of the boundary bin start (depth units, depth = 2 (m - s))
+  float vb;       // fractional part of the boundary bin start
+  float binw;     // boundary bin width (depth units)
+  int n_sel;      // selected candidates (normal mode)
+  int level;
+  double Z;       // sum exp(s - m) over keys <= pos
+  double need;    // top_p * Z minus the mass of the definite keys
+};
+
+struct PfPlan {
+  const uint16_t* q_pre;
+  const uint16_t* w_q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const uint16_t* index;
+  uint16_t* out;
+  int B, Hq, Hkv, G, n_ret, max_seq, n_sink, q_start, Tq;
+  int ret_kv[kMaxKv];
+  float top_p, idx_scale, attn_scale;
+  double theta[kD / 2];
+  int V;       // B * n_ret * G * Tq query vectors, id ((b * n_ret + i) * Tq + row) * G + g
+  int wcap;    // definite words per (vector, wave) list
+  // workspace
+  uint16_t* qsplit;   // [V][3][16] bf16 parts lo, mid, hi of qi (idx_scale folded)
+  PfVec* vec;         // [V]
+  uint2* words;       // [V][4][wcap]  (32-key block, bits of definite keys)
+  int* wcount;        // [V][4]
+  float2* cand;       // [V][8][kPfCandSub]  (score, key bits)
+  int* ccount;        // [V][8]
+  // debug (device pointers or null)
+  int32_t* dbg_idx;
+  int32_t* dbg_cnt;
+  float* dbg_tau;
+  int dbg_cap;
+  hipEvent_t* events;  // phase events or null
+};
+
 // Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base);
 
+size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* plan, char* base);
+
 hipError_t launch_append(const AppendPlan& p, hipStream_t s);
+hipError_t launch_prefill(const PfPlan& p, hipStream_t s);
+hipError_t launch_prefill_debug_all(const PfPlan& p, hipStream_t s);
 hipError_t launch_decode(const DecPlan& p, hipStream_t s);
 hipError_t launch_swa_decode(const SwaPlan& p, hipStream_t s);
+hipError_t launch_swa_prefill(const SwaPlan& p, hipStream_t s);
 
 }  // namespace rtp
