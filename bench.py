@@ -116,6 +116,9 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="prefill only (profiling)")
+    ap.add_argument("--serial-streams", action="store_true",
+                    help="run the local heads on the main stream too (clean per-kernel "
+                         "times under a profiler; the step then does the same work serially)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
@@ -175,7 +178,8 @@ def decode_leg(args):
 
     hip = Hip()
     main_s = torch.cuda.current_stream()
-    side_s = torch.cuda.Stream()          # local heads run beside the retrieval chain
+    # local heads run beside the retrieval chain
+    side_s = main_s if args.serial_streams else torch.cuda.Stream()
     stream = main_s.cuda_stream
     n_ph = 6
     ph_events = [hip.event() for _ in range(n_ph)]
@@ -338,7 +342,7 @@ def prefill_leg(args):
 
     hip = Hip()
     main_s = torch.cuda.current_stream()
-    side_s = torch.cuda.Stream()
+    side_s = main_s if args.serial_streams else torch.cuda.Stream()
     stream = main_s.cuda_stream
     ph = [hip.event() for _ in range(5)]
     ex = [hip.event() for _ in range(4)]

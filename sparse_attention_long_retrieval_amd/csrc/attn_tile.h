@@ -89,7 +89,7 @@ __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kba
     }
     const float tmax = wave_max(logit);
     const float m_new = fmaxf(m, tmax);
-    const float p = valid ? exp2f(logit - m_new) : 0.f;
+    const float p = valid ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
     alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
     l = l * alpha + wave_sum(p);
     sm.ps[h][lane] = p;

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     for (int k = 0; k < TPT; ++k) {
       const float sv = s[k][h];
       if (sv > -INFINITY) {
-        const float wt = exp2f((sv - e_top) * kLog2e);  // <= 1
+        const float wt = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
         z += wt;
         const int j = kt - score_key(sv, kInvDelta);
         if (j < kNB) {

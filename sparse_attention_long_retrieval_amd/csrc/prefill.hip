@@ -17,19 +17,20 @@
 //                 (lane = query vector, 32 keys per step).  Sweeps over the keys:
 //                   A  max score m per vector;
 //                   B  exact mass histogram on the depth coordinate d = 2 (m - s):
-//                      32 bins, weights exp(s - edge) of their bin's upper edge in
-//                      2^-31 fixed point (order-free integer sums), first sweep also
-//                      the tail mass for Z.  The boundary bin is where the running
-//                      mass reaches p * Z; a boundary below the window shifts the
-//                      window down, one with too many keys is refined into 32
-//                      sub-bins (up to 4 levels);
+//                      128 bins of 0.25 (16 score units), weights exp(s - edge) of
+//                      their bin's upper edge in 2^-31 fixed point (order-free
+//                      integer sums), first sweep also the tail mass for Z.  The
+//                      boundary bin is where the running mass reaches p * Z; a
+//                      boundary below the window shifts the window down, one with
+//                      too many keys is refined into 128 sub-bins (up to 2 levels:
+//                      the finest bins are 7.6e-6 score units wide);
 //                   C  definite keys (above the boundary bin) as 32-bit words per
 //                      32-key block, boundary-bin keys as candidates.
 //   k_pf_resolve  exact threshold inside the boundary bin: bisection on the
 //                 ordered fp32 score with 2^-36 fixed-point masses (one wave per
 //                 vector).
-//   k_pf_attend   attention of one query vector over sinks, definite keys and
-//                 candidates >= tau, from LDS-staged K/V tiles.
+//   k_pf_attend   attention of one query vector (one wave) over sinks, definite
+//                 keys and candidates >= tau, 64 gathered rows at a time.
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
@@ -43,7 +44,6 @@ constexpr float kL2e = 1.4426950408889634f;
 constexpr float kFxPf = 2147483648.0f;            // 2^31: histogram weights
 constexpr double kFxPfD = 2147483648.0;
 constexpr double kFxRes = 68719476736.0;          // 2^36: candidate masses
-constexpr int kPfRowBuf = 4096;
 
 __device__ __forceinline__ bf16x8 pf_bf16x8(uint4 v) {
   bf16x8 r;
@@ -95,8 +95,10 @@ struct PfWork {
   double need;
 };
 
-__global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
-  __shared__ unsigned long long bins[kPfVecs][32];
+__global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
+  // one extra column per row: a sink slot for out-of-window lanes (so the update
+  // needs no branch) that also staggers the rows over the banks
+  __shared__ unsigned long long bins[kPfVecs][kPfBins + 1];
   __shared__ float red_m[4][kPfVecs];
   __shared__ double red_z[4][kPfVecs];
   __shared__ PfWork st[kPfVecs];
@@ -159,13 +161,17 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
     const int key = kb + j;
     return key < Nk ? *(const uint4*)(idx + (size_t)key * kR + 8 * hi) : make_uint4(0, 0, 0, 0);
   };
-  // Run fn(kb, acc) over this wave's key blocks with one block of load lookahead.
+  // Run fn(kb, acc) over this wave's key blocks, loads three blocks ahead.
   auto sweep = [&](auto&& fn) {
     if (kw0 >= kw1) return;
-    uint4 nxt = load_a(kw0);
+    uint4 a0 = load_a(kw0);
+    uint4 a1 = kw0 + 32 < kw1 ? load_a(kw0 + 32) : make_uint4(0, 0, 0, 0);
+    uint4 a2 = kw0 + 64 < kw1 ? load_a(kw0 + 64) : make_uint4(0, 0, 0, 0);
     for (int kb = kw0; kb < kw1; kb += 32) {
-      const uint4 cur = nxt;
-      if (kb + 32 < kw1) nxt = load_a(kb + 32);
+      const uint4 cur = a0;
+      a0 = a1;
+      a1 = a2;
+      if (kb + 96 < kw1) a2 = load_a(kb + 96);
       f32x16 acc[2];
       score_block(kb, cur, acc);
       fn(kb, acc);
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
     w.level = 0;
     w.b0 = 0;
     w.v = 0.f;
-    w.binw = 1.f;
+    w.binw = kPfBinW0;
     w.vb = 0.f;
     w.first = 1;
     w.Z = 0.0;
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
 
     if (needB) {
       // ---- sweep B: histogram of the window, tail mass on the first pass
-      for (int e = tid; e < kPfVecs * 32; e += 256) (&bins[0][0])[e] = 0ull;
+      for (int e = tid; e < kPfVecs * (kPfBins + 1); e += 256) (&bins[0][0])[e] = 0ull;
       __syncthreads();
       bool act[2];
       float mm[2], b0f[2], vv[2], ib[2], bw[2];
@@ -256,14 +262,15 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
             const float u = fmaf(s, -2.f, 2.f * mm[c]);
             const float x = (u - b0f[c]) - vv[c];
             const float jf = floorf(x * ib[c]);
-            if (jf >= 0.f && jf < 32.f) {
-              const float sref = mm[c] - 0.5f * (b0f[c] + (vv[c] + jf * bw[c]));
-              const float wgt = exp2f((s - sref) * kL2e);
-              atomicAdd(&bins[32 * c + j][(int)jf],
-                        (unsigned long long)__float2uint_rn(wgt * kFxPf));
-            } else if (first[c] && jf >= 32.f) {
-              tl += exp2f((s - mm[c]) * kL2e);
-            }
+            const bool inwin = jf >= 0.f && jf < (float)kPfBins;
+            // weight relative to the bin's upper edge (window) or to the max (tail);
+            // the exponent is <= 0 and exp2 of anything below -126 may flush to 0
+            const float sref = inwin ? mm[c] - 0.5f * (b0f[c] + (vv[c] + jf * bw[c])) : mm[c];
+            const float wgt = __builtin_amdgcn_exp2f((s - sref) * kL2e);
+            atomicAdd(&bins[32 * c + j][inwin ? (int)jf : kPfBins],
+                      (unsigned long long)(inwin ? (unsigned)(wgt * kFxPf) : 0u));
+            // the first window starts at the max, so nothing lies above it
+            tl += (first[c] && !inwin) ? wgt : 0.f;
           }
           tail[c] += (double)tl;
         }
@@ -280,16 +287,16 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
           const float sref = w.m - 0.5f * ((float)w.b0 + (w.v + (float)q * w.binw));
           return (double)bins[tid][q] / kFxPfD * exp((double)sref - (double)w.m);
         };
-        double tot = 0.0;
-        for (int q = 0; q < 32; ++q) tot += M(q);
         if (w.first) {
+          double tot = 0.0;
+          for (int q = 0; q < kPfBins; ++q) tot += M(q);
           w.Z = tot + ((red_z[0][tid] + red_z[1][tid]) + (red_z[2][tid] + red_z[3][tid]));
           w.first = 0;
         }
         const double pZ = (double)p.top_p * w.Z;
         double cum = w.above;
         int found = -1;
-        for (int q = 0; q < 32; ++q) {
+        for (int q = 0; q < kPfBins; ++q) {
           const double mq = M(q);
           if (cum + mq >= pZ) {
             found = q;
@@ -299,15 +306,15 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
         }
         if (found < 0) {
           if (w.level == 0 && iter < 64) {
-            // the running mass stops short of p * Z inside the window: next 16 units
+            // the running mass stops short of p * Z inside the window: the next one
             w.above = cum;
-            w.b0 += 32;
+            w.b0 += (int)(kPfBins * kPfBinW0);
           } else if (w.level == 0) {
             w.status = kStDone;  // no boundary found after 64 windows: keep every key
             w.mode = kPfAll;
           } else {
             // rounding between a bin and its sub-bins: the last non-empty sub-bin
-            found = 31;
+            found = kPfBins - 1;
             while (found > 0 && bins[tid][found] == 0ull) --found;
             cum = w.above;
             for (int q = 0; q < found; ++q) cum += M(q);
@@ -357,15 +364,16 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
+          const float defb = incl[c] ? bw[c] : 0.f;   // definite: depth below this
+          const float candb = incl[c] ? 0.f : bw[c];  // candidate: depth in [0, candb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float s = acc[c][r];
             const float u = fmaf(s, -2.f, 2.f * mm[c]);
             const float x = (u - b0f[c]) - vb[c];
             const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
-            const bool def = incl[c] ? (x < bw[c]) : (x < 0.f);
-            bits[c] |= (uint32_t)def << bit;
-            if (!incl[c] && x >= 0.f && x < bw[c]) {
+            bits[c] |= (x < defb ? 1u : 0u) << bit;
+            if (x >= 0.f && x < candb) {
               if (ccnt[c] < kPfCandSub)
                 cl[c][ccnt[c]] = make_float2(s, __int_as_float(kb + bit));
               ++ccnt[c];
@@ -402,10 +410,10 @@ __global__ __launch_bounds__(256) void k_pf_index(PfPlan p) {
         if (!ovf[tid]) {
           w.status = kStDone;
         } else if (w.level < kPfLevels) {
-          // refine the boundary bin into 32 sub-bins
+          // refine the boundary bin into kPfBins sub-bins
           w.level += 1;
           w.v = w.vb;
-          w.binw *= (1.f / 32.f);
+          w.binw *= (1.f / kPfBins);
           w.status = kStNeedB;
         } else {
           w.status = kStNeedCIncl;
@@ -530,125 +538,197 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
 
 // ------------------------------------------------------------------ gather attention
 
-__device__ __forceinline__ int block_excl_scan(int x, int* total) {
-  __shared__ int wsum[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    base += w < wave ? wsum[w] : 0;
-    tot += wsum[w];
-  }
-  __syncthreads();
-  *total = tot;
-  return base + incl - x;
+// LDS written by some lanes of a wave and read by others later in the same wave:
+// the wave's LDS instructions execute in order; this keeps the compiler from
+// moving them across the exchange point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+constexpr int kAwBatch = 16;                   // words expanded per batch
+constexpr int kAwQueue = kAwBatch * 32 + 64;   // one batch of words plus a partial tile
+
+// One wave per query vector, four per block, no block-wide barriers.  The wave
+// expands its selection (sinks, definite words, candidates >= tau) into a row
+// queue in LDS and attends it 64 rows at a time.  The rows are gathered from
+// all over the cache (at C5 shapes 5% of them hit L2), so the kernel is bound
+// by random 256 B reads from the Infinity Cache and HBM.
 __global__ __launch_bounds__(256) void k_pf_attend(PfPlan p) {
-  __shared__ TileSmem<1> sm;
-  __shared__ int rowbuf[kPfRowBuf];
-  const int tid = threadIdx.x;
-  const int vid = blockIdx.x;
+  __shared__ float qs[4][kD];
+  __shared__ float ps[4][64];
+  __shared__ int rq[4][kAwQueue];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int vid = blockIdx.x * 4 + wave;
+  if (vid >= p.V) return;  // wave-uniform; the kernel has no block barrier
   const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
   const int b = bi / p.n_ret, ri = bi % p.n_ret;
   const int kv = p.ret_kv[ri], h = kv * p.G + g;
   const int pos = p.q_start + row;
   const PfVec v = p.vec[vid];
+  int* queue = rq[wave];
+  float* qv = qs[wave];
 
-  load_q_rope<1>(sm, p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD, 0, pos, p.theta,
-                 p.attn_scale * kL2e);
+  {  // RoPE'd query, scaled into the log2 domain: lane i rotates dims (i, i + 64)
+    const uint16_t* q = p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
+    double cs, sn;
+    sincos((double)pos * p.theta[lane], &sn, &cs);
+    const double x = (double)bf16_to_f32(q[lane]), y = (double)bf16_to_f32(q[lane + 64]);
+    const float sc = p.attn_scale * kL2e;
+    qv[lane] = (float)(x * cs - y * sn) * sc;
+    qv[lane + 64] = (float)(y * cs + x * sn) * sc;
+  }
+  wave_lds_sync();
+
   const size_t head = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
   const uint16_t* kb = p.k_cache + head;
   const uint16_t* vb = p.v_cache + head;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  int nbuf = 0;  // rows queued in rowbuf (block-uniform)
 
-  // attend rowbuf[0, upto) in tiles of 64 and keep the rest at the front
-  auto flush = [&](bool all) {
-    const int upto = all ? nbuf : nbuf / kTileRows * kTileRows;
-    for (int c = 0; c < upto; c += kTileRows) {
-      const int nr = min(kTileRows, upto - c);
-      __syncthreads();
-      if (tid < nr) {
-        sm.rows[tid] = rowbuf[c + tid];
-        sm.masks[tid] = 1u;
+  // Attend rows[0, n): every load of the tile is issued before the first use, so
+  // a tile costs one memory round trip.  Lane r loads key row r; row ids and
+  // probabilities reach the other lanes through readlane.
+  // Attend rows[0, n): lane r loads key row r (256 B) and computes its logit
+  // against q in LDS; for P.V each lane owns output dims 2 lane, 2 lane + 1 and
+  // reads them from 16 V rows per batch of loads.
+  float* pw = ps[wave];
+  auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
+    float logit = -INFINITY;
+    if (lane < n) {
+      const uint4* kr = (const uint4*)(kb + (size_t)rows[lane] * kD);
+      uint4 kk[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) kk[i] = kr[i];
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 qa = *(const float4*)&qv[8 * i];
+        const float4 qb = *(const float4*)&qv[8 * i + 4];
+        acc = fmaf(qa.x, bf16_lo(kk[i].x), acc);
+        acc = fmaf(qa.y, bf16_hi(kk[i].x), acc);
+        acc = fmaf(qa.z, bf16_lo(kk[i].y), acc);
+        acc = fmaf(qa.w, bf16_hi(kk[i].y), acc);
+        acc = fmaf(qb.x, bf16_lo(kk[i].z), acc);
+        acc = fmaf(qb.y, bf16_hi(kk[i].z), acc);
+        acc = fmaf(qb.z, bf16_lo(kk[i].w), acc);
+        acc = fmaf(qb.w, bf16_hi(kk[i].w), acc);
       }
-      __syncthreads();
-      tile_attend<1, 256>(sm, kb, vb, nr, m, l, o0, o1);
+      logit = acc;
     }
-    const int rest = nbuf - upto;
-    __syncthreads();
-    if (tid < rest) sm.rows[tid] = rowbuf[upto + tid];
-    __syncthreads();
-    if (tid < rest) rowbuf[tid] = sm.rows[tid];
-    __syncthreads();
-    nbuf = rest;
-  };
-  // append the keys [k0, k1) in order
-  auto push_range = [&](int k0, int k1) {
-    for (int c = k0; c < k1; c += 256) {
-      if (nbuf > kPfRowBuf - 256) flush(false);
-      const int n = min(256, k1 - c);
-      if (tid < n) rowbuf[nbuf + tid] = c + tid;
-      nbuf += n;
-      __syncthreads();
+    const float m_new = fmaxf(m, wave_max(logit));
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+    const float pr = lane < n ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
+    l = l * alpha + wave_sum(pr);
+    m = m_new;
+    pw[lane] = pr;
+    wave_lds_sync();
+    o0 *= alpha;
+    o1 *= alpha;
+    for (int r0 = 0; r0 < n; r0 += 16) {
+      uint32_t vv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        vv[u] = r0 + u < n ? *(const uint32_t*)(vb + (size_t)rows[r0 + u] * kD + 2 * lane) : 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float pu = r0 + u < n ? pw[r0 + u] : 0.f;
+        o0 = fmaf(pu, bf16_lo(vv[u]), o0);
+        o1 = fmaf(pu, bf16_hi(vv[u]), o1);
+      }
     }
+    wave_lds_sync();
   };
 
-  // sinks
-  push_range(0, min(p.n_sink, pos + 1));
-  if (v.mode == kPfAll) {
-    push_range(min(p.n_sink, pos + 1), pos + 1);
-  } else if (v.mode == kPfNormal || v.mode == kPfInclusive) {
-    // definite keys: 64 words (<= 2048 keys) per round
-    for (int w = 0; w < 4; ++w) {
-      const int cnt = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
-      const uint2* src = p.words + ((size_t)vid * 4 + w) * p.wcap;
-      for (int e0 = 0; e0 < cnt; e0 += 64) {
-        if (nbuf > kPfRowBuf - 2048) flush(false);
-        uint2 ent = make_uint2(0u, 0u);
-        if (tid < 64 && e0 + tid < cnt) ent = src[e0 + tid];
-        int total;
-        const int off = block_excl_scan(__popc(ent.y), &total);
-        uint32_t bits = ent.y;
-        int o = nbuf + off;
-        while (bits) {
-          const int bit = __ffs(bits) - 1;
-          bits &= bits - 1u;
-          rowbuf[o++] = (int)(ent.x * 32u + (uint32_t)bit);
+  // The selection is produced in batches (at most 16 words = 512 keys) from, in
+  // order: the sinks (every key in keep-all mode), the definite words of the four
+  // wave ranges, the candidates at or above tau.  After each batch the full tiles
+  // of the queue are attended; the last rows once the sources are exhausted.
+  const bool words = v.mode == kPfNormal || v.mode == kPfInclusive;
+  const bool cands = v.mode == kPfNormal;
+  const int rng1 = v.mode == kPfAll ? pos + 1 : min(p.n_sink, pos + 1);
+  int rng0 = 0, src = 0, sub = 0, e0 = 0, nq = 0;
+  bool more = true;
+  while (more || nq > 0) {
+    if (more) {
+      if (src == 0) {
+        if (rng0 < rng1) {
+          const int n = min(64, rng1 - rng0);
+          if (lane < n) queue[nq + lane] = rng0 + lane;
+          nq += n;
+          rng0 += n;
+        } else {
+          src = words ? 1 : 3;
         }
-        nbuf += total;
-        __syncthreads();
+      } else if (src == 1) {
+        const int cnt = sub < 4 ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap) : 0;
+        if (sub == 4) {
+          src = cands ? 2 : 3;
+          sub = 0;
+          e0 = 0;
+        } else if (e0 >= cnt) {
+          ++sub;
+          e0 = 0;
+        } else {
+          const uint2* src_w = p.words + ((size_t)vid * 4 + sub) * p.wcap;
+          const uint2 ent = (lane < kAwBatch && e0 + lane < cnt) ? src_w[e0 + lane]
+                                                                 : make_uint2(0u, 0u);
+          const int c = __popc(ent.y);
+          int incl = c;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+          }
+          int at = nq + incl - c;
+          uint32_t bits = ent.y;
+          while (bits) {
+            const int bit = __ffs(bits) - 1;
+            bits &= bits - 1u;
+            queue[at++] = (int)(ent.x * 32u + (uint32_t)bit);
+          }
+          nq += __shfl(incl, 63, 64);
+          e0 += kAwBatch;
+        }
+      } else if (src == 2) {
+        const int cnt = sub < kPfSubLists ? p.ccount[(size_t)vid * kPfSubLists + sub] : 0;
+        if (sub == kPfSubLists) {
+          src = 3;
+        } else if (e0 >= cnt) {
+          ++sub;
+          e0 = 0;
+        } else {
+          const float2* src_c = p.cand + ((size_t)vid * kPfSubLists + sub) * kPfCandSub;
+          const float2 c = e0 + lane < cnt ? src_c[e0 + lane] : make_float2(-INFINITY, 0.f);
+          const int key = __float_as_int(c.y);
+          const bool sel = e0 + lane < cnt && c.x >= v.tau && key >= p.n_sink;
+          const unsigned long long bal = __ballot(sel);
+          if (sel) queue[nq + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+          nq += __popcll(bal);
+          e0 += 64;
+        }
+      } else {
+        more = false;
       }
+      wave_lds_sync();
     }
-    // candidates at or above the threshold (sinks excluded)
-    if (v.mode == kPfNormal) {
-      for (int sl = 0; sl < kPfSubLists; ++sl) {
-        if (nbuf > kPfRowBuf - 256) flush(false);
-        const int cnt = p.ccount[(size_t)vid * kPfSubLists + sl];
-        const float2* src = p.cand + ((size_t)vid * kPfSubLists + sl) * kPfCandSub;
-        float2 c = make_float2(-INFINITY, 0.f);
-        if (tid < cnt) c = src[tid];
-        const int key = __float_as_int(c.y);
-        const int sel = (tid < cnt && c.x >= v.tau && key >= p.n_sink) ? 1 : 0;
-        int total;
-        const int off = block_excl_scan(sel, &total);
-        if (sel) rowbuf[nbuf + off] = key;
-        nbuf += total;
-        __syncthreads();
-      }
+    int done = 0;
+    while (nq - done >= 64 || (!more && nq > done)) {
+      const int n = min(64, nq - done);
+      tile(queue + done, n);
+      done += n;
     }
+    const int rest = nq - done;
+    const int t = lane < rest ? queue[done + lane] : 0;
+    wave_lds_sync();
+    if (lane < rest) queue[lane] = t;
+    wave_lds_sync();
+    nq = rest;
   }
-  flush(true);
-  if (tid < 64) store_output(p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD, l, o0, o1);
+  uint16_t* dst = p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  *(uint32_t*)&dst[2 * lane] =
+      (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
 }
 
 // ------------------------------------------------------------------ inspection
@@ -745,7 +825,7 @@ __global__ void k_pf_debug_all(PfPlan p) {
 hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
   const int Gv = p.Tq * p.G;
   auto mark = [&](int k) {
-    if (p.events) hipEventRecord(p.events[k], s);
+    if (p.events) (void)hipEventRecord(p.events[k], s);
   };
   mark(0);
   hipLaunchKernelGGL(k_pf_qprep, dim3((p.V * 16 + 255) / 256), dim3(256), 0, s, p);
@@ -755,7 +835,7 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
   mark(2);
   hipLaunchKernelGGL(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
   mark(3);
-  hipLaunchKernelGGL(k_pf_attend, dim3(p.V), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_attend, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
   mark(4);
   if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
     hipLaunchKernelGGL(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), 0, s, p);

@@ -117,7 +117,9 @@ struct AppendPlan {
 constexpr int kPfVecs = 64;                  // query vectors (row, q-head) per index block
 constexpr int kPfSubLists = 8;               // candidate sub-lists per vector
 constexpr int kPfCandSub = 256;              // candidates per sub-list
-constexpr int kPfLevels = 4;                 // histogram refinements below the first one
+constexpr int kPfBins = 128;                 // histogram bins per level
+constexpr float kPfBinW0 = 0.25f;            // first-level bin width, depth units 2 (m - s)
+constexpr int kPfLevels = 2;                 // refinements below the first level
 
 // Selection state of one query vector after the index pass.
 enum PfMode : int {

@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_swa_prefill(SwaPlan p) {
     for (int bk = 0; bk < 2; ++bk) {
       float pv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pv[r] = exp2f(sacc[bk][r] - m_use);
+      for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(sacc[bk][r] - m_use);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         uint32_t w[4];
