@@ -8,10 +8,14 @@ Default workload: 1M-context decode shaped like Qwen3-30B-A3B attention (B=1,
 32 q / 4 KV heads, KV head 0 retrieval with a 1M x 16 index, 3 SWA heads with
 window 8192 + 4 sinks, 512 planted clusters, p = 0.9), synthetic seeded inputs.
 
-Timing: W warm-up steps, then K timed steps.  Before each timed step a 512 MiB
-scratch write flushes the 256 MB Infinity Cache, so every step reads its
-working set from HBM; HIP events around each step (flush excluded) give the
-step time.  A second pass of K steps records the library's phase events for the
+Timing: W warm-up steps, then K timed steps.  Before each timed step a read of
+a 512 MiB scratch buffer evicts the step's working set from the 256 MB Infinity
+Cache and the L2s, so every step reads it from HBM; HIP events around each step
+(flush excluded) give the step time.  The flush reads rather than writes: a
+write leaves ~256 MB of dirty lines whose write-back would stall the next
+kernel's reads (a 32 MiB cold read takes 15 us after a write flush, 8.6 us
+after a read flush on this part), a cost no decode step pays.  A second pass
+of K steps records the library's phase events for the
 per-kernel durations used by the roofline.  The CPU oracle is timed on a sample
 of whole steps on the host cores (rank 0, N=1 only).
 The same run also measures the chunked prefill at 256K (a 4096-row chunk
@@ -77,6 +81,13 @@ def measured_traffic(workload: str):
         return int(float(kv["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def flush_caches(buf) -> None:
+    """Evict the Infinity Cache and L2s by reading a 512 MiB buffer (clean lines),
+    twice: the reads also give the host time to queue the next step behind them."""
+    buf.view(-1).sum()
+    buf.view(-1).sum()
 
 
 def log(msg: str) -> None:
@@ -166,7 +177,7 @@ def decode_leg(args):
     out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
     ws = torch.zeros(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
     wss = torch.zeros(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
     # plain copy of known size: the reference point for the FETCH_SIZE / WRITE_SIZE counters
     calib_src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
     calib_dst = torch.empty_like(calib_src)
@@ -188,20 +199,22 @@ def decode_leg(args):
     fork, join = torch.cuda.Event(), torch.cuda.Event()
 
     def step(debug=None, mark=False):
+        cur = torch.cuda.current_stream()   # the capture stream while recording a graph
+        side = cur if args.serial_streams else side_s
         if mark:
-            hip.record(extra[0], stream)
+            hip.record(extra[0], cur.cuda_stream)
         R.index_append(layer, new_k, new_v, w_k, N - 1, k_cache, v_cache, index)
-        fork.record(main_s)
-        side_s.wait_event(fork)
+        fork.record(cur)
+        side.wait_event(fork)
         if mark:
-            hip.record(extra[1], side_s.cuda_stream)
-        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss, stream=side_s)
+            hip.record(extra[1], side.cuda_stream)
+        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss, stream=side)
         if mark:
-            hip.record(extra[2], side_s.cuda_stream)
-        join.record(side_s)
+            hip.record(extra[2], side.cuda_stream)
+        join.record(side)
         R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws,
                              debug=debug)
-        main_s.wait_event(join)
+        cur.wait_event(join)
 
     for _ in range(args.warmup):
         step()
@@ -213,24 +226,46 @@ def decode_leg(args):
     union = dbg_sets.union_count.cpu().numpy().astype(np.int64)
     set_sizes = dbg_sets.sel_count.cpu().numpy().tolist()
 
-    # ---- headline: K steps, Infinity Cache flushed before each, events around each step
+    # ---- the step captured in a HIP graph (a serving loop may issue it this way)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(main_s)
+    with torch.cuda.stream(cap):
+        step()
+    main_s.wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- headline: K steps, Infinity Cache flushed before each, events around each
+    # step.  The flush is enqueued first, so the step's launches are queued behind it
+    # and the GPU does not wait for the host inside the timed region.
     e0, e1 = hip.event(), hip.event()
-    step_ms = []
+
+    def timed(run, cold=True):
+        out_ms = []
+        for _ in range(args.steps):
+            if cold:
+                flush_caches(flush)
+            hip.record(e0, stream)
+            run()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            out_ms.append(hip.elapsed_ms(e0, e1))
+        return out_ms
+
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        flush.fill_(i & 0xFF)
-        hip.record(e0, stream)
-        step()
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        step_ms.append(hip.elapsed_ms(e0, e1))
-    torch.cuda.synchronize()
+    step_ms = timed(step)
     wall = time.perf_counter() - wall0
+    graph_ms = timed(graph.replay)
     ms = float(np.mean(step_ms))
-    log(f"cold step: mean {ms * 1e3:.1f} us, median {np.median(step_ms) * 1e3:.1f} us")
+    log(f"cold step: mean {ms * 1e3:.1f} us, median {np.median(step_ms) * 1e3:.1f} us; "
+        f"as a graph replay {np.mean(graph_ms) * 1e3:.1f} us")
 
-    # ---- warm: K back-to-back steps without flushing (working set may sit in the MALL)
+    # ---- warm: K back-to-back steps without flushing (working set may sit in the
+    # Infinity Cache)
     torch.cuda.synchronize()
     hip.record(e0, stream)
     for _ in range(args.steps):
@@ -243,7 +278,7 @@ def decode_leg(args):
     names = ["scan", "threshold", "select", "finish", "merge"]
     ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
     for i in range(args.steps):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush)
         step(debug=dbg_ph, mark=True)
         torch.cuda.synchronize()
         for k, n in enumerate(names):
@@ -288,6 +323,10 @@ def decode_leg(args):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "median_us_per_step": round(float(np.median(step_ms)) * 1e3, 2),
+        "graph_us_per_step": round(float(np.mean(graph_ms)) * 1e3, 2),
+        "step_issue": "launched call by call (append, local-head SWA on a second stream, "
+                      "retrieval decode); graph_us_per_step: the same step as one HIP "
+                      "graph replay",
         "wall_s_timed": round(wall, 3),
         "set_sizes": set_sizes,
         "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
@@ -337,7 +376,7 @@ def prefill_leg(args):
     out = torch.zeros((B, wl.Hq, Tq, 128), dtype=torch.int16, device="cuda")
     ws = torch.empty(R.workspace_size(layer, R.OP_PREFILL, N, Tq=Tq), dtype=torch.uint8,
                      device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
     hip = Hip()
@@ -373,7 +412,7 @@ def prefill_leg(args):
     e0, e1 = hip.event(), hip.event()
     step_ms = []
     for i in range(args.prefill_steps):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush)
         hip.record(e0, stream)
         step()
         hip.record(e1, stream)
@@ -382,7 +421,7 @@ def prefill_leg(args):
     names = ["qprep", "index", "resolve", "attend"]
     phs = {n: [] for n in names + ["append", "swa_local", "retrieval_total", "step"]}
     for i in range(max(3, args.prefill_steps // 2)):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush)
         step(mark=True)
         torch.cuda.synchronize()
         for k, n in enumerate(names):

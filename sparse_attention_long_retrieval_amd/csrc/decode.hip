@@ -213,14 +213,33 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float redm[NT / 64];
   __shared__ double redz[NT / 64];
-  __shared__ unsigned long long rows[NT][kNB];
+  // one padding column: the rows of consecutive threads start on different banks
+  __shared__ unsigned long long rows[NT][kNB + 1];
   __shared__ unsigned long long colp[NT / kNB][kNB];
   __shared__ double mass_s[kNB];
 
   if (tid == 0 && h == 0) p.uni_cnt[pair] = 0u;
   const size_t base = (size_t)pair * p.nA;
+  // every summary this thread needs is loaded up front (one round trip)
+  constexpr int kMaxPer = 8;  // blocks per thread held in registers (nA <= 2048)
+  float mbv[kMaxPer];
+  unsigned long long zbv[kMaxPer];
+  int nmine = 0;
   float ml = -INFINITY;
-  for (int k = tid; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u) {
+    const int k = tid + u * NT;
+    mbv[u] = -INFINITY;
+    zbv[u] = 0ull;
+    if (k < p.nA) {
+      const size_t so = (base + k) * G + h;
+      mbv[u] = p.blk_m[so];
+      zbv[u] = p.blk_z[so];
+      ml = fmaxf(ml, mbv[u]);
+      nmine = u + 1;
+    }
+  }
+  for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
   ml = wave_max(ml);
   if (lane == 0) redm[wave] = ml;
 #pragma unroll
@@ -231,12 +250,11 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   const int kt = score_key(m, kInvDelta);
 
   double z = 0.0;
-  for (int k = tid; k < p.nA; k += NT) {
+  auto add_block = [&](int k, float mb, unsigned long long zb) {
     const size_t so = (base + k) * G + h;
-    const float mb = p.blk_m[so];
     const int ktb = score_key(mb, kInvDelta);
     const double e_top_b = (double)(ktb + 1) * (double)kDelta;
-    z += (double)p.blk_z[so] / kFxZ * exp(e_top_b - (double)m);
+    z += (double)zb / kFxZ * exp(e_top_b - (double)m);
     const uint4* src = (const uint4*)(p.blk_bins + so * kNB);
     uint4 v[kNB / 4];
 #pragma unroll
@@ -246,7 +264,12 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
       if (j + shift < kNB) rows[tid][j + shift] += vv[j];
-  }
+  };
+#pragma unroll
+  for (int u = 0; u < kMaxPer; ++u)
+    if (u < nmine) add_block(tid + u * NT, mbv[u], zbv[u]);
+  for (int k = tid + kMaxPer * NT; k < p.nA; k += NT)
+    add_block(k, p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h]);
   z = wave_sum_f64(z);
   if (lane == 0) redz[wave] = z;
   __syncthreads();
@@ -553,6 +576,79 @@ __device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
   return lo;
 }
 
+// The same threshold for candidates held in LDS, digit by digit: four passes over
+// 8-bit digits of the ordered key, from the top.  Each pass builds a 256-bucket
+// histogram of the masses of the candidates that match the digits fixed so far,
+// scans it from the highest digit, and fixes the digit at which the running mass
+// reaches what is still needed.  Integer masses make every pass exact.
+template <int NT>
+__device__ uint32_t radix_key(unsigned C, const uint32_t* key_s, const unsigned long long* w_s,
+                              double need_fx) {
+  static_assert(NT == 256, "one thread per digit");
+  constexpr int CPT = kCandCap / NT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ unsigned long long hist[256];
+  __shared__ unsigned long long wtot[NT / 64];
+  __shared__ uint32_t rmin[NT / 64];
+  __shared__ int dig_s;
+  __shared__ unsigned long long above_s;
+  uint32_t kr[CPT];
+  unsigned long long wr[CPT];
+  uint32_t kmin = 0xffffffffu;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const unsigned c = i * NT + tid;
+    kr[i] = c < C ? key_s[c] : 0u;  // 0: empty slot (no finite score maps to it)
+    wr[i] = c < C ? w_s[c] : 0ull;
+    if (kr[i]) kmin = min(kmin, kr[i]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+  if (lane == 0) rmin[wave] = kmin;
+  double need = need_fx;
+  uint32_t prefix = 0u, pmask = 0u;
+  for (int level = 0; level < 4; ++level) {
+    const int shift = 24 - 8 * level;
+    hist[tid] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (kr[i] && (kr[i] & pmask) == prefix) atomicAdd(&hist[(kr[i] >> shift) & 255u], wr[i]);
+    __syncthreads();
+    // thread t holds digit 255 - t; inclusive running mass from the highest digit
+    const unsigned long long hv = hist[255 - tid];
+    unsigned long long inc = hv;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wtot[wave] = inc;
+    if (tid == 0) dig_s = -1;
+    __syncthreads();
+    for (int q = 0; q < wave; ++q) inc += wtot[q];
+    // the running mass grows with t: the first thread (highest digit) whose running
+    // mass reaches the need is the one whose predecessor's does not
+    if ((double)inc >= need && (double)(inc - hv) < need) {
+      dig_s = 255 - tid;
+      above_s = inc - hv;
+    }
+    __syncthreads();
+    const int d = dig_s;
+    if (d < 0) {
+      // even the whole mass falls short of the need (rounding of p * Z): keep all
+      uint32_t lo = rmin[0];
+      for (int q = 1; q < NT / 64; ++q) lo = min(lo, rmin[q]);
+      return lo;
+    }
+    need -= (double)above_s;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
 template <int G>
 __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   constexpr int NT = kFinishThreads;
@@ -624,7 +720,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
           if (c0 + u < n) {
             key_s[o + c0 + u] = f32_ord(e[u].x);
             tok_s[o + c0 + u] = __float_as_int(e[u].y);
-            w_s[o + c0 + u] = (unsigned long long)(exp((double)e[u].x - (double)t.m) * kFxCand);
+            w_s[o + c0 + u] = (unsigned long long)(
+                (double)__builtin_amdgcn_exp2f((e[u].x - t.m) * kLog2e) * kFxCand);
           }
         }
       }
@@ -638,8 +735,9 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
       tau = INFINITY;
       kstar = 0xffffffffu;
     } else {
-      kstar = bisect_key<NT>(C, in_lds, key_s, w_s, cand, blk_cnt, p.nA, t.m, t.need * kFxCand,
-                             red);
+      kstar = in_lds ? radix_key<NT>(C, key_s, w_s, t.need * kFxCand)
+                     : bisect_key<NT>(C, in_lds, key_s, w_s, cand, blk_cnt, p.nA, t.m,
+                                      t.need * kFxCand, red);
       tau = ord_f32(kstar);
     }
   }

@@ -162,3 +162,64 @@ def test_swa_edges(window, n_sink):
     wl = W.random_decode(45, 1, 8, 2, 1000, [0], window, n_sink=n_sink)
     kc, vc, idx, res = _run(wl, 0.9)
     print(P.compare_decode(wl, kc, vc, idx, res, 0.9))
+
+
+def test_graph_replay_matches_eager():
+    """The whole decode step (append of the newest token, local-head SWA on a second
+    stream, retrieval decode) captured in a HIP graph gives the eager step's output on
+    every replay, with unrelated eager work and synchronizations between replays."""
+    import sparse_attention_long_retrieval_amd as R
+    wl = W.random_decode(46, 1, 16, 4, 30000, [0, 2], 2048, n_needles=2, q_scale=1.5)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx)
+    N = wl.N
+    new_k = P.to_dev(wl.k_pre[:, :, N - 1:N])
+    new_v = P.to_dev(wl.v[:, :, N - 1:N])
+    w_k = P.to_dev(wl.w_k)
+    out = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+    ws = torch.zeros(R.workspace_size(dev.layer, R.OP_DECODE, N), dtype=torch.uint8,
+                     device="cuda")
+    wss = torch.zeros(R.workspace_size(dev.layer, R.OP_SWA, N), dtype=torch.uint8,
+                      device="cuda")
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    def step():
+        cur = torch.cuda.current_stream()
+        R.index_append(dev.layer, new_k, new_v, w_k, N - 1, dev.kc, dev.vc, dev.idx)
+        fork.record(cur)
+        side.wait_event(fork)
+        R.swa_attn(dev.layer, dev.q, N - 1, 1, dev.kc, dev.vc, out, wss, stream=side)
+        join.record(side)
+        R.decode_sparse_attn(dev.layer, dev.q, dev.w_q, dev.kc, dev.vc, dev.idx, N, 0.9, out,
+                             ws)
+        cur.wait_event(join)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    other = torch.zeros_like(out)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager step"
+        # eager work between replays: another decode into another buffer, torch ops
+        R.decode_sparse_attn(dev.layer, dev.q, dev.w_q, dev.kc, dev.vc, dev.idx, N, 0.5,
+                             other, ws)
+        torch.cuda.synchronize()
+        _ = (other.float() * 2).sum().item()
+    # the eager result itself is the oracle's (parity of the step)
+    res = {"out": P.from_dev(out)}
+    ref = O.decode(wl, kc, vc, idx, 0.9)
+    for (b, h), r in ref.items():
+        P.check_out(res["out"][b, h], r["out"], f"graph b{b} h{h}")
