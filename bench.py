@@ -432,12 +432,35 @@ def prefill_leg(args):
         phs["step"].append(hip.elapsed_ms(ex[0], ex[3]))
     phases_ms = {k: round(float(np.median(v)), 4) for k, v in phs.items()}
     ms = float(np.mean(step_ms))
+    # the dense alternative for the retrieval heads: p = 1 selects every key, which the
+    # library runs as causal flash attention on the matrix cores
+    dense_ms = []
+    for i in range(max(3, args.prefill_steps // 2)):
+        flush_caches(flush)
+        hip.record(e0, stream)
+        R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, 1.0, out, ws)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        dense_ms.append(hip.elapsed_ms(e0, e1))
+    dense = float(np.median(dense_ms))
+    # the local heads alone (their kernel otherwise shares the GPU with the retrieval
+    # chain on the second stream)
+    swa_ms = []
+    for i in range(max(3, args.prefill_steps // 2)):
+        flush_caches(flush)
+        hip.record(e0, stream)
+        R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        swa_ms.append(hip.elapsed_ms(e0, e1))
+    phases_ms["swa_local_alone"] = round(float(np.median(swa_ms)), 4)
+    ret_flops = 4.0 * 128 * sum(q0 + t + 1 for t in range(Tq)) * wl.n_ret * wl.G * B
     # local heads: causal window attention, 4 D flops (QK + PV) per (row, key) pair
     n_loc_q = (wl.Hkv - wl.n_ret) * wl.G * B
     pairs = sum(min(q0 + t + 1, wl.window) + (wl.n_sink if q0 + t + 1 > wl.window else 0)
                 for t in range(Tq))
     swa_flops = 4.0 * 128 * pairs * n_loc_q
-    swa_tflops = swa_flops / (phases_ms["swa_local"] * 1e-3) / 1e12
+    swa_tflops = swa_flops / (phases_ms["swa_local_alone"] * 1e-3) / 1e12
     # retrieval indexer: 2 r = 32 flops per causal (row, key) pair and retrieval q-head
     ret_pairs = sum(q0 + t + 1 for t in range(Tq)) * wl.n_ret * wl.G * B
     idx_tflops = 32.0 * ret_pairs / (phases_ms["index"] * 1e-3) / 1e12
@@ -455,6 +478,11 @@ def prefill_leg(args):
                     "achieved": round(idx_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(idx_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
                     "scores_per_s": round(ret_pairs / (phases_ms["index"] * 1e-3), 1)},
+        "dense_retrieval": {"kernel": "k_swa_prefill with the window = context (p = 1)",
+                            "ms": round(dense, 4),
+                            "tflops": round(ret_flops / (dense * 1e-3) / 1e12, 1),
+                            "sparse_retrieval_ms": phases_ms["retrieval_total"],
+                            "dense_over_sparse": round(dense / phases_ms["retrieval_total"], 3)},
     }
     log(f"prefill: {ms:.3f} ms/chunk -> {res['value']:.0f} tok/s; phases {phases_ms}")
     if not args.no_cpu_baseline:
