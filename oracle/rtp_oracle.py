@@ -29,6 +29,7 @@ Steps, in the order the step performs them:
   top_p_set     softmax-normalised mass; smallest highest-scoring set whose mass
                 reaches p ([techwalker] §4; [zhichai] 02 insight three;
                 [v2] finding 4)
+  top_k_set     the fixed-budget baseline: the k highest scores ([techwalker] §4, §7)
   with_sinks    union with the first n_sink tokens ([techwalker] §2 attention
                 sinks, §8: 4 sinks)
   attention     exact 128-dim softmax attention over the chosen rows only
@@ -180,6 +181,23 @@ def top_p_set(s: np.ndarray, p: float) -> Dict[str, object]:
     return {"set": chosen, "tau": tau, "m": mm["m"], "Z": mm["Z"]}
 
 
+def top_k_set(s: np.ndarray, k: int) -> Dict[str, object]:
+    """Fixed top-k budget, the baseline the pages set dynamic top-p against
+    ([techwalker] §4 and §7: a fixed token budget per head; [v2] finding 4).
+
+    Keeps the k highest-scoring keys: tau is the k-th largest score and the set is
+    {j : s_j >= tau}, ties included (the same threshold form as top_p_set).
+    k >= number of keys keeps every key and tau = -inf.
+    """
+    s = np.asarray(s, dtype=np.float32)
+    if k >= len(s):
+        return {"set": np.arange(len(s)), "tau": -np.inf, "m": float(s.max())}
+    order = np.argsort(-s.astype(np.float64), kind="stable")
+    tau = float(s[order[k - 1]])
+    chosen = np.nonzero(s >= np.float32(tau))[0]
+    return {"set": chosen, "tau": tau, "m": float(s.max())}
+
+
 def with_sinks(chosen: np.ndarray, n_sink: int, n_keys: int) -> np.ndarray:
     """S = T u {j < n_sink}, sorted ([techwalker] §2, §8: first tokens always kept)."""
     sinks = np.arange(min(n_sink, n_keys))
@@ -207,17 +225,18 @@ def swa_keys(pos: int, window: int, n_sink: int) -> np.ndarray:
 
 def retrieval_head(q_pre_row, w_q_head, k_cache_head, v_cache_head, index_head, pos: int,
                    top_p: float, n_sink: int, idx_scale: float, attn_scale: float,
-                   rope_base: float = 1e6) -> Dict[str, object]:
-    """One retrieval q-head at query position pos over keys 0..pos."""
+                   rope_base: float = 1e6, top_k: Optional[int] = None) -> Dict[str, object]:
+    """One retrieval q-head at query position pos over keys 0..pos (top-p, or a fixed
+    top-k budget when top_k is given)."""
     n = pos + 1
     qi = query_index(q_pre_row, w_q_head)
     s = scores(qi, index_head[:n], idx_scale)
-    tp = top_p_set(s, top_p)
+    tp = top_p_set(s, top_p) if top_k is None else top_k_set(s, top_k)
     S = with_sinks(tp["set"], n_sink, n)
     qr = rope(bf16_to_f64(q_pre_row), pos, rope_base)
     o = attention(qr, k_cache_head[S], v_cache_head[S], attn_scale)
     return {"out": o, "scores": s, "qi": qi, "T": tp["set"], "S": S, "tau": tp["tau"],
-            "m": tp["m"], "Z": tp["Z"]}
+            "m": tp["m"], "Z": tp.get("Z")}
 
 
 def local_head(q_pre_row, k_cache_head, v_cache_head, pos: int, window: int, n_sink: int,
@@ -228,10 +247,12 @@ def local_head(q_pre_row, k_cache_head, v_cache_head, pos: int, window: int, n_s
 
 
 def decode(wl, k_cache, v_cache, index, top_p: float, heads: Optional[Iterable] = None,
-           batches: Optional[Iterable] = None) -> Dict:
+           batches: Optional[Iterable] = None, top_k: Optional[int] = None) -> Dict:
     """Decode step for a workload: query at position N-1 of every batch row.
 
-    Returns {(b, h): head result} for the requested heads (default: all).
+    Returns {(b, h): head result} for the requested heads (default: all).  With top_k
+    the retrieval heads keep a fixed budget of the top_k highest scores instead of
+    the top-p set.
     """
     G = wl.Hq // wl.Hkv
     pos = wl.N - 1
@@ -245,7 +266,7 @@ def decode(wl, k_cache, v_cache, index, top_p: float, heads: Optional[Iterable] 
                 res[(b, h)] = retrieval_head(
                     wl.q_pre[b, h], wl.w_q[i * G + h % G], k_cache[b, kv], v_cache[b, kv],
                     index[b, i], pos, top_p, wl.n_sink, wl.idx_scale, wl.attn_scale,
-                    wl.rope_base)
+                    wl.rope_base, top_k=top_k)
             else:
                 res[(b, h)] = local_head(wl.q_pre[b, h], k_cache[b, kv], v_cache[b, kv], pos,
                                          wl.window, wl.n_sink, wl.attn_scale, wl.rope_base)

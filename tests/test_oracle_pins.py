@@ -278,3 +278,24 @@ def test_prefill_row_p_one_is_causal_dense():
         ref = _sdpa64(q, K, O.bf16_to_f64(wl.v[0, 0, :pos + 1]), wl.attn_scale)
         assert np.allclose(r["out"], ref, atol=1e-12)
         assert len(r["S"]) == pos + 1
+
+
+# ---------------------------------------------------------------- fixed top-k budget
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_k_is_the_k_largest(seed):
+    """Distinct scores: the set is exactly the k largest, by an independent sort."""
+    rng = np.random.default_rng(300 + seed)
+    s = rng.permutation(np.arange(40, dtype=np.float32) * np.float32(0.37) - np.float32(5))
+    for k in (1, 2, 7, 39, 40, 55):
+        got = np.sort(O.top_k_set(s, k)["set"])
+        want = np.sort(sorted(range(len(s)), key=lambda j: -float(s[j]))[:min(k, len(s))])
+        assert np.array_equal(got, want), k
+
+
+def test_top_k_ties_and_budget_past_n():
+    s = np.array([3, 1, 3, 3, 2, 0], dtype=np.float32)
+    assert np.array_equal(np.sort(O.top_k_set(s, 2)["set"]), [0, 2, 3])  # ties at tau kept
+    assert np.array_equal(np.sort(O.top_k_set(s, 4)["set"]), [0, 2, 3, 4])
+    assert np.array_equal(O.top_k_set(s, 6)["set"], np.arange(6))
+    assert O.top_k_set(s, 9)["tau"] == -np.inf
