@@ -288,6 +288,28 @@ def decode_leg(args):
         ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[5]))
     phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
 
+    # ---- the fixed-budget decode (the pages' ablation baseline) on the same inputs
+    topk_us = {}
+    for kb in (4096, 16384):
+        t_ms = []
+        for i in range(max(5, args.steps // 4)):
+            flush_caches(flush)
+            hip.record(e0, stream)
+            R.decode_topk(layer, q, w_q, k_cache, v_cache, index, N, kb, out, ws)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            t_ms.append(hip.elapsed_ms(e0, e1))
+        topk_us[f"top{kb}_retrieval_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
+    t_ms = []
+    for i in range(max(5, args.steps // 4)):
+        flush_caches(flush)
+        hip.record(e0, stream)
+        R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        t_ms.append(hip.elapsed_ms(e0, e1))
+    topk_us["top_p_retrieval_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
+
     # ---- algorithmic bytes of one step
     n_loc = wl.Hkv - wl.n_ret
     lo = max(0, N - 1 - wl.window + 1)
@@ -332,6 +354,7 @@ def decode_leg(args):
         "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
                        "small": bytes_small, "union_rows": int(union.sum())},
         "phases_us": phases_us,
+        "fixed_budget": topk_us,
         "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -163,6 +163,23 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * rtp_decode_topk - the decode step above with a fixed budget instead of top-p:
+ *   T = the top_k highest-scoring keys, realised as {j : s_j >= tau} with tau the
+ *       top_k-th largest score (ties at tau included); top_k >= seq_len keeps every
+ *       key.  S = T united with the sinks; exact attention over S as above.
+ * The fixed per-head token budget is the baseline the pages compare dynamic top-p
+ * against ([techwalker] §4 and §7; [v2] finding 4).  Arguments, workspace (op
+ * RTP_OP_DECODE) and errors as for rtp_decode_sparse_attn, except top_k: RTP_ERR_RANGE
+ * if top_k < 1.
+ */
+rtp_status rtp_decode_topk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                           const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                           const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                           int32_t top_k, float idx_scale, float attn_scale, rtp_bf16* out,
+                           const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
  * rtp_prefill_chunk - retrieval q-heads of a chunk of Tq query rows at positions
  * q_start .. q_start+Tq-1 (their tokens already appended).  Each row t runs the
  * decode computation above with keys j <= q_start+t (causal): indexer scores,

@@ -23,7 +23,8 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE"
           4: "RTP_ERR_RANGE", 5: "RTP_ERR_UNSUPPORTED", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 EXPORTED = ["rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk", "rtp_swa_attn",
-            "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version"]
+            "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version",
+            "rtp_decode_topk"]
 
 
 class RtpError(RuntimeError):
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_index_append.argtypes = [dp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
         L.rtp_decode_sparse_attn.argtypes = [dp, vp, vp, vp, vp, vp, i32, f32, f32, f32, vp,
                                              ctypes.POINTER(DebugOut), vp, sz, vp]
+        L.rtp_decode_topk.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32, f32, f32, vp,
+                                      ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_prefill_chunk.argtypes = [dp, vp, i32, i32, vp, vp, vp, vp, f32, f32, f32, vp,
                                         ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_swa_attn.argtypes = [dp, vp, i32, i32, vp, vp, f32, vp, vp, sz, vp]
@@ -73,8 +76,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_last_error.argtypes = []
         L.rtp_last_error.restype = ctypes.c_char_p
         L.rtp_abi_version.restype = ctypes.c_int32
-        for name in ("rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk",
-                     "rtp_swa_attn", "rtp_workspace_size"):
+        for name in ("rtp_index_append", "rtp_decode_sparse_attn", "rtp_decode_topk",
+                     "rtp_prefill_chunk", "rtp_swa_attn", "rtp_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -180,6 +183,18 @@ def decode_sparse_attn(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_le
     _check(lib().rtp_decode_sparse_attn(
         layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
         top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
+        _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_topk(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_len: int, top_k: int,
+                out, workspace, idx_scale: float = 1.0, attn_scale: Optional[float] = None,
+                debug: Optional[Debug] = None, stream=None) -> None:
+    """The decode step with a fixed budget of top_k keys per retrieval q-head."""
+    if attn_scale is None:
+        attn_scale = 1.0 / math.sqrt(layer.head_dim)
+    _check(lib().rtp_decode_topk(
+        layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
+        top_k, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
         _p(workspace), _nbytes(workspace), _stream(stream)))
 
 

@@ -182,12 +182,16 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, c
   return RTP_OK;
 }
 
-rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
-                                  const rtp_bf16* w_q, const rtp_bf16* k_cache,
-                                  const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
-                                  float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
-                                  const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
-                                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the top-p and the fixed-budget decode: top_k > 0 selects the budget.
+rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const rtp_bf16* w_q,
+                       const rtp_bf16* k_cache, const rtp_bf16* v_cache, const rtp_bf16* index,
+                       int32_t seq_len, float top_p, int32_t top_k, float idx_scale,
+                       float attn_scale, rtp_bf16* out, const rtp_debug_out* dbg,
+                       void* workspace, size_t ws_bytes, void* stream) {
   RTP_TRY(check_desc(desc));
   const int G = group(desc);
   if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
@@ -229,6 +233,11 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
   p.n_sink = desc->n_sink;
   for (int i = 0; i < desc->n_ret; ++i) p.ret_kv[i] = desc->ret_kv_heads[i];
   p.top_p = top_p;
+  p.budget = 0;
+  if (top_k > 0) {
+    if (top_k >= seq_len) p.top_p = 1.0f;  // the budget covers every key
+    else p.budget = top_k;
+  }
   p.idx_scale = idx_scale;
   p.attn_scale = attn_scale;
   rope_theta(desc->rope_base, p.theta);
@@ -244,6 +253,31 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
   hipError_t e = rtp::launch_decode(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RTP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return RTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                  const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                  const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                                  float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                                  const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, top_p, 0, idx_scale,
+                     attn_scale, out, dbg, workspace, ws_bytes, stream);
+}
+
+rtp_status rtp_decode_topk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                           const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                           const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                           int32_t top_k, float idx_scale, float attn_scale, rtp_bf16* out,
+                           const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (top_k < 1) return fail(RTP_ERR_RANGE, "top_k %d < 1", top_k);
+  return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, 0.5f, top_k,
+                     idx_scale, attn_scale, out, dbg, workspace, ws_bytes, stream);
 }
 
 rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,

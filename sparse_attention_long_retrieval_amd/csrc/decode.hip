@@ -166,6 +166,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   }
   __syncthreads();
 
+  const bool counting = p.budget > 0;  // fixed top-k: every key weighs 1
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int kt = kt_s[h];
@@ -175,12 +176,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     for (int k = 0; k < TPT; ++k) {
       const float sv = s[k][h];
       if (sv > -INFINITY) {
-        const float wt = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
+        const float wt = counting ? 1.f : __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
         z += wt;
         const int j = kt - score_key(sv, kInvDelta);
         if (j < kNB) {
           // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1]
-          const float wb = fminf(wt * bscale[j], 1.0f);
+          const float wb = counting ? 1.f : fminf(wt * bscale[j], 1.0f);
           atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
         }
       }
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
     const size_t so = (base + k) * G + h;
     const int ktb = score_key(mb, kInvDelta);
     const double e_top_b = (double)(ktb + 1) * (double)kDelta;
-    z += (double)zb / kFxZ * exp(e_top_b - (double)m);
+    z += (double)zb / kFxZ * (p.budget > 0 ? 1.0 : exp(e_top_b - (double)m));
     const uint4* src = (const uint4*)(p.blk_bins + so * kNB);
     uint4 v[kNB / 4];
 #pragma unroll
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
     for (int q = 0; q < NT / kNB; ++q) acc += colp[q][tid];
     // bin tid covers key kt - tid; its weights are relative to its upper edge
     mass_s[tid] = (double)acc / (double)kFxBin *
-                  exp((double)(kt - tid + 1) * (double)kDelta - (double)m);
+                  (p.budget > 0 ? 1.0 : exp((double)(kt - tid + 1) * (double)kDelta - (double)m));
   }
   __syncthreads();
   if (tid == 0) {
@@ -304,7 +305,8 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
       t.above = Z;
       t.need = 0.0;
     } else {
-      const double target = (double)p.top_p * Z;
+      // top-p: the mass p * Z; fixed budget: the count (Z is then the key count)
+      const double target = p.budget > 0 ? (double)p.budget : (double)p.top_p * Z;
       double cum = 0.0;
       int g = 0;
       for (; g < kNB; ++g) {
@@ -499,7 +501,7 @@ template <int NT>
 __device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
                                const unsigned long long* w_s, const float2* cand,
                                const unsigned* blk_cnt, int nA, float m, double need_fx,
-                               unsigned long long* red) {
+                               unsigned long long* red, bool counting) {
   constexpr int CPT = kCandCap / NT;  // candidates per thread when they fit in LDS
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint32_t kr[CPT];
@@ -522,7 +524,8 @@ __device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
         const float2* src = cand + (size_t)bb * kPassTokens;
         for (unsigned c = tid; c < n; c += NT) {
           const float sv = src[c].x;
-          fn(f32_ord(sv), (unsigned long long)(exp((double)sv - (double)m) * kFxCand));
+          fn(f32_ord(sv),
+             (unsigned long long)((counting ? 1.0 : exp((double)sv - (double)m)) * kFxCand));
         }
       }
     }
@@ -721,7 +724,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
             key_s[o + c0 + u] = f32_ord(e[u].x);
             tok_s[o + c0 + u] = __float_as_int(e[u].y);
             w_s[o + c0 + u] = (unsigned long long)(
-                (double)__builtin_amdgcn_exp2f((e[u].x - t.m) * kLog2e) * kFxCand);
+                (p.budget > 0 ? 1.0 : (double)__builtin_amdgcn_exp2f((e[u].x - t.m) * kLog2e)) *
+                kFxCand);
           }
         }
       }
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     } else {
       kstar = in_lds ? radix_key<NT>(C, key_s, w_s, t.need * kFxCand)
                      : bisect_key<NT>(C, in_lds, key_s, w_s, cand, blk_cnt, p.nA, t.m,
-                                      t.need * kFxCand, red);
+                                      t.need * kFxCand, red, p.budget > 0);
       tau = ord_f32(kstar);
     }
   }

@@ -52,6 +52,7 @@ struct DecPlan {
   int B, Hq, Hkv, G, n_ret, max_seq, N, n_sink;
   int ret_kv[kMaxKv];
   float top_p, idx_scale, attn_scale;
+  int budget;  // > 0: fixed top-k budget (every key weighs 1, the target is the count)
   double theta[kD / 2];
   // decomposition
   int P;       // B * n_ret pairs

@@ -69,15 +69,19 @@ class Device:
                                                                  device="cuda")
 
     def decode(self, top_p: float, debug_cap: int = 0, idx_scale: float = 1.0, ws=None,
-               wss=None):
+               wss=None, top_k: Optional[int] = None):
         wl = self.wl
         out = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.int16, device="cuda")
         if ws is None:
             ws = torch.zeros(max(256, R.workspace_size(self.layer, R.OP_DECODE, wl.N)),
                              dtype=torch.uint8, device="cuda")
         dbg = R.Debug(wl.B * wl.n_ret * wl.G, debug_cap) if debug_cap else None
-        R.decode_sparse_attn(self.layer, self.q, self.w_q, self.kc, self.vc, self.idx, wl.N,
-                             top_p, out, ws, idx_scale=idx_scale, debug=dbg)
+        if top_k is None:
+            R.decode_sparse_attn(self.layer, self.q, self.w_q, self.kc, self.vc, self.idx, wl.N,
+                                 top_p, out, ws, idx_scale=idx_scale, debug=dbg)
+        else:
+            R.decode_topk(self.layer, self.q, self.w_q, self.kc, self.vc, self.idx, wl.N,
+                          top_k, out, ws, idx_scale=idx_scale, debug=dbg)
         if wss is None:
             wss = torch.zeros(max(256, R.workspace_size(self.layer, R.OP_SWA, wl.N)),
                               dtype=torch.uint8, device="cuda")
@@ -127,6 +131,23 @@ def check_set(S_gpu: np.ndarray, tau_gpu: float, r: Dict, p: float, n_sink: int)
     allowed = np.union1d(T_g, np.arange(min(n_sink, n)))
     assert np.all(np.isin(S_gpu, allowed)), "GPU set holds keys below its threshold"
     return "valid-alt"
+
+
+def check_set_topk(S_gpu: np.ndarray, r: Dict, top_k: int, n_sink: int) -> str:
+    """Fixed budget: the GPU set equals the oracle's except for keys in the band
+    around the oracle's threshold (a count decides, so no mass tolerance applies)."""
+    n = len(r["scores"])
+    if top_k >= n:
+        assert np.array_equal(S_gpu, np.arange(n)), "a budget >= n must keep every key"
+        return "exact"
+    if np.array_equal(S_gpu, r["S"]):
+        return "exact"
+    s = r["scores"].astype(np.float64)
+    tau = float(r["tau"])
+    diff = np.setxor1d(S_gpu, r["S"])
+    assert np.all(np.abs(s[diff] - tau) <= BAND_REL * max(abs(tau), 1.0)), \
+        f"top-{top_k} set differs outside the band: {diff[:8]}"
+    return "band"
 
 
 def check_out(o_gpu_bits: np.ndarray, o_ref: np.ndarray, what: str = "") -> float:

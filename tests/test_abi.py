@@ -110,3 +110,14 @@ def test_append_and_swa_validation():
                             1 << 20, None) == 4
     assert lib.rtp_swa_attn(lay.desc(), FAKE, 5, 1, FAKE, FAKE, 0.088, FAKE, FAKE, 16,
                             None) == 6
+
+
+def test_topk_validation():
+    """rtp_decode_topk rejects a budget below 1 before touching any pointer."""
+    import ctypes
+    import sparse_attention_long_retrieval_amd as R
+    layer = R.Layer(1, 4, 2, 1024, [0])
+    fake = ctypes.c_void_p(0x10000)
+    st = R.lib().rtp_decode_topk(layer.desc(), fake, fake, fake, fake, fake, 100, 0, 1.0,
+                                 0.088, fake, None, fake, 1 << 20, None)
+    assert st == 4  # RTP_ERR_RANGE

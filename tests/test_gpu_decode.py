@@ -223,3 +223,60 @@ def test_graph_replay_matches_eager():
     ref = O.decode(wl, kc, vc, idx, 0.9)
     for (b, h), r in ref.items():
         P.check_out(res["out"][b, h], r["out"], f"graph b{b} h{h}")
+
+
+TOPK_CASES = [
+    # (seed, B, Hq, Hkv, N, ret_kv, window)
+    (51, 1, 4, 2, 4096, [0], 512),
+    (52, 2, 16, 2, 20000, [1], 1000),       # G = 8, B = 2
+    (53, 1, 8, 4, 9000, [0, 3], 700),       # two retrieval heads, G = 2
+]
+
+
+@pytest.mark.parametrize("top_k", [1, 7, 300, 4096, 10 ** 6])
+@pytest.mark.parametrize("case", TOPK_CASES, ids=[f"s{c[0]}" for c in TOPK_CASES])
+def test_decode_topk(case, top_k):
+    """Fixed budget decode: the top_k highest scores plus sinks, against the oracle."""
+    seed, B, Hq, Hkv, N, ret, window = case
+    wl = W.random_decode(seed, B, Hq, Hkv, N, ret, window, n_needles=2, q_scale=1.5)
+    kc, vc, idx = O.caches_for(wl)
+    res = P.Device(wl, kc, vc, idx).decode(0.9, debug_cap=N, top_k=top_k)
+    ref = O.decode(wl, kc, vc, idx, 0.9, top_k=top_k)
+    kinds = {}
+    for (b, h), r in ref.items():
+        kv = h // wl.G
+        if kv not in wl.ret_kv_heads:
+            continue
+        i = wl.ret_kv_heads.index(kv)
+        unit = (b * wl.n_ret + i) * wl.G + h % wl.G
+        S = P.gpu_set(res, unit)
+        kind = P.check_set_topk(S, r, top_k, wl.n_sink)
+        kinds[kind] = kinds.get(kind, 0) + 1
+        qr = O.rope(P.bf16_f64(wl.q_pre[b, h]), N - 1, wl.rope_base)
+        own = O.attention(qr, kc[b, kv][S], vc[b, kv][S], wl.attn_scale)
+        P.check_out(res["out"][b, h], own, f"own set b{b} h{h}")
+        if kind == "exact":
+            P.check_out(res["out"][b, h], r["out"], f"b{b} h{h}")
+    print(f"{wl.name} top-{top_k}: {kinds}")
+
+
+def test_decode_topk_million_budgets():
+    """1M-context decode (512 clusters, 8 retrieval q-heads) with the pages' ablation
+    budgets 4096 and 16384: every set and output against the oracle."""
+    wl = W.make(4)
+    rows = {kv: np.union1d(np.arange(wl.N - wl.window, wl.N), np.arange(wl.n_sink))
+            for kv in range(wl.Hkv) if kv not in wl.ret_kv_heads}
+    kc, vc, idx = O.caches_for(wl, rows_needed=rows)
+    dev = P.Device(wl, kc, vc, idx)
+    for k in (4096, 16384):
+        res = dev.decode(0.9, debug_cap=2 * k, top_k=k)
+        ref = O.decode(wl, kc, vc, idx, 0.9, heads=wl.ret_q_heads(), top_k=k)
+        for (b, h), r in ref.items():
+            unit = (b * wl.n_ret + wl.ret_kv_heads.index(h // wl.G)) * wl.G + h % wl.G
+            S = P.gpu_set(res, unit)
+            kind = P.check_set_topk(S, r, k, wl.n_sink)
+            qr = O.rope(P.bf16_f64(wl.q_pre[b, h]), wl.N - 1, wl.rope_base)
+            own = O.attention(qr, kc[b, h // wl.G][S], vc[b, h // wl.G][S], wl.attn_scale)
+            P.check_out(res["out"][b, h], own, f"top-{k} own set h{h}")
+            if kind == "exact":
+                P.check_out(res["out"][b, h], r["out"], f"top-{k} h{h}")
