@@ -173,6 +173,15 @@ def decode_leg(args):
     R.index_append(layer, k_pre, v_pre, w_k, 0, k_cache, v_cache, index)   # bulk prefill of caches
     new_k = k_pre[:, :, N - 1:N].contiguous()
     new_v = v_pre[:, :, N - 1:N].contiguous()
+    # local heads as a ring of the sinks + the window (rtp_ring_append)
+    ring_len = wl.window
+    n_loc = wl.Hkv - wl.n_ret
+    k_ring = torch.zeros((B, n_loc, wl.n_sink + ring_len, 128), dtype=torch.int16, device="cuda")
+    v_ring = torch.zeros_like(k_ring)
+    R.ring_append(layer, k_pre[:, :, :wl.n_sink].contiguous(), v_pre[:, :, :wl.n_sink].contiguous(),
+                  0, ring_len, k_ring, v_ring)
+    R.ring_append(layer, k_pre[:, :, N - ring_len:].contiguous(),
+                  v_pre[:, :, N - ring_len:].contiguous(), N - ring_len, ring_len, k_ring, v_ring)
     del k_pre, v_pre
     out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
     ws = torch.zeros(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
@@ -310,8 +319,26 @@ def decode_leg(args):
         t_ms.append(hip.elapsed_ms(e0, e1))
     topk_us["top_p_retrieval_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
 
+    # ---- local heads from the ring versus the full cache (same kernel, same rows)
+    ring = {}
+    for name, kk, vv, fn in (("full_cache", k_cache, v_cache, None),
+                             ("ring", k_ring, v_ring, ring_len)):
+        t_ms = []
+        for i in range(max(5, args.steps // 4)):
+            flush_caches(flush)
+            hip.record(e0, stream)
+            if fn is None:
+                R.swa_attn(layer, q, N - 1, 1, kk, vv, out, wss)
+            else:
+                R.swa_attn_ring(layer, q, N - 1, 1, fn, kk, vv, out, wss)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            t_ms.append(hip.elapsed_ms(e0, e1))
+        ring[f"swa_{name}_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
+    ring["local_kv_bytes_full_cache"] = B * n_loc * N * 512
+    ring["local_kv_bytes_ring"] = B * n_loc * (wl.n_sink + ring_len) * 512
+
     # ---- algorithmic bytes of one step
-    n_loc = wl.Hkv - wl.n_ret
     lo = max(0, N - 1 - wl.window + 1)
     swa_rows = min(wl.n_sink, lo) + (N - 1 - lo + 1)
     bytes_index = B * wl.n_ret * N * 32
@@ -355,6 +382,7 @@ def decode_leg(args):
                        "small": bytes_small, "union_rows": int(union.sum())},
         "phases_us": phases_us,
         "fixed_budget": topk_us,
+        "local_ring": ring,
         "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -364,7 +392,7 @@ def decode_leg(args):
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, top_p, args.cpu_seconds)
-    del k_cache, v_cache, index, flush, ws, wss
+    del k_cache, v_cache, index, flush, ws, wss, k_ring, v_ring
     torch.cuda.empty_cache()
     return res
 

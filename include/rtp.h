@@ -214,6 +214,42 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
                         void* stream);
 
 /*
+ * Ring caches for local heads.  A local (streaming) head only ever reads the sinks
+ * and its sliding window ([techwalker] §2 and §8; the "5x KV compression" of the
+ * zhichai summary §02 comes from dropping the rest), so its K/V can live in a ring
+ * instead of the full cache:
+ *   k_ring, v_ring  [B][n_loc][n_sink + ring_len][D] bf16, device, local KV heads
+ *                   in ascending head order (the heads not in ret_kv_heads);
+ *   token j < n_sink sits in row j, token j >= n_sink in row
+ *   n_sink + (j - n_sink) mod ring_len.
+ * Rows hold exactly what rtp_index_append writes to the full cache (post-RoPE K, V).
+ */
+
+/*
+ * rtp_ring_append - write T new tokens at positions start_pos .. start_pos+T-1 of
+ * every local KV head into its ring (retrieval heads are not touched; they keep the
+ * full cache and index through rtp_index_append).
+ *   k_pre, v  [B][Hkv][T][D] bf16, device, read (local heads only)
+ * Errors: RTP_ERR_SHAPE if T < 1; RTP_ERR_RANGE if start_pos < 0 or ring_len < T
+ *   (tokens of one call must land in distinct rows).
+ */
+rtp_status rtp_ring_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre,
+                           const rtp_bf16* v, int32_t start_pos, int32_t T, int32_t ring_len,
+                           rtp_bf16* k_ring, rtp_bf16* v_ring, void* stream);
+
+/*
+ * rtp_swa_attn_ring - rtp_swa_attn reading the local heads' K/V from their rings.
+ * Every key a query row needs must still be in the ring:
+ *   ring_len >= window + Tq - 1  (Tq = 1 for decode).
+ * Outputs are bit-identical to rtp_swa_attn over a full cache holding the same rows.
+ * Errors: as rtp_swa_attn; RTP_ERR_RANGE if ring_len is too short.
+ */
+rtp_status rtp_swa_attn_ring(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                             int32_t q_start, int32_t Tq, int32_t ring_len,
+                             const rtp_bf16* k_ring, const rtp_bf16* v_ring, float attn_scale,
+                             rtp_bf16* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * rtp_workspace_size - bytes of workspace an operation needs.
  *   op = RTP_OP_DECODE (Tq ignored), RTP_OP_PREFILL, RTP_OP_SWA (Tq query rows),
  *   RTP_OP_APPEND (always 0).  seq_len = context length of the call (for prefill

@@ -6,5 +6,6 @@ include/rtp.h); this package only binds it.  Build with
 """
 from .binding import (  # noqa: F401
     OP_APPEND, OP_DECODE, OP_PREFILL, OP_SWA, EXPORTED, LIB_PATH, Debug, Layer, RtpError,
-    decode_sparse_attn, decode_topk, index_append, lib, prefill_chunk, swa_attn, workspace_size,
+    decode_sparse_attn, decode_topk, index_append, lib, prefill_chunk, ring_append, swa_attn,
+    swa_attn_ring, workspace_size,
 )

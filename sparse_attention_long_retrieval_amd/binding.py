@@ -24,7 +24,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE"
 
 EXPORTED = ["rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk", "rtp_swa_attn",
             "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version",
-            "rtp_decode_topk"]
+            "rtp_decode_topk", "rtp_ring_append", "rtp_swa_attn_ring"]
 
 
 class RtpError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_prefill_chunk.argtypes = [dp, vp, i32, i32, vp, vp, vp, vp, f32, f32, f32, vp,
                                         ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_swa_attn.argtypes = [dp, vp, i32, i32, vp, vp, f32, vp, vp, sz, vp]
+        L.rtp_ring_append.argtypes = [dp, vp, vp, i32, i32, i32, vp, vp, vp]
+        L.rtp_swa_attn_ring.argtypes = [dp, vp, i32, i32, i32, vp, vp, f32, vp, vp, sz, vp]
         L.rtp_workspace_size.argtypes = [dp, i32, i32, i32, ctypes.POINTER(sz)]
         L.rtp_status_string.argtypes = [ctypes.c_int]
         L.rtp_status_string.restype = ctypes.c_char_p
@@ -77,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_last_error.restype = ctypes.c_char_p
         L.rtp_abi_version.restype = ctypes.c_int32
         for name in ("rtp_index_append", "rtp_decode_sparse_attn", "rtp_decode_topk",
-                     "rtp_prefill_chunk", "rtp_swa_attn", "rtp_workspace_size"):
+                     "rtp_prefill_chunk", "rtp_swa_attn", "rtp_workspace_size",
+                     "rtp_ring_append", "rtp_swa_attn_ring"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -220,3 +223,21 @@ def swa_attn(layer: Layer, q_pre, q_start: int, Tq: int, k_cache, v_cache, out,
     _check(lib().rtp_swa_attn(layer.desc(), _p(q_pre), q_start, Tq, _p(k_cache), _p(v_cache),
                               attn_scale, _p(out), _p(workspace), _nbytes(workspace),
                               _stream(stream)))
+
+
+def ring_append(layer: Layer, k_pre, v, start_pos: int, ring_len: int, k_ring, v_ring,
+                stream=None) -> None:
+    """Write the new tokens of every local KV head into its ring (see rtp_ring_append)."""
+    T = k_pre.shape[2]
+    _check(lib().rtp_ring_append(layer.desc(), _p(k_pre), _p(v), start_pos, T, ring_len,
+                                 _p(k_ring), _p(v_ring), _stream(stream)))
+
+
+def swa_attn_ring(layer: Layer, q_pre, q_start: int, Tq: int, ring_len: int, k_ring, v_ring,
+                  out, workspace=None, attn_scale: Optional[float] = None, stream=None) -> None:
+    """Local heads reading K/V from their rings (see rtp_swa_attn_ring)."""
+    if attn_scale is None:
+        attn_scale = 1.0 / math.sqrt(layer.head_dim)
+    _check(lib().rtp_swa_attn_ring(layer.desc(), _p(q_pre), q_start, Tq, ring_len, _p(k_ring),
+                                   _p(v_ring), attn_scale, _p(out), _p(workspace),
+                                   _nbytes(workspace), _stream(stream)))

@@ -76,6 +76,22 @@ int swa_rows(int pos, int window, int n_sink) {
   return ns_out + (pos - lo + 1);
 }
 
+rtp::RowMap full_map(const rtp_layer_desc* d) {
+  rtp::RowMap m;
+  m.ring_len = 0;
+  m.n_sink = d->n_sink;
+  m.head_rows = d->max_seq;
+  return m;
+}
+
+rtp::RowMap ring_map(const rtp_layer_desc* d, int ring_len) {
+  rtp::RowMap m;
+  m.ring_len = ring_len;
+  m.n_sink = d->n_sink;
+  m.head_rows = d->n_sink + ring_len;
+  return m;
+}
+
 void local_heads(const rtp_layer_desc* d, int* loc, int* n_loc) {
   int n = 0;
   for (int h = 0; h < d->n_kv_heads; ++h) {
@@ -85,6 +101,10 @@ void local_heads(const rtp_layer_desc* d, int* loc, int* n_loc) {
   }
   *n_loc = n;
 }
+
+rtp_status append_impl(const rtp_layer_desc* desc, const rtp_bf16* k_pre, const rtp_bf16* v,
+                       const rtp_bf16* w_k, int32_t start_pos, int32_t T, rtp::RowMap map,
+                       rtp_bf16* k_cache, rtp_bf16* v_cache, rtp_bf16* index, void* stream);
 
 }  // namespace
 
@@ -161,6 +181,37 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, c
   if (T < 1) return fail(RTP_ERR_SHAPE, "T %d < 1", T);
   if (start_pos < 0 || (int64_t)start_pos + T > desc->max_seq)
     return fail(RTP_ERR_RANGE, "start_pos %d + T %d outside max_seq %d", start_pos, T, desc->max_seq);
+  return append_impl(desc, k_pre, v, w_k, start_pos, T, full_map(desc), k_cache, v_cache, index,
+                     stream);
+}
+
+rtp_status rtp_ring_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, const rtp_bf16* v,
+                           int32_t start_pos, int32_t T, int32_t ring_len, rtp_bf16* k_ring,
+                           rtp_bf16* v_ring, void* stream) {
+  RTP_TRY(check_desc(desc));
+  int loc[rtp::kMaxKv], n_loc;
+  local_heads(desc, loc, &n_loc);
+  if (T < 1) return fail(RTP_ERR_SHAPE, "T %d < 1", T);
+  if (start_pos < 0 || (int64_t)start_pos + T > INT32_MAX)
+    return fail(RTP_ERR_RANGE, "start_pos %d + T %d", start_pos, T);
+  if (ring_len < 1 || T > ring_len)
+    return fail(RTP_ERR_RANGE, "ring_len %d must be >= 1 and >= T %d", ring_len, T);
+  if (n_loc == 0) return RTP_OK;
+  RTP_TRY(check_dev(k_pre, "k_pre"));
+  RTP_TRY(check_dev(v, "v"));
+  RTP_TRY(check_dev(k_ring, "k_ring"));
+  RTP_TRY(check_dev(v_ring, "v_ring"));
+  return append_impl(desc, k_pre, v, nullptr, start_pos, T, ring_map(desc, ring_len), k_ring,
+                     v_ring, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+rtp_status append_impl(const rtp_layer_desc* desc, const rtp_bf16* k_pre, const rtp_bf16* v,
+                       const rtp_bf16* w_k, int32_t start_pos, int32_t T, rtp::RowMap map,
+                       rtp_bf16* k_cache, rtp_bf16* v_cache, rtp_bf16* index, void* stream) {
   rtp::AppendPlan p;
   p.k_pre = k_pre;
   p.v = v;
@@ -175,16 +226,21 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre, c
   p.start_pos = start_pos;
   p.T = T;
   rope_theta(desc->rope_base, p.theta);
-  for (int h = 0; h < rtp::kMaxKv; ++h) p.ret_slot[h] = -1;
-  for (int i = 0; i < desc->n_ret; ++i) p.ret_slot[desc->ret_kv_heads[i]] = i;
+  p.map = map;
+  int loc[rtp::kMaxKv];
+  local_heads(desc, loc, &p.n_loc);
+  for (int h = 0; h < rtp::kMaxKv; ++h) {
+    p.ret_slot[h] = -1;
+    p.loc_idx[h] = -1;
+  }
+  for (int i = 0; i < p.n_loc; ++i) p.loc_idx[loc[i]] = i;
+  // the ring holds local heads only and never an index row
+  if (map.ring_len == 0)
+    for (int i = 0; i < desc->n_ret; ++i) p.ret_slot[desc->ret_kv_heads[i]] = i;
   hipError_t e = rtp::launch_append(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RTP_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return RTP_OK;
 }
-
-}  // extern "C"
-
-namespace {
 
 // Shared by the top-p and the fixed-budget decode: top_k > 0 selects the budget.
 rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const rtp_bf16* w_q,
@@ -357,6 +413,7 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
     d.max_seq = desc->max_seq;
     d.n_sink = desc->n_sink;
     d.window = n_keys;  // (pos - window, pos] holds every earlier key
+    d.map = full_map(desc);
     d.n_loc = desc->n_ret;
     for (int i = 0; i < desc->n_ret; ++i) d.loc_kv[i] = desc->ret_kv_heads[i];
     d.attn_scale = attn_scale;
@@ -385,16 +442,56 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
   return RTP_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+rtp_status swa_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                    int32_t Tq, rtp::RowMap map, const rtp_bf16* k_cache,
+                    const rtp_bf16* v_cache, float attn_scale, rtp_bf16* out, void* workspace,
+                    size_t ws_bytes, void* stream);
+
+}  // namespace
+
+extern "C" {
+
 rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
                         int32_t Tq, const rtp_bf16* k_cache, const rtp_bf16* v_cache,
                         float attn_scale, rtp_bf16* out, void* workspace, size_t ws_bytes,
                         void* stream) {
   RTP_TRY(check_desc(desc));
-  const int G = group(desc);
-  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
   if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
   if (q_start < 0 || (int64_t)q_start + Tq > desc->max_seq)
     return fail(RTP_ERR_RANGE, "q_start %d + Tq %d outside max_seq", q_start, Tq);
+  return swa_impl(desc, q_pre, q_start, Tq, full_map(desc), k_cache, v_cache, attn_scale, out,
+                  workspace, ws_bytes, stream);
+}
+
+rtp_status rtp_swa_attn_ring(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                             int32_t Tq, int32_t ring_len, const rtp_bf16* k_ring,
+                             const rtp_bf16* v_ring, float attn_scale, rtp_bf16* out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  RTP_TRY(check_desc(desc));
+  if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
+  if (q_start < 0 || (int64_t)q_start + Tq > INT32_MAX)
+    return fail(RTP_ERR_RANGE, "q_start %d + Tq %d", q_start, Tq);
+  if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+  if ((int64_t)ring_len < (int64_t)desc->window + Tq - 1)
+    return fail(RTP_ERR_RANGE, "ring_len %d < window %d + Tq %d - 1", ring_len, desc->window, Tq);
+  return swa_impl(desc, q_pre, q_start, Tq, ring_map(desc, ring_len), k_ring, v_ring,
+                  attn_scale, out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+rtp_status swa_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,
+                    int32_t Tq, rtp::RowMap map, const rtp_bf16* k_cache,
+                    const rtp_bf16* v_cache, float attn_scale, rtp_bf16* out, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
   if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
   if (!std::isfinite(attn_scale)) return fail(RTP_ERR_RANGE, "attn_scale must be finite");
   int loc[rtp::kMaxKv], n_loc;
@@ -417,6 +514,7 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   p.max_seq = desc->max_seq;
   p.n_sink = desc->n_sink;
   p.window = desc->window;
+  p.map = map;
   p.n_loc = n_loc;
   for (int i = 0; i < n_loc; ++i) p.loc_kv[i] = loc[i];
   p.attn_scale = attn_scale;
@@ -441,4 +539,4 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
   return RTP_OK;
 }
 
-}  // extern "C"
+}  // namespace

@@ -26,13 +26,15 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AppendPlan p) {
   const int b = bk / p.Hkv;
   const int kv = bk % p.Hkv;
   const int slot = p.ret_slot[kv];
+  const int li = p.loc_idx[kv];
+  if (p.map.ring_len > 0 && li < 0) return;  // the ring holds local heads only
   __shared__ float wk[kD * kR];
   __shared__ uint16_t krow[kAppendTokPerIter][kD];
 
   const int tl = threadIdx.x >> 6;
   const int i = threadIdx.x & 63;
   const size_t src_head = ((size_t)b * p.Hkv + kv) * (size_t)p.T;
-  const size_t dst_head = ((size_t)b * p.Hkv + kv) * (size_t)p.max_seq;
+  const size_t dst_head = p.map.slab(b, kv, li, p.Hkv, p.n_loc);
   const int t_begin = blockIdx.x * kAppendTokPerBlock;
   const int t_end = min(p.T, t_begin + kAppendTokPerBlock);
   bool first = true;
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(AppendPlan p) {
       double c, s;
       sincos((double)pos * p.theta[i], &s, &c);
       const double x = (double)bf16_to_f32(xb), y = (double)bf16_to_f32(yb);
-      uint16_t* kd = p.k_cache + (dst_head + pos) * kD;
-      uint16_t* vd = p.v_cache + (dst_head + pos) * kD;
+      uint16_t* kd = p.k_cache + (dst_head + p.map.row(pos)) * kD;
+      uint16_t* vd = p.v_cache + (dst_head + p.map.row(pos)) * kD;
       kd[i] = f64_to_bf16(x * c - y * s);
       kd[i + 64] = f64_to_bf16(y * c + x * s);
       vd[i] = vx;

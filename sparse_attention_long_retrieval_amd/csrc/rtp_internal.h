@@ -81,12 +81,30 @@ struct DecPlan {
   hipEvent_t* events;  // phase events or null
 };
 
+// Where token j of a (batch, KV head) lives.  ring_len == 0: row j of the full
+// cache, heads max_seq rows apart.  ring_len > 0: a local-head ring of n_sink sink
+// rows followed by ring_len window rows (token j >= n_sink at n_sink + (j - n_sink)
+// mod ring_len), local heads only and compact ([B][n_loc][n_sink + ring_len]).
+struct RowMap {
+  int ring_len;
+  int n_sink;
+  int head_rows;  // rows per (batch, head) slab
+  __host__ __device__ int row(int j) const {
+    return (ring_len == 0 || j < n_sink) ? j : n_sink + (j - n_sink) % ring_len;
+  }
+  // first row of the slab of batch b, KV head kv (local index li)
+  __host__ __device__ size_t slab(int b, int kv, int li, int Hkv, int n_loc) const {
+    return (size_t)(ring_len ? b * n_loc + li : b * Hkv + kv) * (size_t)head_rows;
+  }
+};
+
 struct SwaPlan {
   const uint16_t* q_pre;
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   uint16_t* out;
   int B, Hq, Hkv, G, max_seq, n_sink, window;
+  RowMap map;
   int n_loc;
   int loc_kv[kMaxKv];
   float attn_scale;
@@ -109,6 +127,9 @@ struct AppendPlan {
   uint16_t* v_cache;
   uint16_t* index;
   int B, Hkv, n_ret, max_seq, start_pos, T;
+  RowMap map;            // full cache, or the local-head ring
+  int n_loc;
+  int loc_idx[kMaxKv];   // kv head -> local index, or -1 (ring mode skips those heads)
   int ret_slot[kMaxKv];  // kv head -> retrieval slot or -1
   double theta[kD / 2];
 };

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
   const int pos = p.q_start;
   int lo, ns_out, L;
   swa_rows(pos, p.window, p.n_sink, &lo, &ns_out, &L);
-  const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+  const size_t head_base = p.map.slab(b, kv, li, p.Hkv, p.n_loc) * kD;
   load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, pos, p.theta,
                  p.attn_scale * kLog2eS);
   const int r0 = seg * p.segRows;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
     const int nr = min(kTileRows, r1 - t0);
     if ((int)threadIdx.x < nr) {
       const int v = t0 + threadIdx.x;
-      sm.rows[threadIdx.x] = v < ns_out ? v : lo + (v - ns_out);
+      sm.rows[threadIdx.x] = p.map.row(v < ns_out ? v : lo + (v - ns_out));
       sm.masks[threadIdx.x] = 0xffffffffu;
     }
     __syncthreads();

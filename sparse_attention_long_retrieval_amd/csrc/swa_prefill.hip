@@ -76,7 +76,7 @@ struct TileRegs {
 };
 
 __device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* kb, const uint16_t* vb,
-                                          int k0, int kmax) {
+                                          int k0, int kmax, const RowMap& map) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -84,11 +84,13 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const uint16_t* kb, const
     // K: 16 threads per row (coalesced 256 B rows)
     const int kr = c >> 4, kp = c & 15;
     const int key = k0 + kr;
-    r.k[u] = key <= kmax ? *(const uint4*)(kb + (size_t)key * kD + kp * 8) : make_uint4(0, 0, 0, 0);
+    r.k[u] = key <= kmax ? *(const uint4*)(kb + (size_t)map.row(key) * kD + kp * 8)
+                         : make_uint4(0, 0, 0, 0);
     // V: lane = key, so the transposed LDS writes of a wave are consecutive
     const int vr = c & 63, vp = c >> 6;
     const int vkey = k0 + vr;
-    r.v[u] = vkey <= kmax ? *(const uint4*)(vb + (size_t)vkey * kD + vp * 8) : make_uint4(0, 0, 0, 0);
+    r.v[u] = vkey <= kmax ? *(const uint4*)(vb + (size_t)map.row(vkey) * kD + vp * 8)
+                          : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256) void k_swa_prefill(SwaPlan p) {
     }
   }
 
-  const size_t kvoff = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+  const size_t kvoff = p.map.slab(b, kv, li, p.Hkv, p.n_loc) * kD;
   const uint16_t* kb = p.k_cache + kvoff;
   const uint16_t* vb = p.v_cache + kvoff;
   const TileRange tr = tile_range(p_lo, p_hi, W, p.n_sink);
@@ -191,11 +193,11 @@ __global__ __launch_bounds__(256) void k_swa_prefill(SwaPlan p) {
   };
 
   TileRegs regs;
-  load_tile(regs, kb, vb, tile_k0(0), tile_kmax(0));
+  load_tile(regs, kb, vb, tile_k0(0), tile_kmax(0), p.map);
   for (int t = 0; t < tr.n_tiles; ++t) {
     store_tile(sm, regs);
     __syncthreads();
-    if (t + 1 < tr.n_tiles) load_tile(regs, kb, vb, tile_k0(t + 1), tile_kmax(t + 1));
+    if (t + 1 < tr.n_tiles) load_tile(regs, kb, vb, tile_k0(t + 1), tile_kmax(t + 1), p.map);
     const int k0 = tile_k0(t);
     const bool sink_tile = t < tr.n_sink_tiles;
     // every key of the tile valid for every row of the block?

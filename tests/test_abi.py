@@ -121,3 +121,18 @@ def test_topk_validation():
     st = R.lib().rtp_decode_topk(layer.desc(), fake, fake, fake, fake, fake, 100, 0, 1.0,
                                  0.088, fake, None, fake, 1 << 20, None)
     assert st == 4  # RTP_ERR_RANGE
+
+
+def test_ring_validation():
+    """Ring calls reject a ring too short for the window or the chunk before any launch."""
+    import ctypes
+    import sparse_attention_long_retrieval_amd as R
+    layer = R.Layer(1, 4, 2, 1024, [0], n_sink=4, window=256)
+    fake = ctypes.c_void_p(0x10000)
+    # a 300-row chunk needs ring_len >= 256 + 300 - 1
+    st = R.lib().rtp_swa_attn_ring(layer.desc(), fake, 500, 300, 554, fake, fake, 0.088, fake,
+                                   None, 0, None)
+    assert st == 4
+    # a call writing more tokens than ring rows
+    st = R.lib().rtp_ring_append(layer.desc(), fake, fake, 0, 600, 555, fake, fake, None)
+    assert st == 4
