@@ -46,7 +46,8 @@ struct PassCfg {
 
 constexpr int kThrThreads = 256;
 constexpr int kFinishThreads = 256;
-constexpr int kCandCap = 4096;        // candidates resolved in LDS
+constexpr int kKeyCap = 16384;        // candidate keys resolved from LDS
+constexpr int kTokCap = 8192;         // candidates whose tokens are also kept in LDS
 constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
@@ -86,6 +87,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   __shared__ float mb_s[G];
   __shared__ int kt_s[G];
   __shared__ unsigned bins[G][kNB];
+  __shared__ unsigned binc[G][kNB];  // coarse grid, fixed budget only
+  __shared__ int ktc_s[G];
   __shared__ unsigned long long zred[NW][G];
   __shared__ float bscale[kNB];
   __shared__ __align__(16) uint16_t wq_s[G * kD * kR];
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
-  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
+  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = (&binc[0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
   __syncthreads();
   {
@@ -163,6 +166,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     for (int q = 1; q < NW; ++q) v = fmaxf(v, red_m[q][tid]);
     mb_s[tid] = v;
     kt_s[tid] = score_key(v, kInvDelta);
+    ktc_s[tid] = score_key(v, kInvDeltaCoarse);
   }
   __syncthreads();
 
@@ -184,6 +188,10 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
           const float wb = counting ? 1.f : fminf(wt * bscale[j], 1.0f);
           atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
         }
+        if (counting) {
+          const int jc = ktc_s[h] - score_key(sv, kInvDeltaCoarse);
+          if (jc < kNB) atomicAdd(&binc[h][jc], (unsigned)kFxBin);
+        }
       }
     }
     const unsigned long long zfx = wave_sum_u64((unsigned long long)((double)z * kFxZ));
@@ -198,6 +206,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     p.blk_z[so + tid] = zb;
   }
   for (int e = tid; e < G * kNB; e += NT) p.blk_bins[so * kNB + e] = (&bins[0][0])[e];
+  if (counting)
+    for (int e = tid; e < G * kNB; e += NT) p.blk_bins_c[so * kNB + e] = (&binc[0][0])[e];
 }
 
 // ------------------------------------------------------------------ threshold
@@ -243,82 +253,99 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
   ml = wave_max(ml);
   if (lane == 0) redm[wave] = ml;
-#pragma unroll
-  for (int i = 0; i < kNB; ++i) rows[tid][i] = 0ull;
   __syncthreads();
   float m = redm[0];
   for (int q = 1; q < NT / 64; ++q) m = fmaxf(m, redm[q]);
-  const int kt = score_key(m, kInvDelta);
 
+  const bool counting = p.budget > 0;
+  __shared__ int redo_s;
   double z = 0.0;
-  auto add_block = [&](int k, float mb, unsigned long long zb) {
-    const size_t so = (base + k) * G + h;
-    const int ktb = score_key(mb, kInvDelta);
-    const double e_top_b = (double)(ktb + 1) * (double)kDelta;
-    z += (double)zb / kFxZ * (p.budget > 0 ? 1.0 : exp(e_top_b - (double)m));
-    const uint4* src = (const uint4*)(p.blk_bins + so * kNB);
-    uint4 v[kNB / 4];
+  // round 0: the fine grid; round 1: the coarse grid, for a fixed budget that
+  // the fine grid's window does not reach
+  for (int round = 0; round < 2; ++round) {
+    const float inv = round ? kInvDeltaCoarse : kInvDelta;
+    const unsigned* bins = round ? p.blk_bins_c : p.blk_bins;
+    const int kt = score_key(m, inv);
+    // each thread fills only its own row
 #pragma unroll
-    for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
-    const int shift = kt - ktb;
-    const unsigned* vv = (const unsigned*)v;
-#pragma unroll
-    for (int j = 0; j < kNB; ++j)
-      if (j + shift < kNB) rows[tid][j + shift] += vv[j];
-  };
-#pragma unroll
-  for (int u = 0; u < kMaxPer; ++u)
-    if (u < nmine) add_block(tid + u * NT, mbv[u], zbv[u]);
-  for (int k = tid + kMaxPer * NT; k < p.nA; k += NT)
-    add_block(k, p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h]);
-  z = wave_sum_f64(z);
-  if (lane == 0) redz[wave] = z;
-  __syncthreads();
-  // column sums: thread (part, i) sums kNB rows of column i
-  {
-    const int i = tid % kNB, part = tid / kNB;
-    unsigned long long acc = 0ull;
-    for (int r = part * kNB; r < part * kNB + kNB; ++r) acc += rows[r][i];
-    colp[part][i] = acc;
-  }
-  __syncthreads();
-  if (tid < kNB) {
-    unsigned long long acc = 0ull;
-    for (int q = 0; q < NT / kNB; ++q) acc += colp[q][tid];
-    // bin tid covers key kt - tid; its weights are relative to its upper edge
-    mass_s[tid] = (double)acc / (double)kFxBin *
-                  (p.budget > 0 ? 1.0 : exp((double)(kt - tid + 1) * (double)kDelta - (double)m));
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double Z = 0.0;
-    for (int q = 0; q < NT / 64; ++q) Z += redz[q];
-    ThrInfo t;
-    t.key_top = kt;
-    t.m = m;
-    t.Z = Z;
-    t.tau = -INFINITY;
-    t.n_cand = 0;
-    if (p.top_p >= 1.0f) {
-      t.mode = 2;
-      t.key_bnd = INT_MIN;
-      t.above = Z;
-      t.need = 0.0;
-    } else {
-      // top-p: the mass p * Z; fixed budget: the count (Z is then the key count)
-      const double target = p.budget > 0 ? (double)p.budget : (double)p.top_p * Z;
-      double cum = 0.0;
-      int g = 0;
-      for (; g < kNB; ++g) {
-        if (cum + mass_s[g] >= target) break;
-        cum += mass_s[g];
+    for (int i = 0; i < kNB; ++i) rows[tid][i] = 0ull;
+    auto add_block = [&](int k, float mb, unsigned long long zb) {
+      const size_t so = (base + k) * G + h;
+      const int ktb = score_key(mb, inv);
+      if (round == 0) {
+        const double e_top_b = (double)(ktb + 1) * (double)kDelta;
+        z += (double)zb / kFxZ * (counting ? 1.0 : exp(e_top_b - (double)m));
       }
-      t.mode = g < kNB ? 0 : 1;
-      t.key_bnd = g < kNB ? kt - g : kt - kNB;
-      t.above = cum;
-      t.need = target - cum;
+      const uint4* src = (const uint4*)(bins + so * kNB);
+      uint4 v[kNB / 4];
+#pragma unroll
+      for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
+      const int shift = kt - ktb;
+      const unsigned* vv = (const unsigned*)v;
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+        if (j + shift < kNB) rows[tid][j + shift] += vv[j];
+    };
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u)
+      if (u < nmine) add_block(tid + u * NT, mbv[u], zbv[u]);
+    for (int k = tid + kMaxPer * NT; k < p.nA; k += NT)
+      add_block(k, p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h]);
+    if (round == 0) {
+      z = wave_sum_f64(z);
+      if (lane == 0) redz[wave] = z;
     }
-    p.thr[unit] = t;
+    __syncthreads();
+    // column sums: thread (part, i) sums kNB rows of column i
+    {
+      const int i = tid % kNB, part = tid / kNB;
+      unsigned long long acc = 0ull;
+      for (int r = part * kNB; r < part * kNB + kNB; ++r) acc += rows[r][i];
+      colp[part][i] = acc;
+    }
+    __syncthreads();
+    if (tid < kNB) {
+      unsigned long long acc = 0ull;
+      for (int q = 0; q < NT / kNB; ++q) acc += colp[q][tid];
+      // bin tid covers key kt - tid; its weights are relative to its upper edge
+      mass_s[tid] = (double)acc / (double)kFxBin *
+                    (counting ? 1.0 : exp((double)(kt - tid + 1) * (double)kDelta - (double)m));
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double Z = 0.0;
+      for (int q = 0; q < NT / 64; ++q) Z += redz[q];
+      ThrInfo t;
+      t.key_top = kt;
+      t.m = m;
+      t.Z = Z;
+      t.tau = -INFINITY;
+      t.n_cand = 0;
+      t.inv_w = inv;
+      if (p.top_p >= 1.0f) {
+        t.mode = 2;
+        t.key_bnd = INT_MIN;
+        t.above = Z;
+        t.need = 0.0;
+      } else {
+        // top-p: the mass p * Z; fixed budget: the count (Z is then the key count)
+        const double target = counting ? (double)p.budget : (double)p.top_p * Z;
+        double cum = 0.0;
+        int g = 0;
+        for (; g < kNB; ++g) {
+          if (cum + mass_s[g] >= target) break;
+          cum += mass_s[g];
+        }
+        t.mode = g < kNB ? 0 : 1;
+        t.key_bnd = g < kNB ? kt - g : kt - kNB;
+        t.above = cum;
+        t.need = target - cum;
+      }
+      redo_s = round == 0 && counting && t.mode == 1;
+      if (!redo_s) p.thr[unit] = t;
+    }
+    __syncthreads();
+    if (!redo_s) break;
   }
 }
 
@@ -334,6 +361,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   __shared__ TileSmem<G> sm;
   __shared__ float qi_s[G][kR];
   __shared__ int kb_s[G], mode_s[G];
+  __shared__ float inv_s[G];
   __shared__ int relevant;
   __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned list[kPassTokens];
@@ -346,8 +374,9 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
     const ThrInfo t = p.thr[pair * G + tid];
     kb_s[tid] = t.key_bnd;
     mode_s[tid] = t.mode;
+    inv_s[tid] = t.inv_w;
     const float mb = p.blk_m[((size_t)pair * p.nA + blk) * G + tid];
-    if (t.mode != 0 || score_key(mb, kInvDelta) >= t.key_bnd) atomicOr(&relevant, 1);
+    if (t.mode != 0 || score_key(mb, t.inv_w) >= t.key_bnd) atomicOr(&relevant, 1);
   }
   if (tid < G * kR) (&qi_s[0][0])[tid] = p.qi[(size_t)pair * G * kR + tid];
   __syncthreads();
@@ -381,13 +410,14 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
 #pragma unroll
       for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
       const int mode = mode_s[h], kb = kb_s[h];
+      const float inv = inv_s[h];
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int t = tok0 + k * NT + tid;
         if (t < p.N) {
           const float sv = idx_score(w[k], q);
           s[k][h] = sv;
-          const int key = score_key(sv, kInvDelta);
+          const int key = score_key(sv, inv);
           if (mode == 2 || key > kb) dm[k] |= 1u << h;
           else if ((mode == 0 && key == kb) || (mode == 1 && key <= kb)) cm[k] |= 1u << h;
         } else {
@@ -495,47 +525,29 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
 // Exact threshold inside the boundary bin by bisection on the ordered fp32 key:
 // the largest key k with mass{candidates with key >= k} >= need.  Masses are
 // 2^36 fixed point relative to the global max, summed over the block as
-// integers (exact, order free).  All NT threads call it; the candidate keys and
-// weights come from LDS (in_lds) or are recomputed from the global list.
+// integers (exact, order free).  All NT threads call it; it serves candidate
+// lists whose pass-B block offsets do not fit in LDS, walking the blocks' regions.
 template <int NT>
-__device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
-                               const unsigned long long* w_s, const float2* cand,
-                               const unsigned* blk_cnt, int nA, float m, double need_fx,
-                               unsigned long long* red, bool counting) {
-  constexpr int CPT = kCandCap / NT;  // candidates per thread when they fit in LDS
+__device__ uint32_t bisect_key(unsigned C, const float2* cand, const unsigned* blk_cnt, int nA,
+                               float m, double need_fx, unsigned long long* red, bool counting) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint32_t kr[CPT];
-  unsigned long long wr[CPT];
-  if (in_lds) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const unsigned c = i * NT + tid;
-      kr[i] = c < C ? key_s[c] : 0u;
-      wr[i] = c < C ? w_s[c] : 0ull;
-    }
-  }
   auto visit = [&](auto&& fn) {
-    if (in_lds) {
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) fn(kr[i], wr[i]);
-    } else {
-      for (int bb = 0; bb < nA; ++bb) {
-        const unsigned n = blk_cnt[bb];
-        const float2* src = cand + (size_t)bb * kPassTokens;
-        for (unsigned c = tid; c < n; c += NT) {
-          const float sv = src[c].x;
-          fn(f32_ord(sv),
-             (unsigned long long)((counting ? 1.0 : exp((double)sv - (double)m)) * kFxCand));
-        }
+    for (int bb = 0; bb < nA; ++bb) {
+      const unsigned n = blk_cnt[bb];
+      const float2* src = cand + (size_t)bb * kPassTokens;
+      for (unsigned c = tid; c < n; c += NT) {
+        const float sv = src[c].x;
+        fn(f32_ord(sv),
+           (unsigned long long)((counting ? 1.0
+                                          : (double)__builtin_amdgcn_exp2f((sv - m) * kLog2e)) *
+                                kFxCand));
       }
     }
   };
   uint32_t kmin = 0xffffffffu, kmax = 0u;
   visit([&](uint32_t k, unsigned long long) {
-    if (k) {  // 0 pads the register slots; no finite score maps to it
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
-    }
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
   });
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -579,44 +591,56 @@ __device__ uint32_t bisect_key(unsigned C, bool in_lds, const uint32_t* key_s,
   return lo;
 }
 
-// The same threshold for candidates held in LDS, digit by digit: four passes over
-// 8-bit digits of the ordered key, from the top.  Each pass builds a 256-bucket
-// histogram of the masses of the candidates that match the digits fixed so far,
+// The same threshold digit by digit.  The keys' common leading bits are fixed
+// first; the rest are resolved in digits of up to 8 bits from the highest
+// differing bit down (at most four passes).  Each pass builds a 256-bucket
+// histogram of the masses of the candidates that match the bits fixed so far,
 // scans it from the highest digit, and fixes the digit at which the running mass
-// reaches what is still needed.  Integer masses make every pass exact.
-template <int NT>
-__device__ uint32_t radix_key(unsigned C, const uint32_t* key_s, const unsigned long long* w_s,
-                              double need_fx) {
+// reaches what is still needed.  Integer masses make every pass exact.  visit(fn)
+// calls fn(key, mass) once for every candidate the calling thread owns.
+template <int NT, class Visit>
+__device__ uint32_t radix_key(Visit&& visit, double need_fx) {
   static_assert(NT == 256, "one thread per digit");
-  constexpr int CPT = kCandCap / NT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ unsigned long long hist[256];
   __shared__ unsigned long long wtot[NT / 64];
-  __shared__ uint32_t rmin[NT / 64];
+  __shared__ uint32_t rmin[NT / 64], rmax[NT / 64];
   __shared__ int dig_s;
   __shared__ unsigned long long above_s;
-  uint32_t kr[CPT];
-  unsigned long long wr[CPT];
-  uint32_t kmin = 0xffffffffu;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  visit([&](uint32_t k, unsigned long long) {
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  });
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const unsigned c = i * NT + tid;
-    kr[i] = c < C ? key_s[c] : 0u;  // 0: empty slot (no finite score maps to it)
-    wr[i] = c < C ? w_s[c] : 0ull;
-    if (kr[i]) kmin = min(kmin, kr[i]);
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-  if (lane == 0) rmin[wave] = kmin;
+  if (lane == 0) {
+    rmin[wave] = kmin;
+    rmax[wave] = kmax;
+  }
+  __syncthreads();
+  kmin = rmin[0];
+  kmax = rmax[0];
+  for (int q = 1; q < NT / 64; ++q) {
+    kmin = min(kmin, rmin[q]);
+    kmax = max(kmax, rmax[q]);
+  }
+  if (kmin == kmax) return kmin;  // one distinct key: it is the threshold either way
   double need = need_fx;
-  uint32_t prefix = 0u, pmask = 0u;
-  for (int level = 0; level < 4; ++level) {
-    const int shift = 24 - 8 * level;
+  int top = 31 - __clz((int)(kmin ^ kmax));  // highest differing bit
+  uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
+  uint32_t prefix = kmin & pmask;
+  while (top >= 0) {
+    const int shift = max(top - 7, 0);
+    const uint32_t dmask = (2u << (top - shift)) - 1u;  // width top - shift + 1 <= 8
     hist[tid] = 0ull;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < CPT; ++i)
-      if (kr[i] && (kr[i] & pmask) == prefix) atomicAdd(&hist[(kr[i] >> shift) & 255u], wr[i]);
+    visit([&](uint32_t k, unsigned long long w) {
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], w);
+    });
     __syncthreads();
     // thread t holds digit 255 - t; inclusive running mass from the highest digit
     const unsigned long long hv = hist[255 - tid];
@@ -638,15 +662,12 @@ __device__ uint32_t radix_key(unsigned C, const uint32_t* key_s, const unsigned 
     }
     __syncthreads();
     const int d = dig_s;
-    if (d < 0) {
-      // even the whole mass falls short of the need (rounding of p * Z): keep all
-      uint32_t lo = rmin[0];
-      for (int q = 1; q < NT / 64; ++q) lo = min(lo, rmin[q]);
-      return lo;
-    }
+    // even the whole mass falls short of the need (rounding of p * Z): keep all
+    if (d < 0) return kmin;
     need -= (double)above_s;
     prefix |= (uint32_t)d << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
+    top = shift - 1;
     __syncthreads();
   }
   return prefix;
@@ -661,9 +682,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const int kv = p.ret_kv[ret_i], qh = kv * G + h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ TileSmem<1> sm;
-  __shared__ uint32_t key_s[kCandCap];
-  __shared__ int tok_s[kCandCap];
-  __shared__ unsigned long long w_s[kCandCap];
+  // candidate keys, and their tokens while they fit beside them
+  __shared__ uint32_t cbuf[kKeyCap];
+  uint32_t* key_s = cbuf;
+  int* tok_s = (int*)(cbuf + kTokCap);
   __shared__ unsigned boff[kMaxBlocksLds + 1];
   __shared__ unsigned long long red[NT / 64];
   __shared__ unsigned wtot[NT / 64];
@@ -706,8 +728,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     __syncthreads();
     C = C_s;
   }
-  const bool in_lds = small_nA && C <= (unsigned)kCandCap;
-  if (in_lds && C > 0) {
+  // up to kTokCap candidates: keys and tokens in LDS; up to kKeyCap: keys only
+  const bool in_lds = small_nA && C <= (unsigned)kTokCap;
+  const bool keys_lds = small_nA && C <= (unsigned)kKeyCap;
+  if (keys_lds && C > 0) {
     // gather into LDS in canonical order; each thread copies whole blocks, with
     // the loads of a block issued together
     for (int bb = tid; bb < p.nA; bb += NT) {
@@ -722,16 +746,20 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
         for (int u = 0; u < 8; ++u) {
           if (c0 + u < n) {
             key_s[o + c0 + u] = f32_ord(e[u].x);
-            tok_s[o + c0 + u] = __float_as_int(e[u].y);
-            w_s[o + c0 + u] = (unsigned long long)(
-                (p.budget > 0 ? 1.0 : (double)__builtin_amdgcn_exp2f((e[u].x - t.m) * kLog2e)) *
-                kFxCand);
+            if (in_lds) tok_s[o + c0 + u] = __float_as_int(e[u].y);
           }
         }
       }
     }
   }
   __syncthreads();
+  const bool counting = p.budget > 0;
+  // a candidate's mass, 2^36 fixed point relative to the global max
+  auto cand_mass = [&](float sv) {
+    return (unsigned long long)((counting ? 1.0
+                                          : (double)__builtin_amdgcn_exp2f((sv - t.m) * kLog2e)) *
+                                kFxCand);
+  };
   uint32_t kstar = 0u;
   float tau = -INFINITY;
   if (t.mode != 2) {
@@ -739,9 +767,35 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
       tau = INFINITY;
       kstar = 0xffffffffu;
     } else {
-      kstar = in_lds ? radix_key<NT>(C, key_s, w_s, t.need * kFxCand)
-                     : bisect_key<NT>(C, in_lds, key_s, w_s, cand, blk_cnt, p.nA, t.m,
-                                      t.need * kFxCand, red, p.budget > 0);
+      if (keys_lds) {
+        kstar = radix_key<NT>(
+            [&](auto&& fn) {
+              for (unsigned c = tid; c < C; c += NT) {
+                const uint32_t k = key_s[c];
+                fn(k, cand_mass(ord_f32(k)));
+              }
+            },
+            t.need * kFxCand);
+      } else if (small_nA) {
+        // too many for LDS: candidate g (canonical order) is found through the
+        // block offsets and read from its pass-B block's region, all threads at once
+        kstar = radix_key<NT>(
+            [&](auto&& fn) {
+              for (unsigned g = tid; g < C; g += NT) {
+                int lo = 0, hi = p.nA - 1;
+                while (lo < hi) {
+                  const int mid = (lo + hi + 1) >> 1;
+                  if (boff[mid] <= g) lo = mid;
+                  else hi = mid - 1;
+                }
+                const float sv = cand[(size_t)lo * kPassTokens + (g - boff[lo])].x;
+                fn(f32_ord(sv), cand_mass(sv));
+              }
+            },
+            t.need * kFxCand);
+      } else {
+        kstar = bisect_key<NT>(C, cand, blk_cnt, p.nA, t.m, t.need * kFxCand, red, counting);
+      }
       tau = ord_f32(kstar);
     }
   }
@@ -991,6 +1045,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   char* bm = take((size_t)P * nA * G * 4);
   char* bz = take((size_t)P * nA * G * 8);
   char* bb = take((size_t)P * nA * G * kNB * 4);
+  char* bc = take((size_t)P * nA * G * kNB * 4);
   char* th = take((size_t)P * G * sizeof(ThrInfo));
   char* ca = take((size_t)P * G * N * 8);
   char* un = take((size_t)P * N * 8);
@@ -1006,6 +1061,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
     plan->blk_m = (float*)bm;
     plan->blk_z = (unsigned long long*)bz;
     plan->blk_bins = (unsigned*)bb;
+    plan->blk_bins_c = (unsigned*)bc;
     plan->thr = (ThrInfo*)th;
     plan->cand = (float2*)ca;
     plan->uni = (int2*)un;

@@ -22,6 +22,10 @@ constexpr float kDelta = 0.5f;
 constexpr float kFxBin = 1048576.0f;            // 2^20
 constexpr double kFxZ = 1125899906842624.0;     // 2^50: per-block Z relative to the block max
 constexpr double kFxCand = 68719476736.0;       // 2^36: candidate masses relative to the max
+// A fixed budget counts keys rather than weighing them, so its boundary can sit
+// far below the max: a second, coarse grid (bins of 4 score units, reach 128)
+// takes over when the fine one does not reach the budget.
+constexpr float kInvDeltaCoarse = 0.25f;
 
 // Tokens per block of the two index passes.
 constexpr int kPassTokens = 2048;
@@ -39,6 +43,7 @@ struct ThrInfo {
   double need;   // top_p * Z - above
   float tau;     // resolved threshold score
   int n_cand;    // candidates seen by the resolver
+  float inv_w;   // inverse bin width of the grid key_top and key_bnd live on
 };
 
 // Parameters of the retrieval decode.
@@ -66,6 +71,7 @@ struct DecPlan {
   unsigned long long* blk_z;      // [P][nA][G]   sum exp(s - e_top) * 2^50, e_top the
                                   //              upper edge of the block max's bin
   unsigned* blk_bins;             // [P][nA][G][kNB]
+  unsigned* blk_bins_c;           // [P][nA][G][kNB], coarse grid (fixed budget only)
   ThrInfo* thr;                   // [P][G]
   float2* cand;                   // [P][G][N]  (score, token id bits); block b's
                                   //            candidates start at b * kPassTokens

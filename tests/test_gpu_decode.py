@@ -280,3 +280,53 @@ def test_decode_topk_million_budgets():
             P.check_out(res["out"][b, h], own, f"top-{k} own set h{h}")
             if kind == "exact":
                 P.check_out(res["out"][b, h], r["out"], f"top-{k} h{h}")
+
+
+# (needle score, background half-width, N, top_k, candidate range the case is built for)
+FAR_BUDGET_CASES = [
+    (60.0, 4.0, 3000, 100, (1, 8192)),          # coarse grid, keys and tokens in LDS
+    (60.0, 4.0, 24000, 100, (8193, 16384)),     # coarse grid, keys alone in LDS
+    (60.0, 4.0, 50000, 100, (16385, 10 ** 9)),  # coarse grid, candidates read in place
+    (200.0, 4.0, 9000, 100, (8193, 16384)),     # beyond the coarse window too
+]
+
+
+@pytest.mark.parametrize("case", FAR_BUDGET_CASES, ids=[f"n{c[0]:.0f}_N{c[2]}" for c in FAR_BUDGET_CASES])
+def test_decode_topk_far_boundary(case):
+    """A fixed budget whose k-th score lies far below the max: one needle high above
+    a background of scores spread evenly over [-a, a].  The fine 16-unit window
+    misses the boundary, the coarse one (or, past 128 units, its tail) holds the
+    candidates; the sizes put the candidate list in each resolver path."""
+    needle, a, N, k, (c_lo, c_hi) = case
+    wl = W.random_decode(71, 1, 8, 1, N, [0], 512)
+    kc, vc, idx = O.caches_for(wl)
+    rng = np.random.default_rng(72)
+    qi0 = O.query_index(wl.q_pre[0, 0], wl.w_q[0]).astype(np.float64)
+    u = qi0 / (qi0 @ qi0)
+    target = rng.uniform(-a, a, wl.N)
+    target[N // 3] = needle
+    rows = target[:, None] * u[None, :] + 1e-3 * rng.standard_normal((wl.N, 16))
+    idx = idx.copy()
+    idx[0, 0] = O.f64_to_bf16(rows)
+    s0 = O.scores(O.query_index(wl.q_pre[0, 0], wl.w_q[0]), idx[0, 0]).astype(np.float64)
+    kth = np.sort(s0)[::-1][k - 1]
+    assert s0.max() - kth > 16
+    # candidates of the boundary's 4-unit bin (or the whole tail past 128 units)
+    if s0.max() - kth > 128:
+        n_cand = int((s0 < np.floor(s0.max() / 4) * 4 - 124).sum())
+    else:
+        n_cand = int((np.floor(s0 / 4) == np.floor(kth / 4)).sum())
+    assert c_lo <= n_cand <= c_hi, n_cand
+    res = P.Device(wl, kc, vc, idx).decode(0.9, debug_cap=wl.N, top_k=k)
+    ref = O.decode(wl, kc, vc, idx, 0.9, top_k=k)
+    kinds = {}
+    for (b, h), r in ref.items():
+        S = P.gpu_set(res, h)
+        kind = P.check_set_topk(S, r, k, wl.n_sink)
+        kinds[kind] = kinds.get(kind, 0) + 1
+        qr = O.rope(P.bf16_f64(wl.q_pre[b, h]), N - 1, wl.rope_base)
+        own = O.attention(qr, kc[b, 0][S], vc[b, 0][S], wl.attn_scale)
+        P.check_out(res["out"][b, h], own, f"own set h{h}")
+        if kind == "exact":
+            P.check_out(res["out"][b, h], r["out"], f"h{h}")
+    print(f"needle {needle} N {N} top-{k}: head-0 candidates {n_cand}, {kinds}")
