@@ -52,6 +52,9 @@ constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets f
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
 
+// Inverse bin width of coarse grid c: bins of 2^c score units (exact in fp32).
+__device__ __forceinline__ float coarse_inv(int c) { return 1.0f / (float)(1 << c); }
+
 __device__ __forceinline__ void load_index_row(const uint16_t* row, uint32_t (&w)[8]) {
   const uint4 a = *(const uint4*)row;
   const uint4 b = *(const uint4*)(row + 8);
@@ -87,8 +90,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   __shared__ float mb_s[G];
   __shared__ int kt_s[G];
   __shared__ unsigned bins[G][kNB];
-  __shared__ unsigned binc[G][kNB];  // coarse grid, fixed budget only
-  __shared__ int ktc_s[G];
+  __shared__ unsigned binc[kCoarseGrids][G][kNB];  // coarse grids, fixed budget only
+  __shared__ int ktc_s[kCoarseGrids][G];
   __shared__ unsigned long long zred[NW][G];
   __shared__ float bscale[kNB];
   __shared__ __align__(16) uint16_t wq_s[G * kD * kR];
@@ -120,7 +123,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
-  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = (&binc[0][0])[e] = 0u;
+  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
+  for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
   __syncthreads();
   {
@@ -166,7 +170,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     for (int q = 1; q < NW; ++q) v = fmaxf(v, red_m[q][tid]);
     mb_s[tid] = v;
     kt_s[tid] = score_key(v, kInvDelta);
-    ktc_s[tid] = score_key(v, kInvDeltaCoarse);
+#pragma unroll
+    for (int c = 0; c < kCoarseGrids; ++c) ktc_s[c][tid] = score_key(v, coarse_inv(c));
   }
   __syncthreads();
 
@@ -189,8 +194,11 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
           atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
         }
         if (counting) {
-          const int jc = ktc_s[h] - score_key(sv, kInvDeltaCoarse);
-          if (jc < kNB) atomicAdd(&binc[h][jc], (unsigned)kFxBin);
+#pragma unroll
+          for (int c = 0; c < kCoarseGrids; ++c) {
+            const int jc = ktc_s[c][h] - score_key(sv, coarse_inv(c));
+            if (jc < kNB) atomicAdd(&binc[c][h][jc], (unsigned)kFxBin);
+          }
         }
       }
     }
@@ -206,8 +214,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     p.blk_z[so + tid] = zb;
   }
   for (int e = tid; e < G * kNB; e += NT) p.blk_bins[so * kNB + e] = (&bins[0][0])[e];
-  if (counting)
-    for (int e = tid; e < G * kNB; e += NT) p.blk_bins_c[so * kNB + e] = (&binc[0][0])[e];
+  if (counting) {
+    const size_t grid_stride = (size_t)p.P * p.nA * G * kNB;
+    for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) {
+      const int c = e / (G * kNB), r = e % (G * kNB);
+      p.blk_bins_c[c * grid_stride + so * kNB + r] = (&binc[0][0][0])[e];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ threshold
@@ -260,11 +273,12 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   const bool counting = p.budget > 0;
   __shared__ int redo_s;
   double z = 0.0;
-  // round 0: the fine grid; round 1: the coarse grid, for a fixed budget that
-  // the fine grid's window does not reach
-  for (int round = 0; round < 2; ++round) {
-    const float inv = round ? kInvDeltaCoarse : kInvDelta;
-    const unsigned* bins = round ? p.blk_bins_c : p.blk_bins;
+  // round 0: the fine grid; rounds 1..: the coarse grids in turn, for a fixed
+  // budget that the finer windows do not reach
+  for (int round = 0; round <= kCoarseGrids; ++round) {
+    const float inv = round ? coarse_inv(round - 1) : kInvDelta;
+    const unsigned* bins =
+        round ? p.blk_bins_c + (size_t)(round - 1) * p.P * p.nA * G * kNB : p.blk_bins;
     const int kt = score_key(m, inv);
     // each thread fills only its own row
 #pragma unroll
@@ -341,7 +355,7 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
         t.above = cum;
         t.need = target - cum;
       }
-      redo_s = round == 0 && counting && t.mode == 1;
+      redo_s = round < kCoarseGrids && counting && t.mode == 1;
       if (!redo_s) p.thr[unit] = t;
     }
     __syncthreads();
@@ -1045,7 +1059,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   char* bm = take((size_t)P * nA * G * 4);
   char* bz = take((size_t)P * nA * G * 8);
   char* bb = take((size_t)P * nA * G * kNB * 4);
-  char* bc = take((size_t)P * nA * G * kNB * 4);
+  char* bc = take((size_t)kCoarseGrids * P * nA * G * kNB * 4);
   char* th = take((size_t)P * G * sizeof(ThrInfo));
   char* ca = take((size_t)P * G * N * 8);
   char* un = take((size_t)P * N * 8);

@@ -23,9 +23,10 @@ constexpr float kFxBin = 1048576.0f;            // 2^20
 constexpr double kFxZ = 1125899906842624.0;     // 2^50: per-block Z relative to the block max
 constexpr double kFxCand = 68719476736.0;       // 2^36: candidate masses relative to the max
 // A fixed budget counts keys rather than weighing them, so its boundary can sit
-// far below the max: a second, coarse grid (bins of 4 score units, reach 128)
-// takes over when the fine one does not reach the budget.
-constexpr float kInvDeltaCoarse = 0.25f;
+// far below the max: coarser grids (bins of 1, 2, 4 and 8 score units, reaching
+// 32 to 256 below the top) are counted too, and the finest one whose window
+// reaches the budget's boundary is used.
+constexpr int kCoarseGrids = 4;
 
 // Tokens per block of the two index passes.
 constexpr int kPassTokens = 2048;
@@ -71,7 +72,7 @@ struct DecPlan {
   unsigned long long* blk_z;      // [P][nA][G]   sum exp(s - e_top) * 2^50, e_top the
                                   //              upper edge of the block max's bin
   unsigned* blk_bins;             // [P][nA][G][kNB]
-  unsigned* blk_bins_c;           // [P][nA][G][kNB], coarse grid (fixed budget only)
+  unsigned* blk_bins_c;           // [kCoarseGrids][P][nA][G][kNB] (fixed budget only)
   ThrInfo* thr;                   // [P][G]
   float2* cand;                   // [P][G][N]  (score, token id bits); block b's
                                   //            candidates start at b * kPassTokens

@@ -284,11 +284,23 @@ def test_decode_topk_million_budgets():
 
 # (needle score, background half-width, N, top_k, candidate range the case is built for)
 FAR_BUDGET_CASES = [
-    (60.0, 4.0, 3000, 100, (1, 8192)),          # coarse grid, keys and tokens in LDS
-    (60.0, 4.0, 24000, 100, (8193, 16384)),     # coarse grid, keys alone in LDS
-    (60.0, 4.0, 50000, 100, (16385, 10 ** 9)),  # coarse grid, candidates read in place
-    (200.0, 4.0, 9000, 100, (8193, 16384)),     # beyond the coarse window too
+    (25.0, 4.0, 3000, 100, (1, 8192)),           # 1-unit grid
+    (60.0, 4.0, 3000, 100, (1, 8192)),           # 2-unit grid, keys and tokens in LDS
+    (60.0, 4.0, 48000, 100, (8193, 16384)),      # keys alone in LDS
+    (60.0, 4.0, 100000, 100, (16385, 10 ** 9)),  # candidates read in place
+    (300.0, 4.0, 9000, 100, (8193, 16384)),      # beyond the coarsest window too
 ]
+
+
+def _far_candidates(s: np.ndarray, k: int) -> int:
+    """Size of the candidate list the grids leave: the boundary bin of the finest
+    grid (widths 0.5, 1, 2, 4, 8; 32 bins below the top) that reaches the k-th
+    score, else everything below the coarsest window."""
+    kth = np.sort(s)[::-1][k - 1]
+    for w in (0.5, 1.0, 2.0, 4.0, 8.0):
+        if np.floor(s.max() / w) - np.floor(kth / w) < 32:
+            return int((np.floor(s / w) == np.floor(kth / w)).sum())
+    return int((np.floor(s / 8.0) <= np.floor(s.max() / 8.0) - 32).sum())
 
 
 @pytest.mark.parametrize("case", FAR_BUDGET_CASES, ids=[f"n{c[0]:.0f}_N{c[2]}" for c in FAR_BUDGET_CASES])
@@ -311,11 +323,7 @@ def test_decode_topk_far_boundary(case):
     s0 = O.scores(O.query_index(wl.q_pre[0, 0], wl.w_q[0]), idx[0, 0]).astype(np.float64)
     kth = np.sort(s0)[::-1][k - 1]
     assert s0.max() - kth > 16
-    # candidates of the boundary's 4-unit bin (or the whole tail past 128 units)
-    if s0.max() - kth > 128:
-        n_cand = int((s0 < np.floor(s0.max() / 4) * 4 - 124).sum())
-    else:
-        n_cand = int((np.floor(s0 / 4) == np.floor(kth / 4)).sum())
+    n_cand = _far_candidates(s0, k)
     assert c_lo <= n_cand <= c_hi, n_cand
     res = P.Device(wl, kc, vc, idx).decode(0.9, debug_cap=wl.N, top_k=k)
     ref = O.decode(wl, kc, vc, idx, 0.9, top_k=k)
