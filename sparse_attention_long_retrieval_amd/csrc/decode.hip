@@ -51,16 +51,10 @@ constexpr int kTokCap = 8192;         // candidates whose tokens are also kept i
 constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
+constexpr int kScanCopies = 16;       // words per histogram bin in the scan
 
 // Inverse bin width of coarse grid c: bins of 2^c score units (exact in fp32).
 __device__ __forceinline__ float coarse_inv(int c) { return 1.0f / (float)(1 << c); }
-
-__device__ __forceinline__ void load_index_row(const uint16_t* row, uint32_t (&w)[8]) {
-  const uint4 a = *(const uint4*)row;
-  const uint4 b = *(const uint4*)(row + 8);
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-}
 
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
@@ -74,22 +68,147 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// ------------------------------------------------------------------ index scores
+
+// Scores of a pass block on v_mfma_f32_16x16x32_bf16.  An A row holds R = 16/GE
+// consecutive index rows (R * 32 bytes, straight from the cache); output column
+// n is (head n % GE, row slot n / GE), and the B operand is block diagonal: it
+// pairs slot j's 16 index dimensions with the head's qi.  One tile of 16 A rows
+// yields 16 R tokens x GE heads, every output lane busy.  qi (fp32) enters as
+// three bf16 parts hi + mid + lo that sum to it exactly; index values are bf16,
+// so every product is exact and only the fp32 accumulation rounds.  Fewer than
+// four heads are padded to four (the padding heads are skipped).
+//
+// Lane roles: n = lane & 15 (head h = n % GE, slot par = n / GE), kb = lane >> 4.
+// Output r of tile T of a wave is the score of token
+//   (wave * TPW + T) * TILE + R * (4 * kb + r) + par
+// of the block, for head h.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int G>
+struct ScoreTiles {
+  static constexpr int GE = G < 4 ? 4 : G;  // heads in the layout
+  static constexpr int R = 16 / GE;         // index rows per A row
+  static constexpr int CH = R / 2;          // 32-wide K chunks (two index rows) per qi part
+  static constexpr int TILE = 16 * R;       // tokens per tile
+  static constexpr int NW = PassCfg<G>::NW;
+  static constexpr int TPW = kPassTokens / (TILE * NW);  // tiles per wave
+  static_assert(TPW * TILE * NW == kPassTokens, "the tiles cover the block");
+};
+
+// A operands of this wave's tiles: lane loads 16 bytes of A row lane & 15,
+// chunk c, K columns 8 kb .. 8 kb + 7 (index row 2 c + kb / 2, half kb % 2).
+template <int G>
+__device__ __forceinline__ void load_score_tiles(
+    const uint16_t* idx, int tok0, int N,
+    uint4 (&a)[ScoreTiles<G>::TPW][ScoreTiles<G>::CH]) {
+  using S = ScoreTiles<G>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kb = lane >> 4, m = lane & 15;
+#pragma unroll
+  for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+    for (int c = 0; c < S::CH; ++c) {
+      const int t = tok0 + (wave * S::TPW + T) * S::TILE + S::R * m + 2 * c + (kb >> 1);
+      a[T][c] = t < N ? *(const uint4*)(idx + (size_t)t * kR + 8 * (kb & 1)) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// B operands: part 0, 1, 2 = hi, mid, lo of qi, zero off the diagonal blocks.
+template <int G>
+__device__ __forceinline__ void make_score_b(const float (*qi_s)[kR],
+                                             uint4 (&bq)[3][ScoreTiles<G>::CH]) {
+  using S = ScoreTiles<G>;
+  const int lane = threadIdx.x & 63, kb = lane >> 4, n = lane & 15;
+  const int h = n % S::GE, par = n / S::GE, d0 = 8 * (kb & 1);
+  uint32_t pk[3][4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint16_t v[3][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float q = h < G ? qi_s[h][d0 + 2 * e + u] : 0.f;
+      const uint16_t hi = f32_to_bf16(q);
+      const float r1 = q - bf16_to_f32(hi);
+      const uint16_t mid = f32_to_bf16(r1);
+      v[0][u] = hi;
+      v[1][u] = mid;
+      v[2][u] = f32_to_bf16(r1 - bf16_to_f32(mid));
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) pk[s][e] = (uint32_t)v[s][0] | ((uint32_t)v[s][1] << 16);
+  }
+#pragma unroll
+  for (int c = 0; c < S::CH; ++c) {
+    const bool on = h < G && 2 * c + (kb >> 1) == par;
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      bq[s][c] = on ? make_uint4(pk[s][0], pk[s][1], pk[s][2], pk[s][3]) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void score_tiles(const uint4 (&a)[ScoreTiles<G>::TPW][ScoreTiles<G>::CH],
+                                            const uint4 (&bq)[3][ScoreTiles<G>::CH],
+                                            f32x4_t (&acc)[ScoreTiles<G>::TPW]) {
+  using S = ScoreTiles<G>;
+#pragma unroll
+  for (int T = 0; T < S::TPW; ++T) {
+    acc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int c = 0; c < S::CH; ++c)
+        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, a[T][c]), __builtin_bit_cast(bf16x8_t, bq[s][c]), acc[T],
+            0, 0, 0);
+  }
+}
+
+// Token of the block for output r of tile T (see the lane roles above).
+template <int G>
+__device__ __forceinline__ int score_token(int T, int r) {
+  using S = ScoreTiles<G>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  return (wave * S::TPW + T) * S::TILE + S::R * (4 * (lane >> 4) + r) + (lane & 15) / S::GE;
+}
+
+// Reduce over the lanes of one head (lanes equal modulo GE).
+template <int G>
+__device__ __forceinline__ float head_lanes_max(float v) {
+#pragma unroll
+  for (int o = ScoreTiles<G>::GE; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ unsigned long long head_lanes_sum(unsigned long long v) {
+#pragma unroll
+  for (int o = ScoreTiles<G>::GE; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
 // ------------------------------------------------------------------ pass A
 
 template <int G>
 __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
-  constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
+  using S = ScoreTiles<G>;
+  constexpr int NT = PassCfg<G>::NT, NW = PassCfg<G>::NW;
   constexpr int WQ_VEC = G * kD * kR / 8;           // uint4 of W_q for the pair
   constexpr int WQ_PER = WQ_VEC / NT;
   static_assert(WQ_VEC % NT == 0, "every thread loads the same number of W_q vectors");
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = (lane & 15) % S::GE;  // this lane's head in the score layout
   __shared__ float qi_s[G][kR];
   __shared__ float red_m[NW][G];
   __shared__ float mb_s[G];
   __shared__ int kt_s[G];
-  __shared__ unsigned bins[G][kNB];
+  // each bin is split over kScanCopies words, one per lane group, so that lanes
+  // adding to the same bin mostly hit different words; the copies are summed
+  // at the end (integers: the split changes no result)
+  __shared__ unsigned bins[G][kNB][kScanCopies];
   __shared__ unsigned binc[kCoarseGrids][G][kNB];  // coarse grids, fixed budget only
   __shared__ int ktc_s[kCoarseGrids][G];
   __shared__ unsigned long long zred[NW][G];
@@ -109,61 +228,47 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
 
   const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
   const int tok0 = blk * kPassTokens;
-  uint32_t w[TPT][8];
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int t = tok0 + k * NT + tid;
-    if (t < p.N) {
-      load_index_row(idx + (size_t)t * kR, w[k]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) w[k][c] = 0u;
-    }
-  }
+  uint4 a[S::TPW][S::CH];
+  load_score_tiles<G>(idx, tok0, p.N, a);
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
-  for (int e = tid; e < G * kNB; e += NT) (&bins[0][0])[e] = 0u;
+  for (int e = tid; e < G * kNB * kScanCopies; e += NT) (&bins[0][0][0])[e] = 0u;
   for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
   __syncthreads();
   {
     // qi = q . W_q (fp32): four threads per output, 32 terms each, (p0+p1)+(p2+p3)
     float acc = 0.f;
-    const int h = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
-    if (h < G) {
-      const uint16_t* wq = wq_s + h * kD * kR;
-      const uint16_t* qq = q_s + h * kD;
+    const int hh = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
+    if (hh < G) {
+      const uint16_t* wq = wq_s + hh * kD * kR;
+      const uint16_t* qq = q_s + hh * kD;
       for (int d = 32 * part; d < 32 * part + 32; ++d)
         acc = __fmaf_rn(bf16_to_f32(qq[d]), bf16_to_f32(wq[d * kR + c]), acc);
     }
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
-    if (h < G && part == 0) qi_s[h][c] = acc * p.idx_scale;
+    if (hh < G && part == 0) qi_s[hh][c] = acc * p.idx_scale;
   }
   __syncthreads();
   if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
 
-  float s[TPT][G];
-  float mloc[G];
+  uint4 bq[3][S::CH];
+  make_score_b<G>(qi_s, bq);
+  f32x4_t sc[S::TPW];
+  score_tiles<G>(a, bq, sc);
+  const bool hv = h < G;
+  float mloc = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float q[kR];
+  for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-    for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
-    mloc[h] = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int t = tok0 + k * NT + tid;
-      s[k][h] = (t < p.N) ? idx_score(w[k], q) : -INFINITY;
-      mloc[h] = fmaxf(mloc[h], s[k][h]);
+    for (int r = 0; r < 4; ++r) {
+      if (!hv || tok0 + score_token<G>(T, r) >= p.N) sc[T][r] = -INFINITY;
+      mloc = fmaxf(mloc, sc[T][r]);
     }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float v = wave_max(mloc[h]);
-    if (lane == 0) red_m[wave][h] = v;
-  }
+  mloc = head_lanes_max<G>(mloc);
+  if (lane < G) red_m[wave][lane] = mloc;
   __syncthreads();
   if (tid < G) {
     float v = red_m[0][tid];
@@ -176,14 +281,16 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   __syncthreads();
 
   const bool counting = p.budget > 0;  // fixed top-k: every key weighs 1
+  const int hs = hv ? h : 0;
+  const int kt = kt_s[hs];
+  const float e_top = (float)(kt + 1) * kDelta;  // exact: a multiple of 0.5
+  const int copy = (lane / S::GE) & (kScanCopies - 1);
+  float z = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int kt = kt_s[h];
-    const float e_top = (float)(kt + 1) * kDelta;  // exact: a multiple of 0.5
-    float z = 0.f;
+  for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const float sv = s[k][h];
+    for (int r = 0; r < 4; ++r) {
+      const float sv = sc[T][r];
       if (sv > -INFINITY) {
         const float wt = counting ? 1.f : __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
         z += wt;
@@ -191,19 +298,20 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
         if (j < kNB) {
           // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1]
           const float wb = counting ? 1.f : fminf(wt * bscale[j], 1.0f);
-          atomicAdd(&bins[h][j], (unsigned)(wb * kFxBin + 0.5f));
+          atomicAdd(&bins[hs][j][copy], (unsigned)(wb * kFxBin + 0.5f));
         }
         if (counting) {
 #pragma unroll
           for (int c = 0; c < kCoarseGrids; ++c) {
-            const int jc = ktc_s[c][h] - score_key(sv, coarse_inv(c));
-            if (jc < kNB) atomicAdd(&binc[c][h][jc], (unsigned)kFxBin);
+            const int jc = ktc_s[c][hs] - score_key(sv, coarse_inv(c));
+            if (jc < kNB) atomicAdd(&binc[c][hs][jc], (unsigned)kFxBin);
           }
         }
       }
     }
-    const unsigned long long zfx = wave_sum_u64((unsigned long long)((double)z * kFxZ));
-    if (lane == 0) zred[wave][h] = zfx;
+  {
+    const unsigned long long zfx = head_lanes_sum<G>((unsigned long long)((double)z * kFxZ));
+    if (lane < G) zred[wave][lane] = zfx;
   }
   __syncthreads();
   const size_t so = ((size_t)pair * p.nA + blk) * G;
@@ -213,7 +321,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     p.blk_m[so + tid] = mb_s[tid];
     p.blk_z[so + tid] = zb;
   }
-  for (int e = tid; e < G * kNB; e += NT) p.blk_bins[so * kNB + e] = (&bins[0][0])[e];
+  for (int e = tid; e < G * kNB; e += NT) {
+    const unsigned* cp = &bins[0][0][0] + (size_t)e * kScanCopies;
+    unsigned acc = 0u;
+#pragma unroll
+    for (int c = 0; c < kScanCopies; ++c) acc += cp[(c + e) & (kScanCopies - 1)];
+    p.blk_bins[so * kNB + e] = acc;
+  }
   if (counting) {
     const size_t grid_stride = (size_t)p.P * p.nA * G * kNB;
     for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) {
@@ -367,11 +481,13 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
 
 template <int G>
 __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
+  using S = ScoreTiles<G>;
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   const int pair = blockIdx.y, blk = blockIdx.x;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int kv = p.ret_kv[ret_i];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = (lane & 15) % S::GE;  // this lane's head in the score layout
   __shared__ TileSmem<G> sm;
   __shared__ float qi_s[G][kR];
   __shared__ int kb_s[G], mode_s[G];
@@ -379,6 +495,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   __shared__ int relevant;
   __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned list[kPassTokens];
+  // per token of the block: heads it is definite for, and (inspection only) a candidate for
+  __shared__ unsigned dmask[kPassTokens], cmask[kPassTokens];
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
 
@@ -393,6 +511,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
     if (t.mode != 0 || score_key(mb, t.inv_w) >= t.key_bnd) atomicOr(&relevant, 1);
   }
   if (tid < G * kR) (&qi_s[0][0])[tid] = p.qi[(size_t)pair * G * kR + tid];
+  for (int e = tid; e < kPassTokens; e += NT) dmask[e] = cmask[e] = 0u;
   __syncthreads();
 
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
@@ -401,71 +520,58 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
     const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
     const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
     const int tok0 = blk * kPassTokens;
-    uint32_t w[TPT][8];
-#pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int t = tok0 + k * NT + tid;
-      if (t < p.N) {
-        load_index_row(idx + (size_t)t * kR, w[k]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) w[k][c] = 0u;
-      }
-    }
+    const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
+    uint4 a[S::TPW][S::CH];
+    load_score_tiles<G>(idx, tok0, p.N, a);
     load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.theta,
                    p.attn_scale * kLog2e);
-    float s[TPT][G];
-    uint32_t dm[TPT], cm[TPT];
+    uint4 bq[3][S::CH];
+    make_score_b<G>(qi_s, bq);
+    f32x4_t sc[S::TPW];
+    score_tiles<G>(a, bq, sc);
+    // classify this lane's keys (the same scores as pass A)
+    const bool hv = h < G;
+    const int hs = hv ? h : 0;
+    const int mode = mode_s[hs], kbnd = kb_s[hs];
+    const float inv = inv_s[hs];
+    uint32_t cbits = 0u;
+    unsigned ccount = 0u;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) dm[k] = cm[k] = 0u;
+    for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float q[kR];
-#pragma unroll
-      for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
-      const int mode = mode_s[h], kb = kb_s[h];
-      const float inv = inv_s[h];
-#pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        const int t = tok0 + k * NT + tid;
-        if (t < p.N) {
-          const float sv = idx_score(w[k], q);
-          s[k][h] = sv;
-          const int key = score_key(sv, inv);
-          if (mode == 2 || key > kb) dm[k] |= 1u << h;
-          else if ((mode == 0 && key == kb) || (mode == 1 && key <= kb)) cm[k] |= 1u << h;
-        } else {
-          s[k][h] = -INFINITY;
+      for (int r = 0; r < 4; ++r) {
+        const int tl = score_token<G>(T, r);
+        if (hv && tok0 + tl < p.N) {
+          const int key = score_key(sc[T][r], inv);
+          if (mode == 2 || key > kbnd) {
+            atomicOr(&dmask[tl], 1u << h);
+          } else if ((mode == 0 && key == kbnd) || (mode == 1 && key <= kbnd)) {
+            cbits |= 1u << (4 * T + r);
+            ++ccount;
+            if (inspect) atomicOr(&cmask[tl], 1u << h);
+          }
         }
       }
+    // candidates: the block's own region of the head's list, in a fixed order
+    // (wave, lane, tile, output), positions from scans over the head's lanes
+    unsigned inc = ccount;
+#pragma unroll
+    for (int o = S::GE; o < 64; o <<= 1) {
+      const unsigned v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
     }
-    // candidates: the block's own region of the head's list, positions from a
-    // block scan (fixed order), and the block's count for the finish kernel
-    unsigned coff[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      unsigned c = 0u;
-#pragma unroll
-      for (int k = 0; k < TPT; ++k) c += (cm[k] >> h) & 1u;
-      unsigned inc = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned v = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += v;
-      }
-      coff[h] = inc - c;
-      if (lane == 63) cwsum[wave][h] = inc;
-    }
+    if (lane >= 64 - S::GE && hv) cwsum[wave][h] = inc;
     __syncthreads();
+    if (ccount) {
+      unsigned off = inc - ccount;
+      for (int q = 0; q < wave; ++q) off += cwsum[q][h];
+      float2* cd = p.cand + ((size_t)pair * G + h) * p.N + (size_t)blk * kPassTokens + off;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      for (int q = 0; q < wave; ++q) coff[h] += cwsum[q][h];
-      float2* cd = p.cand + ((size_t)pair * G + h) * p.N + (size_t)blk * kPassTokens + coff[h];
-      unsigned c = 0u;
+      for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        if ((cm[k] >> h) & 1u) cd[c++] = make_float2(s[k][h], __int_as_float(tok0 + k * NT + tid));
-      }
+        for (int r = 0; r < 4; ++r)
+          if ((cbits >> (4 * T + r)) & 1u)
+            *cd++ = make_float2(sc[T][r], __int_as_float(tok0 + score_token<G>(T, r)));
     }
     if (tid < G) {
       unsigned tot = 0u;
@@ -473,10 +579,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
       p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = tot;
     }
     // definite rows (sinks join every head): ordered compaction into LDS
+    uint32_t dm[TPT];
     unsigned cnt = 0u;
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int t = tok0 + k * NT + tid;
+      dm[k] = dmask[k * NT + tid];
       if (t < p.N && t < p.n_sink) dm[k] = (1u << G) - 1u;
       cnt += dm[k] ? 1u : 0u;
     }
@@ -494,11 +602,15 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k)
       if (dm[k]) list[off++] = ((unsigned)(k * NT + tid) << 8) | dm[k];
-    if (p.dbg_cnt || p.dbg_idx || p.dbg_union) {
+    if (inspect) {
       // inspection only: the union of definite and candidate keys of this block
+      uint32_t cm[TPT];
       unsigned uc = 0u;
 #pragma unroll
-      for (int k = 0; k < TPT; ++k) uc += (dm[k] | cm[k]) ? 1u : 0u;
+      for (int k = 0; k < TPT; ++k) {
+        cm[k] = cmask[k * NT + tid];
+        uc += (dm[k] | cm[k]) ? 1u : 0u;
+      }
       if (tid == 0) ucount_s = 0u;
       __syncthreads();
       const unsigned uo = uc ? atomicAdd(&ucount_s, uc) : 0u;
@@ -955,56 +1067,46 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecPlan p) {
 
 // ------------------------------------------------------------------ debug sets
 
-// Head mask of a union entry: definite heads, sinks, and candidates whose score
-// reaches the resolved threshold (the score is recomputed bit-identically).
-template <int G>
-__device__ __forceinline__ uint32_t entry_mask(const int2 e, const uint16_t* idx,
-                                               const float (*qi_s)[kR], const float* tau_s) {
-  uint32_t dm = (uint32_t)e.y & 0xffu;
-  const uint32_t cm = ((uint32_t)e.y >> 8) & 0xffu;
-  if (cm) {
-    uint32_t w[8];
-    load_index_row(idx + (size_t)e.x * kR, w);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if ((cm >> h) & 1u) {
-        float q[kR];
-#pragma unroll
-        for (int c = 0; c < kR; ++c) q[c] = qi_s[h][c];
-        if (idx_score(w, q) >= tau_s[h]) dm |= 1u << h;
-      }
-    }
-  }
-  return dm;
-}
-
+// The selected set of one (pair, q-head) for inspection: the definite keys of the
+// union list (sinks included), then the candidates whose ordered key reaches the
+// resolved threshold key, read from the pass-B lists exactly as the finish
+// kernel selects them.
 template <int G>
 __global__ __launch_bounds__(256) void k_debug_sets(DecPlan p) {
   const int unit = blockIdx.x;
   const int pair = unit / G, h = unit % G;
-  const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
-  __shared__ float qi_s[G][kR];
-  __shared__ float tau_s[G];
   __shared__ unsigned cnt;
-  if (threadIdx.x < G * kR) (&qi_s[0][0])[threadIdx.x] = p.qi[(size_t)pair * G * kR + threadIdx.x];
-  if (threadIdx.x < G) tau_s[threadIdx.x] = p.thr[pair * G + threadIdx.x].tau;
   if (threadIdx.x == 0) cnt = 0u;
   __syncthreads();
-  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+  const float tau = p.thr[unit].tau;
+  auto add = [&](int tok) {
+    const unsigned slot = atomicAdd(&cnt, 1u);
+    if (p.dbg_idx && (int)slot < p.dbg_cap) p.dbg_idx[(size_t)unit * p.dbg_cap + slot] = tok;
+  };
   const unsigned M = p.uni_cnt[pair];
   const int2* uni = p.uni + (size_t)pair * p.N;
   for (unsigned e = threadIdx.x; e < M; e += 256) {
     const int2 en = uni[e];
-    if ((entry_mask<G>(en, idx, qi_s, tau_s) >> h) & 1u) {
-      const unsigned slot = atomicAdd(&cnt, 1u);
-      if (p.dbg_idx && (int)slot < p.dbg_cap) p.dbg_idx[(size_t)unit * p.dbg_cap + slot] = en.x;
+    if (((unsigned)en.y >> h) & 1u) add(en.x);
+  }
+  if (p.thr[unit].mode != 2 && tau < INFINITY) {
+    const uint32_t kstar = f32_ord(tau);
+    const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
+    const float2* cand = p.cand + (size_t)unit * p.N;
+    for (int bb = 0; bb < p.nA; ++bb) {
+      const unsigned n = blk_cnt[bb];
+      for (unsigned c = threadIdx.x; c < n; c += 256) {
+        const float2 e = cand[(size_t)bb * kPassTokens + c];
+        const int tok = __float_as_int(e.y);
+        if (f32_ord(e.x) >= kstar && tok >= p.n_sink) add(tok);
+      }
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     if (p.dbg_union && h == 0) p.dbg_union[pair] = (int)M;
     if (p.dbg_cnt) p.dbg_cnt[unit] = (int)cnt;
-    if (p.dbg_tau) p.dbg_tau[unit] = (p.thr[unit].mode == 2) ? -INFINITY : tau_s[h];
+    if (p.dbg_tau) p.dbg_tau[unit] = (p.thr[unit].mode == 2) ? -INFINITY : tau;
   }
 }
 

@@ -75,21 +75,6 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
-// ------------------------------------------------------------------ indexer score
-
-// Score of one index row (16 bf16 packed in 8 dwords) against an fp32 query
-// vector qi[16] that already carries idx_scale.  The fused multiply-add order
-// is fixed so that every kernel that recomputes a score gets the same bits.
-__device__ __forceinline__ float idx_score(const uint32_t (&w)[8], const float* qi) {
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    acc = __fmaf_rn(qi[2 * c], bf16_lo(w[c]), acc);
-    acc = __fmaf_rn(qi[2 * c + 1], bf16_hi(w[c]), acc);
-  }
-  return acc;
-}
-
 // Key of the absolute score grid with bins of width 1/inv_delta.
 __device__ __forceinline__ int score_key(float s, float inv_delta) {
   float k = floorf(s * inv_delta);
