@@ -48,6 +48,12 @@ __device__ __forceinline__ void load_q_rope(TileSmem<G>& sm, const uint16_t* q_h
   sm.qs[h][i + 64] = (float)(y * c + x * s) * scale;
 }
 
+// Copy the rotated, pre-scaled queries of G heads (src[h * D + i]) into sm.qs.
+template <int G>
+__device__ __forceinline__ void load_q_ready(TileSmem<G>& sm, const float* src) {
+  for (int e = threadIdx.x; e < G * RTP_D; e += blockDim.x) (&sm.qs[0][0])[e] = src[e];
+}
+
 // Attend one tile of nr rows (ids in sm.rows, per-row head masks in sm.masks).
 // kbase / vbase point at row 0 of this KV head's cache.  All NT threads call it.
 template <int G, int NT>

@@ -53,20 +53,21 @@ constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
 constexpr int kScanCopies = 16;       // words per histogram bin in the scan
 
+// floor(f * 2^36) for a finite f >= 0, from the bits: the 24-bit significand
+// shifted by the exponent (equal to converting f * 2^36 in double and truncating).
+__device__ __forceinline__ unsigned long long fx36(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const int e = (int)(u >> 23) - 127;
+  if (e < -36) return 0ull;  // zero, subnormals and everything below 2^-36
+  const unsigned long long mant = (u & 0x7fffffu) | 0x800000u;
+  const int sh = e + 13;  // f * 2^36 = mant * 2^(e - 23 + 36)
+  return sh >= 0 ? mant << sh : mant >> (-sh);
+}
+static_assert(kFxCand == 68719476736.0, "candidate masses are 2^36 fixed point");
+
 // Inverse bin width of coarse grid c: bins of 2^c score units (exact in fp32).
 __device__ __forceinline__ float coarse_inv(int c) { return 1.0f / (float)(1 << c); }
 
-__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // ------------------------------------------------------------------ index scores
 
@@ -360,8 +361,10 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   const size_t base = (size_t)pair * p.nA;
   // every summary this thread needs is loaded up front (one round trip)
   constexpr int kMaxPer = 8;  // blocks per thread held in registers (nA <= 2048)
+  constexpr int kPre = 2;     // of which the fine bins too (nA <= 512: one round trip)
   float mbv[kMaxPer];
   unsigned long long zbv[kMaxPer];
+  uint4 bpre[kPre][kNB / 4];
   int nmine = 0;
   float ml = -INFINITY;
 #pragma unroll
@@ -373,9 +376,26 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
       const size_t so = (base + k) * G + h;
       mbv[u] = p.blk_m[so];
       zbv[u] = p.blk_z[so];
+      if (u < kPre) {
+        const uint4* src = (const uint4*)(p.blk_bins + so * kNB);
+#pragma unroll
+        for (int e = 0; e < kNB / 4; ++e) bpre[u < kPre ? u : 0][e] = src[e];
+      }
       ml = fmaxf(ml, mbv[u]);
       nmine = u + 1;
     }
+  }
+  if (tid < kD / 2) {
+    // this head's query, rotated at the newest position (fp64 angles) and scaled
+    // into the log2 domain, once for the select and finish passes
+    const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+    const uint16_t* q = p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G + h) * kD;
+    double c, sn;
+    sincos((double)(p.N - 1) * p.theta[tid], &sn, &c);
+    const double x = (double)bf16_to_f32(q[tid]), y = (double)bf16_to_f32(q[tid + 64]);
+    const float scale = p.attn_scale * kLog2e;
+    p.qrope[(size_t)unit * kD + tid] = (float)(x * c - y * sn) * scale;
+    p.qrope[(size_t)unit * kD + tid + 64] = (float)(y * c + x * sn) * scale;
   }
   for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
   ml = wave_max(ml);
@@ -397,17 +417,17 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
     // each thread fills only its own row
 #pragma unroll
     for (int i = 0; i < kNB; ++i) rows[tid][i] = 0ull;
-    auto add_block = [&](int k, float mb, unsigned long long zb) {
-      const size_t so = (base + k) * G + h;
+    auto load_bins = [&](int k, uint4 (&v)[kNB / 4]) {
+      const uint4* src = (const uint4*)(bins + ((base + k) * G + h) * kNB);
+#pragma unroll
+      for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
+    };
+    auto add_block = [&](float mb, unsigned long long zb, const uint4 (&v)[kNB / 4]) {
       const int ktb = score_key(mb, inv);
       if (round == 0) {
         const double e_top_b = (double)(ktb + 1) * (double)kDelta;
         z += (double)zb / kFxZ * (counting ? 1.0 : exp(e_top_b - (double)m));
       }
-      const uint4* src = (const uint4*)(bins + so * kNB);
-      uint4 v[kNB / 4];
-#pragma unroll
-      for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
       const int shift = kt - ktb;
       const unsigned* vv = (const unsigned*)v;
 #pragma unroll
@@ -415,12 +435,25 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
         if (j + shift < kNB) rows[tid][j + shift] += vv[j];
     };
 #pragma unroll
-    for (int u = 0; u < kMaxPer; ++u)
-      if (u < nmine) add_block(tid + u * NT, mbv[u], zbv[u]);
-    for (int k = tid + kMaxPer * NT; k < p.nA; k += NT)
-      add_block(k, p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h]);
+    for (int u = 0; u < kMaxPer; ++u) {
+      if (u < nmine) {
+        uint4 v[kNB / 4];
+        if (u < kPre && round == 0) {
+#pragma unroll
+          for (int e = 0; e < kNB / 4; ++e) v[e] = bpre[u < kPre ? u : 0][e];
+        } else {
+          load_bins(tid + u * NT, v);
+        }
+        add_block(mbv[u], zbv[u], v);
+      }
+    }
+    for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) {
+      uint4 v[kNB / 4];
+      load_bins(k, v);
+      add_block(p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h], v);
+    }
     if (round == 0) {
-      z = wave_sum_f64(z);
+      z = wave_sum_d(z);
       if (lane == 0) redz[wave] = z;
     }
     __syncthreads();
@@ -523,8 +556,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
     const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
     uint4 a[S::TPW][S::CH];
     load_score_tiles<G>(idx, tok0, p.N, a);
-    load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, p.N - 1, p.theta,
-                   p.attn_scale * kLog2e);
+    load_q_ready<G>(sm, p.qrope + (size_t)pair * G * kD);
     uint4 bq[3][S::CH];
     make_score_b<G>(qi_s, bq);
     f32x4_t sc[S::TPW];
@@ -588,12 +620,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
       if (t < p.N && t < p.n_sink) dm[k] = (1u << G) - 1u;
       cnt += dm[k] ? 1u : 0u;
     }
-    unsigned incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
+    const unsigned incl = wave_incl_sum_u32(cnt);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     unsigned off = incl - cnt;
@@ -663,10 +690,7 @@ __device__ uint32_t bisect_key(unsigned C, const float2* cand, const unsigned* b
       const float2* src = cand + (size_t)bb * kPassTokens;
       for (unsigned c = tid; c < n; c += NT) {
         const float sv = src[c].x;
-        fn(f32_ord(sv),
-           (unsigned long long)((counting ? 1.0
-                                          : (double)__builtin_amdgcn_exp2f((sv - m) * kLog2e)) *
-                                kFxCand));
+        fn(f32_ord(sv), fx36(counting ? 1.f : __builtin_amdgcn_exp2f((sv - m) * kLog2e)));
       }
     }
   };
@@ -675,11 +699,8 @@ __device__ uint32_t bisect_key(unsigned C, const float2* cand, const unsigned* b
     kmin = min(kmin, k);
     kmax = max(kmax, k);
   });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   __shared__ uint32_t rmin[NT / 64], rmax[NT / 64];
   if (lane == 0) {
     rmin[wave] = kmin;
@@ -738,11 +759,8 @@ __device__ uint32_t radix_key(Visit&& visit, double need_fx) {
     kmin = min(kmin, k);
     kmax = max(kmax, k);
   });
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     rmin[wave] = kmin;
     rmax[wave] = kmax;
@@ -770,12 +788,7 @@ __device__ uint32_t radix_key(Visit&& visit, double need_fx) {
     __syncthreads();
     // thread t holds digit 255 - t; inclusive running mass from the highest digit
     const unsigned long long hv = hist[255 - tid];
-    unsigned long long inc = hv;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
+    unsigned long long inc = wave_incl_sum_u64(hv);
     if (lane == 63) wtot[wave] = inc;
     if (tid == 0) dig_s = -1;
     __syncthreads();
@@ -820,8 +833,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const ThrInfo t = p.thr[unit];
   const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
   const float2* cand = p.cand + (size_t)unit * p.N;
-  load_q_rope<1>(sm, p.q_pre + ((size_t)b * p.Hq + qh) * kD, 0, p.N - 1, p.theta,
-                 p.attn_scale * kLog2e);
+  load_q_ready<1>(sm, p.qrope + (size_t)unit * kD);
   // candidate counts of the pass-B blocks and their exclusive prefix (fixed order)
   const bool small_nA = p.nA <= kMaxBlocksLds;
   unsigned C = 0u;
@@ -834,12 +846,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
         boff[bb] = run;
         run += blk_cnt[bb];
       }
-      unsigned inc = run;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned v = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += v;
-      }
+      const unsigned inc = wave_incl_sum_u32(run);
       if (lane == 63) wtot[wave] = inc;
       __syncthreads();
       unsigned base = inc - run;
@@ -882,9 +889,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const bool counting = p.budget > 0;
   // a candidate's mass, 2^36 fixed point relative to the global max
   auto cand_mass = [&](float sv) {
-    return (unsigned long long)((counting ? 1.0
-                                          : (double)__builtin_amdgcn_exp2f((sv - t.m) * kLog2e)) *
-                                kFxCand);
+    return fx36(counting ? 1.f : __builtin_amdgcn_exp2f((sv - t.m) * kLog2e));
   };
   uint32_t kstar = 0u;
   float tau = -INFINITY;
@@ -1158,6 +1163,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   char* cc = take((size_t)P * G * nA * 4);
   char* uc = take((size_t)P * 4);
   char* qi = take((size_t)P * G * kR * 4);
+  char* qr = take((size_t)P * G * kD * 4);
   char* bm = take((size_t)P * nA * G * 4);
   char* bz = take((size_t)P * nA * G * 8);
   char* bb = take((size_t)P * nA * G * kNB * 4);
@@ -1174,6 +1180,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
     plan->cand_blk = (unsigned*)cc;
     plan->uni_cnt = (unsigned*)uc;
     plan->qi = (float*)qi;
+    plan->qrope = (float*)qr;
     plan->blk_m = (float*)bm;
     plan->blk_z = (unsigned long long*)bz;
     plan->blk_bins = (unsigned*)bb;

@@ -1,6 +1,8 @@
 // Device helpers shared by the gfx950 kernels of the head-wise sparse attention step.
 #pragma once
 
+#include <climits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,27 +54,102 @@ __device__ __forceinline__ float ord_f32(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// ------------------------------------------------------------------ wave64 scans
+
+// Inclusive scans over the 64 lanes of a wave on DPP: row shifts by 1, 2, 4, 8
+// within each row of 16 lanes, then the broadcasts of lane 15 into rows 1 and 3
+// and of lane 31 into rows 2 and 3 (GFX9 DPP controls).  Every step is a VALU
+// move, no LDS round trip.  A lane whose source is outside its row (or whose row
+// is masked off) takes the identity.  Reductions read lane 63.
+namespace dpp {
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t mov(uint32_t ident, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)x, CTRL, ROWS, 0xf, false);
+}
+}  // namespace dpp
+
+// x of the lane that supplies step CTRL, or ident; 32-bit payloads.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t x, uint32_t ident, Op op) {
+  x = op(x, dpp::mov<dpp::kShr1, 0xf>(ident, x));
+  x = op(x, dpp::mov<dpp::kShr2, 0xf>(ident, x));
+  x = op(x, dpp::mov<dpp::kShr4, 0xf>(ident, x));
+  x = op(x, dpp::mov<dpp::kShr8, 0xf>(ident, x));
+  x = op(x, dpp::mov<dpp::kBcast15, 0xa>(ident, x));
+  x = op(x, dpp::mov<dpp::kBcast31, 0xc>(ident, x));
+  return x;
+}
+// 64-bit payloads: both halves move with the same control.
+template <class Op>
+__device__ __forceinline__ unsigned long long wave_scan_u64(unsigned long long x,
+                                                            unsigned long long ident, Op op) {
+  auto step = [&](auto mv) {
+    const uint32_t lo = mv((uint32_t)ident, (uint32_t)x);
+    const uint32_t hi = mv((uint32_t)(ident >> 32), (uint32_t)(x >> 32));
+    x = op(x, ((unsigned long long)hi << 32) | lo);
+  };
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kShr1, 0xf>(i, v); });
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kShr2, 0xf>(i, v); });
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kShr4, 0xf>(i, v); });
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kShr8, 0xf>(i, v); });
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kBcast15, 0xa>(i, v); });
+  step([](uint32_t i, uint32_t v) { return dpp::mov<dpp::kBcast31, 0xc>(i, v); });
+  return x;
+}
+__device__ __forceinline__ uint32_t lane63_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ unsigned long long lane63_u64(unsigned long long x) {
+  return ((unsigned long long)lane63_u32((uint32_t)(x >> 32)) << 32) | lane63_u32((uint32_t)x);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t x) {
+  return wave_scan_u32(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ unsigned long long wave_incl_sum_u64(unsigned long long x) {
+  return wave_scan_u64(x, 0ull, [](unsigned long long a, unsigned long long b) { return a + b; });
+}
+
 // ------------------------------------------------------------------ wave64 reductions
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  const uint32_t r = wave_scan_u32(__float_as_uint(v), __float_as_uint(-INFINITY),
+                                   [](uint32_t a, uint32_t b) {
+                                     return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                                   });
+  return __uint_as_float(lane63_u32(r));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const uint32_t r = wave_scan_u32(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float(lane63_u32(r));
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  const unsigned long long r =
+      wave_scan_u64((unsigned long long)__double_as_longlong(v), 0ull,
+                    [](unsigned long long a, unsigned long long b) {
+                      return (unsigned long long)__double_as_longlong(
+                          __longlong_as_double((long long)a) + __longlong_as_double((long long)b));
+                    });
+  return __longlong_as_double((long long)lane63_u64(r));
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  return v;
+  const uint32_t r = wave_scan_u32((uint32_t)v, (uint32_t)INT_MIN, [](uint32_t a, uint32_t b) {
+    return (uint32_t)max((int)a, (int)b);
+  });
+  return (int)lane63_u32(r);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return lane63_u32(wave_scan_u32(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return lane63_u32(wave_scan_u32(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  return lane63_u64(wave_incl_sum_u64(v));
 }
 
 // Key of the absolute score grid with bins of width 1/inv_delta.

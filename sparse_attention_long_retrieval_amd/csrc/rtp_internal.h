@@ -68,6 +68,7 @@ struct DecPlan {
   unsigned* cand_blk;  // [P*G][nA]    candidates of each pass-B block
   unsigned* uni_cnt;   // [P]          zeroed by the threshold kernel
   float* qi;                      // [P][G][16] (idx_scale folded in)
+  float* qrope;                   // [P][G][128] RoPE'd queries, attn_scale * log2(e) folded in
   float* blk_m;                   // [P][nA][G]   block max score
   unsigned long long* blk_z;      // [P][nA][G]   sum exp(s - e_top) * 2^50, e_top the
                                   //              upper edge of the block max's bin
