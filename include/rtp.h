@@ -215,9 +215,10 @@ rtp_status rtp_swa_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32
 
 /*
  * Ring caches for local heads.  A local (streaming) head only ever reads the sinks
- * and its sliding window ([techwalker] §2 and §8; the "5x KV compression" of the
- * zhichai summary §02 comes from dropping the rest), so its K/V can live in a ring
- * instead of the full cache:
+ * and its sliding window ([techwalker] §2 and §8), and only retrieval heads keep the
+ * full KV cache ([ngjoo] abstract; [v2] finding 1: turning most heads into SWA is
+ * what compresses the KV cache), so a local head's K/V can live in a ring instead of
+ * the full cache:
  *   k_ring, v_ring  [B][n_loc][n_sink + ring_len][D] bf16, device, local KV heads
  *                   in ascending head order (the heads not in ret_kv_heads);
  *   token j < n_sink sits in row j, token j >= n_sink in row
