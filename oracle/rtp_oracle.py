@@ -37,6 +37,9 @@ Steps, in the order the step performs them:
   swa_keys      local heads: sliding window of W tokens ending at the query,
                 plus the sinks ([techwalker] §2, §8: window 8192 + 4 sinks)
   prefill_row   the decode computation for query row t with keys j <= t
+  kmeans_index  the V2 cluster index: k-means over the index rows ([v2] finding 3)
+  cluster_head  decode through it: coarse match of the centres, top-p over clusters,
+                exact attention over the hit clusters' tokens ([v2] finding 3)
 
 Readings where the pages are silent (each repeated at the function):
   * idx_scale multiplies the dot product; 1.0 in every workload.
@@ -311,3 +314,126 @@ def caches_for(wl, rows_needed: Optional[Dict[int, np.ndarray]] = None):
                 idx[b, i, s0:s0 + (1 << 16)] = f64_to_bf16(
                     bf16_to_f64(wl.k_pre[b, h, s0:s0 + (1 << 16)]) @ bf16_to_f64(wl.w_k[i]))
     return kc, wl.v, idx
+
+
+# ---------------------------------------------------------------- V2 cluster index
+#
+# [v2] finding 3: the low-rank index rows of the cached tokens are grouped into K
+# semantic clusters (K = 128 in the article's example); a query first matches the K
+# cluster centres (coarse), and full attention then runs only over the tokens of the
+# clusters it hits (fine).  The retrieval heads of the V2 recipe combine the low-rank
+# projection, this cluster index and dynamic top-p ([v2] summary of the recipe).
+#
+# Readings where the pages give only the outline:
+#  * clustering is Lloyd's k-means on the 16-dim index rows with squared Euclidean
+#    distance, seeded with the index rows of K caller-chosen tokens and run for a
+#    caller-chosen number of iterations; a final assignment to the last centres
+#    defines the clusters;
+#  * the nearest-centre decision is taken in fp32, the precision of the kernel that
+#    takes it: the distance accumulates (x_d - c_d)^2 over d = 0..15 in order, each
+#    subtraction, square and addition rounded to fp32; ties go to the lowest centre;
+#  * a centre is the mean of its rows: every bf16 value becomes an integer multiple of
+#    2^-24 (truncated toward zero; exact for |x| >= 2^-17), the integers are summed,
+#    and the sum is divided in fp64 and rounded to fp32; an empty cluster keeps its
+#    centre;
+#  * the coarse match scores a cluster by sigma_c = fp32(idx_scale <qi, centre_c>) and
+#    weighs it by its size: w_c = n_c exp(sigma_c - max sigma), the softmax mass its
+#    tokens would have if each scored sigma_c; the clusters hit are the top-p set of
+#    these masses (same threshold rule as tokens, ties included; p >= 1 takes every
+#    non-empty cluster);
+#  * the tokens attended are the members of the hit clusters, the tokens appended
+#    after the build (n_tokens .. pos), and the sinks.
+
+FX_CENTRE = 16777216.0   # 2^-24 units of the centre sums
+
+
+def kmeans_assign(x32: np.ndarray, c32: np.ndarray) -> np.ndarray:
+    """Nearest centre of every row (reading: fp32 distance in dimension order,
+    ties to the lowest centre)."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    c32 = np.asarray(c32, dtype=np.float32)
+    n, r = x32.shape
+    best = np.full(n, np.inf, dtype=np.float32)
+    arg = np.zeros(n, dtype=np.int64)
+    for k in range(c32.shape[0]):
+        acc = np.zeros(n, dtype=np.float32)
+        for d in range(r):
+            t = x32[:, d] - c32[k, d]
+            acc = acc + t * t
+        better = acc < best
+        best = np.where(better, acc, best)
+        arg = np.where(better, k, arg)
+    return arg
+
+
+def kmeans_centres(x_bits: np.ndarray, assign: np.ndarray, prev_c32: np.ndarray) -> np.ndarray:
+    """Means of the clusters' rows from exact integer sums (reading above); an empty
+    cluster keeps its previous centre."""
+    K, r = prev_c32.shape
+    fx = np.trunc(bf16_to_f64(x_bits) * FX_CENTRE).astype(np.int64)
+    sums = np.zeros((K, r), dtype=np.int64)
+    np.add.at(sums, np.asarray(assign, dtype=np.int64), fx)
+    cnt = np.bincount(assign, minlength=K)
+    c = np.array(prev_c32, dtype=np.float32, copy=True)
+    nz = cnt > 0
+    c[nz] = (sums[nz].astype(np.float64) /
+             (cnt[nz, None].astype(np.float64) * FX_CENTRE)).astype(np.float32)
+    return c
+
+
+def kmeans_index(index_bits: np.ndarray, init: Sequence[int], iters: int) -> Dict[str, object]:
+    """The cluster index of one retrieval KV head ([v2] finding 3): Lloyd's k-means on
+    the index rows (N, 16) seeded with the rows of tokens `init`, `iters` updates,
+    then the final assignment.  members lists the tokens grouped by cluster, in
+    ascending token order within a cluster; cluster c holds
+    members[offsets[c]:offsets[c + 1]]."""
+    index_bits = np.asarray(index_bits, dtype=np.uint16)
+    x32 = bf16_to_f64(index_bits).astype(np.float32)
+    c32 = x32[np.asarray(init, dtype=np.int64)].copy()
+    for _ in range(iters):
+        c32 = kmeans_centres(index_bits, kmeans_assign(x32, c32), c32)
+    assign = kmeans_assign(x32, c32)
+    K = c32.shape[0]
+    members = np.argsort(assign, kind="stable")
+    offsets = np.concatenate([[0], np.cumsum(np.bincount(assign, minlength=K))]).astype(np.int64)
+    return {"centroids": c32, "assign": assign, "members": members, "offsets": offsets}
+
+
+def cluster_select(qi: np.ndarray, centroids: np.ndarray, counts: np.ndarray, p: float,
+                   idx_scale: float = 1.0) -> Dict[str, object]:
+    """Coarse match and dynamic top-p over clusters (reading above): sigma_c, the
+    size-weighted masses w_c, and the hit clusters {c : n_c > 0, sigma_c >= tau_c}."""
+    sigma = (np.float64(idx_scale) * (np.asarray(centroids, dtype=np.float64) @
+                                      np.asarray(qi, dtype=np.float64))).astype(np.float32)
+    counts = np.asarray(counts, dtype=np.int64)
+    live = np.nonzero(counts > 0)[0]
+    if p >= 1.0:
+        return {"sigma": sigma, "hit": live, "tau": -np.inf}
+    s = sigma[live].astype(np.float64)
+    w = counts[live].astype(np.float64) * np.exp(s - s.max())
+    order = np.argsort(-s, kind="stable")
+    cum = np.cumsum(w[order])
+    i = int(np.searchsorted(cum, p * w.sum(), side="left"))
+    i = min(i, len(order) - 1)
+    tau = float(sigma[live][order[i]])
+    hit = live[sigma[live] >= np.float32(tau)]
+    return {"sigma": sigma, "hit": hit, "tau": tau, "W": float(w.sum())}
+
+
+def cluster_head(q_pre_row, w_q_head, k_cache_head, v_cache_head, cl: Dict[str, object],
+                 n_tokens: int, pos: int, top_p: float, n_sink: int, idx_scale: float,
+                 attn_scale: float, rope_base: float = 1e6) -> Dict[str, object]:
+    """One retrieval q-head decoding through the cluster index built over tokens
+    0 .. n_tokens-1: S = members of the hit clusters u (n_tokens .. pos) u sinks, then
+    exact attention over S."""
+    qi = query_index(q_pre_row, w_q_head)
+    counts = np.diff(np.asarray(cl["offsets"], dtype=np.int64))
+    sel = cluster_select(qi, cl["centroids"], counts, top_p, idx_scale)
+    off = np.asarray(cl["offsets"], dtype=np.int64)
+    parts = [np.asarray(cl["members"][off[c]:off[c + 1]], dtype=np.int64) for c in sel["hit"]]
+    parts.append(np.arange(n_tokens, pos + 1, dtype=np.int64))
+    S = with_sinks(np.concatenate(parts) if parts else np.zeros(0, np.int64), n_sink, pos + 1)
+    qr = rope(bf16_to_f64(q_pre_row), pos, rope_base)
+    o = attention(qr, k_cache_head[S], v_cache_head[S], attn_scale)
+    return {"out": o, "S": S, "hit": sel["hit"], "sigma": sel["sigma"], "tau": sel["tau"],
+            "qi": qi}

@@ -299,3 +299,161 @@ def test_top_k_ties_and_budget_past_n():
     assert np.array_equal(np.sort(O.top_k_set(s, 4)["set"]), [0, 2, 3, 4])
     assert np.array_equal(O.top_k_set(s, 6)["set"], np.arange(6))
     assert O.top_k_set(s, 9)["tau"] == -np.inf
+
+
+# ------------------------------------------------------------------ V2 cluster index
+
+def _rand_index_bits(rng, n, scale=1.0):
+    return O.f64_to_bf16(rng.standard_normal((n, 16)) * scale)
+
+
+def test_kmeans_assign_is_nearest_centre():
+    """Against scipy's fp64 distances: equal except where the two nearest centres are
+    within fp32 rounding of each other."""
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(400)
+    x = O.bf16_to_f64(_rand_index_bits(rng, 3000)).astype(np.float32)
+    c = rng.standard_normal((37, 16)).astype(np.float32)
+    got = O.kmeans_assign(x, c)
+    d = cdist(x.astype(np.float64), c.astype(np.float64), "sqeuclidean")
+    want = d.argmin(axis=1)
+    two = np.sort(d, axis=1)[:, :2]
+    near_tie = (two[:, 1] - two[:, 0]) <= 1e-5 * two[:, 1]
+    assert np.array_equal(got[~near_tie], want[~near_tie])
+    assert near_tie.mean() < 0.01
+
+
+def test_kmeans_ties_go_to_lowest_centre():
+    x = np.zeros((3, 16), dtype=np.float32)
+    x[1, 0] = 1.0
+    c = np.zeros((4, 16), dtype=np.float32)
+    c[0, 0], c[1, 0], c[2, 0], c[3, 0] = 2.0, 0.0, 0.0, 1.0   # rows 1 and 2 are identical
+    a = O.kmeans_assign(x, c)
+    assert a[0] == 1           # equal distance to centres 1 and 2 -> 1
+    assert a[1] == 3           # exactly on centre 3
+    assert a[2] == 1
+
+
+def test_kmeans_single_cluster_is_the_mean():
+    rng = np.random.default_rng(401)
+    bits = _rand_index_bits(rng, 5000, 3.0)
+    r = O.kmeans_index(bits, [17], iters=2)
+    mean = O.bf16_to_f64(bits).mean(axis=0)
+    assert np.all(np.abs(r["centroids"][0] - mean) <= 2.0 ** -22 * np.maximum(np.abs(mean), 1))
+    assert np.array_equal(r["assign"], np.zeros(5000))
+    assert np.array_equal(r["members"], np.arange(5000))
+    assert list(r["offsets"]) == [0, 5000]
+
+
+def test_kmeans_recovers_planted_clusters():
+    """Well-separated clusters seeded with one row of each: the partition is the planted
+    one and the centres are the members' means."""
+    rng = np.random.default_rng(402)
+    centres = rng.standard_normal((6, 16)) * 20.0
+    label = rng.integers(0, 6, 900)
+    bits = O.f64_to_bf16(centres[label] + 0.1 * rng.standard_normal((900, 16)))
+    seeds = [int(np.nonzero(label == t)[0][0]) for t in (3, 0, 5, 1, 4, 2)]
+    r = O.kmeans_index(bits, seeds, iters=3)
+    order = [3, 0, 5, 1, 4, 2]               # cluster c was seeded from planted order[c]
+    assert np.array_equal(np.asarray(order)[r["assign"]], label)
+    x = O.bf16_to_f64(bits)
+    for c, t in enumerate(order):
+        assert np.allclose(r["centroids"][c], x[label == t].mean(axis=0), atol=1e-5)
+
+
+def test_kmeans_objective_never_increases():
+    rng = np.random.default_rng(403)
+    bits = _rand_index_bits(rng, 4000)
+    x = O.bf16_to_f64(bits)
+    init = rng.choice(4000, 24, replace=False)
+    prev = np.inf
+    for it in range(6):
+        r = O.kmeans_index(bits, init, iters=it)
+        obj = ((x - r["centroids"][r["assign"]].astype(np.float64)) ** 2).sum()
+        assert obj <= prev * (1 + 1e-9), (it, obj, prev)
+        prev = obj
+
+
+def test_kmeans_empty_cluster_keeps_its_centre():
+    """Centre 2 duplicates centre 0, so the first assignment gives it no rows (ties go
+    to the lower centre) and the first update leaves it where it was."""
+    rng = np.random.default_rng(404)
+    bits = _rand_index_bits(rng, 300)
+    x32 = O.bf16_to_f64(bits).astype(np.float32)
+    assert 2 not in set(O.kmeans_assign(x32, x32[[5, 9, 5]]).tolist())
+    r = O.kmeans_index(bits, [5, 9, 5], iters=1)
+    assert np.array_equal(r["centroids"][2], x32[5])
+    assert not np.array_equal(r["centroids"][0], x32[5])
+
+
+def test_kmeans_members_grouped_by_cluster_ascending():
+    rng = np.random.default_rng(405)
+    bits = _rand_index_bits(rng, 2000)
+    r = O.kmeans_index(bits, rng.choice(2000, 16, replace=False), iters=2)
+    want = [j for _, j in sorted((int(r["assign"][j]), j) for j in range(2000))]
+    assert np.array_equal(r["members"], want)
+    assert np.array_equal(np.diff(r["offsets"]), np.bincount(r["assign"], minlength=16))
+
+
+def _select_brute(sigma, counts, p):
+    """Largest threshold t among the live sigmas whose set {sigma >= t} holds p of the
+    size-weighted mass (enumeration over thresholds)."""
+    live = [c for c in range(len(sigma)) if counts[c] > 0]
+    m = max(float(sigma[c]) for c in live)
+    w = {c: counts[c] * math.exp(float(sigma[c]) - m) for c in live}
+    W = sum(w.values())
+    best = None
+    for t in sorted({float(sigma[c]) for c in live}):
+        mass = sum(w[c] for c in live if float(sigma[c]) >= t)
+        if mass >= p * W:
+            best = t
+    return sorted(c for c in live if float(sigma[c]) >= best)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cluster_select_brute_force(seed):
+    rng = np.random.default_rng(410 + seed)
+    K = 7
+    cen = rng.standard_normal((K, 16)).astype(np.float32)
+    qi = rng.standard_normal(16).astype(np.float32)
+    counts = rng.integers(0, 50, K)
+    counts[0] = max(counts[0], 1)
+    if seed % 2:
+        cen[3] = cen[5]                           # a tie between two clusters
+    for p in (0.05, 0.3, 0.6, 0.9, 0.999):
+        r = O.cluster_select(qi, cen, counts, p)
+        assert list(np.sort(r["hit"])) == _select_brute(r["sigma"], counts, p), p
+
+
+def test_cluster_select_p_one_and_dominant_cluster():
+    cen = np.zeros((5, 16), dtype=np.float32)
+    cen[2, 0] = 30.0
+    qi = np.zeros(16, dtype=np.float32)
+    qi[0] = 1.0
+    counts = np.array([10, 0, 3, 40, 7])
+    assert list(O.cluster_select(qi, cen, counts, 1.0)["hit"]) == [0, 2, 3, 4]
+    assert list(O.cluster_select(qi, cen, counts, 0.99)["hit"]) == [2]
+
+
+def test_cluster_head_p_one_is_dense_and_keeps_tail_and_sinks():
+    wl = _small_wl(N=600)
+    kc, vc, idx = O.caches_for(wl)
+    n_tok = 520
+    rng = np.random.default_rng(420)
+    cl = O.kmeans_index(idx[0, 0, :n_tok], rng.choice(n_tok, 8, replace=False), iters=3)
+    pos = wl.N - 1
+    q = _rope_complex(O.bf16_to_f64(wl.q_pre[0, 0]), pos)
+    K = O.bf16_to_f64(O.f64_to_bf16(_rope_complex(O.bf16_to_f64(wl.k_pre[0, 0]), np.arange(wl.N))))
+    r = O.cluster_head(wl.q_pre[0, 0], wl.w_q[0], kc[0, 0], vc[0, 0], cl, n_tok, pos, 1.0,
+                       wl.n_sink, 1.0, wl.attn_scale, wl.rope_base)
+    assert np.array_equal(r["S"], np.arange(wl.N))
+    ref = _sdpa64(q, K, O.bf16_to_f64(wl.v[0, 0]), wl.attn_scale)
+    assert np.allclose(r["out"], ref, rtol=0, atol=1e-12)
+    r = O.cluster_head(wl.q_pre[0, 0], wl.w_q[0], kc[0, 0], vc[0, 0], cl, n_tok, pos, 1e-6,
+                       wl.n_sink, 1.0, wl.attn_scale, wl.rope_base)
+    assert len(r["hit"]) >= 1
+    members = np.concatenate([cl["members"][cl["offsets"][c]:cl["offsets"][c + 1]]
+                              for c in r["hit"]])
+    assert set(range(wl.n_sink)) <= set(r["S"].tolist())
+    assert set(range(n_tok, wl.N)) <= set(r["S"].tolist())
+    assert set(r["S"].tolist()) == set(members.tolist()) | set(range(wl.n_sink)) | set(range(n_tok, wl.N))
