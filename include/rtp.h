@@ -12,7 +12,9 @@
  *                low-dimensional projections, dynamic top-p thresholding).
  *   [v2]         RTPurboV2 article (aitntnews): finding 1 (85% of heads are
  *                streaming heads served by a sliding window), finding 2
- *                (16-dim projector), finding 4 (top-p).
+ *                (16-dim projector), finding 3 (clustering of the index rows,
+ *                coarse match of the centres, fine attention in the hit
+ *                clusters), finding 4 (top-p).
  *
  * Conventions shared by every call
  *   - bf16 tensors are raw bf16 bit patterns (rtp_bf16), row-major, contiguous,
@@ -101,7 +103,14 @@ typedef struct {
 } rtp_debug_out;
 
 /* Operation ids for rtp_workspace_size(). */
-enum { RTP_OP_DECODE = 0, RTP_OP_PREFILL = 1, RTP_OP_SWA = 2, RTP_OP_APPEND = 3 };
+enum {
+  RTP_OP_DECODE = 0,
+  RTP_OP_PREFILL = 1,
+  RTP_OP_SWA = 2,
+  RTP_OP_APPEND = 3,
+  RTP_OP_CLUSTER_BUILD = 4,  /* Tq = n_clusters, seq_len = n_tokens */
+  RTP_OP_CLUSTER_DECODE = 5  /* Tq = n_clusters */
+};
 
 /*
  * rtp_index_append - write T new tokens at positions start_pos .. start_pos+T-1.
@@ -249,6 +258,75 @@ rtp_status rtp_swa_attn_ring(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
                              int32_t q_start, int32_t Tq, int32_t ring_len,
                              const rtp_bf16* k_ring, const rtp_bf16* v_ring, float attn_scale,
                              rtp_bf16* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Cluster index of the retrieval KV heads ([v2] finding 3: after the low-rank
+ * projection the index rows of related tokens sit close together, so the cached
+ * tokens are grouped into K clusters, K = 128 in the article's example; a query
+ * first matches the K centres and full attention then runs only over the tokens of
+ * the clusters it hits; the V2 retrieval heads combine this index with the low-rank
+ * projection and dynamic top-p).  Per (batch, retrieval KV head) pair, over the
+ * index rows of tokens 0 .. n_tokens-1:
+ *   centroids  [B][n_ret][K][16] float, device
+ *   members    [B][n_ret][n_tokens] int32, device: token ids grouped by cluster,
+ *              ascending within a cluster
+ *   offsets    [B][n_ret][K + 1] int32, device: cluster c holds
+ *              members[offsets[c] .. offsets[c+1]-1]
+ * K = n_clusters, 1 .. 256.  Index values must satisfy |x| < 2^15.
+ */
+
+/*
+ * rtp_cluster_build - Lloyd's k-means over the index rows.
+ *   index   [B][n_ret][max_seq][16] bf16, device, read (rtp_index_append's output)
+ *   init    [B][n_ret][K] int32, device: the tokens whose index rows seed the
+ *           centres (the caller's random draw); entries are clamped into
+ *           0 .. n_tokens-1
+ *   iters   centre updates.  Each update assigns every row to its nearest centre
+ *           (squared distance accumulated over the 16 dimensions in order, every
+ *           subtraction, square and addition rounded to fp32; ties go to the lowest
+ *           centre) and moves each centre to the mean of its rows (the rows summed
+ *           exactly as integers in 2^-24 units, truncated toward zero, divided in
+ *           fp64 and rounded to fp32; a centre without rows stays).  A last
+ *           assignment to the final centres defines members and offsets.
+ * The result is deterministic: every run gives the same bits.
+ * Workspace: op RTP_OP_CLUSTER_BUILD (Tq = n_clusters, seq_len = n_tokens).
+ * Errors: RTP_ERR_SHAPE if n_clusters is outside 1 .. 256 or n_tokens outside
+ *   1 .. max_seq; RTP_ERR_RANGE if iters is outside 0 .. 10000; RTP_ERR_WORKSPACE,
+ *   RTP_ERR_NULL, RTP_ERR_ALIGN as for the other calls (init, members and offsets
+ *   4-byte aligned).
+ */
+rtp_status rtp_cluster_build(const rtp_layer_desc* desc, const rtp_bf16* index, int32_t n_tokens,
+                             int32_t n_clusters, int32_t iters, const int32_t* init,
+                             float* centroids, int32_t* members, int32_t* offsets,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_decode_cluster_attn - the decode step of every retrieval q-head through the
+ * cluster index built over tokens 0 .. n_tokens-1 (n_tokens <= seq_len):
+ *   sigma_c = idx_scale <qi, centroid_c>, qi = q_pre . W_q as for the indexer;
+ *   w_c = n_c exp(sigma_c - max sigma) over the clusters with n_c > 0 members;
+ *   C = {c : n_c > 0, sigma_c >= tau}, tau the sigma at which the cumulative w in
+ *       descending sigma first reaches top_p * sum w (ties included; top_p = 1
+ *       takes every non-empty cluster);
+ *   S = the members of C, plus tokens n_tokens .. seq_len-1 (appended after the
+ *       build), plus the n_sink sinks; exact attention over S, query at position
+ *       seq_len-1, as for rtp_decode_sparse_attn.
+ * Arguments as for rtp_decode_sparse_attn; centroids, members, offsets as written
+ * by rtp_cluster_build with the same n_clusters and n_tokens.  dbg (optional):
+ * sel_idx / sel_count give S per retrieval q-head, tau gives tau.
+ * Workspace: op RTP_OP_CLUSTER_DECODE (Tq = n_clusters).
+ * Errors: RTP_ERR_SHAPE if n_clusters is outside 1 .. 256; RTP_ERR_RANGE if seq_len
+ *   is outside 1 .. max_seq, n_tokens outside 1 .. seq_len or top_p outside (0, 1];
+ *   otherwise as for rtp_decode_sparse_attn.
+ */
+rtp_status rtp_decode_cluster_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                   const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                   const rtp_bf16* v_cache, const float* centroids,
+                                   const int32_t* members, const int32_t* offsets,
+                                   int32_t n_clusters, int32_t n_tokens, int32_t seq_len,
+                                   float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                                   const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                                   void* stream);
 
 /*
  * rtp_workspace_size - bytes of workspace an operation needs.

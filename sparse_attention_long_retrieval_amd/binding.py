@@ -18,13 +18,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librtp.so")
 
 OP_DECODE, OP_PREFILL, OP_SWA, OP_APPEND = 0, 1, 2, 3
+OP_CLUSTER_BUILD, OP_CLUSTER_DECODE = 4, 5
 
 STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE",
           4: "RTP_ERR_RANGE", 5: "RTP_ERR_UNSUPPORTED", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
 
 EXPORTED = ["rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk", "rtp_swa_attn",
             "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version",
-            "rtp_decode_topk", "rtp_ring_append", "rtp_swa_attn_ring"]
+            "rtp_decode_topk", "rtp_ring_append", "rtp_swa_attn_ring", "rtp_cluster_build",
+            "rtp_decode_cluster_attn"]
 
 
 class RtpError(RuntimeError):
@@ -72,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.rtp_swa_attn.argtypes = [dp, vp, i32, i32, vp, vp, f32, vp, vp, sz, vp]
         L.rtp_ring_append.argtypes = [dp, vp, vp, i32, i32, i32, vp, vp, vp]
         L.rtp_swa_attn_ring.argtypes = [dp, vp, i32, i32, i32, vp, vp, f32, vp, vp, sz, vp]
+        L.rtp_cluster_build.argtypes = [dp, vp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.rtp_decode_cluster_attn.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                              f32, f32, f32, vp, ctypes.POINTER(DebugOut), vp,
+                                              sz, vp]
         L.rtp_workspace_size.argtypes = [dp, i32, i32, i32, ctypes.POINTER(sz)]
         L.rtp_status_string.argtypes = [ctypes.c_int]
         L.rtp_status_string.restype = ctypes.c_char_p
@@ -80,7 +86,8 @@ def lib() -> ctypes.CDLL:
         L.rtp_abi_version.restype = ctypes.c_int32
         for name in ("rtp_index_append", "rtp_decode_sparse_attn", "rtp_decode_topk",
                      "rtp_prefill_chunk", "rtp_swa_attn", "rtp_workspace_size",
-                     "rtp_ring_append", "rtp_swa_attn_ring"):
+                     "rtp_ring_append", "rtp_swa_attn_ring", "rtp_cluster_build",
+                     "rtp_decode_cluster_attn"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -241,3 +248,27 @@ def swa_attn_ring(layer: Layer, q_pre, q_start: int, Tq: int, ring_len: int, k_r
     _check(lib().rtp_swa_attn_ring(layer.desc(), _p(q_pre), q_start, Tq, ring_len, _p(k_ring),
                                    _p(v_ring), attn_scale, _p(out), _p(workspace),
                                    _nbytes(workspace), _stream(stream)))
+
+
+def cluster_build(layer: Layer, index, n_tokens: int, n_clusters: int, iters: int, init,
+                  centroids, members, offsets, workspace, stream=None) -> None:
+    """k-means cluster index over the index rows of tokens 0 .. n_tokens-1 of every
+    retrieval KV head (see rtp_cluster_build); init is an int32 device tensor."""
+    _check(lib().rtp_cluster_build(layer.desc(), _p(index), n_tokens, n_clusters, iters, _p(init),
+                                   _p(centroids), _p(members), _p(offsets), _p(workspace),
+                                   _nbytes(workspace), _stream(stream)))
+
+
+def decode_cluster_attn(layer: Layer, q_pre, w_q, k_cache, v_cache, centroids, members,
+                        offsets, n_clusters: int, n_tokens: int, seq_len: int, top_p: float,
+                        out, workspace, idx_scale: float = 1.0,
+                        attn_scale: Optional[float] = None, debug: Optional[Debug] = None,
+                        stream=None) -> None:
+    """The decode step through the cluster index (see rtp_decode_cluster_attn)."""
+    if attn_scale is None:
+        attn_scale = 1.0 / math.sqrt(layer.head_dim)
+    _check(lib().rtp_decode_cluster_attn(
+        layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(centroids), _p(members),
+        _p(offsets), n_clusters, n_tokens, seq_len, top_p, idx_scale, attn_scale, _p(out),
+        None if debug is None else debug.ref(), _p(workspace), _nbytes(workspace),
+        _stream(stream)))

@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librtp.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["append.hip", "decode.hip", "swa.hip", "swa_prefill.hip", "prefill.hip", "api.cpp"]
+SOURCES = ["append.hip", "decode.hip", "swa.hip", "swa_prefill.hip", "prefill.hip", "cluster.hip",
+           "api.cpp"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -162,6 +162,17 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
       }
       *bytes = rtp::prefill_workspace(desc->batch, desc->n_ret, G, Tq, seq_len, nullptr, nullptr);
       return RTP_OK;
+    case RTP_OP_CLUSTER_BUILD:
+      if (Tq < 1 || Tq > rtp::kClMaxK)
+        return fail(RTP_ERR_SHAPE, "n_clusters %d outside [1, %d]", Tq, rtp::kClMaxK);
+      *bytes = rtp::cluster_build_workspace(desc->batch * desc->n_ret, Tq, seq_len, nullptr,
+                                            nullptr);
+      return RTP_OK;
+    case RTP_OP_CLUSTER_DECODE:
+      if (Tq < 1 || Tq > rtp::kClMaxK)
+        return fail(RTP_ERR_SHAPE, "n_clusters %d outside [1, %d]", Tq, rtp::kClMaxK);
+      *bytes = rtp::cluster_decode_workspace(desc->batch * desc->n_ret, G, Tq, nullptr, nullptr);
+      return RTP_OK;
     default: return fail(RTP_ERR_RANGE, "unknown op %d", op);
   }
 }
@@ -439,6 +450,117 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
   rtp::prefill_workspace(desc->batch, desc->n_ret, G, Tq, n_keys, &p, (char*)workspace);
   hipError_t e = rtp::launch_prefill(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(RTP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return RTP_OK;
+}
+
+rtp_status rtp_cluster_build(const rtp_layer_desc* desc, const rtp_bf16* index, int32_t n_tokens,
+                             int32_t n_clusters, int32_t iters, const int32_t* init,
+                             float* centroids, int32_t* members, int32_t* offsets,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  RTP_TRY(check_desc(desc));
+  if (n_clusters < 1 || n_clusters > rtp::kClMaxK)
+    return fail(RTP_ERR_SHAPE, "n_clusters %d outside [1, %d]", n_clusters, rtp::kClMaxK);
+  if (n_tokens < 1 || n_tokens > desc->max_seq)
+    return fail(RTP_ERR_SHAPE, "n_tokens %d outside [1, max_seq %d]", n_tokens, desc->max_seq);
+  if (iters < 0 || iters > 10000) return fail(RTP_ERR_RANGE, "iters %d outside [0, 10000]", iters);
+  if (desc->n_ret == 0) return RTP_OK;
+  if ((int64_t)desc->batch * desc->n_ret > 65535)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret > 65535");
+  RTP_TRY(check_dev(index, "index"));
+  RTP_TRY(check_dev(init, "init", 4));
+  RTP_TRY(check_dev(centroids, "centroids"));
+  RTP_TRY(check_dev(members, "members", 4));
+  RTP_TRY(check_dev(offsets, "offsets", 4));
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  const int P = desc->batch * desc->n_ret;
+  const size_t need = rtp::cluster_build_workspace(P, n_clusters, n_tokens, nullptr, nullptr);
+  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rtp::ClBuildPlan p = {};
+  p.index = index;
+  p.init = init;
+  p.centroids = centroids;
+  p.members = members;
+  p.offsets = offsets;
+  p.P = P;
+  p.K = n_clusters;
+  p.n_tok = n_tokens;
+  p.max_seq = desc->max_seq;
+  rtp::cluster_build_workspace(P, n_clusters, n_tokens, &p, (char*)workspace);
+  hipError_t e = rtp::launch_cluster_build(p, iters, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "cluster build launch: %s", hipGetErrorString(e));
+  return RTP_OK;
+}
+
+rtp_status rtp_decode_cluster_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                   const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                   const rtp_bf16* v_cache, const float* centroids,
+                                   const int32_t* members, const int32_t* offsets,
+                                   int32_t n_clusters, int32_t n_tokens, int32_t seq_len,
+                                   float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                                   const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                                   void* stream) {
+  RTP_TRY(check_desc(desc));
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
+  if (n_clusters < 1 || n_clusters > rtp::kClMaxK)
+    return fail(RTP_ERR_SHAPE, "n_clusters %d outside [1, %d]", n_clusters, rtp::kClMaxK);
+  if (seq_len < 1 || seq_len > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "seq_len %d outside [1, max_seq %d]", seq_len, desc->max_seq);
+  if (n_tokens < 1 || n_tokens > seq_len)
+    return fail(RTP_ERR_RANGE, "n_tokens %d outside [1, seq_len %d]", n_tokens, seq_len);
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return fail(RTP_ERR_RANGE, "top_p must lie in (0, 1]");
+  if (!std::isfinite(idx_scale) || !std::isfinite(attn_scale))
+    return fail(RTP_ERR_RANGE, "idx_scale and attn_scale must be finite");
+  if (dbg && dbg->sel_idx && dbg->sel_cap < 1) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
+  if (desc->n_ret == 0) return RTP_OK;
+  if ((int64_t)desc->batch * desc->n_ret * G > 65535)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > 65535");
+  RTP_TRY(check_dev(q_pre, "q_pre"));
+  RTP_TRY(check_dev(w_q, "w_q"));
+  RTP_TRY(check_dev(k_cache, "k_cache"));
+  RTP_TRY(check_dev(v_cache, "v_cache"));
+  RTP_TRY(check_dev(centroids, "centroids"));
+  RTP_TRY(check_dev(members, "members", 4));
+  RTP_TRY(check_dev(offsets, "offsets", 4));
+  RTP_TRY(check_dev(out, "out"));
+  RTP_TRY(check_dev(workspace, "workspace", 256));
+  const int P = desc->batch * desc->n_ret;
+  const size_t need = rtp::cluster_decode_workspace(P, G, n_clusters, nullptr, nullptr);
+  if (ws_bytes < need) return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  rtp::ClDecPlan p = {};
+  p.q_pre = q_pre;
+  p.w_q = w_q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.centroids = centroids;
+  p.members = members;
+  p.offsets = offsets;
+  p.out = out;
+  p.B = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.Hkv = desc->n_kv_heads;
+  p.G = G;
+  p.n_ret = desc->n_ret;
+  p.max_seq = desc->max_seq;
+  p.K = n_clusters;
+  p.n_tok = n_tokens;
+  p.N = seq_len;
+  p.n_sink = desc->n_sink;
+  p.P = P;
+  for (int i = 0; i < desc->n_ret; ++i) p.ret_kv[i] = desc->ret_kv_heads[i];
+  p.top_p = top_p;
+  p.idx_scale = idx_scale;
+  p.attn_scale = attn_scale;
+  rope_theta(desc->rope_base, p.theta);
+  rtp::cluster_decode_workspace(P, G, n_clusters, &p, (char*)workspace);
+  if (dbg) {
+    p.dbg_idx = dbg->sel_idx;
+    p.dbg_cnt = dbg->sel_count;
+    p.dbg_tau = dbg->tau;
+    p.dbg_cap = dbg->sel_cap;
+  }
+  hipError_t e = rtp::launch_cluster_decode(p, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "cluster decode launch: %s", hipGetErrorString(e));
   return RTP_OK;
 }
 

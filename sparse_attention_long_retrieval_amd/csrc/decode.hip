@@ -1138,6 +1138,11 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_merge(const DecPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_merge, dim3(p.P * p.G, kD / kMergeDims), dim3(kMergeThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecPlan& p, hipStream_t s) {
   switch (p.G) {
     case 1: return launch_decode_g<1>(p, s);

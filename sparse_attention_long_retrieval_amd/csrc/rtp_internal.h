@@ -201,7 +201,58 @@ struct PfPlan {
 };
 
 // Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
+// ------------------------------------------------------------------ cluster index
+
+constexpr int kClMaxK = 256;      // clusters per (batch, retrieval KV head)
+constexpr int kClTokens = 2048;   // tokens per block of the assignment passes
+constexpr int kClNF = 64;         // attention blocks per (pair, q-head)
+
+// k-means over the index rows of every (batch, retrieval KV head) pair.
+struct ClBuildPlan {
+  const uint16_t* index;  // [P][max_seq][16]
+  const int* init;        // [P][K] seed tokens
+  float* centroids;       // [P][K][16]
+  int* members;           // [P][n_tok]
+  int* offsets;           // [P][K + 1]
+  int P, K, n_tok, nb, max_seq;
+  // workspace
+  unsigned long long* acc;  // [P][K][16] centre sums, 2^-24 units (two's complement)
+  unsigned* cnt;            // [P][K]     rows per centre
+  int* assign;              // [P][n_tok] final assignment
+  unsigned* bcnt;           // [P][nb][K] rows per (block, cluster), then the block's bases
+};
+
+// Decode through the cluster index.
+struct ClDecPlan {
+  const uint16_t* q_pre;
+  const uint16_t* w_q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const float* centroids;  // [P][K][16]
+  const int* members;      // [P][n_tok]
+  const int* offsets;      // [P][K + 1]
+  uint16_t* out;
+  int B, Hq, Hkv, G, n_ret, max_seq, K, n_tok, N, n_sink, P, nF;
+  int ret_kv[kMaxKv];
+  float top_p, idx_scale, attn_scale;
+  double theta[kD / 2];
+  // workspace
+  int* sel;       // [P*G][K]     hit clusters, ascending id
+  int* pref;      // [P*G][K + 1] exclusive prefix of their sizes
+  int* nsel;      // [P*G]
+  float* tau;     // [P*G]
+  float* qrope;   // [P*G][128]
+  float* partF;   // [P*G][nF][kPartStride]
+  // debug (device pointers or null)
+  int32_t* dbg_idx;
+  int32_t* dbg_cnt;
+  float* dbg_tau;
+  int dbg_cap;
+};
+
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
+size_t cluster_build_workspace(int P, int K, int n_tok, ClBuildPlan* plan, char* base);
+size_t cluster_decode_workspace(int P, int G, int K, ClDecPlan* plan, char* base);
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base);
 
 size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* plan, char* base);
@@ -210,6 +261,9 @@ hipError_t launch_append(const AppendPlan& p, hipStream_t s);
 hipError_t launch_prefill(const PfPlan& p, hipStream_t s);
 hipError_t launch_prefill_debug_all(const PfPlan& p, hipStream_t s);
 hipError_t launch_decode(const DecPlan& p, hipStream_t s);
+hipError_t launch_merge(const DecPlan& p, hipStream_t s);
+hipError_t launch_cluster_build(const ClBuildPlan& p, int iters, hipStream_t s);
+hipError_t launch_cluster_decode(const ClDecPlan& p, hipStream_t s);
 hipError_t launch_swa_decode(const SwaPlan& p, hipStream_t s);
 hipError_t launch_swa_prefill(const SwaPlan& p, hipStream_t s);
 

@@ -136,3 +136,33 @@ def test_ring_validation():
     # a call writing more tokens than ring rows
     st = R.lib().rtp_ring_append(layer.desc(), fake, fake, 0, 600, 555, fake, fake, None)
     assert st == 4
+
+
+def test_cluster_validation():
+    """Cluster calls reject bad sizes before any launch."""
+    import ctypes
+    import sparse_attention_long_retrieval_amd as R
+    layer = R.Layer(1, 8, 2, 4096, [0], n_sink=4, window=256)
+    fake = ctypes.c_void_p(0x10000)
+    L = R.lib()
+    ws = R.workspace_size(layer, R.OP_CLUSTER_BUILD, 3000, Tq=128)
+    assert ws > 0
+    for K, n_tok, iters, want in ((0, 3000, 2, 3), (257, 3000, 2, 3), (128, 5000, 2, 3),
+                                  (128, 0, 2, 3), (128, 3000, -1, 4)):
+        st = L.rtp_cluster_build(layer.desc(), fake, n_tok, K, iters, fake, fake, fake, fake,
+                                 fake, ws, None)
+        assert st == want, (K, n_tok, iters, st)
+    st = L.rtp_cluster_build(layer.desc(), fake, 3000, 128, 2, fake, fake, fake, fake, fake,
+                             ws - 1, None)
+    assert st == 6
+    wsd = R.workspace_size(layer, R.OP_CLUSTER_DECODE, 4000, Tq=128)
+    assert wsd > 0
+    for K, n_tok, seq, p, want in ((128, 4001, 4000, 0.9, 4), (128, 3000, 4097, 0.9, 4),
+                                   (128, 3000, 4000, 0.0, 4), (128, 3000, 4000, 1.5, 4),
+                                   (300, 3000, 4000, 0.9, 3)):
+        st = L.rtp_decode_cluster_attn(layer.desc(), fake, fake, fake, fake, fake, fake, fake, K,
+                                       n_tok, seq, p, 1.0, 0.088, fake, None, fake, wsd, None)
+        assert st == want, (K, n_tok, seq, p, st)
+    st = L.rtp_decode_cluster_attn(layer.desc(), fake, fake, fake, fake, fake, fake, fake, 128,
+                                   3000, 4000, 0.9, 1.0, 0.088, fake, None, fake, wsd - 1, None)
+    assert st == 6
