@@ -338,6 +338,46 @@ def decode_leg(args):
     ring["local_kv_bytes_full_cache"] = B * n_loc * N * 512
     ring["local_kv_bytes_ring"] = B * n_loc * (wl.n_sink + ring_len) * 512
 
+    # ---- the V2 cluster index (K = 128 clusters, three updates) and decode through it
+    K_CL, IT_CL = 128, 3
+    seeds = np.stack([np.random.default_rng(wl.seed + i).choice(N, K_CL, replace=False)
+                      for i in range(B * wl.n_ret)]).astype(np.int32)
+    init = torch.from_numpy(seeds).cuda()
+    cen = torch.empty((B * wl.n_ret, K_CL, 16), dtype=torch.float32, device="cuda")
+    mem = torch.empty((B * wl.n_ret, N), dtype=torch.int32, device="cuda")
+    off = torch.empty((B * wl.n_ret, K_CL + 1), dtype=torch.int32, device="cuda")
+    wsb = torch.zeros(R.workspace_size(layer, R.OP_CLUSTER_BUILD, N, Tq=K_CL), dtype=torch.uint8,
+                      device="cuda")
+    wsc = torch.zeros(R.workspace_size(layer, R.OP_CLUSTER_DECODE, N, Tq=K_CL),
+                      dtype=torch.uint8, device="cuda")
+    build_ms = []
+    for i in range(3):
+        flush_caches(flush)
+        hip.record(e0, stream)
+        R.cluster_build(layer, index, N, K_CL, IT_CL, init, cen, mem, off, wsb)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        build_ms.append(hip.elapsed_ms(e0, e1))
+    dbg = R.Debug(B * wl.n_ret * G, N)
+    R.decode_cluster_attn(layer, q, w_q, k_cache, v_cache, cen, mem, off, K_CL, N, N, top_p,
+                          out, wsc, debug=dbg)
+    torch.cuda.synchronize()
+    cl_sizes = [int(c) for c in dbg.sel_count.cpu().numpy()]
+    del dbg
+    t_ms = []
+    for i in range(max(5, args.steps // 4)):
+        flush_caches(flush)
+        hip.record(e0, stream)
+        R.decode_cluster_attn(layer, q, w_q, k_cache, v_cache, cen, mem, off, K_CL, N, N, top_p,
+                              out, wsc)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        t_ms.append(hip.elapsed_ms(e0, e1))
+    cluster = {"clusters": K_CL, "updates": IT_CL, "build_ms": round(float(np.mean(build_ms)), 3),
+               "decode_retrieval_us": round(float(np.mean(t_ms)) * 1e3, 2),
+               "top_p_retrieval_us": topk_us["top_p_retrieval_us"], "set_sizes": cl_sizes}
+    del cen, mem, off, wsb, wsc, init
+
     # ---- algorithmic bytes of one step
     lo = max(0, N - 1 - wl.window + 1)
     swa_rows = min(wl.n_sink, lo) + (N - 1 - lo + 1)
@@ -383,6 +423,7 @@ def decode_leg(args):
         "phases_us": phases_us,
         "fixed_budget": topk_us,
         "local_ring": ring,
+        "cluster_index": cluster,
         "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),

@@ -205,7 +205,7 @@ struct PfPlan {
 
 constexpr int kClMaxK = 256;      // clusters per (batch, retrieval KV head)
 constexpr int kClTokens = 2048;   // tokens per block of the assignment passes
-constexpr int kClNF = 64;         // attention blocks per (pair, q-head)
+constexpr int kClNF = 256;        // attention blocks per (pair, q-head)
 
 // k-means over the index rows of every (batch, retrieval KV head) pair.
 struct ClBuildPlan {
