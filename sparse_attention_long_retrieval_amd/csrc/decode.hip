@@ -236,7 +236,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
   for (int e = tid; e < G * kNB * kScanCopies; e += NT) (&bins[0][0][0])[e] = 0u;
   for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
-  if (tid < kNB) bscale[tid] = expf((float)tid * kDelta);
+  if (tid < kNB) bscale[tid] = expf((float)tid * kDelta) * kFxBin;
   __syncthreads();
   {
     // qi = q . W_q (fp32): four threads per output, 32 terms each, (p0+p1)+(p2+p3)
@@ -261,13 +261,18 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   score_tiles<G>(a, bq, sc);
   const bool hv = h < G;
   float mloc = -INFINITY;
+  if (G < 4 || tok0 + kPassTokens > p.N) {
+    // padding heads and tokens past N score -inf (full blocks of real heads skip this)
+#pragma unroll
+    for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!hv || tok0 + score_token<G>(T, r) >= p.N) sc[T][r] = -INFINITY;
+  }
 #pragma unroll
   for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (!hv || tok0 + score_token<G>(T, r) >= p.N) sc[T][r] = -INFINITY;
-      mloc = fmaxf(mloc, sc[T][r]);
-    }
+    for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[T][r]);
   mloc = head_lanes_max<G>(mloc);
   if (lane < G) red_m[wave][lane] = mloc;
   __syncthreads();
@@ -287,21 +292,16 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   const float e_top = (float)(kt + 1) * kDelta;  // exact: a multiple of 0.5
   const int copy = (lane / S::GE) & (kScanCopies - 1);
   float z = 0.f;
+  if (counting) {
 #pragma unroll
-  for (int T = 0; T < S::TPW; ++T)
+    for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sv = sc[T][r];
-      if (sv > -INFINITY) {
-        const float wt = counting ? 1.f : __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
-        z += wt;
-        const int j = kt - score_key(sv, kInvDelta);
-        if (j < kNB) {
-          // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1]
-          const float wb = counting ? 1.f : fminf(wt * bscale[j], 1.0f);
-          atomicAdd(&bins[hs][j][copy], (unsigned)(wb * kFxBin + 0.5f));
-        }
-        if (counting) {
+      for (int r = 0; r < 4; ++r) {
+        const float sv = sc[T][r];
+        if (sv > -INFINITY) {
+          z += 1.f;
+          const int j = kt - score_key(sv, kInvDelta);
+          if (j < kNB) atomicAdd(&bins[hs][j][copy], (unsigned)kFxBin);
 #pragma unroll
           for (int c = 0; c < kCoarseGrids; ++c) {
             const int jc = ktc_s[c][hs] - score_key(sv, coarse_inv(c));
@@ -309,7 +309,22 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
           }
         }
       }
-    }
+  } else {
+#pragma unroll
+    for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // a -inf score weighs 0 and its key (-1e9) lies far outside the bins
+        const float sv = sc[T][r];
+        const float wt = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
+        z += wt;
+        const unsigned j = (unsigned)(kt - score_key(sv, kInvDelta));
+        if (j < (unsigned)kNB) {
+          // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1], 2^-20 units
+          atomicAdd(&bins[hs][j][copy], (unsigned)__builtin_fmaf(wt, bscale[j], 0.5f));
+        }
+      }
+  }
   {
     const unsigned long long zfx = head_lanes_sum<G>((unsigned long long)((double)z * kFxZ));
     if (lane < G) zred[wave][lane] = zfx;

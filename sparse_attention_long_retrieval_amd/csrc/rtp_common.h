@@ -152,11 +152,10 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return lane63_u64(wave_incl_sum_u64(v));
 }
 
-// Key of the absolute score grid with bins of width 1/inv_delta.
+// Key of the absolute score grid with bins of width 1/inv_delta (clamped to
+// +-1e9 so that differences of keys stay inside int; -inf maps to -1e9).
 __device__ __forceinline__ int score_key(float s, float inv_delta) {
-  float k = floorf(s * inv_delta);
-  k = fminf(fmaxf(k, -1.0e9f), 1.0e9f);
-  return (int)k;
+  return (int)__builtin_amdgcn_fmed3f(floorf(s * inv_delta), -1.0e9f, 1.0e9f);
 }
 
 }  // namespace rtp
