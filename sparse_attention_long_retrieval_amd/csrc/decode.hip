@@ -581,21 +581,25 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
     const int hs = hv ? h : 0;
     const int mode = mode_s[hs], kbnd = kb_s[hs];
     const float inv = inv_s[hs];
+    // definite: key > dthr; candidate otherwise when key >= clo (mode 0: the boundary
+    // key; mode 1: every key at or below it; mode 2: every key is definite)
+    const int dthr = mode == 2 ? INT_MIN : kbnd;
+    const int clo = mode == 0 ? kbnd : INT_MIN;
+    const bool full = G >= 4 && tok0 + kPassTokens <= p.N;
     uint32_t cbits = 0u;
     unsigned ccount = 0u;
 #pragma unroll
     for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int tl = score_token<G>(T, r);
-        if (hv && tok0 + tl < p.N) {
+        if (full || (hv && tok0 + score_token<G>(T, r) < p.N)) {
           const int key = score_key(sc[T][r], inv);
-          if (mode == 2 || key > kbnd) {
-            atomicOr(&dmask[tl], 1u << h);
-          } else if ((mode == 0 && key == kbnd) || (mode == 1 && key <= kbnd)) {
+          if (key > dthr) {
+            atomicOr(&dmask[score_token<G>(T, r)], 1u << h);
+          } else if (key >= clo) {
             cbits |= 1u << (4 * T + r);
             ++ccount;
-            if (inspect) atomicOr(&cmask[tl], 1u << h);
+            if (inspect) atomicOr(&cmask[score_token<G>(T, r)], 1u << h);
           }
         }
       }
