@@ -758,75 +758,96 @@ __device__ uint32_t bisect_key(unsigned C, const float2* cand, const unsigned* b
 }
 
 // The same threshold digit by digit.  The keys' common leading bits are fixed
-// first; the rest are resolved in digits of up to 8 bits from the highest
-// differing bit down (at most four passes).  Each pass builds a 256-bucket
+// first; the rest are resolved in digits of up to 11 bits from the highest
+// differing bit down (at most three passes).  Each pass builds a 2048-bucket
 // histogram of the masses of the candidates that match the bits fixed so far,
 // scans it from the highest digit, and fixes the digit at which the running mass
 // reaches what is still needed.  Integer masses make every pass exact.  visit(fn)
-// calls fn(key, mass) once for every candidate the calling thread owns.
+// calls fn(key, mass) once for every candidate the calling thread owns.  When the
+// caller knows bounds [lo_key, hi_key] of the keys (the boundary bin's edges) the
+// pass that finds them is skipped.
 template <int NT, class Visit>
-__device__ uint32_t radix_key(Visit&& visit, double need_fx) {
-  static_assert(NT == 256, "one thread per digit");
+__device__ uint32_t radix_key(Visit&& visit, double need_fx, bool have_range, uint32_t lo_key,
+                              uint32_t hi_key) {
+  constexpr int RB = 11, NBK = 1 << RB, PER = NBK / NT;
+  static_assert(NBK % NT == 0, "every thread owns whole buckets");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __shared__ unsigned long long hist[256];
+  __shared__ unsigned long long hist[NBK];
   __shared__ unsigned long long wtot[NT / 64];
   __shared__ uint32_t rmin[NT / 64], rmax[NT / 64];
-  __shared__ int dig_s;
-  __shared__ unsigned long long above_s;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  visit([&](uint32_t k, unsigned long long) {
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
-  });
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane == 0) {
-    rmin[wave] = kmin;
-    rmax[wave] = kmax;
-  }
-  __syncthreads();
-  kmin = rmin[0];
-  kmax = rmax[0];
-  for (int q = 1; q < NT / 64; ++q) {
-    kmin = min(kmin, rmin[q]);
-    kmax = max(kmax, rmax[q]);
+  // the digit found and the mass above it, one slot per level parity
+  __shared__ int dig_s[2];
+  __shared__ unsigned long long above_s[2];
+  uint32_t kmin = lo_key, kmax = hi_key;
+  if (!have_range) {
+    kmin = 0xffffffffu;
+    kmax = 0u;
+    visit([&](uint32_t k, unsigned long long) {
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    });
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
+    if (lane == 0) {
+      rmin[wave] = kmin;
+      rmax[wave] = kmax;
+    }
+    __syncthreads();
+    kmin = rmin[0];
+    kmax = rmax[0];
+    for (int q = 1; q < NT / 64; ++q) {
+      kmin = min(kmin, rmin[q]);
+      kmax = max(kmax, rmax[q]);
+    }
   }
   if (kmin == kmax) return kmin;  // one distinct key: it is the threshold either way
   double need = need_fx;
   int top = 31 - __clz((int)(kmin ^ kmax));  // highest differing bit
   uint32_t pmask = top == 31 ? 0u : ~((2u << top) - 1u);
   uint32_t prefix = kmin & pmask;
-  while (top >= 0) {
-    const int shift = max(top - 7, 0);
-    const uint32_t dmask = (2u << (top - shift)) - 1u;  // width top - shift + 1 <= 8
-    hist[tid] = 0ull;
+  for (int level = 0; top >= 0; ++level) {
+    const int par = level & 1;
+    const int shift = max(top - (RB - 1), 0);
+    const uint32_t dmask = (2u << (top - shift)) - 1u;  // width top - shift + 1 <= RB
+#pragma unroll
+    for (int i = 0; i < PER; ++i) hist[tid * PER + i] = 0ull;
+    if (tid == 0) dig_s[par] = -1;
     __syncthreads();
     visit([&](uint32_t k, unsigned long long w) {
       if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], w);
     });
     __syncthreads();
-    // thread t holds digit 255 - t; inclusive running mass from the highest digit
-    const unsigned long long hv = hist[255 - tid];
-    unsigned long long inc = wave_incl_sum_u64(hv);
+    // thread t owns digits NBK-1-PER*t .. NBK-PER*(t+1), highest first
+    unsigned long long v[PER], tsum = 0ull;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      v[i] = hist[NBK - 1 - (PER * tid + i)];
+      tsum += v[i];
+    }
+    const unsigned long long inc = wave_incl_sum_u64(tsum);
     if (lane == 63) wtot[wave] = inc;
-    if (tid == 0) dig_s = -1;
     __syncthreads();
-    for (int q = 0; q < wave; ++q) inc += wtot[q];
-    // the running mass grows with t: the first thread (highest digit) whose running
-    // mass reaches the need is the one whose predecessor's does not
-    if ((double)inc >= need && (double)(inc - hv) < need) {
-      dig_s = 255 - tid;
-      above_s = inc - hv;
+    unsigned long long run = inc - tsum;
+    for (int q = 0; q < wave; ++q) run += wtot[q];
+    // the running mass grows with the digit rank: the digit whose running mass
+    // reaches the need while its predecessor's does not
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const unsigned long long prev = run;
+      run += v[i];
+      if ((double)run >= need && (double)prev < need) {
+        dig_s[par] = NBK - 1 - (PER * tid + i);
+        above_s[par] = prev;
+      }
     }
     __syncthreads();
-    const int d = dig_s;
+    const int d = dig_s[par];
     // even the whole mass falls short of the need (rounding of p * Z): keep all
     if (d < 0) return kmin;
-    need -= (double)above_s;
+    need -= (double)above_s[par];
     prefix |= (uint32_t)d << shift;
     pmask |= dmask << shift;
     top = shift - 1;
-    __syncthreads();
   }
   return prefix;
 }
@@ -917,6 +938,15 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
       tau = INFINITY;
       kstar = 0xffffffffu;
     } else {
+      // in normal mode the candidates are the boundary bin's keys: its edges bound them
+      bool have_range = false;
+      uint32_t lo_key = 0u, hi_key = 0u;
+      if (t.mode == 0 && abs(t.key_bnd) < (1 << 22)) {
+        const float lo = (float)t.key_bnd / t.inv_w, hi = (float)(t.key_bnd + 1) / t.inv_w;
+        lo_key = f32_ord(lo == 0.f ? -0.f : lo);  // -0 scores fall in the bin starting at 0
+        hi_key = f32_ord(hi) - 1u;
+        have_range = true;
+      }
       if (keys_lds) {
         kstar = radix_key<NT>(
             [&](auto&& fn) {
@@ -925,7 +955,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
                 fn(k, cand_mass(ord_f32(k)));
               }
             },
-            t.need * kFxCand);
+            t.need * kFxCand, have_range, lo_key, hi_key);
       } else if (small_nA) {
         // too many for LDS: candidate g (canonical order) is found through the
         // block offsets and read from its pass-B block's region, all threads at once
@@ -942,7 +972,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
                 fn(f32_ord(sv), cand_mass(sv));
               }
             },
-            t.need * kFxCand);
+            t.need * kFxCand, have_range, lo_key, hi_key);
       } else {
         kstar = bisect_key<NT>(C, cand, blk_cnt, p.nA, t.m, t.need * kFxCand, red, counting);
       }
