@@ -65,9 +65,16 @@ rtp_status check_dev(const void* p, const char* name, size_t align = 16) {
     if (_s != RTP_OK) return _s;    \
   } while (0)
 
-// RoPE frequencies theta_i = base^(-2i/D), i < D/2, in fp64.
+// RoPE frequencies theta_i = base^(-2i/D), i < D/2, in fp64; the table of the last
+// base a thread used is kept, so steady-state calls skip the 64 pow() calls.
 void rope_theta(double base, double* theta) {
-  for (int i = 0; i < rtp::kD / 2; ++i) theta[i] = std::pow(base, -2.0 * i / rtp::kD);
+  thread_local double cached_base = 0.0;
+  thread_local double cached[rtp::kD / 2];
+  if (base != cached_base) {
+    for (int i = 0; i < rtp::kD / 2; ++i) cached[i] = std::pow(base, -2.0 * i / rtp::kD);
+    cached_base = base;
+  }
+  std::memcpy(theta, cached, sizeof(cached));
 }
 
 int swa_rows(int pos, int window, int n_sink) {

@@ -874,24 +874,34 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
   const float2* cand = p.cand + (size_t)unit * p.N;
   load_q_ready<1>(sm, p.qrope + (size_t)unit * kD);
-  // candidate counts of the pass-B blocks and their exclusive prefix (fixed order)
+  // candidate counts of the pass-B blocks and their exclusive prefix (fixed order);
+  // the counts are loaded together with the threshold state (one round trip)
   const bool small_nA = p.nA <= kMaxBlocksLds;
+  constexpr int kPerMax = kMaxBlocksLds / NT;
+  const int per = (p.nA + NT - 1) / NT;
+  const int b0 = tid * per, b1 = min(p.nA, b0 + per);
+  unsigned cnt_r[kPerMax];
+#pragma unroll
+  for (int i = 0; i < kPerMax; ++i) cnt_r[i] = (small_nA && b0 + i < b1) ? blk_cnt[b0 + i] : 0u;
   unsigned C = 0u;
   if (t.mode != 2) {
     if (small_nA) {
-      const int per = (p.nA + NT - 1) / NT;
-      const int b0 = tid * per, b1 = min(p.nA, b0 + per);
       unsigned run = 0u;
-      for (int bb = b0; bb < b1; ++bb) {
-        boff[bb] = run;
-        run += blk_cnt[bb];
+#pragma unroll
+      for (int i = 0; i < kPerMax; ++i) {
+        if (b0 + i < b1) {
+          boff[b0 + i] = run;
+          run += cnt_r[i];
+        }
       }
       const unsigned inc = wave_incl_sum_u32(run);
       if (lane == 63) wtot[wave] = inc;
       __syncthreads();
       unsigned base = inc - run;
       for (int q = 0; q < wave; ++q) base += wtot[q];
-      for (int bb = b0; bb < b1; ++bb) boff[bb] += base;
+#pragma unroll
+      for (int i = 0; i < kPerMax; ++i)
+        if (b0 + i < b1) boff[b0 + i] += base;
       if (tid == NT - 1) C_s = base + run;
     } else if (tid == 0) {
       unsigned s = 0u;
