@@ -55,6 +55,8 @@ __device__ __forceinline__ bf16x8 pf_bf16x8(uint4 v) {
 
 __global__ __launch_bounds__(256) void k_pf_qprep(PfPlan p) {
   const int t = blockIdx.x * 256 + threadIdx.x;
+  // the attend order's key counts start from zero in every call
+  for (int e = t; e < p.nbucket; e += gridDim.x * 256) p.obucket[e] = 0;
   const int vid = t >> 4, c = t & 15;
   if (vid >= p.V) return;
   const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
@@ -536,6 +538,73 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
   }
 }
 
+// ------------------------------------------------------------------ attend order
+
+// The attend kernel's vectors, bucketed by (pair, first definite 32-key block):
+// vectors whose selections start at the same block mostly select the same rows
+// (at C5 about 64 query vectors share each cluster), and running them together
+// on one XCD lets its L2 serve the shared rows.  Each vector's output is computed
+// by its own wave, so the order changes no result; positions within a bucket are
+// taken by atomics.
+__global__ __launch_bounds__(256) void k_pf_okey(PfPlan p) {
+  const int vid = blockIdx.x * 256 + threadIdx.x;
+  if (vid >= p.V) return;
+  const int bi = vid / (p.G * p.Tq);
+  const int nblk = p.nbucket / (p.B * p.n_ret) - 1;
+  int first = nblk;  // no definite word
+  for (int w = 0; w < 4; ++w) {
+    const int cnt = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+    if (cnt > 0) {
+      first = min((int)p.words[((size_t)vid * 4 + w) * p.wcap].x, nblk);
+      break;
+    }
+  }
+  const int key = bi * (nblk + 1) + first;
+  p.okey[vid] = key;
+  atomicAdd(&p.obucket[key], 1);
+}
+
+// Exclusive scan of the bucket counts in place (one block).
+__global__ __launch_bounds__(1024) void k_pf_oscan(PfPlan p) {
+  constexpr int NT = 1024;
+  __shared__ unsigned ws[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (p.nbucket + NT - 1) / NT;
+  const int e0 = tid * per, e1 = min(p.nbucket, e0 + per);
+  unsigned run = 0u;
+  for (int e = e0; e < e1; ++e) run += (unsigned)p.obucket[e];
+  const unsigned inc = wave_incl_sum_u32(run);
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  unsigned base = inc - run;
+  for (int q = 0; q < wave; ++q) base += ws[q];
+  for (int e = e0; e < e1; ++e) {
+    const unsigned c = (unsigned)p.obucket[e];
+    p.obucket[e] = (int)base;
+    base += c;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pf_oscatter(PfPlan p) {
+  const int vid = blockIdx.x * 256 + threadIdx.x;
+  if (vid >= p.V) return;
+  p.perm[atomicAdd(&p.obucket[p.okey[vid]], 1)] = vid;
+}
+
+// Position in the attend order of block b's wave w.  Blocks are handed to the 8
+// XCDs in turn (block b runs on XCD b % 8); the order is dealt to the XCDs in
+// chunks of 64 vectors (16 blocks), so that a bucket's vectors share one L2 while
+// every XCD still receives an even mix of light and heavy vectors.
+constexpr int kPfChunkBlocks = 16;
+__device__ inline int attend_pos(int b, int w) {
+  const int xcd = b % 8, j = b / 8;
+  return ((j / kPfChunkBlocks) * 8 + xcd) * (kPfChunkBlocks * 4) + (j % kPfChunkBlocks) * 4 + w;
+}
+inline int attend_blocks(int V) {
+  const int chunks = (V + kPfChunkBlocks * 4 - 1) / (kPfChunkBlocks * 4);
+  return (chunks + 7) / 8 * 8 * kPfChunkBlocks;
+}
+
 // ------------------------------------------------------------------ gather attention
 
 // LDS written by some lanes of a wave and read by others later in the same wave:
@@ -560,8 +629,9 @@ __global__ __launch_bounds__(256) void k_pf_attend(PfPlan p) {
   __shared__ float ps[4][64];
   __shared__ int rq[4][kAwQueue];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int vid = blockIdx.x * 4 + wave;
-  if (vid >= p.V) return;  // wave-uniform; the kernel has no block barrier
+  const int opos = attend_pos(blockIdx.x, wave);
+  if (opos >= p.V) return;  // wave-uniform; the kernel has no block barrier
+  const int vid = p.perm[opos];
   const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
   const int b = bi / p.n_ret, ri = bi % p.n_ret;
   const int kv = p.ret_kv[ri], h = kv * p.G + g;
@@ -586,12 +656,10 @@ __global__ __launch_bounds__(256) void k_pf_attend(PfPlan p) {
   const uint16_t* vb = p.v_cache + head;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
 
-  // Attend rows[0, n): every load of the tile is issued before the first use, so
-  // a tile costs one memory round trip.  Lane r loads key row r; row ids and
-  // probabilities reach the other lanes through readlane.
-  // Attend rows[0, n): lane r loads key row r (256 B) and computes its logit
-  // against q in LDS; for P.V each lane owns output dims 2 lane, 2 lane + 1 and
-  // reads them from 16 V rows per batch of loads.
+  // Attend rows[0, n): lane r loads key row r (256 B), all of its loads issued
+  // before the first use, and computes its logit against q in LDS; for P.V each
+  // lane owns output dims 2 lane, 2 lane + 1 and reads them from 16 V rows per
+  // batch of loads.
   float* pw = ps[wave];
   auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
     float logit = -INFINITY;
@@ -795,6 +863,10 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_wcnt = take(V * 4 * sizeof(int));
   const size_t o_cand = take(V * kPfSubLists * kPfCandSub * sizeof(float2));
   const size_t o_ccnt = take(V * kPfSubLists * sizeof(int));
+  const size_t nbucket = (size_t)B * n_ret * ((n_keys + 31) / 32 + 1);
+  const size_t o_okey = take(V * sizeof(int));
+  const size_t o_obkt = take(nbucket * sizeof(int));
+  const size_t o_perm = take(V * sizeof(int));
   if (plan && base) {
     plan->V = (int)V;
     plan->wcap = (int)wcap;
@@ -804,6 +876,10 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
     plan->wcount = (int*)(base + o_wcnt);
     plan->cand = (float2*)(base + o_cand);
     plan->ccount = (int*)(base + o_ccnt);
+    plan->okey = (int*)(base + o_okey);
+    plan->obucket = (int*)(base + o_obkt);
+    plan->perm = (int*)(base + o_perm);
+    plan->nbucket = (int)nbucket;
   }
   return off;
 }
@@ -834,8 +910,11 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
                      s, p);
   mark(2);
   hipLaunchKernelGGL(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_okey, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_oscan, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(k_pf_oscatter, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
   mark(3);
-  hipLaunchKernelGGL(k_pf_attend, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_attend, dim3(attend_blocks(p.V)), dim3(256), 0, s, p);
   mark(4);
   if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
     hipLaunchKernelGGL(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), 0, s, p);

@@ -192,6 +192,10 @@ struct PfPlan {
   int* wcount;        // [V][4]
   float2* cand;       // [V][8][kPfCandSub]  (score, key bits)
   int* ccount;        // [V][8]
+  int* okey;          // [V] attend order key: (pair, first definite 32-key block)
+  int* obucket;       // [nbucket] vectors per key, then their first position
+  int* perm;          // [V] vectors in attend order
+  int nbucket;        // P * (key blocks + 1)
   // debug (device pointers or null)
   int32_t* dbg_idx;
   int32_t* dbg_cnt;
@@ -200,7 +204,6 @@ struct PfPlan {
   hipEvent_t* events;  // phase events or null
 };
 
-// Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
 // ------------------------------------------------------------------ cluster index
 
 constexpr int kClMaxK = 256;      // clusters per (batch, retrieval KV head)
@@ -250,6 +253,7 @@ struct ClDecPlan {
   int dbg_cap;
 };
 
+// Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
 size_t cluster_build_workspace(int P, int K, int n_tok, ClBuildPlan* plan, char* base);
 size_t cluster_decode_workspace(int P, int G, int K, ClDecPlan* plan, char* base);
