@@ -382,6 +382,9 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
   if (dbg && dbg->phase_events && dbg->n_phase_events < 5)
     return fail(RTP_ERR_RANGE, "prefill records 5 phase events");
   const int n_keys = q_start + Tq;
+  if (n_keys >= rtp::kPfMaxKeys)
+    return fail(RTP_ERR_UNSUPPORTED, "q_start + Tq = %d >= %d causal keys", n_keys,
+                rtp::kPfMaxKeys);
 
   rtp::PfPlan p;
   memset(&p, 0, sizeof(p));

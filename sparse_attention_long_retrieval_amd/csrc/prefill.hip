@@ -14,18 +14,26 @@
 //                 products are exact and scores keep fp32 accuracy.
 //   k_pf_index    one block = 64 query vectors of one (batch, KV head) against
 //                 every causal key; S^T = index . qi^T on v_mfma_f32_32x32x16_bf16
-//                 (lane = query vector, 32 keys per step).  Sweeps over the keys:
+//                 (lane = query vector, 32 keys per step).  Every key gets one
+//                 integer depth code D = floor(2^17 (m - s)); bins at every level
+//                 are ranges of D, so levels nest exactly and every sweep sorts a
+//                 key into the same bin.  Sweeps over the keys:
 //                   A  max score m per vector;
-//                   B  exact mass histogram on the depth coordinate d = 2 (m - s):
-//                      128 bins of 0.25 (16 score units), weights exp(s - edge) of
-//                      their bin's upper edge in 2^-31 fixed point (order-free
-//                      integer sums), first sweep also the tail mass for Z.  The
-//                      boundary bin is where the running mass reaches p * Z; a
-//                      boundary below the window shifts the window down, one with
-//                      too many keys is refined into 128 sub-bins (up to 2 levels:
-//                      the finest bins are 7.6e-6 score units wide);
+//                   B  mass histogram over 128 bins of a window of D: a bin holds
+//                      its key count and the sum of exp(s - edge) relative to its
+//                      upper edge in 2^-21 units, packed in one 64-bit word (one
+//                      LDS atomic per key); keys below the first window collect
+//                      in a tail bin for Z.  The boundary bin is where the running
+//                      mass reaches p * Z; a boundary below the window moves the
+//                      window down, a boundary bin with more keys than one
+//                      candidate list holds is refined into 128 sub-bins (levels
+//                      of 2^14, 2^7 and 1 depth codes: 0.125, 9.8e-4, 7.6e-6
+//                      score units);
 //                   C  definite keys (above the boundary bin) as 32-bit words per
-//                      32-key block, boundary-bin keys as candidates.
+//                      32-key block, boundary-bin keys as candidates; each wave
+//                      keeps its own word and candidate lists, filled in program
+//                      order, so the lists (and the attention's row order) are
+//                      the same on every run.
 //   k_pf_resolve  exact threshold inside the boundary bin: bisection on the
 //                 ordered fp32 score with 2^-36 fixed-point masses (one wave per
 //                 vector).
@@ -41,9 +49,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kL2e = 1.4426950408889634f;
-constexpr float kFxPf = 2147483648.0f;            // 2^31: histogram weights
-constexpr double kFxPfD = 2147483648.0;
+constexpr float kPfCode = 131072.0f;              // 2^17 depth codes per score unit
+constexpr float kPfCodeMax = 1073741824.0f;       // 2^30: codes of -inf scores clamp here
+constexpr int kPfSh0 = 14;                        // first-level bin: 2^14 codes
+constexpr float kFxPf = 2097152.0f;               // 2^21: histogram weight units
+constexpr double kFxPfD = 2097152.0;
+constexpr int kPfCntShift = 43;                   // key count above the weight sum
+constexpr unsigned long long kPfMassMask = (1ull << kPfCntShift) - 1ull;
 constexpr double kFxRes = 68719476736.0;          // 2^36: candidate masses
+static_assert(kPfSubLists == 4, "one candidate list per index wave");
+static_assert(kPfBins == 128 && kPfSh0 == 2 * 7, "three levels of 128 bins over 2^14 codes");
+// a window bin's weights are at most 2^21 (+ rounding) each
+static_assert((long long)(kPfMaxKeys - 1) * ((1 << 21) + 1) < (1ll << kPfCntShift),
+              "weight sums stay below the count field");
 
 __device__ __forceinline__ bf16x8 pf_bf16x8(uint4 v) {
   bf16x8 r;
@@ -86,25 +104,43 @@ struct PfWork {
   float m;
   int status;
   int level;
-  int b0;
-  float v;      // window start (fractional depth units)
-  float binw;   // bin width
-  float vb;     // boundary bin start
-  int first;    // first histogram: also accumulate the tail mass
+  int sh;       // bin width 2^sh depth codes
+  int dw;       // window start (depth code)
+  int dq;       // boundary bin start (depth code)
+  int nwin;     // first-level windows tried
   int mode;
   double Z;
-  double above; // mass of keys above the window
+  double above; // mass of the keys above the window
   double need;
 };
+
+// Reference score of bin k of a window: its upper edge, m - (dw + k 2^sh) / 2^17,
+// rounded the same way wherever it is evaluated (the histogram weights and the
+// bin masses use the same value, so its rounding cancels).
+struct PfRef {
+  float c0, c1;
+};
+__device__ __forceinline__ PfRef pf_ref(const PfWork& w) {
+  PfRef r;
+  r.c0 = __fsub_rn(w.m, (float)w.dw * (1.f / kPfCode));
+  r.c1 = -__builtin_ldexpf(1.f, w.sh - 17);
+  return r;
+}
+__device__ __forceinline__ float pf_edge(PfRef r, unsigned k) {
+  return __builtin_fmaf((float)k, r.c1, r.c0);
+}
+// Depth code of score s under max m (s <= m; -inf scores give 2^30).
+__device__ __forceinline__ int pf_code(float s, float m_code) {
+  return (int)fminf(__builtin_fmaf(s, -kPfCode, m_code), kPfCodeMax);
+}
 
 __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
   // one extra column per row: a sink slot for out-of-window lanes (so the update
   // needs no branch) that also staggers the rows over the banks
   __shared__ unsigned long long bins[kPfVecs][kPfBins + 1];
   __shared__ float red_m[4][kPfVecs];
-  __shared__ double red_z[4][kPfVecs];
   __shared__ PfWork st[kPfVecs];
-  __shared__ int ovf[kPfVecs];
+  __shared__ int lcnt[4][kPfVecs];
   __shared__ int flags[2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -198,11 +234,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     PfWork w;
     w.m = fmaxf(fmaxf(red_m[0][tid], red_m[1][tid]), fmaxf(red_m[2][tid], red_m[3][tid]));
     w.level = 0;
-    w.b0 = 0;
-    w.v = 0.f;
-    w.binw = kPfBinW0;
-    w.vb = 0.f;
-    w.first = 1;
+    w.sh = kPfSh0;
+    w.dw = 0;
+    w.dq = 0;
+    w.nwin = 0;
     w.Z = 0.0;
     w.above = 0.0;
     w.need = 0.0;
@@ -235,65 +270,54 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     if (!needB && !needC) break;
 
     if (needB) {
-      // ---- sweep B: histogram of the window, tail mass on the first pass
+      // ---- sweep B: counts and edge-relative masses of the window's bins
       for (int e = tid; e < kPfVecs * (kPfBins + 1); e += 256) (&bins[0][0])[e] = 0ull;
       __syncthreads();
       bool act[2];
-      float mm[2], b0f[2], vv[2], ib[2], bw[2];
-      bool first[2];
+      float mc[2];
+      int dw[2], sh[2];
+      PfRef rf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const PfWork& w = st[32 * c + j];
         act[c] = w.status == kStNeedB;
-        mm[c] = w.m;
-        b0f[c] = (float)w.b0;
-        vv[c] = w.v;
-        bw[c] = w.binw;
-        ib[c] = 1.f / w.binw;  // a power of two: exact
-        first[c] = w.first != 0;
+        mc[c] = w.m * kPfCode;  // exact: a power-of-two scale
+        dw[c] = w.dw;
+        sh[c] = w.sh;
+        rf[c] = pf_ref(w);
       }
-      double tail[2] = {0.0, 0.0};
       sweep([&](int, f32x16 (&acc)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
-          float tl = 0.f;
+          unsigned long long* row = &bins[32 * c + j][0];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float s = acc[c][r];
-            const float u = fmaf(s, -2.f, 2.f * mm[c]);
-            const float x = (u - b0f[c]) - vv[c];
-            const float jf = floorf(x * ib[c]);
-            const bool inwin = jf >= 0.f && jf < (float)kPfBins;
-            // weight relative to the bin's upper edge (window) or to the max (tail);
-            // the exponent is <= 0 and exp2 of anything below -126 may flush to 0
-            const float sref = inwin ? mm[c] - 0.5f * (b0f[c] + (vv[c] + jf * bw[c])) : mm[c];
-            const float wgt = __builtin_amdgcn_exp2f((s - sref) * kL2e);
-            atomicAdd(&bins[32 * c + j][inwin ? (int)jf : kPfBins],
-                      (unsigned long long)(inwin ? (unsigned)(wgt * kFxPf) : 0u));
-            // the first window starts at the max, so nothing lies above it
-            tl += (first[c] && !inwin) ? wgt : 0.f;
+            // bins 0..127 of the window; keys outside it land in column 128 (below
+            // the first window: the tail of Z; anything else there is never read)
+            const unsigned k = min((unsigned)(pf_code(s, mc[c]) - dw[c]) >> sh[c],
+                                   (unsigned)kPfBins);
+            const float x = fminf((s - pf_edge(rf[c], k)) * kL2e, 1.f);
+            const unsigned wfx = (unsigned)__builtin_fmaf(__builtin_amdgcn_exp2f(x), kFxPf, 0.5f);
+            atomicAdd(&row[k], (1ull << kPfCntShift) | wfx);
           }
-          tail[c] += (double)tl;
         }
       });
-#pragma unroll
-      for (int c = 0; c < 2; ++c) tail[c] += __shfl_xor(tail[c], 32, 64);
-      red_z[wave][lane] = hi ? tail[1] : tail[0];
       __syncthreads();
       // ---- boundary bin per vector
       if (tid < kPfVecs && st[tid].status == kStNeedB) {
         PfWork w = st[tid];
-        // mass of bin q relative to the max (recomputed where needed: no local array)
+        const PfRef rf0 = pf_ref(w);
+        // mass of bin q relative to the max
         auto M = [&](int q) {
-          const float sref = w.m - 0.5f * ((float)w.b0 + (w.v + (float)q * w.binw));
-          return (double)bins[tid][q] / kFxPfD * exp((double)sref - (double)w.m);
+          return (double)(bins[tid][q] & kPfMassMask) / kFxPfD *
+                 exp((double)pf_edge(rf0, q) - (double)w.m);
         };
-        if (w.first) {
+        if (w.level == 0 && w.nwin == 0) {
           double tot = 0.0;
-          for (int q = 0; q < kPfBins; ++q) tot += M(q);
-          w.Z = tot + ((red_z[0][tid] + red_z[1][tid]) + (red_z[2][tid] + red_z[3][tid]));
-          w.first = 0;
+          for (int q = 0; q <= kPfBins; ++q) tot += M(q);  // with the tail
+          w.Z = tot;
         }
         const double pZ = (double)p.top_p * w.Z;
         double cum = w.above;
@@ -307,26 +331,37 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
           cum += mq;
         }
         if (found < 0) {
-          if (w.level == 0 && iter < 64) {
+          if (w.level == 0 && w.nwin < 63) {
             // the running mass stops short of p * Z inside the window: the next one
             w.above = cum;
-            w.b0 += (int)(kPfBins * kPfBinW0);
+            w.dw += kPfBins << kPfSh0;
+            w.nwin += 1;
           } else if (w.level == 0) {
             w.status = kStDone;  // no boundary found after 64 windows: keep every key
             w.mode = kPfAll;
           } else {
             // rounding between a bin and its sub-bins: the last non-empty sub-bin
             found = kPfBins - 1;
-            while (found > 0 && bins[tid][found] == 0ull) --found;
+            while (found > 0 && (bins[tid][found] >> kPfCntShift) == 0ull) --found;
             cum = w.above;
             for (int q = 0; q < found; ++q) cum += M(q);
           }
         }
         if (found >= 0) {
+          const int nq = (int)(bins[tid][found] >> kPfCntShift);
           w.need = pZ - cum;
           w.above = cum;
-          w.vb = w.v + (float)found * w.binw;
-          w.status = kStNeedC;
+          w.dq = w.dw + (found << w.sh);
+          if (nq <= kPfCandSub) {  // fits the list of whichever wave meets them
+            w.status = kStNeedC;
+          } else if (w.level < kPfLevels) {
+            // too many keys for the candidate list: 128 sub-bins of the boundary bin
+            w.level += 1;
+            w.dw = w.dq;
+            w.sh -= 7;
+          } else {
+            w.status = kStNeedCIncl;  // finest bins: select the whole boundary bin
+          }
         }
         st[tid] = w;
       }
@@ -335,50 +370,56 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     }
 
     // ---- sweep C: definite words and boundary candidates
-    if (tid < kPfVecs) ovf[tid] = 0;
+    if (tid < kPfVecs) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lcnt[q][tid] = 0;
+    }
     __syncthreads();
     {
-      bool act[2], incl[2];
-      float mm[2], b0f[2], vb[2], bw[2];
-      size_t vid[2];
+      bool act[2];
+      float mc[2];
+      int ddef[2], dq[2];
+      unsigned cw[2];
+      float2* cl[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const PfWork& w = st[32 * c + j];
         act[c] = w.status == kStNeedC || w.status == kStNeedCIncl;
-        incl[c] = w.status == kStNeedCIncl;
-        mm[c] = w.m;
-        b0f[c] = (float)w.b0;
-        vb[c] = w.vb;
-        bw[c] = w.binw;
-        vid[c] = vbase + 32 * c + j;
+        const bool incl = w.status == kStNeedCIncl;
+        mc[c] = w.m * kPfCode;
+        dq[c] = w.dq;
+        ddef[c] = incl ? w.dq + (1 << w.sh) : w.dq;  // definite: code below this
+        cw[c] = incl ? 0u : (1u << w.sh);            // candidate: code in [dq, dq + cw)
+        cl[c] = p.cand + ((vbase + 32 * c + j) * kPfSubLists + wave) * (size_t)kPfCandSub;
       }
       const bool my_act = hi ? act[1] : act[0];
       const size_t my_vid = vbase + lane;
       uint2* wl = p.words + (my_vid * 4 + wave) * (size_t)p.wcap;
       int wcnt = 0;
-      int ccnt[2] = {0, 0};
-      float2* cl[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        cl[c] = p.cand + (vid[c] * kPfSubLists + wave * 2 + hi) * (size_t)kPfCandSub;
       sweep([&](int kb, f32x16 (&acc)[2]) {
         uint32_t bits[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
-          const float defb = incl[c] ? bw[c] : 0.f;   // definite: depth below this
-          const float candb = incl[c] ? 0.f : bw[c];  // candidate: depth in [0, candb)
+          uint32_t cbits = 0u;  // candidates among the lane's 16 keys
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float s = acc[c][r];
-            const float u = fmaf(s, -2.f, 2.f * mm[c]);
-            const float x = (u - b0f[c]) - vb[c];
+            const int d = pf_code(acc[c][r], mc[c]);
             const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
-            bits[c] |= (x < defb ? 1u : 0u) << bit;
-            if (x >= 0.f && x < candb) {
-              if (ccnt[c] < kPfCandSub)
-                cl[c][ccnt[c]] = make_float2(s, __int_as_float(kb + bit));
-              ++ccnt[c];
+            bits[c] |= (d < ddef[c] ? 1u : 0u) << bit;
+            cbits |= ((unsigned)(d - dq[c]) < cw[c] ? 1u : 0u) << r;
+          }
+          // one slot reservation per lane and step, then the stores
+          if (cbits) {
+            int slot = atomicAdd(&lcnt[wave][32 * c + j], __builtin_popcount(cbits));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if ((cbits >> r) & 1u) {
+                if (slot < kPfCandSub)
+                  cl[c][slot] = make_float2(acc[c][r],
+                                            __int_as_float(kb + 8 * (r >> 2) + 4 * hi + (r & 3)));
+                ++slot;
+              }
             }
           }
         }
@@ -394,12 +435,12 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
           ++wcnt;
         }
       });
-      if (my_act) p.wcount[my_vid * 4 + wave] = wcnt;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (!act[c] || incl[c]) continue;
-        p.ccount[vid[c] * kPfSubLists + wave * 2 + hi] = min(ccnt[c], kPfCandSub);
-        if (ccnt[c] > kPfCandSub) ovf[32 * c + j] = 1;
+      if (my_act) {
+        p.wcount[my_vid * 4 + wave] = wcnt;
+        // this wave's candidate count (its own LDS counter: no barrier needed)
+        const PfWork& w = st[lane];
+        if (w.status == kStNeedC)
+          p.ccount[my_vid * kPfSubLists + wave] = min(lcnt[wave][lane], kPfCandSub);
       }
     }
     __syncthreads();
@@ -409,17 +450,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
         w.status = kStDone;
         w.mode = kPfInclusive;
       } else if (w.status == kStNeedC) {
-        if (!ovf[tid]) {
-          w.status = kStDone;
-        } else if (w.level < kPfLevels) {
-          // refine the boundary bin into kPfBins sub-bins
-          w.level += 1;
-          w.v = w.vb;
-          w.binw *= (1.f / kPfBins);
-          w.status = kStNeedB;
-        } else {
-          w.status = kStNeedCIncl;
-        }
+        w.status = kStDone;
       }
       st[tid] = w;
     }
@@ -432,9 +463,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     o.m = w.m;
     o.tau = -INFINITY;
     o.mode = w.mode;
-    o.b0 = w.b0;
-    o.vb = w.vb;
-    o.binw = w.binw;
+    o.dq = w.dq;
+    o.sh = w.sh;
     o.n_sel = 0;
     o.level = w.level;
     o.Z = w.Z;

@@ -145,11 +145,11 @@ struct AppendPlan {
 // ------------------------------------------------------------------ chunked prefill
 
 constexpr int kPfVecs = 64;                  // query vectors (row, q-head) per index block
-constexpr int kPfSubLists = 8;               // candidate sub-lists per vector
-constexpr int kPfCandSub = 256;              // candidates per sub-list
+constexpr int kPfSubLists = 4;               // candidate lists per vector (one per index wave)
+constexpr int kPfCandSub = 512;              // candidates per list
 constexpr int kPfBins = 128;                 // histogram bins per level
-constexpr float kPfBinW0 = 0.25f;            // first-level bin width, depth units 2 (m - s)
 constexpr int kPfLevels = 2;                 // refinements below the first level
+constexpr int kPfMaxKeys = 1 << 21;          // causal keys per query (histogram count field)
 
 // Selection state of one query vector after the index pass.
 enum PfMode : int {
@@ -163,9 +163,8 @@ struct PfVec {
   float m;        // max score over keys <= pos
   float tau;      // threshold score (normal mode), set by the resolver
   int mode;
-  int b0;         // integer part of the boundary bin start (depth units, depth = 2 (m - s))
-  float vb;       // fractional part of the boundary bin start
-  float binw;     // boundary bin width (depth units)
+  int dq;         // boundary bin start, depth code floor(2^17 (m - s))
+  int sh;         // boundary bin width: 2^sh depth codes
   int n_sel;      // selected candidates (normal mode)
   int level;
   double Z;       // sum exp(s - m) over keys <= pos
@@ -190,8 +189,8 @@ struct PfPlan {
   PfVec* vec;         // [V]
   uint2* words;       // [V][4][wcap]  (32-key block, bits of definite keys)
   int* wcount;        // [V][4]
-  float2* cand;       // [V][8][kPfCandSub]  (score, key bits)
-  int* ccount;        // [V][8]
+  float2* cand;       // [V][4][kPfCandSub]  (score, key bits)
+  int* ccount;        // [V][4]
   int* okey;          // [V] attend order key: (pair, first definite 32-key block)
   int* obucket;       // [nbucket] vectors per key, then their first position
   int* perm;          // [V] vectors in attend order
