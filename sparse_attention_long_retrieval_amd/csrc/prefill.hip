@@ -37,8 +37,14 @@
 //   k_pf_resolve  exact threshold inside the boundary bin: bisection on the
 //                 ordered fp32 score with 2^-36 fixed-point masses (one wave per
 //                 vector).
-//   k_pf_attend   attention of one query vector (one wave) over sinks, definite
-//                 keys and candidates >= tau, 64 gathered rows at a time.
+//   k_pf_okey ... order and cut the attend work: vectors bucketed by their first
+//   k_pf_items    definite block (neighbours share rows); a vector with more than
+//                 256 definite words is cut into items of at most 256 words of one
+//                 wave list (its candidates ride with the list's last item).
+//   k_pf_attend   persistent waves take items from per-XCD counters and attend
+//                 each over its sinks, definite keys and candidates >= tau, 64
+//                 gathered rows at a time; k_pf_merge combines the partial
+//                 (m, l, o) of cut vectors with the online-softmax rescaling.
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
@@ -73,8 +79,9 @@ __device__ __forceinline__ bf16x8 pf_bf16x8(uint4 v) {
 
 __global__ __launch_bounds__(256) void k_pf_qprep(PfPlan p) {
   const int t = blockIdx.x * 256 + threadIdx.x;
-  // the attend order's key counts start from zero in every call
+  // the attend order's key counts and the work counters start from zero in every call
   for (int e = t; e < p.nbucket; e += gridDim.x * 256) p.obucket[e] = 0;
+  if (t < 8) p.ictr[t] = 0;
   const int vid = t >> 4, c = t & 15;
   if (vid >= p.V) return;
   const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
@@ -572,7 +579,8 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
 
 // The attend kernel's vectors, bucketed by (pair, first definite 32-key block):
 // vectors whose selections start at the same block mostly select the same rows
-// (at C5 about 64 query vectors share each cluster), and running them together
+// (with 256 planted clusters over a 4096-row chunk about 64 query vectors share
+// each cluster), and running them together
 // on one XCD lets its L2 serve the shared rows.  Each vector's output is computed
 // by its own wave, so the order changes no result; positions within a bucket are
 // taken by atomics.
@@ -592,6 +600,26 @@ __global__ __launch_bounds__(256) void k_pf_okey(PfPlan p) {
   const int key = bi * (nblk + 1) + first;
   p.okey[vid] = key;
   atomicAdd(&p.obucket[key], 1);
+
+  // work items: the whole vector, or pieces of bounded size
+  const PfVec v = p.vec[vid];
+  const int pos = p.q_start + (vid / p.G) % p.Tq;
+  int n = 1;
+  if (v.mode == kPfAll) {
+    n = max(1, (pos + kPfItemKeys) / kPfItemKeys);
+  } else {
+    int wsum = 0;
+    for (int w = 0; w < 4; ++w) wsum += min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+    if (wsum > kPfItemWords) {
+      n = 0;
+      for (int w = 0; w < 4; ++w) {
+        const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+        const bool cands = v.mode == kPfNormal && p.ccount[(size_t)vid * kPfSubLists + w] > 0;
+        n += max((wc + kPfItemWords - 1) / kPfItemWords, (w == 0 || cands) ? 1 : 0);
+      }
+    }
+  }
+  p.nitem[vid] = n;
 }
 
 // Exclusive scan of the bucket counts in place (one block).
@@ -621,19 +649,62 @@ __global__ __launch_bounds__(256) void k_pf_oscatter(PfPlan p) {
   p.perm[atomicAdd(&p.obucket[p.okey[vid]], 1)] = vid;
 }
 
-// Position in the attend order of block b's wave w.  Blocks are handed to the 8
-// XCDs in turn (block b runs on XCD b % 8); the order is dealt to the XCDs in
-// chunks of 64 vectors (16 blocks), so that a bucket's vectors share one L2 while
-// every XCD still receives an even mix of light and heavy vectors.
-constexpr int kPfChunkBlocks = 16;
-__device__ inline int attend_pos(int b, int w) {
-  const int xcd = b % 8, j = b / 8;
-  return ((j / kPfChunkBlocks) * 8 + xcd) * (kPfChunkBlocks * 4) + (j % kPfChunkBlocks) * 4 + w;
+// First item of every vector, in attend order (one block), and the item total.
+__global__ __launch_bounds__(1024) void k_pf_iscan(PfPlan p) {
+  constexpr int NT = 1024;
+  __shared__ unsigned ws[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (p.V + NT - 1) / NT;
+  const int e0 = tid * per, e1 = min(p.V, e0 + per);
+  unsigned run = 0u;
+  for (int e = e0; e < e1; ++e) run += (unsigned)p.nitem[p.perm[e]];
+  const unsigned inc = wave_incl_sum_u32(run);
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  unsigned base = inc - run;
+  for (int q = 0; q < wave; ++q) base += ws[q];
+  for (int e = e0; e < e1; ++e) {
+    const int vid = p.perm[e];
+    p.ibase[vid] = (int)base;
+    base += (unsigned)p.nitem[vid];
+  }
+  if (tid == NT - 1) *p.icount = (int)base;
 }
-inline int attend_blocks(int V) {
-  const int chunks = (V + kPfChunkBlocks * 4 - 1) / (kPfChunkBlocks * 4);
-  return (chunks + 7) / 8 * 8 * kPfChunkBlocks;
+
+// The items of every vector, consecutive in attend order.
+__global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.V) return;
+  const int vid = p.perm[e];
+  const int n = p.nitem[vid];
+  int4* it = p.items + p.ibase[vid];
+  if (n == 1) {
+    it[0] = make_int4(vid, -1, 0, 0);
+    return;
+  }
+  const PfVec v = p.vec[vid];
+  if (v.mode == kPfAll) {
+    const int nk = p.q_start + (vid / p.G) % p.Tq + 1;
+    for (int k = 0; k < n; ++k) it[k] = make_int4(vid, 4, k * kPfItemKeys, min(nk, (k + 1) * kPfItemKeys));
+    return;
+  }
+  int k = 0;
+  for (int w = 0; w < 4; ++w) {
+    const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+    const bool cands = v.mode == kPfNormal && p.ccount[(size_t)vid * kPfSubLists + w] > 0;
+    if (wc == 0) {
+      if (w == 0 || cands) it[k++] = make_int4(vid, w, 0, 0);
+      continue;
+    }
+    for (int lo = 0; lo < wc; lo += kPfItemWords) it[k++] = make_int4(vid, w, lo, min(wc, lo + kPfItemWords));
+  }
 }
+
+// Items are dealt to the XCDs in chunks of 64 consecutive ones (chunk c to XCD
+// c % 8), so a vector's pieces and its bucket neighbours share an L2; within an
+// XCD waves take the next item from that XCD's counter.
+constexpr int kPfChunk = 64;
+constexpr int kPfAttendBlocks = 768;   // persistent: 3 blocks of 4 waves per CU (168 VGPRs)
 
 // ------------------------------------------------------------------ gather attention
 
@@ -646,185 +717,282 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One step of a reduce-scatter between lanes l and l ^ S over part[0, N).
+template <int S, int N>
+__device__ __forceinline__ void rs_step(float (&part)[16], int lane) {
+  const bool up = (lane & S) != 0;
+#pragma unroll
+  for (int k = 0; k < N / 2; ++k) {
+    const float send = up ? part[k] : part[k + N / 2];
+    const float keep = up ? part[k + N / 2] : part[k];
+    // swizzle in bit-mask mode: source lane = (lane & 0x1f) ^ S within 32 lanes
+    part[k] = keep + __int_as_float(
+                         __builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x1f | (S << 10)));
+  }
+}
+
 constexpr int kAwBatch = 16;                   // words expanded per batch
 constexpr int kAwQueue = kAwBatch * 32 + 64;   // one batch of words plus a partial tile
 
-// One wave per query vector, four per block, no block-wide barriers.  The wave
-// expands its selection (sinks, definite words, candidates >= tau) into a row
-// queue in LDS and attends it 64 rows at a time.  The rows are gathered from
-// all over the cache (at C5 shapes 5% of them hit L2), so the kernel is bound
-// by random 256 B reads from the Infinity Cache and HBM.
-__global__ __launch_bounds__(256) void k_pf_attend(PfPlan p) {
+// Persistent waves, four per block, no block-wide barriers.  A wave takes work
+// items from its XCD's counter; for each it expands the item's selection (sinks,
+// definite words, candidates >= tau) into a row queue in LDS and attends it 64
+// rows at a time.  The rows are gathered from all over the cache (at 256K-key
+// chunk shapes 15% of them hit L2), so the kernel is bound by random 512 B row
+// reads from the Infinity Cache and HBM.
+__global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
   __shared__ float qs[4][kD];
   __shared__ float ps[4][64];
   __shared__ int rq[4][kAwQueue];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int opos = attend_pos(blockIdx.x, wave);
-  if (opos >= p.V) return;  // wave-uniform; the kernel has no block barrier
-  const int vid = p.perm[opos];
-  const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
-  const int b = bi / p.n_ret, ri = bi % p.n_ret;
-  const int kv = p.ret_kv[ri], h = kv * p.G + g;
-  const int pos = p.q_start + row;
-  const PfVec v = p.vec[vid];
+  const int xcd = blockIdx.x % 8;
+  const int total = *p.icount;
+  const int nch = (total + kPfChunk - 1) / kPfChunk;
   int* queue = rq[wave];
   float* qv = qs[wave];
-
-  {  // RoPE'd query, scaled into the log2 domain: lane i rotates dims (i, i + 64)
-    const uint16_t* q = p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
-    double cs, sn;
-    sincos((double)pos * p.theta[lane], &sn, &cs);
-    const double x = (double)bf16_to_f32(q[lane]), y = (double)bf16_to_f32(q[lane + 64]);
-    const float sc = p.attn_scale * kL2e;
-    qv[lane] = (float)(x * cs - y * sn) * sc;
-    qv[lane + 64] = (float)(y * cs + x * sn) * sc;
-  }
-  wave_lds_sync();
-
-  const size_t head = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-  const uint16_t* kb = p.k_cache + head;
-  const uint16_t* vb = p.v_cache + head;
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-
-  // Attend rows[0, n): lane r loads key row r (256 B), all of its loads issued
-  // before the first use, and computes its logit against q in LDS; for P.V each
-  // lane owns output dims 2 lane, 2 lane + 1 and reads them from 16 V rows per
-  // batch of loads.
   float* pw = ps[wave];
-  auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
-    float logit = -INFINITY;
-    if (lane < n) {
-      const uint4* kr = (const uint4*)(kb + (size_t)rows[lane] * kD);
+  // Keys: the 16 lanes of group grp = lane / 16 read 16 B each of one 256 B row
+  // per load (rows 4 i + grp, i < 16), so a load takes whole cache lines and no
+  // line is fetched twice; lane (grp, ksub) holds q dims 8 ksub .. 8 ksub + 7.
+  const int ksub = lane & 15, grp = lane >> 4;
+  // after the reduce-scatter below, lane (grp, ksub) holds the logit of this row
+  const int my_row = 4 * ksub + grp;
+
+  for (;;) {
+    int c = 0;
+    if (lane == 0) c = atomicAdd(&p.ictr[xcd], 1);
+    c = __shfl(c, 0, 64);
+    const int gc = (c / kPfChunk) * 8 + xcd;
+    const int j = gc * kPfChunk + c % kPfChunk;
+    if (gc >= nch || j >= total) break;  // wave-uniform; every later take is past the end
+    const int4 it = p.items[j];
+    const int vid = it.x;
+    const bool whole = it.y < 0;
+    const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
+    const int b = bi / p.n_ret, ri = bi % p.n_ret;
+    const int kv = p.ret_kv[ri], h = kv * p.G + g;
+    const int pos = p.q_start + row;
+    const PfVec v = p.vec[vid];
+
+    {  // RoPE'd query, scaled into the log2 domain: lane i rotates dims (i, i + 64)
+      const uint16_t* q = p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
+      double cs, sn;
+      sincos((double)pos * p.theta[lane], &sn, &cs);
+      const double x = (double)bf16_to_f32(q[lane]), y = (double)bf16_to_f32(q[lane + 64]);
+      const float sc = p.attn_scale * kL2e;
+      qv[lane] = (float)(x * cs - y * sn) * sc;
+      qv[lane + 64] = (float)(y * cs + x * sn) * sc;
+    }
+    wave_lds_sync();
+    float qr[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qr[t] = qv[8 * ksub + t];
+
+    const size_t head = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+    const uint16_t* kb = p.k_cache + head;
+    const uint16_t* vb = p.v_cache + head;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+
+    // Attend rows[0, n): for P.V each lane owns output dims 2 lane, 2 lane + 1 and
+    // reads them from 16 V rows per batch of loads.
+    auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
       uint4 kk[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) kk[i] = kr[i];
-      float acc = 0.f;
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 4 * i + grp;
+        kk[i] = rr < n ? *(const uint4*)(kb + (size_t)rows[rr] * kD + 8 * ksub)
+                       : make_uint4(0u, 0u, 0u, 0u);
+      }
+      float part[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float4 qa = *(const float4*)&qv[8 * i];
-        const float4 qb = *(const float4*)&qv[8 * i + 4];
-        acc = fmaf(qa.x, bf16_lo(kk[i].x), acc);
-        acc = fmaf(qa.y, bf16_hi(kk[i].x), acc);
-        acc = fmaf(qa.z, bf16_lo(kk[i].y), acc);
-        acc = fmaf(qa.w, bf16_hi(kk[i].y), acc);
-        acc = fmaf(qb.x, bf16_lo(kk[i].z), acc);
-        acc = fmaf(qb.y, bf16_hi(kk[i].z), acc);
-        acc = fmaf(qb.z, bf16_lo(kk[i].w), acc);
-        acc = fmaf(qb.w, bf16_hi(kk[i].w), acc);
+        float a = qr[0] * bf16_lo(kk[i].x);
+        a = fmaf(qr[1], bf16_hi(kk[i].x), a);
+        a = fmaf(qr[2], bf16_lo(kk[i].y), a);
+        a = fmaf(qr[3], bf16_hi(kk[i].y), a);
+        a = fmaf(qr[4], bf16_lo(kk[i].z), a);
+        a = fmaf(qr[5], bf16_hi(kk[i].z), a);
+        a = fmaf(qr[6], bf16_lo(kk[i].w), a);
+        a = fmaf(qr[7], bf16_hi(kk[i].w), a);
+        part[i] = a;
       }
-      logit = acc;
-    }
-    const float m_new = fmaxf(m, wave_max(logit));
-    const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
-    const float pr = lane < n ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
-    l = l * alpha + wave_sum(pr);
-    m = m_new;
-    pw[lane] = pr;
-    wave_lds_sync();
-    o0 *= alpha;
-    o1 *= alpha;
-    for (int r0 = 0; r0 < n; r0 += 16) {
-      uint32_t vv[16];
+      // reduce-scatter over the group's 16 lanes: at the step with partner lane ^ S
+      // a lane keeps the upper half of its values if (lane & S), adds the partner's
+      // copy of them and sends the other half; it ends with the full sum of value
+      // 8 b3 + 4 b2 + 2 b1 + b0 = ksub, the logit of row 4 ksub + grp
+      rs_step<8, 16>(part, lane);
+      rs_step<4, 8>(part, lane);
+      rs_step<2, 4>(part, lane);
+      rs_step<1, 2>(part, lane);
+      const float logit = my_row < n ? part[0] : -INFINITY;
+      const float m_new = fmaxf(m, wave_max(logit));
+      const float alpha = m == -INFINITY ? 0.f : exp2f(m - m_new);
+      const float pr = my_row < n ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
+      l = l * alpha + wave_sum(pr);
+      m = m_new;
+      pw[my_row] = pr;
+      wave_lds_sync();
+      o0 *= alpha;
+      o1 *= alpha;
+      for (int r0 = 0; r0 < n; r0 += 16) {
+        uint32_t vv[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        vv[u] = r0 + u < n ? *(const uint32_t*)(vb + (size_t)rows[r0 + u] * kD + 2 * lane) : 0u;
+        for (int u = 0; u < 16; ++u)
+          vv[u] = r0 + u < n ? *(const uint32_t*)(vb + (size_t)rows[r0 + u] * kD + 2 * lane) : 0u;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float pu = r0 + u < n ? pw[r0 + u] : 0.f;
-        o0 = fmaf(pu, bf16_lo(vv[u]), o0);
-        o1 = fmaf(pu, bf16_hi(vv[u]), o1);
-      }
-    }
-    wave_lds_sync();
-  };
-
-  // The selection is produced in batches (at most 16 words = 512 keys) from, in
-  // order: the sinks (every key in keep-all mode), the definite words of the four
-  // wave ranges, the candidates at or above tau.  After each batch the full tiles
-  // of the queue are attended; the last rows once the sources are exhausted.
-  const bool words = v.mode == kPfNormal || v.mode == kPfInclusive;
-  const bool cands = v.mode == kPfNormal;
-  const int rng1 = v.mode == kPfAll ? pos + 1 : min(p.n_sink, pos + 1);
-  int rng0 = 0, src = 0, sub = 0, e0 = 0, nq = 0;
-  bool more = true;
-  while (more || nq > 0) {
-    if (more) {
-      if (src == 0) {
-        if (rng0 < rng1) {
-          const int n = min(64, rng1 - rng0);
-          if (lane < n) queue[nq + lane] = rng0 + lane;
-          nq += n;
-          rng0 += n;
-        } else {
-          src = words ? 1 : 3;
+        for (int u = 0; u < 16; ++u) {
+          const float pu = r0 + u < n ? pw[r0 + u] : 0.f;
+          o0 = fmaf(pu, bf16_lo(vv[u]), o0);
+          o1 = fmaf(pu, bf16_hi(vv[u]), o1);
         }
-      } else if (src == 1) {
-        const int cnt = sub < 4 ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap) : 0;
-        if (sub == 4) {
-          src = cands ? 2 : 3;
-          sub = 0;
-          e0 = 0;
-        } else if (e0 >= cnt) {
-          ++sub;
-          e0 = 0;
-        } else {
-          const uint2* src_w = p.words + ((size_t)vid * 4 + sub) * p.wcap;
-          const uint2 ent = (lane < kAwBatch && e0 + lane < cnt) ? src_w[e0 + lane]
-                                                                 : make_uint2(0u, 0u);
-          const int c = __popc(ent.y);
-          int incl = c;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-          }
-          int at = nq + incl - c;
-          uint32_t bits = ent.y;
-          while (bits) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1u;
-            queue[at++] = (int)(ent.x * 32u + (uint32_t)bit);
-          }
-          nq += __shfl(incl, 63, 64);
-          e0 += kAwBatch;
-        }
-      } else if (src == 2) {
-        const int cnt = sub < kPfSubLists ? p.ccount[(size_t)vid * kPfSubLists + sub] : 0;
-        if (sub == kPfSubLists) {
-          src = 3;
-        } else if (e0 >= cnt) {
-          ++sub;
-          e0 = 0;
-        } else {
-          const float2* src_c = p.cand + ((size_t)vid * kPfSubLists + sub) * kPfCandSub;
-          const float2 c = e0 + lane < cnt ? src_c[e0 + lane] : make_float2(-INFINITY, 0.f);
-          const int key = __float_as_int(c.y);
-          const bool sel = e0 + lane < cnt && c.x >= v.tau && key >= p.n_sink;
-          const unsigned long long bal = __ballot(sel);
-          if (sel) queue[nq + __popcll(bal & ((1ull << lane) - 1ull))] = key;
-          nq += __popcll(bal);
-          e0 += 64;
-        }
-      } else {
-        more = false;
       }
       wave_lds_sync();
+    };
+
+    // The item's rows are produced in batches (at most 16 words = 512 keys) from, in
+    // order: a key range (the sinks, every key in keep-all mode, or a keep-all
+    // item's range), definite words, the candidates at or above tau.  A whole
+    // vector takes all four wave lists; a piece takes words [lo, hi) of list it.y
+    // and that list's candidates when it ends the list.  After each batch the full
+    // tiles of the queue are attended; the last rows once the sources are exhausted.
+    const bool words = it.y < 4 && (v.mode == kPfNormal || v.mode == kPfInclusive);
+    int rng0 = 0, rng1 = 0;
+    if (it.y == 4) {
+      rng0 = it.z;
+      rng1 = it.w;
+    } else if (whole || (it.y == 0 && it.z == 0)) {
+      rng1 = v.mode == kPfAll ? pos + 1 : min(p.n_sink, pos + 1);
     }
-    int done = 0;
-    while (nq - done >= 64 || (!more && nq > done)) {
-      const int n = min(64, nq - done);
-      tile(queue + done, n);
-      done += n;
+    const int w_end = whole ? 4 : it.y + 1;  // lists [sub, w_end)
+    int sub = whole ? 0 : it.y;
+    int e0 = whole ? 0 : it.z;
+    bool cands = v.mode == kPfNormal && it.y < 4;
+    if (cands && !whole) cands = it.w == min(p.wcount[(size_t)vid * 4 + it.y], p.wcap);
+    int src = 0, nq = 0;
+    bool more = true;
+    while (more || nq > 0) {
+      if (more) {
+        if (src == 0) {
+          if (rng0 < rng1) {
+            const int n = min(64, rng1 - rng0);
+            if (lane < n) queue[nq + lane] = rng0 + lane;
+            nq += n;
+            rng0 += n;
+          } else {
+            src = words ? 1 : (cands ? 2 : 3);
+          }
+        } else if (src == 1) {
+          const int cnt = sub < w_end ? (whole ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap)
+                                               : it.w)
+                                      : 0;
+          if (sub == w_end) {
+            src = cands ? 2 : 3;
+            sub = whole ? 0 : it.y;
+            e0 = 0;
+          } else if (e0 >= cnt) {
+            ++sub;
+            e0 = 0;
+          } else {
+            const uint2* src_w = p.words + ((size_t)vid * 4 + sub) * p.wcap;
+            const uint2 ent = (lane < kAwBatch && e0 + lane < cnt) ? src_w[e0 + lane]
+                                                                   : make_uint2(0u, 0u);
+            const int cb = __popc(ent.y);
+            int incl = cb;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const int y = __shfl_up(incl, o, 64);
+              if (lane >= o) incl += y;
+            }
+            int at = nq + incl - cb;
+            uint32_t bits = ent.y;
+            while (bits) {
+              const int bit = __ffs(bits) - 1;
+              bits &= bits - 1u;
+              queue[at++] = (int)(ent.x * 32u + (uint32_t)bit);
+            }
+            nq += __shfl(incl, 63, 64);
+            e0 += kAwBatch;
+          }
+        } else if (src == 2) {
+          const int cnt = sub < w_end ? p.ccount[(size_t)vid * kPfSubLists + sub] : 0;
+          if (sub == w_end) {
+            src = 3;
+          } else if (e0 >= cnt) {
+            ++sub;
+            e0 = 0;
+          } else {
+            const float2* src_c = p.cand + ((size_t)vid * kPfSubLists + sub) * kPfCandSub;
+            const float2 cd = e0 + lane < cnt ? src_c[e0 + lane] : make_float2(-INFINITY, 0.f);
+            const int key = __float_as_int(cd.y);
+            const bool sel = e0 + lane < cnt && cd.x >= v.tau && key >= p.n_sink;
+            const unsigned long long bal = __ballot(sel);
+            if (sel) queue[nq + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+            nq += __popcll(bal);
+            e0 += 64;
+          }
+        } else {
+          more = false;
+        }
+        wave_lds_sync();
+      }
+      int done = 0;
+      while (nq - done >= 64 || (!more && nq > done)) {
+        const int n = min(64, nq - done);
+        tile(queue + done, n);
+        done += n;
+      }
+      const int rest = nq - done;
+      const int t = lane < rest ? queue[done + lane] : 0;
+      wave_lds_sync();
+      if (lane < rest) queue[lane] = t;
+      wave_lds_sync();
+      nq = rest;
     }
-    const int rest = nq - done;
-    const int t = lane < rest ? queue[done + lane] : 0;
-    wave_lds_sync();
-    if (lane < rest) queue[lane] = t;
-    wave_lds_sync();
-    nq = rest;
+    if (whole) {
+      uint16_t* dst = p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      *(uint32_t*)&dst[2 * lane] =
+          (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+    } else {
+      float* pr = p.part + (size_t)j * kPfPartStride;
+      if (lane == 0) {
+        pr[0] = m;
+        pr[1] = l;
+      }
+      *(float2*)&pr[2 + 2 * lane] = make_float2(o0, o1);
+    }
   }
+}
+
+// The output of every cut vector from its items' partial results: with
+// M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i (scores are in the
+// log2 domain).  One wave per vector; whole vectors were written by the attend.
+__global__ __launch_bounds__(256) void k_pf_merge(PfPlan p) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int vid = blockIdx.x * 4 + wave;
+  if (vid >= p.V) return;
+  const int n = p.nitem[vid];
+  if (n <= 1) return;
+  const float* pr = p.part + (size_t)p.ibase[vid] * kPfPartStride;
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, pr[(size_t)i * kPfPartStride]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < n; ++i) {
+      const float* q = pr + (size_t)i * kPfPartStride;
+      if (q[0] == -INFINITY) continue;  // an item with no selected row
+      const float sc = exp2f(q[0] - M);
+      const float2 o = *(const float2*)&q[2 + 2 * lane];
+      L = fmaf(sc, q[1], L);
+      o0 = fmaf(sc, o.x, o0);
+      o1 = fmaf(sc, o.y, o1);
+    }
+  }
+  const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
+  const int b = bi / p.n_ret, ri = bi % p.n_ret;
+  const int h = p.ret_kv[ri] * p.G + g;
   uint16_t* dst = p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   *(uint32_t*)&dst[2 * lane] =
       (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
 }
@@ -897,6 +1065,16 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_okey = take(V * sizeof(int));
   const size_t o_obkt = take(nbucket * sizeof(int));
   const size_t o_perm = take(V * sizeof(int));
+  // items per vector: at most one per 256 words of each list (at least one per
+  // list), or one per 8192 keys of a keep-all vector
+  const size_t per_vec = std::max<size_t>(4 * std::max<size_t>((wcap + kPfItemWords - 1) / kPfItemWords, 1),
+                                          ((size_t)n_keys + kPfItemKeys - 1) / kPfItemKeys);
+  const size_t max_items = V * per_vec;
+  const size_t o_nitem = take(V * sizeof(int));
+  const size_t o_ibase = take(V * sizeof(int));
+  const size_t o_items = take(max_items * sizeof(int4));
+  const size_t o_part = take(max_items * kPfPartStride * sizeof(float));
+  const size_t o_ictl = take(16 * sizeof(int));
   if (plan && base) {
     plan->V = (int)V;
     plan->wcap = (int)wcap;
@@ -910,6 +1088,13 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
     plan->obucket = (int*)(base + o_obkt);
     plan->perm = (int*)(base + o_perm);
     plan->nbucket = (int)nbucket;
+    plan->nitem = (int*)(base + o_nitem);
+    plan->ibase = (int*)(base + o_ibase);
+    plan->items = (int4*)(base + o_items);
+    plan->part = (float*)(base + o_part);
+    plan->icount = (int*)(base + o_ictl);
+    plan->ictr = (int*)(base + o_ictl) + 8;
+    plan->max_items = (int)max_items;
   }
   return off;
 }
@@ -943,8 +1128,11 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
   hipLaunchKernelGGL(k_pf_okey, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
   hipLaunchKernelGGL(k_pf_oscan, dim3(1), dim3(1024), 0, s, p);
   hipLaunchKernelGGL(k_pf_oscatter, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_iscan, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(k_pf_items, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
   mark(3);
-  hipLaunchKernelGGL(k_pf_attend, dim3(attend_blocks(p.V)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_attend, dim3(kPfAttendBlocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_merge, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
   mark(4);
   if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
     hipLaunchKernelGGL(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), 0, s, p);

@@ -150,6 +150,9 @@ constexpr int kPfCandSub = 512;              // candidates per list
 constexpr int kPfBins = 128;                 // histogram bins per level
 constexpr int kPfLevels = 2;                 // refinements below the first level
 constexpr int kPfMaxKeys = 1 << 21;          // causal keys per query (histogram count field)
+constexpr int kPfItemWords = 256;            // definite words per attend work item
+constexpr int kPfItemKeys = 8192;            // keys per work item of a keep-all vector
+constexpr int kPfPartStride = 132;           // floats per partial result: m, l, o[128]
 
 // Selection state of one query vector after the index pass.
 enum PfMode : int {
@@ -195,6 +198,13 @@ struct PfPlan {
   int* obucket;       // [nbucket] vectors per key, then their first position
   int* perm;          // [V] vectors in attend order
   int nbucket;        // P * (key blocks + 1)
+  int* nitem;         // [V] attend work items of the vector (1: the whole vector)
+  int* ibase;         // [V] the vector's first item
+  int4* items;        // [max_items] (vid, list or -1 whole or 4 key range, lo, hi)
+  float* part;        // [max_items][kPfPartStride] partial (m, l, o) of split vectors
+  int* icount;        // [1] items in use
+  int* ictr;          // [8] items taken per XCD
+  int max_items;
   // debug (device pointers or null)
   int32_t* dbg_idx;
   int32_t* dbg_cnt;

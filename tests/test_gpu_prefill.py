@@ -22,6 +22,9 @@ from oracle import rtp_oracle as O  # noqa: E402
 from tests import _parity as P  # noqa: E402
 
 
+kPfCandAll = 4 * 512  # candidate capacity per vector (four lists)
+
+
 def _local_rows_needed(wl, rows):
     """KV rows the oracle needs for local heads at the given chunk rows."""
     pos = wl.q_start + np.asarray(rows)
@@ -208,6 +211,24 @@ def test_prefill_retrieval_deterministic():
     a = _prefill_retrieval(wl, kc, vc, idx, 0.9, cap=wl.N)
     b = _prefill_retrieval(wl, kc, vc, idx, 0.9, cap=wl.N)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["cnt"], b["cnt"])
+
+
+def test_prefill_retrieval_split_items():
+    """Near-flat scores (q scaled by 1/32) select most of 40K keys: those vectors have far
+    more than 256 definite words, so the attend cuts them into work items (two per wave
+    list here) and merges the partial results.  Two rows keep their clustered queries
+    (smaller sets) in the same call."""
+    wl = W.random_prefill(39, 1, 4, 2, 40000, 8, [0], 256)
+    q = W.bf16_bits_to_f32(wl.q_pre)
+    q[:, :, :6] *= np.float32(1.0 / 32.0)
+    wl.q_pre = W.f32_to_bf16_bits(q)
+    kc, vc, idx = O.caches_for(wl)
+    res = _prefill_retrieval(wl, kc, vc, idx, 0.9, cap=wl.N)
+    kinds, _ = _check_retrieval(wl, kc, vc, idx, res, 0.9, range(wl.Tq))
+    cnt = res["cnt"].reshape(wl.B * wl.n_ret * wl.G, wl.Tq)
+    # more rows than 256 words of 32 keys plus every candidate list can hold: cut
+    assert (cnt[:, :6] > 256 * 32 + kPfCandAll + wl.n_sink).all(), cnt
+    print(f"split items: {kinds}, set sizes {cnt.tolist()}")
 
 
 def test_prefill_retrieval_chunked_256k_sampled():
