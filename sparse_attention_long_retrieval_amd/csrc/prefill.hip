@@ -280,34 +280,71 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
       // ---- sweep B: counts and edge-relative masses of the window's bins
       for (int e = tid; e < kPfVecs * (kPfBins + 1); e += 256) (&bins[0][0])[e] = 0ull;
       __syncthreads();
-      bool act[2];
-      float mc[2];
+      bool act[2], tail[2];
+      float mc[2], mlo[2];
+      uint32_t fspan[2];
       int dw[2], sh[2];
       PfRef rf[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const PfWork& w = st[32 * c + j];
         act[c] = w.status == kStNeedB;
+        tail[c] = w.level == 0 && w.nwin == 0;  // the first window also sums the tail
         mc[c] = w.m * kPfCode;  // exact: a power-of-two scale
         dw[c] = w.dw;
         sh[c] = w.sh;
         rf[c] = pf_ref(w);
+        // a loose float test for "the code may lie in the window": the margin covers
+        // the floor, the rounding of the bounds and of t - flo (a few ulps of numbers
+        // below 2^28); the exact test follows for the keys that pass
+        const float margin = 4.f + (float)(w.dw + (kPfBins << w.sh)) * 2.4e-7f;
+        mlo[c] = mc[c] - ((float)w.dw - margin);
+        fspan[c] = __float_as_uint((float)(kPfBins << w.sh) + 2.f * margin);
       }
+      // one key: bins 0..127 of the window; keys outside it land in column 128 (below
+      // the first window: the tail of Z; anything else there is never read)
+      auto add_key = [&](int c, float s) __attribute__((always_inline)) {
+        const unsigned k = min((unsigned)(pf_code(s, mc[c]) - dw[c]) >> sh[c], (unsigned)kPfBins);
+        const float x = fminf((s - pf_edge(rf[c], k)) * kL2e, 1.f);
+        const unsigned wfx = (unsigned)__builtin_fmaf(__builtin_amdgcn_exp2f(x), kFxPf, 0.5f);
+        atomicAdd(&bins[32 * c + j][k], (1ull << kPfCntShift) | wfx);
+      };
       sweep([&](int, f32x16 (&acc)[2]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
-          unsigned long long* row = &bins[32 * c + j][0];
+          if (tail[c]) {
+            // the first window starts at the max: dw = 0, bins of 2^14 codes, and no
+            // key lies above it (the weights stay at most 1).  floor(t / 2^14) is the
+            // code's bin exactly (the scale is a power of two), -inf scores included
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float s = acc[c][r];
-            // bins 0..127 of the window; keys outside it land in column 128 (below
-            // the first window: the tail of Z; anything else there is never read)
-            const unsigned k = min((unsigned)(pf_code(s, mc[c]) - dw[c]) >> sh[c],
-                                   (unsigned)kPfBins);
-            const float x = fminf((s - pf_edge(rf[c], k)) * kL2e, 1.f);
-            const unsigned wfx = (unsigned)__builtin_fmaf(__builtin_amdgcn_exp2f(x), kFxPf, 0.5f);
-            atomicAdd(&row[k], (1ull << kPfCntShift) | wfx);
+            for (int r = 0; r < 16; ++r) {
+              const float s = acc[c][r];
+              const float kf = fminf(
+                  floorf(__builtin_fmaf(s, -kPfCode, mc[c]) * (1.f / (1 << kPfSh0))),
+                  (float)kPfBins);
+              const unsigned k = (unsigned)kf;
+              const float x = (s - __builtin_fmaf(kf, rf[c].c1, rf[c].c0)) * kL2e;
+              const unsigned wfx =
+                  (unsigned)__builtin_fmaf(__builtin_amdgcn_exp2f(x), kFxPf, 0.5f);
+              atomicAdd(&bins[32 * c + j][k], (1ull << kPfCntShift) | wfx);
+            }
+          } else {
+            // a later window or a refinement: only keys in the window count, and
+            // there are few of them.  t = code - (dw - margin) lies in [0, span) iff its
+            // bits, as an unsigned number, are below span's (negative t has the sign
+            // bit set)
+            uint32_t inw = 0u;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float t = __builtin_fmaf(acc[c][r], -kPfCode, mlo[c]);
+              inw |= (__float_as_uint(t) < fspan[c] ? 1u : 0u) << r;
+            }
+            if (inw) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if ((inw >> r) & 1u) add_key(c, acc[c][r]);
+            }
           }
         }
       });
