@@ -548,6 +548,16 @@ def prefill_leg(args):
         torch.cuda.synchronize()
         swa_ms.append(hip.elapsed_ms(e0, e1))
     phases_ms["swa_local_alone"] = round(float(np.median(swa_ms)), 4)
+    # selected rows of the chunk (set sizes from one call with the debug counts; not timed)
+    n_vec = wl.B * wl.n_ret * wl.G * Tq
+    dbg_cnt = R.Debug(n_vec, 1)
+    R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, top_p, out, ws, debug=dbg_cnt)
+    torch.cuda.synchronize()
+    sel = dbg_cnt.sel_count.to(torch.int64)
+    sel_rows, sel_max = int(sel.sum().item()), int(sel.max().item())
+    del dbg_cnt, sel
+    attend_bytes = sel_rows * 2 * 128 * 2  # K and V rows, bf16
+    attend_gbs = attend_bytes / (phases_ms["attend"] * 1e-3) / 1e9
     ret_flops = 4.0 * 128 * sum(q0 + t + 1 for t in range(Tq)) * wl.n_ret * wl.G * B
     # local heads: causal window attention, 4 D flops (QK + PV) per (row, key) pair
     n_loc_q = (wl.Hkv - wl.n_ret) * wl.G * B
@@ -572,6 +582,11 @@ def prefill_leg(args):
                     "achieved": round(idx_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(idx_tflops / MFMA_BF16_PEAK_TFLOPS, 5),
                     "scores_per_s": round(ret_pairs / (phases_ms["index"] * 1e-3), 1)},
+        "attend": {"kernel": "k_pf_attend + k_pf_merge (gathered K/V rows of every selected set)",
+                   "selected_rows": sel_rows, "mean_rows": round(sel_rows / n_vec, 1),
+                   "max_rows": sel_max, "algorithmic_gb": round(attend_bytes / 1e9, 2),
+                   "achieved": round(attend_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(attend_gbs / HBM_PEAK_GBS, 4)},
         "dense_retrieval": {"kernel": "k_swa_prefill with the window = context (p = 1)",
                             "ms": round(dense, 4),
                             "tflops": round(ret_flops / (dense * 1e-3) / 1e12, 1),
