@@ -32,8 +32,8 @@ struct TileSmem {
 };
 
 // Rotate q (bf16, [D]) of head h at position pos with the fp64 frequency table
-// theta[64], scale, and store in qs[h].  Threads (h, i) with h < G handle
-// dimensions i and i + 64; other threads do nothing.
+// theta[64] (angles reduced in fp64), scale, and store in qs[h].  Threads (h, i)
+// with h < G handle dimensions i and i + 64; other threads do nothing.
 template <int G>
 __device__ __forceinline__ void load_q_rope(TileSmem<G>& sm, const uint16_t* q_head0,
                                             size_t head_stride, int pos, const double* theta,
@@ -41,11 +41,11 @@ __device__ __forceinline__ void load_q_rope(TileSmem<G>& sm, const uint16_t* q_h
   const int h = threadIdx.x >> 6, i = threadIdx.x & 63;
   if (h >= G) return;
   const uint16_t* q = q_head0 + (size_t)h * head_stride;
-  double c, s;
-  sincos((double)pos * theta[i], &s, &c);
-  double x = (double)bf16_to_f32(q[i]), y = (double)bf16_to_f32(q[i + 64]);
-  sm.qs[h][i] = (float)(x * c - y * s) * scale;
-  sm.qs[h][i + 64] = (float)(y * c + x * s) * scale;
+  float c, s;
+  rope_sincos(pos, theta[i], s, c);
+  const float x = bf16_to_f32(q[i]), y = bf16_to_f32(q[i + 64]);
+  sm.qs[h][i] = (x * c - y * s) * scale;
+  sm.qs[h][i + 64] = (y * c + x * s) * scale;
 }
 
 // Copy the rotated, pre-scaled queries of G heads (src[h * D + i]) into sm.qs.

@@ -286,13 +286,13 @@ __global__ __launch_bounds__(kClThreads) void k_cl_select(ClDecPlan p) {
     part[pt][c] = acc;
   }
   if (tid < kD / 2) {
-    // the rotated query, fp64 angles, scaled into the log2 domain
-    double cs, sn;
-    sincos((double)(p.N - 1) * p.theta[tid], &sn, &cs);
-    const double x = (double)bf16_to_f32(q[tid]), y = (double)bf16_to_f32(q[tid + 64]);
+    // the rotated query, scaled into the log2 domain
+    float cs, sn;
+    rope_sincos(p.N - 1, p.theta[tid], sn, cs);
+    const float x = bf16_to_f32(q[tid]), y = bf16_to_f32(q[tid + 64]);
     const float scale = p.attn_scale * kLog2eCl;
-    p.qrope[(size_t)unit * kD + tid] = (float)(x * cs - y * sn) * scale;
-    p.qrope[(size_t)unit * kD + tid + 64] = (float)(y * cs + x * sn) * scale;
+    p.qrope[(size_t)unit * kD + tid] = (x * cs - y * sn) * scale;
+    p.qrope[(size_t)unit * kD + tid + 64] = (y * cs + x * sn) * scale;
   }
   __syncthreads();
   if (tid < kR) {

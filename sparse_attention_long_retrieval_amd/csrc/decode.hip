@@ -367,9 +367,13 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float redm[NT / 64];
   __shared__ double redz[NT / 64];
-  // one padding column: the rows of consecutive threads start on different banks
-  __shared__ unsigned long long rows[NT][kNB + 1];
+  // Two rows per thread, one per block summary it holds (u32, as stored), written
+  // shifted onto this head's grid with plain stores; summaries beyond two per thread
+  // (more than 2 NT blocks) are added into colx with 64-bit LDS atomics.  One padding
+  // column: the rows of consecutive threads start on different banks.
+  __shared__ unsigned rows[2 * NT][kNB + 1];
   __shared__ unsigned long long colp[NT / kNB][kNB];
+  __shared__ unsigned long long colx[kNB];
   __shared__ double mass_s[kNB];
 
   if (tid == 0 && h == 0) p.uni_cnt[pair] = 0u;
@@ -401,16 +405,16 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
     }
   }
   if (tid < kD / 2) {
-    // this head's query, rotated at the newest position (fp64 angles) and scaled
+    // this head's query, rotated at the newest position and scaled
     // into the log2 domain, once for the select and finish passes
     const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
     const uint16_t* q = p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G + h) * kD;
-    double c, sn;
-    sincos((double)(p.N - 1) * p.theta[tid], &sn, &c);
-    const double x = (double)bf16_to_f32(q[tid]), y = (double)bf16_to_f32(q[tid + 64]);
+    float c, sn;
+    rope_sincos(p.N - 1, p.theta[tid], sn, c);
+    const float x = bf16_to_f32(q[tid]), y = bf16_to_f32(q[tid + 64]);
     const float scale = p.attn_scale * kLog2e;
-    p.qrope[(size_t)unit * kD + tid] = (float)(x * c - y * sn) * scale;
-    p.qrope[(size_t)unit * kD + tid + 64] = (float)(y * c + x * sn) * scale;
+    p.qrope[(size_t)unit * kD + tid] = (x * c - y * sn) * scale;
+    p.qrope[(size_t)unit * kD + tid + 64] = (y * c + x * sn) * scale;
   }
   for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
   ml = wave_max(ml);
@@ -429,15 +433,20 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
     const unsigned* bins =
         round ? p.blk_bins_c + (size_t)(round - 1) * p.P * p.nA * G * kNB : p.blk_bins;
     const int kt = score_key(m, inv);
-    // each thread fills only its own row
+    // each thread clears only its own two rows
 #pragma unroll
-    for (int i = 0; i < kNB; ++i) rows[tid][i] = 0ull;
+    for (int i = 0; i < kNB; ++i) {
+      rows[2 * tid][i] = 0u;
+      rows[2 * tid + 1][i] = 0u;
+    }
+    if (tid < kNB) colx[tid] = 0ull;
+    if (p.nA > 2 * NT) __syncthreads();  // colx is clear before any atomic
     auto load_bins = [&](int k, uint4 (&v)[kNB / 4]) {
       const uint4* src = (const uint4*)(bins + ((base + k) * G + h) * kNB);
 #pragma unroll
       for (int u = 0; u < kNB / 4; ++u) v[u] = src[u];
     };
-    auto add_block = [&](float mb, unsigned long long zb, const uint4 (&v)[kNB / 4]) {
+    auto add_block = [&](int slot, float mb, unsigned long long zb, const uint4 (&v)[kNB / 4]) {
       const int ktb = score_key(mb, inv);
       if (round == 0) {
         const double e_top_b = (double)(ktb + 1) * (double)kDelta;
@@ -445,9 +454,15 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
       }
       const int shift = kt - ktb;
       const unsigned* vv = (const unsigned*)v;
+      if (slot < 2) {
 #pragma unroll
-      for (int j = 0; j < kNB; ++j)
-        if (j + shift < kNB) rows[tid][j + shift] += vv[j];
+        for (int j = 0; j < kNB; ++j)
+          if (j + shift < kNB) rows[2 * tid + slot][j + shift] = vv[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+          if (j + shift < kNB && vv[j]) atomicAdd(&colx[j + shift], (unsigned long long)vv[j]);
+      }
     };
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
@@ -459,29 +474,29 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
         } else {
           load_bins(tid + u * NT, v);
         }
-        add_block(mbv[u], zbv[u], v);
+        add_block(u, mbv[u], zbv[u], v);
       }
     }
     for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) {
       uint4 v[kNB / 4];
       load_bins(k, v);
-      add_block(p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h], v);
+      add_block(2, p.blk_m[(base + k) * G + h], p.blk_z[(base + k) * G + h], v);
     }
     if (round == 0) {
       z = wave_sum_d(z);
       if (lane == 0) redz[wave] = z;
     }
     __syncthreads();
-    // column sums: thread (part, i) sums kNB rows of column i
+    // column sums: thread (part, i) sums 2 kNB rows of column i
     {
       const int i = tid % kNB, part = tid / kNB;
       unsigned long long acc = 0ull;
-      for (int r = part * kNB; r < part * kNB + kNB; ++r) acc += rows[r][i];
+      for (int r = 2 * kNB * part; r < 2 * kNB * (part + 1); ++r) acc += rows[r][i];
       colp[part][i] = acc;
     }
     __syncthreads();
     if (tid < kNB) {
-      unsigned long long acc = 0ull;
+      unsigned long long acc = colx[tid];
       for (int q = 0; q < NT / kNB; ++q) acc += colp[q][tid];
       // bin tid covers key kt - tid; its weights are relative to its upper edge
       mass_s[tid] = (double)acc / (double)kFxBin *

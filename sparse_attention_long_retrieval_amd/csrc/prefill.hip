@@ -813,12 +813,12 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
 
     {  // RoPE'd query, scaled into the log2 domain: lane i rotates dims (i, i + 64)
       const uint16_t* q = p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
-      double cs, sn;
-      sincos((double)pos * p.theta[lane], &sn, &cs);
-      const double x = (double)bf16_to_f32(q[lane]), y = (double)bf16_to_f32(q[lane + 64]);
+      float cs, sn;
+      rope_sincos(pos, p.theta[lane], sn, cs);
+      const float x = bf16_to_f32(q[lane]), y = bf16_to_f32(q[lane + 64]);
       const float sc = p.attn_scale * kL2e;
-      qv[lane] = (float)(x * cs - y * sn) * sc;
-      qv[lane + 64] = (float)(y * cs + x * sn) * sc;
+      qv[lane] = (x * cs - y * sn) * sc;
+      qv[lane + 64] = (y * cs + x * sn) * sc;
     }
     wave_lds_sync();
     float qr[8];

@@ -18,6 +18,17 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// sin and cos of the RoPE angle pos * theta (theta from the fp64 frequency table): the
+// angle is reduced to [0, 1) revolutions in fp64, then the hardware sin / cos take it
+// in revolutions.  Used for queries only (outputs carry a tolerance); cached keys are
+// rotated with fp64 sincos.
+__device__ __forceinline__ void rope_sincos(int pos, double theta, float& sn, float& cs) {
+  const double rev = (double)pos * theta * 0.15915494309189535;
+  const float f = (float)(rev - floor(rev));
+  sn = __builtin_amdgcn_sinf(f);
+  cs = __builtin_amdgcn_cosf(f);
+}
+
 // fp32 -> bf16, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
