@@ -340,10 +340,15 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
               const float t = __builtin_fmaf(acc[c][r], -kPfCode, mlo[c]);
               inw |= (__float_as_uint(t) < fspan[c] ? 1u : 0u) << r;
             }
-            if (inw) {
+            // the lane's own keys in the window, one at a time (a wave runs as many
+            // rounds as its busiest lane: one or two in a refinement)
+            while (inw) {
+              const int r = __builtin_ctz(inw);
+              inw &= inw - 1u;
+              float s = acc[c][0];
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if ((inw >> r) & 1u) add_key(c, acc[c][r]);
+              for (int u = 1; u < 16; ++u) s = r == u ? acc[c][u] : s;
+              add_key(c, s);
             }
           }
         }
