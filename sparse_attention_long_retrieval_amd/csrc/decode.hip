@@ -563,6 +563,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
 
+  // the block's index tile is loaded first, beside the threshold state (nearly every
+  // block is relevant; an irrelevant one discards it)
+  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+  const int tok0 = blk * kPassTokens;
+  uint4 a[S::TPW][S::CH];
+  load_score_tiles<G>(idx, tok0, p.N, a);
   if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
   __syncthreads();
   if (tid < G) {
@@ -581,11 +587,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   if (!relevant && tid < G) p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = 0u;
   if (relevant) {
     const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-    const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
-    const int tok0 = blk * kPassTokens;
     const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
-    uint4 a[S::TPW][S::CH];
-    load_score_tiles<G>(idx, tok0, p.N, a);
     load_q_ready<G>(sm, p.qrope + (size_t)pair * G * kD);
     uint4 bq[3][S::CH];
     make_score_b<G>(qi_s, bq);
