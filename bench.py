@@ -133,7 +133,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
-              "step shards by (batch, KV head) with no exchange, see DESIGN.md)", file=sys.stderr)
+              "step would shard by (batch, KV head), each GPU running this path on its "
+              "share with no exchange)", file=sys.stderr)
         return 2
 
     import torch
