@@ -37,10 +37,10 @@
 //   k_pf_resolve  exact threshold inside the boundary bin: bisection on the
 //                 ordered fp32 score with 2^-36 fixed-point masses (one wave per
 //                 vector).
-//   k_pf_okey ... order and cut the attend work: vectors bucketed by their first
-//   k_pf_items    definite block (neighbours share rows); a vector with more than
-//                 256 definite words is cut into items of at most 256 words of one
-//                 wave list (its candidates ride with the list's last item).
+//   k_pf_count    cut the attend work into items (a vector with more than 256
+//   ... iscatter  definite words into pieces of at most 256 words of one wave
+//                 list) and order the items by the first key block they read,
+//                 so that items reading the same rows run together.
 //   k_pf_attend   persistent waves take items from per-XCD counters and attend
 //                 each over its sinks, definite keys and candidates >= tau, 64
 //                 gathered rows at a time; k_pf_merge combines the partial
@@ -617,33 +617,15 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
   }
 }
 
-// ------------------------------------------------------------------ attend order
+// ------------------------------------------------------------------ attend work
 
-// The attend kernel's vectors, bucketed by (pair, first definite 32-key block):
-// vectors whose selections start at the same block mostly select the same rows
-// (with 256 planted clusters over a 4096-row chunk about 64 query vectors share
-// each cluster), and running them together
-// on one XCD lets its L2 serve the shared rows.  Each vector's output is computed
-// by its own wave, so the order changes no result; positions within a bucket are
-// taken by atomics.
-__global__ __launch_bounds__(256) void k_pf_okey(PfPlan p) {
+// Work items of every vector: the whole vector, or, with more than 256 definite
+// words, pieces of at most 256 words of one wave list (each list's candidates
+// ride with its last piece, the sinks with list 0's first); a keep-all vector is
+// cut into ranges of 8192 keys.
+__global__ __launch_bounds__(256) void k_pf_count(PfPlan p) {
   const int vid = blockIdx.x * 256 + threadIdx.x;
   if (vid >= p.V) return;
-  const int bi = vid / (p.G * p.Tq);
-  const int nblk = p.nbucket / (p.B * p.n_ret) - 1;
-  int first = nblk;  // no definite word
-  for (int w = 0; w < 4; ++w) {
-    const int cnt = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
-    if (cnt > 0) {
-      first = min((int)p.words[((size_t)vid * 4 + w) * p.wcap].x, nblk);
-      break;
-    }
-  }
-  const int key = bi * (nblk + 1) + first;
-  p.okey[vid] = key;
-  atomicAdd(&p.obucket[key], 1);
-
-  // work items: the whole vector, or pieces of bounded size
   const PfVec v = p.vec[vid];
   const int pos = p.q_start + (vid / p.G) % p.Tq;
   int n = 1;
@@ -662,6 +644,82 @@ __global__ __launch_bounds__(256) void k_pf_okey(PfPlan p) {
     }
   }
   p.nitem[vid] = n;
+}
+
+// First item of every vector (vector order; one block) and the item total.
+__global__ __launch_bounds__(1024) void k_pf_iscan(PfPlan p) {
+  constexpr int NT = 1024;
+  __shared__ unsigned ws[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (p.V + NT - 1) / NT;
+  const int e0 = tid * per, e1 = min(p.V, e0 + per);
+  unsigned run = 0u;
+  for (int e = e0; e < e1; ++e) run += (unsigned)p.nitem[e];
+  const unsigned inc = wave_incl_sum_u32(run);
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  unsigned base = inc - run;
+  for (int q = 0; q < wave; ++q) base += ws[q];
+  for (int e = e0; e < e1; ++e) {
+    p.ibase[e] = (int)base;
+    base += (unsigned)p.nitem[e];
+  }
+  if (tid == NT - 1) *p.icount = (int)base;
+}
+
+// The items, each with its order key (pair, first 32-key block it reads), counted
+// into the key's bucket.  Items that start at the same block read mostly the same
+// rows: the pieces of diffuse vectors that cover the same key range, and vectors
+// aligned to the same cluster (with 256 planted clusters over a 4096-row chunk
+// about 64 query vectors share each); run together on one XCD, they share its L2
+// and the Infinity Cache.
+__global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
+  const int vid = blockIdx.x * 256 + threadIdx.x;
+  if (vid >= p.V) return;
+  const int n = p.nitem[vid];
+  const int base = p.ibase[vid];
+  const int bi = vid / (p.G * p.Tq);
+  const int nblk = p.nbucket / (p.B * p.n_ret) - 1;
+  auto put = [&](int k, int4 item, int blk) {
+    p.items[base + k] = item;
+    const int key = bi * (nblk + 1) + min(max(blk, 0), nblk);
+    p.ikey[base + k] = key;
+    atomicAdd(&p.obucket[key], 1);
+  };
+  const PfVec v = p.vec[vid];
+  if (n == 1) {
+    int first = 0;  // no definite word: the sinks and candidates only
+    for (int w = 0; w < 4; ++w) {
+      if (min(p.wcount[(size_t)vid * 4 + w], p.wcap) > 0) {
+        first = (int)p.words[((size_t)vid * 4 + w) * p.wcap].x;
+        break;
+      }
+    }
+    put(0, make_int4(vid, -1, 0, 0), first);
+    return;
+  }
+  if (v.mode == kPfAll) {
+    const int nk = p.q_start + (vid / p.G) % p.Tq + 1;
+    for (int k = 0; k < n; ++k)
+      put(k, make_int4(vid, 4, k * kPfItemKeys, min(nk, (k + 1) * kPfItemKeys)),
+          k * kPfItemKeys / 32);
+    return;
+  }
+  int k = 0;
+  for (int w = 0; w < 4; ++w) {
+    const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+    const int cc = v.mode == kPfNormal ? p.ccount[(size_t)vid * kPfSubLists + w] : 0;
+    if (wc == 0) {
+      if (w == 0 || cc > 0) {
+        const int blk = cc > 0 ? __float_as_int(p.cand[((size_t)vid * kPfSubLists + w) * kPfCandSub].y) >> 5 : 0;
+        put(k++, make_int4(vid, w, 0, 0), blk);
+      }
+      continue;
+    }
+    const uint2* wl = p.words + ((size_t)vid * 4 + w) * p.wcap;
+    for (int lo = 0; lo < wc; lo += kPfItemWords)
+      put(k++, make_int4(vid, w, lo, min(wc, lo + kPfItemWords)), (int)wl[lo].x);
+  }
 }
 
 // Exclusive scan of the bucket counts in place (one block).
@@ -685,65 +743,16 @@ __global__ __launch_bounds__(1024) void k_pf_oscan(PfPlan p) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_pf_oscatter(PfPlan p) {
-  const int vid = blockIdx.x * 256 + threadIdx.x;
-  if (vid >= p.V) return;
-  p.perm[atomicAdd(&p.obucket[p.okey[vid]], 1)] = vid;
+// Items in key order; positions within a bucket are taken by atomics.  Every item
+// writes its result to its own slot (item id), so the order changes no result.
+__global__ __launch_bounds__(256) void k_pf_iscatter(PfPlan p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= *p.icount) return;
+  p.iperm[atomicAdd(&p.obucket[p.ikey[i]], 1)] = i;
 }
 
-// First item of every vector, in attend order (one block), and the item total.
-__global__ __launch_bounds__(1024) void k_pf_iscan(PfPlan p) {
-  constexpr int NT = 1024;
-  __shared__ unsigned ws[NT / 64];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int per = (p.V + NT - 1) / NT;
-  const int e0 = tid * per, e1 = min(p.V, e0 + per);
-  unsigned run = 0u;
-  for (int e = e0; e < e1; ++e) run += (unsigned)p.nitem[p.perm[e]];
-  const unsigned inc = wave_incl_sum_u32(run);
-  if (lane == 63) ws[wave] = inc;
-  __syncthreads();
-  unsigned base = inc - run;
-  for (int q = 0; q < wave; ++q) base += ws[q];
-  for (int e = e0; e < e1; ++e) {
-    const int vid = p.perm[e];
-    p.ibase[vid] = (int)base;
-    base += (unsigned)p.nitem[vid];
-  }
-  if (tid == NT - 1) *p.icount = (int)base;
-}
-
-// The items of every vector, consecutive in attend order.
-__global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= p.V) return;
-  const int vid = p.perm[e];
-  const int n = p.nitem[vid];
-  int4* it = p.items + p.ibase[vid];
-  if (n == 1) {
-    it[0] = make_int4(vid, -1, 0, 0);
-    return;
-  }
-  const PfVec v = p.vec[vid];
-  if (v.mode == kPfAll) {
-    const int nk = p.q_start + (vid / p.G) % p.Tq + 1;
-    for (int k = 0; k < n; ++k) it[k] = make_int4(vid, 4, k * kPfItemKeys, min(nk, (k + 1) * kPfItemKeys));
-    return;
-  }
-  int k = 0;
-  for (int w = 0; w < 4; ++w) {
-    const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
-    const bool cands = v.mode == kPfNormal && p.ccount[(size_t)vid * kPfSubLists + w] > 0;
-    if (wc == 0) {
-      if (w == 0 || cands) it[k++] = make_int4(vid, w, 0, 0);
-      continue;
-    }
-    for (int lo = 0; lo < wc; lo += kPfItemWords) it[k++] = make_int4(vid, w, lo, min(wc, lo + kPfItemWords));
-  }
-}
-
-// Items are dealt to the XCDs in chunks of 64 consecutive ones (chunk c to XCD
-// c % 8), so a vector's pieces and its bucket neighbours share an L2; within an
+// Items (in key order) are dealt to the XCDs in chunks of 64 consecutive ones
+// (chunk c to XCD c % 8), so that neighbours in the order share an L2; within an
 // XCD waves take the next item from that XCD's counter.
 constexpr int kPfChunk = 64;
 constexpr int kPfAttendBlocks = 768;   // persistent: 3 blocks of 4 waves per CU (168 VGPRs)
@@ -807,7 +816,8 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
     const int gc = (c / kPfChunk) * 8 + xcd;
     const int j = gc * kPfChunk + c % kPfChunk;
     if (gc >= nch || j >= total) break;  // wave-uniform; every later take is past the end
-    const int4 it = p.items[j];
+    const int iid = p.iperm[j];  // the item; its partial result goes to slot iid
+    const int4 it = p.items[iid];
     const int vid = it.x;
     const bool whole = it.y < 0;
     const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
@@ -996,7 +1006,7 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
       *(uint32_t*)&dst[2 * lane] =
           (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
     } else {
-      float* pr = p.part + (size_t)j * kPfPartStride;
+      float* pr = p.part + (size_t)iid * kPfPartStride;
       if (lane == 0) {
         pr[0] = m;
         pr[1] = l;
@@ -1104,9 +1114,7 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_cand = take(V * kPfSubLists * kPfCandSub * sizeof(float2));
   const size_t o_ccnt = take(V * kPfSubLists * sizeof(int));
   const size_t nbucket = (size_t)B * n_ret * ((n_keys + 31) / 32 + 1);
-  const size_t o_okey = take(V * sizeof(int));
   const size_t o_obkt = take(nbucket * sizeof(int));
-  const size_t o_perm = take(V * sizeof(int));
   // items per vector: at most one per 256 words of each list (at least one per
   // list), or one per 8192 keys of a keep-all vector
   const size_t per_vec = std::max<size_t>(4 * std::max<size_t>((wcap + kPfItemWords - 1) / kPfItemWords, 1),
@@ -1115,6 +1123,8 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_nitem = take(V * sizeof(int));
   const size_t o_ibase = take(V * sizeof(int));
   const size_t o_items = take(max_items * sizeof(int4));
+  const size_t o_ikey = take(max_items * sizeof(int));
+  const size_t o_iperm = take(max_items * sizeof(int));
   const size_t o_part = take(max_items * kPfPartStride * sizeof(float));
   const size_t o_ictl = take(16 * sizeof(int));
   if (plan && base) {
@@ -1126,13 +1136,13 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
     plan->wcount = (int*)(base + o_wcnt);
     plan->cand = (float2*)(base + o_cand);
     plan->ccount = (int*)(base + o_ccnt);
-    plan->okey = (int*)(base + o_okey);
     plan->obucket = (int*)(base + o_obkt);
-    plan->perm = (int*)(base + o_perm);
     plan->nbucket = (int)nbucket;
     plan->nitem = (int*)(base + o_nitem);
     plan->ibase = (int*)(base + o_ibase);
     plan->items = (int4*)(base + o_items);
+    plan->ikey = (int*)(base + o_ikey);
+    plan->iperm = (int*)(base + o_iperm);
     plan->part = (float*)(base + o_part);
     plan->icount = (int*)(base + o_ictl);
     plan->ictr = (int*)(base + o_ictl) + 8;
@@ -1167,11 +1177,11 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
                      s, p);
   mark(2);
   hipLaunchKernelGGL(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_okey, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_oscan, dim3(1), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(k_pf_oscatter, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_count, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
   hipLaunchKernelGGL(k_pf_iscan, dim3(1), dim3(1024), 0, s, p);
   hipLaunchKernelGGL(k_pf_items, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_pf_oscan, dim3(1), dim3(1024), 0, s, p);
+  hipLaunchKernelGGL(k_pf_iscatter, dim3((p.max_items + 255) / 256), dim3(256), 0, s, p);
   mark(3);
   hipLaunchKernelGGL(k_pf_attend, dim3(kPfAttendBlocks), dim3(256), 0, s, p);
   hipLaunchKernelGGL(k_pf_merge, dim3((p.V + 3) / 4), dim3(256), 0, s, p);

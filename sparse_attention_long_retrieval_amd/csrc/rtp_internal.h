@@ -194,13 +194,13 @@ struct PfPlan {
   int* wcount;        // [V][4]
   float2* cand;       // [V][4][kPfCandSub]  (score, key bits)
   int* ccount;        // [V][4]
-  int* okey;          // [V] attend order key: (pair, first definite 32-key block)
-  int* obucket;       // [nbucket] vectors per key, then their first position
-  int* perm;          // [V] vectors in attend order
+  int* obucket;       // [nbucket] items per order key, then their first position
   int nbucket;        // P * (key blocks + 1)
   int* nitem;         // [V] attend work items of the vector (1: the whole vector)
   int* ibase;         // [V] the vector's first item
   int4* items;        // [max_items] (vid, list or -1 whole or 4 key range, lo, hi)
+  int* ikey;          // [max_items] order key: (pair, first 32-key block the item reads)
+  int* iperm;         // [max_items] items in attend order
   float* part;        // [max_items][kPfPartStride] partial (m, l, o) of split vectors
   int* icount;        // [1] items in use
   int* ictr;          // [8] items taken per XCD
