@@ -755,7 +755,7 @@ __global__ __launch_bounds__(256) void k_pf_iscatter(PfPlan p) {
 // (chunk c to XCD c % 8), so that neighbours in the order share an L2; within an
 // XCD waves take the next item from that XCD's counter.
 constexpr int kPfChunk = 64;
-constexpr int kPfAttendBlocks = 768;   // persistent: 3 blocks of 4 waves per CU (168 VGPRs)
+constexpr int kPfAttendBlocks = 512;   // persistent: 2 blocks of 4 waves per CU
 
 // ------------------------------------------------------------------ gather attention
 
@@ -791,7 +791,7 @@ constexpr int kAwQueue = kAwBatch * 32 + 64;   // one batch of words plus a part
 // rows at a time.  The rows are gathered from all over the cache (at 256K-key
 // chunk shapes 15% of them hit L2), so the kernel is bound by random 512 B row
 // reads from the Infinity Cache and HBM.
-__global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
+__global__ __launch_bounds__(256, 2) void k_pf_attend(PfPlan p) {
   __shared__ float qs[4][kD];
   __shared__ float ps[4][64];
   __shared__ int rq[4][kAwQueue];
@@ -843,17 +843,24 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
     const size_t head = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
     const uint16_t* kb = p.k_cache + head;
     const uint16_t* vb = p.v_cache + head;
-    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    float m = -INFINITY, l = 0.f;
+    // P.V: lane (grp, ksub) reads dims 8 ksub .. 8 ksub + 7 of rows 4 i + grp, whole
+    // lines like the keys, and keeps the sums over its quarter of the rows; the four
+    // quarters are added once, after the item's last tile
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = 0.f;
 
-    // Attend rows[0, n): for P.V each lane owns output dims 2 lane, 2 lane + 1 and
-    // reads them from 16 V rows per batch of loads.
+    // Attend rows[0, n).
     auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
-      uint4 kk[16];
+      // K and V rows are requested together: one memory round trip per tile
+      uint4 kk[16], vv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rr = 4 * i + grp;
-        kk[i] = rr < n ? *(const uint4*)(kb + (size_t)rows[rr] * kD + 8 * ksub)
-                       : make_uint4(0u, 0u, 0u, 0u);
+        const size_t off = rr < n ? (size_t)rows[rr] * kD + 8 * ksub : 0;
+        kk[i] = rr < n ? *(const uint4*)(kb + off) : make_uint4(0u, 0u, 0u, 0u);
+        vv[i] = rr < n ? *(const uint4*)(vb + off) : make_uint4(0u, 0u, 0u, 0u);
       }
       float part[16];
 #pragma unroll
@@ -884,19 +891,20 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
       m = m_new;
       pw[my_row] = pr;
       wave_lds_sync();
-      o0 *= alpha;
-      o1 *= alpha;
-      for (int r0 = 0; r0 < n; r0 += 16) {
-        uint32_t vv[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          vv[u] = r0 + u < n ? *(const uint32_t*)(vb + (size_t)rows[r0 + u] * kD + 2 * lane) : 0u;
+      for (int k = 0; k < 8; ++k) o[k] *= alpha;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float pu = r0 + u < n ? pw[r0 + u] : 0.f;
-          o0 = fmaf(pu, bf16_lo(vv[u]), o0);
-          o1 = fmaf(pu, bf16_hi(vv[u]), o1);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int rr = 4 * i + grp;
+        const float pu = rr < n ? pw[rr] : 0.f;
+        o[0] = fmaf(pu, bf16_lo(vv[i].x), o[0]);
+        o[1] = fmaf(pu, bf16_hi(vv[i].x), o[1]);
+        o[2] = fmaf(pu, bf16_lo(vv[i].y), o[2]);
+        o[3] = fmaf(pu, bf16_hi(vv[i].y), o[3]);
+        o[4] = fmaf(pu, bf16_lo(vv[i].z), o[4]);
+        o[5] = fmaf(pu, bf16_hi(vv[i].z), o[5]);
+        o[6] = fmaf(pu, bf16_lo(vv[i].w), o[6]);
+        o[7] = fmaf(pu, bf16_hi(vv[i].w), o[7]);
       }
       wave_lds_sync();
     };
@@ -978,7 +986,10 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
             const int key = __float_as_int(cd.y);
             const bool sel = e0 + lane < cnt && cd.x >= v.tau && key >= p.n_sink;
             const unsigned long long bal = __ballot(sel);
-            if (sel) queue[nq + __popcll(bal & ((1ull << lane) - 1ull))] = key;
+            // rank among the selected lanes below this one (mbcnt: no 64-bit mask)
+            const unsigned below = __builtin_amdgcn_mbcnt_hi(
+                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (sel) queue[nq + (int)below] = key;
             nq += __popcll(bal);
             e0 += 64;
           }
@@ -1000,18 +1011,33 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
       wave_lds_sync();
       nq = rest;
     }
+    // the four row quarters: lanes 0..15 end with dims 8 ksub .. 8 ksub + 7
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      o[k] += __shfl_xor(o[k], 16, 64);
+      o[k] += __shfl_xor(o[k], 32, 64);
+    }
     if (whole) {
-      uint16_t* dst = p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      *(uint32_t*)&dst[2 * lane] =
-          (uint32_t)f32_to_bf16(o0 * inv) | ((uint32_t)f32_to_bf16(o1 * inv) << 16);
+      if (grp == 0) {
+        uint16_t* dst = p.out + (((size_t)b * p.Hq + h) * p.Tq + row) * kD + 8 * ksub;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint4 w;
+        w.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
+        w.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
+        w.z = (uint32_t)f32_to_bf16(o[4] * inv) | ((uint32_t)f32_to_bf16(o[5] * inv) << 16);
+        w.w = (uint32_t)f32_to_bf16(o[6] * inv) | ((uint32_t)f32_to_bf16(o[7] * inv) << 16);
+        *(uint4*)dst = w;
+      }
     } else {
       float* pr = p.part + (size_t)iid * kPfPartStride;
       if (lane == 0) {
         pr[0] = m;
         pr[1] = l;
       }
-      *(float2*)&pr[2 + 2 * lane] = make_float2(o0, o1);
+      if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) *(float2*)&pr[2 + 8 * ksub + k] = make_float2(o[k], o[k + 1]);
+      }
     }
   }
 }
