@@ -52,6 +52,7 @@
 namespace rtp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kL2e = 1.4426950408889634f;
@@ -755,7 +756,7 @@ __global__ __launch_bounds__(256) void k_pf_iscatter(PfPlan p) {
 // (chunk c to XCD c % 8), so that neighbours in the order share an L2; within an
 // XCD waves take the next item from that XCD's counter.
 constexpr int kPfChunk = 64;
-constexpr int kPfAttendBlocks = 512;   // persistent: 2 blocks of 4 waves per CU
+constexpr int kPfAttendBlocks = 768;   // persistent: 3 blocks of 4 waves per CU (at most 168 VGPRs)
 
 // ------------------------------------------------------------------ gather attention
 
@@ -791,7 +792,7 @@ constexpr int kAwQueue = kAwBatch * 32 + 64;   // one batch of words plus a part
 // rows at a time.  The rows are gathered from all over the cache (at 256K-key
 // chunk shapes 15% of them hit L2), so the kernel is bound by random 512 B row
 // reads from the Infinity Cache and HBM.
-__global__ __launch_bounds__(256, 2) void k_pf_attend(PfPlan p) {
+__global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
   __shared__ float qs[4][kD];
   __shared__ float ps[4][64];
   __shared__ int rq[4][kAwQueue];
@@ -816,8 +817,13 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfPlan p) {
     const int gc = (c / kPfChunk) * 8 + xcd;
     const int j = gc * kPfChunk + c % kPfChunk;
     if (gc >= nch || j >= total) break;  // wave-uniform; every later take is past the end
-    const int iid = p.iperm[j];  // the item; its partial result goes to slot iid
-    const int4 it = p.items[iid];
+    // the item (its partial result goes to slot iid); its fields are wave-uniform
+    const int iid = __builtin_amdgcn_readfirstlane(p.iperm[j]);
+    int4 it = p.items[iid];
+    it.x = __builtin_amdgcn_readfirstlane(it.x);
+    it.y = __builtin_amdgcn_readfirstlane(it.y);
+    it.z = __builtin_amdgcn_readfirstlane(it.z);
+    it.w = __builtin_amdgcn_readfirstlane(it.w);
     const int vid = it.x;
     const bool whole = it.y < 0;
     const int g = vid % p.G, row = (vid / p.G) % p.Tq, bi = vid / (p.G * p.Tq);
@@ -836,13 +842,24 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfPlan p) {
       qv[lane + 64] = (y * cs + x * sn) * sc;
     }
     wave_lds_sync();
-    float qr[8];
+    // q as bf16 pairs (dims 2e, 2e + 1 of the lane's eight), hi and lo parts: the
+    // products with the bf16 keys on v_dot2_f32_bf16 keep q to about 2^-17
+    bf16x2 qh[4], ql[4];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) qr[t] = qv[8 * ksub + t];
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = qv[8 * ksub + 2 * e], x1 = qv[8 * ksub + 2 * e + 1];
+      const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+      const uint32_t hw = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      const uint32_t lw = (uint32_t)f32_to_bf16(x0 - bf16_to_f32(h0)) |
+                          ((uint32_t)f32_to_bf16(x1 - bf16_to_f32(h1)) << 16);
+      __builtin_memcpy(&qh[e], &hw, 4);
+      __builtin_memcpy(&ql[e], &lw, 4);
+    }
 
     const size_t head = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
-    const uint16_t* kb = p.k_cache + head;
-    const uint16_t* vb = p.v_cache + head;
+    const char* kb = (const char*)(p.k_cache + head);
+    const char* vb = (const char*)(p.v_cache + head);
+    const uint32_t lane_off = 16u * (uint32_t)ksub;  // bytes of the lane's 8 dims
     float m = -INFINITY, l = 0.f;
     // P.V: lane (grp, ksub) reads dims 8 ksub .. 8 ksub + 7 of rows 4 i + grp, whole
     // lines like the keys, and keeps the sums over its quarter of the rows; the four
@@ -854,25 +871,28 @@ __global__ __launch_bounds__(256, 2) void k_pf_attend(PfPlan p) {
     // Attend rows[0, n).
     auto tile = [&](const int* rows, int n) __attribute__((always_inline)) {
       // K and V rows are requested together: one memory round trip per tile
+      // row offsets fit 32 bits (a head's cache is below 4 GB); rows past n read row
+      // 0 of the tile (their probabilities are zero)
       uint4 kk[16], vv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rr = 4 * i + grp;
-        const size_t off = rr < n ? (size_t)rows[rr] * kD + 8 * ksub : 0;
-        kk[i] = rr < n ? *(const uint4*)(kb + off) : make_uint4(0u, 0u, 0u, 0u);
-        vv[i] = rr < n ? *(const uint4*)(vb + off) : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t off = (uint32_t)rows[rr < n ? rr : 0] * (uint32_t)(kD * 2) + lane_off;
+        kk[i] = *(const uint4*)(kb + off);
+        vv[i] = *(const uint4*)(vb + off);
       }
       float part[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float a = qr[0] * bf16_lo(kk[i].x);
-        a = fmaf(qr[1], bf16_hi(kk[i].x), a);
-        a = fmaf(qr[2], bf16_lo(kk[i].y), a);
-        a = fmaf(qr[3], bf16_hi(kk[i].y), a);
-        a = fmaf(qr[4], bf16_lo(kk[i].z), a);
-        a = fmaf(qr[5], bf16_hi(kk[i].z), a);
-        a = fmaf(qr[6], bf16_lo(kk[i].w), a);
-        a = fmaf(qr[7], bf16_hi(kk[i].w), a);
+        const uint32_t w[4] = {kk[i].x, kk[i].y, kk[i].z, kk[i].w};
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16x2 kp;
+          __builtin_memcpy(&kp, &w[e], 4);
+          a = __builtin_amdgcn_fdot2_f32_bf16(kp, qh[e], a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(kp, ql[e], a, false);
+        }
         part[i] = a;
       }
       // reduce-scatter over the group's 16 lanes: at the step with partner lane ^ S
