@@ -426,10 +426,10 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     }
     __syncthreads();
     {
-      bool act[2];
-      float mc[2];
+      bool act[2], fx[2];
+      float mc[2], fdef[2], fdq[2];
       int ddef[2], dq[2];
-      unsigned cw[2];
+      unsigned cw[2], fcw[2];
       float2* cl[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -440,6 +440,14 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
         dq[c] = w.dq;
         ddef[c] = incl ? w.dq + (1 << w.sh) : w.dq;  // definite: code below this
         cw[c] = incl ? 0u : (1u << w.sh);            // candidate: code in [dq, dq + cw)
+        // With integer bounds that floats hold exactly (multiples of 2^7 below 2^31, or
+        // anything below 2^24) the tests run on t = 2^17 (m - s) itself: the code is
+        // floor(t), so code < n iff t < n, and t - dq is exact near dq and keeps its
+        // order elsewhere (unsigned float bits: negative values fail the test).
+        fx[c] = w.sh >= 7 || w.dq + (1 << w.sh) < (1 << 24);
+        fdef[c] = (float)ddef[c];
+        fdq[c] = (float)dq[c];
+        fcw[c] = __float_as_uint((float)cw[c]);
         cl[c] = p.cand + ((vbase + 32 * c + j) * kPfSubLists + wave) * (size_t)kPfCandSub;
       }
       const bool my_act = hi ? act[1] : act[0];
@@ -452,12 +460,22 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
           uint32_t cbits = 0u;  // candidates among the lane's 16 keys
+          if (fx[c]) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int d = pf_code(acc[c][r], mc[c]);
-            const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
-            bits[c] |= (d < ddef[c] ? 1u : 0u) << bit;
-            cbits |= ((unsigned)(d - dq[c]) < cw[c] ? 1u : 0u) << r;
+            for (int r = 0; r < 16; ++r) {
+              const float t = __builtin_fmaf(acc[c][r], -kPfCode, mc[c]);
+              const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
+              bits[c] |= (t < fdef[c] ? 1u : 0u) << bit;
+              cbits |= (__float_as_uint(t - fdq[c]) < fcw[c] ? 1u : 0u) << r;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int d = pf_code(acc[c][r], mc[c]);
+              const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
+              bits[c] |= (d < ddef[c] ? 1u : 0u) << bit;
+              cbits |= ((unsigned)(d - dq[c]) < cw[c] ? 1u : 0u) << r;
+            }
           }
           // one slot reservation per lane and step, then the stores
           if (cbits) {
