@@ -51,7 +51,6 @@ constexpr int kTokCap = 8192;         // candidates whose tokens are also kept i
 constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
-constexpr int kScanCopies = 16;       // words per histogram bin in the scan
 
 // floor(f * 2^36) for a finite f >= 0, from the bits: the 24-bit significand
 // shifted by the exponent (equal to converting f * 2^36 in double and truncating).
@@ -206,10 +205,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   __shared__ float red_m[NW][G];
   __shared__ float mb_s[G];
   __shared__ int kt_s[G];
-  // each bin is split over kScanCopies words, one per lane group, so that lanes
-  // adding to the same bin mostly hit different words; the copies are summed
-  // at the end (integers: the split changes no result)
-  __shared__ unsigned bins[G][kNB][kScanCopies];
+  // each bin is split over CP words, one per lane group: a lane's (head, copy)
+  // is unique in the wave, and a bin's row of GE * CP = 64 words puts every lane of
+  // a wave on its own bank whatever bins the lanes hit; the copies are summed at
+  // the end (integers: the split changes no result)
+  constexpr int CP = 64 / S::GE;
+  __shared__ unsigned bins[kNB][S::GE][CP];
   __shared__ unsigned binc[kCoarseGrids][G][kNB];  // coarse grids, fixed budget only
   __shared__ int ktc_s[kCoarseGrids][G];
   __shared__ unsigned long long zred[NW][G];
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
-  for (int e = tid; e < G * kNB * kScanCopies; e += NT) (&bins[0][0][0])[e] = 0u;
+  for (int e = tid; e < kNB * S::GE * CP; e += NT) (&bins[0][0][0])[e] = 0u;
   for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta) * kFxBin;
   __syncthreads();
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   const int hs = hv ? h : 0;
   const int kt = kt_s[hs];
   const float e_top = (float)(kt + 1) * kDelta;  // exact: a multiple of 0.5
-  const int copy = (lane / S::GE) & (kScanCopies - 1);
+  const int copy = lane / S::GE;
   float z = 0.f;
   if (counting) {
 #pragma unroll
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
         if (sv > -INFINITY) {
           z += 1.f;
           const int j = kt - score_key(sv, kInvDelta);
-          if (j < kNB) atomicAdd(&bins[hs][j][copy], (unsigned)kFxBin);
+          if (j < kNB) atomicAdd(&bins[j][hs][copy], (unsigned)kFxBin);
 #pragma unroll
           for (int c = 0; c < kCoarseGrids; ++c) {
             const int jc = ktc_s[c][hs] - score_key(sv, coarse_inv(c));
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
         const unsigned j = (unsigned)(kt - score_key(sv, kInvDelta));
         if (j < (unsigned)kNB) {
           // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1], 2^-20 units
-          atomicAdd(&bins[hs][j][copy], (unsigned)__builtin_fmaf(wt, bscale[j], 0.5f));
+          atomicAdd(&bins[j][hs][copy], (unsigned)__builtin_fmaf(wt, bscale[j], 0.5f));
         }
       }
   }
@@ -338,11 +339,14 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     p.blk_z[so + tid] = zb;
   }
   for (int e = tid; e < G * kNB; e += NT) {
-    const unsigned* cp = &bins[0][0][0] + (size_t)e * kScanCopies;
+    // consecutive threads take consecutive heads, and each starts its copies at
+    // (bin mod CP): the threads of a wave read distinct banks
+    const int hh = e % G, j = e / G;
+    const unsigned* cp = &bins[j][hh][0];
     unsigned acc = 0u;
 #pragma unroll
-    for (int c = 0; c < kScanCopies; ++c) acc += cp[(c + e) & (kScanCopies - 1)];
-    p.blk_bins[so * kNB + e] = acc;
+    for (int c = 0; c < CP; ++c) acc += cp[(c + j) % CP];
+    p.blk_bins[(so + hh) * kNB + j] = acc;
   }
   if (counting) {
     const size_t grid_stride = (size_t)p.P * p.nA * G * kNB;
