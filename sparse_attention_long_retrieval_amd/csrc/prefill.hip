@@ -316,16 +316,17 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
           if (!act[c]) continue;
           if (tail[c]) {
             // the first window starts at the max: dw = 0, bins of 2^14 codes, and no
-            // key lies above it (the weights stay at most 1).  floor(t / 2^14) is the
-            // code's bin exactly (the scale is a power of two), -inf scores included
+            // key lies above it (the weights stay at most 1).  With u = 8 (m - s), the
+            // code scaled by 2^-14 (the same rounding: the scale is a power of two),
+            // floor(u) is the code's bin exactly, -inf scores included, and the key
+            // lies (u - k) / 8 below its bin's upper edge m - k / 8
+            const float m8 = mc[c] * (1.f / (1 << kPfSh0));
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const float s = acc[c][r];
-              const float kf = fminf(
-                  floorf(__builtin_fmaf(s, -kPfCode, mc[c]) * (1.f / (1 << kPfSh0))),
-                  (float)kPfBins);
+              const float u = __builtin_fmaf(acc[c][r], -(kPfCode / (1 << kPfSh0)), m8);
+              const float kf = fminf(floorf(u), (float)kPfBins);
               const unsigned k = (unsigned)kf;
-              const float x = (s - __builtin_fmaf(kf, rf[c].c1, rf[c].c0)) * kL2e;
+              const float x = (kf - u) * (kL2e * (1 << kPfSh0) / kPfCode);
               const unsigned wfx =
                   (unsigned)__builtin_fmaf(__builtin_amdgcn_exp2f(x), kFxPf, 0.5f);
               atomicAdd(&bins[32 * c + j][k], (1ull << kPfCntShift) | wfx);
