@@ -460,24 +460,25 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
-          uint32_t cbits = 0u;  // candidates among the lane's 16 keys
+          // definite keys at bits 8 (r / 4) + r % 4 (constant shifts), moved to the
+          // lane's half of the word (+ 4 hi) once; candidates at bit r
+          uint32_t dbits = 0u, cbits = 0u;
           if (fx[c]) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float t = __builtin_fmaf(acc[c][r], -kPfCode, mc[c]);
-              const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
-              bits[c] |= (t < fdef[c] ? 1u : 0u) << bit;
+              dbits |= (t < fdef[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
               cbits |= (__float_as_uint(t - fdq[c]) < fcw[c] ? 1u : 0u) << r;
             }
           } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int d = pf_code(acc[c][r], mc[c]);
-              const int bit = 8 * (r >> 2) + 4 * hi + (r & 3);
-              bits[c] |= (d < ddef[c] ? 1u : 0u) << bit;
+              dbits |= (d < ddef[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
               cbits |= ((unsigned)(d - dq[c]) < cw[c] ? 1u : 0u) << r;
             }
           }
+          bits[c] = dbits << (4 * hi);
           // one slot reservation per lane and step, then the stores
           if (cbits) {
             int slot = atomicAdd(&lcnt[wave][32 * c + j], __builtin_popcount(cbits));
