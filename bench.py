@@ -128,8 +128,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true", help="prefill only (profiling)")
     ap.add_argument("--serial-streams", action="store_true",
-                    help="run the local heads on the main stream too (clean per-kernel "
-                         "times under a profiler; the step then does the same work serially)")
+                    help="run the decode step's local heads on the main stream too (clean "
+                         "per-kernel times under a profiler; the step then does the same work "
+                         "serially; the prefill step always runs on one stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
@@ -476,28 +477,25 @@ def prefill_leg(args):
 
     hip = Hip()
     main_s = torch.cuda.current_stream()
-    side_s = main_s if args.serial_streams else torch.cuda.Stream()
     stream = main_s.cuda_stream
     ph = [hip.event() for _ in range(5)]
     ex = [hip.event() for _ in range(4)]
     dbg_ph = R.Debug(0, 0, events=ph)
-    fork, join = torch.cuda.Event(), torch.cuda.Event()
 
+    # One stream: the index kernel keeps two blocks on every CU for its whole run, so
+    # local-head blocks beside it only delay some of its blocks (measured: 15.5 ms per
+    # chunk with the local heads on a second stream, 14.9 ms one after the other).
     def step(mark=False):
         if mark:
             hip.record(ex[0], stream)
         R.index_append(layer, ck, cv, w_k, q0, k_cache, v_cache, index)
-        fork.record(main_s)
-        side_s.wait_event(fork)
         if mark:
-            hip.record(ex[1], side_s.cuda_stream)
-        R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out, stream=side_s)
+            hip.record(ex[1], stream)
+        R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out)
         if mark:
-            hip.record(ex[2], side_s.cuda_stream)
-        join.record(side_s)
+            hip.record(ex[2], stream)
         R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, top_p, out, ws,
                         debug=dbg_ph if mark else None)
-        main_s.wait_event(join)
         if mark:
             hip.record(ex[3], stream)
 
@@ -521,7 +519,7 @@ def prefill_leg(args):
         torch.cuda.synchronize()
         for k, n in enumerate(names):
             phs[n].append(hip.elapsed_ms(ph[k], ph[k + 1]))
-        phs["append"].append(hip.elapsed_ms(ex[0], ph[0]))
+        phs["append"].append(hip.elapsed_ms(ex[0], ex[1]))
         phs["swa_local"].append(hip.elapsed_ms(ex[1], ex[2]))
         phs["retrieval_total"].append(hip.elapsed_ms(ph[0], ph[4]))
         phs["step"].append(hip.elapsed_ms(ex[0], ex[3]))
@@ -538,8 +536,7 @@ def prefill_leg(args):
         torch.cuda.synchronize()
         dense_ms.append(hip.elapsed_ms(e0, e1))
     dense = float(np.median(dense_ms))
-    # the local heads alone (their kernel otherwise shares the GPU with the retrieval
-    # chain on the second stream)
+    # the local heads alone, without the append before them
     swa_ms = []
     for i in range(max(3, args.prefill_steps // 2)):
         flush_caches(flush)
