@@ -110,7 +110,7 @@ __device__ __forceinline__ void store_tile(PfSmem& sm, const TileRegs& r) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_swa_prefill(SwaPlan p) {
+__global__ __launch_bounds__(256, 2) void k_swa_prefill(SwaPlan p) {
   __shared__ PfSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, hi = lane >> 5;
