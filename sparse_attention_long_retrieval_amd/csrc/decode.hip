@@ -110,8 +110,10 @@ __device__ __forceinline__ void load_score_tiles(
   for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
     for (int c = 0; c < S::CH; ++c) {
-      const int t = tok0 + (wave * S::TPW + T) * S::TILE + S::R * m + 2 * c + (kb >> 1);
-      a[T][c] = t < N ? *(const uint4*)(idx + (size_t)t * kR + 8 * (kb & 1)) : make_uint4(0, 0, 0, 0);
+      // tokens past N read row N - 1 (N >= 1): their scores are masked by every caller.
+      // Unconditional loads keep the wait counts exact for loads issued before them.
+      const int t = min(tok0 + (wave * S::TPW + T) * S::TILE + S::R * m + 2 * c + (kb >> 1), N - 1);
+      a[T][c] = *(const uint4*)(idx + (size_t)t * kR + 8 * (kb & 1));
     }
 }
 
@@ -227,11 +229,6 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   uint4 qreg = make_uint4(0, 0, 0, 0);
   const uint4* qsrc = (const uint4*)(p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G) * kD);
   if (tid < G * kD / 8) qreg = qsrc[tid];
-
-  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
-  const int tok0 = blk * kPassTokens;
-  uint4 a[S::TPW][S::CH];
-  load_score_tiles<G>(idx, tok0, p.N, a);
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
@@ -239,6 +236,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta) * kFxBin;
   __syncthreads();
+  // The index tile is requested once the projection is in LDS (the barrier keeps
+  // the loads here): a wave's loads complete in issue order, so qi below runs while
+  // the tile is in flight instead of waiting behind it.
+  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+  const int tok0 = blk * kPassTokens;
+  uint4 a[S::TPW][S::CH];
+  load_score_tiles<G>(idx, tok0, p.N, a);
   {
     // qi = q . W_q (fp32): four threads per output, 32 terms each, (p0+p1)+(p2+p3)
     float acc = 0.f;
@@ -567,8 +571,30 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
 
-  // the block's index tile is loaded first, beside the threshold state (nearly every
-  // block is relevant; an irrelevant one discards it)
+  // The small loads go first: a wave's loads complete in issue order, so a wait for
+  // one issued after the index tile would wait for the whole tile.  Then the
+  // block's index tile, and the rotated queries (nearly every block is relevant;
+  // an irrelevant one discards them).
+  int t_key = 0, t_mode = 0;
+  float t_inv = 0.f, t_mb = -INFINITY, qi_r = 0.f;
+  if (tid < G) {
+    const ThrInfo& t = p.thr[pair * G + tid];
+    t_key = t.key_bnd;
+    t_mode = t.mode;
+    t_inv = t.inv_w;
+    t_mb = p.blk_m[((size_t)pair * p.nA + blk) * G + tid];
+  }
+  if (tid < G * kR) qi_r = p.qi[(size_t)pair * G * kR + tid];
+  constexpr int QPT = (G * kD + NT - 1) / NT;
+  float qv[QPT];
+  {
+    const float* qsrc = p.qrope + (size_t)pair * G * kD;
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = tid + u * NT;
+      qv[u] = e < G * kD ? qsrc[e] : 0.f;
+    }
+  }
   const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
   const int tok0 = blk * kPassTokens;
   uint4 a[S::TPW][S::CH];
@@ -576,14 +602,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
   __syncthreads();
   if (tid < G) {
-    const ThrInfo t = p.thr[pair * G + tid];
-    kb_s[tid] = t.key_bnd;
-    mode_s[tid] = t.mode;
-    inv_s[tid] = t.inv_w;
-    const float mb = p.blk_m[((size_t)pair * p.nA + blk) * G + tid];
-    if (t.mode != 0 || score_key(mb, t.inv_w) >= t.key_bnd) atomicOr(&relevant, 1);
+    kb_s[tid] = t_key;
+    mode_s[tid] = t_mode;
+    inv_s[tid] = t_inv;
+    if (t_mode != 0 || score_key(t_mb, t_inv) >= t_key) atomicOr(&relevant, 1);
   }
-  if (tid < G * kR) (&qi_s[0][0])[tid] = p.qi[(size_t)pair * G * kR + tid];
+  if (tid < G * kR) (&qi_s[0][0])[tid] = qi_r;
   for (int e = tid; e < kPassTokens; e += NT) dmask[e] = cmask[e] = 0u;
   __syncthreads();
 
@@ -592,7 +616,11 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   if (relevant) {
     const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
     const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
-    load_q_ready<G>(sm, p.qrope + (size_t)pair * G * kD);
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+      const int e = tid + u * NT;
+      if (e < G * kD) (&sm.qs[0][0])[e] = qv[u];
+    }
     uint4 bq[3][S::CH];
     make_score_b<G>(qi_s, bq);
     f32x4_t sc[S::TPW];
@@ -894,9 +922,11 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const ThrInfo t = p.thr[unit];
   const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
   const float2* cand = p.cand + (size_t)unit * p.N;
-  load_q_ready<1>(sm, p.qrope + (size_t)unit * kD);
+  static_assert(kD <= NT, "one query dimension per thread");
+  const float qv = tid < kD ? p.qrope[(size_t)unit * kD + tid] : 0.f;
   // candidate counts of the pass-B blocks and their exclusive prefix (fixed order);
-  // the counts are loaded together with the threshold state (one round trip)
+  // the counts are loaded together with the threshold state and the query (one
+  // round trip)
   const bool small_nA = p.nA <= kMaxBlocksLds;
   constexpr int kPerMax = kMaxBlocksLds / NT;
   const int per = (p.nA + NT - 1) / NT;
@@ -904,6 +934,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   unsigned cnt_r[kPerMax];
 #pragma unroll
   for (int i = 0; i < kPerMax; ++i) cnt_r[i] = (small_nA && b0 + i < b1) ? blk_cnt[b0 + i] : 0u;
+  if (tid < kD) sm.qs[0][tid] = qv;
   unsigned C = 0u;
   if (t.mode != 2) {
     if (small_nA) {
