@@ -54,22 +54,12 @@ __device__ __forceinline__ void load_q_ready(TileSmem<G>& sm, const float* src) 
   for (int e = threadIdx.x; e < G * RTP_D; e += blockDim.x) (&sm.qs[0][0])[e] = src[e];
 }
 
-// Attend one tile of nr rows (ids in sm.rows, per-row head masks in sm.masks).
-// kbase / vbase point at row 0 of this KV head's cache.  All NT threads call it.
-template <int G, int NT>
-__device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kbase,
-                                            const uint16_t* vbase, int nr, float& m, float& l,
-                                            float& o0, float& o1) {
+// Logits, online softmax and P.V of one staged tile of nr rows (K, V and the row
+// masks in LDS).  All threads call it; it ends with a barrier.
+template <int G>
+__device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, float& l,
+                                             float& o0, float& o1) {
   const int tid = threadIdx.x;
-  for (int c = tid; c < kTileRows * 16; c += NT) {
-    const int r = c >> 4, q = c & 15;
-    if (r < nr) {
-      const size_t off = (size_t)sm.rows[r] * RTP_D + q * 8;
-      *(uint4*)&sm.Ks[r][q * 8] = *(const uint4*)(kbase + off);
-      *(uint4*)&sm.Vs[r][q * 8] = *(const uint4*)(vbase + off);
-    }
-  }
-  __syncthreads();
   const int h = tid >> 6, lane = tid & 63;
   float alpha = 1.f;
   if (h < G) {
@@ -115,6 +105,75 @@ __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kba
   }
   __syncthreads();
 }
+
+// Attend one tile of nr rows (ids in sm.rows, per-row head masks in sm.masks).
+// kbase / vbase point at row 0 of this KV head's cache.  All NT threads call it.
+template <int G, int NT>
+__device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kbase,
+                                            const uint16_t* vbase, int nr, float& m, float& l,
+                                            float& o0, float& o1) {
+  const int tid = threadIdx.x;
+  for (int c = tid; c < kTileRows * 16; c += NT) {
+    const int r = c >> 4, q = c & 15;
+    if (r < nr) {
+      const size_t off = (size_t)sm.rows[r] * RTP_D + q * 8;
+      *(uint4*)&sm.Ks[r][q * 8] = *(const uint4*)(kbase + off);
+      *(uint4*)&sm.Vs[r][q * 8] = *(const uint4*)(vbase + off);
+    }
+  }
+  __syncthreads();
+  tile_compute<G>(sm, nr, m, l, o0, o1);
+}
+
+// One row of a list to attend: its id in the cache and its head mask.
+struct RowMask {
+  int row;
+  uint32_t mask;
+};
+
+// Attend rows get(0) .. get(n - 1) in tiles of 64, with the next tile's K and V rows
+// loaded into registers while the current one is computed.  Rows past the end of the
+// list re-read the last row (their lanes are masked), so the loads need no branch.
+// All NT threads call it; get(i) is uniform in what it returns for a given i.
+template <int G, int NT, class Get>
+__device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kbase,
+                                            const uint16_t* vbase, int n, Get&& get, float& m,
+                                            float& l, float& o0, float& o1) {
+  constexpr int PER = kTileRows * 16 / NT;  // 16-byte pieces of K (and of V) per thread
+  static_assert(PER * NT == kTileRows * 16, "the threads cover a tile");
+  if (n <= 0) return;
+  const int tid = threadIdx.x;
+  // native vectors: a uint4 struct would be copied to LDS through private memory
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kr[PER], vr[PER];
+  // iteration t0 stages tile t0 (fetched one iteration earlier), fetches the next
+  // tile into registers, then computes tile t0; the first iteration only fetches
+  for (int t0 = -kTileRows; t0 < n; t0 += kTileRows) {
+    const int nr = min(kTileRows, n - t0);
+    if (t0 >= 0) {
+      if (tid < nr) sm.masks[tid] = get(t0 + tid).mask;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT, r = c >> 4, q = c & 15;
+        *(u32x4*)&sm.Ks[r][q * 8] = kr[u];
+        *(u32x4*)&sm.Vs[r][q * 8] = vr[u];
+      }
+      __syncthreads();
+    }
+    const int tn = t0 + kTileRows;
+    if (tn < n) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = tid + u * NT, r = c >> 4, q = c & 15;
+        const size_t off = (size_t)get(min(tn + r, n - 1)).row * RTP_D + q * 8;
+        kr[u] = *(const u32x4*)(kbase + off);
+        vr[u] = *(const u32x4*)(vbase + off);
+      }
+    }
+    if (t0 >= 0) tile_compute<G>(sm, nr, m, l, o0, o1);
+  }
+}
+
 
 // Cross-block data of one launch goes through device-coherent accesses: relaxed
 // agent-scope atomic stores write through the XCD's L2 and agent-scope loads

@@ -229,6 +229,10 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   uint4 qreg = make_uint4(0, 0, 0, 0);
   const uint4* qsrc = (const uint4*)(p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G) * kD);
   if (tid < G * kD / 8) qreg = qsrc[tid];
+  // block 0 also rotates the queries: one (head, dimension pair) per thread
+  static_assert(NT >= G * kD / 2, "one thread per rotated pair");
+  const bool rot = blk == 0 && tid < G * kD / 2;
+  const double th = rot ? p.theta[tid % (kD / 2)] : 0.0;
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
@@ -259,6 +263,18 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   }
   __syncthreads();
   if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
+  if (rot) {
+    // each q-head's query rotated at the newest position and scaled into the log2
+    // domain, once for the select and finish passes
+    const int hh = tid / (kD / 2), i = tid % (kD / 2);
+    float c, sn;
+    rope_sincos(p.N - 1, th, sn, c);
+    const float x = bf16_to_f32(q_s[hh * kD + i]), y = bf16_to_f32(q_s[hh * kD + i + kD / 2]);
+    const float scale = p.attn_scale * kLog2e;
+    float* dst = p.qrope + ((size_t)pair * G + hh) * kD;
+    dst[i] = (x * c - y * sn) * scale;
+    dst[i + kD / 2] = (y * c + x * sn) * scale;
+  }
 
   uint4 bq[3][S::CH];
   make_score_b<G>(qi_s, bq);
@@ -411,18 +427,6 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
       ml = fmaxf(ml, mbv[u]);
       nmine = u + 1;
     }
-  }
-  if (tid < kD / 2) {
-    // this head's query, rotated at the newest position and scaled
-    // into the log2 domain, once for the select and finish passes
-    const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
-    const uint16_t* q = p.q_pre + ((size_t)b * p.Hq + p.ret_kv[ret_i] * G + h) * kD;
-    float c, sn;
-    rope_sincos(p.N - 1, p.theta[tid], sn, c);
-    const float x = bf16_to_f32(q[tid]), y = bf16_to_f32(q[tid + 64]);
-    const float scale = p.attn_scale * kLog2e;
-    p.qrope[(size_t)unit * kD + tid] = (x * c - y * sn) * scale;
-    p.qrope[(size_t)unit * kD + tid + 64] = (y * c + x * sn) * scale;
   }
   for (int k = tid + kMaxPer * NT; k < p.nA; k += NT) ml = fmaxf(ml, p.blk_m[(base + k) * G + h]);
   ml = wave_max(ml);
@@ -719,17 +723,12 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
           p.uni[(size_t)pair * p.N + u++] = make_int2(tok0 + k * NT + tid, (int)(dm[k] | (cm[k] << 8)));
     }
     __syncthreads();
-    const int n_list = (int)n_list_s;
-    for (int t0 = 0; t0 < n_list; t0 += kTileRows) {
-      const int nr = min(kTileRows, n_list - t0);
-      if (tid < nr) {
-        const unsigned e = list[t0 + tid];
-        sm.rows[tid] = tok0 + (int)(e >> 8);
-        sm.masks[tid] = e & 0xffu;
-      }
-      __syncthreads();
-      tile_attend<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
-    }
+    attend_list<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, (int)n_list_s,
+                       [&](int i) {
+                         const unsigned e = list[i];
+                         return RowMask{tok0 + (int)(e >> 8), e & 0xffu};
+                       },
+                       m, l, o0, o1);
   }
   if (wave < G) {
     float* dst = p.partB + ((size_t)(pair * G + wave) * p.nA + blk) * kPartStride;
@@ -1052,23 +1051,24 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   if (C > 0 && in_lds) {
     const int lo = (int)(((long long)C * f) / p.nF), hi = (int)(((long long)C * (f + 1)) / p.nF);
-    for (int c0 = lo; c0 < hi; c0 += kTileRows) {
-      const int c = c0 + tid;
-      const bool sel = tid < kTileRows && c < hi && key_s[c] >= kstar && tok_s[c] >= p.n_sink;
-      const unsigned long long bal = __ballot(sel);
-      if (wave == 0) {
-        if (sel) {
-          const int slot = __popcll(bal & ((1ull << lane) - 1ull));
-          sm.rows[slot] = tok_s[c];
-          sm.masks[slot] = 1u;
-        }
-        if (lane == 0) nr_s = (unsigned)__popcll(bal);
+    // wave 0 compacts the range's selected tokens in place, to tok_s[lo ...] (a
+    // chunk is read before it is written, and writes never pass the reads), then
+    // the block attends them as one list
+    if (wave == 0) {
+      unsigned cnt = 0u;
+      for (int c0 = lo; c0 < hi; c0 += 64) {
+        const int c = c0 + lane;
+        const int tok = c < hi ? tok_s[c] : 0;
+        const bool sel = c < hi && key_s[c] >= kstar && tok >= p.n_sink;
+        const unsigned long long bal = __ballot(sel);
+        if (sel) tok_s[lo + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = tok;
+        cnt += (unsigned)__popcll(bal);
       }
-      __syncthreads();
-      const int nr = (int)nr_s;
-      if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
-      __syncthreads();
+      if (lane == 0) nr_s = cnt;
     }
+    __syncthreads();
+    attend_list<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, (int)nr_s,
+                       [&](int i) { return RowMask{tok_s[lo + i], 1u}; }, m, l, o0, o1);
   } else if (C > 0) {
     // list too long for LDS: this block walks its range of pass-B blocks
     const int b_lo = (int)(((long long)p.nA * f) / p.nF);
