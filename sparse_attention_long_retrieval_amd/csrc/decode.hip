@@ -49,6 +49,7 @@ constexpr int kFinishThreads = 256;
 constexpr int kKeyCap = 16384;        // candidate keys resolved from LDS
 constexpr int kTokCap = 8192;         // candidates whose tokens are also kept in LDS
 constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
+constexpr int kFinishSplit = 32;      // finish blocks per (pair, q-head)
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
 
@@ -570,8 +571,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
   __shared__ int relevant;
   __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned list[kPassTokens];
-  // per token of the block: heads it is definite for, and (inspection only) a candidate for
-  __shared__ unsigned dmask[kPassTokens], cmask[kPassTokens];
+  // Per token of the block: heads it is definite for, and (inspection only) a
+  // candidate for.  They live in the K tile's space: both are read for the last time
+  // before the first tile is staged, and the smaller footprint lets two select blocks
+  // share a CU with a local-head block.
+  static_assert(2 * kPassTokens * sizeof(unsigned) <= sizeof(sm.Ks), "masks fit the K tile");
+  unsigned* const dmask = (unsigned*)&sm.Ks[0][0];
+  unsigned* const cmask = dmask + kPassTokens;
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
 
@@ -908,11 +914,16 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int kv = p.ret_kv[ret_i], qh = kv * G + h;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __shared__ TileSmem<1> sm;
-  // candidate keys, and their tokens while they fit beside them
-  __shared__ uint32_t cbuf[kKeyCap];
+  // candidate keys, and their tokens while they fit beside them.  Once the threshold
+  // is found and the block's share compacted, the same space holds the attention's
+  // tiles (sm): the smaller footprint lets a local-head block share the CU.
+  __shared__ __align__(16) uint32_t cbuf[kKeyCap];
   uint32_t* key_s = cbuf;
   int* tok_s = (int*)(cbuf + kTokCap);
+  static_assert(sizeof(TileSmem<1>) <= sizeof(cbuf), "the tiles fit the candidate space");
+  TileSmem<1>& sm = *reinterpret_cast<TileSmem<1>*>(cbuf);
+  // the selected tokens of this block's share (at most kTokCap / kFinishSplit)
+  __shared__ int sel_l[kTokCap / kFinishSplit];
   __shared__ unsigned boff[kMaxBlocksLds + 1];
   __shared__ unsigned long long red[NT / 64];
   __shared__ unsigned wtot[NT / 64];
@@ -933,7 +944,6 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   unsigned cnt_r[kPerMax];
 #pragma unroll
   for (int i = 0; i < kPerMax; ++i) cnt_r[i] = (small_nA && b0 + i < b1) ? blk_cnt[b0 + i] : 0u;
-  if (tid < kD) sm.qs[0][tid] = qv;
   unsigned C = 0u;
   if (t.mode != 2) {
     if (small_nA) {
@@ -1051,25 +1061,26 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
   if (C > 0 && in_lds) {
     const int lo = (int)(((long long)C * f) / p.nF), hi = (int)(((long long)C * (f + 1)) / p.nF);
-    // wave 0 compacts the range's selected tokens in place, to tok_s[lo ...] (a
-    // chunk is read before it is written, and writes never pass the reads), then
-    // the block attends them as one list
+    // wave 0 compacts the share's selected tokens into sel_l; then the candidate
+    // space becomes the tile space and the block attends them as one list
     if (wave == 0) {
       unsigned cnt = 0u;
       for (int c0 = lo; c0 < hi; c0 += 64) {
         const int c = c0 + lane;
-        const int tok = c < hi ? tok_s[c] : 0;
-        const bool sel = c < hi && key_s[c] >= kstar && tok >= p.n_sink;
+        const bool sel = c < hi && key_s[c] >= kstar && tok_s[c] >= p.n_sink;
         const unsigned long long bal = __ballot(sel);
-        if (sel) tok_s[lo + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = tok;
+        if (sel) sel_l[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = tok_s[c];
         cnt += (unsigned)__popcll(bal);
       }
       if (lane == 0) nr_s = cnt;
     }
     __syncthreads();
+    if (tid < kD) sm.qs[0][tid] = qv;
     attend_list<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, (int)nr_s,
-                       [&](int i) { return RowMask{tok_s[lo + i], 1u}; }, m, l, o0, o1);
+                       [&](int i) { return RowMask{sel_l[i], 1u}; }, m, l, o0, o1);
   } else if (C > 0) {
+    __syncthreads();  // every read of the candidate space is done
+    if (tid < kD) sm.qs[0][tid] = qv;
     // list too long for LDS: this block walks its range of pass-B blocks
     const int b_lo = (int)(((long long)p.nA * f) / p.nF);
     const int b_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
@@ -1269,7 +1280,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base) {
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
-  const int nF = 32;
+  const int nF = kFinishSplit;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
