@@ -556,7 +556,7 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
 // ------------------------------------------------------------------ pass B
 
 template <int G>
-__global__ __launch_bounds__(PassCfg<G>::NT) void k_select(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT, 6) void k_select(DecPlan p) {
   using S = ScoreTiles<G>;
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   const int pair = blockIdx.y, blk = blockIdx.x;
