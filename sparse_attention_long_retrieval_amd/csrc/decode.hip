@@ -15,6 +15,7 @@
 //                score grid (bins of 0.5 below the block's top bin; each weight
 //                taken relative to its bin's upper edge, so integer bin sums of
 //                different blocks add without rescaling).  One exp per score.
+//                Block 0 also writes qi and the rotated queries.
 //   k_threshold  per (pair, q-head): merge the block summaries, locate the
 //                boundary bin where the running mass reaches p*Z.  A boundary
 //                below the 16-unit window makes the whole tail the candidate set
@@ -24,9 +25,10 @@
 //                from LDS-staged K/V tiles, keys in the boundary bin are written
 //                as candidates to the block's own region (fixed order).
 //   k_finish     per (pair, q-head), nF blocks: exact threshold inside the
-//                boundary bin (bisection on the ordered fp32 key with exact
-//                integer mass sums, candidates held in LDS when they fit), then
-//                attention over a share of the selected candidates.
+//                boundary bin (radix select on the ordered fp32 key with exact
+//                integer mass sums, candidates held in LDS when they fit;
+//                bisection over the global lists otherwise), then attention over
+//                a share of the selected candidates.
 //   k_merge      combine all partial softmax states into the bf16 output.
 // Every sum and row order is fixed, so results are bit-identical across runs.
 #include "attn_tile.h"
