@@ -1142,22 +1142,35 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(DecPlan p) {
   float M = -INFINITY, L = 0.f, O[kMergeDims];
 #pragma unroll
   for (int d = 0; d < kMergeDims; ++d) O[d] = 0.f;
-  for (int k = tid; k < n; k += NT) {
-    const float* q = (k < p.nA) ? p.partB + ((size_t)unit * p.nA + k) * kPartStride
-                                : p.partF + ((size_t)unit * p.nF + (k - p.nA)) * kPartStride;
-    const float mk = q[0];
-    if (mk == -INFINITY) continue;
-    const float lk = q[1];
-    const float4 a = *(const float4*)&q[4 + chunk * kMergeDims];
-    const float4 c = *(const float4*)&q[8 + chunk * kMergeDims];
-    const float nm = fmaxf(M, mk);
-    const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
-    const float sk = exp2f(mk - nm);
-    L = L * so + lk * sk;
-    const float ov[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  // KM partials per thread are requested together (unconditionally: an index past
+  // n re-reads the last partial and is skipped), then folded in order k = tid,
+  // tid + NT, ...
+  constexpr int KM = 4;
+  for (int k0 = 0; k0 < n; k0 += KM * NT) {
+    float mk[KM], lk[KM];
+    float4 a[KM], c[KM];
 #pragma unroll
-    for (int d = 0; d < kMergeDims; ++d) O[d] = O[d] * so + ov[d] * sk;
-    M = nm;
+    for (int u = 0; u < KM; ++u) {
+      const int k = min(k0 + u * NT + tid, n - 1);
+      const float* q = (k < p.nA) ? p.partB + ((size_t)unit * p.nA + k) * kPartStride
+                                  : p.partF + ((size_t)unit * p.nF + (k - p.nA)) * kPartStride;
+      mk[u] = q[0];
+      lk[u] = q[1];
+      a[u] = *(const float4*)&q[4 + chunk * kMergeDims];
+      c[u] = *(const float4*)&q[8 + chunk * kMergeDims];
+    }
+#pragma unroll
+    for (int u = 0; u < KM; ++u) {
+      if (k0 + u * NT + tid >= n || mk[u] == -INFINITY) continue;
+      const float nm = fmaxf(M, mk[u]);
+      const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
+      const float sk = exp2f(mk[u] - nm);
+      L = L * so + lk[u] * sk;
+      const float ov[8] = {a[u].x, a[u].y, a[u].z, a[u].w, c[u].x, c[u].y, c[u].z, c[u].w};
+#pragma unroll
+      for (int d = 0; d < kMergeDims; ++d) O[d] = O[d] * so + ov[d] * sk;
+      M = nm;
+    }
   }
   // butterfly over the wave
 #pragma unroll
