@@ -334,20 +334,32 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
         }
       }
   } else {
+    // eight scores at a time without branches: their bin scales are read together
+    // (one LDS wait), and a score outside the window adds 0 to bin 0
+    static_assert((S::TPW * 4) % 8 == 0, "whole groups of eight scores");
 #pragma unroll
-    for (int T = 0; T < S::TPW; ++T)
+    for (int g = 0; g < S::TPW * 4; g += 8) {
+      float wt[8], bs[8];
+      unsigned jc[8];
+      bool in[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int u = 0; u < 8; ++u) {
         // a -inf score weighs 0 and its key (-1e9) lies far outside the bins
-        const float sv = sc[T][r];
-        const float wt = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
-        z += wt;
+        const float sv = sc[(g + u) >> 2][(g + u) & 3];
+        wt[u] = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);  // <= 1
+        z += wt[u];
         const unsigned j = (unsigned)(kt - score_key(sv, kInvDelta));
-        if (j < (unsigned)kNB) {
-          // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1], 2^-20 units
-          atomicAdd(&bins[j][hs][copy], (unsigned)__builtin_fmaf(wt, bscale[j], 0.5f));
-        }
+        in[u] = j < (unsigned)kNB;
+        jc[u] = in[u] ? j : 0u;
+        bs[u] = bscale[jc[u]];
       }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // relative to the bin's upper edge e_top - j * 0.5: in (e^-0.5, 1], 2^-20 units
+        const unsigned v = in[u] ? (unsigned)__builtin_fmaf(wt[u], bs[u], 0.5f) : 0u;
+        atomicAdd(&bins[jc[u]][hs][copy], v);
+      }
+    }
   }
   {
     const unsigned long long zfx = head_lanes_sum<G>((unsigned long long)((double)z * kFxZ));
