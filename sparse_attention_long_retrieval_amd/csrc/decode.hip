@@ -569,6 +569,8 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
 
 // ------------------------------------------------------------------ pass B
 
+// The occupancy hint keeps the G = 8 kernel at 72 VGPRs (six waves per SIMD), so two
+// select blocks leave room on a CU for a local-head block running beside them.
 template <int G>
 __global__ __launch_bounds__(PassCfg<G>::NT, 6) void k_select(DecPlan p) {
   using S = ScoreTiles<G>;
