@@ -409,7 +409,8 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
   // Two rows per thread, one per block summary it holds (u32, as stored), written
   // shifted onto this head's grid with plain stores; summaries beyond two per thread
   // (more than 2 NT blocks) are added into colx with 64-bit LDS atomics.  One padding
-  // column: the rows of consecutive threads start on different banks.
+  // column: the rows of consecutive threads start on different banks, and entries
+  // shifted past the window are stored there.
   __shared__ unsigned rows[2 * NT][kNB + 1];
   __shared__ unsigned long long colp[NT / kNB][kNB];
   __shared__ unsigned long long colx[kNB];
@@ -482,9 +483,10 @@ __global__ __launch_bounds__(kThrThreads) void k_threshold(DecPlan p) {
       const int shift = kt - ktb;
       const unsigned* vv = (const unsigned*)v;
       if (slot < 2) {
+        // entries shifted past the window land in the padding column (never summed):
+        // no branch per store
 #pragma unroll
-        for (int j = 0; j < kNB; ++j)
-          if (j + shift < kNB) rows[2 * tid + slot][j + shift] = vv[j];
+        for (int j = 0; j < kNB; ++j) rows[2 * tid + slot][min(j + shift, kNB)] = vv[j];
       } else {
 #pragma unroll
         for (int j = 0; j < kNB; ++j)
