@@ -134,7 +134,8 @@ struct RowMask {
 // Attend rows get(0) .. get(n - 1) in tiles of 64, with the next tile's K and V rows
 // loaded into registers while the current one is computed.  Rows past the end of the
 // list re-read the last row (their lanes are masked), so the loads need no branch.
-// All NT threads call it; get(i) is uniform in what it returns for a given i.
+// All NT threads call it; get(i) must give every thread the same entry i (it reads a
+// list the block shares, in LDS), and the list must not change until it returns.
 template <int G, int NT, class Get>
 __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kbase,
                                             const uint16_t* vbase, int n, Get&& get, float& m,
@@ -173,7 +174,6 @@ __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kba
     if (t0 >= 0) tile_compute<G>(sm, nr, m, l, o0, o1);
   }
 }
-
 
 // Cross-block data of one launch goes through device-coherent accesses: relaxed
 // agent-scope atomic stores write through the XCD's L2 and agent-scope loads
