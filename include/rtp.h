@@ -161,7 +161,8 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre,
  *   out      [B][Hq][D] bf16 device; only retrieval q-head rows are written
  *   dbg      optional (NULL or host struct with device pointers)
  * Errors: RTP_ERR_RANGE if seq_len < 1 or > max_seq, top_p not in (0, 1] or NaN;
- *   RTP_ERR_UNSUPPORTED if G is not 1, 2, 4 or 8; RTP_ERR_WORKSPACE if ws_bytes is
+ *   RTP_ERR_UNSUPPORTED if G is not 1, 2, 4 or 8, or batch * n_ret * G > 65535 (one
+ *   launch grid dimension per retrieval q-head); RTP_ERR_WORKSPACE if ws_bytes is
  *   smaller than rtp_workspace_size(desc, RTP_OP_DECODE, 1, seq_len).
  */
 rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
@@ -192,12 +193,17 @@ rtp_status rtp_decode_topk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
  * rtp_prefill_chunk - retrieval q-heads of a chunk of Tq query rows at positions
  * q_start .. q_start+Tq-1 (their tokens already appended).  Each row t runs the
  * decode computation above with keys j <= q_start+t (causal): indexer scores,
- * its own top-p set plus sinks, exact attention over that set.
+ * its own top-p set plus sinks, exact attention over that set.  The pages keep the
+ * retrieval heads dense during prefill and name a sparser prefill as open work
+ * ([techwalker] §8 limitations; [ngjoo] limitations); the per-row selection is the
+ * decode step's ([techwalker] §3, §4), applied to every row of the chunk, and
+ * top_p >= 1 runs the dense causal attention the pages use.
  *
  *   q_pre  [B][Hq][Tq][D] bf16 device;  out [B][Hq][Tq][D] bf16 device (retrieval
  *   q-head rows written).  Other arguments as for rtp_decode_sparse_attn.
  * Errors: RTP_ERR_RANGE if q_start < 0 or q_start + Tq > max_seq; RTP_ERR_SHAPE if
- *   Tq < 1; otherwise as for decode (workspace op RTP_OP_PREFILL).
+ *   Tq < 1; RTP_ERR_UNSUPPORTED if q_start + Tq >= 2^21 causal keys or batch * n_ret
+ *   * G * Tq > 2^30; otherwise as for decode (workspace op RTP_OP_PREFILL).
  */
 rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
                              int32_t q_start, int32_t Tq, const rtp_bf16* w_q,

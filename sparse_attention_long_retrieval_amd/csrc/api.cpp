@@ -145,7 +145,8 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
     case RTP_OP_APPEND: *bytes = 0; return RTP_OK;
     case RTP_OP_DECODE:
       *bytes = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
-      if (*bytes == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
+      if (*bytes == 0)
+        return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d", rtp::kMaxGridY);
       return RTP_OK;
     case RTP_OP_SWA: {
       if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
@@ -285,8 +286,11 @@ rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const 
   if (dbg && (dbg->sel_idx && dbg->sel_cap < 1)) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
   if (dbg && dbg->phase_events && dbg->n_phase_events < 6)
     return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 6");
+  // the index passes launch batch * n_ret blocks in grid y, the finish kernel
+  // batch * n_ret * G; decode_workspace returns 0 past the grid limit
   const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
-  if (need == 0) return fail(RTP_ERR_UNSUPPORTED, "batch * n_ret too large for seq_len");
+  if (need == 0)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d", rtp::kMaxGridY);
   if (ws_bytes < need)
     return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::DecPlan p;

@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kClThreads) void k_cl_select(ClDecPlan p) {
   const int pair = unit / p.G, h = unit % p.G;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
   const int qh = p.ret_kv[ret_i] * p.G + h;
-  __shared__ float part[16][kR];
+  __shared__ double part[16][kR];
   __shared__ float qi_s[kR];
   __shared__ unsigned long long key[kClMaxK];
   __shared__ int val[kClMaxK];
@@ -277,12 +277,14 @@ __global__ __launch_bounds__(kClThreads) void k_cl_select(ClDecPlan p) {
 
   const uint16_t* q = p.q_pre + ((size_t)b * p.Hq + qh) * kD;
   {
-    // qi = q . W_q: thread (part, c) sums 8 dimensions, parts added in order
+    // qi = q . W_q: thread (part, c) sums 8 dimensions, parts added in order; the
+    // bf16 products and their fp64 sums are exact, so qi is the fp32 rounding of the
+    // exact dot product
     const uint16_t* w = p.w_q + (size_t)(ret_i * p.G + h) * kD * kR;
     const int c = tid & 15, pt = tid >> 4;
-    float acc = 0.f;
+    double acc = 0.0;
     for (int d = 8 * pt; d < 8 * pt + 8; ++d)
-      acc = __fmaf_rn(bf16_to_f32(q[d]), bf16_to_f32(w[d * kR + c]), acc);
+      acc = __fma_rn((double)bf16_to_f32(q[d]), (double)bf16_to_f32(w[d * kR + c]), acc);
     part[pt][c] = acc;
   }
   if (tid < kD / 2) {
@@ -296,9 +298,9 @@ __global__ __launch_bounds__(kClThreads) void k_cl_select(ClDecPlan p) {
   }
   __syncthreads();
   if (tid < kR) {
-    float acc = 0.f;
+    double acc = 0.0;
     for (int pt = 0; pt < 16; ++pt) acc += part[pt][tid];
-    qi_s[tid] = acc * p.idx_scale;
+    qi_s[tid] = (float)acc * p.idx_scale;
   }
   __syncthreads();
 
@@ -309,10 +311,12 @@ __global__ __launch_bounds__(kClThreads) void k_cl_select(ClDecPlan p) {
   float sig = -INFINITY;
   if (k < p.K) {
     const float* c = p.centroids + ((size_t)pair * p.K + k) * kR;
-    float acc = 0.f;
+    // fp32 x fp32 products are exact in fp64: sigma is the fp32 rounding of the
+    // (practically always exact) fp64 sum
+    double acc = 0.0;
 #pragma unroll
-    for (int d = 0; d < kR; ++d) acc = __fmaf_rn(qi_s[d], c[d], acc);
-    sig = acc;
+    for (int d = 0; d < kR; ++d) acc = __fma_rn((double)qi_s[d], (double)c[d], acc);
+    sig = (float)acc;
   }
   const bool live = n_k > 0;
   bool hit;
@@ -561,21 +565,21 @@ size_t cluster_decode_workspace(int P, int G, int K, ClDecPlan* plan, char* base
 }
 
 hipError_t launch_cluster_build(const ClBuildPlan& p, int iters, hipStream_t s) {
-  hipLaunchKernelGGL(k_cl_seed, dim3(p.P), dim3(kClThreads), 0, s, p);
+  RTP_LAUNCH(k_cl_seed, dim3(p.P), dim3(kClThreads), s, p);
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(k_cl_assign<false>, dim3(p.nb, p.P), dim3(kClThreads), 0, s, p);
-    hipLaunchKernelGGL(k_cl_update, dim3(p.P), dim3(kClThreads), 0, s, p);
+    RTP_LAUNCH(k_cl_assign<false>, dim3(p.nb, p.P), dim3(kClThreads), s, p);
+    RTP_LAUNCH(k_cl_update, dim3(p.P), dim3(kClThreads), s, p);
   }
-  hipLaunchKernelGGL(k_cl_assign<true>, dim3(p.nb, p.P), dim3(kClThreads), 0, s, p);
-  hipLaunchKernelGGL(k_cl_offsets, dim3(p.P), dim3(kClThreads), 0, s, p);
-  hipLaunchKernelGGL(k_cl_scatter, dim3(p.nb, p.P), dim3(kClThreads), 0, s, p);
-  return hipGetLastError();
+  RTP_LAUNCH(k_cl_assign<true>, dim3(p.nb, p.P), dim3(kClThreads), s, p);
+  RTP_LAUNCH(k_cl_offsets, dim3(p.P), dim3(kClThreads), s, p);
+  RTP_LAUNCH(k_cl_scatter, dim3(p.nb, p.P), dim3(kClThreads), s, p);
+  return hipSuccess;
 }
 
 hipError_t launch_cluster_decode(const ClDecPlan& p, hipStream_t s) {
   const int U = p.P * p.G;
-  hipLaunchKernelGGL(k_cl_select, dim3(U), dim3(kClThreads), 0, s, p);
-  hipLaunchKernelGGL(k_cl_attend, dim3(p.nF, U), dim3(kClThreads), 0, s, p);
+  RTP_LAUNCH(k_cl_select, dim3(U), dim3(kClThreads), s, p);
+  RTP_LAUNCH(k_cl_attend, dim3(p.nF, U), dim3(kClThreads), s, p);
   // the merge of decode.hip over the kClNF slices (no pass-B partials)
   DecPlan m = {};
   m.out = p.out;
@@ -589,13 +593,11 @@ hipError_t launch_cluster_decode(const ClDecPlan& p, hipStream_t s) {
   m.nF = p.nF;
   m.partB = p.partF;
   m.partF = p.partF;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = launch_merge(m, s);
+  const hipError_t e = launch_merge(m, s);
   if (e != hipSuccess) return e;
   if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
-    hipLaunchKernelGGL(k_cl_debug, dim3(U), dim3(kClThreads), 0, s, p);
-  return hipGetLastError();
+    RTP_LAUNCH(k_cl_debug, dim3(U), dim3(kClThreads), s, p);
+  return hipSuccess;
 }
 
 }  // namespace rtp

@@ -120,7 +120,10 @@ __device__ __forceinline__ void load_score_tiles(
     }
 }
 
-// B operands: part 0, 1, 2 = hi, mid, lo of qi, zero off the diagonal blocks.
+// B operands: part 0, 1, 2 = lo, mid, hi of qi, zero off the diagonal blocks.  The
+// parts are summed in that order, smallest first: the fp32 accumulator then rounds
+// a sum whose small parts are already in, which lands on the correctly rounded
+// score more often than the largest-first order.
 template <int G>
 __device__ __forceinline__ void make_score_b(const float (*qi_s)[kR],
                                              uint4 (&bq)[3][ScoreTiles<G>::CH]) {
@@ -137,9 +140,9 @@ __device__ __forceinline__ void make_score_b(const float (*qi_s)[kR],
       const uint16_t hi = f32_to_bf16(q);
       const float r1 = q - bf16_to_f32(hi);
       const uint16_t mid = f32_to_bf16(r1);
-      v[0][u] = hi;
+      v[2][u] = hi;
       v[1][u] = mid;
-      v[2][u] = f32_to_bf16(r1 - bf16_to_f32(mid));
+      v[0][u] = f32_to_bf16(r1 - bf16_to_f32(mid));
     }
 #pragma unroll
     for (int s = 0; s < 3; ++s) pk[s][e] = (uint32_t)v[s][0] | ((uint32_t)v[s][1] << 16);
@@ -251,18 +254,20 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   uint4 a[S::TPW][S::CH];
   load_score_tiles<G>(idx, tok0, p.N, a);
   {
-    // qi = q . W_q (fp32): four threads per output, 32 terms each, (p0+p1)+(p2+p3)
-    float acc = 0.f;
+    // qi = q . W_q, four threads per output, 32 terms each.  The bf16 products are
+    // exact in fp64 and so is their fp64 sum (the terms span far fewer than the 37
+    // bits of headroom), so qi is the fp32 rounding of the exact dot product.
+    double acc = 0.0;
     const int hh = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
     if (hh < G) {
       const uint16_t* wq = wq_s + hh * kD * kR;
       const uint16_t* qq = q_s + hh * kD;
       for (int d = 32 * part; d < 32 * part + 32; ++d)
-        acc = __fmaf_rn(bf16_to_f32(qq[d]), bf16_to_f32(wq[d * kR + c]), acc);
+        acc = __fma_rn((double)bf16_to_f32(qq[d]), (double)bf16_to_f32(wq[d * kR + c]), acc);
     }
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
-    if (hh < G && part == 0) qi_s[hh][c] = acc * p.idx_scale;
+    if (hh < G && part == 0) qi_s[hh][c] = (float)acc * p.idx_scale;
   }
   __syncthreads();
   if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
@@ -1276,24 +1281,24 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
     if (p.events) (void)hipEventRecord(p.events[k], s);
   };
   mark(0);
-  hipLaunchKernelGGL(k_scan<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
+  RTP_LAUNCH(k_scan<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
   mark(1);
-  hipLaunchKernelGGL(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), 0, s, p);
+  RTP_LAUNCH(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), s, p);
   mark(2);
-  hipLaunchKernelGGL(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), 0, s, p);
+  RTP_LAUNCH(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
   mark(3);
-  hipLaunchKernelGGL(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), 0, s, p);
+  RTP_LAUNCH(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), s, p);
   mark(4);
-  hipLaunchKernelGGL(k_merge, dim3(p.P * G, kD / kMergeDims), dim3(kMergeThreads), 0, s, p);
+  RTP_LAUNCH(k_merge, dim3(p.P * G, kD / kMergeDims), dim3(kMergeThreads), s, p);
   mark(5);
   if (p.dbg_cnt || p.dbg_idx || p.dbg_tau || p.dbg_union)
-    hipLaunchKernelGGL(k_debug_sets<G>, dim3(p.P * G), dim3(256), 0, s, p);
-  return hipGetLastError();
+    RTP_LAUNCH(k_debug_sets<G>, dim3(p.P * G), dim3(256), s, p);
+  return hipSuccess;
 }
 
 hipError_t launch_merge(const DecPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3(p.P * p.G, kD / kMergeDims), dim3(kMergeThreads), 0, s, p);
-  return hipGetLastError();
+  RTP_LAUNCH(k_merge, dim3(p.P * p.G, kD / kMergeDims), dim3(kMergeThreads), s, p);
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecPlan& p, hipStream_t s) {
@@ -1312,6 +1317,8 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
   const int nF = kFinishSplit;
+  // grid y of the index passes is P, of the finish kernel P * G
+  if ((long long)P * G > kMaxGridY) return 0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;

@@ -9,7 +9,8 @@
 // p >= 1 (every key selected) runs the dense causal flash kernel instead.
 //
 // Kernels:
-//   k_pf_qprep    qi = q . W_q (fp32, idx_scale folded) per query vector, split
+//   k_pf_qprep    qi = q . W_q (the fp32 rounding of the exact dot product,
+//                 idx_scale folded) per query vector, split
 //                 into three bf16 parts lo + mid + hi = qi exactly, so bf16 MFMA
 //                 products are exact and scores keep fp32 accuracy.
 //   k_pf_index    one block = 64 query vectors of one (batch, KV head) against
@@ -90,9 +91,11 @@ __global__ __launch_bounds__(256) void k_pf_qprep(PfPlan p) {
   const int h = p.ret_kv[i] * p.G + g;
   const uint16_t* q = p.q_pre + (((size_t)b * p.Hq + h) * p.Tq + row) * kD;
   const uint16_t* w = p.w_q + (size_t)(i * p.G + g) * kD * kR + c;
-  float acc = 0.f;
-  for (int d = 0; d < kD; ++d) acc = __fmaf_rn(bf16_to_f32(q[d]), bf16_to_f32(w[d * kR]), acc);
-  const float qi = acc * p.idx_scale;
+  // exact bf16 products summed in fp64 (exact for these magnitudes), one rounding
+  double acc = 0.0;
+  for (int d = 0; d < kD; ++d)
+    acc = __fma_rn((double)bf16_to_f32(q[d]), (double)bf16_to_f32(w[d * kR]), acc);
+  const float qi = (float)acc * p.idx_scale;
   const uint16_t hi = f32_to_bf16(qi);
   const float r1 = qi - bf16_to_f32(hi);
   const uint16_t mid = f32_to_bf16(r1);
@@ -1237,29 +1240,28 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
     if (p.events) (void)hipEventRecord(p.events[k], s);
   };
   mark(0);
-  hipLaunchKernelGGL(k_pf_qprep, dim3((p.V * 16 + 255) / 256), dim3(256), 0, s, p);
+  RTP_LAUNCH(k_pf_qprep, dim3((p.V * 16 + 255) / 256), dim3(256), s, p);
   mark(1);
-  hipLaunchKernelGGL(k_pf_index, dim3((Gv + kPfVecs - 1) / kPfVecs, p.B * p.n_ret), dim3(256), 0,
-                     s, p);
+  RTP_LAUNCH(k_pf_index, dim3((Gv + kPfVecs - 1) / kPfVecs, p.B * p.n_ret), dim3(256), s, p);
   mark(2);
-  hipLaunchKernelGGL(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_count, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_iscan, dim3(1), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(k_pf_items, dim3((p.V + 255) / 256), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_oscan, dim3(1), dim3(1024), 0, s, p);
-  hipLaunchKernelGGL(k_pf_iscatter, dim3((p.max_items + 255) / 256), dim3(256), 0, s, p);
+  RTP_LAUNCH(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), s, p);
+  RTP_LAUNCH(k_pf_count, dim3((p.V + 255) / 256), dim3(256), s, p);
+  RTP_LAUNCH(k_pf_iscan, dim3(1), dim3(1024), s, p);
+  RTP_LAUNCH(k_pf_items, dim3((p.V + 255) / 256), dim3(256), s, p);
+  RTP_LAUNCH(k_pf_oscan, dim3(1), dim3(1024), s, p);
+  RTP_LAUNCH(k_pf_iscatter, dim3((p.max_items + 255) / 256), dim3(256), s, p);
   mark(3);
-  hipLaunchKernelGGL(k_pf_attend, dim3(kPfAttendBlocks), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(k_pf_merge, dim3((p.V + 3) / 4), dim3(256), 0, s, p);
+  RTP_LAUNCH(k_pf_attend, dim3(kPfAttendBlocks), dim3(256), s, p);
+  RTP_LAUNCH(k_pf_merge, dim3((p.V + 3) / 4), dim3(256), s, p);
   mark(4);
   if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
-    hipLaunchKernelGGL(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), 0, s, p);
-  return hipGetLastError();
+    RTP_LAUNCH(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), s, p);
+  return hipSuccess;
 }
 
 hipError_t launch_prefill_debug_all(const PfPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_pf_debug_all, dim3((p.V + 63) / 64), dim3(64), 0, s, p);
-  return hipGetLastError();
+  RTP_LAUNCH(k_pf_debug_all, dim3((p.V + 63) / 64), dim3(64), s, p);
+  return hipSuccess;
 }
 
 }  // namespace rtp

@@ -9,6 +9,18 @@
 
 namespace rtp {
 
+// Launch a kernel and return from the calling launcher if the launch failed, so that
+// no later kernel of the same call runs on the results of one that never started.
+#define RTP_LAUNCH(kernel, grid, block, stream, ...)                          \
+  do {                                                                        \
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);          \
+    const hipError_t rtp_launch_err_ = hipGetLastError();                     \
+    if (rtp_launch_err_ != hipSuccess) return rtp_launch_err_;                \
+  } while (0)
+
+// Largest y and z extent of a launch grid.
+constexpr int kMaxGridY = 65535;
+
 constexpr int kD = 128;
 constexpr int kR = 16;
 constexpr int kMaxKv = 64;
@@ -262,7 +274,8 @@ struct ClDecPlan {
   int dbg_cap;
 };
 
-// Workspace sizing (bytes).  Returns 0 when the shape exceeds the counter region.
+// Workspace sizing (bytes).  Returns 0 when the shape cannot be launched (a grid
+// extent above kMaxGridY, or counters beyond the counter region).
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
 size_t cluster_build_workspace(int P, int K, int n_tok, ClBuildPlan* plan, char* base);
 size_t cluster_decode_workspace(int P, int G, int K, ClDecPlan* plan, char* base);

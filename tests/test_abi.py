@@ -166,3 +166,19 @@ def test_cluster_validation():
     st = L.rtp_decode_cluster_attn(layer.desc(), fake, fake, fake, fake, fake, fake, fake, 128,
                                    3000, 4000, 0.9, 1.0, 0.088, fake, None, fake, wsd - 1, None)
     assert st == 6
+
+
+def test_decode_grid_limit():
+    """The decode launches batch * n_ret * G finish blocks in grid y: beyond 65535 the
+    call and the workspace query return RTP_ERR_UNSUPPORTED before any launch."""
+    lib = R.lib()
+    ok = R.Layer(8191, 8, 1, 64, [0])          # 8191 * 8 = 65528 retrieval q-heads
+    assert R.workspace_size(ok, R.OP_DECODE, 64) > 0
+    big = R.Layer(8192, 8, 1, 64, [0])         # 65536
+    assert _status(lambda: R.workspace_size(big, R.OP_DECODE, 64)) == 5
+    st = lib.rtp_decode_sparse_attn(big.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, 64, 0.9, 1.0,
+                                    0.088, FAKE, None, FAKE, 1 << 40, None)
+    assert st == 5 and b"65535" in lib.rtp_last_error()
+    st = lib.rtp_decode_topk(big.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, 64, 10, 1.0, 0.088, FAKE,
+                             None, FAKE, 1 << 40, None)
+    assert st == 5

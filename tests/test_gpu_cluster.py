@@ -86,15 +86,20 @@ def _check_clusters(hit_gpu, r, counts, p, neutral):
     """Hit sets equal, or differing only in clusters at the threshold (band), or a
     valid top-p cut under the oracle's masses.  Clusters made of sinks only
     (`neutral`) cannot be seen in a set and are left out of the comparison."""
+    st = P.stats()
     hit_o = set(r["hit"].tolist()) - neutral
     hit_g = set(hit_gpu)
     if hit_g == hit_o:
+        st["exact"] += 1
         return "exact"
     sig = r["sigma"].astype(np.float64)
     tau = float(r["tau"])
     diff = hit_g ^ hit_o
     if all(abs(sig[c] - tau) <= P.BAND_REL * max(abs(tau), 1.0) for c in diff):
+        st["band"] += 1
+        st["band_tokens"] += len(diff)
         return "band"
+    assert p > P.STRICT_P, f"p={p}: cluster cut differs outside the band: {sorted(diff)[:8]}"
     live = np.nonzero(counts > 0)[0]
     m = sig[live].max()
     w = {int(c): counts[c] * np.exp(sig[c] - m) for c in live}
@@ -103,8 +108,11 @@ def _check_clusters(hit_gpu, r, counts, p, neutral):
     mass = sum(w[c] for c in hit_full)
     lowest = min(sig[c] for c in hit_full)
     below = sum(w[c] for c in hit_full if sig[c] > lowest)
-    assert mass >= (p - P.MASS_TOL) * W_ and below < (p + P.MASS_TOL) * W_, \
+    assert mass >= p * W_ * (1 - P.MASS_TOL) and below < p * W_ * (1 + P.MASS_TOL), \
         f"cluster cut differs outside the band: {sorted(diff)[:8]}"
+    st["valid-alt"] += 1
+    st["alt_tokens"] += len(diff)
+    st["max_mass_slack"] = max(st["max_mass_slack"], abs(mass / (p * W_) - 1.0))
     return "valid-alt"
 
 
@@ -151,6 +159,7 @@ def _compare_decode(wl, kc, vc, cl_np, n_tok, p, res, K):
                 else:
                     assert set(hit_gpu) == set(np.nonzero(counts)[0].tolist()) - neutral
                     kind = "exact"
+                    P.stats()["exact"] += 1
                 # the set is exactly: members of its clusters, appended tokens, sinks
                 want = set(range(min(wl.n_sink, wl.N))) | set(range(n_tok, wl.N))
                 for c in hit_gpu:
@@ -162,7 +171,7 @@ def _compare_decode(wl, kc, vc, cl_np, n_tok, p, res, K):
                 P.check_out(res["out"][b, h], own, f"own set b{b} h{h}")
                 if kind == "exact":
                     assert np.array_equal(S, r["S"])
-                    P.check_out(res["out"][b, h], r["out"], f"b{b} h{h}")
+                P.check_out(res["out"][b, h], r["out"], f"b{b} h{h} ({kind})")
     return kinds
 
 

@@ -151,16 +151,13 @@ def _check_retrieval(wl, kc, vc, idx, res, top_p, rows, idx_scale=1.0):
                     S = _gpu_set(res, unit)
                     kind = P.check_set(S, res["tau"][unit], r, top_p, wl.n_sink)
                     kinds[kind] = kinds.get(kind, 0) + 1
-                    # attention over the GPU's own set always; end to end against the
-                    # oracle's set when the sets agree (a token exempt at the threshold
-                    # can carry any attention weight, so differing sets give different
-                    # outputs by design)
+                    # attention over the GPU's own set (the attention step alone), and
+                    # the output end to end against the oracle's, whatever the set kind
                     qr = O.rope(O.bf16_to_f64(wl.q_pre[b, h, t]), wl.q_start + t, wl.rope_base)
                     own = O.attention(qr, kc[b, kv][S], vc[b, kv][S], wl.attn_scale)
                     err = P.check_out(res["out"][b, h, t], own, f"own set b{b} h{h} t{t}")
-                    if kind == "exact":
-                        err = max(err, P.check_out(res["out"][b, h, t], r["out"],
-                                                   f"b{b} h{h} row {t}"))
+                    err = max(err, P.check_out(res["out"][b, h, t], r["out"],
+                                               f"b{b} h{h} row {t} ({kind})"))
                     worst = max(worst, err)
     return kinds, worst
 

@@ -345,6 +345,36 @@ def test_kmeans_single_cluster_is_the_mean():
     assert list(r["offsets"]) == [0, 5000]
 
 
+def test_kmeans_tiny_values_truncation_bound():
+    """Index values below 2^-17 are not whole multiples of 2^-24, so the centre sums
+    truncate them (the cluster-index reading).  Each row then loses less than one
+    2^-24 unit per dimension, so a centre of n rows is within 2^-24 of the exact
+    fp64 mean (plus the fp32 rounding of the result); rows and centres of size
+    2^-20 and below are assigned exactly as scipy's fp64 distances say."""
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(402)
+    x = rng.standard_normal((4000, 16)) * 2.0 ** -19            # |x| mostly below 2^-17
+    bits = O.f64_to_bf16(x)
+    xv = O.bf16_to_f64(bits)
+    assert (np.abs(xv) < 2.0 ** -17).mean() > 0.9
+    frac = np.abs(xv * 2.0 ** 24 - np.trunc(xv * 2.0 ** 24))
+    assert (frac > 0).mean() > 0.5                                # truncation really occurs
+    assign = np.arange(4000) % 5
+    c = O.kmeans_centres(bits, assign, np.zeros((5, 16), np.float32))
+    for k in range(5):
+        mean = xv[assign == k].mean(axis=0)
+        err = np.abs(c[k].astype(np.float64) - mean)
+        assert np.all(err <= 2.0 ** -24 + 2.0 ** -24 * np.abs(mean)), (k, err.max())
+    x32 = xv.astype(np.float32)
+    cen = (rng.standard_normal((9, 16)) * 2.0 ** -20).astype(np.float32)
+    got = O.kmeans_assign(x32, cen)
+    d = cdist(x32.astype(np.float64), cen.astype(np.float64), "sqeuclidean")
+    two = np.sort(d, axis=1)[:, :2]
+    far = (two[:, 1] - two[:, 0]) > 1e-5 * two[:, 1]
+    assert far.mean() > 0.98
+    assert np.array_equal(got[far], d.argmin(axis=1)[far])
+
+
 def test_kmeans_recovers_planted_clusters():
     """Well-separated clusters seeded with one row of each: the partition is the planted
     one and the centres are the members' means."""
