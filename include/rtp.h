@@ -173,6 +173,29 @@ rtp_status rtp_decode_sparse_attn(const rtp_layer_desc* desc, const rtp_bf16* q_
                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * rtp_decode_sparse_attn_noalloc - rtp_decode_sparse_attn without a caller
+ * workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Its scratch is a
+ * static device array of RTP_NOALLOC_SCRATCH_BYTES held by every GPU the library
+ * runs on until the process ends; its address is looked up once per device on the
+ * first call there.  The call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap in time on one GPU (other streams,
+ * other host threads) race and give wrong results; stream-ordered calls are safe.
+ * Arguments, results and errors as for rtp_decode_sparse_attn, plus
+ * RTP_ERR_WORKSPACE (nothing enqueued) when the shape needs more scratch than
+ * RTP_NOALLOC_SCRATCH_BYTES, i.e. when rtp_workspace_size(desc, RTP_OP_DECODE, 1,
+ * seq_len) exceeds it (about 8 Mi retrieval q-head x key pairs: a 1M-token context
+ * with 8 retrieval q-heads fits).
+ */
+#define RTP_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+rtp_status rtp_decode_sparse_attn_noalloc(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                          const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                          const rtp_bf16* v_cache, const rtp_bf16* index,
+                                          int32_t seq_len, float top_p, float idx_scale,
+                                          float attn_scale, rtp_bf16* out,
+                                          const rtp_debug_out* dbg, void* stream);
+
+/*
  * rtp_decode_topk - the decode step above with a fixed budget instead of top-p:
  *   T = the top_k highest-scoring keys, realised as {j : s_j >= tau} with tau the
  *       top_k-th largest score (ties at tau included); top_k >= seq_len keeps every

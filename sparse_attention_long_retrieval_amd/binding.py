@@ -26,7 +26,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE"
 EXPORTED = ["rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk", "rtp_swa_attn",
             "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version",
             "rtp_decode_topk", "rtp_ring_append", "rtp_swa_attn_ring", "rtp_cluster_build",
-            "rtp_decode_cluster_attn"]
+            "rtp_decode_cluster_attn", "rtp_decode_sparse_attn_noalloc"]
 
 
 class RtpError(RuntimeError):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_decode_topk.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32, f32, f32, vp,
                                       ctypes.POINTER(DebugOut), vp, sz, vp]
+        L.rtp_decode_sparse_attn_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, i32, f32, f32, f32,
+                                                     vp, ctypes.POINTER(DebugOut), vp]
         L.rtp_prefill_chunk.argtypes = [dp, vp, i32, i32, vp, vp, vp, vp, f32, f32, f32, vp,
                                         ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_swa_attn.argtypes = [dp, vp, i32, i32, vp, vp, f32, vp, vp, sz, vp]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
         for name in ("rtp_index_append", "rtp_decode_sparse_attn", "rtp_decode_topk",
                      "rtp_prefill_chunk", "rtp_swa_attn", "rtp_workspace_size",
                      "rtp_ring_append", "rtp_swa_attn_ring", "rtp_cluster_build",
-                     "rtp_decode_cluster_attn"):
+                     "rtp_decode_cluster_attn", "rtp_decode_sparse_attn_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -194,6 +196,20 @@ def decode_sparse_attn(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_le
         layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
         top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
         _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_sparse_attn_noalloc(layer: Layer, q_pre, w_q, k_cache, v_cache, index,
+                               seq_len: int, top_p: float, out, idx_scale: float = 1.0,
+                               attn_scale: Optional[float] = None,
+                               debug: Optional[Debug] = None, stream=None) -> None:
+    """The decode step on the library's static scratch (see
+    rtp_decode_sparse_attn_noalloc): no workspace argument, nothing allocated."""
+    if attn_scale is None:
+        attn_scale = 1.0 / math.sqrt(layer.head_dim)
+    _check(lib().rtp_decode_sparse_attn_noalloc(
+        layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
+        top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
+        _stream(stream)))
 
 
 def decode_topk(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_len: int, top_k: int,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "rtp.h"
 #include "rtp_internal.h"
@@ -333,6 +334,36 @@ rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const 
   return RTP_OK;
 }
 
+// Scratch of the allocation-free decode (rtp_decode_sparse_attn_noalloc): device
+// memory of this module, one copy per GPU the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device, and is kept here.
+constexpr size_t kNoAllocScratchBytes = (size_t)80 << 20;  // RTP_NOALLOC_SCRATCH_BYTES
+static_assert(kNoAllocScratchBytes == RTP_NOALLOC_SCRATCH_BYTES, "header and library agree");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device (set up on the first call there).
+rtp_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RTP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(RTP_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RTP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RTP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,6 +387,32 @@ rtp_status rtp_decode_topk(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
   if (top_k < 1) return fail(RTP_ERR_RANGE, "top_k %d < 1", top_k);
   return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, 0.5f, top_k,
                      idx_scale, attn_scale, out, dbg, workspace, ws_bytes, stream);
+}
+
+rtp_status rtp_decode_sparse_attn_noalloc(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                                          const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                                          const rtp_bf16* v_cache, const rtp_bf16* index,
+                                          int32_t seq_len, float top_p, float idx_scale,
+                                          float attn_scale, rtp_bf16* out,
+                                          const rtp_debug_out* dbg, void* stream) {
+  RTP_TRY(check_desc(desc));
+  const int G = group(desc);
+  if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
+  if (desc->n_ret == 0) return RTP_OK;
+  if (seq_len < 1 || seq_len > desc->max_seq)
+    return fail(RTP_ERR_RANGE, "seq_len %d outside [1, max_seq %d]", seq_len, desc->max_seq);
+  const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+  if (need == 0)
+    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d", rtp::kMaxGridY);
+  if (need > kNoAllocScratchBytes)
+    return fail(RTP_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch; the allocation-free decode holds %zu "
+                "(use rtp_decode_sparse_attn with a workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  RTP_TRY(noalloc_scratch(&ws));
+  return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, top_p, 0, idx_scale,
+                     attn_scale, out, dbg, ws, kNoAllocScratchBytes, stream);
 }
 
 rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, int32_t q_start,

@@ -182,3 +182,21 @@ def test_decode_grid_limit():
     st = lib.rtp_decode_topk(big.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, 64, 10, 1.0, 0.088, FAKE,
                              None, FAKE, 1 << 40, None)
     assert st == 5
+
+
+def test_noalloc_decode_rejects_shapes_beyond_its_scratch():
+    """The allocation-free decode refuses, before any HIP call, a shape whose workspace
+    exceeds its static scratch; the message names both sizes."""
+    lib = R.lib()
+    big = R.Layer(2, 16, 2, 1 << 20, [0, 1])      # 2 * 2 * 8 q-heads x 1M keys
+    need = R.workspace_size(big, R.OP_DECODE, 1 << 20)
+    assert need > 80 << 20
+    st = lib.rtp_decode_sparse_attn_noalloc(big.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                            0.9, 1.0, 0.088, FAKE, None, None)
+    assert st == 6 and str(need).encode() in lib.rtp_last_error()
+    lay = _layer()
+    for n in (0, 1001):
+        assert lib.rtp_decode_sparse_attn_noalloc(lay.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, n,
+                                                  0.9, 1.0, 0.088, FAKE, None, None) == 4
+    fits = R.Layer(1, 32, 4, 1 << 20, [0])         # the 1M-context decode shape fits
+    assert R.workspace_size(fits, R.OP_DECODE, 1 << 20) <= 80 << 20
