@@ -1,30 +1,27 @@
-"""Benchmark of the head-wise sparse attention decode step on one MI355X.
+"""Benchmark of the head-wise sparse attention step on one MI355X.
 
-One step = the whole decode hot path of one layer over one batch:
-  append of the newest token (K/V caches + 16-dim index), the retrieval-head
-  decode (indexer scan + histogram, threshold, select, resolve, gather attention,
-  merge) and the local-head sliding-window attention.
-Default workload: 1M-context decode shaped like Qwen3-30B-A3B attention (B=1,
-32 q / 4 KV heads, KV head 0 retrieval with a 1M x 16 index, 3 SWA heads with
-window 8192 + 4 sinks, 512 planted clusters, p = 0.9), synthetic seeded inputs.
+One decode step = the whole decode hot path of one layer over one batch: append of
+the newest token (K/V caches + 16-dim index), the retrieval-head decode (indexer scan
++ histogram, threshold, select, resolve, gather attention, merge) and the local-head
+sliding-window attention (on a second stream).
 
-Timing: W warm-up steps, then K timed steps.  Before each timed step a read of
-a 512 MiB scratch buffer evicts the step's working set from the 256 MB Infinity
-Cache and the L2s, so every step reads it from HBM; HIP events around each step
-(flush excluded) give the step time.  The flush reads rather than writes: a
-write leaves ~256 MB of dirty lines whose write-back would stall the next
-kernel's reads (a 32 MiB cold read takes 15 us after a write flush, 8.6 us
-after a read flush on this part), a cost no decode step pays.  A second pass
-of K steps records the library's phase events for the
-per-kernel durations used by the roofline.  The CPU oracle is timed on a sample
-of whole steps on the host cores (rank 0, N=1 only).
-The same run also measures the chunked prefill at 256K (a 4096-row chunk
-appended to 262,144 cached keys, 32 q / 8 KV heads, 2 retrieval KV heads,
-6 local heads with window 8192 + 4 sinks, p = 0.9): append of the chunk,
-per-row top-p selection and gather attention of the retrieval heads, and the
-causal window attention of the local heads on MFMA tiles; prefill tok/s is
-4096 / step time.  Its summary goes in the "prefill" field (skip with
---no-prefill).
+Headline workload: 1M-context decode shaped like Qwen3-30B-A3B attention (B=1, 32 q /
+4 KV heads, KV head 0 retrieval with a 1M x 16 index, 3 SWA heads with window 8192 + 4
+sinks kept in ring caches, 512 planted clusters, p = 0.9).  The same run measures the
+Qwen3-8B-shaped decode at 64K (B=8) and the variable-budget decode at 128K (B=4, p in
+{0.8, 0.9, 0.95}) under "configs", and the chunked prefill (a 4096-row chunk, 32 q / 8
+KV heads, 2 retrieval KV heads) at 256K and at 1M context under "prefill" and
+"prefill_1m".  Inputs are synthetic and seeded.
+
+Timing: W warm-up steps, then exactly K timed steps (the headline value is their
+median).  Before every timed step a read of a 512 MiB buffer evicts the working set
+from the 256 MB Infinity Cache and the L2s, so each step reads its bytes from HBM;
+HIP events on the step's stream bracket each step (flush excluded).  A read flush
+leaves clean lines; a write flush would leave dirty lines whose write-back lands in
+the next kernel.  A second series of at least 200 steps gives the median, p10 and
+p90; a third records the library's phase events for per-kernel durations (each
+event adds a few microseconds to the phase it closes).  The CPU oracle is timed on a
+bounded sample on the host cores (N=1 only).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -32,7 +29,6 @@ from __future__ import annotations
 import argparse
 import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -44,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "sparse decode μs/step + achieved HBM GB/s (% peak) at 128K–1M ctx; prefill tok/s"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "sparse_attention_long_retrieval_amd", "csrc")
 # Sources that define the scan kernel; its counter summary is void once they change.
 SCAN_SOURCES = ("decode.hip", "rtp_common.h", "rtp_internal.h", "attn_tile.h")
@@ -72,7 +69,7 @@ def measured_traffic(workload: str):
     kv = {}
     with open(path) as f:
         for line in f:
-            if ":" in line:
+            if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
     if kv.get("source_digest") != source_digest(SCAN_SOURCES):
@@ -92,6 +89,15 @@ def flush_caches(buf) -> None:
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dist(ms, scale=1e3, nd=2):
+    """median / p10 / p90 / mean of a list of durations in ms, scaled (default: us)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * scale
+    return {"median": round(float(np.median(a)), nd), "p10": round(float(np.percentile(a, 10)), nd),
+            "p90": round(float(np.percentile(a, 90)), nd), "mean": round(float(a.mean()), nd),
+            "n": int(a.size)}
 
 
 class Hip:
@@ -115,22 +121,50 @@ class Hip:
         return f.value
 
 
+class Timer:
+    """Cold timed runs: flush, event, run, event, synchronise."""
+
+    def __init__(self, hip: Hip, flush, stream: int):
+        self.hip, self.flush, self.stream = hip, flush, stream
+        self.e0, self.e1 = hip.event(), hip.event()
+
+    def runs(self, fn, n: int, cold: bool = True):
+        import torch
+        out = []
+        for _ in range(n):
+            if cold:
+                flush_caches(self.flush)
+            self.hip.record(self.e0, self.stream)
+            fn()
+            self.hip.record(self.e1, self.stream)
+            torch.cuda.synchronize()
+            out.append(self.hip.elapsed_ms(self.e0, self.e1))
+        return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed steps of the headline")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4])
+    ap.add_argument("--dist-steps", type=int, default=200,
+                    help="steps of the median/p10/p90 series (at least 200 for the 1M decode)")
+    ap.add_argument("--config", type=int, default=4, choices=[2, 3, 4],
+                    help="headline decode workload")
     ap.add_argument("--top-p", type=float, default=None)
+    ap.add_argument("--no-configs", action="store_true", help="skip the 64K and 128K decodes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true", help="skip both prefill legs")
+    ap.add_argument("--no-prefill-1m", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true", help="prefill only (profiling)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fixed-budget, ring-cache and cluster-index comparisons")
     ap.add_argument("--serial-streams", action="store_true",
                     help="run the decode step's local heads on the main stream too (clean "
-                         "per-kernel times under a profiler; the step then does the same work "
-                         "serially; the prefill step always runs on one stream)")
+                         "per-kernel times under a profiler; the prefill step always runs on "
+                         "one stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
@@ -142,15 +176,203 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    res = {} if args.no_decode else decode_leg(args)
+    res = {}
+    if not args.no_decode:
+        res = headline(args)
+        if not args.no_configs and args.config == 4:
+            res["configs"] = {}
+            for c in (2, 3):
+                name, summ = other_config(args, c)
+                res["configs"][name] = summ
     if not args.no_prefill:
-        res["prefill"] = prefill_leg(args)
+        res["prefill"] = prefill_leg(args, 5)
+        if not args.no_prefill_1m:
+            res["prefill_1m"] = prefill_leg(args, 6)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def decode_leg(args):
-    """The decode step (headline): returns the JSON fields of the bench line."""
+# ------------------------------------------------------------------ decode
+
+class DecodeCtx:
+    """A decode workload resident on the GPU: caches, index, queries, workspaces, and
+    the step (append of the newest token, retrieval decode, local heads on a second
+    stream).  ring=True keeps the local heads' K/V in rings of the window."""
+
+    def __init__(self, wl, args, ring: bool):
+        import numpy as np
+        import torch
+
+        import sparse_attention_long_retrieval_amd as R
+        self.R, self.wl, self.args, self.ring = R, wl, args, ring
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa
+        self.layer = R.Layer(wl.B, wl.Hq, wl.Hkv, wl.N, wl.ret_kv_heads, wl.n_sink,
+                             wl.window, wl.rope_base)
+        N, B = wl.N, wl.B
+        self.k_cache = torch.empty((B, wl.Hkv, N, 128), dtype=torch.int16, device="cuda")
+        self.v_cache = torch.empty_like(self.k_cache)
+        self.index = torch.empty((B, wl.n_ret, N, 16), dtype=torch.int16, device="cuda")
+        self.w_q, self.w_k, self.q = dev(wl.w_q), dev(wl.w_k), dev(wl.q_pre)
+        k_pre, v_pre = dev(wl.k_pre), dev(wl.v)
+        R.index_append(self.layer, k_pre, v_pre, self.w_k, 0, self.k_cache, self.v_cache,
+                       self.index)
+        self.new_k = k_pre[:, :, N - 1:N].contiguous()
+        self.new_v = v_pre[:, :, N - 1:N].contiguous()
+        self.n_loc = wl.Hkv - wl.n_ret
+        self.ring_len = wl.window
+        if ring:
+            self.k_ring = torch.zeros((B, self.n_loc, wl.n_sink + self.ring_len, 128),
+                                      dtype=torch.int16, device="cuda")
+            self.v_ring = torch.zeros_like(self.k_ring)
+            R.ring_append(self.layer, k_pre[:, :, :wl.n_sink].contiguous(),
+                          v_pre[:, :, :wl.n_sink].contiguous(), 0, self.ring_len,
+                          self.k_ring, self.v_ring)
+            R.ring_append(self.layer, k_pre[:, :, N - self.ring_len:].contiguous(),
+                          v_pre[:, :, N - self.ring_len:].contiguous(), N - self.ring_len,
+                          self.ring_len, self.k_ring, self.v_ring)
+        del k_pre, v_pre
+        self.out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+        self.ws = torch.zeros(R.workspace_size(self.layer, R.OP_DECODE, N), dtype=torch.uint8,
+                              device="cuda")
+        self.wss = torch.zeros(R.workspace_size(self.layer, R.OP_SWA, N), dtype=torch.uint8,
+                               device="cuda")
+        self.main_s = torch.cuda.current_stream()
+        self.side_s = self.main_s if args.serial_streams else torch.cuda.Stream()
+        self.fork, self.join = torch.cuda.Event(), torch.cuda.Event()
+        torch.cuda.synchronize()
+
+    def step(self, top_p, debug=None, marks=None, hip=None):
+        import torch
+        R, wl, N = self.R, self.wl, self.wl.N
+        cur = torch.cuda.current_stream()   # the capture stream while recording a graph
+        side = cur if self.args.serial_streams else self.side_s
+        if marks:
+            hip.record(marks[0], cur.cuda_stream)
+        R.index_append(self.layer, self.new_k, self.new_v, self.w_k, N - 1, self.k_cache,
+                       self.v_cache, self.index)
+        self.fork.record(cur)
+        # the retrieval decode is issued first: its kernels queue behind the append
+        # while the host issues the local heads on the side stream
+        R.decode_sparse_attn(self.layer, self.q, self.w_q, self.k_cache, self.v_cache,
+                             self.index, N, top_p, self.out, self.ws, debug=debug)
+        side.wait_event(self.fork)
+        if marks:
+            hip.record(marks[1], side.cuda_stream)
+        if self.ring:
+            R.swa_attn_ring(self.layer, self.q, N - 1, 1, self.ring_len, self.k_ring,
+                            self.v_ring, self.out, self.wss, stream=side)
+        else:
+            R.swa_attn(self.layer, self.q, N - 1, 1, self.k_cache, self.v_cache, self.out,
+                       self.wss, stream=side)
+        if marks:
+            hip.record(marks[2], side.cuda_stream)
+        self.join.record(side)
+        cur.wait_event(self.join)
+
+    def measure(self, top_p, timer, hip, n_steps, n_dist, n_phase):
+        """Step times (K cold steps + a distribution series), phases, set sizes, bytes."""
+        import numpy as np
+        import torch
+        R, wl = self.R, self.wl
+        B, G, N = wl.B, wl.G, wl.N
+        for _ in range(self.args.warmup):
+            self.step(top_p)
+        torch.cuda.synchronize()
+        # one untimed step with the inspection outputs: set and union sizes
+        dbg_sets = R.Debug(B * wl.n_ret * G, 1, pairs=B * wl.n_ret)
+        self.step(top_p, debug=dbg_sets)
+        torch.cuda.synchronize()
+        union = dbg_sets.union_count.cpu().numpy().astype(np.int64)
+        sizes = dbg_sets.sel_count.cpu().numpy().astype(np.int64)
+        del dbg_sets
+        step_ms = timer.runs(lambda: self.step(top_p), n_steps)
+        dist_ms = timer.runs(lambda: self.step(top_p), n_dist) if n_dist > n_steps else step_ms
+        # phases: the library's six events on its launch stream, plus the append and
+        # the local heads bracketed on their streams
+        ph_ev = [hip.event() for _ in range(6)]
+        marks = [hip.event() for _ in range(3)]
+        dbg_ph = R.Debug(0, 0, events=ph_ev)
+        names = ["scan", "threshold", "select", "finish", "merge"]
+        ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
+        for _ in range(n_phase):
+            flush_caches(timer.flush)
+            self.step(top_p, debug=dbg_ph, marks=marks, hip=hip)
+            torch.cuda.synchronize()
+            for k, n in enumerate(names):
+                ph[n].append(hip.elapsed_ms(ph_ev[k], ph_ev[k + 1]))
+            ph["append"].append(hip.elapsed_ms(marks[0], ph_ev[0]))
+            ph["swa"].append(hip.elapsed_ms(marks[1], marks[2]))
+            ph["retrieval_total"].append(hip.elapsed_ms(ph_ev[0], ph_ev[5]))
+        phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
+        # algorithmic bytes of one step
+        lo = max(0, N - wl.window)
+        swa_rows = min(wl.n_sink, lo) + (N - lo)
+        b_index = B * wl.n_ret * N * 32
+        b_gather = int(union.sum()) * 512
+        b_swa = B * self.n_loc * swa_rows * 512
+        b_small = B * wl.Hq * 256 * 2 + wl.w_q.size * 2 + B * wl.Hkv * (512 + 512) + \
+            B * wl.n_ret * 32
+        step_bytes = b_index + b_gather + b_swa + b_small
+        med_ms = float(np.median(step_ms))
+        gbs = lambda b, us: round(b / (us * 1e-6) / 1e9, 1)  # noqa: E731
+        sel_us = phases_us["select"] + phases_us["finish"]
+        return {
+            "top_p": top_p,
+            "us_per_step": dist(step_ms),
+            "us_per_step_dist": dist(dist_ms),
+            "phases_us": phases_us,
+            "set_sizes": {"min": int(sizes.min()), "median": float(np.median(sizes)),
+                          "max": int(sizes.max()), "all": sizes.tolist() if sizes.size <= 32
+                          else None},
+            "union_rows": int(union.sum()),
+            "step_bytes": {"index": b_index, "gather_rows": b_gather, "swa": b_swa,
+                           "small": b_small, "total": step_bytes},
+            "achieved_GBps": gbs(step_bytes, med_ms * 1e3),
+            "hbm_frac": round(step_bytes / (med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "scan_GBps": gbs(b_index, phases_us["scan"]),
+            "select_finish_GBps": gbs(b_gather, sel_us),
+            "swa_GBps": gbs(b_swa, phases_us["swa"]),
+            "_step_ms": step_ms,
+        }
+
+    def free(self):
+        import torch
+        for a in ("k_cache", "v_cache", "index", "k_ring", "v_ring", "ws", "wss", "out"):
+            if hasattr(self, a):
+                delattr(self, a)
+        torch.cuda.empty_cache()
+
+
+def attainable_read(timer):
+    """Cold streaming reads with a plain read kernel (libreadprobe.so, built beside the
+    library): the 32 MiB of the 1M index and 1 GiB, in GB/s, median of 20, best of
+    four grid sizes.  This is what one kernel reading that many bytes reaches here,
+    launch and ramp included, timed the way the decode kernels are."""
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_long_retrieval_amd",
+                                   "libreadprobe.so"))
+    lib.read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                               ctypes.c_void_p]
+    out = torch.zeros(1 << 14, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, nbytes in (("32MiB", 32 << 20), ("1GiB", 1 << 30)):
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        best = 0.0
+        for blocks in (1024, 2048, 4096, 8192):
+            fn = lambda: lib.read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks,  # noqa
+                                        timer.stream)
+            assert fn() == 0
+            ms = timer.runs(fn, 20)
+            best = max(best, nbytes / (float(np.median(ms)) * 1e-3) / 1e9)
+        res[name] = round(best, 1)
+        del buf
+    res["kernel"] = "k_read_probe (16-byte loads, four in flight per thread), cold, HIP events"
+    return res
+
+
+def headline(args):
+    """The 1M decode step (headline), with its extras; returns the bench line fields."""
     import numpy as np
     import torch
 
@@ -162,32 +384,8 @@ def decode_leg(args):
     top_p = args.top_p if args.top_p is not None else wl.top_p[min(1, len(wl.top_p) - 1)]
     log(f"workload {wl.name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} N={wl.N} ret={wl.ret_kv_heads} "
         f"p={top_p} generated in {time.time() - t0:.1f}s")
-
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
-    layer = R.Layer(wl.B, wl.Hq, wl.Hkv, wl.N, wl.ret_kv_heads, wl.n_sink, wl.window,
-                    wl.rope_base)
+    ctx = DecodeCtx(wl, args, ring=True)
     N, B, G = wl.N, wl.B, wl.G
-    k_cache = torch.empty((B, wl.Hkv, N, 128), dtype=torch.int16, device="cuda")
-    v_cache = torch.empty_like(k_cache)
-    index = torch.empty((B, wl.n_ret, N, 16), dtype=torch.int16, device="cuda")
-    w_q, w_k, q = dev(wl.w_q), dev(wl.w_k), dev(wl.q_pre)
-    k_pre, v_pre = dev(wl.k_pre), dev(wl.v)
-    R.index_append(layer, k_pre, v_pre, w_k, 0, k_cache, v_cache, index)   # bulk prefill of caches
-    new_k = k_pre[:, :, N - 1:N].contiguous()
-    new_v = v_pre[:, :, N - 1:N].contiguous()
-    # local heads as a ring of the sinks + the window (rtp_ring_append)
-    ring_len = wl.window
-    n_loc = wl.Hkv - wl.n_ret
-    k_ring = torch.zeros((B, n_loc, wl.n_sink + ring_len, 128), dtype=torch.int16, device="cuda")
-    v_ring = torch.zeros_like(k_ring)
-    R.ring_append(layer, k_pre[:, :, :wl.n_sink].contiguous(), v_pre[:, :, :wl.n_sink].contiguous(),
-                  0, ring_len, k_ring, v_ring)
-    R.ring_append(layer, k_pre[:, :, N - ring_len:].contiguous(),
-                  v_pre[:, :, N - ring_len:].contiguous(), N - ring_len, ring_len, k_ring, v_ring)
-    del k_pre, v_pre
-    out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
-    ws = torch.zeros(R.workspace_size(layer, R.OP_DECODE, N), dtype=torch.uint8, device="cuda")
-    wss = torch.zeros(R.workspace_size(layer, R.OP_SWA, N), dtype=torch.uint8, device="cuda")
     flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
     # plain copy of known size: the reference point for the FETCH_SIZE / WRITE_SIZE counters
     calib_src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -199,202 +397,43 @@ def decode_leg(args):
     log(f"caches built on the GPU ({time.time() - t0:.1f}s)")
 
     hip = Hip()
-    main_s = torch.cuda.current_stream()
-    # local heads run beside the retrieval chain
-    side_s = main_s if args.serial_streams else torch.cuda.Stream()
-    stream = main_s.cuda_stream
-    n_ph = 6
-    ph_events = [hip.event() for _ in range(n_ph)]
-    extra = [hip.event() for _ in range(3)]
-    dbg_ph = R.Debug(0, 0, events=ph_events)
-    fork, join = torch.cuda.Event(), torch.cuda.Event()
-
-    def step(debug=None, mark=False):
-        cur = torch.cuda.current_stream()   # the capture stream while recording a graph
-        side = cur if args.serial_streams else side_s
-        if mark:
-            hip.record(extra[0], cur.cuda_stream)
-        R.index_append(layer, new_k, new_v, w_k, N - 1, k_cache, v_cache, index)
-        fork.record(cur)
-        # the retrieval decode is issued first: its kernels queue behind the append
-        # while the host issues the local heads on the side stream
-        R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws,
-                             debug=debug)
-        side.wait_event(fork)
-        if mark:
-            hip.record(extra[1], side.cuda_stream)
-        R.swa_attn(layer, q, N - 1, 1, k_cache, v_cache, out, wss, stream=side)
-        if mark:
-            hip.record(extra[2], side.cuda_stream)
-        join.record(side)
-        cur.wait_event(join)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # one untimed step with the inspection outputs: union sizes for the byte count
-    dbg_sets = R.Debug(B * wl.n_ret * G, 1, pairs=B * wl.n_ret)
-    step(debug=dbg_sets)
-    torch.cuda.synchronize()
-    union = dbg_sets.union_count.cpu().numpy().astype(np.int64)
-    set_sizes = dbg_sets.sel_count.cpu().numpy().tolist()
+    stream = ctx.main_s.cuda_stream
+    timer = Timer(hip, flush, stream)
+    m = ctx.measure(top_p, timer, hip, args.steps, max(args.dist_steps, args.steps), args.steps)
+    step_ms = m.pop("_step_ms")
+    log(f"cold step: median {m['us_per_step']['median']} us over {args.steps}; "
+        f"{m['us_per_step_dist']}")
 
     # ---- the step captured in a HIP graph (a serving loop may issue it this way)
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
-    cap.wait_stream(main_s)
+    cap.wait_stream(ctx.main_s)
     with torch.cuda.stream(cap):
-        step()
-    main_s.wait_stream(cap)
+        ctx.step(top_p)
+    ctx.main_s.wait_stream(cap)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        step()
+        ctx.step(top_p)
     torch.cuda.synchronize()
-
-    # ---- headline: K steps, Infinity Cache flushed before each, events around each
-    # step.  The flush is enqueued first, so the step's launches are queued behind it
-    # and the GPU does not wait for the host inside the timed region.
+    graph_ms = timer.runs(graph.replay, args.steps)
+    # warm: back-to-back steps without flushing (working set may sit in the Infinity Cache)
     e0, e1 = hip.event(), hip.event()
-
-    def timed(run, cold=True):
-        out_ms = []
-        for _ in range(args.steps):
-            if cold:
-                flush_caches(flush)
-            hip.record(e0, stream)
-            run()
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            out_ms.append(hip.elapsed_ms(e0, e1))
-        return out_ms
-
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    step_ms = timed(step)
-    wall = time.perf_counter() - wall0
-    graph_ms = timed(graph.replay)
-    ms = float(np.mean(step_ms))
-    log(f"cold step: mean {ms * 1e3:.1f} us, median {np.median(step_ms) * 1e3:.1f} us; "
-        f"as a graph replay {np.mean(graph_ms) * 1e3:.1f} us")
-
-    # ---- warm: K back-to-back steps without flushing (working set may sit in the
-    # Infinity Cache)
     torch.cuda.synchronize()
     hip.record(e0, stream)
     for _ in range(args.steps):
-        step()
+        ctx.step(top_p)
     hip.record(e1, stream)
     torch.cuda.synchronize()
     warm_ms = hip.elapsed_ms(e0, e1) / args.steps
 
-    # ---- phases: K more cold steps with the library's phase events
-    names = ["scan", "threshold", "select", "finish", "merge"]
-    ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
-    for i in range(args.steps):
-        flush_caches(flush)
-        step(debug=dbg_ph, mark=True)
-        torch.cuda.synchronize()
-        for k, n in enumerate(names):
-            ph[n].append(hip.elapsed_ms(ph_events[k], ph_events[k + 1]))
-        ph["append"].append(hip.elapsed_ms(extra[0], ph_events[0]))
-        ph["swa"].append(hip.elapsed_ms(extra[1], extra[2]))
-        ph["retrieval_total"].append(hip.elapsed_ms(ph_events[0], ph_events[5]))
-    phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
-
-    # ---- the fixed-budget decode (the pages' ablation baseline) on the same inputs
-    topk_us = {}
-    for kb in (4096, 16384):
-        t_ms = []
-        for i in range(max(5, args.steps // 4)):
-            flush_caches(flush)
-            hip.record(e0, stream)
-            R.decode_topk(layer, q, w_q, k_cache, v_cache, index, N, kb, out, ws)
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            t_ms.append(hip.elapsed_ms(e0, e1))
-        topk_us[f"top{kb}_retrieval_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
-    t_ms = []
-    for i in range(max(5, args.steps // 4)):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        R.decode_sparse_attn(layer, q, w_q, k_cache, v_cache, index, N, top_p, out, ws)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        t_ms.append(hip.elapsed_ms(e0, e1))
-    topk_us["top_p_retrieval_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
-
-    # ---- local heads from the ring versus the full cache (same kernel, same rows)
-    ring = {}
-    for name, kk, vv, fn in (("full_cache", k_cache, v_cache, None),
-                             ("ring", k_ring, v_ring, ring_len)):
-        t_ms = []
-        for i in range(max(5, args.steps // 4)):
-            flush_caches(flush)
-            hip.record(e0, stream)
-            if fn is None:
-                R.swa_attn(layer, q, N - 1, 1, kk, vv, out, wss)
-            else:
-                R.swa_attn_ring(layer, q, N - 1, 1, fn, kk, vv, out, wss)
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            t_ms.append(hip.elapsed_ms(e0, e1))
-        ring[f"swa_{name}_us"] = round(float(np.mean(t_ms)) * 1e3, 2)
-    ring["local_kv_bytes_full_cache"] = B * n_loc * N * 512
-    ring["local_kv_bytes_ring"] = B * n_loc * (wl.n_sink + ring_len) * 512
-
-    # ---- the V2 cluster index (K = 128 clusters, three updates) and decode through it
-    K_CL, IT_CL = 128, 3
-    seeds = np.stack([np.random.default_rng(wl.seed + i).choice(N, K_CL, replace=False)
-                      for i in range(B * wl.n_ret)]).astype(np.int32)
-    init = torch.from_numpy(seeds).cuda()
-    cen = torch.empty((B * wl.n_ret, K_CL, 16), dtype=torch.float32, device="cuda")
-    mem = torch.empty((B * wl.n_ret, N), dtype=torch.int32, device="cuda")
-    off = torch.empty((B * wl.n_ret, K_CL + 1), dtype=torch.int32, device="cuda")
-    wsb = torch.zeros(R.workspace_size(layer, R.OP_CLUSTER_BUILD, N, Tq=K_CL), dtype=torch.uint8,
-                      device="cuda")
-    wsc = torch.zeros(R.workspace_size(layer, R.OP_CLUSTER_DECODE, N, Tq=K_CL),
-                      dtype=torch.uint8, device="cuda")
-    build_ms = []
-    for i in range(3):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        R.cluster_build(layer, index, N, K_CL, IT_CL, init, cen, mem, off, wsb)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        build_ms.append(hip.elapsed_ms(e0, e1))
-    dbg = R.Debug(B * wl.n_ret * G, N)
-    R.decode_cluster_attn(layer, q, w_q, k_cache, v_cache, cen, mem, off, K_CL, N, N, top_p,
-                          out, wsc, debug=dbg)
-    torch.cuda.synchronize()
-    cl_sizes = [int(c) for c in dbg.sel_count.cpu().numpy()]
-    del dbg
-    t_ms = []
-    for i in range(max(5, args.steps // 4)):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        R.decode_cluster_attn(layer, q, w_q, k_cache, v_cache, cen, mem, off, K_CL, N, N, top_p,
-                              out, wsc)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        t_ms.append(hip.elapsed_ms(e0, e1))
-    cluster = {"clusters": K_CL, "updates": IT_CL, "build_ms": round(float(np.mean(build_ms)), 3),
-               "decode_retrieval_us": round(float(np.mean(t_ms)) * 1e3, 2),
-               "top_p_retrieval_us": topk_us["top_p_retrieval_us"], "set_sizes": cl_sizes}
-    del cen, mem, off, wsb, wsc, init
-
-    # ---- algorithmic bytes of one step
-    lo = max(0, N - 1 - wl.window + 1)
-    swa_rows = min(wl.n_sink, lo) + (N - 1 - lo + 1)
-    bytes_index = B * wl.n_ret * N * 32
-    bytes_gather = int(union.sum()) * 512
-    bytes_swa = B * n_loc * swa_rows * 512
-    bytes_small = B * wl.Hq * 256 * 2 + wl.w_q.size * 2 + B * wl.Hkv * (512 + 512) + \
-        B * wl.n_ret * 32
-    step_bytes = bytes_index + bytes_gather + bytes_swa + bytes_small
-    gbs = step_bytes / (ms * 1e-3) / 1e9
-    score_us = phases_us["scan"]
-    ach = bytes_index / (score_us * 1e-6) / 1e9
-
+    extras = {}
+    if not args.no_extras:
+        extras = decode_extras(ctx, top_p, timer, args)
+    reads = attainable_read(timer)
+    ms = float(np.median(step_ms))
+    ph = m["phases_us"]
+    b_index = m["step_bytes"]["index"]
+    ach = b_index / (ph["scan"] * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": round(ms * 1e3, 2),
@@ -412,39 +451,132 @@ def decode_leg(args):
                    "kv_heads": wl.Hkv, "retrieval_kv_heads": wl.ret_kv_heads,
                    "window": wl.window, "sinks": wl.n_sink, "top_p": top_p,
                    "parallelism": "single GPU"},
-        "achieved_GBps": round(gbs, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "value_stat": "median of the K timed cold steps",
+        "us_per_step": m["us_per_step"],
+        "us_per_step_dist": m["us_per_step_dist"],
+        "achieved_GBps": m["achieved_GBps"],
+        "hbm_frac": m["hbm_frac"],
+        "attainable_read_GBps": reads,
+        "hbm_frac_of_attainable": round(m["achieved_GBps"] / reads["1GiB"], 4),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
-        "median_us_per_step": round(float(np.median(step_ms)) * 1e3, 2),
-        "graph_us_per_step": round(float(np.mean(graph_ms)) * 1e3, 2),
+        "graph_us_per_step": dist(graph_ms),
         "step_issue": "launched call by call (append, retrieval decode, local-head SWA on "
                       "a second stream); graph_us_per_step: the same step as one HIP "
                       "graph replay",
-        "wall_s_timed": round(wall, 3),
-        "set_sizes": set_sizes,
-        "step_bytes": {"index": bytes_index, "gather_rows": bytes_gather, "swa": bytes_swa,
-                       "small": bytes_small, "union_rows": int(union.sum())},
-        "phases_us": phases_us,
-        "fixed_budget": topk_us,
-        "local_ring": ring,
-        "cluster_index": cluster,
+        "set_sizes": m["set_sizes"],
+        "union_rows": m["union_rows"],
+        "step_bytes": m["step_bytes"],
+        "phases_us": ph,
+        "phase_GBps": {"scan": m["scan_GBps"], "select_finish": m["select_finish_GBps"],
+                       "swa": m["swa_GBps"]},
         "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "frac_of_attainable_32MiB": round(ach / reads["32MiB"], 4),
                      "traffic": measured_traffic(wl.name),
-                     "algorithmic_bytes": bytes_index},
+                     "algorithmic_bytes": b_index},
     }
-
+    res.update(extras)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, top_p, args.cpu_seconds)
-    del k_cache, v_cache, index, flush, ws, wss, k_ring, v_ring
+    ctx.free()
+    del flush
     torch.cuda.empty_cache()
     return res
 
 
-def prefill_leg(args):
-    """Chunked prefill at 256K: one step = append of the 4096-row chunk, retrieval
-    heads (per-row top-p + gather attention), local heads (causal window attention)."""
+def decode_extras(ctx, top_p, timer, args):
+    """Fixed budgets, the ring cache against the full cache, the cluster index."""
+    import numpy as np
+    import torch
+    R, wl = ctx.R, ctx.wl
+    N, B, G = wl.N, wl.B, wl.G
+    n = max(5, args.steps // 4)
+    med = lambda ms: round(float(np.median(ms)) * 1e3, 2)  # noqa: E731
+    topk = {}
+    for kb in (4096, 16384):
+        topk[f"top{kb}_retrieval_us"] = med(timer.runs(
+            lambda: R.decode_topk(ctx.layer, ctx.q, ctx.w_q, ctx.k_cache, ctx.v_cache,
+                                  ctx.index, N, kb, ctx.out, ctx.ws), n))
+    topk["top_p_retrieval_us"] = med(timer.runs(
+        lambda: R.decode_sparse_attn(ctx.layer, ctx.q, ctx.w_q, ctx.k_cache, ctx.v_cache,
+                                     ctx.index, N, top_p, ctx.out, ctx.ws), n))
+    topk["top_p_noalloc_retrieval_us"] = med(timer.runs(
+        lambda: R.decode_sparse_attn_noalloc(ctx.layer, ctx.q, ctx.w_q, ctx.k_cache,
+                                             ctx.v_cache, ctx.index, N, top_p, ctx.out), n))
+    ring = {
+        "swa_full_cache_us": med(timer.runs(
+            lambda: R.swa_attn(ctx.layer, ctx.q, N - 1, 1, ctx.k_cache, ctx.v_cache, ctx.out,
+                               ctx.wss), n)),
+        "swa_ring_us": med(timer.runs(
+            lambda: R.swa_attn_ring(ctx.layer, ctx.q, N - 1, 1, ctx.ring_len, ctx.k_ring,
+                                    ctx.v_ring, ctx.out, ctx.wss), n)),
+        "local_kv_bytes_full_cache": B * ctx.n_loc * N * 512,
+        "local_kv_bytes_ring": B * ctx.n_loc * (wl.n_sink + ctx.ring_len) * 512,
+    }
+    K_CL, IT_CL = 128, 3
+    seeds = np.stack([np.random.default_rng(wl.seed + i).choice(N, K_CL, replace=False)
+                      for i in range(B * wl.n_ret)]).astype(np.int32)
+    init = torch.from_numpy(seeds).cuda()
+    cen = torch.empty((B * wl.n_ret, K_CL, 16), dtype=torch.float32, device="cuda")
+    mem = torch.empty((B * wl.n_ret, N), dtype=torch.int32, device="cuda")
+    off = torch.empty((B * wl.n_ret, K_CL + 1), dtype=torch.int32, device="cuda")
+    wsb = torch.zeros(R.workspace_size(ctx.layer, R.OP_CLUSTER_BUILD, N, Tq=K_CL),
+                      dtype=torch.uint8, device="cuda")
+    wsc = torch.zeros(R.workspace_size(ctx.layer, R.OP_CLUSTER_DECODE, N, Tq=K_CL),
+                      dtype=torch.uint8, device="cuda")
+    build_ms = timer.runs(lambda: R.cluster_build(ctx.layer, ctx.index, N, K_CL, IT_CL, init,
+                                                  cen, mem, off, wsb), 3)
+    dbg = R.Debug(B * wl.n_ret * G, N)
+    R.decode_cluster_attn(ctx.layer, ctx.q, ctx.w_q, ctx.k_cache, ctx.v_cache, cen, mem, off,
+                          K_CL, N, N, top_p, ctx.out, wsc, debug=dbg)
+    torch.cuda.synchronize()
+    cl_sizes = [int(c) for c in dbg.sel_count.cpu().numpy()]
+    del dbg
+    cl_us = med(timer.runs(
+        lambda: R.decode_cluster_attn(ctx.layer, ctx.q, ctx.w_q, ctx.k_cache, ctx.v_cache, cen,
+                                      mem, off, K_CL, N, N, top_p, ctx.out, wsc), n))
+    cluster = {"clusters": K_CL, "updates": IT_CL,
+               "build_ms": round(float(np.median(build_ms)), 3),
+               "decode_retrieval_us": cl_us, "top_p_retrieval_us": topk["top_p_retrieval_us"],
+               "set_sizes": cl_sizes}
+    return {"fixed_budget": topk, "local_ring": ring, "cluster_index": cluster}
+
+
+def other_config(args, config: int):
+    """The 64K (B=8) or 128K (B=4, three p) decode: step distribution, phases, sizes."""
+    import torch
+
+    import workloads as W
+    t0 = time.time()
+    wl = W.make(config)
+    log(f"workload {wl.name}: B={wl.B} N={wl.N} p={wl.top_p} generated in "
+        f"{time.time() - t0:.1f}s")
+    ctx = DecodeCtx(wl, args, ring=False)
+    flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
+    hip = Hip()
+    timer = Timer(hip, flush, ctx.main_s.cuda_stream)
+    out = {"batch": wl.B, "context": wl.N, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+           "retrieval_kv_heads": wl.ret_kv_heads, "window": wl.window, "runs": {}}
+    n_dist = max(100, args.steps)
+    for p in wl.top_p:
+        m = ctx.measure(p, timer, hip, args.steps, n_dist, max(10, args.steps // 2))
+        m.pop("_step_ms")
+        out["runs"][f"p{p}"] = m
+        log(f"{wl.name} p={p}: median {m['us_per_step']['median']} us, "
+            f"{m['achieved_GBps']} GB/s, sets {m['set_sizes']['min']}..{m['set_sizes']['max']}")
+    ctx.free()
+    del flush
+    torch.cuda.empty_cache()
+    return wl.name, out
+
+
+# ------------------------------------------------------------------ prefill
+
+def prefill_leg(args, config: int):
+    """Chunked prefill: one step = append of the 4096-row chunk, the local heads (causal
+    window attention on MFMA tiles), the retrieval heads (per-row top-p + gather
+    attention), all on one stream.  prefill tok/s = 4096 / step time."""
     import numpy as np
     import torch
 
@@ -452,12 +584,12 @@ def prefill_leg(args):
     import workloads as W
 
     t0 = time.time()
-    wl = W.make(5)
+    wl = W.make(config)
     top_p = wl.top_p[0]
     B, N, Tq, q0 = wl.B, wl.N, wl.Tq, wl.q_start
     log(f"prefill workload {wl.name}: N={N} Tq={Tq} ret={wl.ret_kv_heads} generated in "
         f"{time.time() - t0:.1f}s")
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa: E731
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()  # noqa
     layer = R.Layer(B, wl.Hq, wl.Hkv, N, wl.ret_kv_heads, wl.n_sink, wl.window, wl.rope_base)
     k_cache = torch.empty((B, wl.Hkv, N, 128), dtype=torch.int16, device="cuda")
     v_cache = torch.empty_like(k_cache)
@@ -470,21 +602,20 @@ def prefill_leg(args):
     cv = v_pre[:, :, q0:].contiguous()
     del k_pre, v_pre
     out = torch.zeros((B, wl.Hq, Tq, 128), dtype=torch.int16, device="cuda")
-    ws = torch.empty(R.workspace_size(layer, R.OP_PREFILL, N, Tq=Tq), dtype=torch.uint8,
-                     device="cuda")
+    ws_bytes = R.workspace_size(layer, R.OP_PREFILL, N, Tq=Tq)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     flush = torch.ones((512 << 20) // 4, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
 
     hip = Hip()
-    main_s = torch.cuda.current_stream()
-    stream = main_s.cuda_stream
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = Timer(hip, flush, stream)
     ph = [hip.event() for _ in range(5)]
     ex = [hip.event() for _ in range(4)]
     dbg_ph = R.Debug(0, 0, events=ph)
 
     # One stream: the index kernel keeps two blocks on every CU for its whole run, so
-    # local-head blocks beside it only delay some of its blocks (measured: 15.5 ms per
-    # chunk with the local heads on a second stream, 14.9 ms one after the other).
+    # local-head blocks beside it only delay some of its blocks.
     def step(mark=False):
         if mark:
             hip.record(ex[0], stream)
@@ -502,18 +633,11 @@ def prefill_leg(args):
     for _ in range(2):
         step()
     torch.cuda.synchronize()
-    e0, e1 = hip.event(), hip.event()
-    step_ms = []
-    for i in range(args.prefill_steps):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        step()
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        step_ms.append(hip.elapsed_ms(e0, e1))
+    n_steps = args.prefill_steps if config == 5 else max(10, args.prefill_steps // 2)
+    step_ms = timer.runs(step, n_steps)
     names = ["qprep", "index", "resolve", "attend"]
     phs = {n: [] for n in names + ["append", "swa_local", "retrieval_total", "step"]}
-    for i in range(max(3, args.prefill_steps // 2)):
+    for _ in range(max(5, n_steps // 4)):
         flush_caches(flush)
         step(mark=True)
         torch.cuda.synchronize()
@@ -524,38 +648,32 @@ def prefill_leg(args):
         phs["retrieval_total"].append(hip.elapsed_ms(ph[0], ph[4]))
         phs["step"].append(hip.elapsed_ms(ex[0], ex[3]))
     phases_ms = {k: round(float(np.median(v)), 4) for k, v in phs.items()}
-    ms = float(np.mean(step_ms))
+    ms = float(np.median(step_ms))
     # the dense alternative for the retrieval heads: p = 1 selects every key, which the
     # library runs as causal flash attention on the matrix cores
-    dense_ms = []
-    for i in range(max(3, args.prefill_steps // 2)):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, 1.0, out, ws)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        dense_ms.append(hip.elapsed_ms(e0, e1))
+    dense_ms = timer.runs(lambda: R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index,
+                                                  1.0, out, ws), max(5, n_steps // 4))
     dense = float(np.median(dense_ms))
-    # the local heads alone, without the append before them
-    swa_ms = []
-    for i in range(max(3, args.prefill_steps // 2)):
-        flush_caches(flush)
-        hip.record(e0, stream)
-        R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        swa_ms.append(hip.elapsed_ms(e0, e1))
+    swa_ms = timer.runs(lambda: R.swa_attn(layer, q, q0, Tq, k_cache, v_cache, out),
+                        max(5, n_steps // 4))
     phases_ms["swa_local_alone"] = round(float(np.median(swa_ms)), 4)
-    # selected rows of the chunk (set sizes from one call with the debug counts; not timed)
+    # selected rows of the chunk (set sizes and the union per KV head from one call with
+    # the inspection outputs; not timed)
     n_vec = wl.B * wl.n_ret * wl.G * Tq
-    dbg_cnt = R.Debug(n_vec, 1)
+    dbg_cnt = R.Debug(n_vec, 1, pairs=B * wl.n_ret)
     R.prefill_chunk(layer, q, q0, w_q, k_cache, v_cache, index, top_p, out, ws, debug=dbg_cnt)
     torch.cuda.synchronize()
     sel = dbg_cnt.sel_count.to(torch.int64)
     sel_rows, sel_max = int(sel.sum().item()), int(sel.max().item())
+    sel_med = float(sel.float().median().item())
+    union_rows = int(dbg_cnt.union_count.to(torch.int64).sum().item())
     del dbg_cnt, sel
-    attend_bytes = sel_rows * 2 * 128 * 2  # K and V rows, bf16
-    attend_gbs = attend_bytes / (phases_ms["attend"] * 1e-3) / 1e9
+    # attend: algorithmic bytes are the distinct selected K/V rows (512 B each) of each
+    # retrieval KV head over the chunk; every further read of a row is a re-read
+    att_s = phases_ms["attend"] * 1e-3
+    attend_bytes = union_rows * 512
+    reread_bytes = sel_rows * 512
+    attend_flops = 4.0 * 128 * sel_rows          # QK and PV, 2 flops per multiply-add
     ret_flops = 4.0 * 128 * sum(q0 + t + 1 for t in range(Tq)) * wl.n_ret * wl.G * B
     # local heads: causal window attention, 4 D flops (QK + PV) per (row, key) pair
     n_loc_q = (wl.Hkv - wl.n_ret) * wl.G * B
@@ -569,7 +687,8 @@ def prefill_leg(args):
     res = {
         "workload": wl.name, "context": N, "chunk": Tq, "top_p": top_p,
         "value": round(Tq * B / (ms * 1e-3), 1), "unit": "tok/s",
-        "ms_per_chunk": round(ms, 4), "steps": args.prefill_steps,
+        "ms_per_chunk": dist(step_ms, 1.0, 4), "steps": n_steps,
+        "workspace_bytes": ws_bytes,
         "phases_ms": phases_ms,
         "swa_mfma": {"kernel": "k_swa_prefill (causal window 8192 + 4 sinks, bf16 MFMA)",
                      "algorithmic_tflop": round(swa_flops / 1e12, 2),
@@ -582,24 +701,41 @@ def prefill_leg(args):
                     "scores_per_s": round(ret_pairs / (phases_ms["index"] * 1e-3), 1)},
         "attend": {"kernel": "k_pf_attend + k_pf_merge (gathered K/V rows of every selected set)",
                    "selected_rows": sel_rows, "mean_rows": round(sel_rows / n_vec, 1),
-                   "max_rows": sel_max, "algorithmic_gb": round(attend_bytes / 1e9, 2),
-                   "achieved": round(attend_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(attend_gbs / HBM_PEAK_GBS, 4),
-                   "note": "achieved counts each selected row once per query vector; rows that "
-                           "neighbouring work items share come from L2 and the Infinity Cache, "
-                           "so it can exceed the HBM peak"},
+                   "median_rows": sel_med, "max_rows": sel_max,
+                   "distinct_rows": union_rows,
+                   "algorithmic_bytes": attend_bytes,
+                   "achieved": round(attend_bytes / att_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(attend_bytes / att_s / 1e9 / HBM_PEAK_GBS, 4),
+                   "row_reads_bytes": reread_bytes,
+                   "row_reads_GBps": round(reread_bytes / att_s / 1e9, 1),
+                   "flops": attend_flops,
+                   "tflops": round(attend_flops / att_s / 1e12, 2),
+                   "fp32_valu_frac": round(attend_flops / att_s / 1e12 / FP32_VALU_PEAK_TFLOPS, 4),
+                   "note": "algorithmic bytes count each distinct selected row of a KV head "
+                           "once; row_reads counts every (row, query vector) read, most of "
+                           "which hit L2 and the Infinity Cache"},
         "dense_retrieval": {"kernel": "k_swa_prefill with the window = context (p = 1)",
                             "ms": round(dense, 4),
                             "tflops": round(ret_flops / (dense * 1e-3) / 1e12, 1),
+                            "mfma_frac": round(ret_flops / (dense * 1e-3) / 1e12 /
+                                               MFMA_BF16_PEAK_TFLOPS, 4),
                             "sparse_retrieval_ms": phases_ms["retrieval_total"],
                             "dense_over_sparse": round(dense / phases_ms["retrieval_total"], 3)},
     }
-    log(f"prefill: {ms:.3f} ms/chunk -> {res['value']:.0f} tok/s; phases {phases_ms}")
+    log(f"prefill {wl.name}: {ms:.3f} ms/chunk -> {res['value']:.0f} tok/s; phases {phases_ms}")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = prefill_cpu_baseline(wl, top_p)
+        res["cpu_baseline"] = prefill_cpu_baseline(wl, top_p, n_rows=6 if config == 5 else 2)
     del k_cache, v_cache, index, flush, ws
     torch.cuda.empty_cache()
     return res
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
 
 
 def prefill_cpu_baseline(wl, top_p: float, n_rows: int = 6):
@@ -607,27 +743,22 @@ def prefill_cpu_baseline(wl, top_p: float, n_rows: int = 6):
     import numpy as np
 
     from oracle import rtp_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     t0 = time.time()
-    rows_loc = np.union1d(np.arange(max(0, wl.q_start - wl.window), wl.N),
-                          np.arange(min(wl.n_sink, wl.N)))
-    kc, vc, idx = O.caches_for(wl, rows_needed={kv: rows_loc for kv in range(wl.Hkv)
+    rows = np.linspace(0, wl.Tq - 1, n_rows).astype(int)
+    pos = wl.q_start + rows
+    win = np.unique(np.concatenate([np.arange(max(0, p - wl.window + 1), p + 1) for p in pos] +
+                                   [np.arange(min(wl.n_sink, wl.N))]))
+    kc, vc, idx = O.caches_for(wl, rows_needed={kv: win for kv in range(wl.Hkv)
                                                  if kv not in wl.ret_kv_heads})
     log(f"oracle prefill caches built in {time.time() - t0:.1f}s")
-    rows = np.linspace(0, wl.Tq - 1, n_rows).astype(int)
     t = time.perf_counter()
     for r in rows:
         for h in range(wl.Hq):
             O.prefill_row(wl, kc, vc, idx, 0, h, int(r), top_p)
     spent = time.perf_counter() - t
     per_row = spent / len(rows)
-    tok_s = 1.0 / per_row
-    log(f"oracle prefill: {per_row * 1e3:.1f} ms per row (all heads)")
-    return {"value": round(tok_s, 3), "unit": "tok/s", "cores": int(threads),
+    log(f"oracle prefill {wl.name}: {per_row * 1e3:.1f} ms per row (all heads)")
+    return {"value": round(1.0 / per_row, 3), "unit": "tok/s", "cores": int(_threads()),
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(rows)} chunk rows spread over the chunk, all {wl.Hq} q-heads each "
                       f"(append excluded), extrapolated to the {wl.Tq}-row chunk"}
@@ -638,11 +769,6 @@ def cpu_baseline(wl, top_p: float, budget_s: float):
     import numpy as np
 
     from oracle import rtp_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
     t0 = time.time()
     N = wl.N
     lo = max(0, N - wl.window)
@@ -661,7 +787,7 @@ def cpu_baseline(wl, top_p: float, budget_s: float):
         n += 1
     us = spent / n * 1e6
     log(f"oracle: {n} steps, {us / 1e3:.1f} ms/step")
-    return {"value": round(us, 1), "unit": "us/step", "cores": int(threads),
+    return {"value": round(us, 1), "unit": "us/step", "cores": int(_threads()),
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{n} whole decode steps (append of the newest token + all {wl.Hq} "
                       f"heads) of the same workload; oracle caches built beforehand"}
