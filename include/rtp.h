@@ -54,6 +54,10 @@ extern "C" {
 
 typedef uint16_t rtp_bf16; /* bf16 bit pattern */
 
+/* Byte offset, in a decode workspace, of the word a decode sets when one of its
+ * bounded waits gave up (see rtp_decode_sparse_attn); zero otherwise. */
+#define RTP_DECODE_ERROR_OFFSET 65532
+
 typedef enum {
   RTP_OK = 0,
   RTP_ERR_NULL = 1,        /* a required pointer is NULL */
@@ -86,12 +90,14 @@ typedef struct {
  * entry in unspecified order, at most sel_cap of them; sel_count holds the true
  * set size even when it exceeds sel_cap; tau holds the threshold score (-inf
  * when top_p >= 1 keeps every key); union_count [B][n_ret] holds, per retrieval
- * KV head, the number of distinct K/V rows read (the union of the G sets).
+ * KV head, the number of distinct K/V rows read (decode: the union of the G sets;
+ * prefill: the union of the sets of every row and q-head of the chunk).
  * phase_events, when non-NULL, are n_phase_events caller-created hipEvent_t
  * handles; the decode records event 0 before its first kernel and event k after
  * kernel k of: 1 index scan + mass histogram, 2 threshold bin, 3 select +
  * attention of the keys above the boundary bin, 4 exact threshold + boundary
- * keys, 5 merge of the partial states (n_phase_events must be >= 6). */
+ * keys, 5 merge of the partial states (n_phase_events must be >= 6).  When the
+ * first three run as one fused launch, events 1, 2 and 3 are recorded after it. */
 typedef struct {
   int32_t* sel_idx;     /* [entries][sel_cap] device */
   int32_t* sel_count;   /* [entries] device */
@@ -153,6 +159,13 @@ rtp_status rtp_index_append(const rtp_layer_desc* desc, const rtp_bf16* k_pre,
  * Scores and masses are fp32 per token with fp64 reductions; the attention
  * accumulates in fp32 and rounds the output to bf16.  The selection is
  * deterministic (integer-exact mass sums).
+ * When every index block of the call fits the GPU at once (batch * n_ret *
+ * ceil(seq_len / 2048) blocks; 512 fit an MI355X), scan, threshold and select run
+ * as one launch whose blocks wait for the last block of their (batch, KV head)
+ * pair.  Such a wait is bounded: if it gives up (the GPU stayed full of other work
+ * for about a quarter second), the call's outputs are void and the 32-bit word at
+ * byte offset RTP_DECODE_ERROR_OFFSET of the workspace is non-zero; the counter
+ * region must then be zero-filled again before the workspace is reused.
  *
  *   q_pre    [B][Hq][D] bf16 device; only retrieval q-heads are read
  *   w_q      [n_ret*G][D][r] bf16 device: retrieval q-heads in head order

@@ -346,8 +346,15 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
-// The scratch address on the current device (set up on the first call there).
-rtp_status noalloc_scratch(void** out) {
+// Zero n words (the scratch's counter region, once per device before its first use).
+__global__ void k_zero_words(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The scratch address on the current device (set up on the first call there: the
+// counter region is cleared on the call's stream, ahead of its kernels).
+rtp_status noalloc_scratch(void** out, hipStream_t stream) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(RTP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -358,6 +365,10 @@ rtp_status noalloc_scratch(void** out) {
     e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
     if (e != hipSuccess || !ptr)
       return fail(RTP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    constexpr int n = (int)(rtp::kCounterBytes / sizeof(unsigned));
+    hipLaunchKernelGGL(k_zero_words, dim3((n + 255) / 256), dim3(256), 0, stream, (unsigned*)ptr, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(RTP_ERR_HIP, "scratch clear: %s", hipGetErrorString(e));
     g_scratch_ptr[dev] = ptr;
   }
   *out = g_scratch_ptr[dev];
@@ -410,7 +421,7 @@ rtp_status rtp_decode_sparse_attn_noalloc(const rtp_layer_desc* desc, const rtp_
                 "(use rtp_decode_sparse_attn with a workspace)",
                 need, kNoAllocScratchBytes);
   void* ws = nullptr;
-  RTP_TRY(noalloc_scratch(&ws));
+  RTP_TRY(noalloc_scratch(&ws, (hipStream_t)stream));
   return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, top_p, 0, idx_scale,
                      attn_scale, out, dbg, ws, kNoAllocScratchBytes, stream);
 }
@@ -470,11 +481,13 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
   p.attn_scale = attn_scale;
   rope_theta(desc->rope_base, p.theta);
   p.V = desc->batch * desc->n_ret * G * Tq;
+  p.n_keys = q_start + Tq;
   if (dbg) {
     p.dbg_idx = dbg->sel_idx;
     p.dbg_cnt = dbg->sel_count;
     p.dbg_tau = dbg->tau;
     p.dbg_cap = dbg->sel_cap;
+    p.dbg_union = dbg->union_count;
     p.events = dbg->phase_events ? (hipEvent_t*)dbg->phase_events : nullptr;
   }
 
@@ -506,7 +519,7 @@ rtp_status rtp_prefill_chunk(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
     hipError_t e = rtp::launch_swa_prefill(d, (hipStream_t)stream);
     if (p.events)
       for (int k = 1; k < 5; ++k) hipEventRecord(p.events[k], (hipStream_t)stream);
-    if (e == hipSuccess && (p.dbg_idx || p.dbg_cnt || p.dbg_tau))
+    if (e == hipSuccess && (p.dbg_idx || p.dbg_cnt || p.dbg_tau || p.dbg_union))
       e = rtp::launch_prefill_debug_all(p, (hipStream_t)stream);
     if (e != hipSuccess) return fail(RTP_ERR_HIP, "dense prefill launch: %s", hipGetErrorString(e));
     return RTP_OK;

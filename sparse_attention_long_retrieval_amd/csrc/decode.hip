@@ -31,12 +31,16 @@
 //                a share of the selected candidates.
 //   k_merge      combine all partial softmax states into the bf16 output.
 // Every sum and row order is fixed, so results are bit-identical across runs.
+#include <cstdlib>
+#include <mutex>
+
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
 
 namespace rtp {
 
+constexpr int kMaxDevicesDecode = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int G>
@@ -51,7 +55,9 @@ constexpr int kFinishThreads = 256;
 constexpr int kKeyCap = 16384;        // candidate keys resolved from LDS
 constexpr int kTokCap = 8192;         // candidates whose tokens are also kept in LDS
 constexpr int kMaxBlocksLds = 2048;   // pass-B blocks whose candidate offsets fit in LDS
-constexpr int kFinishSplit = 32;      // finish blocks per (pair, q-head)
+constexpr int kFinishSplit = 32;      // finish blocks per (pair, q-head), at most
+constexpr int kMinFinishSplit = 4;    // ... and at least
+constexpr int kFinishBlocks = 256;    // total finish blocks aimed at: one per CU (LDS)
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
 
@@ -239,6 +245,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   static_assert(NT >= G * kD / 2, "one thread per rotated pair");
   const bool rot = blk == 0 && tid < G * kD / 2;
   const double th = rot ? p.theta[tid % (kD / 2)] : 0.0;
+  // The index tile is requested right behind the projection: a wave's loads complete
+  // in issue order, so the projection is in registers (and qi computed) while the
+  // tile is still in flight, and the tile's requests do not wait for a barrier.
+  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+  const int tok0 = blk * kPassTokens;
+  uint4 a[S::TPW][S::CH];
+  load_score_tiles<G>(idx, tok0, p.N, a);
 #pragma unroll
   for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
   if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
@@ -246,24 +259,29 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
   for (int e = tid; e < kCoarseGrids * G * kNB; e += NT) (&binc[0][0][0])[e] = 0u;
   if (tid < kNB) bscale[tid] = expf((float)tid * kDelta) * kFxBin;
   __syncthreads();
-  // The index tile is requested once the projection is in LDS (the barrier keeps
-  // the loads here): a wave's loads complete in issue order, so qi below runs while
-  // the tile is in flight instead of waiting behind it.
-  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
-  const int tok0 = blk * kPassTokens;
-  uint4 a[S::TPW][S::CH];
-  load_score_tiles<G>(idx, tok0, p.N, a);
   {
     // qi = q . W_q, four threads per output, 32 terms each.  The bf16 products are
     // exact in fp64 and so is their fp64 sum (the terms span far fewer than the 37
     // bits of headroom), so qi is the fp32 rounding of the exact dot product.
+    // The operands are read from LDS eight at a time (one wait each), then summed.
     double acc = 0.0;
     const int hh = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
     if (hh < G) {
-      const uint16_t* wq = wq_s + hh * kD * kR;
-      const uint16_t* qq = q_s + hh * kD;
-      for (int d = 32 * part; d < 32 * part + 32; ++d)
-        acc = __fma_rn((double)bf16_to_f32(qq[d]), (double)bf16_to_f32(wq[d * kR + c]), acc);
+      const uint16_t* wq = wq_s + hh * kD * kR + 32 * part * kR + c;
+      const uint4* qq = (const uint4*)(q_s + hh * kD + 32 * part);
+#pragma unroll
+      for (int d0 = 0; d0 < 32; d0 += 8) {
+        const uint4 qw = qq[d0 / 8];
+        const uint32_t qp[4] = {qw.x, qw.y, qw.z, qw.w};
+        float wv[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) wv[d] = bf16_to_f32(wq[(d0 + d) * kR]);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const float qv = (d & 1) ? bf16_hi(qp[d >> 1]) : bf16_lo(qp[d >> 1]);
+          acc = __fma_rn((double)qv, (double)wv[d], acc);
+        }
+      }
     }
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
@@ -769,6 +787,560 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 6) void k_select(DecPlan p) {
   }
 }
 
+// ------------------------------------------------------------------ fused pass
+
+// Polls of a pair's threshold flag before a block gives up (about a quarter second).
+constexpr unsigned kSpinLimit = 1u << 18;
+
+// Scan, threshold and select in one launch, for top-p when every block of the grid
+// can run at once (the host checks the GPU's room for the grid).  Each block scores
+// its 2048 tokens, keeps the scores in registers and writes its summary (max, mass,
+// bins) through to memory.  The last block of each group of kGroupBlocks merges the
+// group's summaries; the last group of the pair merges the groups, finds each
+// q-head's boundary bin as the threshold kernel does, and raises the pair's flag.
+// The other blocks wait for the flag (bounded: a wait that gives up sets p.err),
+// then classify their registered scores and attend their definite rows as the
+// select kernel does, without reading the index a second time.
+template <int G>
+__global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
+  using S = ScoreTiles<G>;
+  constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
+  constexpr int WQ_VEC = G * kD * kR / 8;
+  constexpr int WQ_PER = WQ_VEC / NT;
+  constexpr int CP = 64 / S::GE;
+  static_assert(WQ_VEC % NT == 0, "every thread loads the same number of W_q vectors");
+  static_assert(G <= NW, "one wave per q-head in the merges");
+  const int pair = blockIdx.y, blk = blockIdx.x;
+  const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
+  const int kv = p.ret_kv[ret_i];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int h = (lane & 15) % S::GE;  // this lane's head in the score layout
+  const bool hv = h < G;
+  const int hs = hv ? h : 0;
+
+  // The attention tiles' space first holds the projection and the bf16 queries, then
+  // the per-token head masks of the classification, then the K/V tiles; lb first
+  // holds the histogram, then the list of definite rows.
+  __shared__ TileSmem<G> sm;
+  __shared__ unsigned lb[kPassTokens];
+  static_assert(sizeof(uint16_t) * (G * kD * kR + G * kD) <= sizeof(sm.Ks) + sizeof(sm.Vs),
+                "the projection and the queries fit the tile space");
+  static_assert(2 * kPassTokens * sizeof(unsigned) <= sizeof(sm.Ks), "masks fit the K tile");
+  static_assert(sizeof(unsigned) * kNB * S::GE * CP <= sizeof(lb), "bins fit the list space");
+  uint16_t* const wq_s = &sm.Ks[0][0];
+  uint16_t* const q_s = wq_s + G * kD * kR;
+  unsigned (*const bins)[S::GE][CP] = reinterpret_cast<unsigned (*)[S::GE][CP]>(lb);
+  unsigned* const dmask = (unsigned*)&sm.Ks[0][0];
+  unsigned* const cmask = dmask + kPassTokens;
+  unsigned* const list = lb;
+  __shared__ float qi_s[G][kR];
+  __shared__ float red_m[NW][G];
+  __shared__ float mb_s[G];
+  __shared__ int kt_s[G];
+  __shared__ unsigned long long zred[NW][G];
+  __shared__ float bscale[kNB];
+  __shared__ unsigned long long gb[G][kNB];
+  __shared__ double ms[G][kNB];
+  __shared__ float mk_s[kMaxGroups][G];
+  __shared__ double zk_s[kMaxGroups][G];
+  __shared__ float gm_s[G];
+  __shared__ double gz_s[G];
+  __shared__ int kb_s[G], mode_s[G];
+  __shared__ float inv_s[G];
+  __shared__ int relevant, flag_s;
+  __shared__ unsigned cwsum[NW][G];
+  __shared__ unsigned wsum[NW];
+  __shared__ unsigned n_list_s, ubase_s, ucount_s;
+
+  // ---- scan: projection, queries and the index tile requested together
+  uint4 wreg[WQ_PER];
+  const uint4* wsrc = (const uint4*)(p.w_q + (size_t)ret_i * G * kD * kR);
+#pragma unroll
+  for (int u = 0; u < WQ_PER; ++u) wreg[u] = wsrc[u * NT + tid];
+  uint4 qreg = make_uint4(0, 0, 0, 0);
+  const uint4* qsrc = (const uint4*)(p.q_pre + ((size_t)b * p.Hq + kv * G) * kD);
+  if (tid < G * kD / 8) qreg = qsrc[tid];
+  static_assert(NT >= G * kD / 2, "one thread per rotated pair");
+  const bool rot = tid < G * kD / 2;
+  const double th = rot ? p.theta[tid % (kD / 2)] : 0.0;
+  const uint16_t* idx = p.index + ((size_t)(b * p.n_ret + ret_i) * p.max_seq) * kR;
+  const int tok0 = blk * kPassTokens;
+  uint4 a[S::TPW][S::CH];
+  load_score_tiles<G>(idx, tok0, p.N, a);
+#pragma unroll
+  for (int u = 0; u < WQ_PER; ++u) ((uint4*)wq_s)[u * NT + tid] = wreg[u];
+  if (tid < G * kD / 8) ((uint4*)q_s)[tid] = qreg;
+  for (int e = tid; e < kNB * S::GE * CP; e += NT) (&bins[0][0][0])[e] = 0u;
+  for (int e = tid; e < G * kNB; e += NT) (&gb[0][0])[e] = 0ull;
+  if (tid < kNB) bscale[tid] = expf((float)tid * kDelta) * kFxBin;
+  __syncthreads();
+  {
+    // qi: the fp32 rounding of the exact dot product (fp64 sums of exact products)
+    double acc = 0.0;
+    const int hh = tid >> 6, c = (tid >> 2) & 15, part = tid & 3;
+    if (hh < G) {
+      const uint16_t* wq = wq_s + hh * kD * kR + 32 * part * kR + c;
+      const uint4* qq = (const uint4*)(q_s + hh * kD + 32 * part);
+#pragma unroll
+      for (int d0 = 0; d0 < 32; d0 += 8) {
+        const uint4 qw = qq[d0 / 8];
+        const uint32_t qp[4] = {qw.x, qw.y, qw.z, qw.w};
+        float wv[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) wv[d] = bf16_to_f32(wq[(d0 + d) * kR]);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const float qv = (d & 1) ? bf16_hi(qp[d >> 1]) : bf16_lo(qp[d >> 1]);
+          acc = __fma_rn((double)qv, (double)wv[d], acc);
+        }
+      }
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (hh < G && part == 0) qi_s[hh][c] = (float)acc * p.idx_scale;
+  }
+  if (rot) {
+    // every block rotates the queries for its own attention; block 0 also stores
+    // them for the finish kernel
+    const int hh = tid / (kD / 2), i = tid % (kD / 2);
+    float c, sn;
+    rope_sincos(p.N - 1, th, sn, c);
+    const float x = bf16_to_f32(q_s[hh * kD + i]), y = bf16_to_f32(q_s[hh * kD + i + kD / 2]);
+    const float scale = p.attn_scale * kLog2e;
+    const float r0 = (x * c - y * sn) * scale, r1 = (y * c + x * sn) * scale;
+    sm.qs[hh][i] = r0;
+    sm.qs[hh][i + kD / 2] = r1;
+    if (blk == 0) {
+      float* dst = p.qrope + ((size_t)pair * G + hh) * kD;
+      dst[i] = r0;
+      dst[i + kD / 2] = r1;
+    }
+  }
+  __syncthreads();
+  if (blk == 0 && tid < G * kR) p.qi[(size_t)pair * G * kR + tid] = (&qi_s[0][0])[tid];
+
+  uint4 bq[3][S::CH];
+  make_score_b<G>(qi_s, bq);
+  f32x4_t sc[S::TPW];
+  score_tiles<G>(a, bq, sc);
+  float mloc = -INFINITY;
+  if (G < 4 || tok0 + kPassTokens > p.N) {
+#pragma unroll
+    for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!hv || tok0 + score_token<G>(T, r) >= p.N) sc[T][r] = -INFINITY;
+  }
+#pragma unroll
+  for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sc[T][r]);
+  mloc = head_lanes_max<G>(mloc);
+  if (lane < G) red_m[wave][lane] = mloc;
+  __syncthreads();
+  if (tid < G) {
+    float v = red_m[0][tid];
+    for (int q = 1; q < NW; ++q) v = fmaxf(v, red_m[q][tid]);
+    mb_s[tid] = v;
+    kt_s[tid] = score_key(v, kInvDelta);
+  }
+  __syncthreads();
+  {
+    const int kt = kt_s[hs];
+    const float e_top = (float)(kt + 1) * kDelta;
+    const int copy = lane / S::GE;
+    float z = 0.f;
+    static_assert((S::TPW * 4) % 8 == 0, "whole groups of eight scores");
+#pragma unroll
+    for (int g = 0; g < S::TPW * 4; g += 8) {
+      float wt[8], bs[8];
+      unsigned jc[8];
+      bool in[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float sv = sc[(g + u) >> 2][(g + u) & 3];
+        wt[u] = __builtin_amdgcn_exp2f((sv - e_top) * kLog2e);
+        z += wt[u];
+        const unsigned j = (unsigned)(kt - score_key(sv, kInvDelta));
+        in[u] = j < (unsigned)kNB;
+        jc[u] = in[u] ? j : 0u;
+        bs[u] = bscale[jc[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const unsigned v = in[u] ? (unsigned)__builtin_fmaf(wt[u], bs[u], 0.5f) : 0u;
+        atomicAdd(&bins[jc[u]][hs][copy], v);
+      }
+    }
+    const unsigned long long zfx = head_lanes_sum<G>((unsigned long long)((double)z * kFxZ));
+    if (lane < G) zred[wave][lane] = zfx;
+  }
+  __syncthreads();
+  // the block's summary, written through to memory for the merging blocks
+  const size_t so = ((size_t)pair * p.nA + blk) * G;
+  if (tid < G) {
+    unsigned long long zb = 0ull;
+    for (int q = 0; q < NW; ++q) zb += zred[q][tid];
+    st_dev(&p.blk_m[so + tid], mb_s[tid]);
+    st_dev(&p.blk_z[so + tid], zb);
+  }
+  for (int e = tid; e < G * kNB; e += NT) {
+    const int hh = e % G, j = e / G;
+    const unsigned* cp = &bins[j][hh][0];
+    unsigned acc = 0u;
+#pragma unroll
+    for (int c = 0; c < CP; ++c) acc += cp[(c + j) % CP];
+    st_dev(&p.blk_bins[(so + hh) * kNB + j], acc);
+  }
+
+  // ---- threshold: the last block of the group merges the group's summaries, the last
+  // group the pair's.  Every load of a merge is issued at once, over all the block's
+  // threads; the shifted bins add up in LDS as integers (order free).
+  const int grp = blk / kGroupBlocks, g0 = grp * kGroupBlocks;
+  const int nin = min(kGroupBlocks, p.nA - g0);
+  if (arrive_last(&p.cnt_grp[pair * p.nGrp + grp], (unsigned)nin)) {
+    constexpr int PER1 = (kGroupBlocks * G * kNB / 2 + NT - 1) / NT;  // bin pairs per thread
+    const int n_pairs = nin * G * (kNB / 2);
+    unsigned long long w[PER1];
+    float mk = -INFINITY;
+    double zk = 0.0;
+#pragma unroll
+    for (int u = 0; u < PER1; ++u) {
+      const int e = tid + u * NT;
+      w[u] = 0ull;
+      if (e < n_pairs) {
+        const int k = e / (G * kNB / 2), hh = (e / (kNB / 2)) % G, jp = e % (kNB / 2);
+        const size_t sk = ((size_t)pair * p.nA + g0 + k) * G + hh;
+        w[u] = ld_dev((const unsigned long long*)(p.blk_bins + sk * kNB) + jp);
+      }
+    }
+    if (tid < nin * G) {
+      const size_t sk = ((size_t)pair * p.nA + g0) * G + tid;
+      mk = ld_dev(&p.blk_m[sk]);
+      zk = (double)ld_dev(&p.blk_z[sk]) / kFxZ;
+    }
+    // the group's max per q-head, each summary's shift, the group's mass
+    if (tid < nin * G) mk_s[tid / G][tid % G] = mk;
+    __syncthreads();
+    if (tid < G) {
+      float gm = -INFINITY;
+      for (int k = 0; k < nin; ++k) gm = fmaxf(gm, mk_s[k][tid]);
+      gm_s[tid] = gm;
+    }
+    __syncthreads();
+    // each summary's mass moved onto the group's grid by its own thread (one exp
+    // each), then added in a fixed order
+    if (tid < nin * G)
+      zk_s[tid / G][tid % G] =
+          zk * exp((double)(score_key(mk, kInvDelta) - score_key(gm_s[tid % G], kInvDelta)) *
+                   (double)kDelta);
+    __syncthreads();
+    if (tid < G) {
+      double gz = 0.0;
+      for (int k = 0; k < nin; ++k) gz += zk_s[k][tid];
+      gz_s[tid] = gz;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER1; ++u) {
+      const int e = tid + u * NT;
+      if (e < n_pairs && w[u]) {
+        const int k = e / (G * kNB / 2), hh = (e / (kNB / 2)) % G, jp = e % (kNB / 2);
+        const int sh = score_key(gm_s[hh], kInvDelta) - score_key(mk_s[k][hh], kInvDelta);
+        const unsigned v0 = (unsigned)w[u], v1 = (unsigned)(w[u] >> 32);
+        if (2 * jp + sh < kNB && v0) atomicAdd(&gb[hh][2 * jp + sh], (unsigned long long)v0);
+        if (2 * jp + 1 + sh < kNB && v1) atomicAdd(&gb[hh][2 * jp + 1 + sh], (unsigned long long)v1);
+      }
+    }
+    __syncthreads();
+    {
+      const size_t gs = ((size_t)pair * p.nGrp + grp) * G;
+      if (tid < G) {
+        st_dev(&p.grp_m[gs + tid], gm_s[tid]);
+        st_dev((unsigned long long*)&p.grp_z[gs + tid],
+               (unsigned long long)__double_as_longlong(gz_s[tid]));
+      }
+      if (tid < G * kNB) {
+        st_dev(&p.grp_bins[gs * kNB + tid], (&gb[0][0])[tid]);
+        (&gb[0][0])[tid] = 0ull;
+      }
+    }
+    if (arrive_last(&p.cnt_pair[pair], (unsigned)p.nGrp)) {
+      constexpr int PER2 = 8;  // group bins per thread and round
+      const int n_bins = p.nGrp * G * kNB;
+      float mg = -INFINITY;
+      double zg = 0.0;
+      if (tid < p.nGrp * G) {
+        const size_t sg = (size_t)pair * p.nGrp * G + tid;
+        mg = ld_dev(&p.grp_m[sg]);
+        zg = __longlong_as_double((long long)ld_dev((const unsigned long long*)&p.grp_z[sg]));
+      }
+      unsigned long long v[PER2];
+#pragma unroll
+      for (int u = 0; u < PER2; ++u) {
+        const int e = tid + u * NT;
+        v[u] = e < n_bins ? ld_dev(&p.grp_bins[(size_t)pair * p.nGrp * G * kNB + e]) : 0ull;
+      }
+      if (tid < p.nGrp * G) mk_s[tid / G][tid % G] = mg;
+      __syncthreads();
+      if (tid < G) {
+        float m = -INFINITY;
+        for (int k = 0; k < p.nGrp; ++k) m = fmaxf(m, mk_s[k][tid]);
+        gm_s[tid] = m;
+      }
+      __syncthreads();
+      if (tid < p.nGrp * G)
+        zk_s[tid / G][tid % G] =
+            zg * exp((double)(score_key(mg, kInvDelta) + 1) * (double)kDelta -
+                     (double)gm_s[tid % G]);
+      __syncthreads();
+      if (tid < G) {
+        double Z = 0.0;
+        for (int k = 0; k < p.nGrp; ++k) Z += zk_s[k][tid];
+        gz_s[tid] = Z;
+      }
+      __syncthreads();
+      auto add_bins = [&](const unsigned long long (&vv)[PER2], int base) {
+#pragma unroll
+        for (int u = 0; u < PER2; ++u) {
+          const int e = base + tid + u * NT;
+          if (e < n_bins && vv[u]) {
+            const int k = e / (G * kNB), hh = (e / kNB) % G, j = e % kNB;
+            const int sh = score_key(gm_s[hh], kInvDelta) - score_key(mk_s[k][hh], kInvDelta);
+            if (j + sh < kNB) atomicAdd(&gb[hh][j + sh], vv[u]);
+          }
+        }
+      };
+      add_bins(v, 0);
+      for (int base = PER2 * NT; base < n_bins; base += PER2 * NT) {
+#pragma unroll
+        for (int u = 0; u < PER2; ++u) {
+          const int e = base + tid + u * NT;
+          v[u] = e < n_bins ? ld_dev(&p.grp_bins[(size_t)pair * p.nGrp * G * kNB + e]) : 0ull;
+        }
+        add_bins(v, base);
+      }
+      __syncthreads();
+      if (tid < G * kNB) {
+        const int hh = tid / kNB, j = tid % kNB;
+        const int kt = score_key(gm_s[hh], kInvDelta);
+        ms[hh][j] = (double)gb[hh][j] / (double)kFxBin *
+                    exp((double)(kt - j + 1) * (double)kDelta - (double)gm_s[hh]);
+      }
+      __syncthreads();
+      if (tid < G) {
+        // the boundary bin: where the running mass reaches p * Z (the threshold
+        // kernel's search over the same bins)
+        const float m = gm_s[tid];
+        const double Z = gz_s[tid];
+        const int kt = score_key(m, kInvDelta);
+        int mode = 2, key_bnd = INT_MIN;
+        double above = Z, need = 0.0;
+        if (p.top_p < 1.0f) {
+          const double target = (double)p.top_p * Z;
+          double cum = 0.0;
+          int g = 0;
+          for (; g < kNB; ++g) {
+            if (cum + ms[tid][g] >= target) break;
+            cum += ms[tid][g];
+          }
+          mode = g < kNB ? 0 : 1;
+          key_bnd = g < kNB ? kt - g : kt - kNB;
+          above = cum;
+          need = target - cum;
+        }
+        ThrInfo t;
+        t.key_top = kt;
+        t.key_bnd = key_bnd;
+        t.mode = mode;
+        t.m = m;
+        t.Z = Z;
+        t.above = above;
+        t.need = need;
+        t.tau = -INFINITY;
+        t.n_cand = 0;
+        t.inv_w = kInvDelta;
+        p.thr[pair * G + tid] = t;  // read by the finish kernel (a later launch)
+        kb_s[tid] = key_bnd;
+        mode_s[tid] = mode;
+      }
+      if (tid == 0) st_dev(&p.uni_cnt[pair], 0u);
+      __syncthreads();
+      // every block's mailbox: one 64-bit word per q-head, its boundary key in the low
+      // half, its mode in bits 32-33 and bit 63 set: a word is whole or absent
+      for (int k = tid; k < p.nA; k += NT) {
+        unsigned long long* mb = p.mbox + ((size_t)pair * p.nA + k) * kMboxWords;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+          st_dev(&mb[hh], (1ull << 63) | ((unsigned long long)mode_s[hh] << 32) |
+                              (unsigned long long)(unsigned)kb_s[hh]);
+      }
+    }
+  }
+  // ---- wait for this block's mailbox: every q-head's word present, then clear them
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long* mb = p.mbox + ((size_t)pair * p.nA + blk) * kMboxWords;
+    unsigned long long wv[G];
+    bool all = false;
+    for (unsigned it = 0; it < kSpinLimit && !all; ++it) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) wv[hh] = ld_dev(&mb[hh]);
+      all = true;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) all = all && (wv[hh] >> 63);
+      if (!all) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!all) {
+      st_dev(p.err, 1u);
+      flag_s = 0;
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        kb_s[hh] = (int)(unsigned)wv[hh];
+        mode_s[hh] = (int)((wv[hh] >> 32) & 3ull);
+        inv_s[hh] = kInvDelta;
+        st_dev(&mb[hh], 0ull);
+      }
+      flag_s = 1;
+    }
+  }
+  __syncthreads();
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  if (!flag_s) {
+    // gave up: this block contributes nothing (the call's results are void; p.err says so)
+    if (tid < G) p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = 0u;
+  } else {
+    // ---- select: classify the registered scores against the boundary bins
+    if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
+    for (int e = tid; e < kPassTokens; e += NT) dmask[e] = cmask[e] = 0u;
+    __syncthreads();
+    if (tid < G && (mode_s[tid] != 0 || score_key(mb_s[tid], inv_s[tid]) >= kb_s[tid]))
+      atomicOr(&relevant, 1);
+    __syncthreads();
+    if (!relevant && tid < G) p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = 0u;
+    if (relevant) {
+      const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
+      const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
+      const int mode = mode_s[hs], kbnd = kb_s[hs];
+      const float inv = inv_s[hs];
+      const int dthr = mode == 2 ? INT_MIN : kbnd;
+      const int clo = mode == 0 ? kbnd : INT_MIN;
+      const bool full = G >= 4 && tok0 + kPassTokens <= p.N;
+      // Each lane's keys as two bit masks (definite, candidate) without branches;
+      // the definite heads then go to the per-token masks only for the elements that
+      // some lane of the wave has definite.
+      static_assert(S::TPW * 4 <= 32, "one mask bit per element");
+      uint32_t dbits = 0u, cbits = 0u;
+#pragma unroll
+      for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool valid = full || (hv && tok0 + score_token<G>(T, r) < p.N);
+          const int key = score_key(sc[T][r], inv);
+          dbits |= (uint32_t)(valid && key > dthr) << (4 * T + r);
+          cbits |= (uint32_t)(valid && key <= dthr && key >= clo) << (4 * T + r);
+        }
+      const unsigned ccount = (unsigned)__popc(cbits);
+#pragma unroll
+      for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool d = (dbits >> (4 * T + r)) & 1u;
+          if (__ballot(d) != 0ull) {  // wave-uniform: skipped where no lane has one
+            if (d) atomicOr(&dmask[score_token<G>(T, r)], 1u << h);
+          }
+        }
+      if (inspect) {
+#pragma unroll
+        for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((cbits >> (4 * T + r)) & 1u) atomicOr(&cmask[score_token<G>(T, r)], 1u << h);
+      }
+      unsigned inc = ccount;
+#pragma unroll
+      for (int o = S::GE; o < 64; o <<= 1) {
+        const unsigned v = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += v;
+      }
+      if (lane >= 64 - S::GE && hv) cwsum[wave][h] = inc;
+      __syncthreads();
+      if (ccount) {
+        unsigned off = inc - ccount;
+        for (int q = 0; q < wave; ++q) off += cwsum[q][h];
+        float2* cd = p.cand + ((size_t)pair * G + h) * p.N + (size_t)blk * kPassTokens + off;
+#pragma unroll
+        for (int T = 0; T < S::TPW; ++T)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if ((cbits >> (4 * T + r)) & 1u)
+              *cd++ = make_float2(sc[T][r], __int_as_float(tok0 + score_token<G>(T, r)));
+      }
+      if (tid < G) {
+        unsigned tot = 0u;
+        for (int q = 0; q < NW; ++q) tot += cwsum[q][tid];
+        p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = tot;
+      }
+      // definite rows (sinks join every head): ordered compaction into LDS
+      uint32_t dm[TPT];
+      unsigned cnt = 0u;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k) {
+        const int t = tok0 + k * NT + tid;
+        dm[k] = dmask[k * NT + tid];
+        if (t < p.N && t < p.n_sink) dm[k] = (1u << G) - 1u;
+        cnt += dm[k] ? 1u : 0u;
+      }
+      const unsigned incl = wave_incl_sum_u32(cnt);
+      if (lane == 63) wsum[wave] = incl;
+      __syncthreads();
+      unsigned off = incl - cnt;
+      for (int q = 0; q < wave; ++q) off += wsum[q];
+      if (tid == NT - 1) n_list_s = off + cnt;
+#pragma unroll
+      for (int k = 0; k < TPT; ++k)
+        if (dm[k]) list[off++] = ((unsigned)(k * NT + tid) << 8) | dm[k];
+      if (inspect) {
+        uint32_t cm[TPT];
+        unsigned uc = 0u;
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+          cm[k] = cmask[k * NT + tid];
+          uc += (dm[k] | cm[k]) ? 1u : 0u;
+        }
+        if (tid == 0) ucount_s = 0u;
+        __syncthreads();
+        const unsigned uo = uc ? atomicAdd(&ucount_s, uc) : 0u;
+        __syncthreads();
+        if (tid == 0) ubase_s = ucount_s ? atomicAdd(&p.uni_cnt[pair], ucount_s) : 0u;
+        __syncthreads();
+        unsigned u = ubase_s + uo;
+#pragma unroll
+        for (int k = 0; k < TPT; ++k)
+          if (dm[k] | cm[k])
+            p.uni[(size_t)pair * p.N + u++] =
+                make_int2(tok0 + k * NT + tid, (int)(dm[k] | (cm[k] << 8)));
+      }
+      __syncthreads();
+      attend_list<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, (int)n_list_s,
+                         [&](int i) {
+                           const unsigned e = list[i];
+                           return RowMask{tok0 + (int)(e >> 8), e & 0xffu};
+                         },
+                         m, l, o0, o1);
+    }
+  }
+  if (wave < G) {
+    float* dst = p.partB + ((size_t)(pair * G + wave) * p.nA + blk) * kPartStride;
+    if (lane == 0) {
+      dst[0] = m;
+      dst[1] = l;
+    }
+    *(float2*)&dst[4 + 2 * lane] = make_float2(o0, o1);
+  }
+}
+
 // ------------------------------------------------------------------ finish
 
 // Exact threshold inside the boundary bin by bisection on the ordered fp32 key:
@@ -945,8 +1517,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   int* tok_s = (int*)(cbuf + kTokCap);
   static_assert(sizeof(TileSmem<1>) <= sizeof(cbuf), "the tiles fit the candidate space");
   TileSmem<1>& sm = *reinterpret_cast<TileSmem<1>*>(cbuf);
-  // the selected tokens of this block's share (at most kTokCap / kFinishSplit)
-  __shared__ int sel_l[kTokCap / kFinishSplit];
+  // the selected tokens of this block's share (at most kTokCap / kMinFinishSplit)
+  __shared__ int sel_l[kTokCap / kMinFinishSplit];
   __shared__ unsigned boff[kMaxBlocksLds + 1];
   __shared__ unsigned long long red[NT / 64];
   __shared__ unsigned wtot[NT / 64];
@@ -1275,17 +1847,50 @@ __global__ __launch_bounds__(256) void k_debug_sets(DecPlan p) {
 
 // ------------------------------------------------------------------ launch
 
+// Blocks of the fused pass that can run at once on the current device (occupancy of
+// its launch bounds times the compute units), found once per device.
+template <int G>
+static long long pass_capacity() {
+  static std::mutex mu;
+  static long long cap[kMaxDevicesDecode];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesDecode) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_pass<G>, PassCfg<G>::NT, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cap[dev] = (long long)per_cu * cus;
+  }
+  return cap[dev];
+}
+
 template <int G>
 static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   auto mark = [&](int k) {
     if (p.events) (void)hipEventRecord(p.events[k], s);
   };
+  // The fused pass waits inside the launch for the last block of each pair, so every
+  // block must be able to run at once; otherwise (or for a fixed budget, whose
+  // threshold retries coarser grids) the scan, threshold and select kernels run in turn.
+  // RTP_DECODE_PASSES=3 in the environment forces the three launches.
+  const char* env = getenv("RTP_DECODE_PASSES");
+  const bool fused = p.budget == 0 && p.fusable && !(env && env[0] == '3') &&
+                     (long long)p.P * p.nA <= pass_capacity<G>();
   mark(0);
-  RTP_LAUNCH(k_scan<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
-  mark(1);
-  RTP_LAUNCH(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), s, p);
-  mark(2);
-  RTP_LAUNCH(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+  if (fused) {
+    RTP_LAUNCH(k_pass<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+    mark(1);
+    mark(2);
+  } else {
+    RTP_LAUNCH(k_scan<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+    mark(1);
+    RTP_LAUNCH(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), s, p);
+    mark(2);
+    RTP_LAUNCH(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+  }
   mark(3);
   RTP_LAUNCH(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), s, p);
   mark(4);
@@ -1316,10 +1921,20 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base) {
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
-  const int nF = kFinishSplit;
+  // Every finish block resolves its head's threshold (the candidate buffer allows one
+  // block per CU): as many blocks per head as keep the launch to about one block per
+  // CU, between kMinFinishSplit and kFinishSplit.
+  int nF = kFinishSplit;
+  while (nF > kMinFinishSplit && (long long)P * G * nF > kFinishBlocks) nF >>= 1;
   // grid y of the index passes is P, of the finish kernel P * G
   if ((long long)P * G > kMaxGridY) return 0;
-  size_t off = 0;
+  const int nGrp = (nA + kGroupBlocks - 1) / kGroupBlocks;
+  // the fused pass's counters and mailboxes live in the counter region (zero at rest);
+  // the last word is the give-up flag
+  const size_t n_cnt = ((size_t)P * nGrp + P + 2 * kMboxWords - 1) / (2 * kMboxWords) * (2 * kMboxWords);
+  const size_t n_words = n_cnt + (size_t)P * nA * kMboxWords * 2 + 1;
+  const bool fusable = nGrp <= kMaxGroups && n_words * sizeof(unsigned) <= kCounterBytes;
+  size_t off = kCounterBytes;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off += align256(bytes);
@@ -1338,7 +1953,20 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   char* un = take((size_t)P * N * 8);
   char* pB = take((size_t)P * G * nA * kPartStride * 4);
   char* pF = take((size_t)P * G * nF * kPartStride * 4);
+  char* gm = take(fusable ? (size_t)P * nGrp * G * 4 : 0);
+  char* gz = take(fusable ? (size_t)P * nGrp * G * 8 : 0);
+  char* gbn = take(fusable ? (size_t)P * nGrp * G * kNB * 8 : 0);
   if (plan) {
+    plan->fusable = fusable;
+    plan->nGrp = nGrp;
+    unsigned* cnt = (unsigned*)base;
+    plan->cnt_grp = cnt;
+    plan->cnt_pair = cnt + (size_t)P * nGrp;
+    plan->mbox = (unsigned long long*)(cnt + n_cnt);
+    plan->err = (unsigned*)(base + kDecodeErrOffset);
+    plan->grp_m = (float*)gm;
+    plan->grp_z = (double*)gz;
+    plan->grp_bins = (unsigned long long*)gbn;
     plan->P = P;
     plan->nA = nA;
     plan->nF = nF;

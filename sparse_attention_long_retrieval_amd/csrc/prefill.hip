@@ -1132,8 +1132,10 @@ __global__ void k_pf_debug(PfPlan p) {
   const PfVec v = p.vec[vid];
   int32_t* out = p.dbg_idx ? p.dbg_idx + unit * p.dbg_cap : nullptr;
   int n = 0;
+  unsigned* ub = p.dbg_union ? p.ubits + (size_t)bi * p.uwords : nullptr;
   auto put = [&](int k) {
     if (out && n < p.dbg_cap) out[n] = k;
+    if (ub) atomicOr(&ub[k >> 5], 1u << (k & 31));
     ++n;
   };
   for (int k = 0; k < min(p.n_sink, pos + 1); ++k) put(k);
@@ -1162,6 +1164,31 @@ __global__ void k_pf_debug(PfPlan p) {
   if (p.dbg_cnt) p.dbg_cnt[unit] = n;
   if (p.dbg_tau)
     p.dbg_tau[unit] = v.mode == kPfNormal ? v.tau : (v.mode == kPfAll ? -INFINITY : NAN);
+}
+
+// Union of the selected keys of every (batch, retrieval KV head) pair over the chunk
+// (inspection only): the bitmap is cleared before k_pf_debug marks it and counted after.
+__global__ void k_pf_ubits_clear(PfPlan p) {
+  const size_t n = (size_t)p.B * p.n_ret * p.uwords;
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x)
+    p.ubits[e] = 0u;
+}
+__global__ __launch_bounds__(256) void k_pf_ubits_count(PfPlan p) {
+  const int pair = blockIdx.x;
+  const unsigned* ub = p.ubits + (size_t)pair * p.uwords;
+  unsigned c = 0u;
+  for (int e = threadIdx.x; e < p.uwords; e += 256) c += __popc(ub[e]);
+  c = wave_incl_sum_u32(c);
+  __shared__ unsigned part[4];
+  if ((threadIdx.x & 63) == 63) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) p.dbg_union[pair] = (int32_t)(part[0] + part[1] + part[2] + part[3]);
+}
+// Every causal key is read when every key is selected.
+__global__ void k_pf_union_all(PfPlan p) {
+  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pair < p.B * p.n_ret) p.dbg_union[pair] = p.n_keys;
 }
 
 // ------------------------------------------------------------------ host side
@@ -1196,6 +1223,8 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_iperm = take(max_items * sizeof(int));
   const size_t o_part = take(max_items * kPfPartStride * sizeof(float));
   const size_t o_ictl = take(16 * sizeof(int));
+  const size_t uwords = ((size_t)n_keys + 31) / 32;
+  const size_t o_ubits = take((size_t)B * n_ret * uwords * sizeof(unsigned));
   if (plan && base) {
     plan->V = (int)V;
     plan->wcap = (int)wcap;
@@ -1216,6 +1245,8 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
     plan->icount = (int*)(base + o_ictl);
     plan->ictr = (int*)(base + o_ictl) + 8;
     plan->max_items = (int)max_items;
+    plan->ubits = (unsigned*)(base + o_ubits);
+    plan->uwords = (int)uwords;
   }
   return off;
 }
@@ -1254,13 +1285,17 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
   RTP_LAUNCH(k_pf_attend, dim3(kPfAttendBlocks), dim3(256), s, p);
   RTP_LAUNCH(k_pf_merge, dim3((p.V + 3) / 4), dim3(256), s, p);
   mark(4);
-  if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
+  if (p.dbg_union) RTP_LAUNCH(k_pf_ubits_clear, dim3(256), dim3(256), s, p);
+  if (p.dbg_idx || p.dbg_cnt || p.dbg_tau || p.dbg_union)
     RTP_LAUNCH(k_pf_debug, dim3((p.V + 63) / 64), dim3(64), s, p);
+  if (p.dbg_union) RTP_LAUNCH(k_pf_ubits_count, dim3(p.B * p.n_ret), dim3(256), s, p);
   return hipSuccess;
 }
 
 hipError_t launch_prefill_debug_all(const PfPlan& p, hipStream_t s) {
-  RTP_LAUNCH(k_pf_debug_all, dim3((p.V + 63) / 64), dim3(64), s, p);
+  if (p.dbg_idx || p.dbg_cnt || p.dbg_tau)
+    RTP_LAUNCH(k_pf_debug_all, dim3((p.V + 63) / 64), dim3(64), s, p);
+  if (p.dbg_union) RTP_LAUNCH(k_pf_union_all, dim3((p.B * p.n_ret + 63) / 64), dim3(64), s, p);
   return hipSuccess;
 }
 

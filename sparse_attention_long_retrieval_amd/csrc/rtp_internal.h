@@ -44,6 +44,9 @@ constexpr int kCoarseGrids = 4;
 constexpr int kPassTokens = 2048;
 // Bytes reserved at the start of each workspace for self-resetting counters.
 constexpr size_t kCounterBytes = 65536;
+// The decode's give-up flag: the last word of its counter region.
+constexpr size_t kDecodeErrOffset = kCounterBytes - 4;
+static_assert(kDecodeErrOffset == RTP_DECODE_ERROR_OFFSET, "header and library agree");
 
 // Threshold state of one (pair, q-head).
 struct ThrInfo {
@@ -92,6 +95,19 @@ struct DecPlan {
   int2* uni;                      // [P][N]     debug: (token, definite | candidate << 8)
   float* partB;                   // [P*G][nA][kPartStride]
   float* partF;                   // [P*G][nF][kPartStride]
+  // fused index pass (scan, threshold and select in one launch whose blocks all run
+  // at once): self-resetting counters in the workspace's counter region, and the
+  // merge groups' summaries
+  int fusable;                    // the counters fit (the launch also needs the GPU room)
+  int nGrp;                       // merge groups of kGroupBlocks blocks per pair
+  unsigned* cnt_grp;              // [P][nGrp] blocks of the group done
+  unsigned* cnt_pair;             // [P]       groups of the pair merged
+  unsigned long long* mbox;       // [P][nA][kMboxWords] per block and q-head: set bit 63,
+                                  //           mode in bits 32-33, boundary key below
+  unsigned* err;                  // [1]       a wait gave up (the call's results are void)
+  float* grp_m;                   // [P][nGrp][G]
+  double* grp_z;                  // [P][nGrp][G]   relative to the upper edge of grp_m's bin
+  unsigned long long* grp_bins;   // [P][nGrp][G][kNB]
   // debug (device pointers or null)
   int32_t* dbg_idx;
   int32_t* dbg_cnt;
@@ -100,6 +116,12 @@ struct DecPlan {
   int32_t* dbg_union;
   hipEvent_t* events;  // phase events or null
 };
+
+// Blocks per first-level merge group of the fused index pass, and the most groups
+// per pair it merges.
+constexpr int kGroupBlocks = 16;
+constexpr int kMaxGroups = 64;
+constexpr int kMboxWords = 8;   // a block's mailbox: one 64-bit word per q-head (G <= 8)
 
 // Where token j of a (batch, KV head) lives.  ring_len == 0: row j of the full
 // cache, heads max_seq rows apart.  ring_len > 0: a local-head ring of n_sink sink
@@ -222,6 +244,10 @@ struct PfPlan {
   int32_t* dbg_cnt;
   float* dbg_tau;
   int dbg_cap;
+  int32_t* dbg_union;  // [B * n_ret] distinct keys selected over the chunk
+  unsigned* ubits;     // [B * n_ret][uwords] key bitmap of the union (debug only)
+  int uwords;
+  int n_keys;          // q_start + Tq
   hipEvent_t* events;  // phase events or null
 };
 

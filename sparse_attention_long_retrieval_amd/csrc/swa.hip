@@ -40,16 +40,16 @@ __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
   const int r0 = seg * p.segRows;
   const int r1 = min(L, r0 + p.segRows);
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t0 = r0; t0 < r1; t0 += kTileRows) {
-    const int nr = min(kTileRows, r1 - t0);
-    if ((int)threadIdx.x < nr) {
-      const int v = t0 + threadIdx.x;
-      sm.rows[threadIdx.x] = p.map.row(v < ns_out ? v : lo + (v - ns_out));
-      sm.masks[threadIdx.x] = 0xffffffffu;
-    }
-    __syncthreads();
-    tile_attend<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
-  }
+  // the segment's rows in tiles of 64, the next tile's K/V in flight while the current
+  // one is computed; window row v is sink v (v < ns_out) or token lo + v - ns_out
+  __syncthreads();  // the rotated queries are in sm.qs
+  attend_list<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, max(0, r1 - r0),
+                     [&](int i) {
+                       const int v = r0 + i;
+                       return RowMask{p.map.row(v < ns_out ? v : lo + (v - ns_out)),
+                                      0xffffffffu};
+                     },
+                     m, l, o0, o1);
   const size_t unit = (size_t)bl * G + h;
   store_partial(p.part + (unit * p.nSeg + seg) * kPartStride, m, l, o0, o1);
 
@@ -89,11 +89,15 @@ hipError_t launch_swa_decode(const SwaPlan& p, hipStream_t s) {
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Decode sizing: rows = window rows + sinks outside the window; segments of a
-// multiple of 64 rows so that about 2048 blocks cover the GPU.
+// multiple of 64 rows, about kSwaBlocks of them over all units (two blocks per CU:
+// enough loads in flight to stream the window, and several tiles per block to
+// overlap the next tile's loads with the current one's arithmetic when the
+// windows are long).
+constexpr int kSwaBlocks = 512;
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base) {
   (void)Tq;
   const int units = B * n_loc;
-  int nSeg = units > 0 ? (2048 + units - 1) / units : 1;
+  int nSeg = units > 0 ? (kSwaBlocks + units - 1) / units : 1;
   const int max_seg = (rows + kTileRows - 1) / kTileRows;
   if (nSeg > max_seg) nSeg = max_seg;
   if (nSeg < 1) nSeg = 1;

@@ -335,3 +335,43 @@ def test_decode_topk_far_boundary(case):
         P.check_out(res["out"][b, h], own, f"own set h{h}")
         P.check_out(res["out"][b, h], r["out"], f"h{h} ({kind})")
     print(f"needle {needle} N {N} top-{k}: head-0 candidates {n_cand}, {kinds}")
+
+
+@pytest.mark.parametrize("case", [CASES[5], CASES[6], CASES[8]],
+                         ids=[f"s{c[0]}_N{c[4]}_G{c[2] // c[3]}" for c in (CASES[5], CASES[6], CASES[8])])
+@pytest.mark.parametrize("top_p", [0.5, 0.9, 0.999, 1.0])
+def test_three_launch_path_matches_fused(case, top_p, monkeypatch):
+    """The scan, threshold and select kernels in turn (the path for grids that do not
+    fit the GPU at once) give the fused pass's sets and outputs bit for bit, and both
+    meet the oracle."""
+    seed, B, Hq, Hkv, N, ret, window, needles, qs = case
+    wl = W.random_decode(seed, B, Hq, Hkv, N, ret, window, n_needles=needles, q_scale=qs)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx, max_seq=N + 7)
+    fused = dev.decode(top_p, debug_cap=N)
+    monkeypatch.setenv("RTP_DECODE_PASSES", "3")
+    three = dev.decode(top_p, debug_cap=N)
+    assert np.array_equal(fused["out"], three["out"])
+    assert np.array_equal(fused["cnt"], three["cnt"]) and np.array_equal(fused["tau"], three["tau"])
+    for u in range(len(fused["cnt"])):
+        assert np.array_equal(P.gpu_set(fused, u), P.gpu_set(three, u))
+    P.compare_decode(wl, kc, vc, idx, three, top_p)
+
+
+def test_fused_pass_leaves_no_error_and_counters_at_rest():
+    """After fused decodes of several shapes on one workspace, the give-up word is zero
+    and every counter of the counter region is back at zero."""
+    import sparse_attention_long_retrieval_amd as R
+    wls = [W.random_decode(47, 1, 8, 2, n, [0], 256, n_needles=2, q_scale=1.5)
+           for n in (40000, 2049, 300000)]
+    ws = None
+    for wl in wls:
+        kc, vc, idx = O.caches_for(wl)
+        dev = P.Device(wl, kc, vc, idx)
+        need = R.workspace_size(dev.layer, R.OP_DECODE, wl.N)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda")
+        res = dev.decode(0.9, debug_cap=wl.N, ws=ws)
+        P.compare_decode(wl, kc, vc, idx, res, 0.9)
+        counters = ws[:65536].view(torch.int32).cpu().numpy()
+        assert not counters.any(), np.nonzero(counters)[0][:8]

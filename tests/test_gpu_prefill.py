@@ -115,10 +115,19 @@ def _prefill_retrieval(wl, kc, vc, idx, top_p, cap, idx_scale=1.0, max_seq=None,
     nbytes = R.workspace_size(dev.layer, R.OP_PREFILL, wl.N, Tq=wl.Tq)
     ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device="cuda")
     V = wl.B * wl.n_ret * wl.G * wl.Tq
-    dbg = R.Debug(V, cap)
+    dbg = R.Debug(V, cap, pairs=wl.B * wl.n_ret)
     R.prefill_chunk(dev.layer, dev.q, wl.q_start, dev.w_q, dev.kc, dev.vc, dev.idx, top_p, out,
                     ws, idx_scale=idx_scale, debug=dbg)
     torch.cuda.synchronize()
+    if units is None:
+        # the union count of each (batch, retrieval KV head) pair is the number of
+        # distinct keys in the sets of all its rows and q-heads
+        cnt = dbg.sel_count.cpu().numpy()
+        sel = dbg.sel_idx.cpu().numpy()
+        per = wl.G * wl.Tq
+        for pr, u in enumerate(dbg.union_count.cpu().numpy()):
+            keys = np.concatenate([sel[v, :min(cnt[v], cap)] for v in range(pr * per, (pr + 1) * per)])
+            assert int(u) == len(np.unique(keys)), (pr, int(u), len(np.unique(keys)))
     if units is None:
         sel = dbg.sel_idx.cpu().numpy()
     else:  # only the sampled entries come back to the host
@@ -243,3 +252,42 @@ def test_prefill_retrieval_chunked_256k_sampled():
     sizes = [int(res["cnt"][u]) for u in range(0, len(res["cnt"]), 997)]
     print(f"chunked_prefill_256k retrieval: {kinds} worst |err| {worst:.3g} "
           f"sample set sizes {sizes[:12]}")
+
+
+@pytest.fixture(scope="module")
+def million_chunk():
+    """The 1M-context chunk and the oracle caches its sampled rows need."""
+    wl = W.make(6)
+    rng = np.random.default_rng(66)
+    rows = sorted(set([0, 1, 2048, 4095] + rng.integers(0, wl.Tq, 2).tolist()))
+    kc, vc, idx = O.caches_for(wl, rows_needed=_local_rows_needed(wl, rows))
+    return wl, rows, kc, vc, idx
+
+
+@pytest.mark.timeout(900)
+def test_prefill_retrieval_chunked_1m_sampled(million_chunk):
+    """Chunked prefill at 1M context (a 4096-row chunk at the end of 2^20 keys, 8
+    retrieval q-heads): the workspace the call asks for fits the GPU with room to
+    spare, the whole chunk runs, and the sets and outputs of sampled rows of every
+    retrieval q-head match the oracle."""
+    wl, rows, kc, vc, idx = million_chunk
+    layer = R.Layer(wl.B, wl.Hq, wl.Hkv, wl.N, wl.ret_kv_heads, wl.n_sink, wl.window)
+    nbytes = R.workspace_size(layer, R.OP_PREFILL, wl.N, Tq=wl.Tq)
+    assert nbytes < 16 << 30, nbytes
+    units = [((b * wl.n_ret + i) * wl.G + g) * wl.Tq + t for b in range(wl.B)
+             for i in range(wl.n_ret) for g in range(wl.G) for t in rows]
+    res = _prefill_retrieval(wl, kc, vc, idx, 0.9, cap=1 << 18, units=units)
+    kinds, worst = _check_retrieval(wl, kc, vc, idx, res, 0.9, rows)
+    assert kinds.get("valid-alt", 0) == 0
+    print(f"chunked_prefill_1m retrieval: workspace {nbytes / 2**30:.2f} GiB, {kinds}, "
+          f"worst |err| {worst:.3g}, sampled set sizes {[int(res['cnt'][u]) for u in units]}")
+
+
+@pytest.mark.timeout(600)
+def test_swa_prefill_chunked_1m_sampled(million_chunk):
+    """The local heads of the same 1M-context chunk (24 q-heads, window 8192 + 4
+    sinks): the full chunk on the GPU, sampled rows against the oracle."""
+    wl, rows, kc, vc, _ = million_chunk
+    out = _swa_chunk(wl, kc, vc)
+    worst = _check_rows(wl, kc, vc, out, rows)
+    print(f"chunked_prefill_1m local heads: worst |err| {worst:.3g}")

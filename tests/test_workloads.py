@@ -67,3 +67,20 @@ def test_million_clusters_are_sparse():
     wl = W.million_decode()
     sizes = [len(tp["set"]) for _, (_, tp) in _sets(wl, 0, 0, 0.9).items()]
     assert np.median(sizes) <= 0.02 * wl.N
+
+
+@pytest.mark.slow
+def test_million_prefill_shape_and_density():
+    """The 1M chunk: 4096 rows at the end of 2^20 keys, C5's head layout, clusters at
+    C5's density (about three quarters of the keys clustered), rows aligned to
+    clusters select a small fraction of the keys."""
+    wl = W.make(6)
+    assert (wl.N, wl.Tq, wl.q_start, wl.Hq, wl.Hkv) == (1 << 20, 4096, (1 << 20) - 4096, 32, 8)
+    assert wl.ret_kv_heads == [0, 5] and wl.q_pre.shape == (1, 32, 4096, 128)
+    kv = wl.ret_kv_heads[0]
+    idx = O.f64_to_bf16(O.bf16_to_f64(wl.k_pre[0, kv]) @ O.bf16_to_f64(wl.w_k[0]))
+    sizes = []
+    for t in (0, 2047, 4095):
+        s = O.scores(O.query_index(wl.q_pre[0, 0, t], wl.w_q[0]), idx[:wl.q_start + t + 1])
+        sizes.append(len(O.top_p_set(s, 0.9)["set"]))
+    assert np.median(sizes) <= 0.02 * wl.N, sizes

@@ -6,10 +6,9 @@ top-p selection and no attention.  It only draws Gaussian tensors with NumPy's
 PCG64 generator, plants keys aligned to a direction, and rounds fp32 draws to
 bf16 bit patterns (round to nearest even).
 
-Workload shapes follow the five configurations of the build: a tiny needle
-decode, a Qwen3-8B-shaped decode at 64K, a variable-budget decode at 128K, a
-1M-context decode shaped like Qwen3-30B-A3B's attention, and a 4096-token
-chunked prefill at 256K.  The pages measure on RULER, LongBench, AIME and
+Workload shapes: a tiny needle decode, a Qwen3-8B-shaped decode at 64K, a
+variable-budget decode at 128K, a 1M-context decode shaped like Qwen3-30B-A3B's
+attention, and a 4096-token chunked prefill at 256K and at 1M.  The pages measure on RULER, LongBench, AIME and
 needle-in-a-haystack; these synthetic inputs stand in for them and imitate the
 regimes the pages report (a needle query covered by a couple of tokens, a
 diffuse query needing thousands; "Full Attention Strikes Back", techwalker
@@ -277,7 +276,8 @@ def variable_budget_decode(seed: int = 1003, B: int = 4, N: int = 131072,
 
 
 def chunked_prefill(seed: int = 1005, N: int = 262144, Tq: int = 4096,
-                    n_clusters: int = 256, B: int = 1) -> Workload:
+                    n_clusters: int = 256, B: int = 1,
+                    name: str = "chunked_prefill_256k") -> Workload:
     """Chunked prefill: the last Tq of N cached tokens are the query chunk.
 
     32 q / 8 KV heads, KV {0,5} retrieval with planted clusters; each (row, retrieval
@@ -301,8 +301,16 @@ def chunked_prefill(seed: int = 1005, N: int = 262144, Tq: int = 4096,
                 h = kv * G + g
                 t = rng.integers(0, n_clusters, size=Tq)
                 q[b, h] = cents[t] + np.float32(0.3) * _normal(rng, (Tq, D))
-    return Workload("chunked_prefill_256k", seed, B, Hq, Hkv, N, ret_kv, n_sink, 8192, 1e6,
+    return Workload(name, seed, B, Hq, Hkv, N, ret_kv, n_sink, 8192, 1e6,
                     [0.9], f32_to_bf16_bits(q), k, v, w_q, w_k, Tq=Tq, q_start=N - Tq)
+
+
+def million_prefill(seed: int = 1006, N: int = 1 << 20, Tq: int = 4096,
+                    n_clusters: int = 1024) -> Workload:
+    """The chunked prefill at 1M context (the pages quote their largest prefill gain
+    there): a 4096-row chunk at the end of 1,048,576 cached keys, the head layout of
+    the 256K chunk, and 1024 clusters, the same cluster density as 256 over 256K."""
+    return chunked_prefill(seed, N, Tq, n_clusters, name="chunked_prefill_1m")
 
 
 def random_decode(seed: int, B: int, Hq: int, Hkv: int, N: int, ret_kv: List[int],
@@ -355,10 +363,12 @@ CONFIGS = {
     3: variable_budget_decode,
     4: million_decode,
     5: chunked_prefill,
+    6: million_prefill,
 }
 
 
 def make(config: int, seed: Optional[int] = None, **kw) -> Workload:
-    """Build configuration 1..5 with seed 1000 + config unless given."""
+    """Build configuration 1..6 with seed 1000 + config unless given (6: the chunked
+    prefill at 1M context)."""
     fn = CONFIGS[config]
     return fn(seed=1000 + config if seed is None else seed, **kw)
