@@ -115,7 +115,8 @@ enum {
   RTP_OP_SWA = 2,
   RTP_OP_APPEND = 3,
   RTP_OP_CLUSTER_BUILD = 4,  /* Tq = n_clusters, seq_len = n_tokens */
-  RTP_OP_CLUSTER_DECODE = 5  /* Tq = n_clusters */
+  RTP_OP_CLUSTER_DECODE = 5, /* Tq = n_clusters */
+  RTP_OP_DECODE_STEP = 6     /* rtp_decode_step (Tq ignored) */
 };
 
 /*
@@ -300,6 +301,38 @@ rtp_status rtp_swa_attn_ring(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
                              int32_t q_start, int32_t Tq, int32_t ring_len,
                              const rtp_bf16* k_ring, const rtp_bf16* v_ring, float attn_scale,
                              rtp_bf16* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * rtp_decode_step - one decode step of a whole layer: every retrieval q-head as
+ * rtp_decode_sparse_attn computes it and every local q-head as rtp_swa_attn (ring_len
+ * == 0: K/V rows from k_cache, v_cache) or rtp_swa_attn_ring (ring_len > 0: from
+ * k_ring, v_ring) computes it, for the query at position seq_len-1.  The pages split
+ * a layer's heads this way: retrieval heads with dynamic top-p over the full cache,
+ * the rest streaming heads over sinks and a window ([techwalker] §2, §3, §8; [v2]
+ * findings 1 and 4).
+ * When the index pass runs as one fused launch, its blocks attend the local heads'
+ * window segments while they wait for their threshold, so the local heads add no
+ * launch of their own; otherwise the local-head kernel runs after the index passes on
+ * the same stream.  Retrieval outputs are bit-identical to rtp_decode_sparse_attn's.
+ * The local windows are split into segments sized to the fused pass, so local outputs
+ * equal rtp_swa_attn's up to the rounding of a different segment order (the same for
+ * ring and full cache).
+ *   k_ring, v_ring  as for rtp_swa_attn_ring (ignored, may be NULL, when ring_len == 0)
+ *   out      [B][Hq][D] bf16 device; every q-head row is written
+ *   other arguments as for rtp_decode_sparse_attn; dbg covers the retrieval heads
+ * Workspace: op RTP_OP_DECODE_STEP.  The give-up word of a fused launch is at
+ * RTP_DECODE_ERROR_OFFSET as for rtp_decode_sparse_attn.
+ * Errors: as rtp_decode_sparse_attn and rtp_swa_attn_ring; RTP_ERR_RANGE if
+ *   ring_len < 0, or 0 < ring_len < window; RTP_ERR_UNSUPPORTED if the local heads'
+ *   merge counters do not fit the workspace's counter region.
+ */
+rtp_status rtp_decode_step(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                           const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                           const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                           int32_t ring_len, const rtp_bf16* k_ring, const rtp_bf16* v_ring,
+                           float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                           const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                           void* stream);
 
 /*
  * Cluster index of the retrieval KV heads ([v2] finding 3: after the low-rank

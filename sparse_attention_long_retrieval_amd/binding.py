@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librtp.so")
 
 OP_DECODE, OP_PREFILL, OP_SWA, OP_APPEND = 0, 1, 2, 3
-OP_CLUSTER_BUILD, OP_CLUSTER_DECODE = 4, 5
+OP_CLUSTER_BUILD, OP_CLUSTER_DECODE, OP_DECODE_STEP = 4, 5, 6
 
 STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE",
           4: "RTP_ERR_RANGE", 5: "RTP_ERR_UNSUPPORTED", 6: "RTP_ERR_WORKSPACE", 7: "RTP_ERR_HIP"}
@@ -26,7 +26,7 @@ STATUS = {0: "RTP_OK", 1: "RTP_ERR_NULL", 2: "RTP_ERR_ALIGN", 3: "RTP_ERR_SHAPE"
 EXPORTED = ["rtp_index_append", "rtp_decode_sparse_attn", "rtp_prefill_chunk", "rtp_swa_attn",
             "rtp_workspace_size", "rtp_status_string", "rtp_last_error", "rtp_abi_version",
             "rtp_decode_topk", "rtp_ring_append", "rtp_swa_attn_ring", "rtp_cluster_build",
-            "rtp_decode_cluster_attn", "rtp_decode_sparse_attn_noalloc"]
+            "rtp_decode_cluster_attn", "rtp_decode_sparse_attn_noalloc", "rtp_decode_step"]
 
 
 class RtpError(RuntimeError):
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_decode_sparse_attn_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, i32, f32, f32, f32,
                                                      vp, ctypes.POINTER(DebugOut), vp]
+        L.rtp_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, i32, i32, vp, vp, f32, f32, f32, vp,
+                                      ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_prefill_chunk.argtypes = [dp, vp, i32, i32, vp, vp, vp, vp, f32, f32, f32, vp,
                                         ctypes.POINTER(DebugOut), vp, sz, vp]
         L.rtp_swa_attn.argtypes = [dp, vp, i32, i32, vp, vp, f32, vp, vp, sz, vp]
@@ -196,6 +198,22 @@ def decode_sparse_attn(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_le
         layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
         top_p, idx_scale, attn_scale, _p(out), None if debug is None else debug.ref(),
         _p(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def decode_step(layer: Layer, q_pre, w_q, k_cache, v_cache, index, seq_len: int, top_p: float,
+                out, workspace, ring_len: int = 0, k_ring=None, v_ring=None,
+                idx_scale: float = 1.0, attn_scale: Optional[float] = None,
+                debug: Optional[Debug] = None, stream=None) -> None:
+    """One decode step of the whole layer (rtp_decode_step): retrieval q-heads by
+    dynamic top-p, local q-heads over sinks + window from the full cache (ring_len 0)
+    or from the rings."""
+    if attn_scale is None:
+        attn_scale = 1.0 / math.sqrt(layer.head_dim)
+    _check(lib().rtp_decode_step(
+        layer.desc(), _p(q_pre), _p(w_q), _p(k_cache), _p(v_cache), _p(index), seq_len,
+        ring_len, _p(k_ring), _p(v_ring), top_p, idx_scale, attn_scale, _p(out),
+        None if debug is None else debug.ref(), _p(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 def decode_sparse_attn_noalloc(layer: Layer, q_pre, w_q, k_cache, v_cache, index,

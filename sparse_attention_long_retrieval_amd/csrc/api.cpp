@@ -149,6 +149,21 @@ rtp_status rtp_workspace_size(const rtp_layer_desc* desc, int32_t op, int32_t Tq
       if (*bytes == 0)
         return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d", rtp::kMaxGridY);
       return RTP_OK;
+    case RTP_OP_DECODE_STEP: {
+      int loc[rtp::kMaxKv], n_loc;
+      local_heads(desc, loc, &n_loc);
+      if (n_loc > 0 && desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+      const int rows = n_loc ? swa_rows(seq_len - 1, desc->window, desc->n_sink) : 0;
+      if (desc->n_ret == 0) {
+        *bytes = rtp::swa_workspace(desc->batch, n_loc, G, 1, rows, nullptr, nullptr);
+      } else {
+        *bytes = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr,
+                                       n_loc, rows);
+      }
+      if (*bytes == 0)
+        return fail(RTP_ERR_UNSUPPORTED, "batch * q-heads too large for one decode step");
+      return RTP_OK;
+    }
     case RTP_OP_SWA: {
       if (Tq < 1) return fail(RTP_ERR_SHAPE, "Tq %d < 1", Tq);
       if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
@@ -262,12 +277,21 @@ rtp_status append_impl(const rtp_layer_desc* desc, const rtp_bf16* k_pre, const 
   return RTP_OK;
 }
 
-// Shared by the top-p and the fixed-budget decode: top_k > 0 selects the budget.
+// The local heads of a decode step: where their K/V rows live.
+struct LocalHeads {
+  int ring_len;       // 0: the full cache
+  const rtp_bf16* k;  // k_cache or k_ring
+  const rtp_bf16* v;
+};
+
+// Shared by the top-p and the fixed-budget decode: top_k > 0 selects the budget;
+// local != nullptr adds the local heads of the step (rtp_decode_step).
 rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const rtp_bf16* w_q,
                        const rtp_bf16* k_cache, const rtp_bf16* v_cache, const rtp_bf16* index,
                        int32_t seq_len, float top_p, int32_t top_k, float idx_scale,
                        float attn_scale, rtp_bf16* out, const rtp_debug_out* dbg,
-                       void* workspace, size_t ws_bytes, void* stream) {
+                       void* workspace, size_t ws_bytes, void* stream,
+                       const LocalHeads* local = nullptr) {
   RTP_TRY(check_desc(desc));
   const int G = group(desc);
   if (!supported_group(G)) return fail(RTP_ERR_UNSUPPORTED, "G=%d (1, 2, 4 or 8)", G);
@@ -287,11 +311,19 @@ rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const 
   if (dbg && (dbg->sel_idx && dbg->sel_cap < 1)) return fail(RTP_ERR_RANGE, "dbg->sel_cap < 1");
   if (dbg && dbg->phase_events && dbg->n_phase_events < 6)
     return fail(RTP_ERR_RANGE, "dbg->n_phase_events < 6");
+  int loc[rtp::kMaxKv], n_loc = 0, rows = 0;
+  if (local) {
+    local_heads(desc, loc, &n_loc);
+    rows = swa_rows(seq_len - 1, desc->window, desc->n_sink);
+  }
   // the index passes launch batch * n_ret blocks in grid y, the finish kernel
-  // batch * n_ret * G; decode_workspace returns 0 past the grid limit
-  const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr, nullptr);
+  // batch * n_ret * G; decode_workspace returns 0 past the grid limit (or when the
+  // local heads' merge counters do not fit the counter region)
+  const size_t need = rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, nullptr,
+                                            nullptr, n_loc, rows);
   if (need == 0)
-    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d", rtp::kMaxGridY);
+    return fail(RTP_ERR_UNSUPPORTED, "batch * retrieval q-heads > %d (or too many local heads)",
+                rtp::kMaxGridY);
   if (ws_bytes < need)
     return fail(RTP_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   rtp::DecPlan p;
@@ -320,7 +352,28 @@ rtp_status decode_impl(const rtp_layer_desc* desc, const rtp_bf16* q_pre, const 
   p.idx_scale = idx_scale;
   p.attn_scale = attn_scale;
   rope_theta(desc->rope_base, p.theta);
-  rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, &p, (char*)workspace);
+  rtp::decode_workspace(desc->batch, desc->n_ret, G, seq_len, &p, (char*)workspace, n_loc, rows);
+  if (p.with_swa) {
+    rtp::SwaPlan& w = p.sw;
+    w.q_pre = q_pre;
+    w.k_cache = local->k;
+    w.v_cache = local->v;
+    w.out = out;
+    w.B = desc->batch;
+    w.Hq = desc->n_q_heads;
+    w.Hkv = desc->n_kv_heads;
+    w.G = G;
+    w.max_seq = desc->max_seq;
+    w.n_sink = desc->n_sink;
+    w.window = desc->window;
+    w.map = local->ring_len ? ring_map(desc, local->ring_len) : full_map(desc);
+    w.n_loc = n_loc;
+    for (int i = 0; i < n_loc; ++i) w.loc_kv[i] = loc[i];
+    w.attn_scale = attn_scale;
+    memcpy(w.theta, p.theta, sizeof(w.theta));
+    w.q_start = seq_len - 1;
+    w.Tq = 1;
+  }
   if (dbg) {
     p.dbg_idx = dbg->sel_idx;
     p.dbg_cnt = dbg->sel_count;
@@ -686,6 +739,40 @@ rtp_status rtp_swa_attn_ring(const rtp_layer_desc* desc, const rtp_bf16* q_pre, 
     return fail(RTP_ERR_RANGE, "ring_len %d < window %d + Tq %d - 1", ring_len, desc->window, Tq);
   return swa_impl(desc, q_pre, q_start, Tq, ring_map(desc, ring_len), k_ring, v_ring,
                   attn_scale, out, workspace, ws_bytes, stream);
+}
+
+rtp_status rtp_decode_step(const rtp_layer_desc* desc, const rtp_bf16* q_pre,
+                           const rtp_bf16* w_q, const rtp_bf16* k_cache,
+                           const rtp_bf16* v_cache, const rtp_bf16* index, int32_t seq_len,
+                           int32_t ring_len, const rtp_bf16* k_ring, const rtp_bf16* v_ring,
+                           float top_p, float idx_scale, float attn_scale, rtp_bf16* out,
+                           const rtp_debug_out* dbg, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  RTP_TRY(check_desc(desc));
+  int loc[rtp::kMaxKv], n_loc;
+  local_heads(desc, loc, &n_loc);
+  if (ring_len < 0) return fail(RTP_ERR_RANGE, "ring_len %d < 0", ring_len);
+  if (n_loc > 0) {
+    if (desc->window < 1) return fail(RTP_ERR_RANGE, "window < 1");
+    if (ring_len > 0) {
+      if (ring_len < desc->window)
+        return fail(RTP_ERR_RANGE, "ring_len %d < window %d", ring_len, desc->window);
+      RTP_TRY(check_dev(k_ring, "k_ring"));
+      RTP_TRY(check_dev(v_ring, "v_ring"));
+    }
+  }
+  LocalHeads lh;
+  lh.ring_len = ring_len;
+  lh.k = ring_len ? k_ring : k_cache;
+  lh.v = ring_len ? v_ring : v_cache;
+  if (desc->n_ret == 0) {
+    if (seq_len < 1 || seq_len > desc->max_seq)
+      return fail(RTP_ERR_RANGE, "seq_len %d outside [1, max_seq %d]", seq_len, desc->max_seq);
+    return swa_impl(desc, q_pre, seq_len - 1, 1, ring_len ? ring_map(desc, ring_len) : full_map(desc),
+                    lh.k, lh.v, attn_scale, out, workspace, ws_bytes, stream);
+  }
+  return decode_impl(desc, q_pre, w_q, k_cache, v_cache, index, seq_len, top_p, 0, idx_scale,
+                     attn_scale, out, dbg, workspace, ws_bytes, stream, n_loc ? &lh : nullptr);
 }
 
 }  // extern "C"

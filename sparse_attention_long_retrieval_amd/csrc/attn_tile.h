@@ -44,8 +44,7 @@ __device__ __forceinline__ void load_q_rope(TileSmem<G>& sm, const uint16_t* q_h
   float c, s;
   rope_sincos(pos, theta[i], s, c);
   const float x = bf16_to_f32(q[i]), y = bf16_to_f32(q[i + 64]);
-  sm.qs[h][i] = (x * c - y * s) * scale;
-  sm.qs[h][i + 64] = (y * c + x * s) * scale;
+  rope_rotate(x, y, c, s, scale, sm.qs[h][i], sm.qs[h][i + 64]);
 }
 
 // Copy the rotated, pre-scaled queries of G heads (src[h * D + i]) into sm.qs.

@@ -31,16 +31,20 @@
 //                a share of the selected candidates.
 //   k_merge      combine all partial softmax states into the bf16 output.
 // Every sum and row order is fixed, so results are bit-identical across runs.
+#include <algorithm>
+#include <cfloat>
 #include <cstdlib>
 #include <mutex>
 
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
+#include "swa_segment.h"
 
 namespace rtp {
 
 constexpr int kMaxDevicesDecode = 64;
+static_assert(sizeof(DecPlan) <= 4096, "the plan fits the kernel argument space");
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int G>
@@ -60,6 +64,7 @@ constexpr int kMinFinishSplit = 4;    // ... and at least
 constexpr int kFinishBlocks = 256;    // total finish blocks aimed at: one per CU (LDS)
 constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 8;         // output dimensions per merge block
+constexpr int kFinPB = 16;            // index-pass partials a finish block requests up front
 
 // floor(f * 2^36) for a finite f >= 0, from the bits: the 24-bit significand
 // shifted by the exponent (equal to converting f * 2^36 in double and truncating).
@@ -72,6 +77,20 @@ __device__ __forceinline__ unsigned long long fx36(float f) {
   return sh >= 0 ? mant << sh : mant >> (-sh);
 }
 static_assert(kFxCand == 68719476736.0, "candidate masses are 2^36 fixed point");
+
+// Fold one partial softmax state (mk, lk, ok0, ok1) into the running state of the
+// calling wave (lane = dimension pair); -inf states hold nothing.
+__device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float& A1, float mk,
+                                           float lk, float ok0, float ok1) {
+  if (mk == -INFINITY) return;
+  const float nm = fmaxf(M, mk);
+  const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
+  const float sk = exp2f(mk - nm);
+  L = L * so + lk * sk;
+  A0 = A0 * so + ok0 * sk;
+  A1 = A1 * so + ok1 * sk;
+  M = nm;
+}
 
 // Inverse bin width of coarse grid c: bins of 2^c score units (exact in fp32).
 __device__ __forceinline__ float coarse_inv(int c) { return 1.0f / (float)(1 << c); }
@@ -298,8 +317,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT) void k_scan(DecPlan p) {
     const float x = bf16_to_f32(q_s[hh * kD + i]), y = bf16_to_f32(q_s[hh * kD + i + kD / 2]);
     const float scale = p.attn_scale * kLog2e;
     float* dst = p.qrope + ((size_t)pair * G + hh) * kD;
-    dst[i] = (x * c - y * sn) * scale;
-    dst[i + kD / 2] = (y * c + x * sn) * scale;
+    rope_rotate(x, y, c, sn, scale, dst[i], dst[i + kD / 2]);
   }
 
   uint4 bq[3][S::CH];
@@ -842,15 +860,14 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   __shared__ unsigned long long gb[G][kNB];
   __shared__ double ms[G][kNB];
   __shared__ float mk_s[kMaxGroups][G];
-  __shared__ double zk_s[kMaxGroups][G];
   __shared__ float gm_s[G];
   __shared__ double gz_s[G];
   __shared__ int kb_s[G], mode_s[G];
-  __shared__ float inv_s[G];
   __shared__ int relevant, flag_s;
   __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
+  __shared__ float qs_keep[G * kD];
 
   // ---- scan: projection, queries and the index tile requested together
   uint4 wreg[WQ_PER];
@@ -907,7 +924,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
     rope_sincos(p.N - 1, th, sn, c);
     const float x = bf16_to_f32(q_s[hh * kD + i]), y = bf16_to_f32(q_s[hh * kD + i + kD / 2]);
     const float scale = p.attn_scale * kLog2e;
-    const float r0 = (x * c - y * sn) * scale, r1 = (y * c + x * sn) * scale;
+    float r0, r1;
+    rope_rotate(x, y, c, sn, scale, r0, r1);
     sm.qs[hh][i] = r0;
     sm.qs[hh][i + kD / 2] = r1;
     if (blk == 0) {
@@ -1014,31 +1032,24 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
         w[u] = ld_dev((const unsigned long long*)(p.blk_bins + sk * kNB) + jp);
       }
     }
-    if (tid < nin * G) {
-      const size_t sk = ((size_t)pair * p.nA + g0) * G + tid;
-      mk = ld_dev(&p.blk_m[sk]);
-      zk = (double)ld_dev(&p.blk_z[sk]) / kFxZ;
-    }
-    // the group's max per q-head, each summary's shift, the group's mass
-    if (tid < nin * G) mk_s[tid / G][tid % G] = mk;
-    __syncthreads();
-    if (tid < G) {
-      float gm = -INFINITY;
-      for (int k = 0; k < nin; ++k) gm = fmaxf(gm, mk_s[k][tid]);
-      gm_s[tid] = gm;
-    }
-    __syncthreads();
-    // each summary's mass moved onto the group's grid by its own thread (one exp
-    // each), then added in a fixed order
-    if (tid < nin * G)
-      zk_s[tid / G][tid % G] =
-          zk * exp((double)(score_key(mk, kInvDelta) - score_key(gm_s[tid % G], kInvDelta)) *
-                   (double)kDelta);
-    __syncthreads();
-    if (tid < G) {
-      double gz = 0.0;
-      for (int k = 0; k < nin; ++k) gz += zk_s[k][tid];
-      gz_s[tid] = gz;
+    // wave hh, lane k: summary k's max and mass for q-head hh; the group's max and its
+    // mass (each summary moved onto the group's grid by one exp, then a fixed butterfly)
+    if (wave < G) {
+      if (lane < nin) {
+        const size_t sk = ((size_t)pair * p.nA + g0 + lane) * G + wave;
+        mk = ld_dev(&p.blk_m[sk]);
+        zk = (double)ld_dev(&p.blk_z[sk]) / kFxZ;
+      }
+      const float gm = wave_max(mk);
+      double zt = lane < nin ? zk * exp((double)(score_key(mk, kInvDelta) -
+                                                 score_key(gm, kInvDelta)) * (double)kDelta)
+                             : 0.0;
+      zt = wave_sum_d(zt);
+      if (lane < nin) mk_s[lane][wave] = mk;
+      if (lane == 0) {
+        gm_s[wave] = gm;
+        gz_s[wave] = zt;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -1066,38 +1077,34 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
       }
     }
     if (arrive_last(&p.cnt_pair[pair], (unsigned)p.nGrp)) {
-      constexpr int PER2 = 8;  // group bins per thread and round
+      constexpr int PER2 = (32 * G * kNB + NT - 1) / NT;  // group bins per thread and round
       const int n_bins = p.nGrp * G * kNB;
-      float mg = -INFINITY;
-      double zg = 0.0;
-      if (tid < p.nGrp * G) {
-        const size_t sg = (size_t)pair * p.nGrp * G + tid;
-        mg = ld_dev(&p.grp_m[sg]);
-        zg = __longlong_as_double((long long)ld_dev((const unsigned long long*)&p.grp_z[sg]));
-      }
       unsigned long long v[PER2];
 #pragma unroll
       for (int u = 0; u < PER2; ++u) {
         const int e = tid + u * NT;
         v[u] = e < n_bins ? ld_dev(&p.grp_bins[(size_t)pair * p.nGrp * G * kNB + e]) : 0ull;
       }
-      if (tid < p.nGrp * G) mk_s[tid / G][tid % G] = mg;
-      __syncthreads();
-      if (tid < G) {
-        float m = -INFINITY;
-        for (int k = 0; k < p.nGrp; ++k) m = fmaxf(m, mk_s[k][tid]);
-        gm_s[tid] = m;
-      }
-      __syncthreads();
-      if (tid < p.nGrp * G)
-        zk_s[tid / G][tid % G] =
-            zg * exp((double)(score_key(mg, kInvDelta) + 1) * (double)kDelta -
-                     (double)gm_s[tid % G]);
-      __syncthreads();
-      if (tid < G) {
-        double Z = 0.0;
-        for (int k = 0; k < p.nGrp; ++k) Z += zk_s[k][tid];
-        gz_s[tid] = Z;
+      // wave hh, lane k: group k's max and mass for q-head hh; the pair's max and Z
+      static_assert(kMaxGroups <= 64, "one lane per group");
+      if (wave < G) {
+        float mg = -INFINITY;
+        double zg = 0.0;
+        if (lane < p.nGrp) {
+          const size_t sg = ((size_t)pair * p.nGrp + lane) * G + wave;
+          mg = ld_dev(&p.grp_m[sg]);
+          zg = __longlong_as_double((long long)ld_dev((const unsigned long long*)&p.grp_z[sg]));
+        }
+        const float m = wave_max(mg);
+        double zt = lane < p.nGrp
+                        ? zg * exp((double)(score_key(mg, kInvDelta) + 1) * (double)kDelta - (double)m)
+                        : 0.0;
+        zt = wave_sum_d(zt);
+        if (lane < p.nGrp) mk_s[lane][wave] = mg;
+        if (lane == 0) {
+          gm_s[wave] = m;
+          gz_s[wave] = zt;
+        }
       }
       __syncthreads();
       auto add_bins = [&](const unsigned long long (&vv)[PER2], int base) {
@@ -1128,26 +1135,31 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
                     exp((double)(kt - j + 1) * (double)kDelta - (double)gm_s[hh]);
       }
       __syncthreads();
-      if (tid < G) {
-        // the boundary bin: where the running mass reaches p * Z (the threshold
-        // kernel's search over the same bins)
-        const float m = gm_s[tid];
-        const double Z = gz_s[tid];
+      if (wave < G) {
+        // the boundary bin of q-head hh: the first bin (highest first) at which the
+        // running mass reaches p * Z; lane j holds the running mass through bin j
+        // (a fixed-order scan)
+        const int hh = wave;
+        const float m = gm_s[hh];
+        const double Z = gz_s[hh];
         const int kt = score_key(m, kInvDelta);
+        double run = lane < kNB ? ms[hh][lane] : 0.0;
+#pragma unroll
+        for (int o = 1; o < kNB; o <<= 1) {
+          const double u = __shfl_up(run, o, 64);
+          if (lane >= o) run += u;
+        }
         int mode = 2, key_bnd = INT_MIN;
         double above = Z, need = 0.0;
         if (p.top_p < 1.0f) {
           const double target = (double)p.top_p * Z;
-          double cum = 0.0;
-          int g = 0;
-          for (; g < kNB; ++g) {
-            if (cum + ms[tid][g] >= target) break;
-            cum += ms[tid][g];
-          }
+          const unsigned long long hit = __ballot(lane < kNB && run >= target);
+          const int g = hit ? __ffsll((long long)hit) - 1 : kNB;
+          const double before = __shfl(run, g > 0 ? g - 1 : 0, 64);
           mode = g < kNB ? 0 : 1;
           key_bnd = g < kNB ? kt - g : kt - kNB;
-          above = cum;
-          need = target - cum;
+          above = g > 0 ? before : 0.0;
+          need = target - above;
         }
         ThrInfo t;
         t.key_top = kt;
@@ -1160,49 +1172,70 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
         t.tau = -INFINITY;
         t.n_cand = 0;
         t.inv_w = kInvDelta;
-        p.thr[pair * G + tid] = t;  // read by the finish kernel (a later launch)
-        kb_s[tid] = key_bnd;
-        mode_s[tid] = mode;
+        if (lane == 0) {
+          p.thr[pair * G + hh] = t;  // read by the finish kernel (a later launch)
+          kb_s[hh] = key_bnd;
+          mode_s[hh] = mode;
+        }
       }
       if (tid == 0) st_dev(&p.uni_cnt[pair], 0u);
       __syncthreads();
       // every block's mailbox: one 64-bit word per q-head, its boundary key in the low
       // half, its mode in bits 32-33 and bit 63 set: a word is whole or absent
-      for (int k = tid; k < p.nA; k += NT) {
-        unsigned long long* mb = p.mbox + ((size_t)pair * p.nA + k) * kMboxWords;
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-          st_dev(&mb[hh], (1ull << 63) | ((unsigned long long)mode_s[hh] << 32) |
-                              (unsigned long long)(unsigned)kb_s[hh]);
+      // consecutive threads write consecutive words, so each store instruction covers
+      // whole mailboxes (full lines)
+      {
+        unsigned long long* mb = p.mbox + (size_t)pair * p.nA * kMboxWords;
+        const int n_words = p.nA * kMboxWords;
+        for (int e = tid; e < n_words; e += NT) {
+          const int hh = e % kMboxWords;
+          if (hh < G)
+            st_dev(&mb[e], (1ull << 63) | ((unsigned long long)mode_s[hh] << 32) |
+                               (unsigned long long)(unsigned)kb_s[hh]);
+        }
       }
     }
   }
-  // ---- wait for this block's mailbox: every q-head's word present, then clear them
+  // ---- local heads of a decode step: this block's window segments, run while the
+  // threshold is being found (the retrieval queries wait aside in LDS meanwhile)
+  if (p.with_swa) {
+    const int n_items = p.B * p.sw.n_loc * p.sw.nSeg;
+    int it = pair * p.nA + blk;
+    if (it < n_items) {
+      __syncthreads();
+      for (int e = tid; e < G * kD; e += NT) qs_keep[e] = (&sm.qs[0][0])[e];
+      __syncthreads();
+      for (; it < n_items; it += p.P * p.nA)
+        swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
+      __syncthreads();
+      for (int e = tid; e < G * kD; e += NT) (&sm.qs[0][0])[e] = qs_keep[e];
+    }
+  }
+  // ---- wait for this block's mailbox: every q-head's word present, then clear them.
+  // Lane hh of wave 0 polls word hh (one load instruction per poll).
   __syncthreads();
-  if (tid == 0) {
+  if (wave == 0) {
     unsigned long long* mb = p.mbox + ((size_t)pair * p.nA + blk) * kMboxWords;
-    unsigned long long wv[G];
+    const unsigned long long want = (1ull << G) - 1ull;
+    unsigned long long wv = 0ull;
     bool all = false;
     for (unsigned it = 0; it < kSpinLimit && !all; ++it) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) wv[hh] = ld_dev(&mb[hh]);
-      all = true;
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) all = all && (wv[hh] >> 63);
+      if (lane < G) wv = ld_dev(&mb[lane]);
+      all = (__ballot(lane < G && (wv >> 63)) & want) == want;
       if (!all) __builtin_amdgcn_s_sleep(2);
     }
     if (!all) {
-      st_dev(p.err, 1u);
-      flag_s = 0;
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        kb_s[hh] = (int)(unsigned)wv[hh];
-        mode_s[hh] = (int)((wv[hh] >> 32) & 3ull);
-        inv_s[hh] = kInvDelta;
-        st_dev(&mb[hh], 0ull);
+      if (lane == 0) {
+        st_dev(p.err, 1u);
+        flag_s = 0;
       }
-      flag_s = 1;
+    } else {
+      if (lane < G) {
+        kb_s[lane] = (int)(unsigned)wv;
+        mode_s[lane] = (int)((wv >> 32) & 3ull);
+        st_dev(&mb[lane], 0ull);
+      }
+      if (lane == 0) flag_s = 1;
     }
   }
   __syncthreads();
@@ -1213,9 +1246,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   } else {
     // ---- select: classify the registered scores against the boundary bins
     if (tid == 0) relevant = (blk == 0 && p.n_sink > 0) ? 1 : 0;
-    for (int e = tid; e < kPassTokens; e += NT) dmask[e] = cmask[e] = 0u;
     __syncthreads();
-    if (tid < G && (mode_s[tid] != 0 || score_key(mb_s[tid], inv_s[tid]) >= kb_s[tid]))
+    if (tid < G && (mode_s[tid] != 0 || score_key(mb_s[tid], kInvDelta) >= kb_s[tid]))
       atomicOr(&relevant, 1);
     __syncthreads();
     if (!relevant && tid < G) p.cand_blk[((size_t)pair * G + tid) * p.nA + blk] = 0u;
@@ -1223,41 +1255,41 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
       const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
       const bool inspect = p.dbg_cnt || p.dbg_idx || p.dbg_union;
       const int mode = mode_s[hs], kbnd = kb_s[hs];
-      const float inv = inv_s[hs];
-      const int dthr = mode == 2 ? INT_MIN : kbnd;
-      const int clo = mode == 0 ? kbnd : INT_MIN;
-      const bool full = G >= 4 && tok0 + kPassTokens <= p.N;
-      // Each lane's keys as two bit masks (definite, candidate) without branches;
-      // the definite heads then go to the per-token masks only for the elements that
-      // some lane of the wave has definite.
-      static_assert(S::TPW * 4 <= 32, "one mask bit per element");
-      uint32_t dbits = 0u, cbits = 0u;
+      // On the fine grid 2 s is exact, so key(s) > k <=> 2 s >= k + 1 and key(s) >= k
+      // <=> 2 s >= k: each test is one fp32 comparison against the bound rounded up
+      // (keys clamp at +-1e9, hence the ends).  Scores of absent tokens are -inf and
+      // never pass; in mode 2 every present score is definite.
+      static_assert(kInvDelta == 2.0f && kDelta == 0.5f, "the fine grid has bins of 1/2");
+      float dthr_f = -FLT_MAX, clo_f = FLT_MAX;
+      if (mode != 2) {
+        dthr_f = kbnd >= 1000000000 ? INFINITY : __int2float_ru(kbnd + 1) * kDelta;
+        clo_f = (mode != 0 || kbnd <= -1000000000) ? -FLT_MAX : __int2float_ru(kbnd) * kDelta;
+      }
+      // A token's heads sit in S::GE consecutive lanes: the ballot of a test, shifted to
+      // the token's first lane, is the token's head mask, stored (one byte per token) by
+      // that lane.  Every token of the block is stored once, so nothing is cleared.
+      static_assert(S::TPW * 4 <= 32, "one candidate bit per element");
+      static_assert(G <= 8 && 64 % S::GE == 0, "a head mask fits a byte");
+      uint8_t* const dm8 = reinterpret_cast<uint8_t*>(dmask);
+      uint8_t* const cm8 = reinterpret_cast<uint8_t*>(cmask);
+      const unsigned hm = (1u << G) - 1u;
+      const int first = lane - h;
+      uint32_t cbits = 0u;
 #pragma unroll
       for (int T = 0; T < S::TPW; ++T)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool valid = full || (hv && tok0 + score_token<G>(T, r) < p.N);
-          const int key = score_key(sc[T][r], inv);
-          dbits |= (uint32_t)(valid && key > dthr) << (4 * T + r);
-          cbits |= (uint32_t)(valid && key <= dthr && key >= clo) << (4 * T + r);
-        }
-      const unsigned ccount = (unsigned)__popc(cbits);
-#pragma unroll
-      for (int T = 0; T < S::TPW; ++T)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool d = (dbits >> (4 * T + r)) & 1u;
-          if (__ballot(d) != 0ull) {  // wave-uniform: skipped where no lane has one
-            if (d) atomicOr(&dmask[score_token<G>(T, r)], 1u << h);
+          const float sv = sc[T][r];
+          const unsigned long long bd = __ballot(sv >= dthr_f);
+          const bool c = sv < dthr_f && sv >= clo_f;
+          cbits |= (uint32_t)c << (4 * T + r);
+          if (h == 0) dm8[score_token<G>(T, r)] = (uint8_t)((unsigned)(bd >> first) & hm);
+          if (inspect) {
+            const unsigned long long bc = __ballot(c);
+            if (h == 0) cm8[score_token<G>(T, r)] = (uint8_t)((unsigned)(bc >> first) & hm);
           }
         }
-      if (inspect) {
-#pragma unroll
-        for (int T = 0; T < S::TPW; ++T)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if ((cbits >> (4 * T + r)) & 1u) atomicOr(&cmask[score_token<G>(T, r)], 1u << h);
-      }
+      const unsigned ccount = (unsigned)__popc(cbits);
       unsigned inc = ccount;
 #pragma unroll
       for (int o = S::GE; o < 64; o <<= 1) {
@@ -1288,7 +1320,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int t = tok0 + k * NT + tid;
-        dm[k] = dmask[k * NT + tid];
+        dm[k] = dm8[k * NT + tid];
         if (t < p.N && t < p.n_sink) dm[k] = (1u << G) - 1u;
         cnt += dm[k] ? 1u : 0u;
       }
@@ -1306,7 +1338,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
         unsigned uc = 0u;
 #pragma unroll
         for (int k = 0; k < TPT; ++k) {
-          cm[k] = cmask[k * NT + tid];
+          cm[k] = cm8[k * NT + tid];
           uc += (dm[k] | cm[k]) ? 1u : 0u;
         }
         if (tid == 0) ucount_s = 0u;
@@ -1529,6 +1561,26 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   const float2* cand = p.cand + (size_t)unit * p.N;
   static_assert(kD <= NT, "one query dimension per thread");
   const float qv = tid < kD ? p.qrope[(size_t)unit * kD + tid] : 0.f;
+  // this block's share of the index pass's partial states, folded in at the end; the
+  // first kFinPB are requested now, with the threshold state
+  const int pb_lo = (int)(((long long)p.nA * f) / p.nF);
+  const int pb_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
+  float pbm[kFinPB], pbl[kFinPB];
+  float2 pbo[kFinPB];
+  if (wave == 0) {
+#pragma unroll
+    for (int u = 0; u < kFinPB; ++u) {
+      pbm[u] = -INFINITY;
+      pbl[u] = 0.f;
+      pbo[u] = make_float2(0.f, 0.f);
+      if (pb_lo + u < pb_hi) {
+        const float* q = p.partB + ((size_t)unit * p.nA + pb_lo + u) * kPartStride;
+        pbm[u] = q[0];
+        pbl[u] = q[1];
+        pbo[u] = *(const float2*)&q[4 + 2 * lane];
+      }
+    }
+  }
   // candidate counts of the pass-B blocks and their exclusive prefix (fixed order);
   // the counts are loaded together with the threshold state and the query (one
   // round trip)
@@ -1707,12 +1759,38 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     }
   }
   if (wave == 0) {
-    float* dst = p.partF + ((size_t)unit * p.nF + f) * kPartStride;
+    // the block's state: its share of the index pass's partials in order, then its
+    // candidates
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < kFinPB; ++u) fold_state(M, L, A0, A1, pbm[u], pbl[u], pbo[u].x, pbo[u].y);
+    if (pb_hi - pb_lo > kFinPB)
+      merge_partials_wave(p.partB + ((size_t)unit * p.nA + pb_lo + kFinPB) * kPartStride,
+                          pb_hi - pb_lo - kFinPB, M, L, A0, A1);
+    fold_state(M, L, A0, A1, m, l, o0, o1);
+    store_partial(p.partF + ((size_t)unit * p.nF + f) * kPartStride, M, L, A0, A1);
+  }
+  if (!p.fold_merge) return;
+  // the last of the head's finish blocks combines their states (wave w folds a quarter
+  // of them in order, then wave 0 the quarters in order) and writes the bf16 output
+  if (!arrive_last(&p.cnt_fin[unit], (unsigned)p.nF)) return;
+  __shared__ float qm[NT / 64], ql[NT / 64];
+  __shared__ float2 qo[NT / 64][64];
+  {
+    const int w0 = (p.nF * wave) / (NT / 64), w1 = (p.nF * (wave + 1)) / (NT / 64);
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    merge_partials_wave(p.partF + ((size_t)unit * p.nF + w0) * kPartStride, w1 - w0, M, L, A0, A1);
     if (lane == 0) {
-      dst[0] = m;
-      dst[1] = l;
+      qm[wave] = M;
+      ql[wave] = L;
     }
-    *(float2*)&dst[4 + 2 * lane] = make_float2(o0, o1);
+    qo[wave][lane] = make_float2(A0, A1);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int q = 0; q < NT / 64; ++q) fold_state(M, L, A0, A1, qm[q], ql[q], qo[q][lane].x, qo[q][lane].y);
+    store_output(p.out + ((size_t)b * p.Hq + qh) * kD, L, A0, A1);
   }
 }
 
@@ -1890,11 +1968,22 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
     RTP_LAUNCH(k_threshold<G>, dim3(p.P * G), dim3(kThrThreads), s, p);
     mark(2);
     RTP_LAUNCH(k_select<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+    // the local heads of a decode step, which the fused pass runs inside
+    if (p.with_swa) {
+      const hipError_t e = launch_swa_decode(p.sw, s);
+      if (e != hipSuccess) return e;
+    }
   }
   mark(3);
   RTP_LAUNCH(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), s, p);
   mark(4);
-  RTP_LAUNCH(k_merge, dim3(p.P * G, kD / kMergeDims), dim3(kMergeThreads), s, p);
+  if (!p.fold_merge) {
+    // the finish states already hold the index pass's partials
+    DecPlan m = p;
+    m.nA = 0;
+    m.partB = p.partF;
+    RTP_LAUNCH(k_merge, dim3(p.P * G, kD / kMergeDims), dim3(kMergeThreads), s, m);
+  }
   mark(5);
   if (p.dbg_cnt || p.dbg_idx || p.dbg_tau || p.dbg_union)
     RTP_LAUNCH(k_debug_sets<G>, dim3(p.P * G), dim3(256), s, p);
@@ -1918,7 +2007,8 @@ hipError_t launch_decode(const DecPlan& p, hipStream_t s) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base) {
+size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base, int n_loc,
+                        int swa_rows) {
   const int P = B * n_ret;
   const int nA = (N + kPassTokens - 1) / kPassTokens;
   // Every finish block resolves its head's threshold (the candidate buffer allows one
@@ -1929,9 +2019,29 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   // grid y of the index passes is P, of the finish kernel P * G
   if ((long long)P * G > kMaxGridY) return 0;
   const int nGrp = (nA + kGroupBlocks - 1) / kGroupBlocks;
-  // the fused pass's counters and mailboxes live in the counter region (zero at rest);
-  // the last word is the give-up flag
-  const size_t n_cnt = ((size_t)P * nGrp + P + 2 * kMboxWords - 1) / (2 * kMboxWords) * (2 * kMboxWords);
+  // Local heads of a decode step (n_loc > 0): segments of their windows, sized so that
+  // every block of the fused pass runs about one (several when the local heads
+  // outnumber the blocks); the group merges as in the local-head decode kernel.
+  const int units = B * n_loc;
+  int sSeg = 0, sRows = 0, sGsz = 0, sGrp = 0;
+  if (units > 0 && swa_rows > 0) {
+    const long long blocks = (long long)P * nA;
+    sSeg = (int)std::max(1LL, blocks / units);
+    sSeg = std::min(sSeg, (swa_rows + kTileRows - 1) / kTileRows);
+    sRows = (swa_rows + sSeg - 1) / sSeg;
+    sRows = (sRows + kTileRows - 1) / kTileRows * kTileRows;
+    sSeg = (swa_rows + sRows - 1) / sRows;
+    sGsz = 4;
+    while (sGsz * sGsz < sSeg) ++sGsz;
+    sGrp = (sSeg + sGsz - 1) / sGsz;
+  }
+  // the counters (fused pass, finish arrivals, local-head merges) and the fused pass's
+  // mailboxes live in the counter region (zero at rest); the last word is the give-up flag
+  const size_t n_cnt_ret = (size_t)P * nGrp + P + (size_t)P * G;
+  const size_t n_cnt0 = n_cnt_ret + (size_t)units * (sGrp + 1);
+  if (sSeg > 0 && (n_cnt0 + 1) * sizeof(unsigned) > kCounterBytes) return 0;
+  const bool fold_merge = (n_cnt0 + 1) * sizeof(unsigned) <= kCounterBytes;
+  const size_t n_cnt = (n_cnt0 + 2 * kMboxWords - 1) / (2 * kMboxWords) * (2 * kMboxWords);
   const size_t n_words = n_cnt + (size_t)P * nA * kMboxWords * 2 + 1;
   const bool fusable = nGrp <= kMaxGroups && n_words * sizeof(unsigned) <= kCounterBytes;
   size_t off = kCounterBytes;
@@ -1956,12 +2066,28 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   char* gm = take(fusable ? (size_t)P * nGrp * G * 4 : 0);
   char* gz = take(fusable ? (size_t)P * nGrp * G * 8 : 0);
   char* gbn = take(fusable ? (size_t)P * nGrp * G * kNB * 8 : 0);
+  char* sp = take((size_t)units * G * sSeg * kPartStride * 4);
+  char* spg = take((size_t)units * G * sGrp * kPartStride * 4);
   if (plan) {
+    plan->with_swa = sSeg > 0;
+    if (sSeg > 0) {
+      unsigned* cnt = (unsigned*)base + n_cnt_ret;
+      plan->sw.nSeg = sSeg;
+      plan->sw.segRows = sRows;
+      plan->sw.gsz = sGsz;
+      plan->sw.nGrp = sGrp;
+      plan->sw.cnt_grp = cnt;
+      plan->sw.cnt_top = cnt + (size_t)units * sGrp;
+      plan->sw.part = (float*)sp;
+      plan->sw.partg = (float*)spg;
+    }
     plan->fusable = fusable;
     plan->nGrp = nGrp;
     unsigned* cnt = (unsigned*)base;
     plan->cnt_grp = cnt;
     plan->cnt_pair = cnt + (size_t)P * nGrp;
+    plan->cnt_fin = cnt + (size_t)P * nGrp + P;
+    plan->fold_merge = fold_merge;
     plan->mbox = (unsigned long long*)(cnt + n_cnt);
     plan->err = (unsigned*)(base + kDecodeErrOffset);
     plan->grp_m = (float*)gm;

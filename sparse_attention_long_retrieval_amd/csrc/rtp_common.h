@@ -29,6 +29,16 @@ __device__ __forceinline__ void rope_sincos(int pos, double theta, float& sn, fl
   cs = __builtin_amdgcn_cosf(f);
 }
 
+// Rotate the pair (x, y) by the angle with cosine c and sine s, then scale.  Each
+// operation rounds on its own (no contraction into fma), so every kernel that
+// rotates a query gets the same bits.
+__device__ __forceinline__ void rope_rotate(float x, float y, float c, float s, float scale,
+                                            float& r0, float& r1) {
+#pragma clang fp contract(off)
+  r0 = (x * c - y * s) * scale;
+  r1 = (y * c + x * s) * scale;
+}
+
 // fp32 -> bf16, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);

@@ -48,6 +48,44 @@ constexpr size_t kCounterBytes = 65536;
 constexpr size_t kDecodeErrOffset = kCounterBytes - 4;
 static_assert(kDecodeErrOffset == RTP_DECODE_ERROR_OFFSET, "header and library agree");
 
+// Where token j of a (batch, KV head) lives.  ring_len == 0: row j of the full
+// cache, heads max_seq rows apart.  ring_len > 0: a local-head ring of n_sink sink
+// rows followed by ring_len window rows (token j >= n_sink at n_sink + (j - n_sink)
+// mod ring_len), local heads only and compact ([B][n_loc][n_sink + ring_len]).
+struct RowMap {
+  int ring_len;
+  int n_sink;
+  int head_rows;  // rows per (batch, head) slab
+  __host__ __device__ int row(int j) const {
+    return (ring_len == 0 || j < n_sink) ? j : n_sink + (j - n_sink) % ring_len;
+  }
+  // first row of the slab of batch b, KV head kv (local index li)
+  __host__ __device__ size_t slab(int b, int kv, int li, int Hkv, int n_loc) const {
+    return (size_t)(ring_len ? b * n_loc + li : b * Hkv + kv) * (size_t)head_rows;
+  }
+};
+
+struct SwaPlan {
+  const uint16_t* q_pre;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  uint16_t* out;
+  int B, Hq, Hkv, G, max_seq, n_sink, window;
+  RowMap map;
+  int n_loc;
+  int loc_kv[kMaxKv];
+  float attn_scale;
+  double theta[kD / 2];
+  int q_start, Tq;
+  int nSeg;      // segments per (b, local kv head)
+  int segRows;   // rows per segment (multiple of 64)
+  int gsz, nGrp;
+  unsigned* cnt_grp;  // [B*n_loc][nGrp]   (counter region)
+  unsigned* cnt_top;  // [B*n_loc]
+  float* part;        // [B*n_loc*G][nSeg][kPartStride]
+  float* partg;       // [B*n_loc*G][nGrp][kPartStride]
+};
+
 // Threshold state of one (pair, q-head).
 struct ThrInfo {
   int key_top;   // key of the global max score
@@ -102,6 +140,11 @@ struct DecPlan {
   int nGrp;                       // merge groups of kGroupBlocks blocks per pair
   unsigned* cnt_grp;              // [P][nGrp] blocks of the group done
   unsigned* cnt_pair;             // [P]       groups of the pair merged
+  unsigned* cnt_fin;              // [P*G]     finish blocks of the head done (when fold_merge)
+  int fold_merge;                 // the finish kernel's last block per head writes the output
+  // local heads run by the fused pass while it waits for the threshold (decode step)
+  int with_swa;
+  SwaPlan sw;
   unsigned long long* mbox;       // [P][nA][kMboxWords] per block and q-head: set bit 63,
                                   //           mode in bits 32-33, boundary key below
   unsigned* err;                  // [1]       a wait gave up (the call's results are void)
@@ -122,44 +165,6 @@ struct DecPlan {
 constexpr int kGroupBlocks = 16;
 constexpr int kMaxGroups = 64;
 constexpr int kMboxWords = 8;   // a block's mailbox: one 64-bit word per q-head (G <= 8)
-
-// Where token j of a (batch, KV head) lives.  ring_len == 0: row j of the full
-// cache, heads max_seq rows apart.  ring_len > 0: a local-head ring of n_sink sink
-// rows followed by ring_len window rows (token j >= n_sink at n_sink + (j - n_sink)
-// mod ring_len), local heads only and compact ([B][n_loc][n_sink + ring_len]).
-struct RowMap {
-  int ring_len;
-  int n_sink;
-  int head_rows;  // rows per (batch, head) slab
-  __host__ __device__ int row(int j) const {
-    return (ring_len == 0 || j < n_sink) ? j : n_sink + (j - n_sink) % ring_len;
-  }
-  // first row of the slab of batch b, KV head kv (local index li)
-  __host__ __device__ size_t slab(int b, int kv, int li, int Hkv, int n_loc) const {
-    return (size_t)(ring_len ? b * n_loc + li : b * Hkv + kv) * (size_t)head_rows;
-  }
-};
-
-struct SwaPlan {
-  const uint16_t* q_pre;
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
-  uint16_t* out;
-  int B, Hq, Hkv, G, max_seq, n_sink, window;
-  RowMap map;
-  int n_loc;
-  int loc_kv[kMaxKv];
-  float attn_scale;
-  double theta[kD / 2];
-  int q_start, Tq;
-  int nSeg;      // segments per (b, local kv head)
-  int segRows;   // rows per segment (multiple of 64)
-  int gsz, nGrp;
-  unsigned* cnt_grp;  // [B*n_loc][nGrp]   (counter region)
-  unsigned* cnt_top;  // [B*n_loc]
-  float* part;        // [B*n_loc*G][nSeg][kPartStride]
-  float* partg;       // [B*n_loc*G][nGrp][kPartStride]
-};
 
 struct AppendPlan {
   const uint16_t* k_pre;
@@ -302,7 +307,8 @@ struct ClDecPlan {
 
 // Workspace sizing (bytes).  Returns 0 when the shape cannot be launched (a grid
 // extent above kMaxGridY, or counters beyond the counter region).
-size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base);
+size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* base,
+                        int n_loc = 0, int swa_rows = 0);
 size_t cluster_build_workspace(int P, int K, int n_tok, ClBuildPlan* plan, char* base);
 size_t cluster_decode_workspace(int P, int G, int K, ClDecPlan* plan, char* base);
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base);

@@ -10,64 +10,14 @@
 #include "attn_tile.h"
 #include "rtp_common.h"
 #include "rtp_internal.h"
+#include "swa_segment.h"
 
 namespace rtp {
 
-constexpr float kLog2eS = 1.4426950408889634f;
-
-// Rows of a decode query at position pos: sinks before the window, then the window.
-__device__ __forceinline__ void swa_rows(int pos, int window, int n_sink, int* lo, int* ns_out,
-                                         int* L) {
-  *lo = max(0, pos - window + 1);
-  *ns_out = min(n_sink, *lo);
-  *L = *ns_out + (pos - *lo + 1);
-}
-
 template <int G>
 __global__ __launch_bounds__(64 * G) void k_swa_decode(SwaPlan p) {
-  constexpr int NT = 64 * G;
-  const int bl = blockIdx.y, seg = blockIdx.x;
-  const int b = bl / p.n_loc, li = bl % p.n_loc;
-  const int kv = p.loc_kv[li];
-  const int h = threadIdx.x >> 6;
   __shared__ TileSmem<G> sm;
-  const int pos = p.q_start;
-  int lo, ns_out, L;
-  swa_rows(pos, p.window, p.n_sink, &lo, &ns_out, &L);
-  const size_t head_base = p.map.slab(b, kv, li, p.Hkv, p.n_loc) * kD;
-  load_q_rope<G>(sm, p.q_pre + ((size_t)b * p.Hq + kv * G) * kD, kD, pos, p.theta,
-                 p.attn_scale * kLog2eS);
-  const int r0 = seg * p.segRows;
-  const int r1 = min(L, r0 + p.segRows);
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  // the segment's rows in tiles of 64, the next tile's K/V in flight while the current
-  // one is computed; window row v is sink v (v < ns_out) or token lo + v - ns_out
-  __syncthreads();  // the rotated queries are in sm.qs
-  attend_list<G, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, max(0, r1 - r0),
-                     [&](int i) {
-                       const int v = r0 + i;
-                       return RowMask{p.map.row(v < ns_out ? v : lo + (v - ns_out)),
-                                      0xffffffffu};
-                     },
-                     m, l, o0, o1);
-  const size_t unit = (size_t)bl * G + h;
-  store_partial(p.part + (unit * p.nSeg + seg) * kPartStride, m, l, o0, o1);
-
-  const int grp = seg / p.gsz;
-  const int s0 = grp * p.gsz;
-  const int nin = min(p.gsz, p.nSeg - s0);
-  if (!arrive_last(&p.cnt_grp[bl * p.nGrp + grp], (unsigned)nin)) return;
-  {
-    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
-    merge_partials_wave(p.part + (unit * p.nSeg + s0) * kPartStride, nin, gm, gl, g0, g1);
-    store_partial(p.partg + (unit * p.nGrp + grp) * kPartStride, gm, gl, g0, g1);
-  }
-  if (!arrive_last(&p.cnt_top[bl], (unsigned)p.nGrp)) return;
-  {
-    float gm = -INFINITY, gl = 0.f, g0 = 0.f, g1 = 0.f;
-    merge_partials_wave(p.partg + unit * p.nGrp * kPartStride, p.nGrp, gm, gl, g0, g1);
-    store_output(p.out + ((size_t)b * p.Hq + kv * G + h) * kD, gl, g0, g1);
-  }
+  swa_decode_segment<G, 64 * G>(p, sm, blockIdx.y, blockIdx.x);
 }
 
 template <int G>
