@@ -1,9 +1,10 @@
 """Benchmark of the head-wise sparse attention step on one MI355X.
 
 One decode step = the whole decode hot path of one layer over one batch: append of
-the newest token (K/V caches + 16-dim index), the retrieval-head decode (indexer scan
-+ histogram, threshold, select, resolve, gather attention, merge) and the local-head
-sliding-window attention (on a second stream).
+the newest token (K/V caches + 16-dim index), then one rtp_decode_step call: the
+retrieval heads (indexer scan + histogram, threshold, select, resolve, gather
+attention) and the local heads (sliding window + sinks), whose window segments the
+fused index pass attends while it waits for its threshold.
 
 Headline workload: 1M-context decode shaped like Qwen3-30B-A3B attention (B=1, 32 q /
 4 KV heads, KV head 0 retrieval with a 1M x 16 index, 3 SWA heads with window 8192 + 4
@@ -19,9 +20,12 @@ from the 256 MB Infinity Cache and the L2s, so each step reads its bytes from HB
 HIP events on the step's stream bracket each step (flush excluded).  A read flush
 leaves clean lines; a write flush would leave dirty lines whose write-back lands in
 the next kernel.  A second series of at least 200 steps gives the median, p10 and
-p90; a third records the library's phase events for per-kernel durations (each
-event adds a few microseconds to the phase it closes).  The CPU oracle is timed on a
-bounded sample on the host cores (N=1 only).
+p90.  The parts of the step are also timed alone, cold (append; the retrieval decode
+and the local heads as separate calls; the step as three calls on two streams), next
+to an empty event pair, which is what a timing event pair costs by itself; a last
+series records the library's phase events for the fused pass and the finish kernel
+(each event adds a few microseconds to the phase it closes).  The CPU oracle is
+timed on a bounded sample on the host cores (N=1 only).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -42,8 +46,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_VALU_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "sparse_attention_long_retrieval_amd", "csrc")
-# Sources that define the scan kernel; its counter summary is void once they change.
-SCAN_SOURCES = ("decode.hip", "rtp_common.h", "rtp_internal.h", "attn_tile.h")
+# Sources that define the fused pass; its counter summary is void once they change.
+PASS_SOURCES = ("decode.hip", "rtp_common.h", "rtp_internal.h", "attn_tile.h", "swa_segment.h")
 CALIB_BYTES = 256 << 20   # plain device copy run once per bench for counter calibration
 
 
@@ -57,13 +61,13 @@ def source_digest(names) -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per scan launch from the committed counter summary, or None.
+    """HBM bytes per fused-pass launch from the committed counter summary, or None.
 
-    The summary (profiles/traffic_k_scan_<workload>.txt) holds the FETCH_SIZE and
-    WRITE_SIZE readings of the scan kernel already scaled by the plain-copy
+    The summary (profiles/traffic_k_pass_<workload>.txt) holds the FETCH_SIZE and
+    WRITE_SIZE readings of the pass kernel already scaled by the plain-copy
     calibration, and the digest of the sources it was taken on.
     """
-    path = os.path.join(ROOT, "profiles", f"traffic_k_scan_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_k_pass_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -72,7 +76,7 @@ def measured_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_digest") != source_digest(SCAN_SOURCES):
+    if kv.get("source_digest") != source_digest(PASS_SOURCES):
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))
@@ -161,10 +165,6 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true", help="prefill only (profiling)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the fixed-budget, ring-cache and cluster-index comparisons")
-    ap.add_argument("--serial-streams", action="store_true",
-                    help="run the decode step's local heads on the main stream too (clean "
-                         "per-kernel times under a profiler; the prefill step always runs on "
-                         "one stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode "
@@ -196,8 +196,8 @@ def main() -> int:
 
 class DecodeCtx:
     """A decode workload resident on the GPU: caches, index, queries, workspaces, and
-    the step (append of the newest token, retrieval decode, local heads on a second
-    stream).  ring=True keeps the local heads' K/V in rings of the window."""
+    the step (append of the newest token, then one rtp_decode_step call for every
+    q-head).  ring=True keeps the local heads' K/V in rings of the window."""
 
     def __init__(self, wl, args, ring: bool):
         import numpy as np
@@ -232,54 +232,74 @@ class DecodeCtx:
                           self.ring_len, self.k_ring, self.v_ring)
         del k_pre, v_pre
         self.out = torch.zeros((B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+        self.ws_step = torch.zeros(R.workspace_size(self.layer, R.OP_DECODE_STEP, N),
+                                   dtype=torch.uint8, device="cuda")
         self.ws = torch.zeros(R.workspace_size(self.layer, R.OP_DECODE, N), dtype=torch.uint8,
                               device="cuda")
         self.wss = torch.zeros(R.workspace_size(self.layer, R.OP_SWA, N), dtype=torch.uint8,
                                device="cuda")
         self.main_s = torch.cuda.current_stream()
-        self.side_s = self.main_s if args.serial_streams else torch.cuda.Stream()
+        self.side_s = torch.cuda.Stream()
         self.fork, self.join = torch.cuda.Event(), torch.cuda.Event()
         torch.cuda.synchronize()
 
-    def step(self, top_p, debug=None, marks=None, hip=None):
-        import torch
-        R, wl, N = self.R, self.wl, self.wl.N
-        cur = torch.cuda.current_stream()   # the capture stream while recording a graph
-        side = cur if self.args.serial_streams else self.side_s
-        if marks:
-            hip.record(marks[0], cur.cuda_stream)
-        R.index_append(self.layer, self.new_k, self.new_v, self.w_k, N - 1, self.k_cache,
-                       self.v_cache, self.index)
-        self.fork.record(cur)
-        # the retrieval decode is issued first: its kernels queue behind the append
-        # while the host issues the local heads on the side stream
-        R.decode_sparse_attn(self.layer, self.q, self.w_q, self.k_cache, self.v_cache,
-                             self.index, N, top_p, self.out, self.ws, debug=debug)
-        side.wait_event(self.fork)
-        if marks:
-            hip.record(marks[1], side.cuda_stream)
+    def append(self):
+        self.R.index_append(self.layer, self.new_k, self.new_v, self.w_k, self.wl.N - 1,
+                            self.k_cache, self.v_cache, self.index)
+
+    def decode_step(self, top_p, debug=None):
+        R, N = self.R, self.wl.N
+        if self.ring:
+            R.decode_step(self.layer, self.q, self.w_q, self.k_cache, self.v_cache, self.index,
+                          N, top_p, self.out, self.ws_step, ring_len=self.ring_len,
+                          k_ring=self.k_ring, v_ring=self.v_ring, debug=debug)
+        else:
+            R.decode_step(self.layer, self.q, self.w_q, self.k_cache, self.v_cache, self.index,
+                          N, top_p, self.out, self.ws_step, debug=debug)
+
+    def step(self, top_p, debug=None):
+        """The timed step: append, then the whole layer's decode in one call."""
+        self.append()
+        self.decode_step(top_p, debug=debug)
+
+    def retrieval(self, top_p):
+        self.R.decode_sparse_attn(self.layer, self.q, self.w_q, self.k_cache, self.v_cache,
+                                  self.index, self.wl.N, top_p, self.out, self.ws)
+
+    def local(self, stream=None):
+        R, N = self.R, self.wl.N
         if self.ring:
             R.swa_attn_ring(self.layer, self.q, N - 1, 1, self.ring_len, self.k_ring,
-                            self.v_ring, self.out, self.wss, stream=side)
+                            self.v_ring, self.out, self.wss, stream=stream)
         else:
             R.swa_attn(self.layer, self.q, N - 1, 1, self.k_cache, self.v_cache, self.out,
-                       self.wss, stream=side)
-        if marks:
-            hip.record(marks[2], side.cuda_stream)
-        self.join.record(side)
+                       self.wss, stream=stream)
+
+    def step_separate(self, top_p):
+        """The same step as three calls: append, retrieval decode, and the local heads on
+        a second stream beside the retrieval decode."""
+        import torch
+        cur = torch.cuda.current_stream()
+        self.append()
+        self.fork.record(cur)
+        self.retrieval(top_p)
+        self.side_s.wait_event(self.fork)
+        self.local(stream=self.side_s)
+        self.join.record(self.side_s)
         cur.wait_event(self.join)
 
     def measure(self, top_p, timer, hip, n_steps, n_dist, n_phase):
-        """Step times (K cold steps + a distribution series), phases, set sizes, bytes."""
+        """Step times (K cold steps + a distribution series), the parts alone, the
+        library's phases, set sizes, bytes."""
         import numpy as np
         import torch
         R, wl = self.R, self.wl
-        B, G, N = wl.B, wl.G, wl.N
+        B, N = wl.B, wl.N
         for _ in range(self.args.warmup):
             self.step(top_p)
         torch.cuda.synchronize()
         # one untimed step with the inspection outputs: set and union sizes
-        dbg_sets = R.Debug(B * wl.n_ret * G, 1, pairs=B * wl.n_ret)
+        dbg_sets = R.Debug(B * wl.n_ret * wl.G, 1, pairs=B * wl.n_ret)
         self.step(top_p, debug=dbg_sets)
         torch.cuda.synchronize()
         union = dbg_sets.union_count.cpu().numpy().astype(np.int64)
@@ -287,57 +307,61 @@ class DecodeCtx:
         del dbg_sets
         step_ms = timer.runs(lambda: self.step(top_p), n_steps)
         dist_ms = timer.runs(lambda: self.step(top_p), n_dist) if n_dist > n_steps else step_ms
-        # phases: the library's six events on its launch stream, plus the append and
-        # the local heads bracketed on their streams
+        med = lambda ms: round(float(np.median(ms)) * 1e3, 2)  # noqa: E731
+        # the parts alone (cold), and what an empty event pair costs
+        parts_us = {
+            "event_pair": med(timer.runs(lambda: None, n_phase)),
+            "append": med(timer.runs(self.append, n_phase)),
+            "decode_step": med(timer.runs(lambda: self.decode_step(top_p), n_phase)),
+            "retrieval_decode": med(timer.runs(lambda: self.retrieval(top_p), n_phase)),
+            "local_heads": med(timer.runs(self.local, n_phase)),
+            "step_as_three_calls": med(timer.runs(lambda: self.step_separate(top_p), n_phase)),
+        }
+        # phases inside the decode step: the library's events on its launch stream
         ph_ev = [hip.event() for _ in range(6)]
-        marks = [hip.event() for _ in range(3)]
         dbg_ph = R.Debug(0, 0, events=ph_ev)
-        names = ["scan", "threshold", "select", "finish", "merge"]
-        ph = {n: [] for n in names + ["append", "swa", "retrieval_total"]}
+        ph = {"pass": [], "finish": []}
         for _ in range(n_phase):
             flush_caches(timer.flush)
-            self.step(top_p, debug=dbg_ph, marks=marks, hip=hip)
+            self.append()
+            self.decode_step(top_p, debug=dbg_ph)
             torch.cuda.synchronize()
-            for k, n in enumerate(names):
-                ph[n].append(hip.elapsed_ms(ph_ev[k], ph_ev[k + 1]))
-            ph["append"].append(hip.elapsed_ms(marks[0], ph_ev[0]))
-            ph["swa"].append(hip.elapsed_ms(marks[1], marks[2]))
-            ph["retrieval_total"].append(hip.elapsed_ms(ph_ev[0], ph_ev[5]))
-        phases_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in ph.items()}
+            ph["pass"].append(hip.elapsed_ms(ph_ev[0], ph_ev[1]))
+            ph["finish"].append(hip.elapsed_ms(ph_ev[3], ph_ev[4]))
+        phases_us = {k: round(float(np.median(v)) * 1e3, 2) for k, v in ph.items()}
         # algorithmic bytes of one step
         lo = max(0, N - wl.window)
         swa_rows = min(wl.n_sink, lo) + (N - lo)
         b_index = B * wl.n_ret * N * 32
         b_gather = int(union.sum()) * 512
-        b_swa = B * self.n_loc * swa_rows * 512
+        b_local = B * self.n_loc * swa_rows * 512
         b_small = B * wl.Hq * 256 * 2 + wl.w_q.size * 2 + B * wl.Hkv * (512 + 512) + \
             B * wl.n_ret * 32
-        step_bytes = b_index + b_gather + b_swa + b_small
+        step_bytes = b_index + b_gather + b_local + b_small
         med_ms = float(np.median(step_ms))
         gbs = lambda b, us: round(b / (us * 1e-6) / 1e9, 1)  # noqa: E731
-        sel_us = phases_us["select"] + phases_us["finish"]
         return {
             "top_p": top_p,
             "us_per_step": dist(step_ms),
             "us_per_step_dist": dist(dist_ms),
+            "parts_us": parts_us,
             "phases_us": phases_us,
             "set_sizes": {"min": int(sizes.min()), "median": float(np.median(sizes)),
                           "max": int(sizes.max()), "all": sizes.tolist() if sizes.size <= 32
                           else None},
             "union_rows": int(union.sum()),
-            "step_bytes": {"index": b_index, "gather_rows": b_gather, "swa": b_swa,
+            "step_bytes": {"index": b_index, "gather_rows": b_gather, "local_window": b_local,
                            "small": b_small, "total": step_bytes},
             "achieved_GBps": gbs(step_bytes, med_ms * 1e3),
             "hbm_frac": round(step_bytes / (med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "scan_GBps": gbs(b_index, phases_us["scan"]),
-            "select_finish_GBps": gbs(b_gather, sel_us),
-            "swa_GBps": gbs(b_swa, phases_us["swa"]),
+            "pass_streamed_GBps": gbs(b_index + b_local, phases_us["pass"]),
             "_step_ms": step_ms,
         }
 
     def free(self):
         import torch
-        for a in ("k_cache", "v_cache", "index", "k_ring", "v_ring", "ws", "wss", "out"):
+        for a in ("k_cache", "v_cache", "index", "k_ring", "v_ring", "ws", "wss", "ws_step",
+                  "out"):
             if hasattr(self, a):
                 delattr(self, a)
         torch.cuda.empty_cache()
@@ -432,8 +456,8 @@ def headline(args):
     reads = attainable_read(timer)
     ms = float(np.median(step_ms))
     ph = m["phases_us"]
-    b_index = m["step_bytes"]["index"]
-    ach = b_index / (ph["scan"] * 1e-6) / 1e9
+    b_pass = m["step_bytes"]["index"] + m["step_bytes"]["local_window"]
+    ach = b_pass / (ph["pass"] * 1e-6) / 1e9
     res = {
         "metric": METRIC,
         "value": round(ms * 1e3, 2),
@@ -460,21 +484,24 @@ def headline(args):
         "hbm_frac_of_attainable": round(m["achieved_GBps"] / reads["1GiB"], 4),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "graph_us_per_step": dist(graph_ms),
-        "step_issue": "launched call by call (append, retrieval decode, local-head SWA on "
-                      "a second stream); graph_us_per_step: the same step as one HIP "
-                      "graph replay",
+        "step_issue": "append, then one rtp_decode_step call (retrieval and local heads); "
+                      "graph_us_per_step: the same step as one HIP graph replay",
         "set_sizes": m["set_sizes"],
         "union_rows": m["union_rows"],
         "step_bytes": m["step_bytes"],
+        "parts_us": m["parts_us"],
         "phases_us": ph,
-        "phase_GBps": {"scan": m["scan_GBps"], "select_finish": m["select_finish_GBps"],
-                       "swa": m["swa_GBps"]},
-        "roofline": {"bound": "hbm", "kernel": "k_scan (indexer scan + mass histogram)",
+        "phase_GBps": {"pass_streamed": m["pass_streamed_GBps"]},
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_pass (fused index scan, threshold, definite rows and the "
+                               "local heads' window segments)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4),
                      "frac_of_attainable_32MiB": round(ach / reads["32MiB"], 4),
                      "traffic": measured_traffic(wl.name),
-                     "algorithmic_bytes": b_index},
+                     "algorithmic_bytes": b_pass,
+                     "bytes_note": "the index and the local window rows, each read once; "
+                                   "the definite-row gathers of the pass are not counted"},
     }
     res.update(extras)
     if not args.no_cpu_baseline:

@@ -24,6 +24,7 @@ constexpr int kPartStride = 132;  // floats per partial state: m, l, pad, pad, o
 template <int G>
 struct TileSmem {
   float qs[G][RTP_D];
+  uint16_t qp[3][G][RTP_D];  // qs as three bf16 parts hi, mid, lo (qs = hi + mid + lo)
   uint16_t Ks[kTileRows][kKvPitch];
   uint16_t Vs[kTileRows][kKvPitch];
   float ps[G][kTileRows];
@@ -53,35 +54,67 @@ __device__ __forceinline__ void load_q_ready(TileSmem<G>& sm, const float* src) 
   for (int e = threadIdx.x; e < G * RTP_D; e += blockDim.x) (&sm.qs[0][0])[e] = src[e];
 }
 
+typedef __bf16 tile_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float tile_f32x4 __attribute__((ext_vector_type(4)));
+
+// Split the queries in sm.qs into the bf16 parts of sm.qp.  hi = bf16(q), mid =
+// bf16(q - hi), lo = bf16(q - hi - mid): each difference is exact in fp32 and the
+// three parts sum to q exactly, so bf16 products with bf16 keys stay exact and the
+// logits keep fp32 accuracy.  All NT threads call it after sm.qs is written.
+template <int G, int NT>
+__device__ __forceinline__ void prepare_q_parts(TileSmem<G>& sm) {
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * RTP_D; e += NT) {
+    const float q = (&sm.qs[0][0])[e];
+    const uint16_t hi = f32_to_bf16(q);
+    const float r1 = q - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    (&sm.qp[0][0][0])[e] = hi;
+    (&sm.qp[1][0][0])[e] = mid;
+    (&sm.qp[2][0][0])[e] = f32_to_bf16(r1 - bf16_to_f32(mid));
+  }
+  __syncthreads();
+}
+
 // Logits, online softmax and P.V of one staged tile of nr rows (K, V and the row
-// masks in LDS).  All threads call it; it ends with a barrier.
-template <int G>
+// masks in LDS; the query parts in sm.qp).  The logits run on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 with A = 16 key rows x 32 dimensions straight from the
+// staged tile (lane: row lane & 15, dimensions 8 (lane >> 4) .. + 7) and B = the
+// query parts of 16 head columns (heads >= G are zero), summed lo, mid, hi; one wave
+// per block of 16 rows.  Wave h < G then runs head h's online softmax (lane = row)
+// and P.V (lane = a pair of output dimensions).  All NT threads call it; it ends
+// with a barrier.
+template <int G, int NT>
 __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, float& l,
                                              float& o0, float& o1) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int h = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, kb = lane >> 4;
+  for (int rb = h; rb < kTileRows / 16; rb += NW) {
+    tile_f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < RTP_D / 32; ++kc) {
+      const uint4 a = *(const uint4*)&sm.Ks[rb * 16 + n][kc * 32 + 8 * kb];
+#pragma unroll
+      for (int part = 2; part >= 0; --part) {
+        const uint4 b = n < G ? *(const uint4*)&sm.qp[part][n < G ? n : 0][kc * 32 + 8 * kb]
+                              : make_uint4(0, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(tile_bf16x8, a),
+                                                    __builtin_bit_cast(tile_bf16x8, b), c, 0, 0,
+                                                    0);
+      }
+    }
+    if (n < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.ps[n][rb * 16 + 4 * kb + i] = c[i];
+    }
+  }
+  __syncthreads();
   float alpha = 1.f;
   if (h < G) {
     const bool valid = lane < nr && ((sm.masks[lane] >> h) & 1u);
-    float logit = -INFINITY;
-    if (valid) {
-      float acc = 0.f;
-#pragma unroll
-      for (int d = 0; d < RTP_D; d += 8) {
-        const uint4 kk = *(const uint4*)&sm.Ks[lane][d];
-        const float4 qa = *(const float4*)&sm.qs[h][d];
-        const float4 qb = *(const float4*)&sm.qs[h][d + 4];
-        acc = fmaf(qa.x, bf16_lo(kk.x), acc);
-        acc = fmaf(qa.y, bf16_hi(kk.x), acc);
-        acc = fmaf(qa.z, bf16_lo(kk.y), acc);
-        acc = fmaf(qa.w, bf16_hi(kk.y), acc);
-        acc = fmaf(qb.x, bf16_lo(kk.z), acc);
-        acc = fmaf(qb.y, bf16_hi(kk.z), acc);
-        acc = fmaf(qb.z, bf16_lo(kk.w), acc);
-        acc = fmaf(qb.w, bf16_hi(kk.w), acc);
-      }
-      logit = acc;
-    }
+    const float logit = valid ? sm.ps[h][lane] : -INFINITY;
     const float tmax = wave_max(logit);
     const float m_new = fmaxf(m, tmax);
     const float p = valid ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
@@ -106,7 +139,8 @@ __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, 
 }
 
 // Attend one tile of nr rows (ids in sm.rows, per-row head masks in sm.masks).
-// kbase / vbase point at row 0 of this KV head's cache.  All NT threads call it.
+// kbase / vbase point at row 0 of this KV head's cache; the caller has run
+// prepare_q_parts since it last wrote sm.qs.  All NT threads call it.
 template <int G, int NT>
 __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kbase,
                                             const uint16_t* vbase, int nr, float& m, float& l,
@@ -121,7 +155,7 @@ __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kba
     }
   }
   __syncthreads();
-  tile_compute<G>(sm, nr, m, l, o0, o1);
+  tile_compute<G, NT>(sm, nr, m, l, o0, o1);
 }
 
 // One row of a list to attend: its id in the cache and its head mask.
@@ -142,6 +176,7 @@ __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kba
   constexpr int PER = kTileRows * 16 / NT;  // 16-byte pieces of K (and of V) per thread
   static_assert(PER * NT == kTileRows * 16, "the threads cover a tile");
   if (n <= 0) return;
+  prepare_q_parts<G, NT>(sm);
   const int tid = threadIdx.x;
   // native vectors: a uint4 struct would be copied to LDS through private memory
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -170,7 +205,7 @@ __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kba
         vr[u] = *(const u32x4*)(vbase + off);
       }
     }
-    if (t0 >= 0) tile_compute<G>(sm, nr, m, l, o0, o1);
+    if (t0 >= 0) tile_compute<G, NT>(sm, nr, m, l, o0, o1);
   }
 }
 

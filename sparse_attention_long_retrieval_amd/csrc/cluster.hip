@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kClThreads) void k_cl_attend(ClDecPlan p) {
   for (int i = tid; i < nsel; i += NT) sel_s[i] = p.sel[(size_t)unit * p.K + i];
   for (int i = tid; i <= nsel; i += NT) pref_s[i] = p.pref[(size_t)unit * (p.K + 1) + i];
   load_q_ready<1>(sm, p.qrope + (size_t)unit * kD);
-  __syncthreads();
+  prepare_q_parts<1, NT>(sm);
   const ClRows rows = cl_rows(p, unit, sel_s, pref_s);
   const int lo = (int)(((long long)rows.R * f) / p.nF);
   const int hi = (int)(((long long)rows.R * (f + 1)) / p.nF);

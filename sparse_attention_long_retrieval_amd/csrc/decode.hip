@@ -1728,6 +1728,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   } else if (C > 0) {
     __syncthreads();  // every read of the candidate space is done
     if (tid < kD) sm.qs[0][tid] = qv;
+    prepare_q_parts<1, NT>(sm);
     // list too long for LDS: this block walks its range of pass-B blocks
     const int b_lo = (int)(((long long)p.nA * f) / p.nF);
     const int b_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
