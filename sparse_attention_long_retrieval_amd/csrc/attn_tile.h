@@ -282,6 +282,43 @@ __device__ __forceinline__ void merge_partials_wave(const float* src, int n, flo
   o1 = A1;
 }
 
+// Fold one partial softmax state (mk, lk, ok0, ok1) into the running state of the
+// calling wave (lane = dimension pair); -inf states hold nothing.
+__device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float& A1, float mk,
+                                           float lk, float ok0, float ok1) {
+  if (mk == -INFINITY) return;
+  const float nm = fmaxf(M, mk);
+  const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
+  const float sk = exp2f(mk - nm);
+  L = L * so + lk * sk;
+  A0 = A0 * so + ok0 * sk;
+  A1 = A1 * so + ok1 * sk;
+  M = nm;
+}
+
+// Fold partial states src[0], src[kPartStride], ... (n of them, written by an earlier
+// launch) into the calling wave's running state one by one, in order; sixteen are
+// requested at a time.
+__device__ __forceinline__ void fold_partials_in_order(const float* src, int n, float& M, float& L,
+                                                       float& A0, float& A1) {
+  const int lane = threadIdx.x & 63;
+  constexpr int B = 16;
+  for (int k0 = 0; k0 < n; k0 += B) {
+    float mk[B], lk[B];
+    float2 ok[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float* q = src + (size_t)min(k0 + u, n - 1) * kPartStride;
+      mk[u] = q[0];
+      lk[u] = q[1];
+      ok[u] = *(const float2*)&q[4 + 2 * lane];
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (k0 + u < n) fold_state(M, L, A0, A1, mk[u], lk[u], ok[u].x, ok[u].y);
+  }
+}
+
 // Write the normalised output of one head (lane = dimension pair) as bf16.
 __device__ __forceinline__ void store_output(uint16_t* dst, float l, float o0, float o1) {
   const int lane = threadIdx.x & 63;

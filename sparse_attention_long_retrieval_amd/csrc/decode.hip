@@ -78,20 +78,6 @@ __device__ __forceinline__ unsigned long long fx36(float f) {
 }
 static_assert(kFxCand == 68719476736.0, "candidate masses are 2^36 fixed point");
 
-// Fold one partial softmax state (mk, lk, ok0, ok1) into the running state of the
-// calling wave (lane = dimension pair); -inf states hold nothing.
-__device__ __forceinline__ void fold_state(float& M, float& L, float& A0, float& A1, float mk,
-                                           float lk, float ok0, float ok1) {
-  if (mk == -INFINITY) return;
-  const float nm = fmaxf(M, mk);
-  const float so = (M == -INFINITY) ? 0.f : exp2f(M - nm);
-  const float sk = exp2f(mk - nm);
-  L = L * so + lk * sk;
-  A0 = A0 * so + ok0 * sk;
-  A1 = A1 * so + ok1 * sk;
-  M = nm;
-}
-
 // Inverse bin width of coarse grid c: bins of 2^c score units (exact in fp32).
 __device__ __forceinline__ float coarse_inv(int c) { return 1.0f / (float)(1 << c); }
 
@@ -1533,9 +1519,46 @@ __device__ uint32_t radix_key(Visit&& visit, double need_fx, bool have_range, ui
   return prefix;
 }
 
+// The local heads of a decode step whose window segments the fused pass attended:
+// block (x, P*G + local unit) merges q-heads x, x + nF, ... of that unit.  Wave w folds
+// a quarter of the segment states in segment order, then wave 0 folds the quarters
+// in order and writes the bf16 output.
+template <int G, int NT>
+__device__ void finish_local_heads(const DecPlan& p, int lu, int f) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NW = NT / 64;
+  const SwaPlan& w = p.sw;
+  const int b = lu / w.n_loc, kv = w.loc_kv[lu % w.n_loc];
+  __shared__ float lm[NW], ll[NW];
+  __shared__ float2 lo[NW][64];
+  for (int hh = f; hh < G; hh += p.nF) {
+    const float* src = w.part + ((size_t)lu * G + hh) * w.nSeg * kPartStride;
+    const int s0 = (w.nSeg * wave) / NW, s1 = (w.nSeg * (wave + 1)) / NW;
+    float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
+    fold_partials_in_order(src + (size_t)s0 * kPartStride, s1 - s0, M, L, A0, A1);
+    if (lane == 0) {
+      lm[wave] = M;
+      ll[wave] = L;
+    }
+    lo[wave][lane] = make_float2(A0, A1);
+    __syncthreads();
+    if (wave == 0) {
+      M = -INFINITY;
+      L = A0 = A1 = 0.f;
+      for (int q = 0; q < NW; ++q) fold_state(M, L, A0, A1, lm[q], ll[q], lo[q][lane].x, lo[q][lane].y);
+      store_output(p.out + ((size_t)b * p.Hq + kv * G + hh) * kD, L, A0, A1);
+    }
+    __syncthreads();
+  }
+}
+
 template <int G>
 __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   constexpr int NT = kFinishThreads;
+  if ((int)blockIdx.y >= p.P * G) {
+    finish_local_heads<G, NT>(p, blockIdx.y - p.P * G, blockIdx.x);
+    return;
+  }
   const int unit = blockIdx.y, f = blockIdx.x;
   const int pair = unit / G, h = unit % G;
   const int b = pair / p.n_ret, ret_i = pair % p.n_ret;
@@ -1976,7 +1999,9 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
     }
   }
   mark(3);
-  RTP_LAUNCH(k_finish<G>, dim3(p.nF, p.P * G), dim3(kFinishThreads), s, p);
+  // grid rows past P * G merge the local heads' segment states of a decode step
+  const int local_rows = p.with_swa ? p.B * p.sw.n_loc : 0;
+  RTP_LAUNCH(k_finish<G>, dim3(p.nF, p.P * G + local_rows), dim3(kFinishThreads), s, p);
   mark(4);
   if (!p.fold_merge) {
     // the finish states already hold the index pass's partials
@@ -2018,7 +2043,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   int nF = kFinishSplit;
   while (nF > kMinFinishSplit && (long long)P * G * nF > kFinishBlocks) nF >>= 1;
   // grid y of the index passes is P, of the finish kernel P * G
-  if ((long long)P * G > kMaxGridY) return 0;
+  if ((long long)P * G + (long long)B * n_loc > kMaxGridY) return 0;
   const int nGrp = (nA + kGroupBlocks - 1) / kGroupBlocks;
   // Local heads of a decode step (n_loc > 0): segments of their windows, sized so that
   // every block of the fused pass runs about one (several when the local heads
@@ -2081,6 +2106,7 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
       plan->sw.cnt_top = cnt + (size_t)units * sGrp;
       plan->sw.part = (float*)sp;
       plan->sw.partg = (float*)spg;
+      plan->sw.defer_merge = 1;  // the finish kernel merges the segments in order
     }
     plan->fusable = fusable;
     plan->nGrp = nGrp;

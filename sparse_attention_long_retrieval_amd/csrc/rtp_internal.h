@@ -84,6 +84,7 @@ struct SwaPlan {
   unsigned* cnt_top;  // [B*n_loc]
   float* part;        // [B*n_loc*G][nSeg][kPartStride]
   float* partg;       // [B*n_loc*G][nGrp][kPartStride]
+  int defer_merge;    // segments only store their states; a later kernel merges them
 };
 
 // Threshold state of one (pair, q-head).

@@ -25,7 +25,8 @@ __device__ __forceinline__ void swa_rows(int pos, int window, int n_sink, int* l
 }
 
 // Segment seg of unit bl (= b * n_loc + local index): attend, store the partial
-// states, and take part in the merges.  All NT threads of the block call it; it
+// states, and take part in the merges (unless p.defer_merge: then a later kernel
+// merges the states in segment order).  All NT threads of the block call it; it
 // overwrites sm (queries and tiles) and returns in every block.
 template <int G, int NT>
 __device__ __forceinline__ void swa_decode_segment(const SwaPlan& p, TileSmem<G>& sm, int bl,
@@ -54,6 +55,7 @@ __device__ __forceinline__ void swa_decode_segment(const SwaPlan& p, TileSmem<G>
                      m, l, o0, o1);
   const size_t unit = (size_t)bl * G + h;
   if (h < G) store_partial(p.part + (unit * p.nSeg + seg) * kPartStride, m, l, o0, o1);
+  if (p.defer_merge) return;
 
   const int grp = seg / p.gsz;
   const int s0 = grp * p.gsz;
