@@ -1578,6 +1578,9 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   __shared__ unsigned long long red[NT / 64];
   __shared__ unsigned wtot[NT / 64];
   __shared__ unsigned C_s, nr_s;
+  // each candidate's weight exp(s - m) (before the 2^36 fixed point), while the tokens
+  // are in LDS too: the radix passes then only convert it
+  __shared__ float wt_s[kTokCap];
 
   const ThrInfo t = p.thr[unit];
   const unsigned* blk_cnt = p.cand_blk + (size_t)unit * p.nA;
@@ -1585,23 +1588,24 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   static_assert(kD <= NT, "one query dimension per thread");
   const float qv = tid < kD ? p.qrope[(size_t)unit * kD + tid] : 0.f;
   // this block's share of the index pass's partial states, folded in at the end; the
-  // first kFinPB are requested now, with the threshold state
+  // first kFinPB are requested now, with the threshold state, kFinPW per wave
+  constexpr int kFinPW = kFinPB / (NT / 64);
+  static_assert(kFinPW * (NT / 64) == kFinPB, "every wave requests the same number");
   const int pb_lo = (int)(((long long)p.nA * f) / p.nF);
   const int pb_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
-  float pbm[kFinPB], pbl[kFinPB];
-  float2 pbo[kFinPB];
-  if (wave == 0) {
+  float pbm[kFinPW], pbl[kFinPW];
+  float2 pbo[kFinPW];
 #pragma unroll
-    for (int u = 0; u < kFinPB; ++u) {
-      pbm[u] = -INFINITY;
-      pbl[u] = 0.f;
-      pbo[u] = make_float2(0.f, 0.f);
-      if (pb_lo + u < pb_hi) {
-        const float* q = p.partB + ((size_t)unit * p.nA + pb_lo + u) * kPartStride;
-        pbm[u] = q[0];
-        pbl[u] = q[1];
-        pbo[u] = *(const float2*)&q[4 + 2 * lane];
-      }
+  for (int u = 0; u < kFinPW; ++u) {
+    const int k = pb_lo + wave * kFinPW + u;
+    pbm[u] = -INFINITY;
+    pbl[u] = 0.f;
+    pbo[u] = make_float2(0.f, 0.f);
+    if (k < pb_hi) {
+      const float* q = p.partB + ((size_t)unit * p.nA + k) * kPartStride;
+      pbm[u] = q[0];
+      pbl[u] = q[1];
+      pbo[u] = *(const float2*)&q[4 + 2 * lane];
     }
   }
   // candidate counts of the pass-B blocks and their exclusive prefix (fixed order);
@@ -1642,6 +1646,10 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     __syncthreads();
     C = C_s;
   }
+  const bool counting = p.budget > 0;
+  auto cand_w = [&](float sv) {
+    return counting ? 1.f : __builtin_amdgcn_exp2f((sv - t.m) * kLog2e);
+  };
   // up to kTokCap candidates: keys and tokens in LDS; up to kKeyCap: keys only
   const bool in_lds = small_nA && C <= (unsigned)kTokCap;
   const bool keys_lds = small_nA && C <= (unsigned)kKeyCap;
@@ -1651,27 +1659,27 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     for (int bb = tid; bb < p.nA; bb += NT) {
       const unsigned n = blk_cnt[bb], o = boff[bb];
       const float2* src = cand + (size_t)bb * kPassTokens;
-      for (unsigned c0 = 0; c0 < n; c0 += 8) {
-        float2 e[8];
+      for (unsigned c0 = 0; c0 < n; c0 += 16) {
+        float2 e[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
           if (c0 + u < n) e[u] = src[c0 + u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           if (c0 + u < n) {
             key_s[o + c0 + u] = f32_ord(e[u].x);
-            if (in_lds) tok_s[o + c0 + u] = __float_as_int(e[u].y);
+            if (in_lds) {
+              tok_s[o + c0 + u] = __float_as_int(e[u].y);
+              wt_s[o + c0 + u] = cand_w(e[u].x);
+            }
           }
         }
       }
     }
   }
   __syncthreads();
-  const bool counting = p.budget > 0;
   // a candidate's mass, 2^36 fixed point relative to the global max
-  auto cand_mass = [&](float sv) {
-    return fx36(counting ? 1.f : __builtin_amdgcn_exp2f((sv - t.m) * kLog2e));
-  };
+  auto cand_mass = [&](float sv) { return fx36(cand_w(sv)); };
   uint32_t kstar = 0u;
   float tau = -INFINITY;
   if (t.mode != 2) {
@@ -1693,7 +1701,7 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
             [&](auto&& fn) {
               for (unsigned c = tid; c < C; c += NT) {
                 const uint32_t k = key_s[c];
-                fn(k, cand_mass(ord_f32(k)));
+                fn(k, in_lds ? fx36(wt_s[c]) : cand_mass(ord_f32(k)));
               }
             },
             t.need * kFxCand, have_range, lo_key, hi_key);
@@ -1782,17 +1790,31 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
       }
     }
   }
-  if (wave == 0) {
-    // the block's state: its share of the index pass's partials in order, then its
+  {
+    // the block's state: its share of the index pass's partials in order (each wave
+    // folds its own, wave 0 folds the waves' in order and any past kFinPB), then its
     // candidates
+    __shared__ float fm[NT / 64], fl[NT / 64];
+    __shared__ float2 fo[NT / 64][64];
     float M = -INFINITY, L = 0.f, A0 = 0.f, A1 = 0.f;
 #pragma unroll
-    for (int u = 0; u < kFinPB; ++u) fold_state(M, L, A0, A1, pbm[u], pbl[u], pbo[u].x, pbo[u].y);
-    if (pb_hi - pb_lo > kFinPB)
-      merge_partials_wave(p.partB + ((size_t)unit * p.nA + pb_lo + kFinPB) * kPartStride,
-                          pb_hi - pb_lo - kFinPB, M, L, A0, A1);
-    fold_state(M, L, A0, A1, m, l, o0, o1);
-    store_partial(p.partF + ((size_t)unit * p.nF + f) * kPartStride, M, L, A0, A1);
+    for (int u = 0; u < kFinPW; ++u) fold_state(M, L, A0, A1, pbm[u], pbl[u], pbo[u].x, pbo[u].y);
+    if (lane == 0) {
+      fm[wave] = M;
+      fl[wave] = L;
+    }
+    fo[wave][lane] = make_float2(A0, A1);
+    __syncthreads();
+    if (wave == 0) {
+      M = -INFINITY;
+      L = A0 = A1 = 0.f;
+      for (int q = 0; q < NT / 64; ++q) fold_state(M, L, A0, A1, fm[q], fl[q], fo[q][lane].x, fo[q][lane].y);
+      if (pb_hi - pb_lo > kFinPB)
+        merge_partials_wave(p.partB + ((size_t)unit * p.nA + pb_lo + kFinPB) * kPartStride,
+                            pb_hi - pb_lo - kFinPB, M, L, A0, A1);
+      fold_state(M, L, A0, A1, m, l, o0, o1);
+      store_partial(p.partF + ((size_t)unit * p.nF + f) * kPartStride, M, L, A0, A1);
+    }
   }
   if (!p.fold_merge) return;
   // the last of the head's finish blocks combines their states (wave w folds a quarter
