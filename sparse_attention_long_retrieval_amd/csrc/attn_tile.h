@@ -18,8 +18,14 @@
 namespace rtp {
 
 constexpr int kTileRows = 64;
-constexpr int kKvPitch = 136;     // bf16 elements per staged row: 256 B + 16 B pad
+constexpr int kKvPitch = 128;     // bf16 elements per staged row (256 B, no padding)
 constexpr int kPartStride = 132;  // floats per partial state: m, l, pad, pad, o[128]
+
+// Staged K rows are swizzled: the 16-byte chunk c of row r (dimensions 8c .. 8c + 7)
+// sits at chunk c ^ (r & 15), so sixteen rows read at one logical chunk (the
+// matrix-core A operand) fall on sixteen different chunk positions.  V rows are read
+// whole (P.V, lane = a pair of dimensions) and stay in order.
+__device__ __forceinline__ int kv_chunk(int r, int c) { return c ^ (r & 15); }
 
 template <int G>
 struct TileSmem {
@@ -95,7 +101,7 @@ __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, 
     tile_f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < RTP_D / 32; ++kc) {
-      const uint4 a = *(const uint4*)&sm.Ks[rb * 16 + n][kc * 32 + 8 * kb];
+      const uint4 a = *(const uint4*)&sm.Ks[rb * 16 + n][kv_chunk(n, kc * 4 + kb) * 8];
 #pragma unroll
       for (int part = 2; part >= 0; --part) {
         const uint4 b = n < G ? *(const uint4*)&sm.qp[part][n < G ? n : 0][kc * 32 + 8 * kb]
@@ -126,7 +132,22 @@ __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, 
   __syncthreads();
   if (h < G) {
     float a0 = o0 * alpha, a1 = o1 * alpha;
-    for (int r = 0; r < nr; ++r) {
+    int r = 0;
+    // eight rows at a time: their probabilities and V words are requested together
+    for (; r + 8 <= nr; r += 8) {
+      const float4 pa = *(const float4*)&sm.ps[h][r];
+      const float4 pb = *(const float4*)&sm.ps[h][r + 4];
+      uint32_t vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vv[u] = *(const uint32_t*)&sm.Vs[r + u][2 * lane];
+      const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0 = fmaf(pr[u], bf16_lo(vv[u]), a0);
+        a1 = fmaf(pr[u], bf16_hi(vv[u]), a1);
+      }
+    }
+    for (; r < nr; ++r) {
       const float pr = sm.ps[h][r];
       const uint32_t vv = *(const uint32_t*)&sm.Vs[r][2 * lane];
       a0 = fmaf(pr, bf16_lo(vv), a0);
@@ -150,7 +171,7 @@ __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kba
     const int r = c >> 4, q = c & 15;
     if (r < nr) {
       const size_t off = (size_t)sm.rows[r] * RTP_D + q * 8;
-      *(uint4*)&sm.Ks[r][q * 8] = *(const uint4*)(kbase + off);
+      *(uint4*)&sm.Ks[r][kv_chunk(r, q) * 8] = *(const uint4*)(kbase + off);
       *(uint4*)&sm.Vs[r][q * 8] = *(const uint4*)(vbase + off);
     }
   }
@@ -190,7 +211,7 @@ __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kba
 #pragma unroll
       for (int u = 0; u < PER; ++u) {
         const int c = tid + u * NT, r = c >> 4, q = c & 15;
-        *(u32x4*)&sm.Ks[r][q * 8] = kr[u];
+        *(u32x4*)&sm.Ks[r][kv_chunk(r, q) * 8] = kr[u];
         *(u32x4*)&sm.Vs[r][q * 8] = vr[u];
       }
       __syncthreads();

@@ -822,17 +822,18 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   const bool hv = h < G;
   const int hs = hv ? h : 0;
 
-  // The attention tiles' space first holds the projection and the bf16 queries, then
-  // the per-token head masks of the classification, then the K/V tiles; lb first
-  // holds the histogram, then the list of definite rows.
+  // The attention tiles' space first holds the projection (the bf16 queries sit in the
+  // query-parts space), then the per-token head masks of the classification, then the
+  // K/V tiles; lb first holds the histogram, then the list of definite rows.
   __shared__ TileSmem<G> sm;
   __shared__ unsigned lb[kPassTokens];
-  static_assert(sizeof(uint16_t) * (G * kD * kR + G * kD) <= sizeof(sm.Ks) + sizeof(sm.Vs),
-                "the projection and the queries fit the tile space");
+  static_assert(sizeof(uint16_t) * G * kD * kR <= sizeof(sm.Ks) + sizeof(sm.Vs),
+                "the projection fits the tile space");
+  static_assert(sizeof(uint16_t) * G * kD <= sizeof(sm.qp), "the queries fit the parts space");
   static_assert(2 * kPassTokens * sizeof(unsigned) <= sizeof(sm.Ks), "masks fit the K tile");
   static_assert(sizeof(unsigned) * kNB * S::GE * CP <= sizeof(lb), "bins fit the list space");
   uint16_t* const wq_s = &sm.Ks[0][0];
-  uint16_t* const q_s = wq_s + G * kD * kR;
+  uint16_t* const q_s = &sm.qp[0][0][0];
   unsigned (*const bins)[S::GE][CP] = reinterpret_cast<unsigned (*)[S::GE][CP]>(lb);
   unsigned* const dmask = (unsigned*)&sm.Ks[0][0];
   unsigned* const cmask = dmask + kPassTokens;
@@ -1184,18 +1185,16 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   }
   // ---- local heads of a decode step: this block's window segments, run while the
   // threshold is being found (the retrieval queries wait aside in LDS meanwhile)
-  if (p.with_swa) {
-    const int n_items = p.B * p.sw.n_loc * p.sw.nSeg;
-    int it = pair * p.nA + blk;
-    if (it < n_items) {
-      __syncthreads();
-      for (int e = tid; e < G * kD; e += NT) qs_keep[e] = (&sm.qs[0][0])[e];
-      __syncthreads();
-      for (; it < n_items; it += p.P * p.nA)
-        swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
-      __syncthreads();
-      for (int e = tid; e < G * kD; e += NT) (&sm.qs[0][0])[e] = qs_keep[e];
-    }
+  const int swa_items = p.with_swa ? p.B * p.sw.n_loc * p.sw.nSeg : 0;
+  const int swa_first = pair * p.nA + blk;
+  if (swa_first < swa_items) {
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += NT) qs_keep[e] = (&sm.qs[0][0])[e];
+    __syncthreads();
+    for (int it = swa_first; it < swa_items; it += p.P * p.nA)
+      swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += NT) (&sm.qs[0][0])[e] = qs_keep[e];
   }
   // ---- wait for this block's mailbox: every q-head's word present, then clear them.
   // Lane hh of wave 0 polls word hh (one load instruction per poll).
