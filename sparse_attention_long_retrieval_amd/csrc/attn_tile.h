@@ -348,24 +348,27 @@ __device__ __forceinline__ void store_output(uint16_t* dst, float l, float o0, f
   *(uint32_t*)&dst[2 * lane] = v;
 }
 
-// Last-arrival test for a group of `expected` blocks sharing `counter`.  Returns
-// true in the one block that arrives last; that block also resets the counter
-// for the next call.  The data the group exchanges is written with st_dev and
+// Arrival of a block at a group of `expected` blocks sharing `counter`: its rank in
+// arrival order (0 .. expected - 1).  The last one (arrive_last is true there) also
+// resets the counter for the next call.  The data the group exchanges is written with st_dev and
 // read with ld_dev; every wave waits for its stores to complete before the
 // block's arrival is counted, so the last block reads complete data.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {
-  __shared__ int last_flag;
+__device__ __forceinline__ unsigned arrive_rank(unsigned* counter, unsigned expected) {
+  __shared__ unsigned rank_s;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev + 1u == expected;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = last;
+    if (prev + 1u == expected)
+      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    rank_s = prev;
   }
   __syncthreads();
-  return last_flag != 0;
+  return rank_s;
+}
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {
+  return arrive_rank(counter, expected) + 1u == expected;
 }
 
 }  // namespace rtp

@@ -1003,7 +1003,8 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   // threads; the shifted bins add up in LDS as integers (order free).
   const int grp = blk / kGroupBlocks, g0 = grp * kGroupBlocks;
   const int nin = min(kGroupBlocks, p.nA - g0);
-  if (arrive_last(&p.cnt_grp[pair * p.nGrp + grp], (unsigned)nin)) {
+  const unsigned grp_rank = arrive_rank(&p.cnt_grp[pair * p.nGrp + grp], (unsigned)nin);
+  if (grp_rank + 1u == (unsigned)nin) {
     constexpr int PER1 = (kGroupBlocks * G * kNB / 2 + NT - 1) / NT;  // bin pairs per thread
     const int n_pairs = nin * G * (kNB / 2);
     unsigned long long w[PER1];
@@ -1183,18 +1184,26 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
       }
     }
   }
-  // ---- local heads of a decode step: this block's window segments, run while the
-  // threshold is being found (the retrieval queries wait aside in LDS meanwhile)
-  const int swa_items = p.with_swa ? p.B * p.sw.n_loc * p.sw.nSeg : 0;
-  const int swa_first = pair * p.nA + blk;
-  if (swa_first < swa_items) {
-    __syncthreads();
-    for (int e = tid; e < G * kD; e += NT) qs_keep[e] = (&sm.qs[0][0])[e];
-    __syncthreads();
-    for (int it = swa_first; it < swa_items; it += p.P * p.nA)
-      swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
-    __syncthreads();
-    for (int e = tid; e < G * kD; e += NT) (&sm.qs[0][0])[e] = qs_keep[e];
+  // ---- local heads of a decode step: window segments, run while the threshold is
+  // being found.  Each merge group owns an equal share of the segments, taken in
+  // arrival order by the blocks that do not merge (the only block of a one-block group
+  // takes them all), so the merging blocks are not held up.  Which block runs a segment
+  // changes no result.  The retrieval queries wait aside in LDS meanwhile.
+  if (p.with_swa) {
+    const int items = p.B * p.sw.n_loc * p.sw.nSeg;
+    const long long gg = (long long)pair * p.nGrp + grp, ngg = (long long)p.P * p.nGrp;
+    const int i0 = (int)(items * gg / ngg), i1 = (int)(items * (gg + 1) / ngg);
+    const int workers = nin > 1 ? nin - 1 : 1;
+    const int first = nin > 1 ? (grp_rank + 1u == (unsigned)nin ? i1 : i0 + (int)grp_rank) : i0;
+    if (first < i1) {
+      __syncthreads();
+      for (int e = tid; e < G * kD; e += NT) qs_keep[e] = (&sm.qs[0][0])[e];
+      __syncthreads();
+      for (int it = first; it < i1; it += workers)
+        swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
+      __syncthreads();
+      for (int e = tid; e < G * kD; e += NT) (&sm.qs[0][0])[e] = qs_keep[e];
+    }
   }
   // ---- wait for this block's mailbox: every q-head's word present, then clear them.
   // Lane hh of wave 0 polls word hh (one load instruction per poll).
