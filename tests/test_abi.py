@@ -200,3 +200,33 @@ def test_noalloc_decode_rejects_shapes_beyond_its_scratch():
                                                   0.9, 1.0, 0.088, FAKE, None, None) == 4
     fits = R.Layer(1, 32, 4, 1 << 20, [0])         # the 1M-context decode shape fits
     assert R.workspace_size(fits, R.OP_DECODE, 1 << 20) <= 80 << 20
+
+
+def test_decode_step_validation():
+    """rtp_decode_step checks the ring, the window and the workspace before any launch,
+    and sizes its workspace to hold the local heads' segment states beside the decode."""
+    lib = R.lib()
+    lay = R.Layer(1, 8, 2, 1000, [0], n_sink=4, window=256)
+    call = lambda **o: lib.rtp_decode_step(  # noqa: E731
+        lay.desc(), FAKE, FAKE, FAKE, FAKE, FAKE, o.get("n", 600), o.get("ring", 0),
+        o.get("kr", FAKE), o.get("vr", FAKE), o.get("p", 0.9), 1.0, 0.088, FAKE, None,
+        o.get("ws", FAKE), o.get("wsb", 16), None)
+    assert call(ring=-1) == 4                         # RTP_ERR_RANGE
+    assert call(ring=255) == 4                        # shorter than the window
+    assert call(ring=300, kr=None) == 1               # a ring needs its buffers
+    assert call(n=0) == 4 and call(n=1001) == 4
+    assert call(p=1.5) == 4
+    assert call(wsb=16) == 6 and b"workspace" in lib.rtp_last_error()
+    assert lib.rtp_decode_step(R.Layer(1, 8, 2, 1000, [0], window=0).desc(), FAKE, FAKE, FAKE,
+                               FAKE, FAKE, 600, 0, None, None, 0.9, 1.0, 0.088, FAKE, None,
+                               FAKE, 1 << 30, None) == 4          # local heads need a window
+    # the step's workspace holds the retrieval decode's and the local segment states
+    step = R.workspace_size(lay, R.OP_DECODE_STEP, 600)
+    assert step > R.workspace_size(lay, R.OP_DECODE, 600)
+    # no local heads: the decode's workspace; no retrieval heads: the local heads' one
+    only_ret = R.Layer(1, 8, 2, 1000, [0, 1], window=256)
+    assert R.workspace_size(only_ret, R.OP_DECODE_STEP, 600) == \
+        R.workspace_size(only_ret, R.OP_DECODE, 600)
+    only_loc = R.Layer(1, 8, 2, 1000, [], window=256)
+    assert R.workspace_size(only_loc, R.OP_DECODE_STEP, 600) == \
+        R.workspace_size(only_loc, R.OP_SWA, 600)

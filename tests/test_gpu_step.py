@@ -110,3 +110,20 @@ def test_step_million_shaped_layer():
     ref = O.decode(wl, kc, vc, idx, 0.9, heads=heads)
     for (b, h), r in ref.items():
         P.check_out(step["out"][b, h], r["out"], f"local b{b} h{h}")
+
+
+@pytest.mark.parametrize("ret", [[], [0, 1, 2, 3]], ids=["local_only", "retrieval_only"])
+def test_step_with_one_kind_of_head(ret):
+    """A layer of local heads only runs the local-head kernel; a layer of retrieval heads
+    only gives the retrieval decode's bits."""
+    wl = W.random_decode(68, 2, 16, 4, 3000, ret, 500, n_needles=2 if ret else 0, n_sink=4)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx)
+    step = _step(dev, wl, 0.9, debug_cap=wl.N if ret else 0)
+    if ret:
+        sep = dev.decode(0.9, debug_cap=wl.N)
+        assert np.array_equal(step["out"], sep["out"])
+    else:
+        ring = (wl.window,) + _rings(wl, kc, vc, wl.window)
+        assert np.array_equal(_step(dev, wl, 0.9, ring=ring)["out"], step["out"])
+    P.compare_decode(wl, kc, vc, idx, step, 0.9)
