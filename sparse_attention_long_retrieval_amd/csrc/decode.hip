@@ -1213,7 +1213,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
     const unsigned long long want = (1ull << G) - 1ull;
     unsigned long long wv = 0ull;
     bool all = false;
-    for (unsigned it = 0; it < kSpinLimit && !all; ++it) {
+    for (unsigned it = 0; it < p.spin_limit && !all; ++it) {
       if (lane < G) wv = ld_dev(&mb[lane]);
       all = (__ballot(lane < G && (wv >> 63)) & want) == want;
       if (!all) __builtin_amdgcn_s_sleep(2);
@@ -2011,9 +2011,17 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   const char* env = getenv("RTP_DECODE_PASSES");
   const bool fused = p.budget == 0 && p.fusable && !(env && env[0] == '3') &&
                      (long long)p.P * p.nA <= pass_capacity<G>();
+  // RTP_DECODE_SPIN_LIMIT=n caps a fused wait at n polls: the tests force the give-up
+  // path with it (every kernel still ends normally)
+  DecPlan q = p;
+  q.spin_limit = kSpinLimit;
+  if (const char* sl = getenv("RTP_DECODE_SPIN_LIMIT")) {
+    const long v = strtol(sl, nullptr, 10);
+    if (v > 0 && v < (long)kSpinLimit) q.spin_limit = (unsigned)v;
+  }
   mark(0);
   if (fused) {
-    RTP_LAUNCH(k_pass<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, p);
+    RTP_LAUNCH(k_pass<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, q);
     mark(1);
     mark(2);
   } else {

@@ -149,6 +149,7 @@ struct DecPlan {
   unsigned long long* mbox;       // [P][nA][kMboxWords] per block and q-head: set bit 63,
                                   //           mode in bits 32-33, boundary key below
   unsigned* err;                  // [1]       a wait gave up (the call's results are void)
+  unsigned spin_limit;            // polls of a fused-pass wait before it gives up
   float* grp_m;                   // [P][nGrp][G]
   double* grp_z;                  // [P][nGrp][G]   relative to the upper edge of grp_m's bin
   unsigned long long* grp_bins;   // [P][nGrp][G][kNB]

@@ -375,3 +375,26 @@ def test_fused_pass_leaves_no_error_and_counters_at_rest():
         P.compare_decode(wl, kc, vc, idx, res, 0.9)
         counters = ws[:65536].view(torch.int32).cpu().numpy()
         assert not counters.any(), np.nonzero(counters)[0][:8]
+
+
+def test_fused_wait_give_up_raises_the_error_word(monkeypatch):
+    """Capped at one poll (RTP_DECODE_SPIN_LIMIT, a test hook), the blocks that do not
+    see their threshold at once give up: every kernel ends, the call's give-up word is
+    set, and after the documented zero-fill of the counter region the same workspace
+    gives the oracle's results again."""
+    import sparse_attention_long_retrieval_amd as R
+    wl = W.random_decode(71, 1, 8, 2, 300000, [0], 256, n_needles=2, q_scale=1.5)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx)
+    ws = torch.zeros(R.workspace_size(dev.layer, R.OP_DECODE, wl.N), dtype=torch.uint8,
+                     device="cuda")
+    monkeypatch.setenv("RTP_DECODE_SPIN_LIMIT", "1")
+    dev.decode(0.9, ws=ws)
+    err = ws[65532:65536].view(torch.int32).item()
+    assert err == 1, "no wait gave up at one poll"
+    monkeypatch.delenv("RTP_DECODE_SPIN_LIMIT")
+    ws[:65536].zero_()
+    res = dev.decode(0.9, debug_cap=wl.N, ws=ws)
+    assert ws[65532:65536].view(torch.int32).item() == 0
+    assert not ws[:65536].view(torch.int32).cpu().numpy().any()
+    P.compare_decode(wl, kc, vc, idx, res, 0.9)

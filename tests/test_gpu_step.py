@@ -127,3 +127,49 @@ def test_step_with_one_kind_of_head(ret):
         ring = (wl.window,) + _rings(wl, kc, vc, wl.window)
         assert np.array_equal(_step(dev, wl, 0.9, ring=ring)["out"], step["out"])
     P.compare_decode(wl, kc, vc, idx, step, 0.9)
+
+
+def test_step_graph_replay_matches_eager():
+    """Append + rtp_decode_step captured in one HIP graph gives the eager step's bits on
+    every replay, with other decode steps and torch work between the replays."""
+    wl = W.random_decode(69, 1, 32, 4, 60000, [0], 8192, n_needles=2, q_scale=1.5)
+    kc, vc, idx = O.caches_for(wl)
+    dev = P.Device(wl, kc, vc, idx)
+    N = wl.N
+    new_k = P.to_dev(wl.k_pre[:, :, N - 1:N])
+    new_v = P.to_dev(wl.v[:, :, N - 1:N])
+    w_k = P.to_dev(wl.w_k)
+    out = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.int16, device="cuda")
+    ws = torch.zeros(R.workspace_size(dev.layer, R.OP_DECODE_STEP, N), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(p=0.9, o=out):
+        R.index_append(dev.layer, new_k, new_v, w_k, N - 1, dev.kc, dev.vc, dev.idx)
+        R.decode_step(dev.layer, dev.q, dev.w_q, dev.kc, dev.vc, dev.idx, N, p, o, ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    other = torch.zeros_like(out)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager step"
+        step(0.5, other)
+        torch.cuda.synchronize()
+        _ = (other.float() * 2).sum().item()
+    assert not ws[:65536].view(torch.int32).cpu().numpy().any()
+    ref = O.decode(wl, kc, vc, idx, 0.9)
+    got = P.from_dev(out)
+    for (b, h), r in ref.items():
+        P.check_out(got[b, h], r["out"], f"graph b{b} h{h}")
