@@ -18,13 +18,16 @@
 namespace rtp {
 
 constexpr int kTileRows = 64;
-constexpr int kKvPitch = 128;     // bf16 elements per staged row (256 B, no padding)
+constexpr int kKvPitch = 128;     // bf16 elements per staged K row (256 B, no padding)
+constexpr int kVPitch = 144;      // per staged V row: 256 B + 32 B pad
 constexpr int kPartStride = 132;  // floats per partial state: m, l, pad, pad, o[128]
+constexpr int kDimBlocks = RTP_D / 16;  // 16-dimension blocks of the output
 
 // Staged K rows are swizzled: the 16-byte chunk c of row r (dimensions 8c .. 8c + 7)
 // sits at chunk c ^ (r & 15), so sixteen rows read at one logical chunk (the
-// matrix-core A operand) fall on sixteen different chunk positions.  V rows are read
-// whole (P.V, lane = a pair of dimensions) and stay in order.
+// matrix-core A operand of the logits) fall on sixteen different chunk positions.
+// V rows stay in order, padded by 8 banks so that the four consecutive rows the P.V
+// operand reads together sit on different banks.
 __device__ __forceinline__ int kv_chunk(int r, int c) { return c ^ (r & 15); }
 
 template <int G>
@@ -32,10 +35,26 @@ struct TileSmem {
   float qs[G][RTP_D];
   uint16_t qp[3][G][RTP_D];  // qs as three bf16 parts hi, mid, lo (qs = hi + mid + lo)
   uint16_t Ks[kTileRows][kKvPitch];
-  uint16_t Vs[kTileRows][kKvPitch];
+  uint16_t Vs[kTileRows][kVPitch];
   float ps[G][kTileRows];
+  uint16_t pp[2][G][kTileRows];  // probabilities as bf16 hi, lo in the P.V operand order
+  float os[G][RTP_D];        // the output state passed between layouts
+  float al[G];               // each head's rescale of the output in the current tile
   int rows[kTileRows];
   uint32_t masks[kTileRows];
+};
+
+// The output state of P.V on the matrix cores: wave w holds dimension blocks w, w + NW,
+// ... as 16 x 16 accumulators (lane: heads 4 (lane >> 4) .. + 3, dimension lane & 15).
+template <int NT>
+struct OutBlocks {
+  static constexpr int NW = NT / 64;
+  static constexpr int PER = (kDimBlocks + NW - 1) / NW;
+};
+// With G = 8 heads P.V runs on the vector ALUs, one wave per head (tile_compute).
+template <int G>
+struct ValuPv {
+  static constexpr bool on = G == 8;
 };
 
 // Rotate q (bf16, [D]) of head h at position pos with the fp64 frequency table
@@ -62,6 +81,8 @@ __device__ __forceinline__ void load_q_ready(TileSmem<G>& sm, const float* src) 
 
 typedef __bf16 tile_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float tile_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t tile_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t tile_u16x8 __attribute__((ext_vector_type(8)));
 
 // Split the queries in sm.qs into the bf16 parts of sm.qp.  hi = bf16(q), mid =
 // bf16(q - hi), lo = bf16(q - hi - mid): each difference is exact in fp32 and the
@@ -83,16 +104,20 @@ __device__ __forceinline__ void prepare_q_parts(TileSmem<G>& sm) {
 }
 
 // Logits, online softmax and P.V of one staged tile of nr rows (K, V and the row
-// masks in LDS; the query parts in sm.qp).  The logits run on the matrix cores:
-// v_mfma_f32_16x16x32_bf16 with A = 16 key rows x 32 dimensions straight from the
-// staged tile (lane: row lane & 15, dimensions 8 (lane >> 4) .. + 7) and B = the
-// query parts of 16 head columns (heads >= G are zero), summed lo, mid, hi; one wave
-// per block of 16 rows.  Wave h < G then runs head h's online softmax (lane = row)
-// and P.V (lane = a pair of output dimensions).  All NT threads call it; it ends
-// with a barrier.
+// masks in LDS; the query parts in sm.qp; V rows past nr finite).  Logits run on
+// v_mfma_f32_16x16x32_bf16: A = 16 staged K rows x 32 dimensions (lane: row lane & 15,
+// dimensions 8 (lane >> 4) .. + 7), B = the query parts of 16 head columns (heads >= G
+// are zero), summed lo, mid, hi; one wave per block of 16 rows.  Wave h < G then runs
+// head h's online softmax (lane = row).  P.V, with G < 8: on the same instruction, A =
+// the probabilities of 16 head rows x 32 key rows as two bf16 parts (hi + lo within
+// 2^-17 of p), B = 32 V rows x 16 dimensions (lane: dimension lane & 15, rows kb + 4 j
+// with kb = lane >> 4); wave w accumulates its dimension blocks in oc.  With G = 8 every
+// wave owns a head and the matrix instruction would leave half its columns empty, so
+// wave h accumulates head h on the vector ALUs instead (lane = a pair of dimensions,
+// oc[0][0..1]).  All NT threads call it; it ends with a barrier.
 template <int G, int NT>
 __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, float& l,
-                                             float& o0, float& o1) {
+                                             tile_f32x4 (&oc)[OutBlocks<NT>::PER]) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int h = tid >> 6, lane = tid & 63;
@@ -117,55 +142,137 @@ __device__ __forceinline__ void tile_compute(TileSmem<G>& sm, int nr, float& m, 
     }
   }
   __syncthreads();
-  float alpha = 1.f;
+  float alpha = 1.f, p = 0.f;
   if (h < G) {
     const bool valid = lane < nr && ((sm.masks[lane] >> h) & 1u);
     const float logit = valid ? sm.ps[h][lane] : -INFINITY;
     const float tmax = wave_max(logit);
     const float m_new = fmaxf(m, tmax);
-    const float p = valid ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
+    p = valid ? __builtin_amdgcn_exp2f(logit - m_new) : 0.f;
     alpha = (m == -INFINITY) ? 0.f : exp2f(m - m_new);
     l = l * alpha + wave_sum(p);
-    sm.ps[h][lane] = p;
     m = m_new;
   }
-  __syncthreads();
-  if (h < G) {
-    float a0 = o0 * alpha, a1 = o1 * alpha;
-    int r = 0;
-    // eight rows at a time: their probabilities and V words are requested together
-    for (; r + 8 <= nr; r += 8) {
-      const float4 pa = *(const float4*)&sm.ps[h][r];
-      const float4 pb = *(const float4*)&sm.ps[h][r + 4];
-      uint32_t vv[8];
+  if constexpr (ValuPv<G>::on) {
+    if (h < G) {
+      sm.ps[h][lane] = p;  // read back by this wave only
+      float a0 = oc[0][0] * alpha, a1 = oc[0][1] * alpha;
+      int r = 0;
+      // eight rows at a time: their probabilities and V words are requested together
+      for (; r + 8 <= nr; r += 8) {
+        const float4 pa = *(const float4*)&sm.ps[h][r];
+        const float4 pb = *(const float4*)&sm.ps[h][r + 4];
+        uint32_t vv[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) vv[u] = *(const uint32_t*)&sm.Vs[r + u][2 * lane];
-      const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        for (int u = 0; u < 8; ++u) vv[u] = *(const uint32_t*)&sm.Vs[r + u][2 * lane];
+        const float pr[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a0 = fmaf(pr[u], bf16_lo(vv[u]), a0);
-        a1 = fmaf(pr[u], bf16_hi(vv[u]), a1);
+        for (int u = 0; u < 8; ++u) {
+          a0 = fmaf(pr[u], bf16_lo(vv[u]), a0);
+          a1 = fmaf(pr[u], bf16_hi(vv[u]), a1);
+        }
+      }
+      for (; r < nr; ++r) {
+        const float pr = sm.ps[h][r];
+        const uint32_t vv = *(const uint32_t*)&sm.Vs[r][2 * lane];
+        a0 = fmaf(pr, bf16_lo(vv), a0);
+        a1 = fmaf(pr, bf16_hi(vv), a1);
+      }
+      oc[0][0] = a0;
+      oc[0][1] = a1;
+    }
+  } else {
+    if (h < G) {
+      // p as bf16 hi + lo (hi + lo within 2^-17 p), stored in the P.V operand order:
+      // row 32 kc + kb + 4 j at 32 kc + 8 kb + j
+      const int at = (lane & 32) + 8 * (lane & 3) + ((lane >> 2) & 7);
+      const uint16_t hi = f32_to_bf16(p);
+      sm.pp[0][h][at] = hi;
+      sm.pp[1][h][at] = f32_to_bf16(p - bf16_to_f32(hi));
+      if (lane == 0) sm.al[h] = alpha;
+    }
+    __syncthreads();
+    float ar[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ar[i] = 4 * kb + i < G ? sm.al[4 * kb + i < G ? 4 * kb + i : 0] : 0.f;
+#pragma unroll
+    for (int b = 0; b < OutBlocks<NT>::PER; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oc[b][i] *= ar[i];
+    }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      // A operands: head row n's probabilities (zero for heads >= G) for key rows
+      // 32 kc + kb + 4 j (j = 0 .. 7), hi and lo; shared by the wave's dimension blocks
+      tile_u32x4 phi = {0u, 0u, 0u, 0u}, plo = {0u, 0u, 0u, 0u};
+      if (n < G) {
+        phi = *(const tile_u32x4*)&sm.pp[0][n < G ? n : 0][32 * kc + 8 * kb];
+        plo = *(const tile_u32x4*)&sm.pp[1][n < G ? n : 0][32 * kc + 8 * kb];
+      }
+#pragma unroll
+      for (int b = 0; b < OutBlocks<NT>::PER; ++b) {
+        const int nb = h + b * NW;
+        if (nb < kDimBlocks) {
+          tile_u16x8 vb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vb[j] = sm.Vs[32 * kc + kb + 4 * j][16 * nb + n];
+          const tile_bf16x8 bv = __builtin_bit_cast(tile_bf16x8, vb);
+          oc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(tile_bf16x8, plo),
+                                                          bv, oc[b], 0, 0, 0);
+          oc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(tile_bf16x8, phi),
+                                                          bv, oc[b], 0, 0, 0);
+        }
       }
     }
-    for (; r < nr; ++r) {
-      const float pr = sm.ps[h][r];
-      const uint32_t vv = *(const uint32_t*)&sm.Vs[r][2 * lane];
-      a0 = fmaf(pr, bf16_lo(vv), a0);
-      a1 = fmaf(pr, bf16_hi(vv), a1);
-    }
-    o0 = a0;
-    o1 = a1;
   }
   __syncthreads();
 }
 
+// The empty output state in the layout of tile_compute.
+template <int NT>
+__device__ __forceinline__ void out_blocks_clear(tile_f32x4 (&oc)[OutBlocks<NT>::PER]) {
+#pragma unroll
+  for (int b = 0; b < OutBlocks<NT>::PER; ++b) oc[b] = tile_f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// The output state from the layout of tile_compute to (o0, o1) of wave h < G (lane =
+// a pair of dimensions).  All NT threads call it.
+template <int G, int NT>
+__device__ __forceinline__ void blocks_to_out(TileSmem<G>& sm, const tile_f32x4 (&oc)[OutBlocks<NT>::PER],
+                                              float& o0, float& o1) {
+  if constexpr (ValuPv<G>::on) {
+    o0 = oc[0][0];
+    o1 = oc[0][1];
+  } else {
+    constexpr int NW = NT / 64;
+    const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int b = 0; b < OutBlocks<NT>::PER; ++b) {
+      const int nb = h + b * NW;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * (lane >> 4) + i;
+        if (nb < kDimBlocks && hd < G) sm.os[hd][16 * nb + (lane & 15)] = oc[b][i];
+      }
+    }
+    __syncthreads();
+    if (h < G) {
+      o0 = sm.os[h][2 * lane];
+      o1 = sm.os[h][2 * lane + 1];
+    }
+    __syncthreads();
+  }
+}
+
 // Attend one tile of nr rows (ids in sm.rows, per-row head masks in sm.masks).
 // kbase / vbase point at row 0 of this KV head's cache; the caller has run
-// prepare_q_parts since it last wrote sm.qs.  All NT threads call it.
+// prepare_q_parts since it last wrote sm.qs.  The running state is (m, l) of wave
+// h < G and the output blocks oc (start: m = -inf, l = 0, out_blocks_clear; end:
+// blocks_to_out).  All NT threads call it.
 template <int G, int NT>
 __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kbase,
                                             const uint16_t* vbase, int nr, float& m, float& l,
-                                            float& o0, float& o1) {
+                                            tile_f32x4 (&oc)[OutBlocks<NT>::PER]) {
   const int tid = threadIdx.x;
   for (int c = tid; c < kTileRows * 16; c += NT) {
     const int r = c >> 4, q = c & 15;
@@ -173,10 +280,12 @@ __device__ __forceinline__ void tile_attend(TileSmem<G>& sm, const uint16_t* kba
       const size_t off = (size_t)sm.rows[r] * RTP_D + q * 8;
       *(uint4*)&sm.Ks[r][kv_chunk(r, q) * 8] = *(const uint4*)(kbase + off);
       *(uint4*)&sm.Vs[r][q * 8] = *(const uint4*)(vbase + off);
+    } else {
+      *(uint4*)&sm.Vs[r][q * 8] = make_uint4(0, 0, 0, 0);  // zero weight times finite values
     }
   }
   __syncthreads();
-  tile_compute<G, NT>(sm, nr, m, l, o0, o1);
+  tile_compute<G, NT>(sm, nr, m, l, oc);
 }
 
 // One row of a list to attend: its id in the cache and its head mask.
@@ -186,18 +295,23 @@ struct RowMask {
 };
 
 // Attend rows get(0) .. get(n - 1) in tiles of 64, with the next tile's K and V rows
-// loaded into registers while the current one is computed.  Rows past the end of the
-// list re-read the last row (their lanes are masked), so the loads need no branch.
-// All NT threads call it; get(i) must give every thread the same entry i (it reads a
-// list the block shares, in LDS), and the list must not change until it returns.
+// loaded into registers while the current one is computed, from the empty state:
+// (m, l, o0, o1) of wave h < G receive the result.  Rows past the end of the list
+// re-read the last row (their lanes are masked), so the loads need no branch.  All NT
+// threads call it; get(i) must give every thread the same entry i (it reads a list the
+// block shares, in LDS), and the list must not change until it returns.
 template <int G, int NT, class Get>
 __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kbase,
                                             const uint16_t* vbase, int n, Get&& get, float& m,
                                             float& l, float& o0, float& o1) {
   constexpr int PER = kTileRows * 16 / NT;  // 16-byte pieces of K (and of V) per thread
   static_assert(PER * NT == kTileRows * 16, "the threads cover a tile");
+  m = -INFINITY;
+  l = o0 = o1 = 0.f;
   if (n <= 0) return;
   prepare_q_parts<G, NT>(sm);
+  tile_f32x4 oc[OutBlocks<NT>::PER];
+  out_blocks_clear<NT>(oc);
   const int tid = threadIdx.x;
   // native vectors: a uint4 struct would be copied to LDS through private memory
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -226,8 +340,9 @@ __device__ __forceinline__ void attend_list(TileSmem<G>& sm, const uint16_t* kba
         vr[u] = *(const u32x4*)(vbase + off);
       }
     }
-    if (t0 >= 0) tile_compute<G, NT>(sm, nr, m, l, o0, o1);
+    if (t0 >= 0) tile_compute<G, NT>(sm, nr, m, l, oc);
   }
+  blocks_to_out<G, NT>(sm, oc, o0, o1);
 }
 
 // Cross-block data of one launch goes through device-coherent accesses: relaxed

@@ -459,6 +459,8 @@ __global__ __launch_bounds__(kClThreads) void k_cl_attend(ClDecPlan p) {
   const int hi = (int)(((long long)rows.R * (f + 1)) / p.nF);
   const size_t head_base = ((size_t)b * p.Hkv + kv) * p.max_seq * kD;
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  tile_f32x4 oc[OutBlocks<NT>::PER];
+  out_blocks_clear<NT>(oc);
   for (int c0 = lo; c0 < hi; c0 += kTileRows) {
     int tok = -1;
     if (tid < kTileRows && c0 + tid < hi) tok = rows.token(c0 + tid, p.n_tok, p.n_sink);
@@ -474,9 +476,10 @@ __global__ __launch_bounds__(kClThreads) void k_cl_attend(ClDecPlan p) {
     }
     __syncthreads();
     const int nr = (int)nr_s;
-    if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+    if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, oc);
     __syncthreads();
   }
+  blocks_to_out<1, NT>(sm, oc, o0, o1);
   if (wave == 0) {
     float* dst = p.partF + ((size_t)unit * p.nF + f) * kPartStride;
     if (lane == 0) {

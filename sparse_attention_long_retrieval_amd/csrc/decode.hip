@@ -1768,6 +1768,8 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
     __syncthreads();  // every read of the candidate space is done
     if (tid < kD) sm.qs[0][tid] = qv;
     prepare_q_parts<1, NT>(sm);
+    tile_f32x4 oc[OutBlocks<NT>::PER];
+    out_blocks_clear<NT>(oc);
     // list too long for LDS: this block walks its range of pass-B blocks
     const int b_lo = (int)(((long long)p.nA * f) / p.nF);
     const int b_hi = (int)(((long long)p.nA * (f + 1)) / p.nF);
@@ -1793,10 +1795,11 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
         }
         __syncthreads();
         const int nr = (int)nr_s;
-        if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, o0, o1);
+        if (nr) tile_attend<1, NT>(sm, p.k_cache + head_base, p.v_cache + head_base, nr, m, l, oc);
         __syncthreads();
       }
     }
+    blocks_to_out<1, NT>(sm, oc, o0, o1);
   }
   {
     // the block's state: its share of the index pass's partials in order (each wave
