@@ -1661,9 +1661,17 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
   // up to kTokCap candidates: keys and tokens in LDS; up to kKeyCap: keys only
   const bool in_lds = small_nA && C <= (unsigned)kTokCap;
   const bool keys_lds = small_nA && C <= (unsigned)kKeyCap;
-  if (keys_lds && C > 0) {
-    // gather into LDS in canonical order; each thread copies whole blocks, with
-    // the loads of a block issued together
+  // one candidate into its LDS slot (canonical order)
+  auto put = [&](unsigned g, float2 e) {
+    key_s[g] = f32_ord(e.x);
+    if (in_lds) {
+      tok_s[g] = __float_as_int(e.y);
+      wt_s[g] = cand_w(e.x);
+    }
+  };
+  if (keys_lds && C > 0 && p.nA >= NT) {
+    // gather into LDS: with a pass-B block per thread or more, each thread copies
+    // whole blocks, the loads of a block issued together
     for (int bb = tid; bb < p.nA; bb += NT) {
       const unsigned n = blk_cnt[bb], o = boff[bb];
       const float2* src = cand + (size_t)bb * kPassTokens;
@@ -1673,15 +1681,35 @@ __global__ __launch_bounds__(kFinishThreads) void k_finish(DecPlan p) {
         for (int u = 0; u < 16; ++u)
           if (c0 + u < n) e[u] = src[c0 + u];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (c0 + u < n) {
-            key_s[o + c0 + u] = f32_ord(e[u].x);
-            if (in_lds) {
-              tok_s[o + c0 + u] = __float_as_int(e[u].y);
-              wt_s[o + c0 + u] = cand_w(e[u].x);
-            }
-          }
+        for (int u = 0; u < 16; ++u)
+          if (c0 + u < n) put(o + c0 + u, e[u]);
+      }
+    }
+  } else if (keys_lds && C > 0) {
+    // with fewer blocks than threads: each candidate slot is first marked with its
+    // pass-B block (the slots of block bb are boff[bb] .. + blk_cnt[bb]); then thread
+    // t copies candidates t, t + NT, ... (consecutive threads read consecutive entries
+    // of a block's list), sixteen loads in flight, each into the slot that named it
+    for (int bb = tid; bb < p.nA; bb += NT) {
+      const unsigned o = boff[bb], n = (bb + 1 < p.nA ? boff[bb + 1] : C) - o;
+      for (unsigned i = 0; i < n; ++i) key_s[o + i] = (uint32_t)bb;
+    }
+    __syncthreads();
+    constexpr int kGB = 16;
+    for (unsigned c0 = 0; c0 < C; c0 += kGB * NT) {
+      float2 e[kGB];
+#pragma unroll
+      for (int u = 0; u < kGB; ++u) {
+        const unsigned g = c0 + u * NT + tid;
+        if (g < C) {
+          const unsigned bb = key_s[g];
+          e[u] = cand[(size_t)bb * kPassTokens + (g - boff[bb])];
         }
+      }
+#pragma unroll
+      for (int u = 0; u < kGB; ++u) {
+        const unsigned g = c0 + u * NT + tid;
+        if (g < C) put(g, e[u]);
       }
     }
   }
