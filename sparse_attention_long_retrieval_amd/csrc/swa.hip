@@ -12,6 +12,8 @@
 #include "rtp_internal.h"
 #include "swa_segment.h"
 
+#include <mutex>
+
 namespace rtp {
 
 template <int G>
@@ -38,16 +40,42 @@ hipError_t launch_swa_decode(const SwaPlan& p, hipStream_t s) {
 
 static size_t align256s(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Blocks of k_swa_decode<G> that run at once on the current device (occupancy of its
+// launch bounds times the compute units), found once per device and group size; 512
+// when the device cannot be queried.
+constexpr int kSwaMaxDevices = 64;
+static long long swa_capacity(int G) {
+  static std::mutex mu;
+  static long long cap[kSwaMaxDevices][4];
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSwaMaxDevices) return 512;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cap[dev][gi] == 0) {
+    const void* fn = G == 1   ? (const void*)k_swa_decode<1>
+                     : G == 2 ? (const void*)k_swa_decode<2>
+                     : G == 4 ? (const void*)k_swa_decode<4>
+                              : (const void*)k_swa_decode<8>;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * G, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0)
+      return 512;
+    cap[dev][gi] = (long long)per_cu * cus;
+  }
+  return cap[dev][gi];
+}
+
 // Decode sizing: rows = window rows + sinks outside the window; segments of a
-// multiple of 64 rows, about kSwaBlocks of them over all units (two blocks per CU:
-// enough loads in flight to stream the window, and several tiles per block to
-// overlap the next tile's loads with the current one's arithmetic when the
-// windows are long).
-constexpr int kSwaBlocks = 512;
+// multiple of 64 rows, as many over all units as blocks that run at once (each block
+// streams its segment a tile ahead, so the bytes in flight grow with the resident
+// blocks; several tiles per block overlap the next tile's loads with the current
+// one's arithmetic when the windows are long).
 size_t swa_workspace(int B, int n_loc, int G, int Tq, int rows, SwaPlan* plan, char* base) {
   (void)Tq;
   const int units = B * n_loc;
-  int nSeg = units > 0 ? (kSwaBlocks + units - 1) / units : 1;
+  const long long blocks = swa_capacity(G);
+  int nSeg = units > 0 ? (int)((blocks + units - 1) / units) : 1;
   const int max_seg = (rows + kTileRows - 1) / kTileRows;
   if (nSeg > max_seg) nSeg = max_seg;
   if (nSeg < 1) nSeg = 1;
