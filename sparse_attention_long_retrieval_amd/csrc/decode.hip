@@ -187,10 +187,19 @@ __device__ __forceinline__ void score_tiles(const uint4 (&a)[ScoreTiles<G>::TPW]
 
 // Token of the block for output r of tile T (see the lane roles above).
 template <int G>
-__device__ __forceinline__ int score_token(int T, int r) {
+__device__ __forceinline__ int score_token(int T, int r, int tx = threadIdx.x) {
   using S = ScoreTiles<G>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tx >> 6, lane = tx & 63;
   return (wave * S::TPW + T) * S::TILE + S::R * (4 * (lane >> 4) + r) + (lane & 15) / S::GE;
+}
+
+// threadIdx.x as a value the compiler cannot relate to its earlier uses: token
+// offsets needed again long after the scan are recomputed from it instead of being
+// kept live (or spilled) across the whole pass.
+__device__ __forceinline__ int opaque_tid() {
+  int tx = threadIdx.x;
+  asm volatile("" : "+v"(tx));
+  return tx;
 }
 
 // Reduce over the lanes of one head (lanes equal modulo GE).
@@ -1267,6 +1276,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
       uint8_t* const dm8 = reinterpret_cast<uint8_t*>(dmask);
       uint8_t* const cm8 = reinterpret_cast<uint8_t*>(cmask);
       const unsigned hm = (1u << G) - 1u;
+      const int txo = opaque_tid();
       const int first = lane - h;
       uint32_t cbits = 0u;
 #pragma unroll
@@ -1277,10 +1287,10 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
           const unsigned long long bd = __ballot(sv >= dthr_f);
           const bool c = sv < dthr_f && sv >= clo_f;
           cbits |= (uint32_t)c << (4 * T + r);
-          if (h == 0) dm8[score_token<G>(T, r)] = (uint8_t)((unsigned)(bd >> first) & hm);
+          if (h == 0) dm8[score_token<G>(T, r, txo)] = (uint8_t)((unsigned)(bd >> first) & hm);
           if (inspect) {
             const unsigned long long bc = __ballot(c);
-            if (h == 0) cm8[score_token<G>(T, r)] = (uint8_t)((unsigned)(bc >> first) & hm);
+            if (h == 0) cm8[score_token<G>(T, r, txo)] = (uint8_t)((unsigned)(bc >> first) & hm);
           }
         }
       const unsigned ccount = (unsigned)__popc(cbits);
@@ -1301,7 +1311,7 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if ((cbits >> (4 * T + r)) & 1u)
-              *cd++ = make_float2(sc[T][r], __int_as_float(tok0 + score_token<G>(T, r)));
+              *cd++ = make_float2(sc[T][r], __int_as_float(tok0 + score_token<G>(T, r, txo)));
       }
       if (tid < G) {
         unsigned tot = 0u;
