@@ -36,9 +36,8 @@ struct TileSmem {
   uint16_t qp[3][G][RTP_D];  // qs as three bf16 parts hi, mid, lo (qs = hi + mid + lo)
   uint16_t Ks[kTileRows][kKvPitch];
   uint16_t Vs[kTileRows][kVPitch];
-  float ps[G][kTileRows];
+  alignas(16) float ps[G][kTileRows];
   uint16_t pp[2][G][kTileRows];  // probabilities as bf16 hi, lo in the P.V operand order
-  float os[G][RTP_D];        // the output state passed between layouts
   float al[G];               // each head's rescale of the output in the current tile
   int rows[kTileRows];
   uint32_t masks[kTileRows];
@@ -236,7 +235,8 @@ __device__ __forceinline__ void out_blocks_clear(tile_f32x4 (&oc)[OutBlocks<NT>:
 }
 
 // The output state from the layout of tile_compute to (o0, o1) of wave h < G (lane =
-// a pair of dimensions).  All NT threads call it.
+// a pair of dimensions), after the last tile (it reuses the K tile).  All NT threads
+// call it.
 template <int G, int NT>
 __device__ __forceinline__ void blocks_to_out(TileSmem<G>& sm, const tile_f32x4 (&oc)[OutBlocks<NT>::PER],
                                               float& o0, float& o1) {
@@ -244,6 +244,9 @@ __device__ __forceinline__ void blocks_to_out(TileSmem<G>& sm, const tile_f32x4 
     o0 = oc[0][0];
     o1 = oc[0][1];
   } else {
+    // the exchange goes through the K tile, free once the last tile is computed
+    static_assert(sizeof(float) * G * RTP_D <= sizeof(sm.Ks), "the state fits the K tile");
+    float (*const os)[RTP_D] = reinterpret_cast<float (*)[RTP_D]>(&sm.Ks[0][0]);
     constexpr int NW = NT / 64;
     const int h = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
@@ -252,13 +255,13 @@ __device__ __forceinline__ void blocks_to_out(TileSmem<G>& sm, const tile_f32x4 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hd = 4 * (lane >> 4) + i;
-        if (nb < kDimBlocks && hd < G) sm.os[hd][16 * nb + (lane & 15)] = oc[b][i];
+        if (nb < kDimBlocks && hd < G) os[hd][16 * nb + (lane & 15)] = oc[b][i];
       }
     }
     __syncthreads();
     if (h < G) {
-      o0 = sm.os[h][2 * lane];
-      o1 = sm.os[h][2 * lane + 1];
+      o0 = os[h][2 * lane];
+      o1 = os[h][2 * lane + 1];
     }
     __syncthreads();
   }

@@ -815,7 +815,7 @@ constexpr unsigned kSpinLimit = 1u << 18;
 // then classify their registered scores and attend their definite rows as the
 // select kernel does, without reading the index a second time.
 template <int G>
-__global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
+__global__ __launch_bounds__(PassCfg<G>::NT, (G == 8 ? 4 : 3)) void k_pass(DecPlan p) {
   using S = ScoreTiles<G>;
   constexpr int NT = PassCfg<G>::NT, TPT = PassCfg<G>::TPT, NW = PassCfg<G>::NW;
   constexpr int WQ_VEC = G * kD * kR / 8;
@@ -854,8 +854,13 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   __shared__ unsigned long long zred[NW][G];
   __shared__ float bscale[kNB];
   __shared__ unsigned long long gb[G][kNB];
-  __shared__ double ms[G][kNB];
-  __shared__ float mk_s[kMaxGroups][G];
+  // the merges' bin masses and summary maxima sit in the tiles' probability space,
+  // unused until the block attends (a merging block attends only after its wait)
+  static_assert(sizeof(double) * G * kNB <= sizeof(sm.ps) &&
+                    sizeof(float) * kMaxGroups * G <= sizeof(sm.pp),
+                "the merge arrays fit the probability space");
+  double (*const ms)[kNB] = reinterpret_cast<double (*)[kNB]>(&sm.ps[0][0]);
+  float (*const mk_s)[G] = reinterpret_cast<float (*)[G]>(&sm.pp[0][0][0]);
   __shared__ float gm_s[G];
   __shared__ double gz_s[G];
   __shared__ int kb_s[G], mode_s[G];
@@ -863,7 +868,20 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
   __shared__ unsigned cwsum[NW][G];
   __shared__ unsigned wsum[NW];
   __shared__ unsigned n_list_s, ubase_s, ucount_s;
-  __shared__ float qs_keep[G * kD];
+  // the retrieval queries, kept while the block attends local segments: the list space
+  // is free between the summary and the compaction
+  static_assert(sizeof(float) * G * kD <= sizeof(lb), "the queries fit the list space");
+  float* const qs_keep = reinterpret_cast<float*>(lb);
+
+  // ---- blocks of the extra rows (room the pass leaves on the GPU): local-head window
+  // segments only, the first items_x of them in turn; they take no part in the scan,
+  // the threshold or the waits
+  if (pair >= p.P) {
+    const int X = p.xr * p.nA, j = (pair - p.P) * p.nA + blk;
+    for (int it = j; it < p.items_x; it += X)
+      swa_decode_segment<G, NT>(p.sw, sm, it / p.sw.nSeg, it % p.sw.nSeg);
+    return;
+  }
 
   // ---- scan: projection, queries and the index tile requested together
   uint4 wreg[WQ_PER];
@@ -1194,14 +1212,16 @@ __global__ __launch_bounds__(PassCfg<G>::NT, 4) void k_pass(DecPlan p) {
     }
   }
   // ---- local heads of a decode step: window segments, run while the threshold is
-  // being found.  Each merge group owns an equal share of the segments, taken in
-  // arrival order by the blocks that do not merge (the only block of a one-block group
-  // takes them all), so the merging blocks are not held up.  Which block runs a segment
-  // changes no result.  The retrieval queries wait aside in LDS meanwhile.
+  // being found.  Each merge group owns an equal share of the segments the extra rows
+  // do not take, taken in arrival order by the blocks that do not merge (the only block
+  // of a one-block group takes them all), so the merging blocks are not held up.  Which
+  // block runs a segment changes no result.  The retrieval queries wait aside in LDS
+  // meanwhile.
   if (p.with_swa) {
-    const int items = p.B * p.sw.n_loc * p.sw.nSeg;
+    const int items = p.B * p.sw.n_loc * p.sw.nSeg - p.items_x;
     const long long gg = (long long)pair * p.nGrp + grp, ngg = (long long)p.P * p.nGrp;
-    const int i0 = (int)(items * gg / ngg), i1 = (int)(items * (gg + 1) / ngg);
+    const int i0 = p.items_x + (int)(items * gg / ngg);
+    const int i1 = p.items_x + (int)(items * (gg + 1) / ngg);
     const int workers = nin > 1 ? nin - 1 : 1;
     const int first = nin > 1 ? (grp_rank + 1u == (unsigned)nin ? i1 : i0 + (int)grp_rank) : i0;
     if (first < i1) {
@@ -2040,6 +2060,16 @@ static long long pass_capacity() {
   return cap[dev];
 }
 
+static long long pass_capacity_of(int G) {
+  switch (G) {
+    case 1: return pass_capacity<1>();
+    case 2: return pass_capacity<2>();
+    case 4: return pass_capacity<4>();
+    case 8: return pass_capacity<8>();
+    default: return 0;
+  }
+}
+
 template <int G>
 static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   auto mark = [&](int k) {
@@ -2051,7 +2081,7 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   // RTP_DECODE_PASSES=3 in the environment forces the three launches.
   const char* env = getenv("RTP_DECODE_PASSES");
   const bool fused = p.budget == 0 && p.fusable && !(env && env[0] == '3') &&
-                     (long long)p.P * p.nA <= pass_capacity<G>();
+                     (long long)(p.P + p.xr) * p.nA <= pass_capacity<G>();
   // RTP_DECODE_SPIN_LIMIT=n caps a fused wait at n polls: the tests force the give-up
   // path with it (every kernel still ends normally)
   DecPlan q = p;
@@ -2062,7 +2092,7 @@ static hipError_t launch_decode_g(const DecPlan& p, hipStream_t s) {
   }
   mark(0);
   if (fused) {
-    RTP_LAUNCH(k_pass<G>, dim3(p.nA, p.P), dim3(PassCfg<G>::NT), s, q);
+    RTP_LAUNCH(k_pass<G>, dim3(p.nA, p.P + p.xr), dim3(PassCfg<G>::NT), s, q);
     mark(1);
     mark(2);
   } else {
@@ -2128,9 +2158,14 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
   // every block of the fused pass runs about one (several when the local heads
   // outnumber the blocks); the group merges as in the local-head decode kernel.
   const int units = B * n_loc;
-  int sSeg = 0, sRows = 0, sGsz = 0, sGrp = 0;
+  int sSeg = 0, sRows = 0, sGsz = 0, sGrp = 0, xr = 0, items_x = 0;
   if (units > 0 && swa_rows > 0) {
-    const long long blocks = (long long)P * nA;
+    // room the pass leaves on the GPU (its blocks resident at once, less its own grid)
+    // becomes extra rows of blocks that run local segments only
+    const long long cap = pass_capacity_of(G);
+    if (cap > (long long)P * nA)
+      xr = (int)std::min<long long>((cap - (long long)P * nA) / nA, kMaxGridY - P);
+    const long long blocks = (long long)(P + xr) * nA;
     sSeg = (int)std::max(1LL, blocks / units);
     sSeg = std::min(sSeg, (swa_rows + kTileRows - 1) / kTileRows);
     sRows = (swa_rows + sSeg - 1) / sSeg;
@@ -2139,6 +2174,11 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
     sGsz = 4;
     while (sGsz * sGsz < sSeg) ++sGsz;
     sGrp = (sSeg + sGsz - 1) / sGsz;
+    // the extra blocks start at once, the others after their scan: a share of the
+    // segments in proportion to the workers (the merging blocks take none)
+    const long long items = (long long)units * sSeg, X = (long long)xr * nA;
+    const long long W = X + (long long)P * (nA - nGrp);
+    items_x = W > 0 ? (int)(items * X / W) : 0;
   }
   // the counters (fused pass, finish arrivals, local-head merges) and the fused pass's
   // mailboxes live in the counter region (zero at rest); the last word is the give-up flag
@@ -2187,6 +2227,8 @@ size_t decode_workspace(int B, int n_ret, int G, int N, DecPlan* plan, char* bas
       plan->sw.partg = (float*)spg;
       plan->sw.defer_merge = 1;  // the finish kernel merges the segments in order
     }
+    plan->xr = xr;
+    plan->items_x = items_x;
     plan->fusable = fusable;
     plan->nGrp = nGrp;
     unsigned* cnt = (unsigned*)base;

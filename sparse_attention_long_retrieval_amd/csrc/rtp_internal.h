@@ -146,6 +146,9 @@ struct DecPlan {
   // local heads run by the fused pass while it waits for the threshold (decode step)
   int with_swa;
   SwaPlan sw;
+  int xr;                         // extra grid rows of the fused pass: blocks that run
+                                  //           local segments only (room the pass leaves)
+  int items_x;                    // local segments taken by those blocks (the first ones)
   unsigned long long* mbox;       // [P][nA][kMboxWords] per block and q-head: set bit 63,
                                   //           mode in bits 32-33, boundary key below
   unsigned* err;                  // [1]       a wait gave up (the call's results are void)
