@@ -20,24 +20,25 @@
 //                 are ranges of D, so levels nest exactly and every sweep sorts a
 //                 key into the same bin.  Sweeps over the keys:
 //                   A  max score m per vector;
-//                   B  mass histogram over 128 bins of a window of D: a bin holds
-//                      its key count and the sum of exp(s - edge) relative to its
-//                      upper edge in 2^-21 units, packed in one 64-bit word (one
-//                      LDS atomic per key); keys below the first window collect
-//                      in a tail bin for Z.  The boundary bin is where the running
-//                      mass reaches p * Z; a boundary below the window moves the
-//                      window down, a boundary bin with more keys than one
-//                      candidate list holds is refined into 128 sub-bins (levels
-//                      of 2^14, 2^7 and 1 depth codes: 0.125, 9.8e-4, 7.6e-6
-//                      score units);
-//                   C  definite keys (above the boundary bin) as 32-bit words per
-//                      32-key block, boundary-bin keys as candidates; each wave
-//                      keeps its own word and candidate lists, filled in program
+//                   B  mass histogram over 128 bins of 2^14 codes (0.125 score
+//                      units) of a window of D: a bin holds its key count and the
+//                      sum of exp(s - edge) relative to its upper edge in 2^-21
+//                      units, packed in one 64-bit word (one LDS atomic per key);
+//                      keys below the first window collect in a tail bin for Z.
+//                      The boundary bin is where the running mass reaches p * Z;
+//                      a boundary below the window moves the window down;
+//                   C  definite keys (above the boundary bin) and candidates (the
+//                      boundary bin's keys) as 32-bit words per 32-key block;
+//                      each wave keeps its own two word lists, filled in program
 //                      order, so the lists (and the attention's row order) are
-//                      the same on every run.
-//   k_pf_resolve  exact threshold inside the boundary bin: bisection on the
-//                 ordered fp32 score with 2^-36 fixed-point masses (one wave per
-//                 vector).
+//                      the same on every run.  A list holds every block of the
+//                      wave's key range, so no boundary bin is ever too large.
+//   k_pf_resolve  exact threshold inside the boundary bin, one wave per vector:
+//                 the candidates' scores are recomputed as the fp32 rounding of
+//                 their exact dot products (the rounding of the exact sum, as the
+//                 definition of the score has it), a radix select over those
+//                 scores with 2^-36 fixed-point masses finds the threshold, and
+//                 the candidate words are rewritten to the selected keys.
 //   k_pf_count    cut the attend work into items (a vector with more than 256
 //   ... iscatter  definite words into pieces of at most 256 words of one wave
 //                 list) and order the items by the first key block they read,
@@ -65,8 +66,8 @@ constexpr double kFxPfD = 2097152.0;
 constexpr int kPfCntShift = 43;                   // key count above the weight sum
 constexpr unsigned long long kPfMassMask = (1ull << kPfCntShift) - 1ull;
 constexpr double kFxRes = 68719476736.0;          // 2^36: candidate masses
-static_assert(kPfSubLists == 4, "one candidate list per index wave");
-static_assert(kPfBins == 128 && kPfSh0 == 2 * 7, "three levels of 128 bins over 2^14 codes");
+static_assert(kPfSubLists == 4, "one candidate word list per index wave");
+static_assert(kPfBins == 128 && kPfSh0 == 14, "windows of 128 bins of 2^14 codes");
 // a window bin's weights are at most 2^21 (+ rounding) each
 static_assert((long long)(kPfMaxKeys - 1) * ((1 << 21) + 1) < (1ll << kPfCntShift),
               "weight sums stay below the count field");
@@ -109,12 +110,11 @@ __global__ __launch_bounds__(256) void k_pf_qprep(PfPlan p) {
 
 // ------------------------------------------------------------------ index pass
 
-enum PfStatus : int { kStNeedB = 0, kStNeedC = 1, kStNeedCIncl = 2, kStDone = 3 };
+enum PfStatus : int { kStNeedB = 0, kStNeedC = 1, kStDone = 2 };
 
 struct PfWork {
   float m;
   int status;
-  int level;
   int sh;       // bin width 2^sh depth codes
   int dw;       // window start (depth code)
   int dq;       // boundary bin start (depth code)
@@ -151,7 +151,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
   __shared__ unsigned long long bins[kPfVecs][kPfBins + 1];
   __shared__ float red_m[4][kPfVecs];
   __shared__ PfWork st[kPfVecs];
-  __shared__ int lcnt[4][kPfVecs];
   __shared__ int flags[2];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -244,7 +243,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
   if (tid < kPfVecs) {
     PfWork w;
     w.m = fmaxf(fmaxf(red_m[0][tid], red_m[1][tid]), fmaxf(red_m[2][tid], red_m[3][tid]));
-    w.level = 0;
     w.sh = kPfSh0;
     w.dw = 0;
     w.dq = 0;
@@ -271,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
       int nb = 0, nc = 0;
       for (int n = 0; n < kPfVecs; ++n) {
         nb |= st[n].status == kStNeedB;
-        nc |= st[n].status == kStNeedC || st[n].status == kStNeedCIncl;
+        nc |= st[n].status == kStNeedC;
       }
       flags[0] = nb;
       flags[1] = nc;
@@ -293,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
       for (int c = 0; c < 2; ++c) {
         const PfWork& w = st[32 * c + j];
         act[c] = w.status == kStNeedB;
-        tail[c] = w.level == 0 && w.nwin == 0;  // the first window also sums the tail
+        tail[c] = w.nwin == 0;  // the first window also sums the tail
         mc[c] = w.m * kPfCode;  // exact: a power-of-two scale
         dw[c] = w.dw;
         sh[c] = w.sh;
@@ -335,8 +333,8 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
               atomicAdd(&bins[32 * c + j][k], (1ull << kPfCntShift) | wfx);
             }
           } else {
-            // a later window or a refinement: only keys in the window count, and
-            // there are few of them.  t = code - (dw - margin) lies in [0, span) iff its
+            // a later window: only keys in the window count, and there are few of
+            // them.  t = code - (dw - margin) lies in [0, span) iff its
             // bits, as an unsigned number, are below span's (negative t has the sign
             // bit set)
             uint32_t inw = 0u;
@@ -346,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
               inw |= (__float_as_uint(t) < fspan[c] ? 1u : 0u) << r;
             }
             // the lane's own keys in the window, one at a time (a wave runs as many
-            // rounds as its busiest lane: one or two in a refinement)
+            // rounds as its busiest lane)
             while (inw) {
               const int r = __builtin_ctz(inw);
               inw &= inw - 1u;
@@ -368,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
           return (double)(bins[tid][q] & kPfMassMask) / kFxPfD *
                  exp((double)pf_edge(rf0, q) - (double)w.m);
         };
-        if (w.level == 0 && w.nwin == 0) {
+        if (w.nwin == 0) {
           double tot = 0.0;
           for (int q = 0; q <= kPfBins; ++q) tot += M(q);  // with the tail
           w.Z = tot;
@@ -385,37 +383,20 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
           cum += mq;
         }
         if (found < 0) {
-          if (w.level == 0 && w.nwin < 63) {
+          if (w.nwin < 63) {
             // the running mass stops short of p * Z inside the window: the next one
             w.above = cum;
             w.dw += kPfBins << kPfSh0;
             w.nwin += 1;
-          } else if (w.level == 0) {
+          } else {
             w.status = kStDone;  // no boundary found after 64 windows: keep every key
             w.mode = kPfAll;
-          } else {
-            // rounding between a bin and its sub-bins: the last non-empty sub-bin
-            found = kPfBins - 1;
-            while (found > 0 && (bins[tid][found] >> kPfCntShift) == 0ull) --found;
-            cum = w.above;
-            for (int q = 0; q < found; ++q) cum += M(q);
           }
-        }
-        if (found >= 0) {
-          const int nq = (int)(bins[tid][found] >> kPfCntShift);
+        } else {
           w.need = pZ - cum;
           w.above = cum;
           w.dq = w.dw + (found << w.sh);
-          if (nq <= kPfCandSub) {  // fits the list of whichever wave meets them
-            w.status = kStNeedC;
-          } else if (w.level < kPfLevels) {
-            // too many keys for the candidate list: 128 sub-bins of the boundary bin
-            w.level += 1;
-            w.dw = w.dq;
-            w.sh -= 7;
-          } else {
-            w.status = kStNeedCIncl;  // finest bins: select the whole boundary bin
-          }
+          w.status = kStNeedC;
         }
         st[tid] = w;
       }
@@ -423,110 +404,77 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
       continue;  // sweep C waits until every vector has its boundary bin
     }
 
-    // ---- sweep C: definite words and boundary candidates
-    if (tid < kPfVecs) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) lcnt[q][tid] = 0;
-    }
-    __syncthreads();
+    // ---- sweep C: definite words and candidate words
     {
-      bool act[2], fx[2];
-      float mc[2], fdef[2], fdq[2];
-      int ddef[2], dq[2];
-      unsigned cw[2], fcw[2];
-      float2* cl[2];
+      bool act[2];
+      float mc[2], fdq[2];
+      uint32_t fcw[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const PfWork& w = st[32 * c + j];
-        act[c] = w.status == kStNeedC || w.status == kStNeedCIncl;
-        const bool incl = w.status == kStNeedCIncl;
+        act[c] = w.status == kStNeedC;
         mc[c] = w.m * kPfCode;
-        dq[c] = w.dq;
-        ddef[c] = incl ? w.dq + (1 << w.sh) : w.dq;  // definite: code below this
-        cw[c] = incl ? 0u : (1u << w.sh);            // candidate: code in [dq, dq + cw)
-        // With integer bounds that floats hold exactly (multiples of 2^7 below 2^31, or
-        // anything below 2^24) the tests run on t = 2^17 (m - s) itself: the code is
-        // floor(t), so code < n iff t < n, and t - dq is exact near dq and keeps its
-        // order elsewhere (unsigned float bits: negative values fail the test).
-        fx[c] = w.sh >= 7 || w.dq + (1 << w.sh) < (1 << 24);
-        fdef[c] = (float)ddef[c];
-        fdq[c] = (float)dq[c];
-        fcw[c] = __float_as_uint((float)cw[c]);
-        cl[c] = p.cand + ((vbase + 32 * c + j) * kPfSubLists + wave) * (size_t)kPfCandSub;
+        // The bounds are multiples of 2^14 below 2^31, which floats hold exactly, so the
+        // tests run on t = 2^17 (m - s) itself: the code is floor(t), so code < dq iff
+        // t < dq (definite), and t - dq is exact near dq and keeps its order elsewhere
+        // (candidate: code in [dq, dq + 2^14), unsigned float bits of t - dq below
+        // 2^14; negative values fail the test)
+        fdq[c] = (float)w.dq;
+        fcw[c] = __float_as_uint((float)(1 << w.sh));
       }
       const bool my_act = hi ? act[1] : act[0];
       const size_t my_vid = vbase + lane;
       uint2* wl = p.words + (my_vid * 4 + wave) * (size_t)p.wcap;
-      int wcnt = 0;
+      uint2* cl = p.cwords + (my_vid * 4 + wave) * (size_t)p.wcap;
+      int wcnt = 0, ccnt = 0, ckn = 0;
       sweep([&](int kb, f32x16 (&acc)[2]) {
-        uint32_t bits[2] = {0u, 0u};
+        uint32_t bits[2] = {0u, 0u}, cbits[2] = {0u, 0u};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           if (!act[c]) continue;
-          // definite keys at bits 8 (r / 4) + r % 4 (constant shifts), moved to the
-          // lane's half of the word (+ 4 hi) once; candidates at bit r
-          uint32_t dbits = 0u, cbits = 0u;
-          if (fx[c]) {
+          // both kinds at bits 8 (r / 4) + r % 4 (constant shifts), moved to the lane's
+          // half of the word (+ 4 hi) once
+          uint32_t db = 0u, cb = 0u;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float t = __builtin_fmaf(acc[c][r], -kPfCode, mc[c]);
-              dbits |= (t < fdef[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
-              cbits |= (__float_as_uint(t - fdq[c]) < fcw[c] ? 1u : 0u) << r;
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int d = pf_code(acc[c][r], mc[c]);
-              dbits |= (d < ddef[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
-              cbits |= ((unsigned)(d - dq[c]) < cw[c] ? 1u : 0u) << r;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const float t = __builtin_fmaf(acc[c][r], -kPfCode, mc[c]);
+            db |= (t < fdq[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
+            cb |= (__float_as_uint(t - fdq[c]) < fcw[c] ? 1u : 0u) << (8 * (r >> 2) + (r & 3));
           }
-          bits[c] = dbits << (4 * hi);
-          // one slot reservation per lane and step, then the stores
-          if (cbits) {
-            int slot = atomicAdd(&lcnt[wave][32 * c + j], __builtin_popcount(cbits));
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              if ((cbits >> r) & 1u) {
-                if (slot < kPfCandSub)
-                  cl[c][slot] = make_float2(acc[c][r],
-                                            __int_as_float(kb + 8 * (r >> 2) + 4 * hi + (r & 3)));
-                ++slot;
-              }
-            }
-          }
+          bits[c] = db << (4 * hi);
+          cbits[c] = cb << (4 * hi);
         }
 #pragma unroll
-        for (int c = 0; c < 2; ++c) bits[c] |= (uint32_t)__shfl_xor((int)bits[c], 32, 64);
+        for (int c = 0; c < 2; ++c) {
+          bits[c] |= (uint32_t)__shfl_xor((int)bits[c], 32, 64);
+          cbits[c] |= (uint32_t)__shfl_xor((int)cbits[c], 32, 64);
+        }
         uint32_t word = hi ? bits[1] : bits[0];
+        const uint32_t cword = hi ? cbits[1] : cbits[0];  // sinks included: their mass counts
         if (kb < p.n_sink) {  // sinks are attended separately
           const int ns = p.n_sink - kb;
           word &= ns >= 32 ? 0u : ~((1u << ns) - 1u);
         }
+        // a list holds every block of the wave's range (wcap blocks), so the tests
+        // never fail; they keep the stores inside the lists whatever the plan
         if (my_act && word) {
           if (wcnt < p.wcap) wl[wcnt] = make_uint2((uint32_t)(kb >> 5), word);
           ++wcnt;
         }
+        if (my_act && cword) {
+          if (ccnt < p.wcap) cl[ccnt] = make_uint2((uint32_t)(kb >> 5), cword);
+          ++ccnt;
+          ckn += __popc(cword);
+        }
       });
       if (my_act) {
         p.wcount[my_vid * 4 + wave] = wcnt;
-        // this wave's candidate count (its own LDS counter: no barrier needed)
-        const PfWork& w = st[lane];
-        if (w.status == kStNeedC)
-          p.ccount[my_vid * kPfSubLists + wave] = min(lcnt[wave][lane], kPfCandSub);
+        p.ccount[my_vid * kPfSubLists + wave] = min(ccnt, p.wcap);
+        p.ckeys[my_vid * kPfSubLists + wave] = ckn;
       }
     }
     __syncthreads();
-    if (tid < kPfVecs) {
-      PfWork w = st[tid];
-      if (w.status == kStNeedCIncl) {
-        w.status = kStDone;
-        w.mode = kPfInclusive;
-      } else if (w.status == kStNeedC) {
-        w.status = kStDone;
-      }
-      st[tid] = w;
-    }
+    if (tid < kPfVecs && st[tid].status == kStNeedC) st[tid].status = kStDone;
     __syncthreads();
   }
 
@@ -539,7 +487,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     o.dq = w.dq;
     o.sh = w.sh;
     o.n_sel = 0;
-    o.level = w.level;
     o.Z = w.Z;
     o.need = w.need;
     p.vec[vbase + tid] = o;
@@ -547,14 +494,24 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
       for (int q = 0; q < 4; ++q) p.wcount[(vbase + tid) * 4 + q] = 0;
     }
     if (w.mode != kPfNormal) {
-      for (int q = 0; q < kPfSubLists; ++q) p.ccount[(vbase + tid) * kPfSubLists + q] = 0;
+      for (int q = 0; q < kPfSubLists; ++q) {
+        p.ccount[(vbase + tid) * kPfSubLists + q] = 0;
+        p.ckeys[(vbase + tid) * kPfSubLists + q] = 0;
+      }
     }
   }
 }
 
 // ------------------------------------------------------------------ exact threshold
 
-constexpr int kResPer = kPfSubLists * kPfCandSub / 64;  // candidates per lane
+// LDS written by some lanes of a wave and read by others later in the same wave:
+// the wave's LDS instructions execute in order; this keeps the compiler from
+// moving them across the exchange point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ unsigned long long wave_sum_u64p(unsigned long long v) {
 #pragma unroll
@@ -562,81 +519,254 @@ __device__ __forceinline__ unsigned long long wave_sum_u64p(unsigned long long v
   return v;
 }
 
+// First score slot of every vector's candidates (vector order; one block): an
+// exclusive scan of the candidate key counts; vectors past the capacity get -1.
+__global__ __launch_bounds__(1024) void k_pf_cscan(PfPlan p) {
+  constexpr int NT = 1024;
+  __shared__ unsigned long long ws[NT / 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = (p.V + NT - 1) / NT;
+  const int e0 = tid * per, e1 = min(p.V, e0 + per);
+  auto keys = [&](int e) {
+    const int* k = p.ckeys + (size_t)e * kPfSubLists;
+    return (unsigned long long)(k[0] + k[1] + k[2] + k[3]);
+  };
+  unsigned long long run = 0ull;
+  for (int e = e0; e < e1; ++e) run += keys(e);
+  const unsigned long long inc = wave_incl_sum_u64(run);
+  if (lane == 63) ws[wave] = inc;
+  __syncthreads();
+  unsigned long long base = inc - run;
+  for (int q = 0; q < wave; ++q) base += ws[q];
+  for (int e = e0; e < e1; ++e) {
+    const unsigned long long n = keys(e);
+    p.coff[e] = base + n <= (unsigned long long)p.cs_cap ? (long long)base : -1ll;
+    base += n;
+  }
+}
+
+// One wave per vector.  The threshold is the largest candidate key k (ordered fp32
+// score) whose candidates at or above it hold at least `need` of mass, or the
+// smallest candidate key when none does; every candidate >= tau is selected.
+//  * Scores: qi = lo + mid + hi (exact), each candidate's score the fp32 rounding of
+//    the fp64 sum of its 16 exact products.  Lane e takes word e of a list and walks
+//    its set bits two at a time (both index rows in flight together).
+//  * The scores are gathered once into the vector's slots of cscore, in word order
+//    (a word's slots follow a wave scan of the bit counts of its batch of 64 words),
+//    together with their range; the later passes read the slots.  A vector past the
+//    slots' capacity computes its scores again in every pass instead.
+//  * Radix select over the ordered keys: the range fixes their common leading bits,
+//    then digits of up to 10 bits from the highest differing bit down, each a
+//    histogram of counts and 2^-36 fixed-point masses exp(s - m) in this wave's LDS
+//    rows; the chosen bucket is the highest non-empty one whose mass with everything
+//    above it reaches the need.  Integer sums: the result does not depend on the
+//    order.
+//  * Last pass: each word keeps only its selected keys that are not sinks (the sinks
+//    are attended on their own), so the attend reads candidate words like definite
+//    ones.
+constexpr int kResDigit = 10;
+constexpr int kResBuckets = 1 << kResDigit;
+
 __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
+  __shared__ unsigned long long rmass[4][kResBuckets];
+  __shared__ unsigned rcnt[4][kResBuckets];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int vid = blockIdx.x * 4 + wave;
   if (vid >= p.V) return;  // wave-uniform
   PfVec& v = p.vec[vid];
   if (v.mode != kPfNormal) return;
-  const float m = v.m;
-  uint32_t kr[kResPer];
-  unsigned long long wr[kResPer];
-  int n = 0;
-#pragma unroll
-  for (int q = 0; q < kResPer; ++q) {
-    kr[q] = 0u;
-    wr[q] = 0ull;
-  }
-  // lane takes entries lane, lane + 64, ... of each sub-list
+  int cnt[kPfSubLists];
+  int tot = 0;
 #pragma unroll
   for (int sl = 0; sl < kPfSubLists; ++sl) {
-    const int cnt = p.ccount[(size_t)vid * kPfSubLists + sl];
-    const float2* src = p.cand + ((size_t)vid * kPfSubLists + sl) * kPfCandSub;
+    cnt[sl] = p.ccount[(size_t)vid * kPfSubLists + sl];
+    tot += p.ckeys[(size_t)vid * kPfSubLists + sl];
+  }
+  if (tot == 0) {  // no candidate
+    if (lane == 0) {
+      v.tau = INFINITY;
+      v.n_sel = 0;
+    }
+    return;
+  }
+  const float m = v.m;
+  const int bi = vid / (p.G * p.Tq), b = bi / p.n_ret, ri = bi % p.n_ret;
+  const uint16_t* idx = p.index + (size_t)(b * p.n_ret + ri) * p.max_seq * kR;
+  const long long off = p.coff[vid];
+  const bool cached = off >= 0;
+  float* cs = p.cscore + (cached ? off : 0ll);
+  double qi[kR];
+  {
+    const uint16_t* qs = p.qsplit + (size_t)vid * 3 * kR;  // lo, mid, hi
 #pragma unroll
-    for (int u = 0; u < kPfCandSub / 64; ++u) {
-      const int e = u * 64 + lane;
-      if (e < cnt) {
-        const float s = src[e].x;
-        kr[sl * (kPfCandSub / 64) + u] = f32_ord(s);
-        wr[sl * (kPfCandSub / 64) + u] =
-            (unsigned long long)(exp((double)s - (double)m) * kFxRes + 0.5);
-        ++n;
+    for (int c = 0; c < kR; ++c)
+      qi[c] = (double)bf16_to_f32(qs[2 * kR + c]) + (double)bf16_to_f32(qs[kR + c]) +
+              (double)bf16_to_f32(qs[c]);
+  }
+  auto score = [&](uint4 a, uint4 c) {
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    double acc = 0.0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      acc = __fma_rn(qi[2 * d], (double)__uint_as_float(u[d] << 16), acc);
+      acc = __fma_rn(qi[2 * d + 1], (double)__uint_as_float(u[d] & 0xffff0000u), acc);
+    }
+    return (float)acc;
+  };
+  auto mass = [&](float sc) {
+    return (unsigned long long)(exp((double)sc - (double)m) * kFxRes + 0.5);
+  };
+  // Walk the candidate words: word(list, e, w, slot) once per word of this lane, slot =
+  // the first score slot of the word; cand(score, slot, bit) per candidate, the score
+  // gathered from the index unless have_scores (then read from the slots)
+  auto walk = [&](bool have_scores, auto&& cand, auto&& word_done) {
+    int base = 0;
+#pragma unroll
+    for (int sl = 0; sl < kPfSubLists; ++sl) {
+      const uint2* cl = p.cwords + ((size_t)vid * kPfSubLists + sl) * p.wcap;
+      for (int e0 = 0; e0 < cnt[sl]; e0 += 64) {
+        const int e = e0 + lane;
+        const uint2 w = e < cnt[sl] ? cl[e] : make_uint2(0u, 0u);
+        const uint32_t nb = (uint32_t)__popc(w.y);
+        const uint32_t incl = wave_incl_sum_u32(nb);
+        int slot = base + (int)(incl - nb);
+        base += (int)__shfl(incl, 63, 64);
+        uint32_t bits = w.y, keep = 0u;
+        while (bits) {
+          const int b0 = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          const bool two = bits != 0u;
+          const int b1 = two ? __builtin_ctz(bits) : b0;
+          if (two) bits &= bits - 1u;
+          float s0, s1;
+          if (have_scores) {
+            s0 = cs[slot];
+            s1 = two ? cs[slot + 1] : s0;
+          } else {
+            const int k0 = (int)(w.x * 32u) + b0, k1 = (int)(w.x * 32u) + b1;
+            const uint4 a0 = *(const uint4*)(idx + (size_t)k0 * kR);
+            const uint4 c0 = *(const uint4*)(idx + (size_t)k0 * kR + 8);
+            const uint4 a1 = *(const uint4*)(idx + (size_t)k1 * kR);
+            const uint4 c1 = *(const uint4*)(idx + (size_t)k1 * kR + 8);
+            s0 = score(a0, c0);
+            s1 = score(a1, c1);
+          }
+          keep |= cand(s0, slot, (int)(w.x * 32u) + b0) ? 1u << b0 : 0u;
+          if (two) keep |= cand(s1, slot + 1, (int)(w.x * 32u) + b1) ? 1u << b1 : 0u;
+          slot += two ? 2 : 1;
+        }
+        if (e < cnt[sl]) word_done(sl, e, w, keep);
       }
     }
-  }
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int q = 0; q < kResPer; ++q)
-    if (kr[q]) {
-      kmin = min(kmin, kr[q]);
-      kmax = max(kmax, kr[q]);
+  };
+  auto no_word = [](int, int, uint2, uint32_t) {};
+  // every candidate's score, in slot order when the slots hold them
+  auto each = [&](auto&& fn) {
+    if (cached) {
+      for (int q = lane; q < tot; q += 64) fn(cs[q]);
+    } else {
+      walk(false, [&](float sc, int, int) { fn(sc); return false; }, no_word);
     }
+  };
+  // pass 1: the range of the keys (and the slots, when the vector has them)
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  walk(false,
+       [&](float sc, int slot, int) {
+         if (cached) cs[slot] = sc;
+         const uint32_t k = f32_ord(sc);
+         kmin = min(kmin, k);
+         kmax = max(kmax, k);
+         return false;
+       },
+       no_word);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
-  const int total = (int)wave_sum_u64p((unsigned long long)n);
-  float tau;
-  int n_sel = 0;
-  if (total == 0) {
-    tau = INFINITY;
-  } else {
-    const double need_fx = v.need * kFxRes;
-    auto mass_ge = [&](uint32_t k) {
-      unsigned long long s = 0ull;
+  // the slots written by every lane are read by others
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const double need_fx = v.need * kFxRes;
+  constexpr int kPer = kResBuckets / 64;  // buckets per lane
+  uint32_t key = kmin;
+  if (kmin != kmax) {
+    const int hb = 31 - __builtin_clz(kmin ^ kmax);
+    uint32_t prefix = hb == 31 ? 0u : (kmin >> (hb + 1)) << (hb + 1);
+    unsigned long long above = 0ull;  // mass of the keys above the current prefix range
+    bool found = true;
+    for (int top = hb; top >= 0 && found; top -= kResDigit) {
+      const int lo = max(top - (kResDigit - 1), 0);
+      const uint32_t dmask = (2u << (top - lo)) - 1u;
 #pragma unroll
-      for (int q = 0; q < kResPer; ++q)
-        if (kr[q] >= k && kr[q]) s += wr[q];
-      return wave_sum_u64p(s);
-    };
-    uint32_t lo = kmin, hi = kmax;
-    if ((double)mass_ge(kmin) >= need_fx) {
-      // largest key whose mass-at-or-above still reaches the need
-      while (lo < hi) {
-        const uint32_t mid = lo + (hi - lo + 1u) / 2u;
-        if ((double)mass_ge(mid) >= need_fx) lo = mid;
-        else hi = mid - 1u;
+      for (int t = 0; t < kPer; ++t) {
+        rmass[wave][lane * kPer + t] = 0ull;
+        rcnt[wave][lane * kPer + t] = 0u;
       }
-    }
-    tau = ord_f32(lo);
-    int c = 0;
+      wave_lds_sync();
+      each([&](float sc) {
+        const uint32_t k = f32_ord(sc);
+        if (top == 31 || (k >> (top + 1)) == (prefix >> (top + 1))) {
+          const uint32_t d = (k >> lo) & dmask;
+          atomicAdd(&rmass[wave][d], mass(sc));
+          atomicAdd(&rcnt[wave][d], 1u);
+        }
+      });
+      wave_lds_sync();
+      // lane l holds buckets kPer l .. kPer l + kPer - 1
+      unsigned long long h[kPer], sum = 0ull;
+      uint32_t nz = 0u;
 #pragma unroll
-    for (int q = 0; q < kResPer; ++q) c += (kr[q] && kr[q] >= lo) ? 1 : 0;
-    n_sel = (int)wave_sum_u64p((unsigned long long)c);
+      for (int t = 0; t < kPer; ++t) {
+        h[t] = rmass[wave][lane * kPer + t];
+        sum += h[t];
+        nz |= (rcnt[wave][lane * kPer + t] != 0u ? 1u : 0u) << t;
+      }
+      unsigned long long suf = sum;  // inclusive suffix sum over lanes l .. 63
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
+      }
+      unsigned long long cum = above + (suf - sum);
+      int best = -1;
+      unsigned long long best_above = 0ull;
+#pragma unroll
+      for (int t = kPer - 1; t >= 0; --t) {
+        if (best < 0 && ((nz >> t) & 1u) && (double)(cum + h[t]) >= need_fx) {
+          best = t;
+          best_above = cum;
+        }
+        cum += h[t];
+      }
+      const unsigned long long bal = __ballot(best >= 0);
+      if (bal == 0ull) {
+        found = false;  // the candidates fall short of the need: every one is selected
+      } else {
+        const int L = 63 - __builtin_clzll(bal);
+        const int bt = __shfl(best, L, 64);
+        above = __shfl(best_above, L, 64);
+        prefix |= (uint32_t)(L * kPer + bt) << lo;
+      }
+      wave_lds_sync();  // the next digit clears the rows
+    }
+    key = found ? prefix : kmin;
   }
+  // keep the selected candidates in the words (sinks dropped: attended on their own)
+  int n_sel = 0;
+  walk(cached,
+       [&](float sc, int, int k) {
+         const bool sel = f32_ord(sc) >= key;
+         n_sel += sel ? 1 : 0;
+         return sel && k >= p.n_sink;
+       },
+       [&](int sl, int e, uint2 w, uint32_t keep) {
+         if (keep != w.y) p.cwords[((size_t)vid * kPfSubLists + sl) * p.wcap + e].y = keep;
+       });
+  n_sel = (int)wave_sum_u64p((unsigned long long)n_sel);
   if (lane == 0) {
-    v.tau = tau;
+    v.tau = ord_f32(key);
     v.n_sel = n_sel;
   }
 }
@@ -735,7 +865,7 @@ __global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
     const int cc = v.mode == kPfNormal ? p.ccount[(size_t)vid * kPfSubLists + w] : 0;
     if (wc == 0) {
       if (w == 0 || cc > 0) {
-        const int blk = cc > 0 ? __float_as_int(p.cand[((size_t)vid * kPfSubLists + w) * kPfCandSub].y) >> 5 : 0;
+        const int blk = cc > 0 ? (int)p.cwords[((size_t)vid * kPfSubLists + w) * p.wcap].x : 0;
         put(k++, make_int4(vid, w, 0, 0), blk);
       }
       continue;
@@ -782,15 +912,6 @@ constexpr int kPfChunk = 64;
 constexpr int kPfAttendBlocks = 768;   // persistent: 3 blocks of 4 waves per CU (at most 168 VGPRs)
 
 // ------------------------------------------------------------------ gather attention
-
-// LDS written by some lanes of a wave and read by others later in the same wave:
-// the wave's LDS instructions execute in order; this keeps the compiler from
-// moving them across the exchange point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // One step of a reduce-scatter between lanes l and l ^ S over part[0, N).
 template <int S, int N>
@@ -954,11 +1075,11 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
 
     // The item's rows are produced in batches (at most 16 words = 512 keys) from, in
     // order: a key range (the sinks, every key in keep-all mode, or a keep-all
-    // item's range), definite words, the candidates at or above tau.  A whole
+    // item's range), definite words, the selected candidate words.  A whole
     // vector takes all four wave lists; a piece takes words [lo, hi) of list it.y
     // and that list's candidates when it ends the list.  After each batch the full
     // tiles of the queue are attended; the last rows once the sources are exhausted.
-    const bool words = it.y < 4 && (v.mode == kPfNormal || v.mode == kPfInclusive);
+    const bool words = it.y < 4 && v.mode == kPfNormal;
     int rng0 = 0, rng1 = 0;
     if (it.y == 4) {
       rng0 = it.z;
@@ -984,19 +1105,23 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
           } else {
             src = words ? 1 : (cands ? 2 : 3);
           }
-        } else if (src == 1) {
-          const int cnt = sub < w_end ? (whole ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap)
-                                               : it.w)
-                                      : 0;
+        } else if (src == 1 || src == 2) {
+          // definite words (src 1) or the selected candidate words (src 2)
+          const bool cw = src == 2;
+          const int cnt = sub < w_end
+                              ? (cw ? p.ccount[(size_t)vid * kPfSubLists + sub]
+                                    : (whole ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap)
+                                             : it.w))
+                              : 0;
           if (sub == w_end) {
-            src = cands ? 2 : 3;
+            src = (!cw && cands) ? 2 : 3;
             sub = whole ? 0 : it.y;
             e0 = 0;
           } else if (e0 >= cnt) {
             ++sub;
             e0 = 0;
           } else {
-            const uint2* src_w = p.words + ((size_t)vid * 4 + sub) * p.wcap;
+            const uint2* src_w = (cw ? p.cwords : p.words) + ((size_t)vid * 4 + sub) * p.wcap;
             const uint2 ent = (lane < kAwBatch && e0 + lane < cnt) ? src_w[e0 + lane]
                                                                    : make_uint2(0u, 0u);
             const int cb = __popc(ent.y);
@@ -1015,26 +1140,6 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
             }
             nq += __shfl(incl, 63, 64);
             e0 += kAwBatch;
-          }
-        } else if (src == 2) {
-          const int cnt = sub < w_end ? p.ccount[(size_t)vid * kPfSubLists + sub] : 0;
-          if (sub == w_end) {
-            src = 3;
-          } else if (e0 >= cnt) {
-            ++sub;
-            e0 = 0;
-          } else {
-            const float2* src_c = p.cand + ((size_t)vid * kPfSubLists + sub) * kPfCandSub;
-            const float2 cd = e0 + lane < cnt ? src_c[e0 + lane] : make_float2(-INFINITY, 0.f);
-            const int key = __float_as_int(cd.y);
-            const bool sel = e0 + lane < cnt && cd.x >= v.tau && key >= p.n_sink;
-            const unsigned long long bal = __ballot(sel);
-            // rank among the selected lanes below this one (mbcnt: no 64-bit mask)
-            const unsigned below = __builtin_amdgcn_mbcnt_hi(
-                (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (sel) queue[nq + (int)below] = key;
-            nq += __popcll(bal);
-            e0 += 64;
           }
         } else {
           more = false;
@@ -1150,13 +1255,13 @@ __global__ void k_pf_debug(PfPlan p) {
           if ((ent.y >> bit) & 1u) put((int)(ent.x * 32u + bit));
       }
     }
-    if (v.mode == kPfNormal) {
+    if (v.mode == kPfNormal) {  // the candidate words hold the selected keys only
       for (int sl = 0; sl < kPfSubLists; ++sl) {
         const int cnt = p.ccount[(size_t)vid * kPfSubLists + sl];
         for (int e = 0; e < cnt; ++e) {
-          const float2 c = p.cand[((size_t)vid * kPfSubLists + sl) * kPfCandSub + e];
-          const int key = __float_as_int(c.y);
-          if (c.x >= v.tau && key >= p.n_sink) put(key);
+          const uint2 ent = p.cwords[((size_t)vid * kPfSubLists + sl) * p.wcap + e];
+          for (int bit = 0; bit < 32; ++bit)
+            if ((ent.y >> bit) & 1u) put((int)(ent.x * 32u + bit));
         }
       }
     }
@@ -1207,8 +1312,14 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_vec = take(V * sizeof(PfVec));
   const size_t o_words = take(V * 4 * wcap * sizeof(uint2));
   const size_t o_wcnt = take(V * 4 * sizeof(int));
-  const size_t o_cand = take(V * kPfSubLists * kPfCandSub * sizeof(float2));
+  const size_t o_cand = take(V * kPfSubLists * wcap * sizeof(uint2));
   const size_t o_ccnt = take(V * kPfSubLists * sizeof(int));
+  const size_t o_ckey = take(V * kPfSubLists * sizeof(int));
+  const size_t o_coff = take(V * sizeof(long long));
+  // candidate score slots: 2048 per vector on average (vectors past them compute their
+  // scores again in every pass)
+  const size_t cs_cap = V * 2048;
+  const size_t o_cs = take(cs_cap * sizeof(float));
   const size_t nbucket = (size_t)B * n_ret * ((n_keys + 31) / 32 + 1);
   const size_t o_obkt = take(nbucket * sizeof(int));
   // items per vector: at most one per 256 words of each list (at least one per
@@ -1232,8 +1343,12 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
     plan->vec = (PfVec*)(base + o_vec);
     plan->words = (uint2*)(base + o_words);
     plan->wcount = (int*)(base + o_wcnt);
-    plan->cand = (float2*)(base + o_cand);
+    plan->cwords = (uint2*)(base + o_cand);
     plan->ccount = (int*)(base + o_ccnt);
+    plan->ckeys = (int*)(base + o_ckey);
+    plan->coff = (long long*)(base + o_coff);
+    plan->cscore = (float*)(base + o_cs);
+    plan->cs_cap = (long long)cs_cap;
     plan->obucket = (int*)(base + o_obkt);
     plan->nbucket = (int)nbucket;
     plan->nitem = (int*)(base + o_nitem);
@@ -1275,6 +1390,7 @@ hipError_t launch_prefill(const PfPlan& p, hipStream_t s) {
   mark(1);
   RTP_LAUNCH(k_pf_index, dim3((Gv + kPfVecs - 1) / kPfVecs, p.B * p.n_ret), dim3(256), s, p);
   mark(2);
+  RTP_LAUNCH(k_pf_cscan, dim3(1), dim3(1024), s, p);
   RTP_LAUNCH(k_pf_resolve, dim3((p.V + 3) / 4), dim3(256), s, p);
   RTP_LAUNCH(k_pf_count, dim3((p.V + 255) / 256), dim3(256), s, p);
   RTP_LAUNCH(k_pf_iscan, dim3(1), dim3(1024), s, p);

@@ -189,10 +189,8 @@ struct AppendPlan {
 // ------------------------------------------------------------------ chunked prefill
 
 constexpr int kPfVecs = 64;                  // query vectors (row, q-head) per index block
-constexpr int kPfSubLists = 4;               // candidate lists per vector (one per index wave)
-constexpr int kPfCandSub = 512;              // candidates per list
-constexpr int kPfBins = 128;                 // histogram bins per level
-constexpr int kPfLevels = 2;                 // refinements below the first level
+constexpr int kPfSubLists = 4;               // candidate word lists per vector (one per index wave)
+constexpr int kPfBins = 128;                 // histogram bins of a window
 constexpr int kPfMaxKeys = 1 << 21;          // causal keys per query (histogram count field)
 constexpr int kPfItemWords = 256;            // definite words per attend work item
 constexpr int kPfItemKeys = 8192;            // keys per work item of a keep-all vector
@@ -200,9 +198,8 @@ constexpr int kPfPartStride = 132;           // floats per partial result: m, l,
 
 // Selection state of one query vector after the index pass.
 enum PfMode : int {
-  kPfNormal = 0,    // definite words + candidates >= tau
-  kPfAll = 1,       // every key <= pos (top_p >= 1)
-  kPfInclusive = 2, // definite words hold the boundary bin too (finest level overflowed)
+  kPfNormal = 0,    // definite words + selected candidate words
+  kPfAll = 1,       // every key <= pos (top_p >= 1, or no boundary within 64 windows)
   kPfEmpty = 3      // padding vector of the last block
 };
 
@@ -213,7 +210,6 @@ struct PfVec {
   int dq;         // boundary bin start, depth code floor(2^17 (m - s))
   int sh;         // boundary bin width: 2^sh depth codes
   int n_sel;      // selected candidates (normal mode)
-  int level;
   double Z;       // sum exp(s - m) over keys <= pos
   double need;    // top_p * Z minus the mass of the definite keys
 };
@@ -236,8 +232,13 @@ struct PfPlan {
   PfVec* vec;         // [V]
   uint2* words;       // [V][4][wcap]  (32-key block, bits of definite keys)
   int* wcount;        // [V][4]
-  float2* cand;       // [V][4][kPfCandSub]  (score, key bits)
-  int* ccount;        // [V][4]
+  uint2* cwords;      // [V][4][wcap]  (32-key block, bits of boundary-bin keys; the
+                      // resolver leaves the selected keys that are not sinks)
+  int* ccount;        // [V][4] candidate words per list
+  int* ckeys;         // [V][4] candidate keys per list
+  long long* coff;    // [V] first slot of the vector's scores in cscore, or -1
+  float* cscore;      // [cs_cap] exact candidate scores, vector after vector
+  long long cs_cap;
   int* obucket;       // [nbucket] items per order key, then their first position
   int nbucket;        // P * (key blocks + 1)
   int* nitem;         // [V] attend work items of the vector (1: the whole vector)
