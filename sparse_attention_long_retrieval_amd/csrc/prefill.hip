@@ -187,12 +187,12 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
   // a vector's position read as -inf.  Lane holds keys kb + 8(r/4) + 4hi + r%4.
   auto score_block = [&](int kb, uint4 a, f32x16 (&acc)[2]) {
     const bf16x8 A = pf_bf16x8(a);
+    const f32x16 zero = {};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, bq[c][0], zero, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
-#pragma unroll
-      for (int part = 0; part < 3; ++part)
+      for (int part = 1; part < 3; ++part)
         acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, bq[c][part], acc[c], 0, 0, 0);
     }
     if (kb + 31 > p_lo) {
@@ -205,24 +205,27 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
         }
     }
   };
+  // rows past the causal keys read row Nk - 1 (their scores are masked to -inf)
   auto load_a = [&](int kb) {
-    const int key = kb + j;
-    return key < Nk ? *(const uint4*)(idx + (size_t)key * kR + 8 * hi) : make_uint4(0, 0, 0, 0);
+    const int key = min(kb + j, Nk - 1);
+    return *(const uint4*)(idx + (size_t)key * kR + 8 * hi);
   };
-  // Run fn(kb, acc) over this wave's key blocks, loads three blocks ahead.
+  // Run fn(kb, acc) over this wave's key blocks, loads three blocks ahead.  The loop
+  // is unrolled by three so each load's registers are renamed, not copied: the load
+  // for block kb + 96 is only waited for two blocks later.
   auto sweep = [&](auto&& fn) {
     if (kw0 >= kw1) return;
-    uint4 a0 = load_a(kw0);
-    uint4 a1 = kw0 + 32 < kw1 ? load_a(kw0 + 32) : make_uint4(0, 0, 0, 0);
-    uint4 a2 = kw0 + 64 < kw1 ? load_a(kw0 + 64) : make_uint4(0, 0, 0, 0);
-    for (int kb = kw0; kb < kw1; kb += 32) {
-      const uint4 cur = a0;
-      a0 = a1;
-      a1 = a2;
-      if (kb + 96 < kw1) a2 = load_a(kb + 96);
+    uint4 a0 = load_a(kw0), a1 = load_a(kw0 + 32), a2 = load_a(kw0 + 64);
+    auto step = [&](int kb, uint4& a) __attribute__((always_inline)) {
       f32x16 acc[2];
-      score_block(kb, cur, acc);
+      score_block(kb, a, acc);
+      a = load_a(kb + 96);
       fn(kb, acc);
+    };
+    for (int kb = kw0; kb < kw1; kb += 96) {
+      step(kb, a0);
+      if (kb + 32 < kw1) step(kb + 32, a1);
+      if (kb + 64 < kw1) step(kb + 64, a2);
     }
   };
 
