@@ -622,44 +622,67 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
   // Walk the candidate words: word(list, e, w, slot) once per word of this lane, slot =
   // the first score slot of the word; cand(score, slot, bit) per candidate, the score
   // gathered from the index unless have_scores (then read from the slots)
+  auto cnt_of = [&](int sl) {
+    return sl == 0 ? cnt[0] : sl == 1 ? cnt[1] : sl == 2 ? cnt[2] : cnt[3];
+  };
+  auto load_words = [&](int sl, int e0) {
+    return sl < kPfSubLists && e0 + lane < cnt_of(sl)
+               ? p.cwords[((size_t)vid * kPfSubLists + sl) * p.wcap + e0 + lane]
+               : make_uint2(0u, 0u);
+  };
+  // the batch after (sl, e0) in the four lists laid end to end
+  auto next_batch = [&](int& sl, int& e0) {
+    e0 += 64;
+    while (sl < kPfSubLists && e0 >= cnt_of(sl)) {
+      ++sl;
+      e0 = 0;
+    }
+  };
+  constexpr int kFly = 4;  // candidates of a lane whose index rows are in flight together
   auto walk = [&](bool have_scores, auto&& cand, auto&& word_done) {
     int base = 0;
+    int sl = 0, e0 = -64;
+    next_batch(sl, e0);
+    uint2 wn = load_words(sl, e0);  // the next batch's words are requested a batch early
+    while (sl < kPfSubLists) {
+      const int csl = sl, e = e0 + lane;
+      const uint2 w = wn;
+      next_batch(sl, e0);
+      wn = load_words(sl, e0);
+      const uint32_t nb = (uint32_t)__popc(w.y);
+      const uint32_t incl = wave_incl_sum_u32(nb);
+      int slot = base + (int)(incl - nb);
+      base += (int)__shfl(incl, 63, 64);
+      uint32_t bits = w.y, keep = 0u;
+      while (bits) {
+        int bt[kFly], n = 0;
 #pragma unroll
-    for (int sl = 0; sl < kPfSubLists; ++sl) {
-      const uint2* cl = p.cwords + ((size_t)vid * kPfSubLists + sl) * p.wcap;
-      for (int e0 = 0; e0 < cnt[sl]; e0 += 64) {
-        const int e = e0 + lane;
-        const uint2 w = e < cnt[sl] ? cl[e] : make_uint2(0u, 0u);
-        const uint32_t nb = (uint32_t)__popc(w.y);
-        const uint32_t incl = wave_incl_sum_u32(nb);
-        int slot = base + (int)(incl - nb);
-        base += (int)__shfl(incl, 63, 64);
-        uint32_t bits = w.y, keep = 0u;
-        while (bits) {
-          const int b0 = __builtin_ctz(bits);
+        for (int t = 0; t < kFly; ++t) {
+          bt[t] = bits ? __builtin_ctz(bits) : 0;
+          n += bits ? 1 : 0;
           bits &= bits - 1u;
-          const bool two = bits != 0u;
-          const int b1 = two ? __builtin_ctz(bits) : b0;
-          if (two) bits &= bits - 1u;
-          float s0, s1;
-          if (have_scores) {
-            s0 = cs[slot];
-            s1 = two ? cs[slot + 1] : s0;
-          } else {
-            const int k0 = (int)(w.x * 32u) + b0, k1 = (int)(w.x * 32u) + b1;
-            const uint4 a0 = *(const uint4*)(idx + (size_t)k0 * kR);
-            const uint4 c0 = *(const uint4*)(idx + (size_t)k0 * kR + 8);
-            const uint4 a1 = *(const uint4*)(idx + (size_t)k1 * kR);
-            const uint4 c1 = *(const uint4*)(idx + (size_t)k1 * kR + 8);
-            s0 = score(a0, c0);
-            s1 = score(a1, c1);
-          }
-          keep |= cand(s0, slot, (int)(w.x * 32u) + b0) ? 1u << b0 : 0u;
-          if (two) keep |= cand(s1, slot + 1, (int)(w.x * 32u) + b1) ? 1u << b1 : 0u;
-          slot += two ? 2 : 1;
         }
-        if (e < cnt[sl]) word_done(sl, e, w, keep);
+        float sc[kFly];
+        if (have_scores) {
+#pragma unroll
+          for (int t = 0; t < kFly; ++t) sc[t] = t < n ? cs[slot + t] : 0.f;
+        } else {
+          uint4 ra[kFly], rc[kFly];
+#pragma unroll
+          for (int t = 0; t < kFly; ++t) {
+            const int k = (int)(w.x * 32u) + bt[t];
+            ra[t] = *(const uint4*)(idx + (size_t)k * kR);
+            rc[t] = *(const uint4*)(idx + (size_t)k * kR + 8);
+          }
+#pragma unroll
+          for (int t = 0; t < kFly; ++t) sc[t] = score(ra[t], rc[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < kFly; ++t)
+          if (t < n) keep |= cand(sc[t], slot + t, (int)(w.x * 32u) + bt[t]) ? 1u << bt[t] : 0u;
+        slot += n;
       }
+      if (e < cnt_of(csl)) word_done(csl, e, w, keep);
     }
   };
   auto no_word = [](int, int, uint2, uint32_t) {};
