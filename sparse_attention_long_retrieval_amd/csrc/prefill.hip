@@ -799,10 +799,10 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
 
 // ------------------------------------------------------------------ attend work
 
-// Work items of every vector: the whole vector, or, with more than 256 definite
-// words, pieces of at most 256 words of one wave list (each list's candidates
-// ride with its last piece, the sinks with list 0's first); a keep-all vector is
-// cut into ranges of 8192 keys.
+// Work items of every vector: the whole vector, or, with more than 256 words in all,
+// pieces of at most 256 words of one wave list, whose words are its definite words
+// followed by its candidate words (the sinks ride with list 0's first piece); a
+// keep-all vector is cut into ranges of 8192 keys.
 __global__ __launch_bounds__(256) void k_pf_count(PfPlan p) {
   const int vid = blockIdx.x * 256 + threadIdx.x;
   if (vid >= p.V) return;
@@ -812,15 +812,17 @@ __global__ __launch_bounds__(256) void k_pf_count(PfPlan p) {
   if (v.mode == kPfAll) {
     n = max(1, (pos + kPfItemKeys) / kPfItemKeys);
   } else {
-    int wsum = 0;
-    for (int w = 0; w < 4; ++w) wsum += min(p.wcount[(size_t)vid * 4 + w], p.wcap);
+    // a list's words: its definite words, then its candidate words
+    int tot[4], wsum = 0;
+    for (int w = 0; w < 4; ++w) {
+      tot[w] = min(p.wcount[(size_t)vid * 4 + w], p.wcap) +
+               (v.mode == kPfNormal ? p.ccount[(size_t)vid * kPfSubLists + w] : 0);
+      wsum += tot[w];
+    }
     if (wsum > kPfItemWords) {
       n = 0;
-      for (int w = 0; w < 4; ++w) {
-        const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
-        const bool cands = v.mode == kPfNormal && p.ccount[(size_t)vid * kPfSubLists + w] > 0;
-        n += max((wc + kPfItemWords - 1) / kPfItemWords, (w == 0 || cands) ? 1 : 0);
-      }
+      for (int w = 0; w < 4; ++w)
+        n += max((tot[w] + kPfItemWords - 1) / kPfItemWords, w == 0 ? 1 : 0);
     }
   }
   p.nitem[vid] = n;
@@ -844,7 +846,7 @@ __global__ __launch_bounds__(1024) void k_pf_iscan(PfPlan p) {
     p.ibase[e] = (int)base;
     base += (unsigned)p.nitem[e];
   }
-  if (tid == NT - 1) *p.icount = (int)base;
+  if (tid == NT - 1) *p.icount = (int)min(base, (unsigned)p.max_items);
 }
 
 // The items, each with its order key (pair, first 32-key block it reads), counted
@@ -861,6 +863,7 @@ __global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
   const int bi = vid / (p.G * p.Tq);
   const int nblk = p.nbucket / (p.B * p.n_ret) - 1;
   auto put = [&](int k, int4 item, int blk) {
+    if (base + k >= p.max_items) return;  // never with the plan's sizes; no write past them
     p.items[base + k] = item;
     const int key = bi * (nblk + 1) + min(max(blk, 0), nblk);
     p.ikey[base + k] = key;
@@ -887,18 +890,19 @@ __global__ __launch_bounds__(256) void k_pf_items(PfPlan p) {
   }
   int k = 0;
   for (int w = 0; w < 4; ++w) {
+    // pieces of at most 256 words of the list's definite words followed by its
+    // candidate words; list 0 has a piece (the sinks ride with it) even when empty
     const int wc = min(p.wcount[(size_t)vid * 4 + w], p.wcap);
     const int cc = v.mode == kPfNormal ? p.ccount[(size_t)vid * kPfSubLists + w] : 0;
-    if (wc == 0) {
-      if (w == 0 || cc > 0) {
-        const int blk = cc > 0 ? (int)p.cwords[((size_t)vid * kPfSubLists + w) * p.wcap].x : 0;
-        put(k++, make_int4(vid, w, 0, 0), blk);
-      }
+    const uint2* wl = p.words + ((size_t)vid * 4 + w) * p.wcap;
+    const uint2* cl = p.cwords + ((size_t)vid * kPfSubLists + w) * p.wcap;
+    if (wc + cc == 0) {
+      if (w == 0) put(k++, make_int4(vid, 0, 0, 0), 0);
       continue;
     }
-    const uint2* wl = p.words + ((size_t)vid * 4 + w) * p.wcap;
-    for (int lo = 0; lo < wc; lo += kPfItemWords)
-      put(k++, make_int4(vid, w, lo, min(wc, lo + kPfItemWords)), (int)wl[lo].x);
+    for (int lo = 0; lo < wc + cc; lo += kPfItemWords)
+      put(k++, make_int4(vid, w, lo, min(wc + cc, lo + kPfItemWords)),
+          (int)(lo < wc ? wl[lo].x : cl[lo - wc].x));
   }
 }
 
@@ -1102,8 +1106,8 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
     // The item's rows are produced in batches (at most 16 words = 512 keys) from, in
     // order: a key range (the sinks, every key in keep-all mode, or a keep-all
     // item's range), definite words, the selected candidate words.  A whole
-    // vector takes all four wave lists; a piece takes words [lo, hi) of list it.y
-    // and that list's candidates when it ends the list.  After each batch the full
+    // vector takes all four wave lists; a piece takes words [lo, hi) of list it.y's
+    // definite words followed by its candidate words.  After each batch the full
     // tiles of the queue are attended; the last rows once the sources are exhausted.
     const bool words = it.y < 4 && v.mode == kPfNormal;
     int rng0 = 0, rng1 = 0;
@@ -1116,8 +1120,11 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
     const int w_end = whole ? 4 : it.y + 1;  // lists [sub, w_end)
     int sub = whole ? 0 : it.y;
     int e0 = whole ? 0 : it.z;
+    // a piece covers [it.z, it.w) of its list's definite words followed by its candidate
+    // words: definite [it.z, min(it.w, wcl)), candidate [max(it.z, wcl), it.w) - wcl
+    const int wcl = whole || it.y >= 4 ? 0 : min(p.wcount[(size_t)vid * 4 + it.y], p.wcap);
     bool cands = v.mode == kPfNormal && it.y < 4;
-    if (cands && !whole) cands = it.w == min(p.wcount[(size_t)vid * 4 + it.y], p.wcap);
+    if (cands && !whole) cands = it.w > wcl;
     int src = 0, nq = 0;
     bool more = true;
     while (more || nq > 0) {
@@ -1135,14 +1142,14 @@ __global__ __launch_bounds__(256, 3) void k_pf_attend(PfPlan p) {
           // definite words (src 1) or the selected candidate words (src 2)
           const bool cw = src == 2;
           const int cnt = sub < w_end
-                              ? (cw ? p.ccount[(size_t)vid * kPfSubLists + sub]
-                                    : (whole ? min(p.wcount[(size_t)vid * 4 + sub], p.wcap)
-                                             : it.w))
+                              ? (whole ? (cw ? p.ccount[(size_t)vid * kPfSubLists + sub]
+                                             : min(p.wcount[(size_t)vid * 4 + sub], p.wcap))
+                                       : (cw ? it.w - wcl : min(it.w, wcl)))
                               : 0;
           if (sub == w_end) {
             src = (!cw && cands) ? 2 : 3;
             sub = whole ? 0 : it.y;
-            e0 = 0;
+            e0 = whole ? 0 : max(it.z - wcl, 0);
           } else if (e0 >= cnt) {
             ++sub;
             e0 = 0;
@@ -1223,7 +1230,7 @@ __global__ __launch_bounds__(256) void k_pf_merge(PfPlan p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int vid = blockIdx.x * 4 + wave;
   if (vid >= p.V) return;
-  const int n = p.nitem[vid];
+  const int n = min(p.nitem[vid], p.max_items - p.ibase[vid]);
   if (n <= 1) return;
   const float* pr = p.part + (size_t)p.ibase[vid] * kPfPartStride;
   float M = -INFINITY;
@@ -1348,10 +1355,12 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_cs = take(cs_cap * sizeof(float));
   const size_t nbucket = (size_t)B * n_ret * ((n_keys + 31) / 32 + 1);
   const size_t o_obkt = take(nbucket * sizeof(int));
-  // items per vector: at most one per 256 words of each list (at least one per
-  // list), or one per 8192 keys of a keep-all vector
-  const size_t per_vec = std::max<size_t>(4 * std::max<size_t>((wcap + kPfItemWords - 1) / kPfItemWords, 1),
-                                          ((size_t)n_keys + kPfItemKeys - 1) / kPfItemKeys);
+  // items per vector: at most one per 256 words of each list (at least one), a list
+  // holding up to wcap - 1 definite words and as many candidate words, or one per
+  // 8192 keys of a keep-all vector
+  const size_t per_vec =
+      std::max<size_t>(4 * std::max<size_t>((2 * wcap + kPfItemWords - 1) / kPfItemWords, 1),
+                       ((size_t)n_keys + kPfItemKeys - 1) / kPfItemKeys);
   const size_t max_items = V * per_vec;
   const size_t o_nitem = take(V * sizeof(int));
   const size_t o_ibase = take(V * sizeof(int));
