@@ -622,33 +622,30 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
   // Walk the candidate words: word(list, e, w, slot) once per word of this lane, slot =
   // the first score slot of the word; cand(score, slot, bit) per candidate, the score
   // gathered from the index unless have_scores (then read from the slots)
-  auto cnt_of = [&](int sl) {
-    return sl == 0 ? cnt[0] : sl == 1 ? cnt[1] : sl == 2 ? cnt[2] : cnt[3];
+  // the four lists' words laid end to end: word g of the vector is word g - b[sl] of
+  // list sl, b the lists' first positions
+  const int b1 = cnt[0], b2 = b1 + cnt[1], b3 = b2 + cnt[2], nwords = b3 + cnt[3];
+  auto word_at = [&](int g, int& sl, int& e) {
+    sl = (g >= b1) + (g >= b2) + (g >= b3);
+    e = g - (sl == 0 ? 0 : sl == 1 ? b1 : sl == 2 ? b2 : b3);
   };
-  auto load_words = [&](int sl, int e0) {
-    return sl < kPfSubLists && e0 + lane < cnt_of(sl)
-               ? p.cwords[((size_t)vid * kPfSubLists + sl) * p.wcap + e0 + lane]
-               : make_uint2(0u, 0u);
-  };
-  // the batch after (sl, e0) in the four lists laid end to end
-  auto next_batch = [&](int& sl, int& e0) {
-    e0 += 64;
-    while (sl < kPfSubLists && e0 >= cnt_of(sl)) {
-      ++sl;
-      e0 = 0;
-    }
+  auto load_words = [&](int g0) {
+    int sl, e;
+    word_at(g0 + lane, sl, e);
+    return g0 + lane < nwords ? p.cwords[((size_t)vid * kPfSubLists + sl) * p.wcap + e]
+                              : make_uint2(0u, 0u);
   };
   constexpr int kFly = 4;  // candidates of a lane whose index rows are in flight together
+  // Walk the candidate words, 64 at a time over the four lists (lane = word), the next
+  // batch requested a batch early: cand(score, slot, key) per candidate, the score
+  // gathered from the index unless have_scores (then read from its slot); word_done
+  // (list, position, word, bits whose cand returned true) per word
   auto walk = [&](bool have_scores, auto&& cand, auto&& word_done) {
     int base = 0;
-    int sl = 0, e0 = -64;
-    next_batch(sl, e0);
-    uint2 wn = load_words(sl, e0);  // the next batch's words are requested a batch early
-    while (sl < kPfSubLists) {
-      const int csl = sl, e = e0 + lane;
+    uint2 wn = load_words(0);
+    for (int g0 = 0; g0 < nwords; g0 += 64) {
       const uint2 w = wn;
-      next_batch(sl, e0);
-      wn = load_words(sl, e0);
+      wn = load_words(g0 + 64);
       const uint32_t nb = (uint32_t)__popc(w.y);
       const uint32_t incl = wave_incl_sum_u32(nb);
       int slot = base + (int)(incl - nb);
@@ -682,7 +679,11 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
           if (t < n) keep |= cand(sc[t], slot + t, (int)(w.x * 32u) + bt[t]) ? 1u << bt[t] : 0u;
         slot += n;
       }
-      if (e < cnt_of(csl)) word_done(csl, e, w, keep);
+      if (g0 + lane < nwords) {
+        int sl, e;
+        word_at(g0 + lane, sl, e);
+        word_done(sl, e, w, keep);
+      }
     }
   };
   auto no_word = [](int, int, uint2, uint32_t) {};
