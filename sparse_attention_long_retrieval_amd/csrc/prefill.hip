@@ -636,38 +636,75 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
                               : make_uint2(0u, 0u);
   };
   constexpr int kFly = 4;  // candidates of a lane whose index rows are in flight together
-  // Walk the candidate words, 64 at a time over the four lists (lane = word), the next
-  // batch requested a batch early: cand(score, slot, key) per candidate, the score
-  // gathered from the index unless have_scores (then read from its slot); word_done
-  // (list, position, word, bits whose cand returned true) per word
+  constexpr int kWpl = 4;  // words of a lane per batch: word g0 + 64 j + lane, j < kWpl
+  // Walk the candidate words, 64 kWpl at a time over the four lists, the next batch
+  // requested a batch early; a lane's candidates are taken across its words kFly at a
+  // time: cand(score, slot, key) per candidate, the score gathered from the index
+  // unless have_scores (then read from its slot); word_done(list, position, word, bits
+  // whose cand returned true) per word
   auto walk = [&](bool have_scores, auto&& cand, auto&& word_done) {
     int base = 0;
-    uint2 wn = load_words(0);
-    for (int g0 = 0; g0 < nwords; g0 += 64) {
-      const uint2 w = wn;
-      wn = load_words(g0 + 64);
-      const uint32_t nb = (uint32_t)__popc(w.y);
-      const uint32_t incl = wave_incl_sum_u32(nb);
-      int slot = base + (int)(incl - nb);
-      base += (int)__shfl(incl, 63, 64);
-      uint32_t bits = w.y, keep = 0u;
+    uint2 wn[kWpl];
+#pragma unroll
+    for (int j = 0; j < kWpl; ++j) wn[j] = load_words(64 * j);
+    for (int g0 = 0; g0 < nwords; g0 += 64 * kWpl) {
+      uint2 w[kWpl];
+      int slot[kWpl];
+      uint32_t keep[kWpl];
+#pragma unroll
+      for (int j = 0; j < kWpl; ++j) {
+        w[j] = wn[j];
+        wn[j] = load_words(g0 + 64 * kWpl + 64 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < kWpl; ++j) {
+        const uint32_t nb = (uint32_t)__popc(w[j].y);
+        const uint32_t incl = wave_incl_sum_u32(nb);
+        slot[j] = base + (int)(incl - nb);
+        base += (int)__shfl(incl, 63, 64);
+        keep[j] = 0u;
+      }
+      // the lane's candidates in word order: word jj, its bits left, its next slot
+      int jj = 0;
+      uint32_t bits = w[0].y, blk = w[0].x;
+      int sn = slot[0];
+      auto next_word = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 1; j < kWpl; ++j) {
+          if (bits == 0u && jj == j - 1) {
+            jj = j;
+            bits = w[j].y;
+            blk = w[j].x;
+            sn = slot[j];
+          }
+        }
+      };
+      next_word();
       while (bits) {
-        int bt[kFly], n = 0;
+        int kt[kFly], st[kFly], jt[kFly], bt[kFly], n = 0;
 #pragma unroll
         for (int t = 0; t < kFly; ++t) {
-          bt[t] = bits ? __builtin_ctz(bits) : 0;
-          n += bits ? 1 : 0;
-          bits &= bits - 1u;
+          const bool have = bits != 0u;
+          bt[t] = have ? __builtin_ctz(bits) : 0;
+          kt[t] = (int)(blk * 32u) + bt[t];
+          st[t] = sn;
+          jt[t] = jj;
+          n += have ? 1 : 0;
+          if (have) {
+            bits &= bits - 1u;
+            ++sn;
+            next_word();
+          }
         }
         float sc[kFly];
         if (have_scores) {
 #pragma unroll
-          for (int t = 0; t < kFly; ++t) sc[t] = t < n ? cs[slot + t] : 0.f;
+          for (int t = 0; t < kFly; ++t) sc[t] = t < n ? cs[st[t]] : 0.f;
         } else {
           uint4 ra[kFly], rc[kFly];
 #pragma unroll
           for (int t = 0; t < kFly; ++t) {
-            const int k = (int)(w.x * 32u) + bt[t];
+            const int k = t < n ? kt[t] : kt[0];
             ra[t] = *(const uint4*)(idx + (size_t)k * kR);
             rc[t] = *(const uint4*)(idx + (size_t)k * kR + 8);
           }
@@ -675,14 +712,21 @@ __global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
           for (int t = 0; t < kFly; ++t) sc[t] = score(ra[t], rc[t]);
         }
 #pragma unroll
-        for (int t = 0; t < kFly; ++t)
-          if (t < n) keep |= cand(sc[t], slot + t, (int)(w.x * 32u) + bt[t]) ? 1u << bt[t] : 0u;
-        slot += n;
+        for (int t = 0; t < kFly; ++t) {
+          if (t < n && cand(sc[t], st[t], kt[t])) {
+#pragma unroll
+            for (int j = 0; j < kWpl; ++j) keep[j] |= jt[t] == j ? 1u << bt[t] : 0u;
+          }
+        }
       }
-      if (g0 + lane < nwords) {
-        int sl, e;
-        word_at(g0 + lane, sl, e);
-        word_done(sl, e, w, keep);
+#pragma unroll
+      for (int j = 0; j < kWpl; ++j) {
+        const int g = g0 + 64 * j + lane;
+        if (g < nwords) {
+          int sl, e;
+          word_at(g, sl, e);
+          word_done(sl, e, w[j], keep[j]);
+        }
       }
     }
   };
