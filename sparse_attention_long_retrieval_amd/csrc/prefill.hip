@@ -51,6 +51,8 @@
 #include "rtp_common.h"
 #include "rtp_internal.h"
 
+#include <stdlib.h>
+
 namespace rtp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -1395,8 +1397,13 @@ size_t prefill_workspace(int B, int n_ret, int G, int Tq, int n_keys, PfPlan* pl
   const size_t o_ckey = take(V * kPfSubLists * sizeof(int));
   const size_t o_coff = take(V * sizeof(long long));
   // candidate score slots: 2048 per vector on average (vectors past them compute their
-  // scores again in every pass)
-  const size_t cs_cap = V * 2048;
+  // scores again in every pass).  Test hook: RTP_PREFILL_SCORE_SLOTS sets the number of
+  // slots (0 sends every vector through the recomputing path).
+  size_t cs_cap = V * 2048;
+  if (const char* e = getenv("RTP_PREFILL_SCORE_SLOTS")) {
+    const long long c = atoll(e);
+    if (c >= 0 && (size_t)c < cs_cap) cs_cap = (size_t)c;
+  }
   const size_t o_cs = take(cs_cap * sizeof(float));
   const size_t nbucket = (size_t)B * n_ret * ((n_keys + 31) / 32 + 1);
   const size_t o_obkt = take(nbucket * sizeof(int));

@@ -191,6 +191,35 @@ def test_prefill_retrieval_small(case, top_p):
     print(f"{wl.name} p={top_p}: {kinds} worst |err| {worst:.3g}")
 
 
+def _same_result(a, b, V):
+    """Two runs of one chunk select the same sets and write the same output bits."""
+    assert np.array_equal(a["cnt"], b["cnt"])
+    assert np.array_equal(a["tau"], b["tau"])
+    for v in range(V):
+        c = int(a["cnt"][v])
+        assert np.array_equal(np.sort(a["idx"][v][:c]), np.sort(b["idx"][v][:c])), v
+    assert np.array_equal(a["out"], b["out"])
+
+
+@pytest.mark.parametrize("slots", ["0", "1000"])
+@pytest.mark.parametrize("top_p", [0.9, 0.999])
+@pytest.mark.parametrize("case", RCASES[1:3], ids=[f"s{c[0]}" for c in RCASES[1:3]])
+def test_prefill_retrieval_recomputed_scores(monkeypatch, case, top_p, slots):
+    """Vectors past the resolver's score slots compute their candidates' scores again in
+    every pass (RTP_PREFILL_SCORE_SLOTS caps the slots: 0 sends every vector that way,
+    1000 the vectors after the first few): the same thresholds, sets and output bits as
+    with every vector in the slots, and parity with the oracle."""
+    seed, B, Hq, Hkv, N, Tq, ret, n_sink = case
+    wl = W.random_prefill(seed, B, Hq, Hkv, N, Tq, ret, 256, n_sink=n_sink)
+    kc, vc, idx = O.caches_for(wl)
+    base = _prefill_retrieval(wl, kc, vc, idx, top_p, cap=N)
+    monkeypatch.setenv("RTP_PREFILL_SCORE_SLOTS", slots)
+    res = _prefill_retrieval(wl, kc, vc, idx, top_p, cap=N)
+    _same_result(base, res, wl.B * wl.n_ret * wl.G * wl.Tq)
+    kinds, worst = _check_retrieval(wl, kc, vc, idx, res, top_p, range(Tq))
+    print(f"{wl.name} p={top_p} slots={slots}: {kinds} worst |err| {worst:.3g}")
+
+
 def test_prefill_retrieval_ties():
     """q = 0 gives qi = 0: every score ties at 0, so every key is selected (ties at the
     threshold are included).  The boundary bin holds every key: each candidate word is
