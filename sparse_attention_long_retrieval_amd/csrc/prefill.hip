@@ -572,7 +572,7 @@ __global__ __launch_bounds__(1024) void k_pf_cscan(PfPlan p) {
 constexpr int kResDigit = 10;
 constexpr int kResBuckets = 1 << kResDigit;
 
-__global__ __launch_bounds__(256) void k_pf_resolve(PfPlan p) {
+__global__ __launch_bounds__(256, 3) void k_pf_resolve(PfPlan p) {
   __shared__ unsigned long long rmass[4][kResBuckets];
   __shared__ unsigned rcnt[4][kResBuckets];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
