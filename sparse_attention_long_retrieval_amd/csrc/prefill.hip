@@ -16,9 +16,9 @@
 //   k_pf_index    one block = 64 query vectors of one (batch, KV head) against
 //                 every causal key; S^T = index . qi^T on v_mfma_f32_32x32x16_bf16
 //                 (lane = query vector, 32 keys per step).  Every key gets one
-//                 integer depth code D = floor(2^17 (m - s)); bins at every level
-//                 are ranges of D, so levels nest exactly and every sweep sorts a
-//                 key into the same bin.  Sweeps over the keys:
+//                 integer depth code D = floor(2^17 (m - s)); bins are ranges of
+//                 D, so every sweep sorts a key into the same bin.  Sweeps over
+//                 the keys:
 //                   A  max score m per vector;
 //                   B  mass histogram over 128 bins of 2^14 codes (0.125 score
 //                      units) of a window of D: a bin holds its key count and the
@@ -33,19 +33,22 @@
 //                      order, so the lists (and the attention's row order) are
 //                      the same on every run.  A list holds every block of the
 //                      wave's key range, so no boundary bin is ever too large.
-//   k_pf_resolve  exact threshold inside the boundary bin, one wave per vector:
+//   k_pf_cscan,   exact threshold inside the boundary bin, one wave per vector:
+//   k_pf_resolve
 //                 the candidates' scores are recomputed as the fp32 rounding of
 //                 their exact dot products (the rounding of the exact sum, as the
 //                 definition of the score has it), a radix select over those
 //                 scores with 2^-36 fixed-point masses finds the threshold, and
-//                 the candidate words are rewritten to the selected keys.
+//                 the candidate words are rewritten to the selected keys (the
+//                 scores sit in per-vector slots placed by an exclusive scan).
 //   k_pf_count    cut the attend work into items (a vector with more than 256
-//   ... iscatter  definite words into pieces of at most 256 words of one wave
-//                 list) and order the items by the first key block they read,
-//                 so that items reading the same rows run together.
+//   ... iscatter  words into pieces of at most 256 words of one wave list: its
+//                 definite words, then its candidate words) and order the items
+//                 by the first key block they read, so that items reading the
+//                 same rows run together.
 //   k_pf_attend   persistent waves take items from per-XCD counters and attend
-//                 each over its sinks, definite keys and candidates >= tau, 64
-//                 gathered rows at a time; k_pf_merge combines the partial
+//                 each over its sinks, definite words and selected candidate
+//                 words, 64 gathered rows at a time; k_pf_merge combines the partial
 //                 (m, l, o) of cut vectors with the online-softmax rescaling.
 #include "attn_tile.h"
 #include "rtp_common.h"
