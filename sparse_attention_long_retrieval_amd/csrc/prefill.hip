@@ -123,7 +123,7 @@ struct PfWork {
   int sh;       // bin width 2^sh depth codes
   int dw;       // window start (depth code)
   int dq;       // boundary bin start (depth code)
-  int nwin;     // first-level windows tried
+  int nwin;     // windows tried before this one
   int mode;
   double Z;
   double above; // mass of the keys above the window
@@ -492,8 +492,6 @@ __global__ __launch_bounds__(256, 2) void k_pf_index(PfPlan p) {
     o.m = w.m;
     o.tau = -INFINITY;
     o.mode = w.mode;
-    o.dq = w.dq;
-    o.sh = w.sh;
     o.n_sel = 0;
     o.Z = w.Z;
     o.need = w.need;

@@ -207,8 +207,6 @@ struct PfVec {
   float m;        // max score over keys <= pos
   float tau;      // threshold score (normal mode), set by the resolver
   int mode;
-  int dq;         // boundary bin start, depth code floor(2^17 (m - s))
-  int sh;         // boundary bin width: 2^sh depth codes
   int n_sel;      // selected candidates (normal mode)
   double Z;       // sum exp(s - m) over keys <= pos
   double need;    // top_p * Z minus the mass of the definite keys
